@@ -1,0 +1,278 @@
+// Decode attention of one query row per head over the draft KV cache.
+//
+// Grid (S context splits, n_head_kv).  A block owns `chunk` consecutive KV
+// rows of one KV head and all G = n_head / n_head_kv query heads that read it
+// (each K/V byte is fetched once per step).  A row is spread over head_dim / 8
+// lanes (16 bytes each), so a wave covers 64 / (head_dim / 8) rows per step.
+// Single pass with an online softmax: each lane group keeps (m, l, o) per query
+// head; K and V of a row are requested together.  Lane groups and waves are
+// merged with the log-sum-exp rule at the end.  With S > 1 each block stores
+// (m, l, unnormalised o) and a second kernel combines the splits per query
+// head; with S == 1 the block writes the normalised output.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace e3 {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnMaxChunk = 512;
+
+// 16 bytes of a KV row as floats: 8 bf16 or 4 fp32 values
+template <typename KT>
+struct KvVec;
+template <>
+struct KvVec<uint16_t> {
+  static constexpr int E = 8;
+  __device__ static void unpack(const uint4 w, float* v) {
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+  }
+};
+template <>
+struct KvVec<float> {
+  static constexpr int E = 4;
+  __device__ static void unpack(const uint4 w, float* v) {
+    v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
+  }
+};
+
+template <int HD, int G, typename KT>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
+  constexpr int E = KvVec<KT>::E;
+  constexpr int LPR = HD / E;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * kAttnWaves;
+  static_assert(LPR <= 64 && RPW >= 1, "a row must fit in one wave");
+  __shared__ float obuf[kAttnWaves][G][HD];
+  __shared__ float s_M[kAttnWaves][G], s_L[kAttnWaves][G];
+
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = lane / LPR, sub = lane % LPR, d0 = sub * E;
+  const int r0 = s * chunk, r1 = min(a.T, r0 + chunk);
+  const float scale = 1.0f / sqrtf(float(HD));
+  const KT* Kb = static_cast<const KT*>(a.k_cache) + (size_t)kvh * a.cap * HD + d0;
+  const KT* Vb = static_cast<const KT*>(a.v_cache) + (size_t)kvh * a.cap * HD + d0;
+
+  int r = r0 + wv * RPW + slot;
+  uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
+  if (r < r1) {  // first row's K/V in flight before q arrives
+    kw = *reinterpret_cast<const uint4*>(Kb + (size_t)r * HD);
+    vw = *reinterpret_cast<const uint4*>(Vb + (size_t)r * HD);
+  }
+  float qv[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < E; ++e) qv[g][e] = a.q[(size_t)(kvh * G + g) * HD + d0 + e];
+  float m[G], l[G], acc[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+  }
+  for (; r < r1; r += RPB) {
+    float kf[E], vf[E];
+    KvVec<KT>::unpack(kw, kf);
+    KvVec<KT>::unpack(vw, vf);
+    if (r + RPB < r1) {  // next row's K/V
+      kw = *reinterpret_cast<const uint4*>(Kb + (size_t)(r + RPB) * HD);
+      vw = *reinterpret_cast<const uint4*>(Vb + (size_t)(r + RPB) * HD);
+    }
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) t = fmaf(kf[e], qv[g][e], t);
+      d[g] = t;
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1)
+#pragma unroll
+      for (int g = 0; g < G; ++g) d[g] += __shfl_xor(d[g], o, kWave);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sc = d[g] * scale;
+      const float mn = fmaxf(m[g], sc);
+      const float fo = expf(m[g] - mn);  // 0 on the first row (m = -inf)
+      const float p = expf(sc - mn);
+      l[g] = fmaf(l[g], fo, p);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], fo, p * vf[e]);
+      m[g] = mn;
+    }
+  }
+
+  // merge lane groups and waves: common maximum per head, then sums
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mw = wave_max(m[g]);
+    if (lane == 0) s_M[wv][g] = mw;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float Mb = s_M[0][g];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    const float f = (m[g] == -INFINITY) ? 0.f : expf(m[g] - Mb);
+    l[g] *= f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[g][e] *= f;
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      l[g] += __shfl_xor(l[g], o, kWave);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, kWave);
+    }
+  if (slot == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) obuf[wv][g][d0 + e] = acc[g][e];
+      if (sub == 0) s_L[wv][g] = l[g];
+    }
+  }
+  __syncthreads();
+
+  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
+    const int g = i / HD, dd = i - g * HD;
+    float v = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      v += obuf[w][g][dd];
+      L += s_L[w][g];
+    }
+    const int h = kvh * G + g;
+    if (S == 1) a.out[(size_t)h * HD + dd] = v / L;
+    else a.part_o[((size_t)h * S + s) * HD + dd] = v;
+  }
+  if (S == 1) return;
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float Mb = s_M[0][g], L = 0.f;
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    for (int w = 0; w < kAttnWaves; ++w) L += s_L[w][g];
+    const int h = kvh * G + g;
+    a.part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
+    a.part_ml[((size_t)h * S + s) * 2 + 1] = L;
+  }
+}
+
+// One block per query head: o = sum_s w_s o_s with w_s = exp(m_s - M) / sum_z l_z exp(m_z - M)
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml, int S,
+                                                      int hd, float* __restrict__ out) {
+  extern __shared__ float w[];  // [S]
+  __shared__ float red[32];
+  const int h = blockIdx.x;
+  const float* ml = part_ml + (size_t)h * S * 2;
+  float M = -INFINITY;
+  for (int z = threadIdx.x; z < S; z += blockDim.x) M = fmaxf(M, ml[2 * z]);
+  M = wave_max(M);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) red[wv] = M;
+  __syncthreads();
+  M = red[0];
+  for (int k = 1; k < nw; ++k) M = fmaxf(M, red[k]);
+  float L = 0.f, dummy = 0.f;
+  for (int z = threadIdx.x; z < S; z += blockDim.x) {
+    const float e = expf(ml[2 * z] - M);
+    w[z] = e;
+    L = fmaf(e, ml[2 * z + 1], L);
+  }
+  __syncthreads();
+  block_sum2(L, dummy, red);
+  const float invL = 1.0f / L;
+  const float* po = part_o + (size_t)h * S * hd;
+  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    int z = 0;
+    for (; z + 3 < S; z += 4) {
+      acc0 = fmaf(w[z], po[(size_t)z * hd + d], acc0);
+      acc1 = fmaf(w[z + 1], po[(size_t)(z + 1) * hd + d], acc1);
+      acc2 = fmaf(w[z + 2], po[(size_t)(z + 2) * hd + d], acc2);
+      acc3 = fmaf(w[z + 3], po[(size_t)(z + 3) * hd + d], acc3);
+    }
+    for (; z < S; ++z) acc0 = fmaf(w[z], po[(size_t)z * hd + d], acc0);
+    out[(size_t)h * hd + d] = ((acc0 + acc1) + (acc2 + acc3)) * invL;
+  }
+}
+
+static inline int rows_per_block(int hd, int kv_f32) {
+  const int lpr = hd / (kv_f32 ? 4 : 8);
+  return kAttnWaves * (64 / lpr);
+}
+
+static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S) {
+  const int rpb = rows_per_block(hd, kv_f32);
+  const int target = n_head_kv >= 512 ? 1 : 512 / n_head_kv;
+  int c = (T + target - 1) / target;
+  c = ((c + rpb - 1) / rpb) * rpb;
+  if (c < rpb) c = rpb;
+  if (c > kAttnMaxChunk) c = kAttnMaxChunk;
+  *chunk = c;
+  *S = (T + c - 1) / c;
+}
+
+int attn_max_splits(int cap, int head_dim, int n_head_kv) {
+  // S = ceil(T / chunk) never exceeds the target split count while chunks are
+  // uncapped, nor ceil(T / kAttnMaxChunk) once they are capped
+  (void)head_dim;
+  const int target = n_head_kv >= 512 ? 1 : 512 / n_head_kv;
+  const int capped = (cap + kAttnMaxChunk - 1) / kAttnMaxChunk;
+  return (target > capped ? target : capped) + 1;
+}
+
+template <int HD, typename KT>
+static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStream_t s) {
+  dim3 grid(S, a.n_head_kv), block(64 * kAttnWaves);
+#define E3_ATTN_CASE(GG)                                                        \
+  case GG:                                                                    \
+    hipLaunchKernelGGL((k_attn<HD, GG, KT>), grid, block, 0, s, a, chunk, S); \
+    break;
+  switch (G) {
+    E3_ATTN_CASE(1)
+    E3_ATTN_CASE(2)
+    E3_ATTN_CASE(3)
+    E3_ATTN_CASE(4)
+    E3_ATTN_CASE(5)
+    E3_ATTN_CASE(6)
+    E3_ATTN_CASE(7)
+    E3_ATTN_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef E3_ATTN_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(128), size_t(S) * sizeof(float), s,
+                     a.part_o, a.part_ml, S, HD, a.out);
+  return hipGetLastError();
+}
+
+template <typename KT>
+static hipError_t launch_kt(const AttnArgs& a, int G, int chunk, int S, hipStream_t s) {
+  switch (a.head_dim) {
+    case 64: return launch_hd<64, KT>(a, G, chunk, S, s);
+    case 128: return launch_hd<128, KT>(a, G, chunk, S, s);
+    case 256: return launch_hd<256, KT>(a, G, chunk, S, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  int chunk, S;
+  pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
+  const int G = a.n_head / a.n_head_kv;
+  return a.kv_f32 ? launch_kt<float>(a, G, chunk, S, s) : launch_kt<uint16_t>(a, G, chunk, S, s);
+}
+
+}  // namespace e3

@@ -1,0 +1,779 @@
+// eagle3 engine: the C ABI of include/eagle3.h on top of the gfx950 kernels.
+//
+// Device layout (all library-owned):
+//   weights  fc [n, 3n]; qkv [(nh + 2 nkv) hd, 2n] with the q and k rows of every
+//            head reordered so that rotary partners (i, i + rope_dim/2) are
+//            adjacent rows; o [n, nh hd]; gate/up interleaved [2 ff, n]
+//            (row 2i = gate_i, 2i+1 = up_i); down [n, ff]; lm_head [dv, n];
+//            embedding [Vt, n]; the four norm vectors as fp32; d2t as int32.
+//   draft KV per sequence: K [nkv][max_ctx + 1][hd] then V, fp32 (or bf16), head-major
+//            so one KV head's rows are contiguous for the attention stream.
+//   chain scratch (fp32 vectors, split-attention partials, argmax partials,
+//            device token slots).
+//   append scratch for up to `tf_rows` teacher-forced rows per GEMM pass.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/eagle3.h"
+#include "../../include/eagle3_ledger.h"
+#include "gemv_cfg.hpp"
+#include "kernels.hpp"
+#include "ledger.hpp"
+
+namespace {
+
+thread_local std::string g_load_error;
+
+constexpr int kProfKernels = 9;
+
+struct Profiler {
+  int kernel = -1;
+  std::vector<hipEvent_t> ev;  // pairs
+  size_t used = 0;
+};
+
+}  // namespace
+
+struct eagle3_ctx {
+  eagle3_config cfg{};
+  int device = 0;
+  int n = 0, nh = 0, nkv = 0, hd = 0, qd = 0, kvd = 0, ff = 0, dv = 0, vt = 0, rot = 0, cap = 0;
+  std::vector<void*> allocs;
+
+  uint16_t *w_fc = nullptr, *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr,
+           *w_lm = nullptr, *embed = nullptr;
+  float *nrm_in = nullptr, *nrm_hid = nullptr, *nrm_post = nullptr, *nrm_fin = nullptr;
+  int32_t* d2t = nullptr;
+  double* inv_freq = nullptr;  // [rot / 2]
+  int gcfg[e3::kGemvKinds] = {};
+  int lm_grid = 0;
+  char* kv = nullptr;
+  int kv_f32 = 1;
+  size_t kv_esize = 4;      // bytes per cache element
+  size_t kv_seq_elems = 0;  // K + V elements per sequence
+
+  float *g1 = nullptr, *gA = nullptr, *gB = nullptr, *x1 = nullptr, *act = nullptr, *q = nullptr,
+        *ao = nullptr, *part_o = nullptr, *part_ml = nullptr, *lm_pv = nullptr;
+  int32_t *lm_pi = nullptr, *tok_slots = nullptr;
+
+  int tf_rows = 0;
+  size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
+  uint16_t *tf_A = nullptr, *tf_A_lo = nullptr, *tf_cat16 = nullptr, *tf_cat16_lo = nullptr;
+  float *tf_cat32 = nullptr, *tf_F = nullptr, *tf_P = nullptr;
+
+  e3::Ledger ledger;
+  std::string err;
+  Profiler prof;
+
+  void* k_of(int s) { return kv + size_t(s) * kv_seq_elems * kv_esize; }
+  void* v_of(int s) { return kv + (size_t(s) * kv_seq_elems + kv_seq_elems / 2) * kv_esize; }
+};
+
+struct eagle3_ledger {
+  e3::Ledger l;
+};
+
+namespace {
+
+int set_err(eagle3_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg; else g_load_error = msg;
+  return code;
+}
+
+int hip_fail(eagle3_ctx* c, hipError_t e, const char* what) {
+  std::string m = std::string(what) + ": " + hipGetErrorString(e);
+  return set_err(c, e == hipErrorOutOfMemory ? EAGLE3_E_OOM : EAGLE3_E_HIP, m);
+}
+
+#define E3_HIP(ctx, expr, what)                    \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(ctx, _e, what); \
+  } while (0)
+
+template <typename T>
+int dalloc(eagle3_ctx* c, T** p, size_t count) {
+  void* v = nullptr;
+  hipError_t e = hipMalloc(&v, count * sizeof(T) > 0 ? count * sizeof(T) : 16);
+  if (e != hipSuccess) return hip_fail(c, e, "hipMalloc");
+  c->allocs.push_back(v);
+  *p = static_cast<T*>(v);
+  return EAGLE3_OK;
+}
+
+void free_all(eagle3_ctx* c) {
+  for (void* p : c->allocs) (void)hipFree(p);
+  c->allocs.clear();
+  for (hipEvent_t e : c->prof.ev) (void)hipEventDestroy(e);
+  c->prof.ev.clear();
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// activation inputs are read in 16-byte vectors
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// --- profiling of one kernel family with events on the launching stream -----
+struct ProfScope {
+  eagle3_ctx* c;
+  hipStream_t s;
+  bool on;
+  ProfScope(eagle3_ctx* cx, int kernel, hipStream_t st) : c(cx), s(st), on(false) {
+    if (c->prof.kernel == kernel && c->prof.used + 2 <= c->prof.ev.size()) {
+      on = true;
+      (void)hipEventRecord(c->prof.ev[c->prof.used], s);
+    }
+  }
+  ~ProfScope() {
+    if (on) {
+      (void)hipEventRecord(c->prof.ev[c->prof.used + 1], s);
+      c->prof.used += 2;
+    }
+  }
+};
+
+int validate_config(const eagle3_config* cfg, const char** why) {
+  auto bad = [&](const char* m, int code) { *why = m; return code; };
+  if (cfg->n_aux != 3) return bad("n_aux must be 3", EAGLE3_E_UNSUPPORTED);
+  if (cfg->n_embd <= 0 || cfg->n_head <= 0 || cfg->n_head_kv <= 0 || cfg->head_dim <= 0 ||
+      cfg->n_ff <= 0 || cfg->draft_vocab <= 0 || cfg->target_vocab <= 0)
+    return bad("non-positive dimension", EAGLE3_E_INVAL);
+  if (cfg->max_ctx < 1 || cfg->max_gamma < 1 || cfg->max_seqs < 1)
+    return bad("max_ctx, max_gamma and max_seqs must be >= 1", EAGLE3_E_INVAL);
+  if (cfg->n_head % cfg->n_head_kv) return bad("n_head % n_head_kv != 0", EAGLE3_E_SHAPE);
+  if (cfg->n_head / cfg->n_head_kv > 8) return bad("more than 8 query heads per KV head", EAGLE3_E_UNSUPPORTED);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128 && cfg->head_dim != 256)
+    return bad("head_dim must be 64, 128 or 256", EAGLE3_E_UNSUPPORTED);
+  if (cfg->rope_dim <= 0 || cfg->rope_dim > cfg->head_dim || (cfg->rope_dim & 1))
+    return bad("rope_dim must be even and in (0, head_dim]", EAGLE3_E_UNSUPPORTED);
+  if (cfg->n_embd % 64) return bad("n_embd must be a multiple of 64", EAGLE3_E_UNSUPPORTED);
+  if (cfg->n_ff % 8) return bad("n_ff must be a multiple of 8", EAGLE3_E_UNSUPPORTED);
+  if (!(cfg->rope_theta > 0.f) || !std::isfinite(cfg->rope_theta)) return bad("rope_theta must be > 0", EAGLE3_E_INVAL);
+  if (!(cfg->rms_eps >= 0.f) || !std::isfinite(cfg->rms_eps)) return bad("rms_eps must be >= 0", EAGLE3_E_INVAL);
+  if (int64_t(cfg->max_ctx) + 1 > (int64_t(1) << 30)) return bad("max_ctx too large", EAGLE3_E_UNSUPPORTED);
+  if (cfg->max_gamma > 64) return bad("max_gamma above 64", EAGLE3_E_UNSUPPORTED);
+  if (cfg->kv_dtype != EAGLE3_KV_F32 && cfg->kv_dtype != EAGLE3_KV_BF16)
+    return bad("unknown kv_dtype", EAGLE3_E_INVAL);
+  {  // the GEMV kernels stage a whole fp32 activation vector in LDS (<= 64 KB)
+    const int64_t n = cfg->n_embd, kmax = std::max<int64_t>(
+        {3 * n, 2 * n, int64_t(cfg->n_head) * cfg->head_dim, int64_t(cfg->n_ff)});
+    if (kmax * 4 > 65536) return bad("an activation vector exceeds 64 KB of LDS", EAGLE3_E_UNSUPPORTED);
+  }
+  return EAGLE3_OK;
+}
+
+// rotary-pair order of one head: position p -> source dim
+int rope_src_dim(int p, int rot) {
+  if (p >= rot) return p;
+  return (p & 1) ? (p >> 1) + rot / 2 : (p >> 1);
+}
+
+}  // namespace
+
+extern "C" {
+
+int eagle3_resolve_rope_dim(int32_t rotary_dim, float partial_factor, int32_t head_dim,
+                            int32_t* out) {
+  if (!out) return EAGLE3_E_INVAL;
+  if (head_dim <= 0 || (head_dim & 1)) return EAGLE3_E_INVAL;
+  if (rotary_dim >= 0) {
+    if (rotary_dim == 0 || rotary_dim > head_dim || (rotary_dim & 1)) return EAGLE3_E_UNSUPPORTED;
+    *out = rotary_dim;
+    return EAGLE3_OK;
+  }
+  if (partial_factor >= 0.f || std::isnan(partial_factor)) {
+    const double f = partial_factor;
+    if (!(std::isfinite(f) && f > 0.0 && f <= 1.0)) {  // malformed: full width
+      *out = head_dim;
+      return EAGLE3_OK;
+    }
+    const double dims = f * double(head_dim);
+    const double r = std::nearbyint(dims);
+    if (std::fabs(dims - r) > 1e-4 || r <= 0.0 || (int64_t(r) & 1)) return EAGLE3_E_UNSUPPORTED;
+    *out = int32_t(r);
+    return EAGLE3_OK;
+  }
+  *out = head_dim;
+  return EAGLE3_OK;
+}
+
+int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
+                eagle3_ctx** out) {
+  g_load_error.clear();
+  if (!out) return set_err(nullptr, EAGLE3_E_INVAL, "out is NULL");
+  *out = nullptr;
+  if (!cfg || !w) return set_err(nullptr, EAGLE3_E_INVAL, "config or weights is NULL");
+  const char* why = nullptr;
+  int rc = validate_config(cfg, &why);
+  if (rc) return set_err(nullptr, rc, why);
+  const void* ptrs[14] = {w->fc, w->input_layernorm, w->hidden_norm, w->q_proj, w->k_proj,
+                          w->v_proj, w->o_proj, w->post_attention_layernorm, w->gate_proj,
+                          w->up_proj, w->down_proj, w->norm, w->lm_head, w->embed};
+  static const char* names[14] = {"fc", "input_layernorm", "hidden_norm", "q_proj", "k_proj",
+                                  "v_proj", "o_proj", "post_attention_layernorm", "gate_proj",
+                                  "up_proj", "down_proj", "norm", "lm_head", "embed"};
+  for (int i = 0; i < 14; ++i)
+    if (!ptrs[i]) return set_err(nullptr, EAGLE3_E_INVAL, std::string(names[i]) + " is NULL");
+  if (!w->d2t_host) return set_err(nullptr, EAGLE3_E_INVAL, "d2t is NULL");
+
+  const int64_t n = cfg->n_embd, nh = cfg->n_head, nkv = cfg->n_head_kv, hd = cfg->head_dim;
+  const int64_t qd = nh * hd, kvd = nkv * hd, ff = cfg->n_ff, dv = cfg->draft_vocab,
+                vt = cfg->target_vocab;
+  const int64_t want[14][2] = {{n, 3 * n}, {n, 1},  {n, 1},  {qd, 2 * n}, {kvd, 2 * n},
+                               {kvd, 2 * n}, {n, qd}, {n, 1},  {ff, n},     {ff, n},
+                               {n, ff},     {n, 1},  {dv, n}, {vt, n}};
+  for (int i = 0; i < 14; ++i)
+    if (w->shape[i][0] != want[i][0] || w->shape[i][1] != want[i][1]) {
+      char buf[160];
+      snprintf(buf, sizeof buf, "%s: declared [%lld, %lld], geometry implies [%lld, %lld]",
+               names[i], (long long)w->shape[i][0], (long long)w->shape[i][1],
+               (long long)want[i][0], (long long)want[i][1]);
+      return set_err(nullptr, EAGLE3_E_SHAPE, buf);
+    }
+  if (w->d2t_len != dv) return set_err(nullptr, EAGLE3_E_SHAPE, "d2t length != draft_vocab");
+  std::vector<int32_t> d2t_i32((size_t)dv);
+  for (int64_t i = 0; i < dv; ++i) {
+    const int64_t t = i + w->d2t_host[i];
+    if (t < 0 || t >= vt) return set_err(nullptr, EAGLE3_E_INVAL, "d2t maps outside the target vocabulary");
+    d2t_i32[size_t(i)] = int32_t(w->d2t_host[i]);
+  }
+
+  eagle3_ctx* c = new (std::nothrow) eagle3_ctx();
+  if (!c) return set_err(nullptr, EAGLE3_E_OOM, "host allocation failed");
+  c->cfg = *cfg;
+  c->n = int(n); c->nh = int(nh); c->nkv = int(nkv); c->hd = int(hd);
+  c->qd = int(qd); c->kvd = int(kvd); c->ff = int(ff); c->dv = int(dv); c->vt = int(vt);
+  c->rot = cfg->rope_dim;
+  c->cap = cfg->max_ctx + 1;
+  c->ledger = e3::Ledger(cfg->max_ctx, cfg->max_seqs, cfg->max_gamma);
+  hipStream_t s = as_stream(stream);
+
+  auto fail = [&](int code) {
+    g_load_error = c->err;
+    (void)hipDeviceSynchronize();
+    free_all(c);
+    delete c;
+    return code;
+  };
+#define E3_TRY(x)            \
+  do {                       \
+    int _rc = (x);           \
+    if (_rc) return fail(_rc); \
+  } while (0)
+#define E3_TRYH(x, what)                                  \
+  do {                                                    \
+    hipError_t _e = (x);                                  \
+    if (_e != hipSuccess) return fail(hip_fail(c, _e, what)); \
+  } while (0)
+
+  E3_TRYH(hipGetDevice(&c->device), "hipGetDevice");
+  const size_t N_qkv = size_t(qd + 2 * kvd);
+  E3_TRY(dalloc(c, &c->w_fc, size_t(n) * 3 * n));
+  E3_TRY(dalloc(c, &c->w_qkv, N_qkv * 2 * n));
+  E3_TRY(dalloc(c, &c->w_o, size_t(n) * qd));
+  E3_TRY(dalloc(c, &c->w_gu, size_t(2 * ff) * n));
+  E3_TRY(dalloc(c, &c->w_d, size_t(n) * ff));
+  E3_TRY(dalloc(c, &c->w_lm, size_t(dv) * n));
+  E3_TRY(dalloc(c, &c->embed, size_t(vt) * n));
+  E3_TRY(dalloc(c, &c->nrm_in, size_t(n)));
+  E3_TRY(dalloc(c, &c->nrm_hid, size_t(n)));
+  E3_TRY(dalloc(c, &c->nrm_post, size_t(n)));
+  E3_TRY(dalloc(c, &c->nrm_fin, size_t(n)));
+  E3_TRY(dalloc(c, &c->d2t, size_t(dv)));
+  c->kv_f32 = cfg->kv_dtype == EAGLE3_KV_F32;
+  c->kv_esize = c->kv_f32 ? 4 : 2;
+  c->kv_seq_elems = size_t(2) * kvd * size_t(c->cap);
+  E3_TRY(dalloc(c, &c->kv, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize));
+
+  E3_TRY(dalloc(c, &c->g1, size_t(n)));
+  E3_TRY(dalloc(c, &c->gA, size_t(n)));
+  E3_TRY(dalloc(c, &c->gB, size_t(n)));
+  E3_TRY(dalloc(c, &c->x1, size_t(n)));
+  E3_TRY(dalloc(c, &c->act, size_t(ff)));
+  E3_TRY(dalloc(c, &c->q, size_t(qd)));
+  E3_TRY(dalloc(c, &c->ao, size_t(qd)));
+  const size_t smax = size_t(e3::attn_max_splits(c->cap, c->hd, c->nkv));
+  E3_TRY(dalloc(c, &c->part_o, size_t(nh) * smax * hd));
+  E3_TRY(dalloc(c, &c->part_ml, size_t(nh) * smax * 2));
+  c->gcfg[e3::kGemvEncode] = e3::gemv_pick(e3::kGemvEncode, int(n), int(3 * n));
+  c->gcfg[e3::kGemvQkv] = e3::gemv_pick(e3::kGemvQkv, int(qd + 2 * kvd), int(2 * n));
+  c->gcfg[e3::kGemvO] = e3::gemv_pick(e3::kGemvO, int(n), int(qd));
+  c->gcfg[e3::kGemvGateUp] = e3::gemv_pick(e3::kGemvGateUp, int(2 * ff), int(n));
+  c->gcfg[e3::kGemvDown] = e3::gemv_pick(e3::kGemvDown, int(n), int(ff));
+  c->gcfg[e3::kGemvLmHead] = e3::gemv_pick(e3::kGemvLmHead, int(dv), int(n));
+  c->lm_grid = e3::lmhead_grid(int(dv), c->gcfg[e3::kGemvLmHead]);
+  E3_TRY(dalloc(c, &c->lm_pv, size_t(c->lm_grid)));
+  E3_TRY(dalloc(c, &c->lm_pi, size_t(c->lm_grid)));
+  E3_TRY(dalloc(c, &c->tok_slots, size_t(cfg->max_gamma) + 1));
+  E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
+
+  c->tf_rows = c->cap < 2048 ? c->cap : 2048;
+  {  // small appends use split-K GEMV partials [splits][16][N]; large ones [splits][T][N]
+    const size_t f_small = size_t(16) * n * size_t((3 * n + 511) / 512);
+    const size_t p_small = size_t(16) * 2 * kvd * size_t((2 * n + 511) / 512);
+    c->tf_F_cap = std::max(size_t(c->tf_rows) * n * 2, f_small);
+    c->tf_P_cap = std::max(size_t(c->tf_rows) * 2 * kvd * 2, p_small);
+  }
+  E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
+  E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));
+  if (c->kv_f32) {
+    E3_TRY(dalloc(c, &c->tf_A_lo, size_t(c->tf_rows) * 3 * n));
+    E3_TRY(dalloc(c, &c->tf_cat16_lo, size_t(c->tf_rows) * 2 * n));
+  }
+  E3_TRY(dalloc(c, &c->tf_cat32, size_t(16) * 2 * n));
+  E3_TRY(dalloc(c, &c->tf_F, c->tf_F_cap));
+  E3_TRY(dalloc(c, &c->tf_P, c->tf_P_cap));
+
+  // zero state
+  E3_TRYH(hipMemsetAsync(c->kv, 0, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize, s),
+          "memset kv");
+
+  // weights: straight copies
+  auto cp = [&](void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+  };
+  E3_TRYH(cp(c->w_fc, w->fc, size_t(n) * 3 * n * 2), "copy fc");
+  E3_TRYH(cp(c->w_o, w->o_proj, size_t(n) * qd * 2), "copy o_proj");
+  E3_TRYH(cp(c->w_d, w->down_proj, size_t(n) * ff * 2), "copy down_proj");
+  E3_TRYH(cp(c->w_lm, w->lm_head, size_t(dv) * n * 2), "copy lm_head");
+  E3_TRYH(cp(c->embed, w->embed, size_t(vt) * n * 2), "copy embed");
+  E3_TRYH(e3::launch_bf16_to_f32((const uint16_t*)w->input_layernorm, c->nrm_in, int(n), s), "norm");
+  E3_TRYH(e3::launch_bf16_to_f32((const uint16_t*)w->hidden_norm, c->nrm_hid, int(n), s), "norm");
+  E3_TRYH(e3::launch_bf16_to_f32((const uint16_t*)w->post_attention_layernorm, c->nrm_post, int(n), s), "norm");
+  E3_TRYH(e3::launch_bf16_to_f32((const uint16_t*)w->norm, c->nrm_fin, int(n), s), "norm");
+  E3_TRYH(hipMemcpyAsync(c->d2t, d2t_i32.data(), size_t(dv) * 4, hipMemcpyHostToDevice, s), "copy d2t");
+  std::vector<double> invf((size_t)(c->rot / 2));
+  for (int i = 0; i < c->rot / 2; ++i)
+    invf[size_t(i)] = std::pow(double(cfg->rope_theta), -2.0 * double(i) / double(c->rot));
+  E3_TRYH(hipMemcpyAsync(c->inv_freq, invf.data(), invf.size() * sizeof(double), hipMemcpyHostToDevice, s),
+          "copy inv_freq");
+
+  // repacks by row gathers: qkv (rotary pairs adjacent), gate/up interleaved
+  {
+    std::vector<int32_t> dst, src;
+    const size_t maxrows = std::max<size_t>(size_t(qd), size_t(ff));
+    int32_t* maps = nullptr;
+    E3_TRY(dalloc(c, &maps, 2 * maxrows));
+    auto gather = [&](uint16_t* D, const void* S, int row_len) -> int {
+      hipError_t e = hipMemcpyAsync(maps, dst.data(), dst.size() * 4, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(maps + maxrows, src.data(), src.size() * 4, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess)
+        e = e3::launch_gather_rows(D, (const uint16_t*)S, maps, maps + maxrows, int(dst.size()),
+                                   row_len, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);  // host maps are reused
+      return e == hipSuccess ? EAGLE3_OK : hip_fail(c, e, "repack");
+    };
+    auto head_perm = [&](int64_t heads, int64_t row_off) {
+      dst.clear(); src.clear();
+      for (int64_t h = 0; h < heads; ++h)
+        for (int p = 0; p < hd; ++p) {
+          dst.push_back(int32_t(row_off + h * hd + p));
+          src.push_back(int32_t(h * hd + rope_src_dim(p, c->rot)));
+        }
+    };
+    head_perm(nh, 0);
+    E3_TRY(gather(c->w_qkv, w->q_proj, int(2 * n)));
+    head_perm(nkv, qd);
+    E3_TRY(gather(c->w_qkv, w->k_proj, int(2 * n)));
+    E3_TRYH(cp(c->w_qkv + size_t(qd + kvd) * 2 * n, w->v_proj, size_t(kvd) * 2 * n * 2), "copy v");
+    dst.clear(); src.clear();
+    for (int64_t i = 0; i < ff; ++i) { dst.push_back(int32_t(2 * i)); src.push_back(int32_t(i)); }
+    E3_TRY(gather(c->w_gu, w->gate_proj, int(n)));
+    for (int64_t i = 0; i < ff; ++i) dst[size_t(i)] = int32_t(2 * i + 1);
+    E3_TRY(gather(c->w_gu, w->up_proj, int(n)));
+  }
+  E3_TRYH(hipStreamSynchronize(s), "load sync");
+#undef E3_TRY
+#undef E3_TRYH
+  *out = c;
+  return EAGLE3_OK;
+}
+
+int eagle3_free(eagle3_ctx* ctx) {
+  if (!ctx) return EAGLE3_OK;
+  (void)hipDeviceSynchronize();
+  free_all(ctx);
+  delete ctx;
+  return EAGLE3_OK;
+}
+
+const char* eagle3_last_error(const eagle3_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_load_error.c_str();
+}
+
+int eagle3_kv_len(const eagle3_ctx* ctx, int32_t seq, int32_t* committed, int32_t* spec) {
+  if (!ctx || !committed || !spec) return EAGLE3_E_INVAL;
+  if (!ctx->ledger.valid_seq(seq)) return EAGLE3_E_INVAL;
+  *committed = ctx->ledger.seq(seq).committed;
+  *spec = ctx->ledger.seq(seq).spec;
+  return EAGLE3_OK;
+}
+
+int eagle3_rewind(eagle3_ctx* ctx, int32_t seq, int32_t new_len) {
+  if (!ctx) return EAGLE3_E_INVAL;
+  const char* why = nullptr;
+  int rc = ctx->ledger.check_rewind(seq, new_len, &why);
+  if (rc) return set_err(ctx, rc, why);
+  ctx->ledger.do_rewind(seq, new_len);
+  return EAGLE3_OK;
+}
+
+int eagle3_kv_read(const eagle3_ctx* cctx, int32_t seq, int32_t row0, int32_t nrows, void* k_dev,
+                   void* v_dev, void* stream) {
+  eagle3_ctx* ctx = const_cast<eagle3_ctx*>(cctx);
+  if (!ctx || !k_dev || !v_dev) return EAGLE3_E_INVAL;
+  if (!ctx->ledger.valid_seq(seq)) return set_err(ctx, EAGLE3_E_INVAL, "bad sequence id");
+  if (row0 < 0 || nrows < 0 || int64_t(row0) + nrows > ctx->cap)
+    return set_err(ctx, EAGLE3_E_INVAL, "rows outside the allocation");
+  if (nrows == 0) return EAGLE3_OK;
+  hipStream_t s = as_stream(stream);
+  // cache is [nkv][cap][hd]; output is [nrows][nkv][hd], same element type
+  const size_t rowb = size_t(ctx->hd) * ctx->kv_esize;
+  for (int half = 0; half < 2; ++half) {
+    const char* base = static_cast<const char*>(half ? ctx->v_of(seq) : ctx->k_of(seq));
+    char* dst = static_cast<char*>(half ? v_dev : k_dev);
+    for (int h = 0; h < ctx->nkv; ++h) {
+      E3_HIP(ctx,
+             hipMemcpy2DAsync(dst + size_t(h) * rowb, size_t(ctx->nkv) * rowb,
+                              base + (size_t(h) * ctx->cap + row0) * rowb, rowb, rowb,
+                              size_t(nrows), hipMemcpyDeviceToDevice, s),
+             "kv_read");
+    }
+  }
+  return EAGLE3_OK;
+}
+
+// ---- teacher-forced append over packed rows ----------------------------------
+namespace {
+
+struct AppendSeg {
+  int seq, row0, T, pos0;
+};
+
+int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, const int32_t* tok,
+                const float* a0, const float* a1, const float* a2, hipStream_t s) {
+  const int n = c->n, kvd2 = 2 * c->kvd;
+  size_t seg_i = 0;
+  for (int c0 = 0; c0 < total; c0 += c->tf_rows) {
+    const int T = std::min(c->tf_rows, total - c0);
+    int sp1 = 1, sp2 = 1;
+    size_t f_split = 0, p_split = 0;
+    if (T <= 16) {
+      // weight-streaming path: every weight chunk applied to all T rows
+      const int M = e3::gemv_multi_width(T);
+      {
+        ProfScope ps(c, 7, s);
+        E3_HIP(c, e3::launch_gemv_multi(c->w_fc, n, 3 * n, a0 + size_t(c0) * n, a1 + size_t(c0) * n,
+                                        a2 + size_t(c0) * n, n, T, c->tf_F, &sp1, s), "fc gemv");
+      }
+      f_split = size_t(M) * n;
+      E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
+                                  c->nrm_hid, c->cfg.rms_eps, nullptr, nullptr, c->tf_cat32, s),
+             "tf cat");
+      {
+        ProfScope ps(c, 8, s);
+        E3_HIP(c, e3::launch_gemv_multi(c->w_qkv + size_t(c->qd) * 2 * n, kvd2, 2 * n, c->tf_cat32,
+                                        nullptr, nullptr, 0, T, c->tf_P, &sp2, s), "kv gemv");
+      }
+      p_split = size_t(M) * kvd2;
+    } else {
+      // MFMA path
+      E3_HIP(c, e3::launch_pack_aux(a0 + size_t(c0) * n, a1 + size_t(c0) * n, a2 + size_t(c0) * n,
+                                    T, n, c->tf_A, c->tf_A_lo, s), "pack aux");
+      sp1 = e3::gemm_pick_splits(T, n, 3 * n);
+      while (sp1 > 1 && (size_t(sp1) * T * n > c->tf_F_cap || (3 * n) % (32 * sp1))) --sp1;
+      {
+        ProfScope ps(c, 7, s);
+        E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, T, n,
+                                       3 * n, sp1, s), "fc gemm");
+      }
+      f_split = size_t(T) * n;
+      E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
+                                  c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s),
+             "tf cat");
+      sp2 = e3::gemm_pick_splits(T, kvd2, 2 * n);
+      while (sp2 > 1 && (size_t(sp2) * T * kvd2 > c->tf_P_cap || (2 * n) % (32 * sp2))) --sp2;
+      {
+        ProfScope ps(c, 8, s);
+        E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n,
+                                       c->w_qkv + size_t(c->qd) * 2 * n, 2 * n, c->tf_P, T, kvd2,
+                                       2 * n, sp2, s), "kv gemm");
+      }
+      p_split = size_t(T) * kvd2;
+    }
+    // store the rows of this pass into each segment's cache rows
+    for (; seg_i < segs.size(); ++seg_i) {
+      const AppendSeg& g = segs[seg_i];
+      const int lo = std::max(g.row0, c0), hi = std::min(g.row0 + g.T, c0 + T);
+      if (hi > lo)
+        E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, lo - c0, hi - lo, c->nkv, c->hd, c->rot,
+                                      c->inv_freq, g.pos0 + (lo - g.row0), c->k_of(g.seq),
+                                      c->v_of(g.seq), c->cap, c->kv_f32, s), "tf store");
+      if (g.row0 + g.T > c0 + T) break;  // continues in the next pass
+    }
+  }
+  return EAGLE3_OK;
+}
+
+}  // namespace
+
+int eagle3_prefill(eagle3_ctx* ctx, int32_t seq, int32_t T, const int32_t* tok_dev,
+                   const float* aux0_dev, const float* aux1_dev, const float* aux2_dev,
+                   void* stream) {
+  if (!ctx) return EAGLE3_E_INVAL;
+  const char* why = nullptr;
+  int rc = ctx->ledger.check_prefill(seq, T, &why);
+  if (rc) return set_err(ctx, rc, why);
+  if (T == 0) return EAGLE3_OK;
+  if (!tok_dev || !aux0_dev || !aux1_dev || !aux2_dev)
+    return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
+  if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
+    return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  const int32_t start = ctx->ledger.seq(seq).committed;
+  std::vector<AppendSeg> segs{{seq, 0, T, start}};
+  rc = append_rows(ctx, segs, T, tok_dev, aux0_dev, aux1_dev, aux2_dev, as_stream(stream));
+  if (rc) return rc;
+  ctx->ledger.do_prefill(seq, T);
+  return EAGLE3_OK;
+}
+
+int eagle3_rebuild_after_verify(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_host,
+                                const int32_t* n_accepted_host, const int32_t* tok_dev,
+                                const float* aux0_dev, const float* aux1_dev,
+                                const float* aux2_dev, void* stream) {
+  if (!ctx) return EAGLE3_E_INVAL;
+  if (n_seq < 0 || (n_seq > 0 && (!seq_ids_host || !n_accepted_host)))
+    return set_err(ctx, EAGLE3_E_INVAL, "bad sequence list");
+  if (n_seq == 0) return EAGLE3_OK;
+  if (!tok_dev || !aux0_dev || !aux1_dev || !aux2_dev)
+    return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
+  if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
+    return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  std::vector<AppendSeg> segs;
+  int total = 0;
+  for (int b = 0; b < n_seq; ++b) {
+    const char* why = nullptr;
+    const int s = seq_ids_host[b];
+    int rc = ctx->ledger.check_rebuild(s, n_accepted_host[b], &why);
+    if (rc) return set_err(ctx, rc, why);
+    for (int j = 0; j < b; ++j)
+      if (seq_ids_host[j] == s) return set_err(ctx, EAGLE3_E_INVAL, "duplicate sequence id");
+    segs.push_back({s, total, n_accepted_host[b] + 1, ctx->ledger.seq(s).committed});
+    total += n_accepted_host[b] + 1;
+  }
+  int rc = append_rows(ctx, segs, total, tok_dev, aux0_dev, aux1_dev, aux2_dev, as_stream(stream));
+  if (rc) return rc;
+  for (int b = 0; b < n_seq; ++b) ctx->ledger.do_rebuild(seq_ids_host[b], n_accepted_host[b]);
+  return EAGLE3_OK;
+}
+
+int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_host,
+                       const int32_t* boundary_tok_dev, const float* aux0_dev,
+                       const float* aux1_dev, const float* aux2_dev, int32_t gamma,
+                       uint32_t flags, int32_t* out_ids_dev, int32_t* gamma_eff_host,
+                       const eagle3_debug* dbg, void* stream) {
+  if (!ctx) return EAGLE3_E_INVAL;
+  if (n_seq < 0 || (n_seq > 0 && (!seq_ids_host || !gamma_eff_host)))
+    return set_err(ctx, EAGLE3_E_INVAL, "bad sequence list");
+  if (flags & ~EAGLE3_KEEP_SPEC) return set_err(ctx, EAGLE3_E_INVAL, "unknown flag");
+  if (n_seq == 0) return EAGLE3_OK;
+  if (!boundary_tok_dev || !aux0_dev || !aux1_dev || !aux2_dev || (gamma > 0 && !out_ids_dev))
+    return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
+  if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
+    return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  std::vector<int32_t> geff((size_t)n_seq);
+  for (int b = 0; b < n_seq; ++b) {
+    const char* why = nullptr;
+    const int s = seq_ids_host[b];
+    int rc = ctx->ledger.admit_chain(s, gamma, &geff[size_t(b)], &why);
+    if (rc) return set_err(ctx, rc, why);
+    for (int j = 0; j < b; ++j)
+      if (seq_ids_host[j] == s) return set_err(ctx, EAGLE3_E_INVAL, "duplicate sequence id");
+  }
+  for (int b = 0; b < n_seq; ++b) gamma_eff_host[b] = geff[size_t(b)];
+
+  hipStream_t s = as_stream(stream);
+  const int n = ctx->n;
+  for (int b = 0; b < n_seq; ++b) {
+    const int sq = seq_ids_host[b];
+    const int L = ctx->ledger.seq(sq).committed;
+    const int ge = geff[size_t(b)];
+    int32_t* out_b = out_ids_dev + size_t(b) * gamma;
+    if (ge < gamma) E3_HIP(ctx, e3::launch_fill_i32(out_b + ge, -1, gamma - ge, s), "fill");
+    if (ge == 0) continue;
+    {
+      ProfScope ps(ctx, 6, s);
+      E3_HIP(ctx, e3::launch_encode(ctx->w_fc, n, aux0_dev + size_t(b) * n, aux1_dev + size_t(b) * n,
+                                    aux2_dev + size_t(b) * n, ctx->g1,
+                                    ctx->gcfg[e3::kGemvEncode], s), "encode");
+    }
+    if (dbg && dbg->hidden)
+      E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + size_t(b) * (gamma + 1) * n, ctx->g1, size_t(n) * 4,
+                                 hipMemcpyDeviceToDevice, s), "dbg hidden");
+    float* g = ctx->g1;
+    for (int j = 0; j < ge; ++j) {
+      const int pos = L + j;
+      float* gnext = (j & 1) ? ctx->gB : ctx->gA;
+      e3::QkvArgs qa{};
+      qa.w_qkv = ctx->w_qkv; qa.n = n; qa.n_head = ctx->nh; qa.n_head_kv = ctx->nkv;
+      qa.head_dim = ctx->hd; qa.rope_dim = ctx->rot; qa.inv_freq = ctx->inv_freq;
+      qa.eps = ctx->cfg.rms_eps; qa.embed = ctx->embed; qa.vocab = ctx->vt;
+      if (j == 0) {
+        qa.tok = boundary_tok_dev + b;
+        qa.prev_count = 0;
+      } else {
+        qa.prev_val = ctx->lm_pv; qa.prev_idx = ctx->lm_pi; qa.prev_count = ctx->lm_grid;
+        qa.d2t = ctx->d2t; qa.dv = ctx->dv;
+        qa.prev_out_id = out_b + (j - 1); qa.tok_store = ctx->tok_slots + (j - 1);
+      }
+      qa.g = g; qa.w_in = ctx->nrm_in; qa.w_hid = ctx->nrm_hid; qa.pos = pos; qa.q_out = ctx->q;
+      qa.k_cache = ctx->k_of(sq); qa.v_cache = ctx->v_of(sq); qa.cap = ctx->cap;
+      qa.kv_f32 = ctx->kv_f32;
+      {
+        ProfScope ps(ctx, 2, s);
+        E3_HIP(ctx, e3::launch_qkv(qa, ctx->gcfg[e3::kGemvQkv], s), "qkv");
+      }
+      e3::AttnArgs aa{};
+      aa.q = ctx->q; aa.k_cache = ctx->k_of(sq); aa.v_cache = ctx->v_of(sq); aa.cap = ctx->cap;
+      aa.kv_f32 = ctx->kv_f32;
+      aa.T = pos + 1; aa.n_head = ctx->nh; aa.n_head_kv = ctx->nkv; aa.head_dim = ctx->hd;
+      aa.part_o = ctx->part_o; aa.part_ml = ctx->part_ml; aa.out = ctx->ao;
+      {
+        ProfScope ps(ctx, 5, s);
+        E3_HIP(ctx, e3::launch_attn(aa, s), "attention");
+      }
+      {
+        ProfScope ps(ctx, 4, s);
+        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_o, n, ctx->qd, ctx->ao, g, ctx->x1,
+                                          ctx->gcfg[e3::kGemvO], s), "o_proj");
+      }
+      {
+        ProfScope ps(ctx, 1, s);
+        E3_HIP(ctx, e3::launch_gateup(ctx->w_gu, ctx->ff, n, ctx->x1, ctx->nrm_post,
+                                      ctx->cfg.rms_eps, ctx->act, ctx->gcfg[e3::kGemvGateUp], s),
+               "gate/up");
+      }
+      {
+        ProfScope ps(ctx, 3, s);
+        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_d, n, ctx->ff, ctx->act, ctx->x1, gnext,
+                                          ctx->gcfg[e3::kGemvDown], s), "down");
+      }
+      e3::LmHeadArgs la{};
+      la.w_lm = ctx->w_lm; la.dv = ctx->dv; la.n = n; la.h = gnext; la.w_norm = ctx->nrm_fin;
+      la.eps = ctx->cfg.rms_eps;
+      la.logits_dbg = (dbg && dbg->logits) ? dbg->logits + (size_t(b) * gamma + j) * ctx->dv : nullptr;
+      la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;
+      {
+        ProfScope ps(ctx, 0, s);
+        E3_HIP(ctx, e3::launch_lmhead(la, ctx->gcfg[e3::kGemvLmHead], s), "lm_head");
+      }
+      if (dbg && dbg->hidden)
+        E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + (size_t(b) * (gamma + 1) + j + 1) * n, gnext,
+                                   size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
+      g = gnext;
+    }
+    E3_HIP(ctx, e3::launch_argmax_finalize(ctx->lm_pv, ctx->lm_pi, ctx->lm_grid, ctx->d2t, ctx->dv,
+                                           out_b + (ge - 1), ctx->tok_slots + (ge - 1), s),
+           "argmax");
+  }
+  for (int b = 0; b < n_seq; ++b)
+    ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
+  return EAGLE3_OK;
+}
+
+int eagle3_profile_enable(eagle3_ctx* ctx, int32_t kernel, int32_t enable) {
+  if (!ctx) return EAGLE3_E_INVAL;
+  if (kernel < 0 || kernel >= kProfKernels) return set_err(ctx, EAGLE3_E_INVAL, "bad kernel id");
+  if (!enable) { ctx->prof.kernel = -1; return EAGLE3_OK; }
+  const size_t want = 2 * 8192;
+  while (ctx->prof.ev.size() < want) {
+    hipEvent_t e;
+    E3_HIP(ctx, hipEventCreate(&e), "hipEventCreate");
+    ctx->prof.ev.push_back(e);
+  }
+  ctx->prof.kernel = kernel;
+  ctx->prof.used = 0;
+  return EAGLE3_OK;
+}
+
+int eagle3_profile_read(eagle3_ctx* ctx, double* total_ms, int64_t* launches) {
+  if (!ctx || !total_ms || !launches) return EAGLE3_E_INVAL;
+  double tot = 0.0;
+  for (size_t i = 0; i + 1 < ctx->prof.used; i += 2) {
+    E3_HIP(ctx, hipEventSynchronize(ctx->prof.ev[i + 1]), "event sync");
+    float ms = 0.f;
+    E3_HIP(ctx, hipEventElapsedTime(&ms, ctx->prof.ev[i], ctx->prof.ev[i + 1]), "elapsed");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = int64_t(ctx->prof.used / 2);
+  return EAGLE3_OK;
+}
+
+// ---- the ledger on its own ----------------------------------------------------
+int eagle3_ledger_create(int32_t max_ctx, int32_t max_seqs, int32_t max_gamma, eagle3_ledger** out) {
+  if (!out) return EAGLE3_E_INVAL;
+  *out = nullptr;
+  if (max_ctx < 1 || max_seqs < 1 || max_gamma < 1) return EAGLE3_E_INVAL;
+  eagle3_ledger* l = new (std::nothrow) eagle3_ledger();
+  if (!l) return EAGLE3_E_OOM;
+  l->l = e3::Ledger(max_ctx, max_seqs, max_gamma);
+  *out = l;
+  return EAGLE3_OK;
+}
+
+void eagle3_ledger_destroy(eagle3_ledger* l) { delete l; }
+
+int eagle3_ledger_prefill(eagle3_ledger* l, int32_t seq, int32_t T) {
+  if (!l) return EAGLE3_E_INVAL;
+  int rc = l->l.check_prefill(seq, T, nullptr);
+  if (rc) return rc;
+  l->l.do_prefill(seq, T);
+  return EAGLE3_OK;
+}
+
+int eagle3_ledger_chain(eagle3_ledger* l, int32_t seq, int32_t gamma, uint32_t flags,
+                        int32_t* gamma_eff) {
+  if (!l || !gamma_eff) return EAGLE3_E_INVAL;
+  if (flags & ~EAGLE3_KEEP_SPEC) return EAGLE3_E_INVAL;
+  int32_t g = 0;
+  int rc = l->l.admit_chain(seq, gamma, &g, nullptr);
+  if (rc) return rc;
+  l->l.do_chain(seq, g, (flags & EAGLE3_KEEP_SPEC) != 0);
+  *gamma_eff = g;
+  return EAGLE3_OK;
+}
+
+int eagle3_ledger_rebuild(eagle3_ledger* l, int32_t seq, int32_t n_accepted) {
+  if (!l) return EAGLE3_E_INVAL;
+  int rc = l->l.check_rebuild(seq, n_accepted, nullptr);
+  if (rc) return rc;
+  l->l.do_rebuild(seq, n_accepted);
+  return EAGLE3_OK;
+}
+
+int eagle3_ledger_rewind(eagle3_ledger* l, int32_t seq, int32_t new_len) {
+  if (!l) return EAGLE3_E_INVAL;
+  int rc = l->l.check_rewind(seq, new_len, nullptr);
+  if (rc) return rc;
+  l->l.do_rewind(seq, new_len);
+  return EAGLE3_OK;
+}
+
+int eagle3_ledger_len(const eagle3_ledger* l, int32_t seq, int32_t* committed, int32_t* spec) {
+  if (!l || !committed || !spec) return EAGLE3_E_INVAL;
+  if (!l->l.valid_seq(seq)) return EAGLE3_E_INVAL;
+  *committed = l->l.seq(seq).committed;
+  *spec = l->l.seq(seq).spec;
+  return EAGLE3_OK;
+}
+
+}  // extern "C"

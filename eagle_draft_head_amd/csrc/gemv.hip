@@ -1,0 +1,596 @@
+// GEMV family: y = W x with bf16 weights streamed from HBM in 16-byte
+// coalesced loads and fp32 activations staged in LDS, fp32 accumulate.
+//
+// Single-vector kernels (the draft step) fuse their neighbours:
+//   k_qkv     prologue: finish the previous step's argmax (+ d2t), gather the
+//             token's embedding row, RMSNorm both halves, concat; epilogue:
+//             NeoX rotation of q/k (rows repacked so partners are adjacent),
+//             q to fp32, k/v rows to the bf16 KV cache;
+//   k_gemv_resid   epilogue: + residual (o_proj, down);
+//   k_gateup  prologue: RMSNorm; epilogue: silu(gate) * up (rows interleaved);
+//   k_lmhead  prologue: RMSNorm; epilogue: per-block (max, argmax) candidate;
+//   k_encode  prologue: concat of the three tap streams.
+// The multi-vector kernel (teacher-forced rows) applies each weight chunk to
+// M activation vectors and splits K so the M vectors fit in LDS; it writes
+// split partials that the next kernel sums.
+//
+// Work split: a wave owns R consecutive rows; lane l reads 16-byte chunks
+// l, l+64, ... of each row (1 KB per row per wave instruction); U chunk steps
+// are issued before their FMAs so each lane keeps U*R loads in flight.  The
+// per-row sums are reduced across the wave at the end.  No block ever waits
+// for another block: cross-block reductions happen in the next kernel.
+#include "common.hpp"
+#include "gemv_cfg.hpp"
+#include "kernels.hpp"
+
+namespace e3 {
+
+// Stream the R rows a wave owns against the fp32 vector in LDS.  Chunks
+// (8 elements, 16 bytes) below `split` accumulate into lo, the rest into hi, so
+// a caller can scale two halves of the input differently afterwards.
+template <int R, int U, bool SPLIT>
+__device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t ldw, int row0,
+                                         int N, int K, int split, const float* __restrict__ xs,
+                                         float (&lo)[R], float (&hi)[R]) {
+  const int lane = threadIdx.x & 63;
+  const uint4* wp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * ldw);
+    lo[r] = 0.f;
+    hi[r] = 0.f;
+  }
+  const int nch = K >> 3;
+  const float4* x4 = reinterpret_cast<const float4*>(xs);
+  int c = lane;
+  for (; c + 64 * (U - 1) < nch; c += 64 * U) {
+    uint4 w[U][R];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[u][r] = ld_stream(wp[r] + c + 64 * u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cc = c + 64 * u;
+      const float4 a = x4[2 * cc], b = x4[2 * cc + 1];
+      if (!SPLIT || cc < split) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) lo[r] = dot8(w[u][r], a, b, lo[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) hi[r] = dot8(w[u][r], a, b, hi[r]);
+      }
+    }
+  }
+  for (; c < nch; c += 64) {
+    uint4 t[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) t[r] = ld_stream(wp[r] + c);
+    const float4 a = x4[2 * c], b = x4[2 * c + 1];
+    if (!SPLIT || c < split) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) lo[r] = dot8(t[r], a, b, lo[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) hi[r] = dot8(t[r], a, b, hi[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    lo[r] = wave_sum(lo[r]);
+    if (SPLIT) hi[r] = wave_sum(hi[r]);
+  }
+}
+
+// xs[i] = v[i] * w[i] (the norm weight applied, not yet the 1/rms factor);
+// returns this thread's share of sum(v^2).  n % 4 == 0; 16-byte loads, four
+// per thread in flight.
+__device__ __forceinline__ float stage_weighted(float* xs, const float* __restrict__ v,
+                                                const float* __restrict__ w, int n) {
+  const float4* v4 = reinterpret_cast<const float4*>(v);
+  const float4* w4 = reinterpret_cast<const float4*>(w);
+  float4* x4 = reinterpret_cast<float4*>(xs);
+  float ss = 0.f;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) {
+    const float4 a = v4[i], b = w4[i];
+    x4[i] = make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+    ss = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, ss))));
+  }
+  return ss;
+}
+
+// xs[i] = e[i] * w[i] for a bf16 row e; returns the share of sum(e^2)
+__device__ __forceinline__ float stage_weighted_bf16(float* xs, const uint16_t* __restrict__ e,
+                                                     const float* __restrict__ w, int n) {
+  const uint2* e4 = reinterpret_cast<const uint2*>(e);
+  const float4* w4 = reinterpret_cast<const float4*>(w);
+  float4* x4 = reinterpret_cast<float4*>(xs);
+  float ss = 0.f;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) {
+    const uint2 u = e4[i];
+    const float4 b = w4[i];
+    const float a0 = bf16_lo(u.x), a1 = bf16_hi(u.x), a2 = bf16_lo(u.y), a3 = bf16_hi(u.y);
+    x4[i] = make_float4(a0 * b.x, a1 * b.y, a2 * b.z, a3 * b.w);
+    ss = fmaf(a0, a0, fmaf(a1, a1, fmaf(a2, a2, fmaf(a3, a3, ss))));
+  }
+  return ss;
+}
+
+// xs[0:n) = v  (n % 4 == 0)
+__device__ __forceinline__ void stage_plain(float* xs, const float* __restrict__ v, int n) {
+  const float4* v4 = reinterpret_cast<const float4*>(v);
+  float4* x4 = reinterpret_cast<float4*>(xs);
+#pragma unroll 4
+  for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) x4[i] = v4[i];
+}
+
+// cos/sin of pos * inv_freq, the angle reduced modulo 2*pi in double first
+__device__ __forceinline__ void rope_cs(int pos, double inv_freq, float* c, float* s) {
+  const double twopi = 6.283185307179586476925286766559;
+  double a = double(pos) * inv_freq;
+  a -= floor(a * (1.0 / twopi)) * twopi;
+  sincosf(float(a), s, c);
+}
+
+// Argmax over `count` (value, index) candidates; every thread gets the result.
+__device__ __forceinline__ int block_argmax(const float* __restrict__ pv,
+                                            const int32_t* __restrict__ pi, int count,
+                                            float* sv, int* si) {
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int b = threadIdx.x; b < count; b += blockDim.x) {
+    const float v = pv[b];
+    const int i = pi[b];
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  }
+  wave_argmax(bv, bi);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  bv = sv[0];
+  bi = si[0];
+  for (int k = 1; k < nw; ++k)
+    if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
+  __syncthreads();
+  return bi;
+}
+
+// ---------------------------------------------------------------------------
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restrict__ W, int n,
+                                                       const float* __restrict__ a0,
+                                                       const float* __restrict__ a1,
+                                                       const float* __restrict__ a2,
+                                                       float* __restrict__ out) {
+  extern __shared__ float xs[];
+  stage_plain(xs, a0, n);
+  stage_plain(xs + n, a1, n);
+  stage_plain(xs + 2 * n, a2, n);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  if (row0 >= n) return;
+  float acc[R], unused[R];
+  rows_dot<R, U, false>(W, size_t(3) * n, row0, n, 3 * n, 0, xs, acc, unused);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (lane == r && row0 + r < n) out[row0 + r] = acc[r];
+}
+
+// ---------------------------------------------------------------------------
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
+  static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
+  extern __shared__ float xs[];
+  __shared__ float red[32];
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int n = a.n;
+  const int hd = a.head_dim;
+  const int qd = a.n_head * hd, kvd = a.n_head_kv * hd;
+  const int N = qd + 2 * kvd;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  // hidden half first: it does not depend on the token
+  float sg = stage_weighted(xs + n, a.g, a.w_hid, n);
+  int tok;
+  if (a.prev_count > 0) {
+    // finish the previous step: argmax over the lm_head candidates, d2t
+    int bi = block_argmax(a.prev_val, a.prev_idx, a.prev_count, sv, si);
+    if (bi < 0 || bi >= a.dv) bi = 0;  // only reachable with NaN logits
+    tok = bi + a.d2t[bi];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *a.prev_out_id = tok;
+      *a.tok_store = tok;
+    }
+  } else {
+    tok = *a.tok;
+  }
+  tok = min(max(tok, 0), a.vocab - 1);  // out-of-range ids are clamped
+  float se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
+  __syncthreads();
+  float acc_e[R], acc_g[R];
+  if (row0 < N) rows_dot<R, U, true>(a.w_qkv, size_t(2) * n, row0, N, 2 * n, n >> 3, xs, acc_e, acc_g);
+  block_sum2(se, sg, red);  // every wave takes part
+  if (row0 >= N) return;
+  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
+  const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+
+#pragma unroll
+  for (int p = 0; p < R / 2; ++p) {
+    const int r = row0 + 2 * p;
+    if (lane != p || r >= N) continue;
+    float y0 = acc_e[2 * p] * ie + acc_g[2 * p] * ig;
+    float y1 = acc_e[2 * p + 1] * ie + acc_g[2 * p + 1] * ig;
+    int seg, rr;
+    if (r < qd) { seg = 0; rr = r; }
+    else if (r < qd + kvd) { seg = 1; rr = r - qd; }
+    else { seg = 2; rr = r - qd - kvd; }
+    const int head = rr / hd, li = rr - head * hd;
+    int d0 = li, d1 = li + 1;
+    if (seg < 2 && li < a.rope_dim) {
+      const int i = li >> 1;
+      d0 = i;
+      d1 = i + (a.rope_dim >> 1);
+      float c, s;
+      rope_cs(a.pos, a.inv_freq[i], &c, &s);
+      const float t0 = y0 * c - y1 * s;
+      const float t1 = y1 * c + y0 * s;
+      y0 = t0;
+      y1 = t1;
+    }
+    if (seg == 0) {
+      a.q_out[head * hd + d0] = y0;
+      a.q_out[head * hd + d1] = y1;
+    } else {
+      void* base = seg == 1 ? a.k_cache : a.v_cache;
+      const size_t row = ((size_t)head * a.cap + a.pos) * hd;
+      kv_store(base, row + d0, y0, a.kv_f32);
+      kv_store(base, row + d1, y1, a.kv_f32);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __restrict__ W, int N,
+                                                           int K, const float* __restrict__ x,
+                                                           const float* __restrict__ resid,
+                                                           float* __restrict__ y) {
+  extern __shared__ float xs[];
+  stage_plain(xs, x, K);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  if (row0 >= N) return;
+  float acc[R], unused[R];
+  rows_dot<R, U, false>(W, size_t(K), row0, N, K, 0, xs, acc, unused);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (lane == r && row0 + r < N) y[row0 + r] = acc[r] + resid[row0 + r];
+}
+
+// ---------------------------------------------------------------------------
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restrict__ W, int n_ff,
+                                                       int n, const float* __restrict__ x1,
+                                                       const float* __restrict__ w_post, float eps,
+                                                       float* __restrict__ act) {
+  static_assert(R % 2 == 0, "gate/up pairs need an even row count per wave");
+  extern __shared__ float xs[];
+  __shared__ float red[32];
+  const int N = 2 * n_ff;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  float ss = stage_weighted(xs, x1, w_post, n), dummy = 0.f;
+  __syncthreads();
+  float acc[R], unused[R];
+  if (row0 < N) rows_dot<R, U, false>(W, size_t(n), row0, N, n, 0, xs, acc, unused);
+  block_sum2(ss, dummy, red);
+  if (row0 >= N) return;
+  const float inv = 1.0f / sqrtf(ss / float(n) + eps);
+#pragma unroll
+  for (int p = 0; p < R / 2; ++p) {
+    const int r = row0 + 2 * p;
+    if (lane == p && r < N) {
+      const float gt = acc[2 * p] * inv, up = acc[2 * p + 1] * inv;
+      act[r >> 1] = (gt / (1.0f + expf(-gt))) * up;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
+  extern __shared__ float xs[];
+  __shared__ float red[32];
+  __shared__ float bv_s[16];
+  __shared__ int bi_s[16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  float ss = stage_weighted(xs, a.h, a.w_norm, a.n), dummy = 0.f;
+  __syncthreads();
+  float acc[R], unused[R];
+  if (row0 < a.dv) rows_dot<R, U, false>(a.w_lm, size_t(a.n), row0, a.dv, a.n, 0, xs, acc, unused);
+  block_sum2(ss, dummy, red);
+  const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  if (row0 < a.dv) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (row0 + r < a.dv) {
+        const float v = acc[r] * inv;
+        if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; }
+        if (a.logits_dbg && lane == r) a.logits_dbg[row0 + r] = v;
+      }
+    }
+  }
+  if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < WAVES; ++w)
+      if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; }
+    a.part_val[blockIdx.x] = bv;
+    a.part_idx[blockIdx.x] = bi;
+  }
+}
+
+// the last step of a chain: argmax over the lm_head candidates, d2t
+__global__ __launch_bounds__(256) void k_argmax_finalize(const float* __restrict__ pv,
+                                                         const int32_t* __restrict__ pi, int count,
+                                                         const int32_t* __restrict__ d2t, int dv,
+                                                         int32_t* out_id, int32_t* tok_store) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  int bi = block_argmax(pv, pi, count, sv, si);
+  if (threadIdx.x == 0) {
+    if (bi < 0 || bi >= dv) bi = 0;
+    const int t = bi + d2t[bi];
+    *out_id = t;
+    if (tok_store) *tok_store = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-vector split-K GEMV: P[z][m][r] = sum_{k in chunk z} W[r, k] * X_m[k]
+// for m < M.  X is either three fp32 tap streams concatenated along K (x0/x1/x2
+// with row length seg) or one fp32 matrix (x1 == nullptr) with row stride K.
+// Each weight chunk is loaded once and applied to all M vectors; a block covers
+// 8 * R rows, with R chosen so the accumulators stay in registers.
+template <int M>
+struct MultiShape {
+  static constexpr int R = M <= 4 ? 8 : (M <= 8 ? 4 : 2);
+  static constexpr int WAVES = 8;
+  static constexpr int ROWS = WAVES * R;
+};
+
+template <int M>
+__global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__ W, int N, int K,
+                                                    int kc, const float* __restrict__ x0,
+                                                    const float* __restrict__ x1,
+                                                    const float* __restrict__ x2, int seg,
+                                                    int rows, float* __restrict__ P) {
+  constexpr int R = MultiShape<M>::R;
+  constexpr int WAVES = MultiShape<M>::WAVES;
+  extern __shared__ float xs[];  // [M][kc]
+  const int z = blockIdx.y;
+  const int k0 = z * kc;
+  const int klen = min(kc, K - k0);
+  const int k4 = klen >> 2;
+  for (int m = 0; m < M; ++m) {
+    float4* dst = reinterpret_cast<float4*>(xs + m * kc);
+    if (m >= rows) {
+      for (int i = threadIdx.x; i < k4; i += blockDim.x) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+#pragma unroll 4
+    for (int i = threadIdx.x; i < k4; i += blockDim.x) {
+      const int k = k0 + 4 * i;
+      const float* src;
+      if (x1) {
+        const int sgi = k / seg;
+        src = (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2)) + (size_t)m * seg + (k - sgi * seg);
+      } else {
+        src = x0 + (size_t)m * K + k;
+      }
+      dst[i] = *reinterpret_cast<const float4*>(src);
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  if (row0 >= N) return;
+  const uint4* wp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * K + k0);
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+  const int nch = klen >> 3;
+  for (int c = lane; c < nch; c += 64) {
+    uint4 w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = ld_stream(wp[r] + c);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4* x4 = reinterpret_cast<const float4*>(xs + m * kc);
+      const float4 a = x4[2 * c], b = x4[2 * c + 1];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][m] = dot8(w[r], a, b, acc[r][m]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+  float* Pz = P + (size_t)z * M * N;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (lane == ((r * M + m) & 63) && row0 + r < N) Pz[(size_t)m * N + row0 + r] = acc[r][m];
+}
+
+// ---------------------------------------------------------------------------
+// launchers: the configuration (waves per block, rows per wave, chunk steps in
+// flight) is picked per matrix shape from the tuned table in gemv_cfg.hpp
+#define E3_DISPATCH_CFG(cfg, CASE)                                                \
+  switch (cfg) {                                                                  \
+    E3_GEMV_CONFIGS(CASE)                                                         \
+    default:                                                                      \
+      return hipErrorInvalidValue;                                                \
+  }
+
+static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const float* a1,
+                         const float* a2, float* g_out, int cfg, hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                               \
+  case ID:                                                                                 \
+    hipLaunchKernelGGL((k_encode<WV, RR, UU>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
+                       size_t(3 * n) * sizeof(float), s, w_fc, n, a0, a1, a2, g_out);      \
+    break;
+  E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
+  const int N = (a.n_head + 2 * a.n_head_kv) * a.head_dim;
+#define CASE(ID, WV, RR, UU)                                                               \
+  case ID:                                                                                 \
+    if (RR % 2) return hipErrorInvalidValue;                                               \
+    hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(N, WV * RR)),    \
+                       dim3(64 * WV), size_t(2 * a.n) * sizeof(float), s, a);              \
+    break;
+  E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_resid(const uint16_t* w, int N, int K, const float* x, const float* resid,
+                             float* y, int cfg, hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                               \
+  case ID:                                                                                 \
+    hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU>), dim3(ceil_div(N, WV * RR)),            \
+                       dim3(64 * WV), size_t(K) * sizeof(float), s, w, N, K, x, resid, y); \
+    break;
+  E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* x1,
+                         const float* w_post, float eps, float* act, int cfg, hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                                \
+  case ID:                                                                                  \
+    if (RR % 2) return hipErrorInvalidValue;                                                \
+    hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(2 * n_ff, WV * RR)), \
+                       dim3(64 * WV), size_t(n) * sizeof(float), s, w_gu, n_ff, n, x1, w_post, \
+                       eps, act);                                                           \
+    break;
+  E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+  return hipGetLastError();
+}
+
+int lmhead_grid(int dv, int cfg) {
+  switch (cfg) {
+#define CASE(ID, WV, RR, UU) \
+  case ID:                   \
+    return ceil_div(dv, WV * RR);
+    E3_GEMV_CONFIGS(CASE)
+#undef CASE
+    default:
+      return -1;
+  }
+}
+
+hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                                  \
+  case ID:                                                                                    \
+    hipLaunchKernelGGL((k_lmhead<WV, RR, UU>), dim3(ceil_div(a.dv, WV * RR)), dim3(64 * WV), \
+                       size_t(a.n) * sizeof(float), s, a);                                    \
+    break;
+  E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, int count, const int32_t* d2t,
+                                  int dv, int32_t* out_id, int32_t* tok_store, hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(256), 0, s, pv, pi, count, d2t, dv, out_id,
+                     tok_store);
+  return hipGetLastError();
+}
+
+// multi-vector: M is rounded up to an instantiated width
+int gemv_multi_width(int rows) {
+  static const int widths[] = {1, 2, 3, 4, 5, 6, 8, 9, 12, 16};
+  for (int w : widths)
+    if (rows <= w) return w;
+  return -1;
+}
+
+static int multi_rows_per_block(int m) {
+  switch (m) {
+#define RCASE(MM) \
+  case MM:        \
+    return MultiShape<MM>::ROWS;
+    RCASE(1) RCASE(2) RCASE(3) RCASE(4) RCASE(5) RCASE(6) RCASE(8) RCASE(9) RCASE(12) RCASE(16)
+#undef RCASE
+    default:
+      return -1;
+  }
+}
+
+// K chunk: at most 64 KB of LDS for the M vectors, at least ~512 blocks in all
+static int multi_kchunk(int m, int N, int K) {
+  const int row_blocks = ceil_div(N, multi_rows_per_block(m));
+  int kc = (65536 / 4) / m;
+  kc = (kc / 512) * 512;
+  const int want_splits = ceil_div(512, row_blocks);
+  int by_blocks = ceil_div(K, want_splits);
+  by_blocks = ceil_div(by_blocks, 512) * 512;
+  if (by_blocks < kc) kc = by_blocks;
+  if (kc < 512) kc = 512;
+  return kc;
+}
+
+int gemv_multi_splits(int rows, int N, int K) {
+  const int m = gemv_multi_width(rows);
+  if (m < 0) return -1;
+  return ceil_div(K, multi_kchunk(m, N, K));
+}
+
+hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, const float* x1,
+                             const float* x2, int seg, int rows, float* P, int* splits_out,
+                             hipStream_t s) {
+  const int m = gemv_multi_width(rows);
+  if (m < 0 || (K % 8) || (x1 && (seg % 4))) return hipErrorInvalidValue;
+  const int kc = multi_kchunk(m, N, K);
+  const int splits = ceil_div(K, kc);
+  *splits_out = splits;
+  dim3 grid(ceil_div(N, multi_rows_per_block(m)), splits), block(512);
+  const size_t lds = size_t(m) * kc * sizeof(float);
+  switch (m) {
+#define MCASE(MM)                                                                              \
+  case MM:                                                                                     \
+    hipLaunchKernelGGL((k_gemv_multi<MM>), grid, block, lds, s, W, N, K, kc, x0, x1, x2, seg,  \
+                       rows, P);                                                               \
+    break;
+    MCASE(1) MCASE(2) MCASE(3) MCASE(4) MCASE(5) MCASE(6) MCASE(8) MCASE(9) MCASE(12) MCASE(16)
+#undef MCASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace e3

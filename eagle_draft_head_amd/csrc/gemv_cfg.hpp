@@ -1,0 +1,37 @@
+// Launch configurations of the GEMV family: (id, waves per block, rows per
+// wave, 16-byte chunk steps in flight per lane).  Rows per wave must be even
+// for the kernels whose epilogue pairs rows (fused QKV, gate/up).
+#pragma once
+
+#define E3_GEMV_CONFIGS(X) \
+  X(0, 4, 4, 2)            \
+  X(1, 8, 2, 4)            \
+  X(2, 8, 1, 8)            \
+  X(3, 4, 2, 4)            \
+  X(4, 8, 4, 2)            \
+  X(5, 4, 1, 8)            \
+  X(6, 8, 2, 8)            \
+  X(7, 16, 1, 8)           \
+  X(8, 4, 2, 8)            \
+  X(9, 16, 2, 4)
+
+namespace e3 {
+
+enum GemvKind { kGemvEncode = 0, kGemvQkv, kGemvO, kGemvGateUp, kGemvDown, kGemvLmHead, kGemvKinds };
+
+// tuned choice per kind (rows/K of the drafter shapes)
+inline int gemv_pick(int kind, int N, int K) {
+  (void)N;
+  (void)K;
+  switch (kind) {
+    case kGemvEncode: return 7;
+    case kGemvQkv: return 8;
+    case kGemvO: return 7;
+    case kGemvGateUp: return 1;
+    case kGemvDown: return 7;
+    case kGemvLmHead: return 1;
+    default: return 0;
+  }
+}
+
+}  // namespace e3

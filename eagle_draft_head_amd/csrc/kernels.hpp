@@ -1,0 +1,135 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per family).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace e3 {
+
+// ---- GEMV family (bf16 weights, fp32 activations and accumulate) ----
+// `cfg` selects a launch configuration from E3_GEMV_CONFIGS (gemv_cfg.hpp).
+
+// g[r] = fc[r,:] . [aux0; aux1; aux2]
+hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const float* a1,
+                         const float* a2, float* g_out, int cfg, hipStream_t s);
+
+// Fused: [finish the previous step's argmax] -> cat = [RMSNorm(E[tok]); RMSNorm(g)] ->
+// q|k|v = W_qkv . cat (rows of q and k repacked so rotary partners are adjacent) ->
+// NeoX rotation of q, k at `pos` -> q_out (fp32, natural order) and the K/V row `pos`
+// of the cache (bf16, head-major).
+struct QkvArgs {
+  const uint16_t* w_qkv;
+  int n, n_head, n_head_kv, head_dim, rope_dim;
+  const double* inv_freq;  // [rope_dim / 2]: theta^(-2i / rope_dim)
+  float eps;
+  const uint16_t* embed;
+  int vocab;               // rows of embed; token ids are clamped to [0, vocab)
+  const int32_t* tok;      // device: the token fed to this step (when prev_count == 0)
+  // when prev_count > 0 the token is the argmax of the previous step's lm_head
+  // candidates mapped through d2t; block 0 stores it to *prev_out_id and *tok_store
+  const float* prev_val;
+  const int32_t* prev_idx;
+  int prev_count;
+  const int32_t* d2t;
+  int dv;
+  int32_t* prev_out_id;
+  int32_t* tok_store;
+  const float* g;          // recurrent hidden
+  const float* w_in;       // input_layernorm
+  const float* w_hid;      // hidden_norm
+  int pos;
+  float* q_out;
+  void* k_cache;           // this sequence's [n_head_kv][cap][head_dim]
+  void* v_cache;
+  int cap;
+  int kv_f32;              // cache element: fp32 (1) or bf16 (0)
+};
+hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s);
+
+// y[r] = W[r,:] . x + resid[r]   (o_proj, down_proj)
+hipError_t launch_gemv_resid(const uint16_t* w, int N, int K, const float* x,
+                             const float* resid, float* y, int cfg, hipStream_t s);
+
+// act[i] = silu(gate_i . z) * (up_i . z), z = RMSNorm(x1, w_post); W_gu rows interleaved
+hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* x1,
+                         const float* w_post, float eps, float* act, int cfg, hipStream_t s);
+
+// logits = lm_head . RMSNorm(h, w_norm); each block stores its best (value, index)
+// (lowest index on ties).  logits_dbg may be NULL.
+struct LmHeadArgs {
+  const uint16_t* w_lm;
+  int dv, n;
+  const float* h;
+  const float* w_norm;
+  float eps;
+  float* logits_dbg;
+  float* part_val;      // [grid]
+  int32_t* part_idx;    // [grid]
+};
+int lmhead_grid(int dv, int cfg);
+hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s);
+// argmax over the candidates, target = i + d2t[i] -> *out_id (and *tok_store if set)
+hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, int count, const int32_t* d2t,
+                                  int dv, int32_t* out_id, int32_t* tok_store, hipStream_t s);
+
+// Multi-vector split-K GEMV for teacher-forced rows: P[z][m][r] (fp32) over K chunks z.
+// Input: three fp32 streams x0|x1|x2 of row length seg concatenated along K, or (x1 ==
+// NULL) one fp32 matrix x0 [rows, K].  rows <= 16; *splits_out receives the chunk count.
+int gemv_multi_width(int rows);
+int gemv_multi_splits(int rows, int N, int K);  // chunk count the launch will use
+hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, const float* x1,
+                             const float* x2, int seg, int rows, float* P, int* splits_out,
+                             hipStream_t s);
+
+// ---- attention over the draft KV (split over context, LSE combine) ----
+struct AttnArgs {
+  const float* q;          // [n_head * hd], roped
+  const void* k_cache;     // [n_head_kv][cap][hd], fp32 or bf16
+  const void* v_cache;
+  int kv_f32;
+  int cap, T;              // rows 0..T-1 attended
+  int n_head, n_head_kv, head_dim;
+  float* part_o;           // [n_head][S][hd]
+  float* part_ml;          // [n_head][S][2]
+  float* out;              // [n_head * hd]
+};
+int attn_max_splits(int cap, int head_dim, int n_head_kv);
+// Splits the context, then (when more than one split) runs the combine kernel.
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+// ---- teacher-forced append (prefill / rebuild) ----
+// A[t, 0:3n] = [aux0[t]; aux1[t]; aux2[t]] as bf16 (A_hi); with A_lo given, also the
+// bf16 remainder A_lo = bf16(a - A_hi), so A_hi + A_lo carries ~16 mantissa bits.
+hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
+                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s);
+// cat[t] = [RMSNorm(E[tok[t]], w_in); RMSNorm(sum_z F[z][t], w_hid)], F row stride n,
+// split stride f_split (elements); written as fp32 (cat32) or as bf16 (cat16, plus the
+// bf16 remainder in cat16_lo when given).
+hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int n,
+                         const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
+                         const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
+                         float* cat32, hipStream_t s);
+// rows t in [row0, row0 + T): kv = sum_z P[z][t] over [k(kvd) | v(kvd)] (k rows repacked,
+// row stride 2*kvd, split stride p_split); rotate k at position pos0 + (t - row0) and
+// store bf16 into that cache row.
+hipError_t launch_tf_store(const float* P, int splits, size_t p_split, int row0, int T,
+                           int n_head_kv, int head_dim, int rope_dim, const double* inv_freq,
+                           int pos0, void* k_cache, void* v_cache, int cap, int kv_f32,
+                           hipStream_t s);
+
+// C[z][M][N] (fp32) = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T on bf16 MFMA
+// (A_lo may be NULL: one product).  Row strides lda, ldb (elements); K split
+// evenly over `splits`.
+hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
+                            int ldb, float* C, int M, int N, int K, int splits, hipStream_t s);
+int gemm_pick_splits(int M, int N, int K);
+
+// ---- load-time and bookkeeping helpers ----
+// dst row dst_rows[i] = src row src_rows[i] (bf16 rows of row_len elements)
+hipError_t launch_gather_rows(uint16_t* dst, const uint16_t* src, const int32_t* dst_rows,
+                              const int32_t* src_rows, int count, int row_len, hipStream_t s);
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
+
+}  // namespace e3

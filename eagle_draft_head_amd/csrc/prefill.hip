@@ -1,0 +1,397 @@
+// Teacher-forced append of T rows (prefill and rebuild_after_verify):
+//   A = bf16[aux0 | aux1 | aux2]            (pack)
+//   F = A . W_fc^T                          (MFMA GEMM, fp32 out, optional split-K)
+//   cat = bf16[RMSNorm(E[tok]) | RMSNorm(F)]
+//   KV = cat . W_kv^T                       (MFMA GEMM over the k|v rows of W_qkv)
+//   rotate k, round to bf16, store rows into the draft KV.
+// Only K and V of teacher-forced rows are ever read again, so Q, attention,
+// the MLP and the head are not run for them.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace e3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
+                                                  const float* __restrict__ a1,
+                                                  const float* __restrict__ a2, int T, int n,
+                                                  uint16_t* __restrict__ A_hi,
+                                                  uint16_t* __restrict__ A_lo) {
+  const size_t total = (size_t)T * 3 * n;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = i / (3 * n);
+    const int c = int(i - t * 3 * n);
+    const int j = c / n, k = c - j * n;
+    const float* src = j == 0 ? a0 : (j == 1 ? a1 : a2);
+    const float v = src[t * n + k];
+    const uint16_t h = f32_to_bf16(v);
+    A_hi[i] = h;
+    if (A_lo) A_lo[i] = f32_to_bf16(v - bf16_to_f32(h));
+  }
+}
+
+hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
+                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s) {
+  const size_t total = (size_t)T * 3 * n;
+  int blocks = int((total + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_pack_aux, dim3(blocks), dim3(256), 0, s, a0, a1, a2, T, n, A_hi, A_lo);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// sum of `splits` partials, loads issued four at a time
+__device__ __forceinline__ float sum_splits(const float* __restrict__ p, int splits, size_t stride) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int z = 0;
+  for (; z + 3 < splits; z += 4) {
+    a0 += p[(size_t)z * stride];
+    a1 += p[(size_t)(z + 1) * stride];
+    a2 += p[(size_t)(z + 2) * stride];
+    a3 += p[(size_t)(z + 3) * stride];
+  }
+  for (; z < splits; ++z) a0 += p[(size_t)z * stride];
+  return (a0 + a1) + (a2 + a3);
+}
+
+__device__ __forceinline__ float4 sum_splits4(const float* __restrict__ p, int splits,
+                                              size_t stride) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+  int z = 0;
+  for (; z + 1 < splits; z += 2) {
+    const float4 u = *reinterpret_cast<const float4*>(p + (size_t)z * stride);
+    const float4 v = *reinterpret_cast<const float4*>(p + (size_t)(z + 1) * stride);
+    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+    b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+  }
+  if (z < splits) {
+    const float4 u = *reinterpret_cast<const float4*>(p + (size_t)z * stride);
+    a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+  }
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// One block per row: f = sum of the fc partials, the two RMSNorms, the concat.
+__global__ __launch_bounds__(512) void k_tf_cat(const float* __restrict__ F, int splits,
+                                                size_t f_split, int T, int n,
+                                                const uint16_t* __restrict__ embed, int vocab,
+                                                const int32_t* __restrict__ tok,
+                                                const float* __restrict__ w_in,
+                                                const float* __restrict__ w_hid, float eps,
+                                                uint16_t* __restrict__ cat16,
+                                                uint16_t* __restrict__ cat16_lo,
+                                                float* __restrict__ cat32) {
+  extern __shared__ float fs[];  // [n]
+  __shared__ float red[32];
+  const int t = blockIdx.x;
+  const int tk = min(max(tok[t], 0), vocab - 1);  // out-of-range ids are clamped
+  const uint2* e4 = reinterpret_cast<const uint2*>(embed + (size_t)tk * n);
+  float4* f4 = reinterpret_cast<float4*>(fs);
+  float se = 0.f, sf = 0.f;
+  const int n4 = n >> 2;
+#pragma unroll 2
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+    const float4 f = sum_splits4(F + (size_t)t * n + 4 * i, splits, f_split);
+    f4[i] = f;
+    sf = fmaf(f.x, f.x, fmaf(f.y, f.y, fmaf(f.z, f.z, fmaf(f.w, f.w, sf))));
+    const uint2 u = e4[i];
+    const float a0 = bf16_lo(u.x), a1 = bf16_hi(u.x), a2 = bf16_lo(u.y), a3 = bf16_hi(u.y);
+    se = fmaf(a0, a0, fmaf(a1, a1, fmaf(a2, a2, fmaf(a3, a3, se))));
+  }
+  block_sum2(se, sf, red);
+  const float ie = 1.0f / sqrtf(se / float(n) + eps);
+  const float iff = 1.0f / sqrtf(sf / float(n) + eps);
+  const float4* wi4 = reinterpret_cast<const float4*>(w_in);
+  const float4* wh4 = reinterpret_cast<const float4*>(w_hid);
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+    const uint2 u = e4[i];
+    const float4 wi = wi4[i], wh = wh4[i], f = f4[i];
+    const float4 ea = make_float4(wi.x * (bf16_lo(u.x) * ie), wi.y * (bf16_hi(u.x) * ie),
+                                  wi.z * (bf16_lo(u.y) * ie), wi.w * (bf16_hi(u.y) * ie));
+    const float4 fb = make_float4(wh.x * (f.x * iff), wh.y * (f.y * iff), wh.z * (f.z * iff),
+                                  wh.w * (f.w * iff));
+    if (cat16) {
+      uint16_t* row = cat16 + (size_t)t * 2 * n;
+      const uint16_t h[8] = {f32_to_bf16(ea.x), f32_to_bf16(ea.y), f32_to_bf16(ea.z),
+                             f32_to_bf16(ea.w), f32_to_bf16(fb.x), f32_to_bf16(fb.y),
+                             f32_to_bf16(fb.z), f32_to_bf16(fb.w)};
+      uint2 pa, pb;
+      pa.x = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+      pa.y = uint32_t(h[2]) | (uint32_t(h[3]) << 16);
+      pb.x = uint32_t(h[4]) | (uint32_t(h[5]) << 16);
+      pb.y = uint32_t(h[6]) | (uint32_t(h[7]) << 16);
+      reinterpret_cast<uint2*>(row)[i] = pa;
+      reinterpret_cast<uint2*>(row + n)[i] = pb;
+      if (cat16_lo) {
+        const float v[8] = {ea.x, ea.y, ea.z, ea.w, fb.x, fb.y, fb.z, fb.w};
+        uint16_t l[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) l[q] = f32_to_bf16(v[q] - bf16_to_f32(h[q]));
+        uint16_t* lrow = cat16_lo + (size_t)t * 2 * n;
+        pa.x = uint32_t(l[0]) | (uint32_t(l[1]) << 16);
+        pa.y = uint32_t(l[2]) | (uint32_t(l[3]) << 16);
+        pb.x = uint32_t(l[4]) | (uint32_t(l[5]) << 16);
+        pb.y = uint32_t(l[6]) | (uint32_t(l[7]) << 16);
+        reinterpret_cast<uint2*>(lrow)[i] = pa;
+        reinterpret_cast<uint2*>(lrow + n)[i] = pb;
+      }
+    } else {
+      float* row = cat32 + (size_t)t * 2 * n;
+      reinterpret_cast<float4*>(row)[i] = ea;
+      reinterpret_cast<float4*>(row + n)[i] = fb;
+    }
+  }
+}
+
+hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int n,
+                         const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
+                         const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
+                         float* cat32, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tf_cat, dim3(T), dim3(512), size_t(n) * sizeof(float), s, F, splits,
+                     f_split, T, n, embed, vocab, tok, w_in, w_hid, eps, cat16, cat16_lo, cat32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// One block per row; a thread handles one adjacent (repacked) pair of k or v.
+__global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, int splits,
+                                                  size_t p_split, int row0, int nkv, int hd,
+                                                  int rope_dim, const double* __restrict__ inv_freq,
+                                                  int pos0, void* __restrict__ k_cache,
+                                                  void* __restrict__ v_cache, int cap,
+                                                  int kv_f32) {
+  const int t = row0 + blockIdx.x;
+  const int kvd = nkv * hd;
+  const int pos = pos0 + blockIdx.x;
+  const float* row = P + (size_t)t * 2 * kvd;
+  for (int pr = threadIdx.x; pr < kvd; pr += blockDim.x) {  // pairs over 2*kvd values
+    const int r = 2 * pr;
+    float y0 = sum_splits(row + r, splits, p_split);
+    float y1 = sum_splits(row + r + 1, splits, p_split);
+    const bool is_k = r < kvd;
+    const int rr = is_k ? r : r - kvd;
+    const int head = rr / hd, li = rr - head * hd;
+    int d0 = li, d1 = li + 1;
+    if (is_k && li < rope_dim) {
+      const int i = li >> 1;
+      d0 = i;
+      d1 = i + (rope_dim >> 1);
+      const double twopi = 6.283185307179586476925286766559;
+      double ang = double(pos) * inv_freq[i];
+      ang -= floor(ang * (1.0 / twopi)) * twopi;
+      float c, sv;
+      sincosf(float(ang), &sv, &c);
+      const float t0 = y0 * c - y1 * sv, t1 = y1 * c + y0 * sv;
+      y0 = t0;
+      y1 = t1;
+    }
+    void* base = is_k ? k_cache : v_cache;
+    const size_t row = ((size_t)head * cap + pos) * hd;
+    kv_store(base, row + d0, y0, kv_f32);
+    kv_store(base, row + d1, y1, kv_f32);
+  }
+}
+
+hipError_t launch_tf_store(const float* P, int splits, size_t p_split, int row0, int T,
+                           int n_head_kv, int head_dim, int rope_dim, const double* inv_freq,
+                           int pos0, void* k_cache, void* v_cache, int cap, int kv_f32,
+                           hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tf_store, dim3(T), dim3(256), 0, s, P, splits, p_split, row0, n_head_kv,
+                     head_dim, rope_dim, inv_freq, pos0, k_cache, v_cache, cap, kv_f32);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ void k_gather_rows(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src,
+                              const int32_t* __restrict__ dst_rows,
+                              const int32_t* __restrict__ src_rows, int row_len) {
+  const uint16_t* s = src + (size_t)src_rows[blockIdx.x] * row_len;
+  uint16_t* d = dst + (size_t)dst_rows[blockIdx.x] * row_len;
+  for (int i = threadIdx.x; i < row_len; i += blockDim.x) d[i] = s[i];
+}
+
+hipError_t launch_gather_rows(uint16_t* dst, const uint16_t* src, const int32_t* dst_rows,
+                              const int32_t* src_rows, int count, int row_len, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_rows, dim3(count), dim3(256), 0, s, dst, src, dst_rows, src_rows,
+                     row_len);
+  return hipGetLastError();
+}
+
+__global__ void k_bf16_to_f32(const uint16_t* __restrict__ src, float* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = bf16_to_f32(src[i]);
+}
+
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bf16_to_f32, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+__global__ void k_fill_i32(int32_t* __restrict__ p, int32_t v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM: C[z] = (A_hi + A_lo)[:, kz] . B[:, kz]^T, bf16 in, fp32 out.
+// The weights B are exact in bf16; the activations may carry a bf16 remainder
+// A_lo, which costs a second MFMA per fragment and gives fp32-grade products.
+// 4 waves in a 2x2 arrangement, wave tile (BM/2) x (BN/2) made of 16x16 MFMA
+// tiles (v_mfma_f32_16x16x32_bf16).  Operand tiles are staged in LDS with rows
+// padded by 8 elements; the next K-tile is fetched into registers while the
+// current one is multiplied.
+template <int BM, int BN, int BK, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ A,
+                                              const uint16_t* __restrict__ A2, int lda,
+                                              const uint16_t* __restrict__ B, int ldb,
+                                              float* __restrict__ C, int M, int N, int kper) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int LDK = BK + 8;
+  constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
+  constexpr int NA = BM * CPR, NB = BN * CPR;  // 16-byte chunks per operand tile
+  constexpr int CA = (NA + 255) / 256, CB = (NB + 255) / 256;
+  constexpr int NSA = SPLIT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t As[NSA][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kb = blockIdx.z * kper;
+  float* Cz = C + (size_t)blockIdx.z * M * N;
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[NSA][CA], rb[CB];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NA % 256 != 0 && idx >= NA) break;
+      const size_t off = (size_t)min(m0 + row, M - 1) * lda + kt + col;
+      ra[0][c] = *reinterpret_cast<const uint4*>(A + off);
+      if (SPLIT) ra[NSA - 1][c] = *reinterpret_cast<const uint4*>(A2 + off);
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NB % 256 != 0 && idx >= NB) break;
+      const int gr = min(n0 + row, N - 1);
+      rb[c] = *reinterpret_cast<const uint4*>(B + (size_t)gr * ldb + kt + col);
+    }
+  };
+
+  gload(kb);
+  for (int kt = kb; kt < kb + kper; kt += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CA; ++c) {
+      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NA % 256 != 0 && idx >= NA) break;
+#pragma unroll
+      for (int h = 0; h < NSA; ++h) *reinterpret_cast<uint4*>(&As[h][row * LDK + col]) = ra[h][c];
+    }
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NB % 256 != 0 && idx >= NB) break;
+      *reinterpret_cast<uint4*>(&Bs[row * LDK + col]) = rb[c];
+    }
+    __syncthreads();
+    if (kt + BK < kb + kper) gload(kt + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 32) {
+      bf16x8 bfr[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(
+            &Bs[(wn * WN + j * 16 + (lane & 15)) * LDK + kk + (lane >> 4) * 8]);
+#pragma unroll
+      for (int h = 0; h < NSA; ++h) {
+        bf16x8 af[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(
+              &As[h][(wm * WM + i * 16 + (lane & 15)) * LDK + kk + (lane >> 4) * 8]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WN + j * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+        if (row < M && col < N) Cz[(size_t)row * N + col] = acc[i][j][v];
+      }
+    }
+}
+
+constexpr int kBK = 32;
+
+int gemm_pick_splits(int M, int N, int K) {
+  const int bm = M <= 32 ? 32 : 128, bn = 128;
+  const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int kt = K / kBK;
+  int want = (512 + tiles - 1) / tiles;
+  if (want > 32) want = 32;
+  int best = 1;
+  for (int sp = 1; sp <= want && sp <= kt; ++sp)
+    if (kt % sp == 0) best = sp;
+  return best;
+}
+
+hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
+                            int ldb, float* C, int M, int N, int K, int splits, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % (kBK * splits) != 0) return hipErrorInvalidValue;
+  const int kper = K / splits;
+  if (M <= 32) {
+    dim3 grid((N + 127) / 128, (M + 31) / 32, splits);
+    if (A_lo)
+      hipLaunchKernelGGL((k_gemm<32, 128, kBK, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
+                         ldb, C, M, N, kper);
+    else
+      hipLaunchKernelGGL((k_gemm<32, 128, kBK, false>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
+                         ldb, C, M, N, kper);
+  } else {
+    dim3 grid((N + 127) / 128, (M + 127) / 128, splits);
+    if (A_lo)
+      hipLaunchKernelGGL((k_gemm<128, 128, kBK, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
+                         ldb, C, M, N, kper);
+    else
+      hipLaunchKernelGGL((k_gemm<128, 128, kBK, false>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
+                         ldb, C, M, N, kper);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace e3

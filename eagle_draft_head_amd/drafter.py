@@ -1,0 +1,78 @@
+"""A small object wrapper over the C entry points (argument marshalling only).
+
+Device memory for inputs and outputs comes from torch tensors on the current
+GPU; every computation runs inside libeagle3.so.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+
+class Drafter:
+    def __init__(self, geom, weights: Dict[str, torch.Tensor], d2t, max_ctx: int,
+                 max_gamma: int = 16, max_seqs: int = 1, kv_dtype: int = B.KV_F32, stream=None):
+        if not torch.cuda.is_available():
+            raise RuntimeError("the eagle3 engine needs a GPU")
+        self.geom = geom
+        self.n = geom.n_embd
+        self.dv = geom.draft_vocab
+        self.max_gamma = max_gamma
+        self.kv_dtype = kv_dtype
+        self.cfg = B.make_config(geom, max_ctx, max_gamma, max_seqs, kv_dtype)
+        self._w = B.make_weights(weights, d2t)
+        self.ctx = B.eagle3_load(self.cfg, self._w, stream)
+
+    def close(self):
+        if self.ctx:
+            B.eagle3_free(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- entry points ---------------------------------------------------------
+    def prefill(self, seq: int, tok: torch.Tensor, aux: Sequence[torch.Tensor], stream=None):
+        T = int(tok.numel())
+        B.eagle3_prefill(self.ctx, seq, T, tok, aux[0], aux[1], aux[2], stream)
+
+    def draft_chain(self, seq_ids: Sequence[int], boundary_tok: torch.Tensor,
+                    aux: Sequence[torch.Tensor], gamma: int, out: Optional[torch.Tensor] = None,
+                    keep_spec: bool = False, debug: bool = False, stream=None):
+        n_seq = len(seq_ids)
+        dev = boundary_tok.device
+        if out is None:
+            out = torch.empty((n_seq, max(gamma, 1)), dtype=torch.int32, device=dev)
+        logits = hidden = None
+        if debug:
+            logits = torch.zeros((n_seq, max(gamma, 1), self.dv), dtype=torch.float32, device=dev)
+            hidden = torch.zeros((n_seq, gamma + 1, self.n), dtype=torch.float32, device=dev)
+        geff = B.eagle3_draft_chain(self.ctx, list(seq_ids), boundary_tok, aux[0], aux[1], aux[2],
+                                    gamma, out, B.KEEP_SPEC if keep_spec else 0, logits, hidden,
+                                    stream)
+        return out, geff, logits, hidden
+
+    def rebuild_after_verify(self, seq_ids: Sequence[int], n_accepted: Sequence[int],
+                             tok: torch.Tensor, aux: Sequence[torch.Tensor], stream=None):
+        B.eagle3_rebuild_after_verify(self.ctx, list(seq_ids), list(n_accepted), tok, aux[0],
+                                      aux[1], aux[2], stream)
+
+    def rewind(self, seq: int, new_len: int):
+        B.eagle3_rewind(self.ctx, seq, new_len)
+
+    def kv_len(self, seq: int):
+        return B.eagle3_kv_len(self.ctx, seq)
+
+    def kv_read(self, seq: int, row0: int, nrows: int):
+        g = self.geom
+        dt = torch.float32 if self.kv_dtype == B.KV_F32 else torch.bfloat16
+        k = torch.empty((nrows, g.n_head_kv, g.head_dim), dtype=dt, device="cuda")
+        v = torch.empty_like(k)
+        B.eagle3_kv_read(self.ctx, seq, row0, nrows, k, v)
+        return k, v

@@ -1,0 +1,197 @@
+/*
+ * eagle3.h — C ABI of the MI355X (gfx950) EAGLE-3 drafter engine.
+ *
+ * The engine runs the EAGLE-3 draft head: an encoder `fc` over three captured
+ * target hidden states, one Llama-style decoder layer with a persistent draft
+ * KV cache, a draft-vocabulary lm_head, greedy argmax and the d2t map to target
+ * ids.  Entry points follow the operations described in pegainfer PR #707
+ * ("feat(eagle3): Qwen3 EAGLE-3 drafter forward pass (single-step + chain
+ * rollout)", PR description: prefill, draft_chain / chain_round,
+ * rebuild_after_verify) and the op sequence in the module doc of the
+ * memra_engine 0.121.0 `eagle.rs` listing.
+ *
+ * Conventions (all entry points):
+ *   - return int status: EAGLE3_OK (0) or a negative EAGLE3_E_* code;
+ *     eagle3_last_error() gives a message for the last failing call;
+ *   - every argument check runs before any device work is queued, so a
+ *     failing call changes no state;
+ *   - "dev" pointers are HIP device pointers, "host" pointers host memory;
+ *     fp32 tap (aux) pointers must be 16-byte aligned (rows are read as vectors);
+ *     inputs are borrowed for the call in stream order, outputs are written
+ *     in stream order and are valid once the stream reaches the call;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream);
+ *   - one handle is used by one host thread at a time.
+ */
+#ifndef EAGLE3_H
+#define EAGLE3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  EAGLE3_OK = 0,
+  EAGLE3_E_INVAL = -1,       /* bad argument (null pointer, id or count out of range) */
+  EAGLE3_E_SHAPE = -2,       /* inconsistent tensor geometry */
+  EAGLE3_E_UNSUPPORTED = -3, /* geometry the kernels do not handle */
+  EAGLE3_E_CAPACITY = -4,    /* draft KV capacity exceeded */
+  EAGLE3_E_STATE = -5,       /* call not allowed in the sequence's current state */
+  EAGLE3_E_HIP = -6,         /* HIP runtime error */
+  EAGLE3_E_OOM = -7          /* device allocation failed */
+};
+
+/* eagle3_draft_chain flag: keep the speculative rows (spec > 0) instead of
+   rewinding at the end of the round; only eagle3_rewind clears them. */
+#define EAGLE3_KEEP_SPEC 1u
+
+typedef struct eagle3_ctx eagle3_ctx;
+
+/* Drafter geometry (memra `Eagle3Draft` fields) plus capacity. */
+typedef struct {
+  int32_t n_embd;        /* hidden size n */
+  int32_t n_head;        /* query heads */
+  int32_t n_head_kv;     /* key/value heads; n_head % n_head_kv == 0 */
+  int32_t head_dim;      /* 64, 128 or 256 */
+  int32_t n_ff;          /* MLP width */
+  int32_t draft_vocab;   /* rows of lm_head */
+  int32_t target_vocab;  /* rows of the token embedding */
+  int32_t n_aux;         /* captured taps; must be 3 */
+  int32_t rope_dim;      /* rotated dims per head (even, <= head_dim); see eagle3_resolve_rope_dim */
+  float rope_theta;
+  float rms_eps;
+  int32_t max_ctx;       /* admission bound per sequence; max_ctx + 1 rows are allocated */
+  int32_t max_gamma;     /* largest chain length accepted */
+  int32_t max_seqs;      /* sequence slots */
+  int32_t kv_dtype;      /* EAGLE3_KV_F32 (default) or EAGLE3_KV_BF16, see below */
+} eagle3_config;
+
+/* Draft-KV precision.  EAGLE3_KV_F32 stores K/V rows in fp32 and feeds the
+   teacher-forced MFMA products with activations split into two bf16 terms, so
+   committed rows carry fp32-grade values.  EAGLE3_KV_BF16 halves the KV bytes
+   (and rounds prefill activations to bf16); at the drafter sizes in the tests
+   that alone moves draft logits by about 1-2e-2 relative to exact arithmetic. */
+#define EAGLE3_KV_F32 0
+#define EAGLE3_KV_BF16 1
+
+/* Weights: device pointers, bf16, PyTorch [out, in] row-major (in contiguous).
+   They are copied (and repacked) at load; the caller may free them afterwards.
+     fc [n, 3n]; input_layernorm, hidden_norm, post_attention_layernorm, norm [n];
+     q_proj [n_head*hd, 2n]; k_proj, v_proj [n_head_kv*hd, 2n]; o_proj [n, n_head*hd];
+     gate_proj, up_proj [n_ff, n]; down_proj [n, n_ff]; lm_head [draft_vocab, n];
+     embed [target_vocab, n] — the token embedding indexed by TARGET id (required:
+     a head without an embedding table is rejected, ExecuTorch PR #20153).
+   d2t_host: host int64 [draft_vocab]; target_id = draft_id + d2t[draft_id]
+   (memra `d2t_map`); every target id must lie in [0, target_vocab). */
+typedef struct {
+  const void *fc, *input_layernorm, *hidden_norm, *q_proj, *k_proj, *v_proj, *o_proj,
+      *post_attention_layernorm, *gate_proj, *up_proj, *down_proj, *norm, *lm_head, *embed;
+  const int64_t *d2t_host;
+  int64_t d2t_len;
+  /* declared [rows, cols] of the 14 tensors above, in field order (norms: [n, 1]);
+     each must equal the shape the config implies, else EAGLE3_E_SHAPE */
+  int64_t shape[14][2];
+} eagle3_weights;
+
+/* Optional per-step outputs of a chain round (NULL fields are skipped):
+     logits: dev fp32 [n_seq, gamma, draft_vocab] — draft logits of step j;
+     hidden: dev fp32 [n_seq, gamma + 1, n_embd] — index 0 is the encoded
+             boundary feature fc(aux), index j the g_next of step j. */
+typedef struct {
+  float *logits;
+  float *hidden;
+} eagle3_debug;
+
+/* Rotary width (memra `EagleConfig::rope_dim_count` and its rope-width tests):
+   an explicit rotated-dims count (rotary_dim >= 0; pass -1 if absent) wins over
+   a fractional partial_factor (pass a negative value if absent), which wins over
+   the full head width; a malformed factor (not in (0, 1]) takes the full width.
+   An explicit count that is odd, zero or above head_dim, or a factor that does
+   not give an even whole number of dims, is EAGLE3_E_UNSUPPORTED.
+   Pure host function; needs no device. */
+int eagle3_resolve_rope_dim(int32_t rotary_dim, float partial_factor, int32_t head_dim,
+                            int32_t *out);
+
+/* Validate the geometry (memra `Eagle3Draft::load` shape checks: fc in = 3n,
+   q_proj in = 2n, q_proj out = n_head*hd, lm_head out = draft_vocab, d2t length =
+   draft_vocab) and the d2t range, copy and repack the weights into library-owned
+   device memory, and allocate the draft KV for max_seqs x (max_ctx + 1) rows.
+   The KV is zero-initialised; every sequence starts with 0 committed rows.
+   On error *out is left NULL and nothing is allocated. */
+int eagle3_load(const eagle3_config *cfg, const eagle3_weights *w, void *stream,
+                eagle3_ctx **out);
+
+/* Release a handle (synchronises its device work first). NULL is a no-op. */
+int eagle3_free(eagle3_ctx *ctx);
+
+/* Teacher-forced prefill (pegainfer PR #707 `prefill_prompt`): append T rows at
+   positions committed .. committed+T-1 of sequence `seq`.  Row t pairs the
+   taps of target position p_t (aux*_dev[t], fp32 [T, n] each, ascending tap
+   order) with tok_dev[t] (int32 [T]) = the target token at p_t + 1 (the shifted
+   pairing of ExecuTorch PR #20153).  Only K and V of the rows are computed.
+   Requires spec == 0 and committed + T <= max_ctx. T == 0 is a no-op. */
+int eagle3_prefill(eagle3_ctx *ctx, int32_t seq, int32_t T, const int32_t *tok_dev,
+                   const float *aux0_dev, const float *aux1_dev, const float *aux2_dev,
+                   void *stream);
+
+/* One chain round per listed sequence (pegainfer PR #707 `chain_round`):
+   g = fc(boundary taps), then gamma_eff greedy draft steps over the persistent
+   draft KV, then rewind (unless flags & EAGLE3_KEEP_SPEC).
+     seq_ids_host[n_seq]: distinct sequence slots;
+     boundary_tok_dev[n_seq] (int32): the token at the boundary position;
+     aux*_dev [n_seq, n] fp32: taps of the position before it;
+     out_ids_dev [n_seq, gamma] int32: target id of draft j+1, -1 beyond gamma_eff;
+     gamma_eff_host[n_seq]: filled before any device work is queued,
+       gamma_eff = clamp(max_ctx - committed, 0, gamma) (reserve for the k+1 commit);
+     dbg: optional per-step outputs, NULL in timed runs.
+   No logits leave the device; argmax and d2t run on the device. */
+int eagle3_draft_chain(eagle3_ctx *ctx, int32_t n_seq, const int32_t *seq_ids_host,
+                       const int32_t *boundary_tok_dev, const float *aux0_dev,
+                       const float *aux1_dev, const float *aux2_dev, int32_t gamma,
+                       uint32_t flags, int32_t *out_ids_dev, int32_t *gamma_eff_host,
+                       const eagle3_debug *dbg, void *stream);
+
+/* Commit accepted drafts after verification (pegainfer PR #707
+   `rebuild_after_verify`): for each listed sequence b, a_b = n_accepted_host[b]
+   and a_b + 1 rows are appended: (boundary taps, boundary token),
+   (taps before d_1, d_1) ... (taps before d_a, d_a).  Rows are packed over
+   sequences in list order: tok_dev [sum(a_b+1)] int32, aux*_dev [sum(a_b+1), n].
+   Requires spec == 0, a preceding chain round on the sequence since its last
+   commit, and a_b <= that round's gamma_eff. */
+int eagle3_rebuild_after_verify(eagle3_ctx *ctx, int32_t n_seq, const int32_t *seq_ids_host,
+                                const int32_t *n_accepted_host, const int32_t *tok_dev,
+                                const float *aux0_dev, const float *aux1_dev,
+                                const float *aux2_dev, void *stream);
+
+/* Drop speculative rows and truncate the committed rows to new_len
+   (abort / cleanup).  Requires 0 <= new_len <= committed.  Host bookkeeping
+   only: no device work. */
+int eagle3_rewind(eagle3_ctx *ctx, int32_t seq, int32_t new_len);
+
+/* Lengths of a sequence: committed rows and live speculative rows. */
+int eagle3_kv_len(const eagle3_ctx *ctx, int32_t seq, int32_t *committed, int32_t *spec);
+
+/* Copy draft-KV rows [row0, row0 + nrows) of a sequence into caller buffers
+   (dev [nrows, n_head_kv, head_dim] each in the cache's element type, fp32 or
+   bf16 per kv_dtype; K rows roped).  Inspection and tests; rows need not be live. */
+int eagle3_kv_read(const eagle3_ctx *ctx, int32_t seq, int32_t row0, int32_t nrows,
+                   void *k_dev, void *v_dev, void *stream);
+
+/* Message of the last failing call on this handle (or of the last failing
+   eagle3_load when ctx is NULL). */
+const char *eagle3_last_error(const eagle3_ctx *ctx);
+
+/* Timing of one kernel family with HIP events on the launching stream, for
+   measurement.  kernel: 0 = lm_head+argmax, 1 = gate/up+SwiGLU, 2 = fused QKV,
+   3 = down, 4 = o_proj, 5 = attention, 6 = fc encode, 7 = prefill fc GEMM,
+   8 = prefill K|V GEMM.  enable != 0 starts a fresh accumulation. */
+int eagle3_profile_enable(eagle3_ctx *ctx, int32_t kernel, int32_t enable);
+/* Synchronises the recorded events and returns the summed duration and count. */
+int eagle3_profile_read(eagle3_ctx *ctx, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLE3_H */

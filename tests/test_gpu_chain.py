@@ -1,0 +1,233 @@
+"""GPU parity of the drafter engine against the oracle through the C ABI:
+chain rounds (ids on pinned steps, logits, hidden), KV rows written by prefill
+and by the chain, rewind bit-identity, determinism, the 97/3/100 capacity edge,
+state errors, and the greedy speculative loop with a CPU trunk."""
+import numpy as np
+import pytest
+import torch
+
+from eagle_draft_head_amd import binding as B
+from oracle import TrunkOracle, greedy_plain, greedy_speculative
+from synth import TINY, gen, small_variant
+from tests.common import aux_np, make_oracle, row_slice, toks_np
+from tests.gpu_harness import (GpuChainAdapter, check_round, compare_round, gpu_drafter, say,
+                               to_dev_aux, weights_both)
+
+pytestmark = pytest.mark.gpu
+
+
+def _tok(x):
+    return torch.as_tensor(np.asarray(x), dtype=torch.int32).reshape(-1).cuda()
+
+
+def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None):
+    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds}")
+    wd, wh = weights_both(cfg)
+    max_ctx = max_ctx or (L + rounds * (gamma + 1) + gamma + 8)
+    dr = gpu_drafter(cfg, wd, max_ctx=max_ctx)
+    orc = make_oracle(cfg, wh, max_ctx=max_ctx)
+    aux = aux_np(cfg, 0, L)
+    toks = toks_np(cfg, 0, L)
+    orc.prefill(0, aux, toks)
+    dr.prefill(0, _tok(toks), to_dev_aux(aux))
+    baux = aux_np(cfg, 1, rounds)
+    btok = toks_np(cfg, 1, rounds)
+    raux = aux_np(cfg, 2, rounds * (gamma + 1))
+    steps = pinned = 0
+    worst_logit = worst_hidden = 0.0
+    for r in range(rounds):
+        b_aux = [a[r] for a in baux]
+        recs = orc.draft_chain(0, b_aux, btok[r], gamma)
+        out, geff, logits, hidden = dr.draft_chain([0], _tok([btok[r]]),
+                                                   [torch.as_tensor(a[r:r + 1], dtype=torch.float32).cuda()
+                                                    for a in baux], gamma, debug=True)
+        torch.cuda.synchronize()
+        # the encoded boundary feature
+        f_ref = orc.encode([a for a in b_aux])
+        f_gpu = hidden[0, 0].double().cpu().numpy()
+        assert np.linalg.norm(f_gpu - f_ref) / np.linalg.norm(f_ref) < 1e-5
+        cmp = compare_round(recs, out, geff[0], logits, hidden)
+        check_round(cmp, f"round {r}")
+        steps += len(cmp)
+        for c in cmp:
+            if not c.pinned:
+                break
+            pinned += 1
+            worst_logit = max(worst_logit, c.logit_err)
+            worst_hidden = max(worst_hidden, c.hidden_rel)
+        if geff[0] < gamma:
+            assert out[0, geff[0]:].eq(-1).all()
+        if rebuild_every and r % rebuild_every == rebuild_every - 1 and geff[0] > 0:
+            a = r % (geff[0] + 1)
+            rows = slice(r * (gamma + 1), r * (gamma + 1) + a)
+            new_aux = [np.concatenate([ba[r:r + 1], ra[rows]]) for ba, ra in zip(baux, raux)]
+            new_tok = np.array([btok[r]] + [x.target_id for x in recs[:a]], dtype=np.int32)
+            orc.rebuild_after_verify(0, a, new_aux, new_tok)
+            dr.rebuild_after_verify([0], [a], _tok(new_tok), to_dev_aux(new_aux))
+        assert dr.kv_len(0) == (orc.ledger.committed(0), 0)
+    say(f"[parity] {cfg.name}: {pinned}/{steps} steps pinned; worst logit {worst_logit:.2e}, "
+        f"hidden {worst_hidden:.2e}")
+    return pinned, steps
+
+
+def test_tiny_chain_parity_many_rounds():
+    pinned, steps = _run_rounds(TINY, rounds=200, L=63, gamma=3, rebuild_every=5)
+    assert pinned >= 0.25 * steps
+
+
+def test_ragged_shape_chain_parity():
+    # rows, K and context all leave ragged tails over the kernels' tiles
+    pinned, steps = _run_rounds(small_variant(), rounds=40, L=300, gamma=4, rebuild_every=3)
+    assert pinned >= 0.25 * steps
+
+
+def test_chain_from_empty_cache():
+    pinned, steps = _run_rounds(TINY, rounds=10, L=0, gamma=5)
+    assert steps == 50
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wd, wh = weights_both(TINY)
+    return wd, wh
+
+
+def test_prefill_kv_rows_match_oracle(tiny):
+    wd, wh = tiny
+    L = 63
+    dr = gpu_drafter(TINY, wd, max_ctx=200)
+    orc = make_oracle(TINY, wh, max_ctx=200)
+    aux, toks = aux_np(TINY, 0, L), toks_np(TINY, 0, L)
+    orc.prefill(0, aux, toks)
+    dr.prefill(0, _tok(toks), to_dev_aux(aux))
+    k, v = dr.kv_read(0, 0, L)
+    for gpu, ref in ((k, orc.K[0][:L]), (v, orc.V[0][:L])):
+        g = gpu.double().cpu().numpy()
+        rel = np.linalg.norm(g - ref, axis=(1, 2)) / np.linalg.norm(ref, axis=(1, 2))
+        assert rel.max() < 1e-2, rel.max()
+
+
+def test_chain_kv_row_matches_step_and_rewinds_bit_identical(tiny):
+    wd, wh = tiny
+    L, gamma = 40, 4
+    dr = gpu_drafter(TINY, wd, max_ctx=200)
+    orc = make_oracle(TINY, wh, max_ctx=200)
+    aux, toks = aux_np(TINY, 3, L + 1), toks_np(TINY, 3, L + 1)
+    orc.prefill(0, row_slice(aux, 0, L), toks[:L])
+    dr.prefill(0, _tok(toks[:L]), to_dev_aux(row_slice(aux, 0, L)))
+    k0, v0 = dr.kv_read(0, 0, L)
+    k0, v0 = k0.clone(), v0.clone()
+    b_aux = [torch.as_tensor(a[L:L + 1], dtype=torch.float32).cuda() for a in aux]
+    recs = orc.draft_chain(0, [a[L] for a in aux], toks[L], gamma)
+    out, geff, _, _ = dr.draft_chain([0], _tok([toks[L]]), b_aux, gamma, keep_spec=True)
+    assert dr.kv_len(0) == (L, gamma)
+    k1, v1 = dr.kv_read(0, L, gamma)
+    for j, r in enumerate(recs):
+        if r.margin <= 0.05 or any(x.margin <= 0.05 for x in recs[:j]):
+            break
+        for gpu, ref in ((k1[j], r.k), (v1[j], r.v)):
+            g = gpu.double().cpu().numpy()
+            assert np.linalg.norm(g - ref) / np.linalg.norm(ref) < 1e-2
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.draft_chain([0], _tok([toks[L]]), b_aux, gamma)
+    assert e.value.code == B.E_STATE
+    dr.rewind(0, L)
+    assert dr.kv_len(0) == (L, 0)
+    for _ in range(3):
+        dr.draft_chain([0], _tok([toks[L]]), b_aux, gamma)
+    k2, v2 = dr.kv_read(0, 0, L)
+    assert torch.equal(k2.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(v2.view(torch.int16), v0.view(torch.int16))
+
+
+def test_chain_is_deterministic(tiny):
+    wd, _ = tiny
+    dr = gpu_drafter(TINY, wd, max_ctx=200)
+    aux, toks = aux_np(TINY, 4, 31), toks_np(TINY, 4, 31)
+    dr.prefill(0, _tok(toks[:30]), to_dev_aux(row_slice(aux, 0, 30)))
+    b_aux = [torch.as_tensor(a[30:31], dtype=torch.float32).cuda() for a in aux]
+    o1, _, l1, h1 = dr.draft_chain([0], _tok([toks[30]]), b_aux, 6, debug=True)
+    o2, _, l2, h2 = dr.draft_chain([0], _tok([toks[30]]), b_aux, 6, debug=True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(h1, h2)
+
+
+def test_capacity_edge_97_3_100(tiny):
+    wd, wh = tiny
+    dr = gpu_drafter(TINY, wd, max_ctx=100, max_seqs=2)
+    aux, toks = aux_np(TINY, 5, 110), toks_np(TINY, 5, 110)
+    dr.prefill(0, _tok(toks[:97]), to_dev_aux(row_slice(aux, 0, 97)))
+    b_aux = [torch.as_tensor(a[97:98], dtype=torch.float32).cuda() for a in aux]
+    out, geff, _, _ = dr.draft_chain([0], _tok([toks[97]]), b_aux, 3)
+    assert geff == [3]
+    orc = make_oracle(TINY, wh, max_ctx=100)
+    orc.prefill(0, row_slice(aux, 0, 97), toks[:97])
+    drafts = [r.target_id for r in orc.draft_chain(0, [a[97] for a in aux], toks[97], 3)]
+    new_tok = np.array([toks[97]] + drafts, dtype=np.int32)     # full acceptance
+    dr.rebuild_after_verify([0], [3], _tok(new_tok), to_dev_aux(row_slice(aux, 97, 101)))
+    assert dr.kv_len(0) == (101, 0)
+    # row 100 (the reserve) now holds the fourth committed row; the oracle agrees
+    orc.rebuild_after_verify(0, 3, row_slice(aux, 97, 101), new_tok)
+    k, v = dr.kv_read(0, 97, 4)
+    rel = np.linalg.norm(k.double().cpu().numpy() - orc.K[0][97:101]) / np.linalg.norm(orc.K[0][97:101])
+    assert rel < 1e-2
+    # the next sequence's region (right after row 100) is untouched
+    k1, v1 = dr.kv_read(1, 0, 101)
+    assert not k1.view(torch.int16).any() and not v1.view(torch.int16).any()
+    out, geff, _, _ = dr.draft_chain([0], _tok([toks[101]]), b_aux, 3)
+    assert geff == [0] and out.eq(-1).all()
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.rebuild_after_verify([0], [0], _tok(toks[101:102]), to_dev_aux(row_slice(aux, 101, 102)))
+    assert e.value.code == B.E_CAPACITY
+    assert dr.kv_len(0) == (101, 0)
+
+
+def test_state_and_argument_errors(tiny):
+    wd, _ = tiny
+    dr = gpu_drafter(TINY, wd, max_ctx=50)
+    aux, toks = aux_np(TINY, 6, 60), toks_np(TINY, 6, 60)
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.prefill(0, _tok(toks[:51]), to_dev_aux(row_slice(aux, 0, 51)))
+    assert e.value.code == B.E_CAPACITY
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.rebuild_after_verify([0], [0], _tok(toks[:1]), to_dev_aux(row_slice(aux, 0, 1)))
+    assert e.value.code == B.E_STATE
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.draft_chain([1], _tok([1]), to_dev_aux(row_slice(aux, 0, 1)), 3)
+    assert e.value.code == B.E_INVAL
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.draft_chain([0], _tok([1]), to_dev_aux(row_slice(aux, 0, 1)), 17)
+    assert e.value.code == B.E_INVAL
+    out, geff, _, _ = dr.draft_chain([0], _tok([1]), to_dev_aux(row_slice(aux, 0, 1)), 2)
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.rebuild_after_verify([0], [3], _tok(toks[:4]), to_dev_aux(row_slice(aux, 0, 4)))
+    assert e.value.code == B.E_INVAL
+    assert dr.kv_len(0) == (0, 0)
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.rewind(0, 1)
+    assert e.value.code == B.E_INVAL
+
+
+@pytest.mark.parametrize("plen,gamma,max_new", [(1, 3, 16), (17, 3, 40), (64, 5, 40)])
+def test_greedy_loop_with_gpu_drafter(tiny, plen, gamma, max_new):
+    wd, wh = tiny
+    tw = gen.trunk_weights(TINY)
+    trunk = TrunkOracle(TINY, tw, wh["embed"], TINY.trunk_layers)
+    prompt = gen.tokens(TINY, 50 + plen, plen).tolist()
+    ref = greedy_plain(trunk, prompt, max_new)
+    dr = gpu_drafter(TINY, wd, max_ctx=plen + max_new + gamma + 8)
+    out, drafted, acc = greedy_speculative(trunk, GpuChainAdapter(dr), prompt, max_new, gamma)
+    assert out == ref
+
+
+@pytest.mark.parametrize("gamma", [1, 3, 5])
+def test_greedy_loop_full_acceptance_on_gpu(tiny, gamma):
+    from tests.test_oracle_loop import echo_weights
+    wd, wh = tiny
+    w_e, tw, image = echo_weights(wh, gen.trunk_weights(TINY))
+    trunk = TrunkOracle(TINY, tw, w_e["embed"], TINY.trunk_layers)
+    prompt = [int(image[7]), int(image[100]), int(image[33])]
+    ref = greedy_plain(trunk, prompt, 30)
+    dr = gpu_drafter(TINY, {k: v.cuda() for k, v in w_e.items()}, max_ctx=64)
+    out, drafted, acc = greedy_speculative(trunk, GpuChainAdapter(dr), prompt, 30, gamma)
+    assert out == ref
+    assert acc == drafted > 0
