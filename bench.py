@@ -28,6 +28,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CALIB_BYTES = 512 << 20
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "lm_head_qwen3-8b_hbm_traffic.md")
+
+
+def kernel_source_digest() -> str:
+    """Digest of the sources the measured kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemv.hip", "common.hpp", "gemv_cfg.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "eagle_draft_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing, is for another kernel, or the kernel source changed."""
+    try:
+        txt = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in txt.splitlines():
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k, v = kv.split("=")
+                vals[k] = v
+    if vals.get("kernel") != kernel or vals.get("source") != kernel_source_digest():
+        return None
+    return float(vals["bytes_per_launch"])
 
 
 def kernel_bytes(cfg, kernel: str, L: int) -> float:
@@ -72,6 +102,8 @@ def main():
     ap.add_argument("--kernel", default="lm_head")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=3)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
@@ -132,6 +164,13 @@ def main():
         dr.rebuild_after_verify([0], [a], r_tok[r0:r0 + a + 1], [x[r0:r0 + a + 1] for x in r_aux])
         dr.rewind(0, L)
 
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -181,7 +220,7 @@ def main():
                    "step": "draft_chain + rebuild_after_verify(a+1 rows, a cycling 0..3) + rewind"},
         "roofline": {"bound": "hbm", "kernel": args.kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(k_avg_s * 1e6, 3),
+                     "traffic": committed_traffic(args.kernel), "avg_launch_us": round(k_avg_s * 1e6, 3),
                      "launches": k_launches, "bytes_per_launch": k_bytes},
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
