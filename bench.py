@@ -99,6 +99,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b")
+    ap.add_argument("--gamma", type=int, default=0, help="override the workload's chain length")
     ap.add_argument("--kernel", default="lm_head")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=3)
@@ -118,7 +119,7 @@ def main():
     from synth import ALL, gen
 
     cfg = ALL[args.workload]
-    gamma = cfg.gamma
+    gamma = args.gamma or cfg.gamma
     L = cfg.context
     dev = "cuda"
     torch.cuda.set_device(0)
@@ -127,7 +128,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     max_ctx = L + 64
-    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=8)
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma))
     stream = torch.cuda.current_stream()
 
     # committed context

@@ -32,6 +32,9 @@ namespace {
 thread_local std::string g_load_error;
 
 constexpr int kProfKernels = 9;
+// gfx950 gives a workgroup up to 160 KB of LDS; the GEMVs keep one fp32
+// activation vector there (the down projection of a 5120-wide drafter: 68 KB)
+constexpr int64_t kMaxStageBytes = 128 * 1024;
 
 struct Profiler {
   int kernel = -1;
@@ -161,10 +164,10 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (cfg->max_gamma > 64) return bad("max_gamma above 64", EAGLE3_E_UNSUPPORTED);
   if (cfg->kv_dtype != EAGLE3_KV_F32 && cfg->kv_dtype != EAGLE3_KV_BF16)
     return bad("unknown kv_dtype", EAGLE3_E_INVAL);
-  {  // the GEMV kernels stage a whole fp32 activation vector in LDS (<= 64 KB)
+  {  // the GEMV kernels stage a whole fp32 activation vector in LDS
     const int64_t n = cfg->n_embd, kmax = std::max<int64_t>(
         {3 * n, 2 * n, int64_t(cfg->n_head) * cfg->head_dim, int64_t(cfg->n_ff)});
-    if (kmax * 4 > 65536) return bad("an activation vector exceeds 64 KB of LDS", EAGLE3_E_UNSUPPORTED);
+    if (kmax * 4 > kMaxStageBytes) return bad("an activation vector exceeds the LDS staging limit", EAGLE3_E_UNSUPPORTED);
   }
   return EAGLE3_OK;
 }

@@ -124,3 +124,24 @@ def test_qwen3_8b_shape_bf16_kv_option():
     k, v = dr.kv_read(0, 0, 4)
     assert k.dtype == torch.bfloat16
     dr.close()
+
+
+def test_long_context_parity():
+    """5120-wide drafter with a 32767-row prefill (2048-row passes) and chains
+    whose attention splits across the whole cache."""
+    from synth import LONG
+    cfg = LONG
+    dr, orc = _setup(cfg, cfg.context, cfg.max_ctx)
+    L = cfg.context
+    k, v = dr.kv_read(0, 0, L)
+    rows = [0, 1, 2047, 2048, 16383, 30000, L - 1]
+    for gpu, ref in ((k, orc.K[0]), (v, orc.V[0])):
+        g = gpu[rows].double().cpu().numpy()
+        r = ref[rows]
+        rel = np.linalg.norm((g - r).reshape(len(rows), -1), axis=1) / np.linalg.norm(r.reshape(len(rows), -1), axis=1)
+        assert rel.max() < 1e-2, rel
+    del k, v
+    pinned, steps = _rounds(cfg, dr, orc, [3, 3], [2, None])
+    say(f"[fullsize] {cfg.name}: {pinned}/{steps} steps pinned")
+    assert pinned >= 1
+    dr.close()
