@@ -62,8 +62,16 @@ struct eagle3_ctx {
   size_t kv_esize = 4;      // bytes per cache element
   size_t kv_seq_elems = 0;  // K + V elements per sequence
 
-  float *g1 = nullptr, *gA = nullptr, *gB = nullptr, *x1 = nullptr, *act = nullptr, *q = nullptr,
+  // recurrent hidden buffers: [0] the encoded boundary feature, [1]/[2] g_next of
+  // alternating steps; each with its hidden_norm- and norm-weighted copies and
+  // the per-block partial sums of its squares
+  struct GBuf {
+    float *y = nullptr, *w_hid = nullptr, *w_norm = nullptr, *ssq = nullptr;
+    int count = 0;
+  } gb[3];
+  float *x1 = nullptr, *x1w = nullptr, *x1_ssq = nullptr, *act = nullptr, *q = nullptr,
         *ao = nullptr, *part_o = nullptr, *part_ml = nullptr, *lm_pv = nullptr;
+  int x1_count = 0;
   int32_t *lm_pi = nullptr, *tok_slots = nullptr;
 
   int tf_rows = 0;
@@ -295,10 +303,8 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   c->kv_seq_elems = size_t(2) * kvd * size_t(c->cap);
   E3_TRY(dalloc(c, &c->kv, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize));
 
-  E3_TRY(dalloc(c, &c->g1, size_t(n)));
-  E3_TRY(dalloc(c, &c->gA, size_t(n)));
-  E3_TRY(dalloc(c, &c->gB, size_t(n)));
   E3_TRY(dalloc(c, &c->x1, size_t(n)));
+  E3_TRY(dalloc(c, &c->x1w, size_t(n)));
   E3_TRY(dalloc(c, &c->act, size_t(ff)));
   E3_TRY(dalloc(c, &c->q, size_t(qd)));
   E3_TRY(dalloc(c, &c->ao, size_t(qd)));
@@ -312,6 +318,16 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   c->gcfg[e3::kGemvDown] = e3::gemv_pick(e3::kGemvDown, int(n), int(ff));
   c->gcfg[e3::kGemvLmHead] = e3::gemv_pick(e3::kGemvLmHead, int(dv), int(n));
   c->lm_grid = e3::lmhead_grid(int(dv), c->gcfg[e3::kGemvLmHead]);
+  for (int i = 0; i < 3; ++i) {
+    eagle3_ctx::GBuf& b = c->gb[i];
+    b.count = e3::gemv_grid(int(n), c->gcfg[i == 0 ? e3::kGemvEncode : e3::kGemvDown]);
+    E3_TRY(dalloc(c, &b.y, size_t(n)));
+    E3_TRY(dalloc(c, &b.w_hid, size_t(n)));
+    E3_TRY(dalloc(c, &b.w_norm, size_t(n)));
+    E3_TRY(dalloc(c, &b.ssq, size_t(b.count)));
+  }
+  c->x1_count = e3::gemv_grid(int(n), c->gcfg[e3::kGemvO]);
+  E3_TRY(dalloc(c, &c->x1_ssq, size_t(c->x1_count)));
   E3_TRY(dalloc(c, &c->lm_pv, size_t(c->lm_grid)));
   E3_TRY(dalloc(c, &c->lm_pi, size_t(c->lm_grid)));
   E3_TRY(dalloc(c, &c->tok_slots, size_t(cfg->max_gamma) + 1));
@@ -613,18 +629,19 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
     if (ge < gamma) E3_HIP(ctx, e3::launch_fill_i32(out_b + ge, -1, gamma - ge, s), "fill");
     if (ge == 0) continue;
     {
+      e3::VecOut eo{ctx->gb[0].y, ctx->gb[0].w_hid, ctx->nrm_hid, nullptr, nullptr, ctx->gb[0].ssq};
       ProfScope ps(ctx, 6, s);
       E3_HIP(ctx, e3::launch_encode(ctx->w_fc, n, aux0_dev + size_t(b) * n, aux1_dev + size_t(b) * n,
-                                    aux2_dev + size_t(b) * n, ctx->g1,
-                                    ctx->gcfg[e3::kGemvEncode], s), "encode");
+                                    aux2_dev + size_t(b) * n, eo, ctx->gcfg[e3::kGemvEncode], s),
+             "encode");
     }
     if (dbg && dbg->hidden)
-      E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + size_t(b) * (gamma + 1) * n, ctx->g1, size_t(n) * 4,
-                                 hipMemcpyDeviceToDevice, s), "dbg hidden");
-    float* g = ctx->g1;
+      E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + size_t(b) * (gamma + 1) * n, ctx->gb[0].y,
+                                 size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
+    const eagle3_ctx::GBuf* g = &ctx->gb[0];
     for (int j = 0; j < ge; ++j) {
       const int pos = L + j;
-      float* gnext = (j & 1) ? ctx->gB : ctx->gA;
+      const eagle3_ctx::GBuf* gn = &ctx->gb[1 + (j & 1)];
       e3::QkvArgs qa{};
       qa.w_qkv = ctx->w_qkv; qa.n = n; qa.n_head = ctx->nh; qa.n_head_kv = ctx->nkv;
       qa.head_dim = ctx->hd; qa.rope_dim = ctx->rot; qa.inv_freq = ctx->inv_freq;
@@ -637,7 +654,8 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
         qa.d2t = ctx->d2t; qa.dv = ctx->dv;
         qa.prev_out_id = out_b + (j - 1); qa.tok_store = ctx->tok_slots + (j - 1);
       }
-      qa.g = g; qa.w_in = ctx->nrm_in; qa.w_hid = ctx->nrm_hid; qa.pos = pos; qa.q_out = ctx->q;
+      qa.gw = g->w_hid; qa.g_ssq = g->ssq; qa.g_ssq_count = g->count;
+      qa.w_in = ctx->nrm_in; qa.pos = pos; qa.q_out = ctx->q;
       qa.k_cache = ctx->k_of(sq); qa.v_cache = ctx->v_of(sq); qa.cap = ctx->cap;
       qa.kv_f32 = ctx->kv_f32;
       {
@@ -654,24 +672,26 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
         E3_HIP(ctx, e3::launch_attn(aa, s), "attention");
       }
       {
+        e3::VecOut oo{ctx->x1, ctx->x1w, ctx->nrm_post, nullptr, nullptr, ctx->x1_ssq};
         ProfScope ps(ctx, 4, s);
-        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_o, n, ctx->qd, ctx->ao, g, ctx->x1,
+        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_o, n, ctx->qd, ctx->ao, g->y, oo,
                                           ctx->gcfg[e3::kGemvO], s), "o_proj");
       }
       {
         ProfScope ps(ctx, 1, s);
-        E3_HIP(ctx, e3::launch_gateup(ctx->w_gu, ctx->ff, n, ctx->x1, ctx->nrm_post,
+        E3_HIP(ctx, e3::launch_gateup(ctx->w_gu, ctx->ff, n, ctx->x1w, ctx->x1_ssq, ctx->x1_count,
                                       ctx->cfg.rms_eps, ctx->act, ctx->gcfg[e3::kGemvGateUp], s),
                "gate/up");
       }
       {
+        e3::VecOut dn{gn->y, gn->w_norm, ctx->nrm_fin, gn->w_hid, ctx->nrm_hid, gn->ssq};
         ProfScope ps(ctx, 3, s);
-        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_d, n, ctx->ff, ctx->act, ctx->x1, gnext,
+        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_d, n, ctx->ff, ctx->act, ctx->x1, dn,
                                           ctx->gcfg[e3::kGemvDown], s), "down");
       }
       e3::LmHeadArgs la{};
-      la.w_lm = ctx->w_lm; la.dv = ctx->dv; la.n = n; la.h = gnext; la.w_norm = ctx->nrm_fin;
-      la.eps = ctx->cfg.rms_eps;
+      la.w_lm = ctx->w_lm; la.dv = ctx->dv; la.n = n; la.hw = gn->w_norm; la.h_ssq = gn->ssq;
+      la.h_ssq_count = gn->count; la.eps = ctx->cfg.rms_eps;
       la.logits_dbg = (dbg && dbg->logits) ? dbg->logits + (size_t(b) * gamma + j) * ctx->dv : nullptr;
       la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;
       {
@@ -679,9 +699,9 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
         E3_HIP(ctx, e3::launch_lmhead(la, ctx->gcfg[e3::kGemvLmHead], s), "lm_head");
       }
       if (dbg && dbg->hidden)
-        E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + (size_t(b) * (gamma + 1) + j + 1) * n, gnext,
+        E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + (size_t(b) * (gamma + 1) + j + 1) * n, gn->y,
                                    size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
-      g = gnext;
+      g = gn;
     }
     E3_HIP(ctx, e3::launch_argmax_finalize(ctx->lm_pv, ctx->lm_pi, ctx->lm_grid, ctx->d2t, ctx->dv,
                                            out_b + (ge - 1), ctx->tok_slots + (ge - 1), s),

@@ -1,15 +1,20 @@
 // GEMV family: y = W x with bf16 weights streamed from HBM in 16-byte
 // coalesced loads and fp32 activations staged in LDS, fp32 accumulate.
 //
-// Single-vector kernels (the draft step) fuse their neighbours:
-//   k_qkv     prologue: finish the previous step's argmax (+ d2t), gather the
-//             token's embedding row, RMSNorm both halves, concat; epilogue:
-//             NeoX rotation of q/k (rows repacked so partners are adjacent),
-//             q to fp32, k/v rows to the bf16 KV cache;
-//   k_gemv_resid   epilogue: + residual (o_proj, down);
-//   k_gateup  prologue: RMSNorm; epilogue: silu(gate) * up (rows interleaved);
-//   k_lmhead  prologue: RMSNorm; epilogue: per-block (max, argmax) candidate;
-//   k_encode  prologue: concat of the three tap streams.
+// RMSNorm is split between producer and consumer: a kernel whose output y
+// feeds a norm also writes y * w_norm (the consumer's weight) and one partial
+// sum of y^2 per block; the consumer stages the weighted vector as is, adds the
+// partial sums and applies 1/rms in its epilogue.  So no prologue loads norm
+// weights or reduces before streaming.
+//   k_encode      g = fc . [taps]            -> g, g*w_hid, partial sum g^2
+//   k_qkv         [finish the previous step's argmax + d2t] -> token; streams the
+//                 hidden half of W_qkv first while the token's embedding row is
+//                 in flight, then the embedding half; epilogue: 1/rms per half,
+//                 NeoX rotation (q/k rows repacked so partners are adjacent),
+//                 q to fp32, k/v rows to the KV cache
+//   k_gemv_resid  y = W x + resid            -> y, y*w1, y*w2, partial sum y^2
+//   k_gateup      silu(gate . z) * (up . z) with z = x1*w_post/rms (rows interleaved)
+//   k_lmhead      logits = lm_head . (h*w_norm/rms) -> per-block (max, argmax)
 // The multi-vector kernel (teacher-forced rows) applies each weight chunk to
 // M activation vectors and splits K so the M vectors fit in LDS; it writes
 // split partials that the next kernel sums.
@@ -25,20 +30,17 @@
 
 namespace e3 {
 
-// Stream the R rows a wave owns against the fp32 vector in LDS.  Chunks
-// (8 elements, 16 bytes) below `split` accumulate into lo, the rest into hi, so
-// a caller can scale two halves of the input differently afterwards.
-template <int R, int U, bool SPLIT>
+// Stream columns [k0, k0 + K) of the R rows a wave owns against xs[0, K).
+template <int R, int U>
 __device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t ldw, int row0,
-                                         int N, int K, int split, const float* __restrict__ xs,
-                                         float (&lo)[R], float (&hi)[R]) {
+                                         int N, int k0, int K, const float* __restrict__ xs,
+                                         float (&acc)[R]) {
   const int lane = threadIdx.x & 63;
   const uint4* wp[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * ldw);
-    lo[r] = 0.f;
-    hi[r] = 0.f;
+    wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * ldw + k0);
+    acc[r] = 0.f;
   }
   const int nch = K >> 3;
   const float4* x4 = reinterpret_cast<const float4*>(xs);
@@ -51,15 +53,9 @@ __device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t 
       for (int r = 0; r < R; ++r) w[u][r] = ld_stream(wp[r] + c + 64 * u);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int cc = c + 64 * u;
-      const float4 a = x4[2 * cc], b = x4[2 * cc + 1];
-      if (!SPLIT || cc < split) {
+      const float4 a = x4[2 * (c + 64 * u)], b = x4[2 * (c + 64 * u) + 1];
 #pragma unroll
-        for (int r = 0; r < R; ++r) lo[r] = dot8(w[u][r], a, b, lo[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) hi[r] = dot8(w[u][r], a, b, hi[r]);
-      }
+      for (int r = 0; r < R; ++r) acc[r] = dot8(w[u][r], a, b, acc[r]);
     }
   }
   for (; c < nch; c += 64) {
@@ -67,37 +63,48 @@ __device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t 
 #pragma unroll
     for (int r = 0; r < R; ++r) t[r] = ld_stream(wp[r] + c);
     const float4 a = x4[2 * c], b = x4[2 * c + 1];
-    if (!SPLIT || c < split) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) lo[r] = dot8(t[r], a, b, lo[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < R; ++r) hi[r] = dot8(t[r], a, b, hi[r]);
-    }
+    for (int r = 0; r < R; ++r) acc[r] = dot8(t[r], a, b, acc[r]);
   }
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    lo[r] = wave_sum(lo[r]);
-    if (SPLIT) hi[r] = wave_sum(hi[r]);
-  }
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
 }
 
-// xs[i] = v[i] * w[i] (the norm weight applied, not yet the 1/rms factor);
-// returns this thread's share of sum(v^2).  n % 4 == 0; 16-byte loads, four
-// per thread in flight.
-__device__ __forceinline__ float stage_weighted(float* xs, const float* __restrict__ v,
-                                                const float* __restrict__ w, int n) {
-  const float4* v4 = reinterpret_cast<const float4*>(v);
-  const float4* w4 = reinterpret_cast<const float4*>(w);
-  float4* x4 = reinterpret_cast<float4*>(xs);
+// sum of `count` per-block partial sums (this thread's share)
+__device__ __forceinline__ float sum_partials(const float* __restrict__ p, int count) {
+  float s = 0.f;
+  for (int i = threadIdx.x; i < count; i += blockDim.x) s += p[i];
+  return s;
+}
+
+// Emit the R rows of a wave: y, y*w1, y*w2 (when given) and this block's sum
+// of y^2 (when given).  Every thread of the block must call it.
+template <int R, int WAVES>
+__device__ __forceinline__ void emit_rows(const float (&y)[R], int row0, int N, const VecOut& o,
+                                          float* red) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float ss = 0.f;
-#pragma unroll 4
-  for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) {
-    const float4 a = v4[i], b = w4[i];
-    x4[i] = make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
-    ss = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, ss))));
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    if (row < N) {
+      if (lane == r) {
+        o.y[row] = y[r];
+        if (o.yw1) o.yw1[row] = y[r] * o.w1[row];
+        if (o.yw2) o.yw2[row] = y[r] * o.w2[row];
+      }
+      ss = fmaf(y[r], y[r], ss);
+    }
   }
-  return ss;
+  if (!o.ssq) return;
+  if (lane == 0) red[wv] = ss;  // every lane holds the same y[] after the reduction
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += red[w];
+    o.ssq[blockIdx.x] = t;
+  }
 }
 
 // xs[i] = e[i] * w[i] for a bf16 row e; returns the share of sum(e^2)
@@ -162,28 +169,30 @@ template <int WAVES, int R, int U>
 __global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restrict__ W, int n,
                                                        const float* __restrict__ a0,
                                                        const float* __restrict__ a1,
-                                                       const float* __restrict__ a2,
-                                                       float* __restrict__ out) {
+                                                       const float* __restrict__ a2, VecOut out) {
   extern __shared__ float xs[];
+  __shared__ float red[16];
   stage_plain(xs, a0, n);
   stage_plain(xs + n, a1, n);
   stage_plain(xs + 2 * n, a2, n);
   __syncthreads();
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  if (row0 >= n) return;
-  float acc[R], unused[R];
-  rows_dot<R, U, false>(W, size_t(3) * n, row0, n, 3 * n, 0, xs, acc, unused);
+  float acc[R];
+  if (row0 < n) rows_dot<R, U>(W, size_t(3) * n, row0, n, 0, 3 * n, xs, acc);
+  else
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (lane == r && row0 + r < n) out[row0 + r] = acc[r];
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  emit_rows<R, WAVES>(acc, row0, n, out, red);
 }
 
 // ---------------------------------------------------------------------------
+constexpr int kQkvERegs = 8;  // float4 chunks of the embedding row held per thread
+
 template <int WAVES, int R, int U>
 __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
-  extern __shared__ float xs[];
+  extern __shared__ float xs[];  // [0, n): embedding half; [n, 2n): hidden half
   __shared__ float red[32];
   __shared__ float sv[16];
   __shared__ int si[16];
@@ -193,8 +202,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   const int N = qd + 2 * kvd;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  // hidden half first: it does not depend on the token
-  float sg = stage_weighted(xs + n, a.g, a.w_hid, n);
+
+  // hidden half: already weighted by hidden_norm; its sum of squares from partials
+  stage_plain(xs + n, a.gw, n);
+  float sg = sum_partials(a.g_ssq, a.g_ssq_count);
   int tok;
   if (a.prev_count > 0) {
     // finish the previous step: argmax over the lm_head candidates, d2t
@@ -209,10 +220,43 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
     tok = *a.tok;
   }
   tok = min(max(tok, 0), a.vocab - 1);  // out-of-range ids are clamped
-  float se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
+  __syncthreads();  // hidden half staged
+  // the embedding row and input_layernorm go to registers; they land while the
+  // hidden half streams
+  const uint2* e4 = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);
+  const float4* w4 = reinterpret_cast<const float4*>(a.w_in);
+  const int n4 = n >> 2;
+  uint2 er[kQkvERegs];
+  float4 wr[kQkvERegs];
+  const bool in_regs = n4 <= kQkvERegs * int(blockDim.x);
+#pragma unroll
+  for (int j = 0; j < kQkvERegs; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (in_regs && i < n4) {
+      er[j] = e4[i];
+      wr[j] = w4[i];
+    }
+  }
+  float acc_g[R], acc_e[R];
+  if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
+  float se = 0.f;
+  float4* x4 = reinterpret_cast<float4*>(xs);
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kQkvERegs; ++j) {
+      const int i = threadIdx.x + j * blockDim.x;
+      if (i < n4) {
+        const float e0 = bf16_lo(er[j].x), e1 = bf16_hi(er[j].x), e2 = bf16_lo(er[j].y),
+                    e3 = bf16_hi(er[j].y);
+        x4[i] = make_float4(e0 * wr[j].x, e1 * wr[j].y, e2 * wr[j].z, e3 * wr[j].w);
+        se = fmaf(e0, e0, fmaf(e1, e1, fmaf(e2, e2, fmaf(e3, e3, se))));
+      }
+    }
+  } else {
+    se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
+  }
   __syncthreads();
-  float acc_e[R], acc_g[R];
-  if (row0 < N) rows_dot<R, U, true>(a.w_qkv, size_t(2) * n, row0, N, 2 * n, n >> 3, xs, acc_e, acc_g);
+  if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, 0, n, xs, acc_e);
   block_sum2(se, sg, red);  // every wave takes part
   if (row0 >= N) return;
   const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
@@ -258,25 +302,31 @@ template <int WAVES, int R, int U>
 __global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __restrict__ W, int N,
                                                            int K, const float* __restrict__ x,
                                                            const float* __restrict__ resid,
-                                                           float* __restrict__ y) {
+                                                           VecOut out) {
   extern __shared__ float xs[];
+  __shared__ float red[16];
   stage_plain(xs, x, K);
   __syncthreads();
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  if (row0 >= N) return;
-  float acc[R], unused[R];
-  rows_dot<R, U, false>(W, size_t(K), row0, N, K, 0, xs, acc, unused);
+  float acc[R];
+  if (row0 < N) {
+    rows_dot<R, U>(W, size_t(K), row0, N, 0, K, xs, acc);
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (lane == r && row0 + r < N) y[row0 + r] = acc[r] + resid[row0 + r];
+    for (int r = 0; r < R; ++r) acc[r] += resid[min(row0 + r, N - 1)];
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  }
+  emit_rows<R, WAVES>(acc, row0, N, out, red);
 }
 
 // ---------------------------------------------------------------------------
 template <int WAVES, int R, int U>
 __global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restrict__ W, int n_ff,
-                                                       int n, const float* __restrict__ x1,
-                                                       const float* __restrict__ w_post, float eps,
+                                                       int n, const float* __restrict__ xw,
+                                                       const float* __restrict__ x_ssq,
+                                                       int ssq_count, float eps,
                                                        float* __restrict__ act) {
   static_assert(R % 2 == 0, "gate/up pairs need an even row count per wave");
   extern __shared__ float xs[];
@@ -284,10 +334,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restric
   const int N = 2 * n_ff;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  float ss = stage_weighted(xs, x1, w_post, n), dummy = 0.f;
+  stage_plain(xs, xw, n);
+  float ss = sum_partials(x_ssq, ssq_count), dummy = 0.f;
   __syncthreads();
-  float acc[R], unused[R];
-  if (row0 < N) rows_dot<R, U, false>(W, size_t(n), row0, N, n, 0, xs, acc, unused);
+  float acc[R];
+  if (row0 < N) rows_dot<R, U>(W, size_t(n), row0, N, 0, n, xs, acc);
   block_sum2(ss, dummy, red);
   if (row0 >= N) return;
   const float inv = 1.0f / sqrtf(ss / float(n) + eps);
@@ -310,10 +361,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
   __shared__ int bi_s[16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  float ss = stage_weighted(xs, a.h, a.w_norm, a.n), dummy = 0.f;
+  stage_plain(xs, a.hw, a.n);
+  float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
   __syncthreads();
-  float acc[R], unused[R];
-  if (row0 < a.dv) rows_dot<R, U, false>(a.w_lm, size_t(a.n), row0, a.dv, a.n, 0, xs, acc, unused);
+  float acc[R];
+  if (row0 < a.dv) rows_dot<R, U>(a.w_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
   block_sum2(ss, dummy, red);
   const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
   float bv = -INFINITY;
@@ -449,12 +501,24 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
 
 static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+int gemv_grid(int N, int cfg) {
+  switch (cfg) {
+#define CASE(ID, WV, RR, UU) \
+  case ID:                   \
+    return ceil_div(N, WV * RR);
+    E3_GEMV_CONFIGS(CASE)
+#undef CASE
+    default:
+      return -1;
+  }
+}
+
 hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const float* a1,
-                         const float* a2, float* g_out, int cfg, hipStream_t s) {
+                         const float* a2, const VecOut& out, int cfg, hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                               \
   case ID:                                                                                 \
     hipLaunchKernelGGL((k_encode<WV, RR, UU>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
-                       size_t(3 * n) * sizeof(float), s, w_fc, n, a0, a1, a2, g_out);      \
+                       size_t(3 * n) * sizeof(float), s, w_fc, n, a0, a1, a2, out);        \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -475,42 +539,33 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
 }
 
 hipError_t launch_gemv_resid(const uint16_t* w, int N, int K, const float* x, const float* resid,
-                             float* y, int cfg, hipStream_t s) {
-#define CASE(ID, WV, RR, UU)                                                               \
-  case ID:                                                                                 \
-    hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU>), dim3(ceil_div(N, WV * RR)),            \
-                       dim3(64 * WV), size_t(K) * sizeof(float), s, w, N, K, x, resid, y); \
+                             const VecOut& out, int cfg, hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                                 \
+  case ID:                                                                                   \
+    hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU>), dim3(ceil_div(N, WV * RR)),              \
+                       dim3(64 * WV), size_t(K) * sizeof(float), s, w, N, K, x, resid, out); \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
   return hipGetLastError();
 }
 
-hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* x1,
-                         const float* w_post, float eps, float* act, int cfg, hipStream_t s) {
+hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* xw,
+                         const float* x_ssq, int ssq_count, float eps, float* act, int cfg,
+                         hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                                \
   case ID:                                                                                  \
     if (RR % 2) return hipErrorInvalidValue;                                                \
     hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(2 * n_ff, WV * RR)), \
-                       dim3(64 * WV), size_t(n) * sizeof(float), s, w_gu, n_ff, n, x1, w_post, \
-                       eps, act);                                                           \
+                       dim3(64 * WV), size_t(n) * sizeof(float), s, w_gu, n_ff, n, xw, x_ssq, \
+                       ssq_count, eps, act);                                                \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
   return hipGetLastError();
 }
 
-int lmhead_grid(int dv, int cfg) {
-  switch (cfg) {
-#define CASE(ID, WV, RR, UU) \
-  case ID:                   \
-    return ceil_div(dv, WV * RR);
-    E3_GEMV_CONFIGS(CASE)
-#undef CASE
-    default:
-      return -1;
-  }
-}
+int lmhead_grid(int dv, int cfg) { return gemv_grid(dv, cfg); }
 
 hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                                  \

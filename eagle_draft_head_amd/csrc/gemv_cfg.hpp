@@ -24,11 +24,11 @@ inline int gemv_pick(int kind, int N, int K) {
   (void)N;
   (void)K;
   switch (kind) {
-    case kGemvEncode: return 7;
+    case kGemvEncode: return 1;
     case kGemvQkv: return 8;
-    case kGemvO: return 7;
+    case kGemvO: return 1;
     case kGemvGateUp: return 1;
-    case kGemvDown: return 7;
+    case kGemvDown: return 1;
     case kGemvLmHead: return 1;
     default: return 0;
   }

@@ -10,11 +10,25 @@ namespace e3 {
 // ---- GEMV family (bf16 weights, fp32 activations and accumulate) ----
 // `cfg` selects a launch configuration from E3_GEMV_CONFIGS (gemv_cfg.hpp).
 
+// Output of a GEMV whose result y feeds an RMSNorm downstream: y itself, y
+// weighted by up to two norm weights, and one partial sum of y^2 per block.
+struct VecOut {
+  float* y;
+  float* yw1;          // y * w1 (or NULL)
+  const float* w1;
+  float* yw2;          // y * w2 (or NULL)
+  const float* w2;
+  float* ssq;          // [grid] (or NULL)
+};
+int gemv_grid(int N, int cfg);  // blocks (= partial sums) of a launch over N rows
+
 // g[r] = fc[r,:] . [aux0; aux1; aux2]
 hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const float* a1,
-                         const float* a2, float* g_out, int cfg, hipStream_t s);
+                         const float* a2, const VecOut& out, int cfg, hipStream_t s);
 
 // Fused: [finish the previous step's argmax] -> cat = [RMSNorm(E[tok]); RMSNorm(g)] ->
+// (the hidden half arrives pre-weighted as gw = g * hidden_norm with the partial
+// sums of g^2) ->
 // q|k|v = W_qkv . cat (rows of q and k repacked so rotary partners are adjacent) ->
 // NeoX rotation of q, k at `pos` -> q_out (fp32, natural order) and the K/V row `pos`
 // of the cache (bf16, head-major).
@@ -35,9 +49,10 @@ struct QkvArgs {
   int dv;
   int32_t* prev_out_id;
   int32_t* tok_store;
-  const float* g;          // recurrent hidden
+  const float* gw;         // recurrent hidden times hidden_norm
+  const float* g_ssq;      // per-block partial sums of g^2
+  int g_ssq_count;
   const float* w_in;       // input_layernorm
-  const float* w_hid;      // hidden_norm
   int pos;
   float* q_out;
   void* k_cache;           // this sequence's [n_head_kv][cap][head_dim]
@@ -49,19 +64,23 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s);
 
 // y[r] = W[r,:] . x + resid[r]   (o_proj, down_proj)
 hipError_t launch_gemv_resid(const uint16_t* w, int N, int K, const float* x,
-                             const float* resid, float* y, int cfg, hipStream_t s);
+                             const float* resid, const VecOut& out, int cfg, hipStream_t s);
 
-// act[i] = silu(gate_i . z) * (up_i . z), z = RMSNorm(x1, w_post); W_gu rows interleaved
-hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* x1,
-                         const float* w_post, float eps, float* act, int cfg, hipStream_t s);
+// act[i] = silu(gate_i . z) * (up_i . z), z = xw / rms with xw = x1 * w_post and the
+// rms from per-block partial sums of x1^2; W_gu rows interleaved
+hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* xw,
+                         const float* x_ssq, int ssq_count, float eps, float* act, int cfg,
+                         hipStream_t s);
 
-// logits = lm_head . RMSNorm(h, w_norm); each block stores its best (value, index)
-// (lowest index on ties).  logits_dbg may be NULL.
+// logits = lm_head . (hw / rms) with hw = h * w_norm and the rms from per-block
+// partial sums of h^2; each block stores its best (value, index) (lowest index on
+// ties).  logits_dbg may be NULL.
 struct LmHeadArgs {
   const uint16_t* w_lm;
   int dv, n;
-  const float* h;
-  const float* w_norm;
+  const float* hw;
+  const float* h_ssq;
+  int h_ssq_count;
   float eps;
   float* logits_dbg;
   float* part_val;      // [grid]
