@@ -337,8 +337,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   {  // small appends use split-K GEMV partials [splits][16][N]; large ones [splits][T][N]
     const size_t f_small = size_t(16) * n * size_t((3 * n + 511) / 512);
     const size_t p_small = size_t(16) * 2 * kvd * size_t((2 * n + 511) / 512);
-    c->tf_F_cap = std::max(size_t(c->tf_rows) * n * 2, f_small);
-    c->tf_P_cap = std::max(size_t(c->tf_rows) * 2 * kvd * 2, p_small);
+    // large appends: up to 8 K-split partials of the MFMA GEMMs
+    c->tf_F_cap = std::max(size_t(c->tf_rows) * n * 8, f_small);
+    c->tf_P_cap = std::max(size_t(c->tf_rows) * 2 * kvd * 8, p_small);
   }
   E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
   E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));

@@ -13,6 +13,7 @@ namespace e3 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
@@ -251,122 +252,170 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s) {
 // MFMA GEMM: C[z] = (A_hi + A_lo)[:, kz] . B[:, kz]^T, bf16 in, fp32 out.
 // The weights B are exact in bf16; the activations may carry a bf16 remainder
 // A_lo, which costs a second MFMA per fragment and gives fp32-grade products.
-// 4 waves in a 2x2 arrangement, wave tile (BM/2) x (BN/2) made of 16x16 MFMA
-// tiles (v_mfma_f32_16x16x32_bf16).  Operand tiles are staged in LDS with rows
-// padded by 8 elements; the next K-tile is fetched into registers while the
-// current one is multiplied.
-template <int BM, int BN, int BK, bool SPLIT>
-__global__ __launch_bounds__(256) void k_gemm(const uint16_t* __restrict__ A,
-                                              const uint16_t* __restrict__ A2, int lda,
-                                              const uint16_t* __restrict__ B, int ldb,
-                                              float* __restrict__ C, int M, int N, int kper) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 16, TN = WN / 16;
+//
+// v_mfma_f32_32x32x16_bf16 tiles: a wave owns a 64 x 64 block of C (2 x 2
+// MFMA tiles); waves tile the block (BM / 64) x (BN / 64).  Operand tiles of
+// BK = 32 are staged in LDS (rows padded by 8 elements), double buffered so
+// one barrier per K-tile suffices: the next tile's global loads are issued
+// before the current tile's MFMAs and written to the other buffer after them.
+// Block order: consecutive blocks are dispatched to different XCDs; the
+// mapping gives every block of one XCD the same weight (N) tile range, so a
+// weight tile is fetched into only one XCD's L2.
+template <int BM, int BN, bool SPLIT, int BK = 32>
+__global__ __launch_bounds__((BM / 64) * (BN / 64) * 64) void k_gemm(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, int lda,
+    const uint16_t* __restrict__ B, int ldb, float* __restrict__ C, int M, int N, int kper,
+    int mt, int nt) {
+  static_assert(BK % 16 == 0, "K tile is a whole number of MFMA steps");
+  constexpr int WMW = BM / 64, WNW = BN / 64;
+  constexpr int NT = WMW * WNW * 64;
   constexpr int LDK = BK + 8;
-  constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
-  constexpr int NA = BM * CPR, NB = BN * CPR;  // 16-byte chunks per operand tile
-  constexpr int CA = (NA + 255) / 256, CB = (NB + 255) / 256;
+  constexpr int CPR = BK / 8;
+  constexpr int NA = BM * CPR, NB = BN * CPR;
+  constexpr int CA = (NA + NT - 1) / NT, CB = (NB + NT - 1) / NT;
   constexpr int NSA = SPLIT ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t As[NSA][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NSA][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
 
+  // XCD-aware tile order
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int n_t = xcd + 8 * (slot / mt), m_t = slot % mt;
+  if (n_t >= nt) return;  // whole block idle (grid rounded up to the XCD pattern)
+  const int m0 = m_t * BM, n0 = n_t * BN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int wm = wv / WNW, wn = wv % WNW;
   const int kb = blockIdx.z * kper;
   float* Cz = C + (size_t)blockIdx.z * M * N;
 
-  f32x4 acc[TM][TN];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   uint4 ra[NSA][CA], rb[CB];
   auto gload = [&](int kt) {
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
-      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NA % 256 != 0 && idx >= NA) break;
+      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NA % NT != 0 && idx >= NA) break;
       const size_t off = (size_t)min(m0 + row, M - 1) * lda + kt + col;
       ra[0][c] = *reinterpret_cast<const uint4*>(A + off);
       if (SPLIT) ra[NSA - 1][c] = *reinterpret_cast<const uint4*>(A2 + off);
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NB % 256 != 0 && idx >= NB) break;
-      const int gr = min(n0 + row, N - 1);
-      rb[c] = *reinterpret_cast<const uint4*>(B + (size_t)gr * ldb + kt + col);
+      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NB % NT != 0 && idx >= NB) break;
+      rb[c] = *reinterpret_cast<const uint4*>(B + (size_t)min(n0 + row, N - 1) * ldb + kt + col);
     }
   };
-
-  gload(kb);
-  for (int kt = kb; kt < kb + kper; kt += BK) {
-    __syncthreads();
+  auto lstore = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CA; ++c) {
-      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NA % 256 != 0 && idx >= NA) break;
+      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NA % NT != 0 && idx >= NA) break;
 #pragma unroll
-      for (int h = 0; h < NSA; ++h) *reinterpret_cast<uint4*>(&As[h][row * LDK + col]) = ra[h][c];
+      for (int h = 0; h < NSA; ++h)
+        *reinterpret_cast<uint4*>(&As[buf][h][row * LDK + col]) = ra[h][c];
     }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-      const int idx = tid + 256 * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NB % 256 != 0 && idx >= NB) break;
-      *reinterpret_cast<uint4*>(&Bs[row * LDK + col]) = rb[c];
+      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
+      if (NB % NT != 0 && idx >= NB) break;
+      *reinterpret_cast<uint4*>(&Bs[buf][row * LDK + col]) = rb[c];
     }
-    __syncthreads();
-    if (kt + BK < kb + kper) gload(kt + BK);
+  };
+
+  const int ntiles = kper / BK;
+  gload(kb);
+  lstore(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(kb + (t + 1) * BK);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8 bfr[TN];
+    for (int kk = 0; kk < BK; kk += 16) {
+      const int kof = kk + (lane >> 5) * 8;
+      bf16x8 bfr[2];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < 2; ++j)
         bfr[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[(wn * WN + j * 16 + (lane & 15)) * LDK + kk + (lane >> 4) * 8]);
+            &Bs[buf][(wn * 64 + j * 32 + (lane & 31)) * LDK + kof]);
 #pragma unroll
       for (int h = 0; h < NSA; ++h) {
-        bf16x8 af[TM];
+        bf16x8 af[2];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < 2; ++i)
           af[i] = *reinterpret_cast<const bf16x8*>(
-              &As[h][(wm * WM + i * 16 + (lane & 15)) * LDK + kk + (lane >> 4) * 8]);
+              &As[buf][h][(wm * 64 + i * 32 + (lane & 31)) * LDK + kof]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
+    if (t + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
   }
 
+  // D layout of a 32x32 tile: lane l holds column l % 32 and rows
+  // 8 * (v / 4) + 4 * (l / 32) + (v % 4) for its 16 values v
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WN + j * 16 + (lane & 15);
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (col >= N) continue;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
-        if (row < M && col < N) Cz[(size_t)row * N + col] = acc[i][j][v];
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < M) Cz[(size_t)row * N + col] = acc[i][j][v];
       }
     }
 }
 
 constexpr int kBK = 32;
 
+// 256 x 256 tiles (16 waves, one block per CU) once there are 256 rows;
+// 128 x 128 below.  The K split is chosen so the blocks fill the 256 CUs.
+static void gemm_tiles(int M, int N, int* bm, int* bn) {
+  (void)N;
+  if (M >= 256) { *bm = 256; *bn = 256; }
+  else { *bm = 128; *bn = 128; }
+}
+
 int gemm_pick_splits(int M, int N, int K) {
-  const int bm = M <= 32 ? 32 : 128, bn = 128;
+  int bm, bn;
+  gemm_tiles(M, N, &bm, &bn);
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int kt = K / kBK;
-  int want = (512 + tiles - 1) / tiles;
-  if (want > 32) want = 32;
+  int want = (256 + tiles - 1) / tiles;
+  if (want > 8) want = 8;
   int best = 1;
   for (int sp = 1; sp <= want && sp <= kt; ++sp)
     if (kt % sp == 0) best = sp;
   return best;
+}
+
+template <int BM, int BN>
+static hipError_t launch_tiles(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
+                               const uint16_t* B, int ldb, float* C, int M, int N, int kper,
+                               int splits, hipStream_t s) {
+  const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
+  const int nt8 = (nt + 7) / 8 * 8;  // N tiles padded to the 8-XCD pattern
+  dim3 grid(mt * nt8, 1, splits), block((BM / 64) * (BN / 64) * 64);
+  if (A_lo)
+    hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, block, 0, s, A_hi, A_lo, lda, B, ldb, C, M, N,
+                       kper, mt, nt);
+  else
+    hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, block, 0, s, A_hi, A_lo, lda, B, ldb, C, M,
+                       N, kper, mt, nt);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
@@ -374,24 +423,10 @@ hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K % (kBK * splits) != 0) return hipErrorInvalidValue;
   const int kper = K / splits;
-  if (M <= 32) {
-    dim3 grid((N + 127) / 128, (M + 31) / 32, splits);
-    if (A_lo)
-      hipLaunchKernelGGL((k_gemm<32, 128, kBK, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
-                         ldb, C, M, N, kper);
-    else
-      hipLaunchKernelGGL((k_gemm<32, 128, kBK, false>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
-                         ldb, C, M, N, kper);
-  } else {
-    dim3 grid((N + 127) / 128, (M + 127) / 128, splits);
-    if (A_lo)
-      hipLaunchKernelGGL((k_gemm<128, 128, kBK, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
-                         ldb, C, M, N, kper);
-    else
-      hipLaunchKernelGGL((k_gemm<128, 128, kBK, false>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B,
-                         ldb, C, M, N, kper);
-  }
-  return hipGetLastError();
+  int bm, bn;
+  gemm_tiles(M, N, &bm, &bn);
+  if (bm == 256) return launch_tiles<256, 256>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  return launch_tiles<128, 128>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
 }
 
 }  // namespace e3
