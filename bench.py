@@ -100,12 +100,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3-8b")
     ap.add_argument("--gamma", type=int, default=0, help="override the workload's chain length")
-    ap.add_argument("--kernel", default="lm_head")
+    ap.add_argument("--kernel", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=3)
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
     args = ap.parse_args()
+    args.kernel_set = args.kernel is not None
+    if args.kernel is None:
+        args.kernel = "lm_head"
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "multi-GPU sharding is not part of this build"}))
@@ -119,6 +122,8 @@ def main():
     from synth import ALL, gen
 
     cfg = ALL[args.workload]
+    if cfg.max_seqs > 1:
+        return run_batched(args, cfg)
     gamma = args.gamma or cfg.gamma
     L = cfg.context
     dev = "cuda"
@@ -231,6 +236,156 @@ def main():
     }
     print(json.dumps(line), flush=True)
     dr.close()
+
+
+def batched_kernel_bytes(cfg, kernel: str, lens, gamma: int, steps_run: int) -> float:
+    """Algorithmic HBM bytes per launch of a batched-step kernel, averaged over the
+    steps of a round (`lens`: committed rows per sequence; fp32 K/V rows)."""
+    n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
+    m = len(lens)
+    if kernel == "attention":
+        rows = sum(L + j + 1 for L in lens for j in range(gamma)) / gamma
+        return 2.0 * 4 * kvd * rows + m * (4 * qd + 4 * qd)
+    act = {"lm_head": (dv, n), "gate_up": (2 * ff, n), "qkv": (qd + 2 * kvd, 2 * n),
+           "down": (n, ff), "o_proj": (n, qd)}[kernel]
+    return 2.0 * act[0] * act[1] + m * 4 * act[1]
+
+
+def run_batched(args, cfg):
+    """Batched drafting: one draft_chain over all sequences per step, then a packed
+    rebuild of a_b + 1 rows per sequence (a_b seeded on [0, gamma]) and a rewind of
+    every sequence to its seeded length."""
+    import numpy as np
+    import torch
+
+    from eagle_draft_head_amd import binding as B
+    from eagle_draft_head_amd.drafter import Drafter
+    from synth import gen
+
+    gamma = args.gamma or cfg.gamma
+    kernel = args.kernel if args.kernel != "lm_head" or args.kernel_set else "attention"
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    lens = gen.batch_lengths(cfg)
+    S = len(lens)
+    wd = gen.drafter_weights(cfg, device=dev)
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=cfg.max_ctx, max_gamma=max(8, gamma), max_seqs=S)
+    t0 = time.time()
+    for s, L in enumerate(lens):
+        aux = gen.aux_taps(cfg, 100 + s, L, device=dev)
+        tok = gen.tokens(cfg, 100 + s, L, device=dev)
+        dr.prefill(s, tok, aux)
+        del aux, tok
+    torch.cuda.synchronize()
+    print(f"[bench] prefill of {S} sequences ({sum(lens)} rows) in {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    nsteps = args.steps + args.warmup
+    b_aux = gen.aux_taps(cfg, 1, nsteps * S, device=dev)
+    b_tok = gen.tokens(cfg, 1, nsteps * S, device=dev)
+    r_aux = gen.aux_taps(cfg, 2, S * (gamma + 1), device=dev)
+    r_tok = gen.tokens(cfg, 2, S * (gamma + 1), device=dev)
+    acc_all = gen.uniform_int(cfg.cfg_id, 40_000, nsteps * S, gamma + 1).view(nsteps, S).tolist()
+    out = torch.empty((S, gamma), dtype=torch.int32, device=dev)
+    seqs = list(range(S))
+    drafted = []
+
+    def step(i):
+        geff = dr.draft_chain(seqs, b_tok[i * S:(i + 1) * S],
+                              [a[i * S:(i + 1) * S] for a in b_aux], gamma, out=out)[1]
+        acc = [min(acc_all[i][s], geff[s]) for s in seqs]
+        live = [s for s in seqs if geff[s] > 0]
+        rows = sum(acc[s] + 1 for s in live)
+        dr.rebuild_after_verify(live, [acc[s] for s in live], r_tok[:rows], [x[:rows] for x in r_aux])
+        for s in seqs:
+            dr.rewind(s, lens[s])
+        drafted.append(sum(geff))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    drafted.clear()
+    t_start = time.perf_counter()
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    tokens = sum(drafted)
+    B.eagle3_profile_enable(dr.ctx, kernel, True)
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    k_ms, k_launches = B.eagle3_profile_read(dr.ctx)
+    B.eagle3_profile_enable(dr.ctx, kernel, False)
+    k_avg_s = (k_ms / 1e3) / max(k_launches, 1)
+    k_bytes = batched_kernel_bytes(cfg, kernel, lens, gamma, gamma)
+    achieved = k_bytes / k_avg_s / 1e9
+
+    n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
+    p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
+    kv_bytes = sum(2.0 * 4 * kvd * (L + j + 1) for L in lens for j in range(gamma))
+    round_bytes = 6.0 * n * n + gamma * (2.0 * p_step) + kv_bytes
+    step_gbs = round_bytes / (elapsed / args.steps) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_batched(cfg, wd, lens, b_aux, b_tok, gamma)
+    line = {
+        "metric": f"draft tokens/sec (gamma={gamma} chain, batch {S}) and achieved HBM GB/s per draft step",
+        "value": round(tokens / elapsed, 2),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights, fp32 accumulate, fp32 draft KV",
+        "data": "synthetic (seeded; random-init weights of the drafter architecture)",
+        "config": {"workload": f"{cfg.name}: {S} sequences of the {cfg.n_embd}-wide drafter with "
+                               f"{min(lens)}..{max(lens)} committed rows (sum {sum(lens)})",
+                   "batch": S, "gamma": gamma,
+                   "step": "batched draft_chain + packed rebuild_after_verify + rewind to the seeded lengths"},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(k_avg_s * 1e6, 3),
+                     "launches": k_launches, "bytes_per_launch": k_bytes},
+        "round_hbm_gbs": round(step_gbs, 1),
+        "round_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    dr.close()
+
+
+def cpu_baseline_batched(cfg, wd, lens, b_aux, b_tok, gamma):
+    """The oracle on a sample of the batched workload: the chain rounds of the two
+    shortest sequences (their prefill is untimed setup)."""
+    import numpy as np
+    from synth import gen
+    from tests.common import make_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    wh = {k: v.cpu() for k, v in wd.items() if k != "embed"}
+    pick = sorted(range(len(lens)), key=lambda s: lens[s])[:2]
+    orc = make_oracle(cfg, wh, max_ctx=cfg.max_ctx, max_seqs=len(lens), lazy_embed=True)
+    S = len(lens)
+    drafted, spent = 0, 0.0
+    for s in pick:
+        aux = gen.aux_taps(cfg, 100 + s, lens[s])
+        tok = gen.tokens(cfg, 100 + s, lens[s])
+        orc.prefill(s, [a.double().numpy() for a in aux], tok.numpy())
+        t1 = time.perf_counter()
+        recs = orc.draft_chain(s, [a[s].double().cpu().numpy() for a in b_aux], int(b_tok[s]), gamma)
+        spent += time.perf_counter() - t1
+        drafted += len(recs)
+    return {"value": round(drafted / spent, 3), "unit": "draft tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle: one gamma={gamma} chain round of each of the sequences "
+                      f"{pick} (committed rows {[lens[s] for s in pick]}), sequentially; prefill untimed"}
 
 
 def cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, rounds):

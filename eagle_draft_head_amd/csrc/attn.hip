@@ -12,6 +12,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace e3 {
 
 constexpr int kAttnWaves = 4;
@@ -50,10 +52,25 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   const int s = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int slot = lane / LPR, sub = lane % LPR, d0 = sub * E;
-  const int r0 = s * chunk, r1 = min(a.T, r0 + chunk);
+  int T = a.T;
+  size_t kv_off = 0;
+  const float* qrow = a.q;
+  float* part_o = a.part_o;
+  float* part_ml = a.part_ml;
+  if (a.batched) {
+    const int rb = blockIdx.z;
+    T = a.br.pos0[rb] + a.step + 1;
+    kv_off = (size_t)a.br.slot[rb] * a.seq_elems;
+    qrow += (size_t)rb * a.n_head * HD;
+    part_o += (size_t)rb * a.n_head * S * HD;
+    part_ml += (size_t)rb * a.n_head * S * 2;
+  }
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  if (r0 >= T) return;  // a split past this row's context (batched rows are ragged)
+  const bool direct = S == 1 && !a.batched;
   const float scale = 1.0f / sqrtf(float(HD));
-  const KT* Kb = static_cast<const KT*>(a.k_cache) + (size_t)kvh * a.cap * HD + d0;
-  const KT* Vb = static_cast<const KT*>(a.v_cache) + (size_t)kvh * a.cap * HD + d0;
+  const KT* Kb = static_cast<const KT*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
+  const KT* Vb = static_cast<const KT*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
 
   int r = r0 + wv * RPW + slot;
   uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
@@ -65,7 +82,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < E; ++e) qv[g][e] = a.q[(size_t)(kvh * G + g) * HD + d0 + e];
+    for (int e = 0; e < E; ++e) qv[g][e] = qrow[(size_t)(kvh * G + g) * HD + d0 + e];
   float m[G], l[G], acc[G][E];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -151,18 +168,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
       L += s_L[w][g];
     }
     const int h = kvh * G + g;
-    if (S == 1) a.out[(size_t)h * HD + dd] = v / L;
-    else a.part_o[((size_t)h * S + s) * HD + dd] = v;
+    if (direct) a.out[(size_t)h * HD + dd] = v / L;
+    else part_o[((size_t)h * S + s) * HD + dd] = v;
   }
-  if (S == 1) return;
+  if (direct) return;
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float Mb = s_M[0][g], L = 0.f;
     for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
     for (int w = 0; w < kAttnWaves; ++w) L += s_L[w][g];
     const int h = kvh * G + g;
-    a.part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
-    a.part_ml[((size_t)h * S + s) * 2 + 1] = L;
+    part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
+    part_ml[((size_t)h * S + s) * 2 + 1] = L;
   }
 }
 
@@ -206,6 +223,54 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   }
 }
 
+// Batched combine: grid (n_head, rows); row r has ceil(T_r / chunk) splits of the
+// Smax-strided partials.  Output as bf16 (hi, lo) pairs [row][ld].
+__global__ __launch_bounds__(128) void k_attn_combine_b(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml, int Smax,
+                                                        int hd, int n_head, int chunk, int step,
+                                                        const BatchRows br,
+                                                        uint16_t* __restrict__ out_hi,
+                                                        uint16_t* __restrict__ out_lo, int ld) {
+  extern __shared__ float w[];  // [Smax]
+  __shared__ float red[32];
+  const int h = blockIdx.x, r = blockIdx.y;
+  const int T = br.pos0[r] + step + 1;
+  const int S = (T + chunk - 1) / chunk;
+  const float* ml = part_ml + ((size_t)r * n_head + h) * Smax * 2;
+  float M = -INFINITY;
+  for (int z = threadIdx.x; z < S; z += blockDim.x) M = fmaxf(M, ml[2 * z]);
+  M = wave_max(M);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if (lane == 0) red[wv] = M;
+  __syncthreads();
+  M = red[0];
+  for (int k = 1; k < nw; ++k) M = fmaxf(M, red[k]);
+  float L = 0.f, dummy = 0.f;
+  for (int z = threadIdx.x; z < S; z += blockDim.x) {
+    const float e = expf(ml[2 * z] - M);
+    w[z] = e;
+    L = fmaf(e, ml[2 * z + 1], L);
+  }
+  __syncthreads();
+  block_sum2(L, dummy, red);
+  const float invL = 1.0f / L;
+  const float* po = part_o + ((size_t)r * n_head + h) * Smax * hd;
+  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+    float acc0 = 0.f, acc1 = 0.f;
+    int z = 0;
+    for (; z + 1 < S; z += 2) {
+      acc0 = fmaf(w[z], po[(size_t)z * hd + d], acc0);
+      acc1 = fmaf(w[z + 1], po[(size_t)(z + 1) * hd + d], acc1);
+    }
+    if (z < S) acc0 = fmaf(w[z], po[(size_t)z * hd + d], acc0);
+    const float o = (acc0 + acc1) * invL;
+    const uint16_t hi = f32_to_bf16(o);
+    const size_t at = (size_t)r * ld + (size_t)h * hd + d;
+    out_hi[at] = hi;
+    out_lo[at] = f32_to_bf16(o - bf16_to_f32(hi));
+  }
+}
+
 static inline int rows_per_block(int hd, int kv_f32) {
   const int lpr = hd / (kv_f32 ? 4 : 8);
   return kAttnWaves * (64 / lpr);
@@ -232,8 +297,9 @@ int attn_max_splits(int cap, int head_dim, int n_head_kv) {
 }
 
 template <int HD, typename KT>
-static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStream_t s) {
-  dim3 grid(S, a.n_head_kv), block(64 * kAttnWaves);
+static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStream_t s,
+                            int rows = 1) {
+  dim3 grid(S, a.n_head_kv, rows), block(64 * kAttnWaves);
 #define E3_ATTN_CASE(GG)                                                        \
   case GG:                                                                    \
     hipLaunchKernelGGL((k_attn<HD, GG, KT>), grid, block, 0, s, a, chunk, S); \
@@ -252,23 +318,65 @@ static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStrea
   }
 #undef E3_ATTN_CASE
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
+  if (e != hipSuccess || S == 1 || a.batched) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(128), size_t(S) * sizeof(float), s,
                      a.part_o, a.part_ml, S, HD, a.out);
   return hipGetLastError();
 }
 
 template <typename KT>
-static hipError_t launch_kt(const AttnArgs& a, int G, int chunk, int S, hipStream_t s) {
+static hipError_t launch_kt(const AttnArgs& a, int G, int chunk, int S, hipStream_t s,
+                            int rows = 1) {
   switch (a.head_dim) {
-    case 64: return launch_hd<64, KT>(a, G, chunk, S, s);
-    case 128: return launch_hd<128, KT>(a, G, chunk, S, s);
-    case 256: return launch_hd<256, KT>(a, G, chunk, S, s);
+    case 64: return launch_hd<64, KT>(a, G, chunk, S, s, rows);
+    case 128: return launch_hd<128, KT>(a, G, chunk, S, s, rows);
+    case 256: return launch_hd<256, KT>(a, G, chunk, S, s, rows);
     default: return hipErrorInvalidValue;
   }
 }
 
+// Batched rows share one chunk size: about 2048 (row, head, split) blocks in
+// total, between kAttnBatchMinChunk and kAttnMaxChunk rows per split.
+constexpr int kAttnBatchMinChunk = 128;
+
+int attn_batch_chunk(const BatchRows& br, int m, int step, int n_head_kv, int head_dim, int kv_f32) {
+  long long rows = 0;
+  for (int r = 0; r < m; ++r) rows += br.pos0[r] + step + 1;
+  const int rpb = rows_per_block(head_dim, kv_f32);
+  long long c = (rows * n_head_kv + 2047) / 2048;
+  c = ((c + rpb - 1) / rpb) * rpb;
+  if (c < kAttnBatchMinChunk) c = kAttnBatchMinChunk;
+  if (c > kAttnMaxChunk) c = kAttnMaxChunk;
+  return int(c);
+}
+
+int attn_batch_max_splits(int cap, int head_dim, int kv_f32) {
+  (void)head_dim;
+  (void)kv_f32;
+  return (cap + kAttnBatchMinChunk - 1) / kAttnBatchMinChunk;
+}
+
+hipError_t launch_attn_batched(const AttnArgs& a, int m, uint16_t* out_hi, uint16_t* out_lo, int ld,
+                               hipStream_t s) {
+  if (!a.batched || m < 1 || m > kBatchRows) return hipErrorInvalidValue;
+  const int chunk = attn_batch_chunk(a.br, m, a.step, a.n_head_kv, a.head_dim, a.kv_f32);
+  int Tmax = 0;
+  for (int r = 0; r < m; ++r) Tmax = std::max(Tmax, a.br.pos0[r] + a.step + 1);
+  const int Smax = (Tmax + chunk - 1) / chunk;
+  if (Smax > attn_batch_max_splits(a.cap, a.head_dim, a.kv_f32) || Tmax > a.cap)
+    return hipErrorInvalidValue;
+  const int G = a.n_head / a.n_head_kv;
+  hipError_t e = a.kv_f32 ? launch_kt<float>(a, G, chunk, Smax, s, m)
+                          : launch_kt<uint16_t>(a, G, chunk, Smax, s, m);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_combine_b, dim3(a.n_head, m), dim3(128), size_t(Smax) * sizeof(float), s,
+                     a.part_o, a.part_ml, Smax, a.head_dim, a.n_head, chunk, a.step, a.br, out_hi,
+                     out_lo, ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
+  if (a.batched) return hipErrorInvalidValue;
   int chunk, S;
   pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   const int G = a.n_head / a.n_head_kv;

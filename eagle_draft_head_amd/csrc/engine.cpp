@@ -79,6 +79,16 @@ struct eagle3_ctx {
   uint16_t *tf_A = nullptr, *tf_A_lo = nullptr, *tf_cat16 = nullptr, *tf_cat16_lo = nullptr;
   float *tf_cat32 = nullptr, *tf_F = nullptr, *tf_P = nullptr;
 
+  // batched drafting scratch (max_seqs > 1): activation pairs A (fc input, cat,
+  // normed x1 / g_next) and B (attention output, SiLU product), split-K partials,
+  // per-row vectors, attention partials, lm_head candidates
+  int bld_a = 0, bld_b = 0;
+  uint16_t *bx_a_hi = nullptr, *bx_a_lo = nullptr, *bx_b_hi = nullptr, *bx_b_lo = nullptr;
+  float *b_P = nullptr, *b_G = nullptr, *b_X1 = nullptr, *b_q = nullptr, *b_po = nullptr,
+        *b_pml = nullptr, *b_cand_v = nullptr, *b_logits = nullptr;
+  int32_t* b_cand_i = nullptr;
+  e3::BGemmPlan bp_enc{}, bp_qkv{}, bp_o{}, bp_gu{}, bp_d{}, bp_lm{};
+
   e3::Ledger ledger;
   std::string err;
   Profiler prof;
@@ -351,6 +361,36 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->tf_F, c->tf_F_cap));
   E3_TRY(dalloc(c, &c->tf_P, c->tf_P_cap));
 
+  if (cfg->max_seqs > 1) {
+    using e3::kBatchRows;
+    c->bp_enc = e3::bgemm_plan(int(n), int(3 * n), e3::kBEpiPartial);
+    c->bp_qkv = e3::bgemm_plan(int(N_qkv), int(2 * n), e3::kBEpiPartial);
+    c->bp_o = e3::bgemm_plan(int(n), int(qd), e3::kBEpiPartial);
+    c->bp_gu = e3::bgemm_plan(int(2 * ff), int(n), e3::kBEpiSilu);
+    c->bp_d = e3::bgemm_plan(int(n), int(ff), e3::kBEpiPartial);
+    c->bp_lm = e3::bgemm_plan(int(dv), int(n), e3::kBEpiArgmax);
+    c->bld_a = int(3 * n);
+    c->bld_b = int(std::max(qd, ff));
+    size_t pmax = 0;
+    for (auto pr : {std::make_pair(c->bp_enc, n), std::make_pair(c->bp_qkv, int64_t(N_qkv)),
+                    std::make_pair(c->bp_o, n), std::make_pair(c->bp_d, n)})
+      pmax = std::max(pmax, size_t(pr.first.splits) * kBatchRows * size_t(pr.second));
+    const size_t bsp = size_t(e3::attn_batch_max_splits(c->cap, c->hd, c->kv_f32));
+    E3_TRY(dalloc(c, &c->bx_a_hi, size_t(kBatchRows) * c->bld_a));
+    E3_TRY(dalloc(c, &c->bx_a_lo, size_t(kBatchRows) * c->bld_a));
+    E3_TRY(dalloc(c, &c->bx_b_hi, size_t(kBatchRows) * c->bld_b));
+    E3_TRY(dalloc(c, &c->bx_b_lo, size_t(kBatchRows) * c->bld_b));
+    E3_TRY(dalloc(c, &c->b_P, pmax));
+    E3_TRY(dalloc(c, &c->b_G, size_t(kBatchRows) * n));
+    E3_TRY(dalloc(c, &c->b_X1, size_t(kBatchRows) * n));
+    E3_TRY(dalloc(c, &c->b_q, size_t(kBatchRows) * qd));
+    E3_TRY(dalloc(c, &c->b_po, size_t(kBatchRows) * nh * bsp * hd));
+    E3_TRY(dalloc(c, &c->b_pml, size_t(kBatchRows) * nh * bsp * 2));
+    E3_TRY(dalloc(c, &c->b_cand_v, size_t(kBatchRows) * c->bp_lm.blocks));
+    E3_TRY(dalloc(c, &c->b_cand_i, size_t(kBatchRows) * c->bp_lm.blocks));
+    E3_TRY(dalloc(c, &c->b_logits, size_t(kBatchRows) * dv));
+  }
+
   // zero state
   E3_TRYH(hipMemsetAsync(c->kv, 0, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize, s),
           "memset kv");
@@ -595,6 +635,136 @@ int eagle3_rebuild_after_verify(eagle3_ctx* ctx, int32_t n_seq, const int32_t* s
   return EAGLE3_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Batched rounds: passes of up to 32 sequences; inside a pass each GEMM streams its
+// weights once for all rows still drafting.
+int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
+                        const int32_t* btok, const float* a0, const float* a1, const float* a2,
+                        int32_t gamma, int32_t* out, const std::vector<int32_t>& geff,
+                        const eagle3_debug* dbg, hipStream_t s) {
+  using e3::kBatchRows;
+  const int n = c->n;
+  for (int g0 = 0; g0 < n_seq; g0 += kBatchRows) {
+    const int gn = std::min(kBatchRows, n_seq - g0);
+    std::vector<int> rows;
+    for (int b = g0; b < g0 + gn; ++b) {
+      const int ge = geff[size_t(b)];
+      if (ge < gamma)
+        E3_HIP(c, e3::launch_fill_i32(out + size_t(b) * gamma + ge, -1, gamma - ge, s), "fill");
+      if (ge > 0) rows.push_back(b);
+    }
+    if (rows.empty()) continue;
+    std::stable_sort(rows.begin(), rows.end(),
+                     [&](int x, int y) { return geff[size_t(x)] > geff[size_t(y)]; });
+    e3::BatchRows br{};
+    br.m = int(rows.size());
+    for (int r = 0; r < br.m; ++r) {
+      const int b = rows[size_t(r)];
+      br.orig[r] = b;
+      br.slot[r] = seq_ids[b];
+      br.pos0[r] = c->ledger.seq(seq_ids[b]).committed;
+      br.geff[r] = geff[size_t(b)];
+    }
+    auto gemm = [&](const uint16_t* W, int N, int K, const uint16_t* xh, const uint16_t* xl, int ldx,
+                    int m, const e3::BGemmPlan& p, int epi) {
+      e3::BGemmArgs ga{};
+      ga.W = W; ga.N = N; ga.K = K; ga.Xhi = xh; ga.Xlo = xl; ga.ldx = ldx; ga.m = m;
+      ga.P = c->b_P;
+      ga.act_hi = c->bx_b_hi; ga.act_lo = c->bx_b_lo; ga.ld_act = c->bld_b;
+      ga.cand_v = c->b_cand_v; ga.cand_i = c->b_cand_i; ga.ncand = c->bp_lm.blocks;
+      ga.logits = (dbg && dbg->logits) ? c->b_logits : nullptr;
+      return e3::launch_bgemm(ga, p, epi, s);
+    };
+    {
+      ProfScope ps(c, 6, s);
+      E3_HIP(c, e3::launch_bpack_aux(br, a0, a1, a2, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, s), "pack");
+      E3_HIP(c, gemm(c->w_fc, n, 3 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, br.m, c->bp_enc,
+                     e3::kBEpiPartial), "encode");
+    }
+    const int steps = br.geff[0];
+    for (int j = 0; j < steps; ++j) {
+      int m = 0;
+      while (m < br.m && br.geff[m] > j) ++m;
+      e3::BPrepArgs pa{};
+      pa.br = br; pa.m = m; pa.step = j; pa.gamma = gamma; pa.boundary_tok = btok;
+      pa.cand_v = c->b_cand_v; pa.cand_i = c->b_cand_i; pa.ncand = c->bp_lm.blocks;
+      pa.d2t = c->d2t; pa.dv = c->dv; pa.out_ids = out; pa.embed = c->embed; pa.vocab = c->vt;
+      pa.n = n; pa.w_in = c->nrm_in; pa.w_hid = c->nrm_hid; pa.eps = c->cfg.rms_eps;
+      pa.G = c->b_G; pa.Penc = c->b_P; pa.S_enc = c->bp_enc.splits;
+      pa.Xhi = c->bx_a_hi; pa.Xlo = c->bx_a_lo; pa.ldx = c->bld_a;
+      pa.dbg_hidden = dbg ? dbg->hidden : nullptr;
+      const int Nqkv = c->qd + 2 * c->kvd;
+      {
+        ProfScope ps(c, 2, s);
+        E3_HIP(c, e3::launch_bprep(pa, s), "prep");
+        E3_HIP(c, gemm(c->w_qkv, Nqkv, 2 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->bp_qkv,
+                       e3::kBEpiPartial), "qkv");
+        e3::BQkvArgs qa{};
+        qa.P = c->b_P; qa.S = c->bp_qkv.splits; qa.N = Nqkv; qa.br = br; qa.m = m; qa.step = j;
+        qa.n_head = c->nh; qa.n_head_kv = c->nkv; qa.head_dim = c->hd; qa.rope_dim = c->rot;
+        qa.inv_freq = c->inv_freq; qa.q = c->b_q; qa.kv = c->kv; qa.seq_elems = c->kv_seq_elems;
+        qa.kv_f32 = c->kv_f32; qa.cap = c->cap;
+        E3_HIP(c, e3::launch_bqkv(qa, s), "qkv rows");
+      }
+      {
+        e3::AttnArgs aa{};
+        aa.q = c->b_q; aa.k_cache = c->k_of(0); aa.v_cache = c->v_of(0); aa.kv_f32 = c->kv_f32;
+        aa.cap = c->cap; aa.n_head = c->nh; aa.n_head_kv = c->nkv; aa.head_dim = c->hd;
+        aa.part_o = c->b_po; aa.part_ml = c->b_pml; aa.batched = 1; aa.step = j;
+        aa.seq_elems = c->kv_seq_elems; aa.br = br;
+        ProfScope ps(c, 5, s);
+        E3_HIP(c, e3::launch_attn_batched(aa, m, c->bx_b_hi, c->bx_b_lo, c->bld_b, s), "attention");
+      }
+      {
+        ProfScope ps(c, 4, s);
+        E3_HIP(c, gemm(c->w_o, n, c->qd, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->bp_o,
+                       e3::kBEpiPartial), "o_proj");
+        e3::BResidArgs ra{};
+        ra.P = c->b_P; ra.S = c->bp_o.splits; ra.n = n; ra.m = m; ra.resid = c->b_G; ra.y = c->b_X1;
+        ra.w = c->nrm_post; ra.eps = c->cfg.rms_eps; ra.Xhi = c->bx_a_hi; ra.Xlo = c->bx_a_lo;
+        ra.ldx = c->bld_a; ra.br = br; ra.step = j; ra.gamma = gamma;
+        E3_HIP(c, e3::launch_bresid(ra, s), "o_proj rows");
+      }
+      {
+        ProfScope ps(c, 1, s);
+        E3_HIP(c, gemm(c->w_gu, 2 * c->ff, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->bp_gu,
+                       e3::kBEpiSilu), "gate/up");
+      }
+      {
+        ProfScope ps(c, 3, s);
+        E3_HIP(c, gemm(c->w_d, n, c->ff, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->bp_d,
+                       e3::kBEpiPartial), "down");
+        e3::BResidArgs ra{};
+        ra.P = c->b_P; ra.S = c->bp_d.splits; ra.n = n; ra.m = m; ra.resid = c->b_X1; ra.y = c->b_G;
+        ra.w = c->nrm_fin; ra.eps = c->cfg.rms_eps; ra.Xhi = c->bx_a_hi; ra.Xlo = c->bx_a_lo;
+        ra.ldx = c->bld_a; ra.br = br; ra.step = j; ra.gamma = gamma;
+        ra.dbg_hidden = dbg ? dbg->hidden : nullptr;
+        E3_HIP(c, e3::launch_bresid(ra, s), "down rows");
+      }
+      {
+        ProfScope ps(c, 0, s);
+        E3_HIP(c, gemm(c->w_lm, c->dv, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->bp_lm,
+                       e3::kBEpiArgmax), "lm_head");
+      }
+      if (dbg && dbg->logits)
+        for (int r = 0; r < m; ++r)
+          E3_HIP(c, hipMemcpyAsync(dbg->logits + (size_t(br.orig[r]) * gamma + j) * c->dv,
+                                   c->b_logits + size_t(r) * c->dv, size_t(c->dv) * 4,
+                                   hipMemcpyDeviceToDevice, s), "dbg logits");
+    }
+    E3_HIP(c, e3::launch_bfinal(br, br.m, gamma, c->b_cand_v, c->b_cand_i, c->bp_lm.blocks, c->d2t,
+                                c->dv, out, s), "argmax");
+  }
+  return EAGLE3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_host,
                        const int32_t* boundary_tok_dev, const float* aux0_dev,
                        const float* aux1_dev, const float* aux2_dev, int32_t gamma,
@@ -622,6 +792,14 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
 
   hipStream_t s = as_stream(stream);
   const int n = ctx->n;
+  if (n_seq > 1) {
+    const int rc = draft_chain_batched(ctx, n_seq, seq_ids_host, boundary_tok_dev, aux0_dev,
+                                       aux1_dev, aux2_dev, gamma, out_ids_dev, geff, dbg, s);
+    if (rc) return rc;
+    for (int b = 0; b < n_seq; ++b)
+      ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
+    return EAGLE3_OK;
+  }
   for (int b = 0; b < n_seq; ++b) {
     const int sq = seq_ids_host[b];
     const int L = ctx->ledger.seq(sq).committed;

@@ -133,36 +133,6 @@ __device__ __forceinline__ void stage_plain(float* xs, const float* __restrict__
   for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) x4[i] = v4[i];
 }
 
-// cos/sin of pos * inv_freq, the angle reduced modulo 2*pi in double first
-__device__ __forceinline__ void rope_cs(int pos, double inv_freq, float* c, float* s) {
-  const double twopi = 6.283185307179586476925286766559;
-  double a = double(pos) * inv_freq;
-  a -= floor(a * (1.0 / twopi)) * twopi;
-  sincosf(float(a), s, c);
-}
-
-// Argmax over `count` (value, index) candidates; every thread gets the result.
-__device__ __forceinline__ int block_argmax(const float* __restrict__ pv,
-                                            const int32_t* __restrict__ pi, int count,
-                                            float* sv, int* si) {
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  for (int b = threadIdx.x; b < count; b += blockDim.x) {
-    const float v = pv[b];
-    const int i = pi[b];
-    if (better(v, i, bv, bi)) { bv = v; bi = i; }
-  }
-  wave_argmax(bv, bi);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (lane == 0) { sv[w] = bv; si[w] = bi; }
-  __syncthreads();
-  bv = sv[0];
-  bi = si[0];
-  for (int k = 1; k < nw; ++k)
-    if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
-  __syncthreads();
-  return bi;
-}
 
 // ---------------------------------------------------------------------------
 template <int WAVES, int R, int U>

@@ -101,6 +101,18 @@ hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, c
                              const float* x2, int seg, int rows, float* P, int* splits_out,
                              hipStream_t s);
 
+// ---- batched drafting: up to kBatchRows sequences per pass ----
+constexpr int kBatchRows = 32;
+// The rows of one batched pass, ordered by admitted chain length (descending) so
+// that the rows still drafting at step j are the prefix [0, m_j).  Passed by value.
+struct BatchRows {
+  int m;                      // rows in the pass
+  int32_t orig[kBatchRows];   // row -> index in the caller's sequence list
+  int32_t pos0[kBatchRows];   // committed rows = position written by step 0
+  int32_t slot[kBatchRows];   // sequence id (draft-KV slot)
+  int32_t geff[kBatchRows];   // admitted chain length (>= 1)
+};
+
 // ---- attention over the draft KV (split over context, LSE combine) ----
 struct AttnArgs {
   const float* q;          // [n_head * hd], roped
@@ -112,10 +124,120 @@ struct AttnArgs {
   float* part_o;           // [n_head][S][hd]
   float* part_ml;          // [n_head][S][2]
   float* out;              // [n_head * hd]
+  // batched form (batched != 0): row r of blockIdx.z attends rows 0..pos0[r]+step of
+  // slot[r], whose K/V start seq_elems * slot elements past k_cache / v_cache; q and
+  // the partials are per row ([row][n_head][hd], [row][n_head][S][...])
+  int batched;
+  int step;
+  size_t seq_elems;
+  BatchRows br;
 };
 int attn_max_splits(int cap, int head_dim, int n_head_kv);
 // Splits the context, then (when more than one split) runs the combine kernel.
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// Batched: split every row's context in chunks of one size, then combine per (row,
+// head) into bf16 (hi, lo) pairs [row][ld] for the output projection.
+int attn_batch_chunk(const BatchRows& br, int m, int step, int n_head_kv, int head_dim, int kv_f32);
+int attn_batch_max_splits(int cap, int head_dim, int kv_f32);
+hipError_t launch_attn_batched(const AttnArgs& a, int m, uint16_t* out_hi, uint16_t* out_lo, int ld,
+                               hipStream_t s);
+
+// ---- batched GEMMs on MFMA: Y[b][r] = sum_k X[b][k] W[r][k], b < m <= 32 ----
+// X arrives as bf16 pairs (hi, lo = bf16(x - hi)) [32][ldx]; both are multiplied
+// (two MFMAs per weight fragment), so the product carries ~16 mantissa bits of x.
+enum BEpi { kBEpiPartial = 0, kBEpiSilu = 1, kBEpiArgmax = 2 };
+struct BGemmArgs {
+  const uint16_t* W;
+  int N, K;
+  const uint16_t* Xhi;
+  const uint16_t* Xlo;
+  int ldx, m;
+  int kb;                  // K per split (set by the plan)
+  float* P;                // kBEpiPartial: [splits][32][N]
+  uint16_t* act_hi;        // kBEpiSilu: rows interleaved (gate_i, up_i) -> silu(gate) * up
+  uint16_t* act_lo;        //   as a (hi, lo) pair [32][ld_act]
+  int ld_act;
+  float* cand_v;           // kBEpiArgmax: per (row b, block) best (value, index) [32][ncand]
+  int32_t* cand_i;
+  int ncand;
+  float* logits;           // kBEpiArgmax, optional: [32][N]
+};
+struct BGemmPlan {
+  int variant, splits, kb, blocks;
+};
+BGemmPlan bgemm_plan(int N, int K, int epi);
+hipError_t launch_bgemm(BGemmArgs a, const BGemmPlan& p, int epi, hipStream_t s);
+
+// X[r] = aux0|aux1|aux2 of caller row orig[r] (fp32 [n_seq][n] each) as (hi, lo)
+hipError_t launch_bpack_aux(const BatchRows& br, const float* a0, const float* a1, const float* a2,
+                            int n, uint16_t* Xhi, uint16_t* Xlo, int ldx, hipStream_t s);
+// Start of step `step` for rows [0, m): the token (boundary token at step 0, else the
+// argmax of the previous lm_head candidates through d2t, also stored to
+// out_ids[orig * gamma + step - 1]), g (at step 0 the sum of the encode partials,
+// stored to G), and X = [RMSNorm(E[tok], w_in); RMSNorm(g, w_hid)] as (hi, lo).
+struct BPrepArgs {
+  BatchRows br;
+  int m, step, gamma;
+  const int32_t* boundary_tok;
+  const float* cand_v;
+  const int32_t* cand_i;
+  int ncand;
+  const int32_t* d2t;
+  int dv;
+  int32_t* out_ids;
+  const uint16_t* embed;
+  int vocab, n;
+  const float* w_in;
+  const float* w_hid;
+  float eps;
+  float* G;                // [32][n]
+  const float* Penc;       // step 0: encode partials [S][32][n]
+  int S_enc;
+  uint16_t* Xhi;
+  uint16_t* Xlo;
+  int ldx;
+  float* dbg_hidden;       // optional [n_seq][gamma + 1][n]
+};
+hipError_t launch_bprep(const BPrepArgs& a, hipStream_t s);
+// q|k|v of rows [0, m) from the QKV partials: rotate q, k at pos0 + step; q -> [32][qd],
+// k, v -> row pos0 + step of each row's cache slot.
+struct BQkvArgs {
+  const float* P;
+  int S, N;
+  BatchRows br;
+  int m, step;
+  int n_head, n_head_kv, head_dim, rope_dim;
+  const double* inv_freq;
+  float* q;
+  void* kv;                // cache of slot 0; slot s starts s * seq_elems elements later
+  size_t seq_elems;
+  int kv_f32, cap;
+};
+hipError_t launch_bqkv(const BQkvArgs& a, hipStream_t s);
+// y = sum_z P[z] + resid (rows [0, m), width n) -> y; X = RMSNorm(y, w) as (hi, lo);
+// optionally y -> dbg_hidden[orig][step + 1].
+struct BResidArgs {
+  const float* P;
+  int S, n, m;
+  const float* resid;
+  float* y;
+  const float* w;
+  float eps;
+  uint16_t* Xhi;
+  uint16_t* Xlo;
+  int ldx;
+  BatchRows br;
+  int step, gamma;
+  float* dbg_hidden;
+};
+hipError_t launch_bresid(const BResidArgs& a, hipStream_t s);
+// act = silu(sum_z P[z][2i]) * sum_z P[z][2i+1] as (hi, lo) [32][ld]
+hipError_t launch_bact(const float* P, int S, int n_ff, int m, uint16_t* Xhi, uint16_t* Xlo, int ld,
+                       hipStream_t s);
+// rows [0, m): out_ids[orig * gamma + geff - 1] = d2t-mapped argmax of the candidates
+hipError_t launch_bfinal(const BatchRows& br, int m, int gamma, const float* cand_v,
+                         const int32_t* cand_i, int ncand, const int32_t* d2t, int dv,
+                         int32_t* out_ids, hipStream_t s);
 
 // ---- teacher-forced append (prefill / rebuild) ----
 // A[t, 0:3n] = [aux0[t]; aux1[t]; aux2[t]] as bf16 (A_hi); with A_lo given, also the

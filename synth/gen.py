@@ -26,7 +26,7 @@ This module holds no arithmetic of the drafter itself.
 from __future__ import annotations
 
 import math
-from typing import Dict, Iterable, Optional, Sequence
+from typing import List, Dict, Iterable, Optional, Sequence
 
 import torch
 
@@ -211,6 +211,15 @@ def tokens(cfg: DrafterConfig, stream: int, count: int, device="cpu") -> torch.T
 def lengths(cfg: DrafterConfig, stream: int, count: int, lo: int, hi: int) -> torch.Tensor:
     """int32 lengths uniform on [lo, hi] (inclusive)."""
     return uniform_int(cfg.cfg_id, 30_000 + stream, count, hi - lo + 1) + lo
+
+
+def batch_lengths(cfg: DrafterConfig) -> List[int]:
+    """Committed lengths of the batched workload: L_b uniform on [512, context] for
+    max_seqs sequences, sequences 0 and 1 at the full context (the capacity edge)."""
+    L = [int(x) for x in lengths(cfg, 0, cfg.max_seqs, 512, cfg.context)]
+    for b in range(min(2, len(L))):
+        L[b] = cfg.context
+    return L
 
 
 # ----------------------------------------------------------------------------
