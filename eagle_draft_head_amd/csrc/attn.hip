@@ -72,11 +72,21 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   const KT* Kb = static_cast<const KT*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
   const KT* Vb = static_cast<const KT*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
 
+  // each lane group keeps the K/V of kDepth rows in flight: slot i of the ring
+  // holds row r + i * RPB and is refilled with the row kDepth strides ahead
+  // once consumed (rows are still visited in order, r, r + RPB, ...)
+  constexpr int kDepth = 4;
   int r = r0 + wv * RPW + slot;
-  uint4 kw = make_uint4(0, 0, 0, 0), vw = kw;
-  if (r < r1) {  // first row's K/V in flight before q arrives
-    kw = *reinterpret_cast<const uint4*>(Kb + (size_t)r * HD);
-    vw = *reinterpret_cast<const uint4*>(Vb + (size_t)r * HD);
+  uint4 kw[kDepth], vw[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) {
+    kw[i] = make_uint4(0, 0, 0, 0);
+    vw[i] = kw[i];
+    const int rr = r + i * RPB;
+    if (rr < r1) {
+      kw[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)rr * HD);
+      vw[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)rr * HD);
+    }
   }
   float qv[G][E];
 #pragma unroll
@@ -91,36 +101,42 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
   }
-  for (; r < r1; r += RPB) {
-    float kf[E], vf[E];
-    KvVec<KT>::unpack(kw, kf);
-    KvVec<KT>::unpack(vw, vf);
-    if (r + RPB < r1) {  // next row's K/V
-      kw = *reinterpret_cast<const uint4*>(Kb + (size_t)(r + RPB) * HD);
-      vw = *reinterpret_cast<const uint4*>(Vb + (size_t)(r + RPB) * HD);
-    }
-    float d[G];
+  for (; r < r1; r += kDepth * RPB) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float t = 0.f;
+    for (int i = 0; i < kDepth; ++i) {
+      const int rr = r + i * RPB;
+      if (rr >= r1) break;
+      float kf[E], vf[E];
+      KvVec<KT>::unpack(kw[i], kf);
+      KvVec<KT>::unpack(vw[i], vf);
+      const int nr = rr + kDepth * RPB;
+      if (nr < r1) {
+        kw[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)nr * HD);
+        vw[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)nr * HD);
+      }
+      float d[G];
 #pragma unroll
-      for (int e = 0; e < E; ++e) t = fmaf(kf[e], qv[g][e], t);
-      d[g] = t;
-    }
+      for (int g = 0; g < G; ++g) {
+        float t = 0.f;
 #pragma unroll
-    for (int o = LPR / 2; o > 0; o >>= 1)
+        for (int e = 0; e < E; ++e) t = fmaf(kf[e], qv[g][e], t);
+        d[g] = t;
+      }
 #pragma unroll
-      for (int g = 0; g < G; ++g) d[g] += __shfl_xor(d[g], o, kWave);
+      for (int o = LPR / 2; o > 0; o >>= 1)
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sc = d[g] * scale;
-      const float mn = fmaxf(m[g], sc);
-      const float fo = expf(m[g] - mn);  // 0 on the first row (m = -inf)
-      const float p = expf(sc - mn);
-      l[g] = fmaf(l[g], fo, p);
+        for (int g = 0; g < G; ++g) d[g] += __shfl_xor(d[g], o, kWave);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], fo, p * vf[e]);
-      m[g] = mn;
+      for (int g = 0; g < G; ++g) {
+        const float sc = d[g] * scale;
+        const float mn = fmaxf(m[g], sc);
+        const float fo = expf(m[g] - mn);  // 0 on the first row (m = -inf)
+        const float p = expf(sc - mn);
+        l[g] = fmaf(l[g], fo, p);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], fo, p * vf[e]);
+        m[g] = mn;
+      }
     }
   }
 

@@ -25,8 +25,12 @@ constexpr int kBChunk = 512;           // k per LDS stage
 constexpr int kBLdk = kBChunk + 8;     // padded LDS row (elements)
 constexpr int kBVecPerChunk = 2 * kBatchRows * (kBChunk / 8);  // 16-byte vectors (hi and lo)
 
-__device__ __forceinline__ u32x4 ld_stream_v(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// Plain (cached) loads: a load instruction here touches 32 weight rows at 32
+// bytes each and the next three instructions finish those lines; with the
+// streaming hint the lines are not kept between them and the kernel fetches at
+// about half the rate (measured on MI355X: lm_head 2.6 vs 5.0 TB/s).
+__device__ __forceinline__ u32x4 ld_frag(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // hi = bf16(x), lo = bf16(x - hi)
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(64 * WM * WK) void k_bgemm(const BGemmArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int k = c0 + g * KW + s * 64 + half * 32 + q * 8;
         w[s][q] = (u32x4){0u, 0u, 0u, 0u};
-        if (k < k_end) w[s][q] = ld_stream_v(wp + k);
+        if (k < k_end) w[s][q] = ld_frag(wp + k);
       }
     __syncthreads();  // the previous chunk's fragments have been read
 #pragma unroll
@@ -184,14 +188,14 @@ __global__ __launch_bounds__(64 * WM * WK) void k_bgemm(const BGemmArgs a) {
 }
 
 // launch shapes: (row tiles, waves per tile)
-#define E3_BGEMM_VARIANTS(X) X(0, 4, 2) X(1, 2, 4) X(2, 1, 8)
+#define E3_BGEMM_VARIANTS(X) X(1, 2, 4) X(2, 1, 8)
 constexpr int kBVariantRows[] = {128, 64, 32};
 
 BGemmPlan bgemm_plan(int N, int K, int epi) {
   // a fused epilogue needs the whole K in one block
   BGemmPlan p{};
   const int chunks = (K + kBChunk - 1) / kBChunk;
-  const int target = 512;  // blocks: two per CU
+  const int target = 768;  // blocks of the split-K form (three per CU)
   if (epi != kBEpiPartial) {
     p.variant = 1;
     const int rows = kBVariantRows[p.variant];
@@ -199,8 +203,8 @@ BGemmPlan bgemm_plan(int N, int K, int epi) {
     p.splits = 1;
     p.kb = chunks * kBChunk;
   } else {
-    p.variant = 0;
-    const int rb = (N + kBVariantRows[0] - 1) / kBVariantRows[0];
+    p.variant = 1;
+    const int rb = (N + kBVariantRows[1] - 1) / kBVariantRows[1];
     int sp = (target + rb - 1) / rb;
     if (sp > chunks) sp = chunks;
     if (sp < 1) sp = 1;
@@ -234,37 +238,65 @@ hipError_t launch_bgemm(BGemmArgs a, const BGemmPlan& p, int epi, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
+// grid (rows, ceil(3n / 1024)): 4 consecutive values per thread
 __global__ __launch_bounds__(256) void k_bpack_aux(const BatchRows br, const float* __restrict__ a0,
                                                    const float* __restrict__ a1,
                                                    const float* __restrict__ a2, int n,
                                                    uint16_t* __restrict__ Xhi,
                                                    uint16_t* __restrict__ Xlo, int ldx) {
   const int r = blockIdx.x;
-  const size_t src = (size_t)br.orig[r] * n;
-  for (int k = threadIdx.x * 4; k < 3 * n; k += blockDim.x * 4) {
-    const int seg = k / n, kk = k - seg * n;
-    const float* a = seg == 0 ? a0 : (seg == 1 ? a1 : a2);
-    const float4 v = *reinterpret_cast<const float4*>(a + src + kk);
-    const float x[4] = {v.x, v.y, v.z, v.w};
+  const int k = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
+  if (k >= 3 * n) return;
+  const int seg = k / n, kk = k - seg * n;
+  const float* a = seg == 0 ? a0 : (seg == 1 ? a1 : a2);
+  const float4 v = *reinterpret_cast<const float4*>(a + (size_t)br.orig[r] * n + kk);
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  uint16_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) split_bf16(x[e], &Xhi[(size_t)r * ldx + k + e], &Xlo[(size_t)r * ldx + k + e]);
-  }
+  for (int e = 0; e < 4; ++e) split_bf16(x[e], &h[e], &l[e]);
+  *reinterpret_cast<uint2*>(Xhi + (size_t)r * ldx + k) =
+      make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16));
+  *reinterpret_cast<uint2*>(Xlo + (size_t)r * ldx + k) =
+      make_uint2(uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16));
 }
 
 hipError_t launch_bpack_aux(const BatchRows& br, const float* a0, const float* a1, const float* a2,
                             int n, uint16_t* Xhi, uint16_t* Xlo, int ldx, hipStream_t s) {
   if (n & 3) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bpack_aux, dim3(br.m), dim3(256), 0, s, br, a0, a1, a2, n, Xhi, Xlo, ldx);
+  hipLaunchKernelGGL(k_bpack_aux, dim3(br.m, (3 * n + 1023) / 1024), dim3(256), 0, s, br, a0, a1, a2,
+                     n, Xhi, Xlo, ldx);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bprep(const BPrepArgs a) {
-  __shared__ float red[16];
-  __shared__ float sv[4];
-  __shared__ int si[4];
+// One block per row; thread i holds the float4 groups i and i + kBRowThreads of it.
+constexpr int kBRowVec = kBRowMax / 4 / kBRowThreads;
+
+__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, float4 v) {
+  const float x[4] = {v.x, v.y, v.z, v.w};
+  uint16_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) split_bf16(x[e], &h[e], &l[e]);
+  *reinterpret_cast<uint2*>(hi) =
+      make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16));
+  *reinterpret_cast<uint2*>(lo) =
+      make_uint2(uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16));
+}
+
+__device__ __forceinline__ float4 scale4(float4 v, float4 w, float s) {
+  return make_float4(v.x * w.x * s, v.y * w.y * s, v.z * w.z * s, v.w * w.w * s);
+}
+
+__device__ __forceinline__ float sq4(float4 v) {
+  return fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, v.w * v.w)));
+}
+
+__global__ __launch_bounds__(kBRowThreads) void k_bprep(const BPrepArgs a) {
+  __shared__ float red[2 * (kBRowThreads / 64)];
+  __shared__ float sv[kBRowThreads / 64];
+  __shared__ int si[kBRowThreads / 64];
   __shared__ int s_tok;
-  const int r = blockIdx.x, n = a.n;
+  const int r = blockIdx.x, n = a.n, nv = n / 4;
   const int orig = a.br.orig[r];
   if (a.step == 0) {
     if (threadIdx.x == 0) s_tok = a.boundary_tok[orig];
@@ -280,127 +312,142 @@ __global__ __launch_bounds__(256) void k_bprep(const BPrepArgs a) {
   }
   __syncthreads();
   const int tok = min(max(s_tok, 0), a.vocab - 1);
-  const uint16_t* e = a.embed + (size_t)tok * n;
-  float* g = a.G + (size_t)r * n;
-  float* hid = a.dbg_hidden ? a.dbg_hidden + (size_t)orig * (a.gamma + 1) * n : nullptr;
-
+  const uint2* erow = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);
+  float4 ev[kBRowVec], gv[kBRowVec];
   float se = 0.f, sg = 0.f;
-  for (int k = threadIdx.x * 4; k < n; k += blockDim.x * 4) {
-    const uint2 ew = *reinterpret_cast<const uint2*>(e + k);
-    const float ev[4] = {bf16_lo(ew.x), bf16_hi(ew.x), bf16_lo(ew.y), bf16_hi(ew.y)};
-    float4 gv;
-    if (a.step == 0) {
-      gv = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int z = 0; z < a.S_enc; ++z) {
-        const float4 p = *reinterpret_cast<const float4*>(a.Penc + ((size_t)z * kBatchRows + r) * n + k);
-        gv.x += p.x; gv.y += p.y; gv.z += p.z; gv.w += p.w;
-      }
-      *reinterpret_cast<float4*>(g + k) = gv;
-      if (hid) *reinterpret_cast<float4*>(hid + k) = gv;
-    } else {
-      gv = *reinterpret_cast<const float4*>(g + k);
-    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) se = fmaf(ev[q], ev[q], se);
-    sg = fmaf(gv.x, gv.x, fmaf(gv.y, gv.y, fmaf(gv.z, gv.z, fmaf(gv.w, gv.w, sg))));
+  for (int j = 0; j < kBRowVec; ++j) {
+    const int v = threadIdx.x + j * kBRowThreads;
+    ev[j] = gv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (v >= nv) continue;
+    const uint2 ew = erow[v];
+    ev[j] = make_float4(bf16_lo(ew.x), bf16_hi(ew.x), bf16_lo(ew.y), bf16_hi(ew.y));
+    se += sq4(ev[j]);
+    if (a.step == 0) {
+      for (int z = 0; z < a.S_enc; ++z) {
+        const float4 p = reinterpret_cast<const float4*>(a.Penc + ((size_t)z * kBatchRows + r) * n)[v];
+        gv[j].x += p.x; gv[j].y += p.y; gv[j].z += p.z; gv[j].w += p.w;
+      }
+      reinterpret_cast<float4*>(a.G + (size_t)r * n)[v] = gv[j];
+      if (a.dbg_hidden) reinterpret_cast<float4*>(a.dbg_hidden + (size_t)orig * (a.gamma + 1) * n)[v] = gv[j];
+      sg += sq4(gv[j]);
+    }
   }
   block_sum2(se, sg, red);
   const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
   const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
   uint16_t* xh = a.Xhi + (size_t)r * a.ldx;
   uint16_t* xl = a.Xlo + (size_t)r * a.ldx;
-  for (int k = threadIdx.x; k < n; k += blockDim.x) {
-    split_bf16(bf16_to_f32(e[k]) * ie * a.w_in[k], &xh[k], &xl[k]);
-    split_bf16(g[k] * ig * a.w_hid[k], &xh[n + k], &xl[n + k]);
+#pragma unroll
+  for (int j = 0; j < kBRowVec; ++j) {
+    const int v = threadIdx.x + j * kBRowThreads;
+    if (v >= nv) continue;
+    store_split4(xh + 4 * v, xl + 4 * v, scale4(ev[j], reinterpret_cast<const float4*>(a.w_in)[v], ie));
+    if (a.step == 0)
+      store_split4(xh + n + 4 * v, xl + n + 4 * v,
+                   scale4(gv[j], reinterpret_cast<const float4*>(a.w_hid)[v], ig));
   }
 }
 
 hipError_t launch_bprep(const BPrepArgs& a, hipStream_t s) {
-  if (a.n & 3) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bprep, dim3(a.m), dim3(256), 0, s, a);
+  if ((a.n & 3) || a.n > kBRowMax || (a.ldx & 3)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bprep, dim3(a.m), dim3(kBRowThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// grid (rows, n_head + 2 n_head_kv heads), one thread per pair of head rows
+// grid (rows, ceil(heads / 2)): two heads per block, one thread per pair of head rows
 __global__ __launch_bounds__(128) void k_bqkv(const BQkvArgs a) {
-  const int r = blockIdx.x, hs = blockIdx.y, p = threadIdx.x;
-  const int hd = a.head_dim;
-  if (2 * p >= hd) return;
-  const int qd = a.n_head * hd, kvd = a.n_head_kv * hd;
-  const int row = hs * hd + 2 * p;  // first of the pair in the (repacked) q|k|v rows
-  float y0 = 0.f, y1 = 0.f;
-  for (int z = 0; z < a.S; ++z) {
-    const float* P = a.P + ((size_t)z * kBatchRows + r) * a.N + row;
-    y0 += P[0];
-    y1 += P[1];
+  const int r = blockIdx.x, hd = a.head_dim;
+  const int hs = blockIdx.y * 2 + threadIdx.x / 64;
+  const int p = threadIdx.x % 64;
+  if (hs >= a.n_head + 2 * a.n_head_kv) return;
+  const int qd = a.n_head * hd;
+  for (int pp = p; 2 * pp < hd; pp += 64) {
+    const int row = hs * hd + 2 * pp;  // first of the pair in the (repacked) q|k|v rows
+    float y0 = 0.f, y1 = 0.f;
+    for (int z = 0; z < a.S; ++z) {
+      const float2 v = *reinterpret_cast<const float2*>(a.P + ((size_t)z * kBatchRows + r) * a.N + row);
+      y0 += v.x;
+      y1 += v.y;
+    }
+    const int seg = hs < a.n_head ? 0 : (hs < a.n_head + a.n_head_kv ? 1 : 2);
+    const int head = seg == 0 ? hs : (seg == 1 ? hs - a.n_head : hs - a.n_head - a.n_head_kv);
+    const int pos = a.br.pos0[r] + a.step;
+    const int li = 2 * pp;
+    int d0 = li, d1 = li + 1;
+    if (seg < 2 && li < a.rope_dim) {
+      d0 = pp;
+      d1 = pp + (a.rope_dim >> 1);
+      float c, sn;
+      rope_cs(pos, a.inv_freq[pp], &c, &sn);
+      const float t0 = y0 * c - y1 * sn;
+      const float t1 = y1 * c + y0 * sn;
+      y0 = t0;
+      y1 = t1;
+    }
+    if (seg == 0) {
+      float* q = a.q + (size_t)r * qd + head * hd;
+      q[d0] = y0;
+      q[d1] = y1;
+    } else {
+      const size_t esz = a.kv_f32 ? 4 : 2;
+      char* base = static_cast<char*>(a.kv) +
+                   ((size_t)a.br.slot[r] * a.seq_elems + (seg == 2 ? a.seq_elems / 2 : 0)) * esz;
+      const size_t at = ((size_t)head * a.cap + pos) * hd;
+      kv_store(base, at + d0, y0, a.kv_f32);
+      kv_store(base, at + d1, y1, a.kv_f32);
+    }
   }
-  const int seg = hs < a.n_head ? 0 : (hs < a.n_head + a.n_head_kv ? 1 : 2);
-  const int head = seg == 0 ? hs : (seg == 1 ? hs - a.n_head : hs - a.n_head - a.n_head_kv);
-  const int pos = a.br.pos0[r] + a.step;
-  const int li = 2 * p;
-  int d0 = li, d1 = li + 1;
-  if (seg < 2 && li < a.rope_dim) {
-    d0 = p;
-    d1 = p + (a.rope_dim >> 1);
-    float c, sn;
-    rope_cs(pos, a.inv_freq[p], &c, &sn);
-    const float t0 = y0 * c - y1 * sn;
-    const float t1 = y1 * c + y0 * sn;
-    y0 = t0;
-    y1 = t1;
-  }
-  if (seg == 0) {
-    float* q = a.q + (size_t)r * qd + head * hd;
-    q[d0] = y0;
-    q[d1] = y1;
-  } else {
-    const size_t esz = a.kv_f32 ? 4 : 2;
-    char* base = static_cast<char*>(a.kv) +
-                 ((size_t)a.br.slot[r] * a.seq_elems + (seg == 2 ? a.seq_elems / 2 : 0)) * esz;
-    const size_t at = ((size_t)head * a.cap + pos) * hd;
-    kv_store(base, at + d0, y0, a.kv_f32);
-    kv_store(base, at + d1, y1, a.kv_f32);
-  }
-  (void)kvd;
 }
 
 hipError_t launch_bqkv(const BQkvArgs& a, hipStream_t s) {
-  if (a.head_dim > 256 || (a.head_dim & 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bqkv, dim3(a.m, a.n_head + 2 * a.n_head_kv), dim3(128), 0, s, a);
+  if (a.head_dim > 256 || (a.head_dim & 1) || (a.N & 1)) return hipErrorInvalidValue;
+  const int heads = a.n_head + 2 * a.n_head_kv;
+  hipLaunchKernelGGL(k_bqkv, dim3(a.m, (heads + 1) / 2), dim3(128), 0, s, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bresid(const BResidArgs a) {
-  __shared__ float red[16];
-  const int r = blockIdx.x, n = a.n;
-  float* y = a.y + (size_t)r * n;
-  const float* rs = a.resid + (size_t)r * n;
-  float* hid = a.dbg_hidden
-                   ? a.dbg_hidden + ((size_t)a.br.orig[r] * (a.gamma + 1) + a.step + 1) * n
-                   : nullptr;
+__global__ __launch_bounds__(kBRowThreads) void k_bresid(const BResidArgs a) {
+  __shared__ float red[2 * (kBRowThreads / 64)];
+  const int r = blockIdx.x, n = a.n, nv = n / 4;
+  float4 yv[kBRowVec];
   float ss = 0.f, dummy = 0.f;
-  for (int k = threadIdx.x * 4; k < n; k += blockDim.x * 4) {
-    float4 v = *reinterpret_cast<const float4*>(rs + k);
+  float* hid = a.dbg_hidden ? a.dbg_hidden + ((size_t)a.br.orig[r] * (a.gamma + 1) + a.step + 1) * n
+                            : nullptr;
+#pragma unroll
+  for (int j = 0; j < kBRowVec; ++j) {
+    const int v = threadIdx.x + j * kBRowThreads;
+    yv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (v >= nv) continue;
+    float4 y = reinterpret_cast<const float4*>(a.resid + (size_t)r * n)[v];
     for (int z = 0; z < a.S; ++z) {
-      const float4 p = *reinterpret_cast<const float4*>(a.P + ((size_t)z * kBatchRows + r) * n + k);
-      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+      const float4 p = reinterpret_cast<const float4*>(a.P + ((size_t)z * kBatchRows + r) * n)[v];
+      y.x += p.x; y.y += p.y; y.z += p.z; y.w += p.w;
     }
-    *reinterpret_cast<float4*>(y + k) = v;
-    if (hid) *reinterpret_cast<float4*>(hid + k) = v;
-    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    yv[j] = y;
+    reinterpret_cast<float4*>(a.y + (size_t)r * n)[v] = y;
+    if (hid) reinterpret_cast<float4*>(hid)[v] = y;
+    ss += sq4(y);
   }
   block_sum2(ss, dummy, red);
   const float inv = 1.0f / sqrtf(ss / float(n) + a.eps);
-  uint16_t* xh = a.Xhi + (size_t)r * a.ldx;
-  uint16_t* xl = a.Xlo + (size_t)r * a.ldx;
-  for (int k = threadIdx.x; k < n; k += blockDim.x) split_bf16(y[k] * inv * a.w[k], &xh[k], &xl[k]);
+#pragma unroll
+  for (int j = 0; j < kBRowVec; ++j) {
+    const int v = threadIdx.x + j * kBRowThreads;
+    if (v >= nv) continue;
+    store_split4(a.x1_hi + (size_t)r * a.ld1 + 4 * v, a.x1_lo + (size_t)r * a.ld1 + 4 * v,
+                 scale4(yv[j], reinterpret_cast<const float4*>(a.w1)[v], inv));
+    if (a.x2_hi)
+      store_split4(a.x2_hi + (size_t)r * a.ld2 + 4 * v, a.x2_lo + (size_t)r * a.ld2 + 4 * v,
+                   scale4(yv[j], reinterpret_cast<const float4*>(a.w2)[v], inv));
+  }
 }
 
 hipError_t launch_bresid(const BResidArgs& a, hipStream_t s) {
-  if (a.n & 3) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bresid, dim3(a.m), dim3(256), 0, s, a);
+  if ((a.n & 3) || a.n > kBRowMax || (a.ld1 & 3) || (a.ld2 & 3)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bresid, dim3(a.m), dim3(kBRowThreads), 0, s, a);
   return hipGetLastError();
 }
 

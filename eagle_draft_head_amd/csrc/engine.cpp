@@ -86,6 +86,8 @@ struct eagle3_ctx {
   uint16_t *bx_a_hi = nullptr, *bx_a_lo = nullptr, *bx_b_hi = nullptr, *bx_b_lo = nullptr;
   float *b_P = nullptr, *b_G = nullptr, *b_X1 = nullptr, *b_q = nullptr, *b_po = nullptr,
         *b_pml = nullptr, *b_cand_v = nullptr, *b_logits = nullptr;
+  // normalised inputs of the gate/up and lm_head GEMMs as (hi, lo) pairs [32][n]
+  uint16_t *bx_z_hi = nullptr, *bx_z_lo = nullptr, *bx_h_hi = nullptr, *bx_h_lo = nullptr;
   int32_t* b_cand_i = nullptr;
   e3::BGemmPlan bp_enc{}, bp_qkv{}, bp_o{}, bp_gu{}, bp_d{}, bp_lm{};
 
@@ -175,6 +177,8 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (cfg->rope_dim <= 0 || cfg->rope_dim > cfg->head_dim || (cfg->rope_dim & 1))
     return bad("rope_dim must be even and in (0, head_dim]", EAGLE3_E_UNSUPPORTED);
   if (cfg->n_embd % 64) return bad("n_embd must be a multiple of 64", EAGLE3_E_UNSUPPORTED);
+  if (cfg->max_seqs > 1 && cfg->n_embd > e3::kBRowMax)
+    return bad("batched drafting supports n_embd up to 8192", EAGLE3_E_UNSUPPORTED);
   if (cfg->n_ff % 8) return bad("n_ff must be a multiple of 8", EAGLE3_E_UNSUPPORTED);
   if (!(cfg->rope_theta > 0.f) || !std::isfinite(cfg->rope_theta)) return bad("rope_theta must be > 0", EAGLE3_E_INVAL);
   if (!(cfg->rms_eps >= 0.f) || !std::isfinite(cfg->rms_eps)) return bad("rms_eps must be >= 0", EAGLE3_E_INVAL);
@@ -389,6 +393,10 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     E3_TRY(dalloc(c, &c->b_cand_v, size_t(kBatchRows) * c->bp_lm.blocks));
     E3_TRY(dalloc(c, &c->b_cand_i, size_t(kBatchRows) * c->bp_lm.blocks));
     E3_TRY(dalloc(c, &c->b_logits, size_t(kBatchRows) * dv));
+    E3_TRY(dalloc(c, &c->bx_z_hi, size_t(kBatchRows) * n));
+    E3_TRY(dalloc(c, &c->bx_z_lo, size_t(kBatchRows) * n));
+    E3_TRY(dalloc(c, &c->bx_h_hi, size_t(kBatchRows) * n));
+    E3_TRY(dalloc(c, &c->bx_h_lo, size_t(kBatchRows) * n));
   }
 
   // zero state
@@ -569,16 +577,30 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       }
       p_split = size_t(T) * kvd2;
     }
-    // store the rows of this pass into each segment's cache rows
+    // store the rows of this pass into each segment's cache rows, up to
+    // kStoreSegs segments per launch
+    e3::StoreSegs ss{};
+    auto flush = [&]() -> int {
+      if (ss.n == 0) return EAGLE3_OK;
+      E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, ss, c->nkv, c->hd, c->rot, c->inv_freq,
+                                    c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s), "tf store");
+      ss = e3::StoreSegs{};
+      return EAGLE3_OK;
+    };
     for (; seg_i < segs.size(); ++seg_i) {
       const AppendSeg& g = segs[seg_i];
       const int lo = std::max(g.row0, c0), hi = std::min(g.row0 + g.T, c0 + T);
-      if (hi > lo)
-        E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, lo - c0, hi - lo, c->nkv, c->hd, c->rot,
-                                      c->inv_freq, g.pos0 + (lo - g.row0), c->k_of(g.seq),
-                                      c->v_of(g.seq), c->cap, c->kv_f32, s), "tf store");
+      if (hi > lo) {
+        if (ss.n == e3::kStoreSegs)
+          if (int rc = flush()) return rc;
+        ss.row0[ss.n] = lo - c0;
+        ss.pos0[ss.n] = g.pos0 + (lo - g.row0);
+        ss.slot[ss.n] = g.seq;
+        ss.row0[++ss.n] = hi - c0;
+      }
       if (g.row0 + g.T > c0 + T) break;  // continues in the next pass
     }
+    if (int rc = flush()) return rc;
   }
   return EAGLE3_OK;
 }
@@ -724,30 +746,34 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
                        e3::kBEpiPartial), "o_proj");
         e3::BResidArgs ra{};
         ra.P = c->b_P; ra.S = c->bp_o.splits; ra.n = n; ra.m = m; ra.resid = c->b_G; ra.y = c->b_X1;
-        ra.w = c->nrm_post; ra.eps = c->cfg.rms_eps; ra.Xhi = c->bx_a_hi; ra.Xlo = c->bx_a_lo;
-        ra.ldx = c->bld_a; ra.br = br; ra.step = j; ra.gamma = gamma;
+        ra.eps = c->cfg.rms_eps; ra.w1 = c->nrm_post; ra.x1_hi = c->bx_z_hi; ra.x1_lo = c->bx_z_lo;
+        ra.ld1 = n; ra.br = br; ra.step = j; ra.gamma = gamma;
         E3_HIP(c, e3::launch_bresid(ra, s), "o_proj rows");
       }
       {
         ProfScope ps(c, 1, s);
-        E3_HIP(c, gemm(c->w_gu, 2 * c->ff, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->bp_gu,
-                       e3::kBEpiSilu), "gate/up");
+        E3_HIP(c, gemm(c->w_gu, 2 * c->ff, n, c->bx_z_hi, c->bx_z_lo, n, m, c->bp_gu, e3::kBEpiSilu),
+               "gate/up");
       }
       {
         ProfScope ps(c, 3, s);
         E3_HIP(c, gemm(c->w_d, n, c->ff, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->bp_d,
                        e3::kBEpiPartial), "down");
+        // g_next; RMSNorm(g_next, norm) for the lm_head and RMSNorm(g_next, hidden_norm)
+        // as the second half of the next step's QKV input
         e3::BResidArgs ra{};
         ra.P = c->b_P; ra.S = c->bp_d.splits; ra.n = n; ra.m = m; ra.resid = c->b_X1; ra.y = c->b_G;
-        ra.w = c->nrm_fin; ra.eps = c->cfg.rms_eps; ra.Xhi = c->bx_a_hi; ra.Xlo = c->bx_a_lo;
-        ra.ldx = c->bld_a; ra.br = br; ra.step = j; ra.gamma = gamma;
+        ra.eps = c->cfg.rms_eps;
+        ra.w1 = c->nrm_fin; ra.x1_hi = c->bx_h_hi; ra.x1_lo = c->bx_h_lo; ra.ld1 = n;
+        ra.w2 = c->nrm_hid; ra.x2_hi = c->bx_a_hi + n; ra.x2_lo = c->bx_a_lo + n; ra.ld2 = c->bld_a;
+        ra.br = br; ra.step = j; ra.gamma = gamma;
         ra.dbg_hidden = dbg ? dbg->hidden : nullptr;
         E3_HIP(c, e3::launch_bresid(ra, s), "down rows");
       }
       {
         ProfScope ps(c, 0, s);
-        E3_HIP(c, gemm(c->w_lm, c->dv, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->bp_lm,
-                       e3::kBEpiArgmax), "lm_head");
+        E3_HIP(c, gemm(c->w_lm, c->dv, n, c->bx_h_hi, c->bx_h_lo, n, m, c->bp_lm, e3::kBEpiArgmax),
+               "lm_head");
       }
       if (dbg && dbg->logits)
         for (int r = 0; r < m; ++r)

@@ -168,13 +168,21 @@ struct BGemmPlan {
 BGemmPlan bgemm_plan(int N, int K, int epi);
 hipError_t launch_bgemm(BGemmArgs a, const BGemmPlan& p, int epi, hipStream_t s);
 
+// Row kernels of the batched step: one block of kBRowThreads per sequence row
+// keeps the row in registers (up to kBRowMax values), so a row's sums, its RMS
+// and the normalised (hi, lo) output take one pass.
+constexpr int kBRowThreads = 1024;
+constexpr int kBRowMax = 2 * 4 * kBRowThreads;
+
 // X[r] = aux0|aux1|aux2 of caller row orig[r] (fp32 [n_seq][n] each) as (hi, lo)
 hipError_t launch_bpack_aux(const BatchRows& br, const float* a0, const float* a1, const float* a2,
                             int n, uint16_t* Xhi, uint16_t* Xlo, int ldx, hipStream_t s);
 // Start of step `step` for rows [0, m): the token (boundary token at step 0, else the
 // argmax of the previous lm_head candidates through d2t, also stored to
-// out_ids[orig * gamma + step - 1]), g (at step 0 the sum of the encode partials,
-// stored to G), and X = [RMSNorm(E[tok], w_in); RMSNorm(g, w_hid)] as (hi, lo).
+// out_ids[orig * gamma + step - 1]), then X[r][0:n] = RMSNorm(E[tok], w_in) as
+// (hi, lo).  At step 0 also g = sum of the encode partials -> G and X[r][n:2n] =
+// RMSNorm(g, w_hid) (later steps receive that half from the down projection's
+// row kernel).
 struct BPrepArgs {
   BatchRows br;
   int m, step, gamma;
@@ -193,7 +201,7 @@ struct BPrepArgs {
   float* G;                // [32][n]
   const float* Penc;       // step 0: encode partials [S][32][n]
   int S_enc;
-  uint16_t* Xhi;
+  uint16_t* Xhi;           // [32][ldx]
   uint16_t* Xlo;
   int ldx;
   float* dbg_hidden;       // optional [n_seq][gamma + 1][n]
@@ -214,18 +222,23 @@ struct BQkvArgs {
   int kv_f32, cap;
 };
 hipError_t launch_bqkv(const BQkvArgs& a, hipStream_t s);
-// y = sum_z P[z] + resid (rows [0, m), width n) -> y; X = RMSNorm(y, w) as (hi, lo);
+// y = sum_z P[z] + resid (rows [0, m), width n) -> y, then RMSNorm(y, w1) and
+// RMSNorm(y, w2) as (hi, lo) pairs (row strides ld1, ld2; the second may be NULL);
 // optionally y -> dbg_hidden[orig][step + 1].
 struct BResidArgs {
   const float* P;
   int S, n, m;
   const float* resid;
   float* y;
-  const float* w;
   float eps;
-  uint16_t* Xhi;
-  uint16_t* Xlo;
-  int ldx;
+  const float* w1;
+  uint16_t* x1_hi;
+  uint16_t* x1_lo;
+  int ld1;
+  const float* w2;
+  uint16_t* x2_hi;
+  uint16_t* x2_lo;
+  int ld2;
   BatchRows br;
   int step, gamma;
   float* dbg_hidden;
@@ -251,13 +264,22 @@ hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int 
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
                          float* cat32, hipStream_t s);
-// rows t in [row0, row0 + T): kv = sum_z P[z][t] over [k(kvd) | v(kvd)] (k rows repacked,
-// row stride 2*kvd, split stride p_split); rotate k at position pos0 + (t - row0) and
-// store bf16 into that cache row.
-hipError_t launch_tf_store(const float* P, int splits, size_t p_split, int row0, int T,
-                           int n_head_kv, int head_dim, int rope_dim, const double* inv_freq,
-                           int pos0, void* k_cache, void* v_cache, int cap, int kv_f32,
-                           hipStream_t s);
+// Up to kStoreSegs runs of consecutive rows of one append pass: rows
+// [row0[s], row0[s + 1]) go to sequence slot[s] from position pos0[s] on.
+constexpr int kStoreSegs = 32;
+struct StoreSegs {
+  int n;
+  int32_t row0[kStoreSegs + 1];
+  int32_t pos0[kStoreSegs];
+  int32_t slot[kStoreSegs];
+};
+// every row t of the segments: kv = sum_z P[z][t] over [k(kvd) | v(kvd)] (k rows
+// repacked, row stride 2*kvd, split stride p_split); rotate k at the row's position
+// and store it into that cache row of its slot (slot s starts s * seq_elems
+// elements past kv; K then V, each [n_head_kv][cap][head_dim]).
+hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const StoreSegs& segs,
+                           int n_head_kv, int head_dim, int rope_dim, const double* inv_freq, void* kv,
+                           size_t seq_elems, int cap, int kv_f32, hipStream_t s);
 
 // C[z][M][N] (fp32) = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T on bf16 MFMA
 // (A_lo may be NULL: one product).  Row strides lda, ldb (elements); K split

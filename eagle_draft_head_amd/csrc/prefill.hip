@@ -161,15 +161,22 @@ hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int 
 
 // ---------------------------------------------------------------------------
 // One block per row; a thread handles one adjacent (repacked) pair of k or v.
+// One block per row; row t of the pass belongs to the segment s with
+// row0[s] <= t < row0[s + 1], which is sequence slot[s] at position pos0[s] + (t - row0[s]).
 __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, int splits,
-                                                  size_t p_split, int row0, int nkv, int hd,
-                                                  int rope_dim, const double* __restrict__ inv_freq,
-                                                  int pos0, void* __restrict__ k_cache,
-                                                  void* __restrict__ v_cache, int cap,
+                                                  size_t p_split, const StoreSegs segs, int nkv,
+                                                  int hd, int rope_dim,
+                                                  const double* __restrict__ inv_freq,
+                                                  char* __restrict__ kv, size_t seq_elems, int cap,
                                                   int kv_f32) {
-  const int t = row0 + blockIdx.x;
+  const int t = segs.row0[0] + blockIdx.x;
+  int sg = 0;
+  while (sg + 1 < segs.n && t >= segs.row0[sg + 1]) ++sg;
   const int kvd = nkv * hd;
-  const int pos = pos0 + blockIdx.x;
+  const int pos = segs.pos0[sg] + (t - segs.row0[sg]);
+  const size_t esz = kv_f32 ? 4 : 2;
+  char* k_cache = kv + (size_t)segs.slot[sg] * seq_elems * esz;
+  char* v_cache = k_cache + seq_elems / 2 * esz;
   const float* row = P + (size_t)t * 2 * kvd;
   for (int pr = threadIdx.x; pr < kvd; pr += blockDim.x) {  // pairs over 2*kvd values
     const int r = 2 * pr;
@@ -183,29 +190,27 @@ __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, i
       const int i = li >> 1;
       d0 = i;
       d1 = i + (rope_dim >> 1);
-      const double twopi = 6.283185307179586476925286766559;
-      double ang = double(pos) * inv_freq[i];
-      ang -= floor(ang * (1.0 / twopi)) * twopi;
       float c, sv;
-      sincosf(float(ang), &sv, &c);
+      rope_cs(pos, inv_freq[i], &c, &sv);
       const float t0 = y0 * c - y1 * sv, t1 = y1 * c + y0 * sv;
       y0 = t0;
       y1 = t1;
     }
     void* base = is_k ? k_cache : v_cache;
-    const size_t row = ((size_t)head * cap + pos) * hd;
-    kv_store(base, row + d0, y0, kv_f32);
-    kv_store(base, row + d1, y1, kv_f32);
+    const size_t at = ((size_t)head * cap + pos) * hd;
+    kv_store(base, at + d0, y0, kv_f32);
+    kv_store(base, at + d1, y1, kv_f32);
   }
 }
 
-hipError_t launch_tf_store(const float* P, int splits, size_t p_split, int row0, int T,
-                           int n_head_kv, int head_dim, int rope_dim, const double* inv_freq,
-                           int pos0, void* k_cache, void* v_cache, int cap, int kv_f32,
-                           hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tf_store, dim3(T), dim3(256), 0, s, P, splits, p_split, row0, n_head_kv,
-                     head_dim, rope_dim, inv_freq, pos0, k_cache, v_cache, cap, kv_f32);
+hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const StoreSegs& segs,
+                           int n_head_kv, int head_dim, int rope_dim, const double* inv_freq, void* kv,
+                           size_t seq_elems, int cap, int kv_f32, hipStream_t s) {
+  if (segs.n < 1 || segs.n > kStoreSegs) return hipErrorInvalidValue;
+  const int rows = segs.row0[segs.n] - segs.row0[0];
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tf_store, dim3(rows), dim3(256), 0, s, P, splits, p_split, segs, n_head_kv,
+                     head_dim, rope_dim, inv_freq, static_cast<char*>(kv), seq_elems, cap, kv_f32);
   return hipGetLastError();
 }
 
