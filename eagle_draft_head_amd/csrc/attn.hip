@@ -199,44 +199,50 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   }
 }
 
-// One block per query head: o = sum_s w_s o_s with w_s = exp(m_s - M) / sum_z l_z exp(m_z - M)
+// One block of hd threads per query head: o = sum_s w_s o_s with
+// w_s = exp(m_s - M) / sum_z l_z exp(m_z - M).  Every load (the (m, l) pairs and
+// this thread's column of the S partial outputs, kCombineRegs splits at a time)
+// is issued before any of them is used; the maximum and the weighted sum of l
+// are wave reductions, shared through LDS.
+constexpr int kCombineRegs = 32;
+
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int S,
                                                       int hd, float* __restrict__ out) {
-  extern __shared__ float w[];  // [S]
-  __shared__ float red[32];
-  const int h = blockIdx.x;
+  __shared__ float sw[kCombineRegs];
+  __shared__ float sL[1];
+  const int h = blockIdx.x, d = threadIdx.x;
+  const int lane = d & 63, wv = d >> 6;
   const float* ml = part_ml + (size_t)h * S * 2;
-  float M = -INFINITY;
-  for (int z = threadIdx.x; z < S; z += blockDim.x) M = fmaxf(M, ml[2 * z]);
-  M = wave_max(M);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (lane == 0) red[wv] = M;
-  __syncthreads();
-  M = red[0];
-  for (int k = 1; k < nw; ++k) M = fmaxf(M, red[k]);
-  float L = 0.f, dummy = 0.f;
-  for (int z = threadIdx.x; z < S; z += blockDim.x) {
-    const float e = expf(ml[2 * z] - M);
-    w[z] = e;
-    L = fmaf(e, ml[2 * z + 1], L);
-  }
-  __syncthreads();
-  block_sum2(L, dummy, red);
-  const float invL = 1.0f / L;
-  const float* po = part_o + (size_t)h * S * hd;
-  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-    int z = 0;
-    for (; z + 3 < S; z += 4) {
-      acc0 = fmaf(w[z], po[(size_t)z * hd + d], acc0);
-      acc1 = fmaf(w[z + 1], po[(size_t)(z + 1) * hd + d], acc1);
-      acc2 = fmaf(w[z + 2], po[(size_t)(z + 2) * hd + d], acc2);
-      acc3 = fmaf(w[z + 3], po[(size_t)(z + 3) * hd + d], acc3);
+  const float* po = part_o + (size_t)h * S * hd + d;
+  float acc = 0.f, Lsum = 0.f, M = -INFINITY;
+  for (int z0 = 0; z0 < S; z0 += kCombineRegs) {
+    const int cnt = min(kCombineRegs, S - z0);
+    float o[kCombineRegs];
+#pragma unroll
+    for (int i = 0; i < kCombineRegs; ++i) o[i] = i < cnt ? po[(size_t)(z0 + i) * hd] : 0.f;
+    if (z0 == 0) {  // the maximum over all splits (loads queued behind the first group)
+      for (int z = lane; z < S; z += 64) M = fmaxf(M, ml[2 * z]);
+      M = wave_max(M);
     }
-    for (; z < S; ++z) acc0 = fmaf(w[z], po[(size_t)z * hd + d], acc0);
-    out[(size_t)h * hd + d] = ((acc0 + acc1) + (acc2 + acc3)) * invL;
+    // weights of this group of splits: lane i of wave 0 computes split z0 + i
+    if (wv == 0 && lane < cnt) {
+      const float e = expf(ml[2 * (z0 + lane)] - M);
+      sw[lane] = e;
+      Lsum = fmaf(e, ml[2 * (z0 + lane) + 1], Lsum);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCombineRegs; ++i)
+      if (i < cnt) acc = fmaf(sw[i], o[i], acc);
+    __syncthreads();
   }
+  if (wv == 0) {
+    Lsum = wave_sum(Lsum);
+    if (lane == 0) sL[0] = Lsum;
+  }
+  __syncthreads();
+  if (d < hd) out[(size_t)h * hd + d] = acc / sL[0];
 }
 
 // Batched combine: grid (n_head, rows); row r has ceil(T_r / chunk) splits of the
@@ -335,8 +341,8 @@ static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStrea
 #undef E3_ATTN_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1 || a.batched) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(128), size_t(S) * sizeof(float), s,
-                     a.part_o, a.part_ml, S, HD, a.out);
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S, HD,
+                     a.out);
   return hipGetLastError();
 }
 

@@ -30,21 +30,20 @@
 
 namespace e3 {
 
-// Stream columns [k0, k0 + K) of the R rows a wave owns against xs[0, K).
-template <int R, int U>
-__device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t ldw, int row0,
-                                         int N, int k0, int K, const float* __restrict__ xs,
-                                         float (&acc)[R]) {
-  const int lane = threadIdx.x & 63;
-  const uint4* wp[R];
+// Row pointers of the R rows a wave owns, at column k0 (rows past N repeat the last row).
+template <int R>
+__device__ __forceinline__ void row_ptrs(const uint16_t* __restrict__ W, size_t ldw, int row0, int N,
+                                         int k0, const uint4* (&wp)[R]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = 0; r < R; ++r)
     wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * ldw + k0);
-    acc[r] = 0.f;
-  }
-  const int nch = K >> 3;
-  const float4* x4 = reinterpret_cast<const float4*>(xs);
-  int c = lane;
+}
+
+// Continue the dot products from 16-byte chunk c (this lane's) to the end: U chunk
+// steps in flight per row, then single steps for the tail.
+template <int R, int U>
+__device__ __forceinline__ void rows_dot_from(const uint4* (&wp)[R], int c, int nch,
+                                              const float4* __restrict__ x4, float (&acc)[R]) {
   for (; c + 64 * (U - 1) < nch; c += 64 * U) {
     uint4 w[U][R];
 #pragma unroll
@@ -68,6 +67,52 @@ __device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t 
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+}
+
+// Stream columns [k0, k0 + K) of the R rows a wave owns against xs[0, K).
+template <int R, int U>
+__device__ __forceinline__ void rows_dot(const uint16_t* __restrict__ W, size_t ldw, int row0,
+                                         int N, int k0, int K, const float* __restrict__ xs,
+                                         float (&acc)[R]) {
+  const uint4* wp[R];
+  row_ptrs<R>(W, ldw, row0, N, k0, wp);
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  rows_dot_from<R, U>(wp, threadIdx.x & 63, K >> 3, reinterpret_cast<const float4*>(xs), acc);
+}
+
+// The first U chunk steps of rows_dot, issued early (before a prologue whose
+// loads can then complete behind them); requires K / 8 >= 64 U.
+template <int R, int U>
+__device__ __forceinline__ void rows_issue(const uint16_t* __restrict__ W, size_t ldw, int row0,
+                                           int N, int k0, uint4 (&w)[U][R]) {
+  const uint4* wp[R];
+  row_ptrs<R>(W, ldw, row0, N, k0, wp);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[u][r] = ld_stream(wp[r] + lane + 64 * u);
+}
+
+// rows_dot whose first U chunk steps were issued by rows_issue.
+template <int R, int U>
+__device__ __forceinline__ void rows_dot_issued(const uint16_t* __restrict__ W, size_t ldw, int row0,
+                                                int N, int k0, int K, const float* __restrict__ xs,
+                                                const uint4 (&w)[U][R], float (&acc)[R]) {
+  const uint4* wp[R];
+  row_ptrs<R>(W, ldw, row0, N, k0, wp);
+  const int lane = threadIdx.x & 63;
+  const float4* x4 = reinterpret_cast<const float4*>(xs);
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float4 a = x4[2 * (lane + 64 * u)], b = x4[2 * (lane + 64 * u) + 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = dot8(w[u][r], a, b, acc[r]);
+  }
+  rows_dot_from<R, U>(wp, lane + 64 * U, K >> 3, x4, acc);
 }
 
 // sum of `count` per-block partial sums (this thread's share)
@@ -173,6 +218,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
 
+  // the first weight loads of the hidden half go out before anything else, so
+  // the prologue below (staging, the previous step's argmax, the embedding row)
+  // overlaps the weight stream
+  uint4 wpf[U][R];
+  const bool issued = row0 < N && (n >> 3) >= 64 * U;
+  if (issued) rows_issue<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, wpf);
   // hidden half: already weighted by hidden_norm; its sum of squares from partials
   stage_plain(xs + n, a.gw, n);
   float sg = sum_partials(a.g_ssq, a.g_ssq_count);
@@ -208,7 +259,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
     }
   }
   float acc_g[R], acc_e[R];
-  if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
+  if (issued) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, wpf, acc_g);
+  else if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
   float se = 0.f;
   float4* x4 = reinterpret_cast<float4*>(xs);
   if (in_regs) {
