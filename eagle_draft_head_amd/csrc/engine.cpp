@@ -557,7 +557,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       E3_HIP(c, e3::launch_pack_aux(a0 + size_t(c0) * n, a1 + size_t(c0) * n, a2 + size_t(c0) * n,
                                     T, n, c->tf_A, c->tf_A_lo, s), "pack aux");
       sp1 = e3::gemm_pick_splits(T, n, 3 * n);
-      while (sp1 > 1 && (size_t(sp1) * T * n > c->tf_F_cap || (3 * n) % (32 * sp1))) --sp1;
+      while (sp1 > 1 && (size_t(sp1) * T * n > c->tf_F_cap || (3 * n) % (64 * sp1))) --sp1;
       {
         ProfScope ps(c, 7, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, T, n,
@@ -568,7 +568,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
                                   c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s),
              "tf cat");
       sp2 = e3::gemm_pick_splits(T, kvd2, 2 * n);
-      while (sp2 > 1 && (size_t(sp2) * T * kvd2 > c->tf_P_cap || (2 * n) % (32 * sp2))) --sp2;
+      while (sp2 > 1 && (size_t(sp2) * T * kvd2 > c->tf_P_cap || (2 * n) % (64 * sp2))) --sp2;
       {
         ProfScope ps(c, 8, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n,

@@ -178,7 +178,8 @@ __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, i
   char* k_cache = kv + (size_t)segs.slot[sg] * seq_elems * esz;
   char* v_cache = k_cache + seq_elems / 2 * esz;
   const float* row = P + (size_t)t * 2 * kvd;
-  for (int pr = threadIdx.x; pr < kvd; pr += blockDim.x) {  // pairs over 2*kvd values
+  // grid.y spreads the kvd value pairs of a row over blocks (one pair per thread)
+  for (int pr = blockIdx.y * blockDim.x + threadIdx.x; pr < kvd; pr += gridDim.y * blockDim.x) {
     const int r = 2 * pr;
     float y0 = sum_splits(row + r, splits, p_split);
     float y1 = sum_splits(row + r + 1, splits, p_split);
@@ -209,7 +210,8 @@ hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const Sto
   if (segs.n < 1 || segs.n > kStoreSegs) return hipErrorInvalidValue;
   const int rows = segs.row0[segs.n] - segs.row0[0];
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tf_store, dim3(rows), dim3(256), 0, s, P, splits, p_split, segs, n_head_kv,
+  const int pair_blocks = (n_head_kv * head_dim + 255) / 256;
+  hipLaunchKernelGGL(k_tf_store, dim3(rows, pair_blocks), dim3(256), 0, s, P, splits, p_split, segs, n_head_kv,
                      head_dim, rope_dim, inv_freq, static_cast<char*>(kv), seq_elems, cap, kv_f32);
   return hipGetLastError();
 }
@@ -258,180 +260,218 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s) {
 // The weights B are exact in bf16; the activations may carry a bf16 remainder
 // A_lo, which costs a second MFMA per fragment and gives fp32-grade products.
 //
-// v_mfma_f32_32x32x16_bf16 tiles: a wave owns a 64 x 64 block of C (2 x 2
-// MFMA tiles); waves tile the block (BM / 64) x (BN / 64).  Operand tiles of
-// BK = 32 are staged in LDS (rows padded by 8 elements), double buffered so
-// one barrier per K-tile suffices: the next tile's global loads are issued
-// before the current tile's MFMAs and written to the other buffer after them.
-// Block order: consecutive blocks are dispatched to different XCDs; the
-// mapping gives every block of one XCD the same weight (N) tile range, so a
-// weight tile is fetched into only one XCD's L2.
-template <int BM, int BN, bool SPLIT, int BK = 32>
-__global__ __launch_bounds__((BM / 64) * (BN / 64) * 64) void k_gemm(
+// C[z] = A[M, kz-range] . B[N, kz-range]^T on v_mfma_f32_16x16x32_bf16.
+//
+// Waves tile the block WM x WN, each owning (BM / WM) x (BN / WN) of C as 16 x 16
+// MFMA tiles.  Operand tiles of BK columns go from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane: a wave instruction fills 1 KB of LDS, lane
+// l at byte 16 l), NST of them in a ring so the loads of tile t + NST - 1 are in
+// flight while tile t is multiplied; one barrier per tile.  LDS rows are BK
+// elements unpadded; chunk c (8 elements) of row r sits in slot c ^ swizzle(r),
+// which keeps the 16-byte fragment reads free of bank conflicts.  With A_lo
+// given, the (hi, lo) halves of A share every B fragment (two MFMAs).
+// Block order: consecutive blocks go to different XCDs; every block of one XCD
+// gets the same weight (N) tile range, so a weight tile is fetched into only one
+// XCD's L2.
+template <int BK>
+__device__ __forceinline__ int tile_swizzle(int r) {
+  return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+
+// s_waitcnt vmcnt(N), the other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define E3_WV(i) \
+  case i:        \
+    wait_vmcnt<i>(); \
+    break;
+    E3_WV(0) E3_WV(1) E3_WV(2) E3_WV(3) E3_WV(4) E3_WV(5) E3_WV(6) E3_WV(7) E3_WV(8) E3_WV(9)
+    E3_WV(10) E3_WV(11) E3_WV(12) E3_WV(13) E3_WV(14) E3_WV(15) E3_WV(16) E3_WV(17) E3_WV(18)
+    E3_WV(19) E3_WV(20) E3_WV(21) E3_WV(22) E3_WV(23)
+#undef E3_WV
+    default:
+      wait_vmcnt<0>();
+      break;
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool SPLIT, int BK, int NST>
+__global__ __launch_bounds__(WM * WN * 64) void k_gemm(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, int lda,
     const uint16_t* __restrict__ B, int ldb, float* __restrict__ C, int M, int N, int kper,
     int mt, int nt) {
-  static_assert(BK % 16 == 0, "K tile is a whole number of MFMA steps");
-  constexpr int WMW = BM / 64, WNW = BN / 64;
-  constexpr int NT = WMW * WNW * 64;
-  constexpr int LDK = BK + 8;
-  constexpr int CPR = BK / 8;
-  constexpr int NA = BM * CPR, NB = BN * CPR;
-  constexpr int CA = (NA + NT - 1) / NT, CB = (NB + NT - 1) / NT;
+  constexpr int TM = BM / (16 * WM), TN = BN / (16 * WN);
+  static_assert(TM * 16 * WM == BM && TN * 16 * WN == BN, "waves must tile the block");
+  constexpr int NW = WM * WN;
   constexpr int NSA = SPLIT ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][NSA][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+  constexpr int CPR = BK / 8, RPI = 64 / CPR;  // chunks per row, rows per load instruction
+  constexpr int IA = BM / RPI, IB = BN / RPI;
+  static_assert(IA * RPI == BM && IB * RPI == BN, "rows per load instruction");
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* As = smem;                        // [NST][NSA][BM * BK]
+  uint16_t* Bs = smem + NST * NSA * BM * BK;  // [NST][BN * BK]
 
-  // XCD-aware tile order
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   const int n_t = xcd + 8 * (slot / mt), m_t = slot % mt;
   if (n_t >= nt) return;  // whole block idle (grid rounded up to the XCD pattern)
   const int m0 = m_t * BM, n0 = n_t * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv / WNW, wn = wv % WNW;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv / WN, wn = wv % WN;
   const int kb = blockIdx.z * kper;
   float* Cz = C + (size_t)blockIdx.z * M * N;
+  // load instructions this wave issues per tile (the count its vmcnt waits use)
+  const int lpt = (IA / NW + (wv < IA % NW ? 1 : 0)) * NSA + IB / NW + (wv < IB % NW ? 1 : 0);
 
-  f32x16 acc[2][2];
+  f32x4 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
-  uint4 ra[NSA][CA], rb[CB];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int c = 0; c < CA; ++c) {
-      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NA % NT != 0 && idx >= NA) break;
-      const size_t off = (size_t)min(m0 + row, M - 1) * lda + kt + col;
-      ra[0][c] = *reinterpret_cast<const uint4*>(A + off);
-      if (SPLIT) ra[NSA - 1][c] = *reinterpret_cast<const uint4*>(A2 + off);
-    }
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NB % NT != 0 && idx >= NB) break;
-      rb[c] = *reinterpret_cast<const uint4*>(B + (size_t)min(n0 + row, N - 1) * ldb + kt + col);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CA; ++c) {
-      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NA % NT != 0 && idx >= NA) break;
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  auto issue = [&](int kt, int st) {
+    for (int q = wv; q < IA; q += NW) {
+      const int r = q * RPI + lrow;
+      const size_t off = (size_t)min(m0 + r, M - 1) * lda + kt + 8 * (lslot ^ tile_swizzle<BK>(r));
 #pragma unroll
       for (int h = 0; h < NSA; ++h)
-        *reinterpret_cast<uint4*>(&As[buf][h][row * LDK + col]) = ra[h][c];
+        __builtin_amdgcn_global_load_lds(
+            (const void*)((h ? A2 : A) + off),
+            (void __attribute__((address_space(3)))*)(As + ((size_t)(st * NSA + h) * BM + q * RPI) * BK),
+            16, 0, 0);
     }
-#pragma unroll
-    for (int c = 0; c < CB; ++c) {
-      const int idx = tid + NT * c, row = idx / CPR, col = (idx % CPR) * 8;
-      if (NB % NT != 0 && idx >= NB) break;
-      *reinterpret_cast<uint4*>(&Bs[buf][row * LDK + col]) = rb[c];
+    for (int q = wv; q < IB; q += NW) {
+      const int r = q * RPI + lrow;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(B + (size_t)min(n0 + r, N - 1) * ldb + kt + 8 * (lslot ^ tile_swizzle<BK>(r))),
+          (void __attribute__((address_space(3)))*)(Bs + ((size_t)st * BN + q * RPI) * BK), 16, 0, 0);
     }
   };
 
   const int ntiles = kper / BK;
-  gload(kb);
-  lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s0 = 0; s0 < NST - 1; ++s0)
+    if (s0 < ntiles) issue(kb + s0 * BK, s0);
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(kb + (t + 1) * BK);
+    const int st = t % NST;
+    // tile t has landed once at most the later tiles' loads are outstanding
+    if (t + NST - 2 < ntiles) wait_vmcnt_dyn((NST - 2) * lpt);
+    else wait_vmcnt<0>();
+    __syncthreads();  // every wave's part of tile t is in LDS; tile t - 1's stage is free
+    if (t + NST - 1 < ntiles) issue(kb + (t + NST - 1) * BK, (t + NST - 1) % NST);
+    const uint16_t* Ab = As + (size_t)st * NSA * BM * BK;
+    const uint16_t* Bb = Bs + (size_t)st * BN * BK;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      const int kof = kk + (lane >> 5) * 8;
-      bf16x8 bfr[2];
+    for (int kk = 0; kk < BK; kk += 32) {
+      // 16x16x32 operands: lane l holds row l % 16, columns 8 (l / 16) .. + 7 of the step
+      const int c = (kk >> 3) + (lane >> 4);
+      bf16x8 bfr[TN];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][(wn * 64 + j * 32 + (lane & 31)) * LDK + kof]);
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * 16 * TN + j * 16 + (lane & 15);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bb[r * BK + 8 * (c ^ tile_swizzle<BK>(r))]);
+      }
 #pragma unroll
       for (int h = 0; h < NSA; ++h) {
-        bf16x8 af[2];
+        bf16x8 af[TM];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(
-              &As[buf][h][(wm * 64 + i * 32 + (lane & 31)) * LDK + kof]);
+        for (int i = 0; i < TM; ++i) {
+          const int r = wm * 16 * TM + i * 16 + (lane & 15);
+          af[i] = *reinterpret_cast<const bf16x8*>(&Ab[((size_t)h * BM + r) * BK + 8 * (c ^ tile_swizzle<BK>(r))]);
+        }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
   }
 
-  // D layout of a 32x32 tile: lane l holds column l % 32 and rows
-  // 8 * (v / 4) + 4 * (l / 32) + (v % 4) for its 16 values v
+  // D of a 16x16 tile: lane l holds column l % 16, rows 4 (l / 16) + v
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * 16 * TN + j * 16 + (lane & 15);
       if (col >= N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + wm * 16 * TM + i * 16 + 4 * (lane >> 4) + v;
         if (row < M) Cz[(size_t)row * N + col] = acc[i][j][v];
       }
     }
 }
 
-constexpr int kBK = 32;
+// K tile: 32 with split activations (three stages fit), 64 otherwise (two stages)
+constexpr int kBKSplit = 32, kBKPlain = 64;
 
-// 256 x 256 tiles (16 waves, one block per CU) once there are 256 rows;
-// 128 x 128 below.  The K split is chosen so the blocks fill the 256 CUs.
-static void gemm_tiles(int M, int N, int* bm, int* bn) {
-  (void)N;
-  if (M >= 256) { *bm = 256; *bn = 256; }
-  else { *bm = 128; *bn = 128; }
-}
+// 256 x 256 blocks once there are 256 rows, 128 x 128 below
+static int gemm_bm(int M) { return M >= 256 ? 256 : 128; }
 
 int gemm_pick_splits(int M, int N, int K) {
-  int bm, bn;
-  gemm_tiles(M, N, &bm, &bn);
-  const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  const int kt = K / kBK;
-  int want = (256 + tiles - 1) / tiles;
-  if (want > 8) want = 8;
+  // K splits s in {1, 2, 4} (each keeping whole 64-wide K tiles): the blocks run in
+  // ceil(tiles s / 256) rounds of 1/s of the work each, so take the s with the
+  // fewest rounds per unit of work (the smaller s on ties); more splits would add
+  // M x N fp32 partials per split to write and sum
+  const int bm = gemm_bm(M);
+  const int tiles = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
   int best = 1;
-  for (int sp = 1; sp <= want && sp <= kt; ++sp)
-    if (kt % sp == 0) best = sp;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= 4; sp *= 2) {
+    if (K % (kBKPlain * sp) != 0) continue;
+    const double cost = double((tiles * sp + 255) / 256) / sp;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
   return best;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int BK, int NST>
 static hipError_t launch_tiles(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
                                const uint16_t* B, int ldb, float* C, int M, int N, int kper,
                                int splits, hipStream_t s) {
+  constexpr int NSA = SPLIT ? 2 : 1;
+  constexpr size_t lds = size_t(NST) * (NSA * BM + BN) * BK * 2;
+  static_assert(lds <= 160 * 1024, "LDS ring exceeds a workgroup's LDS");
+  static bool attr_set = false;  // the attribute is per kernel; setting it twice is harmless
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, SPLIT, BK, NST>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
-  const int nt8 = (nt + 7) / 8 * 8;  // N tiles padded to the 8-XCD pattern
-  dim3 grid(mt * nt8, 1, splits), block((BM / 64) * (BN / 64) * 64);
-  if (A_lo)
-    hipLaunchKernelGGL((k_gemm<BM, BN, true>), grid, block, 0, s, A_hi, A_lo, lda, B, ldb, C, M, N,
-                       kper, mt, nt);
-  else
-    hipLaunchKernelGGL((k_gemm<BM, BN, false>), grid, block, 0, s, A_hi, A_lo, lda, B, ldb, C, M,
-                       N, kper, mt, nt);
+  const int nt8 = (nt + 7) / 8 * 8;
+  dim3 grid(mt * nt8, 1, splits), block(WM * WN * 64);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, SPLIT, BK, NST>), grid, block, lds, s, A_hi, A_lo, lda, B,
+                     ldb, C, M, N, kper, mt, nt);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
                             int ldb, float* C, int M, int N, int K, int splits, hipStream_t s) {
-  if (M <= 0 || N <= 0) return hipSuccess;
-  if (K % (kBK * splits) != 0) return hipErrorInvalidValue;
+  if (M <= 0 || N <= 0 || splits < 1 || K % (kBKPlain * splits) != 0 || (lda & 7) || (ldb & 7))
+    return hipErrorInvalidValue;
   const int kper = K / splits;
-  int bm, bn;
-  gemm_tiles(M, N, &bm, &bn);
-  if (bm == 256) return launch_tiles<256, 256>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
-  return launch_tiles<128, 128>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  const bool big = gemm_bm(M) == 256;
+  if (A_lo) {
+    if (big) return launch_tiles<256, 256, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    return launch_tiles<128, 128, 2, 2, true, kBKSplit, 4>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  }
+  if (big) return launch_tiles<256, 256, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  return launch_tiles<128, 128, 2, 2, false, kBKPlain, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
 }
 
 }  // namespace e3
