@@ -60,8 +60,9 @@ def committed_traffic(kernel: str):
     return float(vals["bytes_per_launch"])
 
 
-def kernel_bytes(cfg, kernel: str, L: int) -> float:
-    """Algorithmic HBM bytes of one launch of a kernel family."""
+def kernel_bytes(cfg, kernel: str, L: int, kv_bytes: int = 4) -> float:
+    """Algorithmic HBM bytes of one launch of a kernel family (K/V elements of
+    kv_bytes bytes)."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     if kernel == "lm_head":
         return 2.0 * dv * n + 4 * n + 4 * n
@@ -76,20 +77,21 @@ def kernel_bytes(cfg, kernel: str, L: int) -> float:
     if kernel == "encode":
         return 2.0 * 3 * n * n + 12 * n + 4 * n
     if kernel == "attention":
-        return 4.0 * kvd * (L + 1) + 8 * qd
+        return 2.0 * kv_bytes * kvd * (L + 1) + 8 * qd
     raise KeyError(kernel)
 
 
-def step_bytes(cfg, L: int, gamma: int, accepted: int) -> float:
-    """Algorithmic HBM bytes of one round: encode, gamma draft steps, rebuild."""
+def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4) -> float:
+    """Algorithmic HBM bytes of one round: encode, gamma draft steps, rebuild (K/V
+    elements of kv_bytes bytes)."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
     tot = 6.0 * n * n + 12 * n                         # encode: W_fc + aux
     for j in range(gamma):
         rows = L + j                                      # rows attended before the new one
-        tot += 2.0 * p_step + 8 * n + 2 * n + rows * 4 * kvd + 4 * kvd
+        tot += 2.0 * p_step + 8 * n + 2 * n + (rows + 1) * 2 * kv_bytes * kvd
     T = accepted + 1                                      # rebuild rows
-    tot += 6.0 * n * n + 2.0 * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 4 * kvd)
+    tot += 6.0 * n * n + 2.0 * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 2 * kv_bytes * kvd)
     return tot
 
 
@@ -103,6 +105,8 @@ def main():
     ap.add_argument("--kernel", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=3)
+    ap.add_argument("--kv", choices=["f32", "bf16"], default="f32",
+                    help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -133,7 +137,8 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     max_ctx = L + 64
-    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma))
+    kv_dtype = B.KV_BF16 if args.kv == "bf16" else B.KV_F32
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype)
     stream = torch.cuda.current_stream()
 
     # committed context
@@ -197,9 +202,10 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = gamma * args.steps / elapsed
     k_avg_s = (k_ms / 1e3) / max(k_launches, 1)
-    k_bytes = kernel_bytes(cfg, args.kernel, L)
+    kvb = 2 if args.kv == "bf16" else 4
+    k_bytes = kernel_bytes(cfg, args.kernel, L, kvb)
     achieved = k_bytes / k_avg_s / 1e9
-    sb = [step_bytes(cfg, L, gamma, accepted[i]) for i in range(args.warmup, nsteps)]
+    sb = [step_bytes(cfg, L, gamma, accepted[i], kvb) for i in range(args.warmup, nsteps)]
     step_gbs = (sum(sb) / args.steps) / (elapsed / args.steps) / 1e9
 
     cpu = None
@@ -217,7 +223,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights, fp32 accumulate",
+        "dtype": f"bf16 weights, fp32 accumulate, {args.kv} draft KV",
         "data": "synthetic (seeded; random-init weights of the drafter architecture)",
         "config": {"workload": f"{cfg.name} drafter: n_embd {cfg.n_embd}, {cfg.n_head}/{cfg.n_head_kv} "
                                f"heads x {cfg.head_dim}, n_ff {cfg.n_ff}, draft vocab {cfg.draft_vocab}, "
@@ -238,14 +244,15 @@ def main():
     dr.close()
 
 
-def batched_kernel_bytes(cfg, kernel: str, lens, gamma: int, steps_run: int) -> float:
+def batched_kernel_bytes(cfg, kernel: str, lens, gamma: int, kv_bytes: int = 4) -> float:
     """Algorithmic HBM bytes per launch of a batched-step kernel, averaged over the
-    steps of a round (`lens`: committed rows per sequence; fp32 K/V rows)."""
+    steps of a round (`lens`: committed rows per sequence; K/V elements of
+    kv_bytes bytes)."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     m = len(lens)
     if kernel == "attention":
         rows = sum(L + j + 1 for L in lens for j in range(gamma)) / gamma
-        return 2.0 * 4 * kvd * rows + m * (4 * qd + 4 * qd)
+        return 2.0 * kv_bytes * kvd * rows + m * (4 * qd + 4 * qd)
     act = {"lm_head": (dv, n), "gate_up": (2 * ff, n), "qkv": (qd + 2 * kvd, 2 * n),
            "down": (n, ff), "o_proj": (n, qd)}[kernel]
     return 2.0 * act[0] * act[1] + m * 4 * act[1]
@@ -269,7 +276,9 @@ def run_batched(args, cfg):
     lens = gen.batch_lengths(cfg)
     S = len(lens)
     wd = gen.drafter_weights(cfg, device=dev)
-    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=cfg.max_ctx, max_gamma=max(8, gamma), max_seqs=S)
+    kv_dtype = B.KV_BF16 if args.kv == "bf16" else B.KV_F32
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=cfg.max_ctx, max_gamma=max(8, gamma), max_seqs=S,
+                 kv_dtype=kv_dtype)
     t0 = time.time()
     for s, L in enumerate(lens):
         aux = gen.aux_taps(cfg, 100 + s, L, device=dev)
@@ -317,12 +326,13 @@ def run_batched(args, cfg):
     k_ms, k_launches = B.eagle3_profile_read(dr.ctx)
     B.eagle3_profile_enable(dr.ctx, kernel, False)
     k_avg_s = (k_ms / 1e3) / max(k_launches, 1)
-    k_bytes = batched_kernel_bytes(cfg, kernel, lens, gamma, gamma)
+    kvb = 2 if args.kv == "bf16" else 4
+    k_bytes = batched_kernel_bytes(cfg, kernel, lens, gamma, kvb)
     achieved = k_bytes / k_avg_s / 1e9
 
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
-    kv_bytes = sum(2.0 * 4 * kvd * (L + j + 1) for L in lens for j in range(gamma))
+    kv_bytes = sum(2.0 * kvb * kvd * (L + j + 1) for L in lens for j in range(gamma))
     round_bytes = 6.0 * n * n + gamma * (2.0 * p_step) + kv_bytes
     step_gbs = round_bytes / (elapsed / args.steps) / 1e9
 
@@ -340,7 +350,7 @@ def run_batched(args, cfg):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights, fp32 accumulate, fp32 draft KV",
+        "dtype": f"bf16 weights, fp32 accumulate, {args.kv} draft KV",
         "data": "synthetic (seeded; random-init weights of the drafter architecture)",
         "config": {"workload": f"{cfg.name}: {S} sequences of the {cfg.n_embd}-wide drafter with "
                                f"{min(lens)}..{max(lens)} committed rows (sum {sum(lens)})",
