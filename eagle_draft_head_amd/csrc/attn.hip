@@ -1,14 +1,18 @@
 // Decode attention of one query row per head over the draft KV cache.
 //
-// Grid (S context splits, n_head_kv).  A block owns `chunk` consecutive KV
-// rows of one KV head and all G = n_head / n_head_kv query heads that read it
-// (each K/V byte is fetched once per step).  A row is spread over head_dim / 8
-// lanes (16 bytes each), so a wave covers 64 / (head_dim / 8) rows per step.
-// Single pass with an online softmax: each lane group keeps (m, l, o) per query
-// head; K and V of a row are requested together.  Lane groups and waves are
-// merged with the log-sum-exp rule at the end.  With S > 1 each block stores
-// (m, l, unnormalised o) and a second kernel combines the splits per query
-// head; with S == 1 the block writes the normalised output.
+// Grid (S context splits, n_head_kv[, batch rows]).  A block owns `chunk`
+// consecutive KV rows of one KV head and all G = n_head / n_head_kv query heads
+// that read it (each K/V byte is fetched once per step).  A lane holds 8
+// consecutive elements of a row (16 bytes of bf16 or 32 of fp32), so a row is
+// spread over head_dim / 8 lanes and a wave covers 512 / head_dim rows per step;
+// fewer lanes per row means fewer cross-lane steps per row for the dot products
+// and the softmax bookkeeping, which bound this kernel rather than HBM.
+// Single pass with an online softmax in base 2 (scores scaled by log2 e): each
+// lane group keeps (m, l, o) per query head, m a reference within 2^8 of the
+// running maximum; K and V of a row are requested together, several rows ahead.
+// Lane groups and waves are merged with the log-sum-exp rule at the end.  With
+// S > 1 each block stores (m, l, unnormalised o) and a second kernel combines the
+// splits per query head; with S == 1 the block writes the normalised output.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,19 +43,24 @@ struct KvVec<float> {
   }
 };
 
+constexpr int kAttnLaneElems = 8;  // elements of a row per lane
+constexpr float kRescale = 8.0f;   // log2 headroom of the online softmax reference
+
 template <int HD, int G, typename KT>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
-  constexpr int E = KvVec<KT>::E;
-  constexpr int LPR = HD / E;
+  constexpr int E = KvVec<KT>::E;            // elements per 16-byte vector
+  constexpr int NV = kAttnLaneElems / E;     // vectors per lane per row (K, and V)
+  constexpr int LPR = HD / kAttnLaneElems;   // lanes per row
   constexpr int RPW = 64 / LPR;
   constexpr int RPB = RPW * kAttnWaves;
-  static_assert(LPR <= 64 && RPW >= 1, "a row must fit in one wave");
+  constexpr int kDepth = NV == 1 ? 4 : 2;    // rows in flight per lane group
+  static_assert(LPR <= 64 && RPW >= 1 && NV * E == kAttnLaneElems, "a row must fit in one wave");
   __shared__ float obuf[kAttnWaves][G][HD];
   __shared__ float s_M[kAttnWaves][G], s_L[kAttnWaves][G];
 
   const int s = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int slot = lane / LPR, sub = lane % LPR, d0 = sub * E;
+  const int slot = lane / LPR, sub = lane % LPR, d0 = sub * kAttnLaneElems;
   int T = a.T;
   size_t kv_off = 0;
   const float* qrow = a.q;
@@ -68,58 +77,67 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   const int r0 = s * chunk, r1 = min(T, r0 + chunk);
   if (r0 >= T) return;  // a split past this row's context (batched rows are ragged)
   const bool direct = S == 1 && !a.batched;
-  const float scale = 1.0f / sqrtf(float(HD));
+  // scores in base 2: s * log2(e) / sqrt(hd), so every exponential is one exp2
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
   const KT* Kb = static_cast<const KT*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
   const KT* Vb = static_cast<const KT*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
 
-  // each lane group keeps the K/V of kDepth rows in flight: slot i of the ring
-  // holds row r + i * RPB and is refilled with the row kDepth strides ahead
-  // once consumed (rows are still visited in order, r, r + RPB, ...)
-  constexpr int kDepth = 4;
+  // ring of kDepth rows per lane group: slot i holds row r + i * RPB and is
+  // refilled with the row kDepth strides ahead once consumed (rows are visited
+  // in order r, r + RPB, ...)
   int r = r0 + wv * RPW + slot;
-  uint4 kw[kDepth], vw[kDepth];
+  uint4 kw[kDepth][NV], vw[kDepth][NV];
 #pragma unroll
   for (int i = 0; i < kDepth; ++i) {
-    kw[i] = make_uint4(0, 0, 0, 0);
-    vw[i] = kw[i];
     const int rr = r + i * RPB;
-    if (rr < r1) {
-      kw[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)rr * HD);
-      vw[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)rr * HD);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      kw[i][j] = make_uint4(0, 0, 0, 0);
+      vw[i][j] = kw[i][j];
+      if (rr < r1) {
+        kw[i][j] = reinterpret_cast<const uint4*>(Kb + (size_t)rr * HD)[j];
+        vw[i][j] = reinterpret_cast<const uint4*>(Vb + (size_t)rr * HD)[j];
+      }
     }
   }
-  float qv[G][E];
+  float qv[G][kAttnLaneElems];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < E; ++e) qv[g][e] = qrow[(size_t)(kvh * G + g) * HD + d0 + e];
-  float m[G], l[G], acc[G][E];
+    for (int e = 0; e < kAttnLaneElems; ++e) qv[g][e] = qrow[(size_t)(kvh * G + g) * HD + d0 + e];
+  float m[G], l[G], acc[G][kAttnLaneElems];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[g][e] = 0.f;
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = 0.f;
   }
   for (; r < r1; r += kDepth * RPB) {
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) {
       const int rr = r + i * RPB;
       if (rr >= r1) break;
-      float kf[E], vf[E];
-      KvVec<KT>::unpack(kw[i], kf);
-      KvVec<KT>::unpack(vw[i], vf);
+      float kf[kAttnLaneElems], vf[kAttnLaneElems];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        KvVec<KT>::unpack(kw[i][j], kf + j * E);
+        KvVec<KT>::unpack(vw[i][j], vf + j * E);
+      }
       const int nr = rr + kDepth * RPB;
       if (nr < r1) {
-        kw[i] = *reinterpret_cast<const uint4*>(Kb + (size_t)nr * HD);
-        vw[i] = *reinterpret_cast<const uint4*>(Vb + (size_t)nr * HD);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          kw[i][j] = reinterpret_cast<const uint4*>(Kb + (size_t)nr * HD)[j];
+          vw[i][j] = reinterpret_cast<const uint4*>(Vb + (size_t)nr * HD)[j];
+        }
       }
       float d[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float t = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) t = fmaf(kf[e], qv[g][e], t);
+        for (int e = 0; e < kAttnLaneElems; ++e) t = fmaf(kf[e], qv[g][e], t);
         d[g] = t;
       }
 #pragma unroll
@@ -128,14 +146,21 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
         for (int g = 0; g < G; ++g) d[g] += __shfl_xor(d[g], o, kWave);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        // m is a reference at most kRescale below the running maximum, not the
+        // maximum itself: (l, acc) are rescaled only when a score passes m by
+        // more than kRescale, so weights stay below 2^kRescale
         const float sc = d[g] * scale;
-        const float mn = fmaxf(m[g], sc);
-        const float fo = expf(m[g] - mn);  // 0 on the first row (m = -inf)
-        const float p = expf(sc - mn);
-        l[g] = fmaf(l[g], fo, p);
+        if (sc > m[g] + kRescale) {
+          const float fo = exp2f(m[g] - sc);  // 0 on the first row (m = -inf)
+          l[g] *= fo;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[g][e] = fmaf(acc[g][e], fo, p * vf[e]);
-        m[g] = mn;
+          for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
+          m[g] = sc;
+        }
+        const float p = exp2f(sc - m[g]);
+        l[g] += p;
+#pragma unroll
+        for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
       }
     }
   }
@@ -152,10 +177,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
     float Mb = s_M[0][g];
 #pragma unroll
     for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
-    const float f = (m[g] == -INFINITY) ? 0.f : expf(m[g] - Mb);
+    const float f = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - Mb);
     l[g] *= f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[g][e] *= f;
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= f;
   }
 #pragma unroll
   for (int o = LPR; o < 64; o <<= 1)
@@ -163,13 +188,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
     for (int g = 0; g < G; ++g) {
       l[g] += __shfl_xor(l[g], o, kWave);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, kWave);
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, kWave);
     }
   if (slot == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) obuf[wv][g][d0 + e] = acc[g][e];
+      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][d0 + e] = acc[g][e];
       if (sub == 0) s_L[wv][g] = l[g];
     }
   }
@@ -200,7 +225,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 }
 
 // One block of hd threads per query head: o = sum_s w_s o_s with
-// w_s = exp(m_s - M) / sum_z l_z exp(m_z - M).  Every load (the (m, l) pairs and
+// w_s = 2^(m_s - M) / sum_z l_z 2^(m_z - M) (m in base 2, M the largest m_s).  Every load (the (m, l) pairs and
 // this thread's column of the S partial outputs, kCombineRegs splits at a time)
 // is issued before any of them is used; the maximum and the weighted sum of l
 // are wave reductions, shared through LDS.
@@ -227,7 +252,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     }
     // weights of this group of splits: lane i of wave 0 computes split z0 + i
     if (wv == 0 && lane < cnt) {
-      const float e = expf(ml[2 * (z0 + lane)] - M);
+      const float e = exp2f(ml[2 * (z0 + lane)] - M);
       sw[lane] = e;
       Lsum = fmaf(e, ml[2 * (z0 + lane) + 1], Lsum);
     }
@@ -269,7 +294,7 @@ __global__ __launch_bounds__(128) void k_attn_combine_b(const float* __restrict_
   for (int k = 1; k < nw; ++k) M = fmaxf(M, red[k]);
   float L = 0.f, dummy = 0.f;
   for (int z = threadIdx.x; z < S; z += blockDim.x) {
-    const float e = expf(ml[2 * z] - M);
+    const float e = exp2f(ml[2 * z] - M);
     w[z] = e;
     L = fmaf(e, ml[2 * z + 1], L);
   }
@@ -294,8 +319,8 @@ __global__ __launch_bounds__(128) void k_attn_combine_b(const float* __restrict_
 }
 
 static inline int rows_per_block(int hd, int kv_f32) {
-  const int lpr = hd / (kv_f32 ? 4 : 8);
-  return kAttnWaves * (64 / lpr);
+  (void)kv_f32;
+  return kAttnWaves * (64 / (hd / kAttnLaneElems));
 }
 
 static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S) {
