@@ -351,9 +351,11 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   {  // small appends use split-K GEMV partials [splits][16][N]; large ones [splits][T][N]
     const size_t f_small = size_t(16) * n * size_t((3 * n + 511) / 512);
     const size_t p_small = size_t(16) * 2 * kvd * size_t((2 * n + 511) / 512);
-    // large appends: up to 8 K-split partials of the MFMA GEMMs
-    c->tf_F_cap = std::max(size_t(c->tf_rows) * n * 8, f_small);
-    c->tf_P_cap = std::max(size_t(c->tf_rows) * 2 * kvd * 8, p_small);
+    // MFMA appends: up to 4 K-split partials of a long pass, 16 of a short one
+    // (<= 256 rows)
+    const size_t big = std::max(size_t(c->tf_rows) * 4, size_t(256) * 16);
+    c->tf_F_cap = std::max(big * n, f_small);
+    c->tf_P_cap = std::max(big * 2 * kvd, p_small);
   }
   E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
   E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));

@@ -16,32 +16,42 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
+// grid (ceil(3n / 2048), T): 8 consecutive values per thread (they stay within one
+// tap since n % 8 == 0), two 16-byte stores per plane
 __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
                                                   const float* __restrict__ a1,
                                                   const float* __restrict__ a2, int T, int n,
                                                   uint16_t* __restrict__ A_hi,
                                                   uint16_t* __restrict__ A_lo) {
-  const size_t total = (size_t)T * 3 * n;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const size_t t = i / (3 * n);
-    const int c = int(i - t * 3 * n);
-    const int j = c / n, k = c - j * n;
-    const float* src = j == 0 ? a0 : (j == 1 ? a1 : a2);
-    const float v = src[t * n + k];
-    const uint16_t h = f32_to_bf16(v);
-    A_hi[i] = h;
-    if (A_lo) A_lo[i] = f32_to_bf16(v - bf16_to_f32(h));
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (t >= T || c >= 3 * n) return;
+  const int j = c / n, k = c - j * n;
+  const float4* src = reinterpret_cast<const float4*>((j == 0 ? a0 : (j == 1 ? a1 : a2)) + (size_t)t * n + k);
+  const float4 v0 = src[0], v1 = src[1];
+  const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16(v[e]);
+    l[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
   }
+  const size_t at = (size_t)t * 3 * n + c;
+  *reinterpret_cast<uint4*>(A_hi + at) =
+      make_uint4(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16),
+                 uint32_t(h[4]) | (uint32_t(h[5]) << 16), uint32_t(h[6]) | (uint32_t(h[7]) << 16));
+  if (A_lo)
+    *reinterpret_cast<uint4*>(A_lo + at) =
+        make_uint4(uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16),
+                   uint32_t(l[4]) | (uint32_t(l[5]) << 16), uint32_t(l[6]) | (uint32_t(l[7]) << 16));
 }
 
 hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
                            uint16_t* A_hi, uint16_t* A_lo, hipStream_t s) {
-  const size_t total = (size_t)T * 3 * n;
-  int blocks = int((total + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_pack_aux, dim3(blocks), dim3(256), 0, s, a0, a1, a2, T, n, A_hi, A_lo);
+  if (T <= 0) return hipSuccess;
+  if ((n & 7) || T > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pack_aux, dim3((3 * n + 2047) / 2048, T), dim3(256), 0, s, a0, a1, a2, T, n,
+                     A_hi, A_lo);
   return hipGetLastError();
 }
 
@@ -419,15 +429,18 @@ constexpr int kBKSplit = 32, kBKPlain = 64;
 static int gemm_bm(int M) { return M >= 256 ? 256 : 128; }
 
 int gemm_pick_splits(int M, int N, int K) {
-  // K splits s in {1, 2, 4} (each keeping whole 64-wide K tiles): the blocks run in
-  // ceil(tiles s / 256) rounds of 1/s of the work each, so take the s with the
-  // fewest rounds per unit of work (the smaller s on ties); more splits would add
-  // M x N fp32 partials per split to write and sum
+  // K splits s (powers of two, each keeping whole 64-wide K tiles): the blocks run
+  // in ceil(tiles s / 256) rounds of 1/s of the work each, so take the s with the
+  // fewest rounds per unit of work (the smaller s on ties).  Every split adds an
+  // M x N fp32 partial to write and sum: up to 4 splits for long appends, up to 16
+  // for short ones (<= 256 rows), whose few tiles would leave most CUs idle and
+  // whose partials are small next to the weights they stream
   const int bm = gemm_bm(M);
   const int tiles = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
+  const int max_sp = M <= 256 ? 16 : 4;
   int best = 1;
   double best_cost = 1e30;
-  for (int sp = 1; sp <= 4; sp *= 2) {
+  for (int sp = 1; sp <= max_sp; sp *= 2) {
     if (K % (kBKPlain * sp) != 0) continue;
     const double cost = double((tiles * sp + 255) / 256) / sp;
     if (cost < best_cost - 1e-9) {
