@@ -81,6 +81,16 @@ def kernel_bytes(cfg, kernel: str, L: int, kv_bytes: int = 4) -> float:
     raise KeyError(kernel)
 
 
+def kernel_bytes_step(cfg, L: int, gamma: int, kv_bytes: int = 4) -> float:
+    """Algorithmic HBM bytes of an average draft step of a round over L committed
+    rows: the step's weights, norms, the embedding row, the K/V rows it reads
+    (L + j + 1 at step j) and the row it writes."""
+    n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
+    p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
+    rows = L + 1 + (gamma - 1) / 2 + 1
+    return 2.0 * p_step + 8 * n + 2 * n + rows * 2 * kv_bytes * kvd
+
+
 def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4) -> float:
     """Algorithmic HBM bytes of one round: encode, gamma draft steps, rebuild (K/V
     elements of kv_bytes bytes)."""
@@ -199,6 +209,33 @@ def main():
     k_ms, k_launches = B.eagle3_profile_read(dr.ctx)
     B.eagle3_profile_enable(dr.ctx, args.kernel, False)
 
+    # round-time distribution and the chain alone (events around every step and
+    # every draft_chain call, in a pass of its own), then the encode kernel's time
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for k, i in enumerate(range(args.warmup, nsteps)):
+        e0, e1, e2 = ev[k]
+        e0.record(stream)
+        dr.draft_chain([0], b_tok[i:i + 1], [a[i:i + 1] for a in b_aux], gamma, out=out)
+        e1.record(stream)
+        a = accepted[i]
+        r0 = i * (gamma + 1)
+        dr.rebuild_after_verify([0], [a], r_tok[r0:r0 + a + 1], [x[r0:r0 + a + 1] for x in r_aux])
+        dr.rewind(0, L)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    round_ms = sorted(e0.elapsed_time(e2) for e0, _, e2 in ev)
+    chain_ms = sorted(e0.elapsed_time(e1) for e0, e1, _ in ev)
+    pct = lambda v, q: v[min(len(v) - 1, int(q * len(v)))]
+    B.eagle3_profile_enable(dr.ctx, "encode", True)
+    for i in range(args.warmup, nsteps):
+        step(i)
+    torch.cuda.synchronize()
+    enc_ms, enc_n = B.eagle3_profile_read(dr.ctx)
+    B.eagle3_profile_enable(dr.ctx, "encode", False)
+    encode_us = enc_ms * 1e3 / max(enc_n, 1)
+    per_step_us = (pct(chain_ms, 0.5) * 1e3 - encode_us) / gamma
+
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = gamma * args.steps / elapsed
     k_avg_s = (k_ms / 1e3) / max(k_launches, 1)
@@ -236,6 +273,13 @@ def main():
                      "launches": k_launches, "bytes_per_launch": k_bytes},
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "round_ms": {"p10": round(pct(round_ms, 0.1), 4), "p50": round(pct(round_ms, 0.5), 4),
+                     "p90": round(pct(round_ms, 0.9), 4)},
+        "chain_ms_p50": round(pct(chain_ms, 0.5), 4),
+        "encode_us": round(encode_us, 2),
+        "draft_step_us": round(per_step_us, 2),
+        "draft_step_hbm_frac": round(kernel_bytes_step(cfg, L, gamma, kvb) / (per_step_us * 1e-6) / 1e9
+                                     / HBM_PEAK_GBS, 4),
         "prefill": {"rows": L, "ms": round(prefill_s * 1e3, 3),
                     "tflops": round(prefill_flop / prefill_s / 1e12, 2)},
         "cpu_baseline": cpu,
