@@ -82,27 +82,67 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-// Argmax over `count` (value, index) candidates; every thread gets the result.
-__device__ __forceinline__ int block_argmax(const float* __restrict__ pv,
-                                            const int32_t* __restrict__ pi, int count,
-                                            float* sv, int* si) {
+constexpr int kArgmaxBatch = 8;  // candidate loads per thread in flight together
+
+// Argmax over `count` (value, index) candidates, the lower index winning a tie;
+// every thread gets the winning index.  When pt is given, pt[c] is a value
+// carried with candidate c and *tok receives the winner's.  Each thread's
+// candidates are loaded kArgmaxBatch at a time, so a block of T threads covers
+// kArgmaxBatch * T candidates per memory round trip.  sv/si/st: LDS, one slot
+// per wave (st only read when pt is given).
+__device__ __forceinline__ int block_argmax_carry(const float* __restrict__ pv,
+                                                  const int32_t* __restrict__ pi,
+                                                  const int32_t* __restrict__ pt, int count,
+                                                  float* sv, int* si, int* st, int* tok) {
   float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  for (int b = threadIdx.x; b < count; b += blockDim.x) {
-    const float v = pv[b];
-    const int i = pi[b];
-    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  int bi = 0x7FFFFFFF, bt = 0;
+  for (int b0 = 0; b0 < count; b0 += kArgmaxBatch * int(blockDim.x)) {
+    float v[kArgmaxBatch];
+    int ix[kArgmaxBatch], t[kArgmaxBatch];
+#pragma unroll
+    for (int j = 0; j < kArgmaxBatch; ++j) {
+      const int b = b0 + int(threadIdx.x) + j * int(blockDim.x);
+      const bool in = b < count;
+      v[j] = in ? pv[b] : -INFINITY;
+      ix[j] = in ? pi[b] : 0x7FFFFFFF;
+      t[j] = (in && pt) ? pt[b] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kArgmaxBatch; ++j)
+      if (better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; bt = t[j]; }
   }
-  wave_argmax(bv, bi);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, kWave);
+    const int oi = __shfl_xor(bi, o, kWave);
+    const int ot = __shfl_xor(bt, o, kWave);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bt = ot; }
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  if (lane == 0) { sv[w] = bv; si[w] = bi; }
+  if (lane == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+    if (pt) st[w] = bt;
+  }
   __syncthreads();
   bv = sv[0];
   bi = si[0];
+  if (pt) bt = st[0];
   for (int k = 1; k < nw; ++k)
-    if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
+    if (better(sv[k], si[k], bv, bi)) {
+      bv = sv[k];
+      bi = si[k];
+      if (pt) bt = st[k];
+    }
   __syncthreads();
+  if (tok) *tok = bt;
   return bi;
+}
+
+__device__ __forceinline__ int block_argmax(const float* __restrict__ pv,
+                                            const int32_t* __restrict__ pi, int count,
+                                            float* sv, int* si) {
+  return block_argmax_carry(pv, pi, nullptr, count, sv, si, nullptr, nullptr);
 }
 
 // cos/sin of pos * inv_freq, the angle reduced modulo 2*pi in double first

@@ -72,7 +72,7 @@ struct eagle3_ctx {
   float *x1 = nullptr, *x1w = nullptr, *x1_ssq = nullptr, *act = nullptr, *q = nullptr,
         *ao = nullptr, *part_o = nullptr, *part_ml = nullptr, *lm_pv = nullptr;
   int x1_count = 0;
-  int32_t *lm_pi = nullptr, *tok_slots = nullptr;
+  int32_t *lm_pi = nullptr, *lm_pt = nullptr, *tok_slots = nullptr;
 
   int tf_rows = 0;
   size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
@@ -344,6 +344,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->x1_ssq, size_t(c->x1_count)));
   E3_TRY(dalloc(c, &c->lm_pv, size_t(c->lm_grid)));
   E3_TRY(dalloc(c, &c->lm_pi, size_t(c->lm_grid)));
+  E3_TRY(dalloc(c, &c->lm_pt, size_t(c->lm_grid)));
   E3_TRY(dalloc(c, &c->tok_slots, size_t(cfg->max_gamma) + 1));
   E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
 
@@ -858,7 +859,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
         qa.prev_count = 0;
       } else {
         qa.prev_val = ctx->lm_pv; qa.prev_idx = ctx->lm_pi; qa.prev_count = ctx->lm_grid;
-        qa.d2t = ctx->d2t; qa.dv = ctx->dv;
+        qa.d2t = ctx->d2t; qa.dv = ctx->dv; qa.prev_tok = ctx->lm_pt;
         qa.prev_out_id = out_b + (j - 1); qa.tok_store = ctx->tok_slots + (j - 1);
       }
       qa.gw = g->w_hid; qa.g_ssq = g->ssq; qa.g_ssq_count = g->count;
@@ -901,6 +902,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       la.h_ssq_count = gn->count; la.eps = ctx->cfg.rms_eps;
       la.logits_dbg = (dbg && dbg->logits) ? dbg->logits + (size_t(b) * gamma + j) * ctx->dv : nullptr;
       la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;
+      la.d2t = ctx->d2t; la.part_tok = ctx->lm_pt;
       {
         ProfScope ps(ctx, 0, s);
         E3_HIP(ctx, e3::launch_lmhead(la, ctx->gcfg[e3::kGemvLmHead], s), "lm_head");
@@ -910,8 +912,8 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
                                    size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
       g = gn;
     }
-    E3_HIP(ctx, e3::launch_argmax_finalize(ctx->lm_pv, ctx->lm_pi, ctx->lm_grid, ctx->d2t, ctx->dv,
-                                           out_b + (ge - 1), ctx->tok_slots + (ge - 1), s),
+    E3_HIP(ctx, e3::launch_argmax_finalize(ctx->lm_pv, ctx->lm_pi, ctx->lm_pt, ctx->lm_grid, ctx->d2t,
+                                           ctx->dv, out_b + (ge - 1), ctx->tok_slots + (ge - 1), s),
            "argmax");
   }
   for (int b = 0; b < n_seq; ++b)

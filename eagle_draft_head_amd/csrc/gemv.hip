@@ -210,7 +210,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   extern __shared__ float xs[];  // [0, n): embedding half; [n, 2n): hidden half
   __shared__ float red[32];
   __shared__ float sv[16];
-  __shared__ int si[16];
+  __shared__ int si[16], st[16];
   const int n = a.n;
   const int hd = a.head_dim;
   const int qd = a.n_head * hd, kvd = a.n_head_kv * hd;
@@ -229,10 +229,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   float sg = sum_partials(a.g_ssq, a.g_ssq_count);
   int tok;
   if (a.prev_count > 0) {
-    // finish the previous step: argmax over the lm_head candidates, d2t
-    int bi = block_argmax(a.prev_val, a.prev_idx, a.prev_count, sv, si);
-    if (bi < 0 || bi >= a.dv) bi = 0;  // only reachable with NaN logits
-    tok = bi + a.d2t[bi];
+    // finish the previous step: argmax over the lm_head candidates, d2t (the
+    // candidates' target ids come with them when prev_tok is given)
+    int bt;
+    int bi = block_argmax_carry(a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, sv, si, st, &bt);
+    if (bi < 0 || bi >= a.dv) tok = a.d2t[0];  // only reachable with NaN logits
+    else tok = a.prev_tok ? bt : bi + a.d2t[bi];
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       *a.prev_out_id = tok;
       *a.tok_store = tok;
@@ -380,9 +382,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
   extern __shared__ float xs[];
   __shared__ float red[32];
   __shared__ float bv_s[16];
-  __shared__ int bi_s[16];
+  __shared__ int bi_s[16], bt_s[16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
+  // d2t of this wave's rows (lane r holds row0 + r's), loaded before the stream
+  const int dt = (a.d2t && lane < R && row0 + lane < a.dv) ? a.d2t[row0 + lane] : 0;
   stage_plain(xs, a.hw, a.n);
   float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
   __syncthreads();
@@ -391,38 +395,44 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
   block_sum2(ss, dummy, red);
   const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
   float bv = -INFINITY;
-  int bi = 0x7FFFFFFF;
+  int bi = 0x7FFFFFFF, br = 0;
   if (row0 < a.dv) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (row0 + r < a.dv) {
         const float v = acc[r] * inv;
-        if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; }
+        if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; br = r; }
         if (a.logits_dbg && lane == r) a.logits_dbg[row0 + r] = v;
       }
     }
   }
-  if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; }
+  int bt = bi + __shfl(dt, br, kWave);
+  if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; bt_s[wv] = bt; }
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < WAVES; ++w)
-      if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; }
+      if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; bt = bt_s[w]; }
     a.part_val[blockIdx.x] = bv;
     a.part_idx[blockIdx.x] = bi;
+    if (a.d2t) a.part_tok[blockIdx.x] = bt;
   }
 }
 
-// the last step of a chain: argmax over the lm_head candidates, d2t
+// the last step of a chain: argmax over the lm_head candidates, d2t (the
+// candidates' target ids come with them when pt is given)
 __global__ __launch_bounds__(256) void k_argmax_finalize(const float* __restrict__ pv,
-                                                         const int32_t* __restrict__ pi, int count,
+                                                         const int32_t* __restrict__ pi,
+                                                         const int32_t* __restrict__ pt, int count,
                                                          const int32_t* __restrict__ d2t, int dv,
                                                          int32_t* out_id, int32_t* tok_store) {
   __shared__ float sv[16];
-  __shared__ int si[16];
-  int bi = block_argmax(pv, pi, count, sv, si);
+  __shared__ int si[16], st[16];
+  int bt;
+  const int bi = block_argmax_carry(pv, pi, pt, count, sv, si, st, &bt);
   if (threadIdx.x == 0) {
-    if (bi < 0 || bi >= dv) bi = 0;
-    const int t = bi + d2t[bi];
+    int t;
+    if (bi < 0 || bi >= dv) t = d2t[0];  // only reachable with NaN logits
+    else t = pt ? bt : bi + d2t[bi];
     *out_id = t;
     if (tok_store) *tok_store = t;
   }
@@ -600,9 +610,10 @@ hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, int count, const int32_t* d2t,
-                                  int dv, int32_t* out_id, int32_t* tok_store, hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(256), 0, s, pv, pi, count, d2t, dv, out_id,
+hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, const int32_t* pt, int count,
+                                  const int32_t* d2t, int dv, int32_t* out_id, int32_t* tok_store,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(256), 0, s, pv, pi, pt, count, d2t, dv, out_id,
                      tok_store);
   return hipGetLastError();
 }

@@ -47,6 +47,7 @@ struct QkvArgs {
   int prev_count;
   const int32_t* d2t;
   int dv;
+  const int32_t* prev_tok;  // [prev_count] target id of each candidate (i + d2t[i]), or NULL
   int32_t* prev_out_id;
   int32_t* tok_store;
   const float* gw;         // recurrent hidden times hidden_norm
@@ -74,7 +75,8 @@ hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* xw,
 
 // logits = lm_head . (hw / rms) with hw = h * w_norm and the rms from per-block
 // partial sums of h^2; each block stores its best (value, index) (lowest index on
-// ties).  logits_dbg may be NULL.
+// ties) and, when d2t is given, that index's target id i + d2t[i].  logits_dbg
+// may be NULL.
 struct LmHeadArgs {
   const uint16_t* w_lm;
   int dv, n;
@@ -83,14 +85,18 @@ struct LmHeadArgs {
   int h_ssq_count;
   float eps;
   float* logits_dbg;
-  float* part_val;      // [grid]
-  int32_t* part_idx;    // [grid]
+  float* part_val;         // [grid]
+  int32_t* part_idx;       // [grid]
+  const int32_t* d2t;      // [dv] or NULL
+  int32_t* part_tok;       // [grid] (written when d2t is given)
 };
 int lmhead_grid(int dv, int cfg);
 hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s);
-// argmax over the candidates, target = i + d2t[i] -> *out_id (and *tok_store if set)
-hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, int count, const int32_t* d2t,
-                                  int dv, int32_t* out_id, int32_t* tok_store, hipStream_t s);
+// argmax over the candidates, target = i + d2t[i] (taken from pt when given)
+// -> *out_id (and *tok_store if set)
+hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, const int32_t* pt, int count,
+                                  const int32_t* d2t, int dv, int32_t* out_id, int32_t* tok_store,
+                                  hipStream_t s);
 
 // Multi-vector split-K GEMV for teacher-forced rows: P[z][m][r] (fp32) over K chunks z.
 // Input: three fp32 streams x0|x1|x2 of row length seg concatenated along K, or (x1 ==
