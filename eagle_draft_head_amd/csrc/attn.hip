@@ -225,11 +225,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 }
 
 // One block of hd threads per query head: o = sum_s w_s o_s with
-// w_s = 2^(m_s - M) / sum_z l_z 2^(m_z - M) (m in base 2, M the largest m_s).  Every load (the (m, l) pairs and
-// this thread's column of the S partial outputs, kCombineRegs splits at a time)
-// is issued before any of them is used; the maximum and the weighted sum of l
-// are wave reductions, shared through LDS.
-constexpr int kCombineRegs = 32;
+// w_s = 2^(m_s - M) / sum_z l_z 2^(m_z - M) (m in base 2, M the largest m_s).
+// Splits are taken kCombineRegs at a time: this thread's column of the group's
+// partial outputs and (wave 0, lane z) split z's (m, l) are loaded together, so
+// up to kCombineRegs splits cost one memory round trip; the maximum and the
+// weighted sum of l are wave reductions, the weights shared through LDS.
+constexpr int kCombineRegs = 64;
 
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int S,
@@ -246,15 +247,22 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     float o[kCombineRegs];
 #pragma unroll
     for (int i = 0; i < kCombineRegs; ++i) o[i] = i < cnt ? po[(size_t)(z0 + i) * hd] : 0.f;
-    if (z0 == 0) {  // the maximum over all splits (loads queued behind the first group)
-      for (int z = lane; z < S; z += 64) M = fmaxf(M, ml[2 * z]);
-      M = wave_max(M);
-    }
-    // weights of this group of splits: lane i of wave 0 computes split z0 + i
+    float mz = -INFINITY, lz = 0.f;
     if (wv == 0 && lane < cnt) {
-      const float e = exp2f(ml[2 * (z0 + lane)] - M);
-      sw[lane] = e;
-      Lsum = fmaf(e, ml[2 * (z0 + lane) + 1], Lsum);
+      mz = ml[2 * (z0 + lane)];
+      lz = ml[2 * (z0 + lane) + 1];
+    }
+    if (wv == 0) {
+      if (z0 == 0) {  // the maximum over all splits
+        float mm = mz;
+        for (int z = kCombineRegs + lane; z < S; z += 64) mm = fmaxf(mm, ml[2 * z]);
+        M = wave_max(mm);
+      }
+      if (lane < cnt) {
+        const float e = exp2f(mz - M);
+        sw[lane] = e;
+        Lsum = fmaf(e, lz, Lsum);
+      }
     }
     __syncthreads();
 #pragma unroll

@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -113,6 +114,36 @@ int set_err(eagle3_ctx* c, int code, const std::string& msg) {
 int hip_fail(eagle3_ctx* c, hipError_t e, const char* what) {
   std::string m = std::string(what) + ": " + hipGetErrorString(e);
   return set_err(c, e == hipErrorOutOfMemory ? EAGLE3_E_OOM : EAGLE3_E_HIP, m);
+}
+
+// Launch-configuration override of the batch-1 GEMV kernels, for tuning on new
+// shapes: EAGLE3_GEMV_CONFIG="qkv=8,o=5,..." (kinds encode, qkv, o, gateup,
+// down, lmhead; ids index E3_GEMV_CONFIGS).  The fused qkv and gate/up kernels
+// need an even row count per wave.
+int gemv_config_override(eagle3_ctx* c) {
+  const char* env = std::getenv("EAGLE3_GEMV_CONFIG");
+  if (!env || !*env) return EAGLE3_OK;
+  static const char* names[e3::kGemvKinds] = {"encode", "qkv", "o", "gateup", "down", "lmhead"};
+  std::string spec(env);
+  size_t at = 0;
+  while (at < spec.size()) {
+    size_t end = spec.find(',', at);
+    if (end == std::string::npos) end = spec.size();
+    const std::string item = spec.substr(at, end - at);
+    at = end + 1;
+    const size_t eq = item.find('=');
+    int kind = -1;
+    for (int k = 0; k < e3::kGemvKinds && eq != std::string::npos; ++k)
+      if (item.compare(0, eq, names[k]) == 0 && std::strlen(names[k]) == eq) kind = k;
+    char* tail = nullptr;
+    const long id = eq == std::string::npos ? -1 : std::strtol(item.c_str() + eq + 1, &tail, 10);
+    const int rows = (id >= 0 && id < e3::kGemvConfigCount) ? e3::gemv_cfg_rows(int(id)) : -1;
+    const bool paired = kind == e3::kGemvQkv || kind == e3::kGemvGateUp;
+    if (kind < 0 || rows < 0 || (tail && *tail) || (paired && rows % 2))
+      return set_err(c, EAGLE3_E_INVAL, "EAGLE3_GEMV_CONFIG: bad item '" + item + "'");
+    c->gcfg[kind] = int(id);
+  }
+  return EAGLE3_OK;
 }
 
 #define E3_HIP(ctx, expr, what)                    \
@@ -331,6 +362,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   c->gcfg[e3::kGemvGateUp] = e3::gemv_pick(e3::kGemvGateUp, int(2 * ff), int(n));
   c->gcfg[e3::kGemvDown] = e3::gemv_pick(e3::kGemvDown, int(n), int(ff));
   c->gcfg[e3::kGemvLmHead] = e3::gemv_pick(e3::kGemvLmHead, int(dv), int(n));
+  E3_TRY(gemv_config_override(c));
   c->lm_grid = e3::lmhead_grid(int(dv), c->gcfg[e3::kGemvLmHead]);
   for (int i = 0; i < 3; ++i) {
     eagle3_ctx::GBuf& b = c->gb[i];
@@ -559,24 +591,26 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       // MFMA path
       E3_HIP(c, e3::launch_pack_aux(a0 + size_t(c0) * n, a1 + size_t(c0) * n, a2 + size_t(c0) * n,
                                     T, n, c->tf_A, c->tf_A_lo, s), "pack aux");
-      sp1 = e3::gemm_pick_splits(T, n, 3 * n);
-      while (sp1 > 1 && (size_t(sp1) * T * n > c->tf_F_cap || (3 * n) % (64 * sp1))) --sp1;
+      e3::GemmPlan p1 = e3::gemm_plan(T, n, 3 * n);
+      while (p1.splits > 1 && size_t(p1.splits) * T * n > c->tf_F_cap) p1.splits /= 2;
+      sp1 = p1.splits;
       {
         ProfScope ps(c, 7, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, T, n,
-                                       3 * n, sp1, s), "fc gemm");
+                                       3 * n, p1, s), "fc gemm");
       }
       f_split = size_t(T) * n;
       E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
                                   c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s),
              "tf cat");
-      sp2 = e3::gemm_pick_splits(T, kvd2, 2 * n);
-      while (sp2 > 1 && (size_t(sp2) * T * kvd2 > c->tf_P_cap || (2 * n) % (64 * sp2))) --sp2;
+      e3::GemmPlan p2 = e3::gemm_plan(T, kvd2, 2 * n);
+      while (p2.splits > 1 && size_t(p2.splits) * T * kvd2 > c->tf_P_cap) p2.splits /= 2;
+      sp2 = p2.splits;
       {
         ProfScope ps(c, 8, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n,
                                        c->w_qkv + size_t(c->qd) * 2 * n, 2 * n, c->tf_P, T, kvd2,
-                                       2 * n, sp2, s), "kv gemm");
+                                       2 * n, p2, s), "kv gemm");
       }
       p_split = size_t(T) * kvd2;
     }

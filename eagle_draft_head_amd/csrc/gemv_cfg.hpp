@@ -17,6 +17,21 @@
 
 namespace e3 {
 
+constexpr int kGemvConfigCount = 10;
+
+// rows per wave of a configuration (-1: no such configuration)
+inline int gemv_cfg_rows(int cfg) {
+  switch (cfg) {
+#define E3_CFG_ROWS(ID, WV, RR, UU) \
+  case ID:                          \
+    return RR;
+    E3_GEMV_CONFIGS(E3_CFG_ROWS)
+#undef E3_CFG_ROWS
+    default:
+      return -1;
+  }
+}
+
 enum GemvKind { kGemvEncode = 0, kGemvQkv, kGemvO, kGemvGateUp, kGemvDown, kGemvLmHead, kGemvKinds };
 
 // tuned choice per kind (rows/K of the drafter shapes)

@@ -289,10 +289,16 @@ hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const Sto
 
 // C[z][M][N] (fp32) = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T on bf16 MFMA
 // (A_lo may be NULL: one product).  Row strides lda, ldb (elements); K split
-// evenly over `splits`.
+// evenly over plan.splits.  The plan's tile width is 256 or 320 columns for
+// 256-row tiles (M >= 256) and 128 for 128-row tiles.
+struct GemmPlan {
+  int bn;      // output tile width
+  int splits;  // K split (z planes of C)
+};
+GemmPlan gemm_plan(int M, int N, int K);
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
-                            int ldb, float* C, int M, int N, int K, int splits, hipStream_t s);
-int gemm_pick_splits(int M, int N, int K);
+                            int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
+                            hipStream_t s);
 
 // ---- load-time and bookkeeping helpers ----
 // dst row dst_rows[i] = src row src_rows[i] (bf16 rows of row_len elements)

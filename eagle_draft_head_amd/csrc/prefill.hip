@@ -425,27 +425,34 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(
 // K tile: 32 with split activations (three stages fit), 64 otherwise (two stages)
 constexpr int kBKSplit = 32, kBKPlain = 64;
 
-// 256 x 256 blocks once there are 256 rows, 128 x 128 below
+// 256-row tiles once there are 256 rows (256 or 320 columns), 128 x 128 below
 static int gemm_bm(int M) { return M >= 256 ? 256 : 128; }
 
-int gemm_pick_splits(int M, int N, int K) {
-  // K splits s (powers of two, each keeping whole 64-wide K tiles): the blocks run
-  // in ceil(tiles s / 256) rounds of 1/s of the work each, so take the s with the
-  // fewest rounds per unit of work (the smaller s on ties).  Every split adds an
-  // M x N fp32 partial to write and sum: up to 4 splits for long appends, up to 16
-  // for short ones (<= 256 rows), whose few tiles would leave most CUs idle and
-  // whose partials are small next to the weights they stream
+GemmPlan gemm_plan(int M, int N, int K) {
+  // Candidates: tile width bn and K split s (a power of two keeping whole 64-wide
+  // K tiles).  The blocks run in ceil(tiles s / 256) rounds, each block doing
+  // bn * K / s of work (per tile row), so the cost is rounds * bn / s; ties go
+  // to the smaller s.  Every split adds an M x N fp32 partial to write and sum:
+  // up to 4 splits for long appends, up to 16 for short ones (<= 256 rows), whose
+  // few tiles would leave most CUs idle and whose partials are small next to the
+  // weights they stream.  The 320-wide tile exists for widths that 256 tiles
+  // cover in a count just past a multiple of 256 (5120 columns at 2048 rows:
+  // 160 tiles of 256, but 128 of 320, two K halves filling every CU once).
   const int bm = gemm_bm(M);
-  const int tiles = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
   const int max_sp = M <= 256 ? 16 : 4;
-  int best = 1;
+  GemmPlan best{bm, 1};
   double best_cost = 1e30;
-  for (int sp = 1; sp <= max_sp; sp *= 2) {
-    if (K % (kBKPlain * sp) != 0) continue;
-    const double cost = double((tiles * sp + 255) / 256) / sp;
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = sp;
+  const int widths[2] = {bm, 320};
+  for (int w = 0; w < (bm == 256 ? 2 : 1); ++w) {
+    const int bn = widths[w];
+    const long long tiles = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    for (int sp = 1; sp <= max_sp; sp *= 2) {
+      if (K % (kBKPlain * sp) != 0) continue;
+      const double cost = double((tiles * sp + 255) / 256) * bn / sp;
+      if (cost < best_cost * (1 - 1e-9)) {
+        best_cost = cost;
+        best = GemmPlan{bn, sp};
+      }
     }
   }
   return best;
@@ -474,16 +481,23 @@ static hipError_t launch_tiles(const uint16_t* A_hi, const uint16_t* A_lo, int l
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
-                            int ldb, float* C, int M, int N, int K, int splits, hipStream_t s) {
+                            int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
+                            hipStream_t s) {
+  const int splits = plan.splits;
   if (M <= 0 || N <= 0 || splits < 1 || K % (kBKPlain * splits) != 0 || (lda & 7) || (ldb & 7))
     return hipErrorInvalidValue;
   const int kper = K / splits;
-  const bool big = gemm_bm(M) == 256;
+  const int bm = gemm_bm(M);
+  if (bm == 256 && plan.bn == 320) {
+    if (A_lo) return launch_tiles<256, 320, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    return launch_tiles<256, 320, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  }
+  if (plan.bn != bm) return hipErrorInvalidValue;
   if (A_lo) {
-    if (big) return launch_tiles<256, 256, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    if (bm == 256) return launch_tiles<256, 256, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
     return launch_tiles<128, 128, 2, 2, true, kBKSplit, 4>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
   }
-  if (big) return launch_tiles<256, 256, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  if (bm == 256) return launch_tiles<256, 256, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
   return launch_tiles<128, 128, 2, 2, false, kBKPlain, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
 }
 
