@@ -141,9 +141,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
         d[g] = t;
       }
 #pragma unroll
-      for (int o = LPR / 2; o > 0; o >>= 1)
-#pragma unroll
-        for (int g = 0; g < G; ++g) d[g] += __shfl_xor(d[g], o, kWave);
+      for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         // m is a reference at most kRescale below the running maximum, not the

@@ -55,6 +55,32 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// DPP lane moves (VALU, no LDS): control codes of the gfx9 encoding
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane i <- i ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8-lane half row
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16-lane row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each aligned group of L consecutive lanes (L a power of two up to 64);
+// every lane of a group gets the same bits (each step adds a lane's value to its
+// partner's, the partner adding the same two values).  Up to 16 lanes in DPP moves.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "power-of-two lane group");
+  if constexpr (L >= 2) v += dpp_move<kDppQuadSwap1>(v);
+  if constexpr (L >= 4) v += dpp_move<kDppQuadSwap2>(v);
+  if constexpr (L >= 8) v += dpp_move<kDppHalfMirror>(v);
+  if constexpr (L >= 16) v += dpp_move<kDppMirror>(v);
+  if constexpr (L >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
 // sum over the block of two values; `red` is LDS with room for 2 * waves floats.
 // Every thread gets the totals.
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
