@@ -475,6 +475,75 @@ hipError_t launch_bact(const float* P, int S, int n_ff, int m, uint16_t* Xhi, ui
 }
 
 // ---------------------------------------------------------------------------
+// grid (bcand_count(N), m): a block sums the split-K partials of kBCandCols columns
+// of one row, eight columns per thread, each split's loads in flight together
+constexpr int kBCandPerThread = kBCandCols / 256;
+
+__global__ __launch_bounds__(256) void k_bcand(const float* __restrict__ P, int S, int N,
+                                               float* __restrict__ cand_v,
+                                               int32_t* __restrict__ cand_i,
+                                               float* __restrict__ logits) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int r = blockIdx.y, c0 = blockIdx.x * kBCandCols + threadIdx.x;
+  float v[kBCandPerThread];
+#pragma unroll
+  for (int j = 0; j < kBCandPerThread; ++j) v[j] = 0.f;
+  // two splits per round trip (the loads of both go out before either is added)
+  int z = 0;
+  for (; z + 1 < S; z += 2) {
+    const float* p0 = P + ((size_t)z * kBatchRows + r) * N;
+    const float* p1 = p0 + (size_t)kBatchRows * N;
+    float a[kBCandPerThread], b[kBCandPerThread];
+#pragma unroll
+    for (int j = 0; j < kBCandPerThread; ++j) {
+      const int c = c0 + 256 * j;
+      a[j] = c < N ? p0[c] : 0.f;
+      b[j] = c < N ? p1[c] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBCandPerThread; ++j) v[j] += a[j] + b[j];
+  }
+  if (z < S) {
+    const float* pz = P + ((size_t)z * kBatchRows + r) * N;
+#pragma unroll
+    for (int j = 0; j < kBCandPerThread; ++j) {
+      const int c = c0 + 256 * j;
+      if (c < N) v[j] += pz[c];
+    }
+  }
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+#pragma unroll
+  for (int j = 0; j < kBCandPerThread; ++j) {
+    const int c = c0 + 256 * j;
+    if (c < N) {
+      if (logits) logits[(size_t)r * N + c] = v[j];
+      if (better(v[j], c, bv, bi)) { bv = v[j]; bi = c; }
+    }
+  }
+  wave_argmax(bv, bi);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k)
+      if (better(sv[k], si[k], bv, bi)) { bv = sv[k]; bi = si[k]; }
+    const size_t at = (size_t)r * gridDim.x + blockIdx.x;
+    cand_v[at] = bv;
+    cand_i[at] = bi;
+  }
+}
+
+hipError_t launch_bcand(const float* P, int S, int N, int m, float* cand_v, int32_t* cand_i,
+                        float* logits, hipStream_t s) {
+  if (m < 1 || m > kBatchRows || S < 1 || N < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bcand, dim3(bcand_count(N), m), dim3(256), 0, s, P, S, N, cand_v, cand_i,
+                     logits);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bfinal(const BatchRows br, int gamma,
                                                 const float* __restrict__ cand_v,
                                                 const int32_t* __restrict__ cand_i, int ncand,

@@ -91,6 +91,10 @@ struct eagle3_ctx {
   uint16_t *bx_z_hi = nullptr, *bx_z_lo = nullptr, *bx_h_hi = nullptr, *bx_h_lo = nullptr;
   int32_t* b_cand_i = nullptr;
   e3::BGemmPlan bp_enc{}, bp_qkv{}, bp_o{}, bp_gu{}, bp_d{}, bp_lm{};
+  // LDS-tiled plans of the same projections (splits 0: K is not a multiple of 64,
+  // the fragment-load GEMM above runs instead)
+  e3::GemmPlan tp_enc{}, tp_qkv{}, tp_o{}, tp_gu{}, tp_d{}, tp_lm{};
+  int b_ncand = 0;  // lm_head candidates per batch row
 
   e3::Ledger ledger;
   std::string err;
@@ -408,12 +412,30 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     c->bp_gu = e3::bgemm_plan(int(2 * ff), int(n), e3::kBEpiSilu);
     c->bp_d = e3::bgemm_plan(int(n), int(ff), e3::kBEpiPartial);
     c->bp_lm = e3::bgemm_plan(int(dv), int(n), e3::kBEpiArgmax);
+    auto tplan = [&](int64_t N, int64_t K) {
+      e3::GemmPlan p{0, 0};
+      if (K % 64 == 0) p = e3::gemm_plan(kBatchRows, int(N), int(K));
+      return p;
+    };
+    c->tp_enc = tplan(n, 3 * n);
+    c->tp_qkv = tplan(N_qkv, 2 * n);
+    c->tp_o = tplan(n, qd);
+    c->tp_gu = tplan(2 * ff, n);
+    c->tp_d = tplan(n, ff);
+    c->tp_lm = tplan(dv, n);
+    c->b_ncand = c->tp_lm.splits ? e3::bcand_count(int(dv)) : c->bp_lm.blocks;
     c->bld_a = int(3 * n);
     c->bld_b = int(std::max(qd, ff));
     size_t pmax = 0;
-    for (auto pr : {std::make_pair(c->bp_enc, n), std::make_pair(c->bp_qkv, int64_t(N_qkv)),
-                    std::make_pair(c->bp_o, n), std::make_pair(c->bp_d, n)})
-      pmax = std::max(pmax, size_t(pr.first.splits) * kBatchRows * size_t(pr.second));
+    auto planes = [](const e3::GemmPlan& tp, const e3::BGemmPlan& bp, bool fused) {
+      return size_t(tp.splits ? tp.splits : (fused ? 0 : bp.splits));
+    };
+    pmax = std::max(pmax, planes(c->tp_enc, c->bp_enc, false) * kBatchRows * size_t(n));
+    pmax = std::max(pmax, planes(c->tp_qkv, c->bp_qkv, false) * kBatchRows * size_t(N_qkv));
+    pmax = std::max(pmax, planes(c->tp_o, c->bp_o, false) * kBatchRows * size_t(n));
+    pmax = std::max(pmax, planes(c->tp_d, c->bp_d, false) * kBatchRows * size_t(n));
+    pmax = std::max(pmax, planes(c->tp_gu, c->bp_gu, true) * kBatchRows * size_t(2 * ff));
+    pmax = std::max(pmax, planes(c->tp_lm, c->bp_lm, true) * kBatchRows * size_t(dv));
     const size_t bsp = size_t(e3::attn_batch_max_splits(c->cap, c->hd, c->kv_f32));
     E3_TRY(dalloc(c, &c->bx_a_hi, size_t(kBatchRows) * c->bld_a));
     E3_TRY(dalloc(c, &c->bx_a_lo, size_t(kBatchRows) * c->bld_a));
@@ -425,8 +447,8 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     E3_TRY(dalloc(c, &c->b_q, size_t(kBatchRows) * qd));
     E3_TRY(dalloc(c, &c->b_po, size_t(kBatchRows) * nh * bsp * hd));
     E3_TRY(dalloc(c, &c->b_pml, size_t(kBatchRows) * nh * bsp * 2));
-    E3_TRY(dalloc(c, &c->b_cand_v, size_t(kBatchRows) * c->bp_lm.blocks));
-    E3_TRY(dalloc(c, &c->b_cand_i, size_t(kBatchRows) * c->bp_lm.blocks));
+    E3_TRY(dalloc(c, &c->b_cand_v, size_t(kBatchRows) * c->b_ncand));
+    E3_TRY(dalloc(c, &c->b_cand_i, size_t(kBatchRows) * c->b_ncand));
     E3_TRY(dalloc(c, &c->b_logits, size_t(kBatchRows) * dv));
     E3_TRY(dalloc(c, &c->bx_z_hi, size_t(kBatchRows) * n));
     E3_TRY(dalloc(c, &c->bx_z_lo, size_t(kBatchRows) * n));
@@ -733,15 +755,28 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       ga.W = W; ga.N = N; ga.K = K; ga.Xhi = xh; ga.Xlo = xl; ga.ldx = ldx; ga.m = m;
       ga.P = c->b_P;
       ga.act_hi = c->bx_b_hi; ga.act_lo = c->bx_b_lo; ga.ld_act = c->bld_b;
-      ga.cand_v = c->b_cand_v; ga.cand_i = c->b_cand_i; ga.ncand = c->bp_lm.blocks;
+      ga.cand_v = c->b_cand_v; ga.cand_i = c->b_cand_i; ga.ncand = c->b_ncand;
       ga.logits = (dbg && dbg->logits) ? c->b_logits : nullptr;
       return e3::launch_bgemm(ga, p, epi, s);
     };
+    // a projection into the split-K partials b_P [splits][32][N]: the LDS-tiled GEMM
+    // over all 32 activation rows (rows past m are never read back), else the
+    // fragment-load GEMM; *S receives the split count
+    auto proj = [&](const uint16_t* W, int N, int K, const uint16_t* xh, const uint16_t* xl,
+                    int ldx, int m, const e3::GemmPlan& tp, const e3::BGemmPlan& bp, int* S) {
+      if (tp.splits) {
+        *S = tp.splits;
+        return e3::launch_gemm_bf16(xh, xl, ldx, W, K, c->b_P, kBatchRows, N, K, tp, s);
+      }
+      *S = bp.splits;
+      return gemm(W, N, K, xh, xl, ldx, m, bp, e3::kBEpiPartial);
+    };
+    int S_enc = 0;
     {
       ProfScope ps(c, 6, s);
       E3_HIP(c, e3::launch_bpack_aux(br, a0, a1, a2, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, s), "pack");
-      E3_HIP(c, gemm(c->w_fc, n, 3 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, br.m, c->bp_enc,
-                     e3::kBEpiPartial), "encode");
+      E3_HIP(c, proj(c->w_fc, n, 3 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, br.m, c->tp_enc,
+                     c->bp_enc, &S_enc), "encode");
     }
     const int steps = br.geff[0];
     for (int j = 0; j < steps; ++j) {
@@ -749,20 +784,21 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       while (m < br.m && br.geff[m] > j) ++m;
       e3::BPrepArgs pa{};
       pa.br = br; pa.m = m; pa.step = j; pa.gamma = gamma; pa.boundary_tok = btok;
-      pa.cand_v = c->b_cand_v; pa.cand_i = c->b_cand_i; pa.ncand = c->bp_lm.blocks;
+      pa.cand_v = c->b_cand_v; pa.cand_i = c->b_cand_i; pa.ncand = c->b_ncand;
       pa.d2t = c->d2t; pa.dv = c->dv; pa.out_ids = out; pa.embed = c->embed; pa.vocab = c->vt;
       pa.n = n; pa.w_in = c->nrm_in; pa.w_hid = c->nrm_hid; pa.eps = c->cfg.rms_eps;
-      pa.G = c->b_G; pa.Penc = c->b_P; pa.S_enc = c->bp_enc.splits;
+      pa.G = c->b_G; pa.Penc = c->b_P; pa.S_enc = S_enc;
       pa.Xhi = c->bx_a_hi; pa.Xlo = c->bx_a_lo; pa.ldx = c->bld_a;
       pa.dbg_hidden = dbg ? dbg->hidden : nullptr;
       const int Nqkv = c->qd + 2 * c->kvd;
       {
         ProfScope ps(c, 2, s);
         E3_HIP(c, e3::launch_bprep(pa, s), "prep");
-        E3_HIP(c, gemm(c->w_qkv, Nqkv, 2 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->bp_qkv,
-                       e3::kBEpiPartial), "qkv");
+        int S_qkv = 0;
+        E3_HIP(c, proj(c->w_qkv, Nqkv, 2 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->tp_qkv,
+                       c->bp_qkv, &S_qkv), "qkv");
         e3::BQkvArgs qa{};
-        qa.P = c->b_P; qa.S = c->bp_qkv.splits; qa.N = Nqkv; qa.br = br; qa.m = m; qa.step = j;
+        qa.P = c->b_P; qa.S = S_qkv; qa.N = Nqkv; qa.br = br; qa.m = m; qa.step = j;
         qa.n_head = c->nh; qa.n_head_kv = c->nkv; qa.head_dim = c->hd; qa.rope_dim = c->rot;
         qa.inv_freq = c->inv_freq; qa.q = c->b_q; qa.kv = c->kv; qa.seq_elems = c->kv_seq_elems;
         qa.kv_f32 = c->kv_f32; qa.cap = c->cap;
@@ -779,27 +815,36 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       }
       {
         ProfScope ps(c, 4, s);
-        E3_HIP(c, gemm(c->w_o, n, c->qd, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->bp_o,
-                       e3::kBEpiPartial), "o_proj");
+        int S_o = 0;
+        E3_HIP(c, proj(c->w_o, n, c->qd, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->tp_o, c->bp_o,
+                       &S_o), "o_proj");
         e3::BResidArgs ra{};
-        ra.P = c->b_P; ra.S = c->bp_o.splits; ra.n = n; ra.m = m; ra.resid = c->b_G; ra.y = c->b_X1;
+        ra.P = c->b_P; ra.S = S_o; ra.n = n; ra.m = m; ra.resid = c->b_G; ra.y = c->b_X1;
         ra.eps = c->cfg.rms_eps; ra.w1 = c->nrm_post; ra.x1_hi = c->bx_z_hi; ra.x1_lo = c->bx_z_lo;
         ra.ld1 = n; ra.br = br; ra.step = j; ra.gamma = gamma;
         E3_HIP(c, e3::launch_bresid(ra, s), "o_proj rows");
       }
       {
         ProfScope ps(c, 1, s);
-        E3_HIP(c, gemm(c->w_gu, 2 * c->ff, n, c->bx_z_hi, c->bx_z_lo, n, m, c->bp_gu, e3::kBEpiSilu),
-               "gate/up");
+        if (c->tp_gu.splits) {
+          E3_HIP(c, e3::launch_gemm_bf16(c->bx_z_hi, c->bx_z_lo, n, c->w_gu, n, c->b_P, kBatchRows,
+                                         2 * c->ff, n, c->tp_gu, s), "gate/up");
+          E3_HIP(c, e3::launch_bact(c->b_P, c->tp_gu.splits, c->ff, m, c->bx_b_hi, c->bx_b_lo,
+                                    c->bld_b, s), "silu");
+        } else {
+          E3_HIP(c, gemm(c->w_gu, 2 * c->ff, n, c->bx_z_hi, c->bx_z_lo, n, m, c->bp_gu,
+                         e3::kBEpiSilu), "gate/up");
+        }
       }
       {
         ProfScope ps(c, 3, s);
-        E3_HIP(c, gemm(c->w_d, n, c->ff, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->bp_d,
-                       e3::kBEpiPartial), "down");
+        int S_d = 0;
+        E3_HIP(c, proj(c->w_d, n, c->ff, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->tp_d, c->bp_d,
+                       &S_d), "down");
         // g_next; RMSNorm(g_next, norm) for the lm_head and RMSNorm(g_next, hidden_norm)
         // as the second half of the next step's QKV input
         e3::BResidArgs ra{};
-        ra.P = c->b_P; ra.S = c->bp_d.splits; ra.n = n; ra.m = m; ra.resid = c->b_X1; ra.y = c->b_G;
+        ra.P = c->b_P; ra.S = S_d; ra.n = n; ra.m = m; ra.resid = c->b_X1; ra.y = c->b_G;
         ra.eps = c->cfg.rms_eps;
         ra.w1 = c->nrm_fin; ra.x1_hi = c->bx_h_hi; ra.x1_lo = c->bx_h_lo; ra.ld1 = n;
         ra.w2 = c->nrm_hid; ra.x2_hi = c->bx_a_hi + n; ra.x2_lo = c->bx_a_lo + n; ra.ld2 = c->bld_a;
@@ -809,8 +854,16 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       }
       {
         ProfScope ps(c, 0, s);
-        E3_HIP(c, gemm(c->w_lm, c->dv, n, c->bx_h_hi, c->bx_h_lo, n, m, c->bp_lm, e3::kBEpiArgmax),
-               "lm_head");
+        if (c->tp_lm.splits) {
+          E3_HIP(c, e3::launch_gemm_bf16(c->bx_h_hi, c->bx_h_lo, n, c->w_lm, n, c->b_P, kBatchRows,
+                                         c->dv, n, c->tp_lm, s), "lm_head");
+          E3_HIP(c, e3::launch_bcand(c->b_P, c->tp_lm.splits, c->dv, m, c->b_cand_v, c->b_cand_i,
+                                     (dbg && dbg->logits) ? c->b_logits : nullptr, s),
+                 "lm_head candidates");
+        } else {
+          E3_HIP(c, gemm(c->w_lm, c->dv, n, c->bx_h_hi, c->bx_h_lo, n, m, c->bp_lm,
+                         e3::kBEpiArgmax), "lm_head");
+        }
       }
       if (dbg && dbg->logits)
         for (int r = 0; r < m; ++r)
@@ -818,7 +871,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
                                    c->b_logits + size_t(r) * c->dv, size_t(c->dv) * 4,
                                    hipMemcpyDeviceToDevice, s), "dbg logits");
     }
-    E3_HIP(c, e3::launch_bfinal(br, br.m, gamma, c->b_cand_v, c->b_cand_i, c->bp_lm.blocks, c->d2t,
+    E3_HIP(c, e3::launch_bfinal(br, br.m, gamma, c->b_cand_v, c->b_cand_i, c->b_ncand, c->d2t,
                                 c->dv, out, s), "argmax");
   }
   return EAGLE3_OK;

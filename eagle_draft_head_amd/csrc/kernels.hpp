@@ -253,6 +253,14 @@ hipError_t launch_bresid(const BResidArgs& a, hipStream_t s);
 // act = silu(sum_z P[z][2i]) * sum_z P[z][2i+1] as (hi, lo) [32][ld]
 hipError_t launch_bact(const float* P, int S, int n_ff, int m, uint16_t* Xhi, uint16_t* Xlo, int ld,
                        hipStream_t s);
+// lm_head candidates from split-K partials P[z][32][N]: for each row r < m and each
+// block of kBCandCols columns, the best (value, index) of sum_z P[z][r][c] (the
+// lowest index on ties) -> cand_v/cand_i[r * ncand + block]; the summed logits also
+// to logits[r * N + c] when logits is not NULL.  ncand = bcand_count(N).
+constexpr int kBCandCols = 2048;
+inline int bcand_count(int N) { return (N + kBCandCols - 1) / kBCandCols; }
+hipError_t launch_bcand(const float* P, int S, int N, int m, float* cand_v, int32_t* cand_i,
+                        float* logits, hipStream_t s);
 // rows [0, m): out_ids[orig * gamma + geff - 1] = d2t-mapped argmax of the candidates
 hipError_t launch_bfinal(const BatchRows& br, int m, int gamma, const float* cand_v,
                          const int32_t* cand_i, int ncand, const int32_t* d2t, int dv,
@@ -290,7 +298,7 @@ hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const Sto
 // C[z][M][N] (fp32) = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T on bf16 MFMA
 // (A_lo may be NULL: one product).  Row strides lda, ldb (elements); K split
 // evenly over plan.splits.  The plan's tile width is 256 or 320 columns for
-// 256-row tiles (M >= 256) and 128 for 128-row tiles.
+// 256-row tiles (M >= 256) and 128 for 128-row and 32-row tiles (M <= 32).
 struct GemmPlan {
   int bn;      // output tile width
   int splits;  // K split (z planes of C)

@@ -303,9 +303,13 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     break;
     E3_WV(0) E3_WV(1) E3_WV(2) E3_WV(3) E3_WV(4) E3_WV(5) E3_WV(6) E3_WV(7) E3_WV(8) E3_WV(9)
     E3_WV(10) E3_WV(11) E3_WV(12) E3_WV(13) E3_WV(14) E3_WV(15) E3_WV(16) E3_WV(17) E3_WV(18)
-    E3_WV(19) E3_WV(20) E3_WV(21) E3_WV(22) E3_WV(23)
+    E3_WV(19) E3_WV(20) E3_WV(21) E3_WV(22) E3_WV(23) E3_WV(24) E3_WV(25) E3_WV(26) E3_WV(27)
+    E3_WV(28) E3_WV(29) E3_WV(30) E3_WV(31) E3_WV(32) E3_WV(33) E3_WV(34) E3_WV(35) E3_WV(36)
+    E3_WV(37) E3_WV(38) E3_WV(39) E3_WV(40) E3_WV(41) E3_WV(42) E3_WV(43) E3_WV(44) E3_WV(45)
+    E3_WV(46) E3_WV(47) E3_WV(48) E3_WV(49) E3_WV(50) E3_WV(51) E3_WV(52) E3_WV(53) E3_WV(54)
+    E3_WV(55) E3_WV(56) E3_WV(57) E3_WV(58) E3_WV(59) E3_WV(60) E3_WV(61) E3_WV(62) E3_WV(63)
 #undef E3_WV
-    default:
+    default:  // beyond the counter's range: wait for everything
       wait_vmcnt<0>();
       break;
   }
@@ -425,8 +429,9 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(
 // K tile: 32 with split activations (three stages fit), 64 otherwise (two stages)
 constexpr int kBKSplit = 32, kBKPlain = 64;
 
-// 256-row tiles once there are 256 rows (256 or 320 columns), 128 x 128 below
-static int gemm_bm(int M) { return M >= 256 ? 256 : 128; }
+// 256-row tiles once there are 256 rows (256 or 320 columns), 128 x 128 below, and
+// 32 x 128 up to 32 rows (batched drafting, short appends)
+static int gemm_bm(int M) { return M >= 256 ? 256 : (M > 32 ? 128 : 32); }
 
 GemmPlan gemm_plan(int M, int N, int K) {
   // Candidates: tile width bn and K split s (a power of two keeping whole 64-wide
@@ -440,6 +445,21 @@ GemmPlan gemm_plan(int M, int N, int K) {
   // 160 tiles of 256, but 128 of 320, two K halves filling every CU once).
   const int bm = gemm_bm(M);
   const int max_sp = M <= 256 ? 16 : 4;
+  if (bm == 32) {
+    // 32-row blocks (74 KB of LDS, two per CU) stream weights: the smallest split
+    // that gives about one and a half blocks per CU keeps enough weight tiles in
+    // flight without more partials than needed (measured with cold weights at the
+    // 4096-wide shapes: lm_head 2, gate/up 2, qkv 8, down and o_proj 16)
+    const long long tiles = (N + 127) / 128;
+    GemmPlan p{128, 0};
+    for (int sp = 1; sp <= max_sp; sp *= 2) {
+      if (K % (kBKPlain * sp) != 0) continue;
+      p.splits = sp;
+      if (tiles * sp >= 384) break;
+    }
+    if (p.splits == 0) p.splits = 1;  // K not a multiple of 64: rejected at launch
+    return p;
+  }
   GemmPlan best{bm, 1};
   double best_cost = 1e30;
   const int widths[2] = {bm, 320};
@@ -488,6 +508,11 @@ hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
     return hipErrorInvalidValue;
   const int kper = K / splits;
   const int bm = gemm_bm(M);
+  if (bm == 32) {
+    if (plan.bn != 128) return hipErrorInvalidValue;
+    if (A_lo) return launch_tiles<32, 128, 1, 4, true, kBKPlain, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    return launch_tiles<32, 128, 1, 4, false, kBKPlain, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  }
   if (bm == 256 && plan.bn == 320) {
     if (A_lo) return launch_tiles<256, 320, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
     return launch_tiles<256, 320, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
