@@ -28,7 +28,9 @@ def _rel_rows(gpu, ref):
 def test_prefill_pieces_of_every_width(cfg):
     say(f"[append] {cfg.name}: pieces")
     wd, wh = weights_both(cfg)
-    pieces = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 13, 16, 17, 40]
+    # 1..16 rows: the weight-streaming path at each width; 17, 24, 32: the 32-row
+    # MFMA tile (partial and full); 40: the 128-row tile
+    pieces = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12, 13, 16, 17, 24, 32, 40]
     L = sum(pieces)
     dr = gpu_drafter(cfg, wd, max_ctx=L + 8)
     orc = make_oracle(cfg, wh, max_ctx=L + 8)
