@@ -17,6 +17,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace e3 {
 
@@ -60,7 +61,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 
   const int s = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int slot = lane / LPR, sub = lane % LPR, d0 = sub * kAttnLaneElems;
+  const int slot = lane / LPR, sub = lane % LPR;
+  // element e of a lane's eight sits at dim(e): vector j = e / E of the lane is
+  // elements [j * HD / NV + sub * E, + E), so one load instruction of vector j
+  // reads a contiguous HD / NV stretch of each row (all of it when NV == 1)
+  auto dim = [&](int e) { return (e / E) * (HD / NV) + sub * E + (e % E); };
   int T = a.T;
   size_t kv_off = 0;
   const float* qrow = a.q;
@@ -79,8 +84,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   const bool direct = S == 1 && !a.batched;
   // scores in base 2: s * log2(e) / sqrt(hd), so every exponential is one exp2
   const float scale = 1.4426950408889634f / sqrtf(float(HD));
-  const KT* Kb = static_cast<const KT*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
-  const KT* Vb = static_cast<const KT*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD + d0;
+  const KT* Kb = static_cast<const KT*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD + sub * E;
+  const KT* Vb = static_cast<const KT*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD + sub * E;
 
   // ring of kDepth rows per lane group: slot i holds row r + i * RPB and is
   // refilled with the row kDepth strides ahead once consumed (rows are visited
@@ -95,20 +100,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
       kw[i][j] = make_uint4(0, 0, 0, 0);
       vw[i][j] = kw[i][j];
       if (rr < r1) {
-        kw[i][j] = reinterpret_cast<const uint4*>(Kb + (size_t)rr * HD)[j];
-        vw[i][j] = reinterpret_cast<const uint4*>(Vb + (size_t)rr * HD)[j];
+        kw[i][j] = *reinterpret_cast<const uint4*>(Kb + (size_t)rr * HD + j * (HD / NV));
+        vw[i][j] = *reinterpret_cast<const uint4*>(Vb + (size_t)rr * HD + j * (HD / NV));
       }
     }
   }
+  // q carries the score scale, so a row's dot product is its base-2 score
   float qv[G][kAttnLaneElems];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
-    for (int e = 0; e < kAttnLaneElems; ++e) qv[g][e] = qrow[(size_t)(kvh * G + g) * HD + d0 + e];
-  float m[G], l[G], acc[G][kAttnLaneElems];
+    for (int e = 0; e < kAttnLaneElems; ++e)
+      qv[g][e] = qrow[(size_t)(kvh * G + g) * HD + dim(e)] * scale;
+  float m[G], mr[G], l[G], acc[G][kAttnLaneElems];  // mr = m + kRescale
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
+    mr[g] = -INFINITY;
     l[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = 0.f;
@@ -128,8 +136,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
       if (nr < r1) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          kw[i][j] = reinterpret_cast<const uint4*>(Kb + (size_t)nr * HD)[j];
-          vw[i][j] = reinterpret_cast<const uint4*>(Vb + (size_t)nr * HD)[j];
+          kw[i][j] = *reinterpret_cast<const uint4*>(Kb + (size_t)nr * HD + j * (HD / NV));
+          vw[i][j] = *reinterpret_cast<const uint4*>(Vb + (size_t)nr * HD + j * (HD / NV));
         }
       }
       float d[G];
@@ -146,16 +154,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
       for (int g = 0; g < G; ++g) {
         // m is a reference at most kRescale below the running maximum, not the
         // maximum itself: (l, acc) are rescaled only when a score passes m by
-        // more than kRescale, so weights stay below 2^kRescale
-        const float sc = d[g] * scale;
-        if (sc > m[g] + kRescale) {
-          const float fo = exp2f(m[g] - sc);  // 0 on the first row (m = -inf)
+        // more than kRescale, so weights stay below 2^kRescale.  The hardware
+        // exp2 flushes results below 2^-126 to zero: such weights vanish next to
+        // the row that set m (weight 1).
+        const float sc = d[g];
+        if (sc > mr[g]) {
+          const float fo = __builtin_amdgcn_exp2f(m[g] - sc);  // 0 on the first row (m = -inf)
           l[g] *= fo;
 #pragma unroll
           for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
           m[g] = sc;
+          mr[g] = sc + kRescale;
         }
-        const float p = exp2f(sc - m[g]);
+        const float p = __builtin_amdgcn_exp2f(sc - m[g]);
         l[g] += p;
 #pragma unroll
         for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
@@ -192,7 +203,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][d0 + e] = acc[g][e];
+      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][dim(e)] = acc[g][e];
       if (sub == 0) s_L[wv][g] = l[g];
     }
   }
@@ -388,15 +399,27 @@ static hipError_t launch_kt(const AttnArgs& a, int G, int chunk, int S, hipStrea
   }
 }
 
-// Batched rows share one chunk size: about 2048 (row, head, split) blocks in
-// total, between kAttnBatchMinChunk and kAttnMaxChunk rows per split.
+// Batched rows share one chunk size: about attn_batch_target() (row, head, split)
+// blocks in total, between kAttnBatchMinChunk and kAttnMaxChunk rows per split.
 constexpr int kAttnBatchMinChunk = 128;
+
+// (row, head, split) blocks aimed at per batched launch; EAGLE3_ATTN_BATCH_BLOCKS
+// overrides it (at least 256) for tuning
+static int attn_batch_target() {
+  static const int t = [] {
+    const char* e = std::getenv("EAGLE3_ATTN_BATCH_BLOCKS");
+    const int v = e ? std::atoi(e) : 0;
+    return v >= 256 ? v : 2048;
+  }();
+  return t;
+}
 
 int attn_batch_chunk(const BatchRows& br, int m, int step, int n_head_kv, int head_dim, int kv_f32) {
   long long rows = 0;
   for (int r = 0; r < m; ++r) rows += br.pos0[r] + step + 1;
   const int rpb = rows_per_block(head_dim, kv_f32);
-  long long c = (rows * n_head_kv + 2047) / 2048;
+  const long long target = attn_batch_target();
+  long long c = (rows * n_head_kv + target - 1) / target;
   c = ((c + rpb - 1) / rpb) * rpb;
   if (c < kAttnBatchMinChunk) c = kAttnBatchMinChunk;
   if (c > kAttnMaxChunk) c = kAttnMaxChunk;
