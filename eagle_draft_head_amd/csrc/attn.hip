@@ -87,24 +87,24 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   const KT* Kb = static_cast<const KT*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD + sub * E;
   const KT* Vb = static_cast<const KT*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD + sub * E;
 
-  // ring of kDepth rows per lane group: slot i holds row r + i * RPB and is
-  // refilled with the row kDepth strides ahead once consumed (rows are visited
-  // in order r, r + RPB, ...)
-  int r = r0 + wv * RPW + slot;
+  // ring of kDepth rows per lane group: slot i holds row rb + off + i * RPB and is
+  // refilled with the row kDepth strides ahead once consumed.  Row indices are
+  // clamped to r1 - 1, so every load is in bounds and unconditional; a slot that
+  // holds a clamped row is never consumed.
+  const int off = wv * RPW + slot;
+  const int rlast = r1 - 1;
   uint4 kw[kDepth][NV], vw[kDepth][NV];
-#pragma unroll
-  for (int i = 0; i < kDepth; ++i) {
-    const int rr = r + i * RPB;
+  auto load_row = [&](int i, int row) {
+    row = min(row, rlast);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      kw[i][j] = make_uint4(0, 0, 0, 0);
-      vw[i][j] = kw[i][j];
-      if (rr < r1) {
-        kw[i][j] = *reinterpret_cast<const uint4*>(Kb + (size_t)rr * HD + j * (HD / NV));
-        vw[i][j] = *reinterpret_cast<const uint4*>(Vb + (size_t)rr * HD + j * (HD / NV));
-      }
+      kw[i][j] = *reinterpret_cast<const uint4*>(Kb + (size_t)row * HD + j * (HD / NV));
+      vw[i][j] = *reinterpret_cast<const uint4*>(Vb + (size_t)row * HD + j * (HD / NV));
     }
-  }
+  };
+  int rb = r0;  // the block's current stride (uniform)
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) load_row(i, rb + off + i * RPB);
   // q carries the score scale, so a row's dot product is its base-2 score
   float qv[G][kAttnLaneElems];
 #pragma unroll
@@ -121,56 +121,59 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 #pragma unroll
     for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = 0.f;
   }
-  for (; r < r1; r += kDepth * RPB) {
+  // consume ring slot i (its row valid), refill it with the row kDepth strides on
+  auto step = [&](int i, int row) {
+    float kf[kAttnLaneElems], vf[kAttnLaneElems];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      KvVec<KT>::unpack(kw[i][j], kf + j * E);
+      KvVec<KT>::unpack(vw[i][j], vf + j * E);
+    }
+    load_row(i, row + kDepth * RPB);
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) t = fmaf(kf[e], qv[g][e], t);
+      d[g] = t;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // m is a reference at most kRescale below the running maximum, not the
+      // maximum itself: (l, acc) are rescaled only when a score passes m by
+      // more than kRescale, so weights stay below 2^kRescale.  The hardware
+      // exp2 flushes results below 2^-126 to zero: such weights vanish next to
+      // the row that set m (weight 1).
+      const float sc = d[g];
+      if (sc > mr[g]) {
+        const float fo = __builtin_amdgcn_exp2f(m[g] - sc);  // 0 on the first row (m = -inf)
+        l[g] *= fo;
+#pragma unroll
+        for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
+        m[g] = sc;
+        mr[g] = sc + kRescale;
+      }
+      const float p = __builtin_amdgcn_exp2f(sc - m[g]);
+      l[g] += p;
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+    }
+  };
+  // strides in which every lane group's kDepth rows are valid: no per-row checks
+  for (; rb + kDepth * RPB <= r1; rb += kDepth * RPB) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) step(i, rb + off + i * RPB);
+  }
+  // the last, partial stride
+  if (rb < r1) {
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) {
-      const int rr = r + i * RPB;
+      const int rr = rb + off + i * RPB;
       if (rr >= r1) break;
-      float kf[kAttnLaneElems], vf[kAttnLaneElems];
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        KvVec<KT>::unpack(kw[i][j], kf + j * E);
-        KvVec<KT>::unpack(vw[i][j], vf + j * E);
-      }
-      const int nr = rr + kDepth * RPB;
-      if (nr < r1) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          kw[i][j] = *reinterpret_cast<const uint4*>(Kb + (size_t)nr * HD + j * (HD / NV));
-          vw[i][j] = *reinterpret_cast<const uint4*>(Vb + (size_t)nr * HD + j * (HD / NV));
-        }
-      }
-      float d[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < kAttnLaneElems; ++e) t = fmaf(kf[e], qv[g][e], t);
-        d[g] = t;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        // m is a reference at most kRescale below the running maximum, not the
-        // maximum itself: (l, acc) are rescaled only when a score passes m by
-        // more than kRescale, so weights stay below 2^kRescale.  The hardware
-        // exp2 flushes results below 2^-126 to zero: such weights vanish next to
-        // the row that set m (weight 1).
-        const float sc = d[g];
-        if (sc > mr[g]) {
-          const float fo = __builtin_amdgcn_exp2f(m[g] - sc);  // 0 on the first row (m = -inf)
-          l[g] *= fo;
-#pragma unroll
-          for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
-          m[g] = sc;
-          mr[g] = sc + kRescale;
-        }
-        const float p = __builtin_amdgcn_exp2f(sc - m[g]);
-        l[g] += p;
-#pragma unroll
-        for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
-      }
+      step(i, rr);
     }
   }
 
