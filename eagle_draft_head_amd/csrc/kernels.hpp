@@ -298,7 +298,8 @@ hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const Sto
 // C[z][M][N] (fp32) = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T on bf16 MFMA
 // (A_lo may be NULL: one product).  Row strides lda, ldb (elements); K split
 // evenly over plan.splits.  The plan's tile width is 256 or 320 columns for
-// 256-row tiles (M >= 256) and 128 for 128-row and 32-row tiles (M <= 32).
+// 256-row tiles (M >= 256), 128 for 128-row tiles, and 128 weight rows per block
+// for the skinny GEMM (M <= 32).
 struct GemmPlan {
   int bn;      // output tile width
   int splits;  // K split (z planes of C)

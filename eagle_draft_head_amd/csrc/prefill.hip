@@ -426,11 +426,152 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny GEMM for M <= 32 activation rows (batched drafting, short appends):
+// C[z][M][N] = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T, B the weight stream.
+// A block owns kSgRows weight rows.  Per 64-wide k step its 256 threads load the
+// weight tile row-contiguously (eight lanes per 128-byte row slice) and the
+// activation tile into registers kSgDepth steps ahead, then copy one step's
+// registers into one of two LDS buffers right before that step's MFMAs: the
+// registers keep kSgDepth x 24 KB per block in flight, several times what an LDS
+// ring of the same footprint holds.  Waves tile the block 1 x 4, each owning
+// 32 x 32 of C as 2 x 2 tiles of 16x16x32 MFMA.  One barrier per step: a buffer
+// is rewritten two steps after its last read, and every wave has passed the
+// barrier in between.  Refills past the last step re-read the last tile (in
+// bounds, never used).
+constexpr int kSgRows = 128;
+constexpr int kSgBK = 64;
+constexpr int kSgDepth = 4;  // even: a step's LDS buffer is its parity
+
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
+                                               const uint16_t* __restrict__ A2, int lda,
+                                               const uint16_t* __restrict__ B, int ldb,
+                                               float* __restrict__ C, int M, int N, int kper,
+                                               int nt) {
+  constexpr int NSA = SPLIT ? 2 : 1;
+  constexpr int D = kSgDepth;
+  static_assert(D % 2 == 0, "buffer parity follows the ring slot");
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kSgRows * kSgBK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][NSA][32 * kSgBK];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // block b owns weight tile b (consecutive blocks, and so tiles, go to different XCDs)
+  const int n_t = blockIdx.x;
+  if (n_t >= nt) return;
+  const int n0 = n_t * kSgRows;
+  const int kb = blockIdx.z * kper;
+  const int nsteps = kper / kSgBK;
+  float* Cz = C + (size_t)blockIdx.z * M * N;
+
+  // thread t loads weight rows (t >> 3) + 32 q and activation row t >> 3, chunk t & 7
+  const int lr = tid >> 3, lc = tid & 7;
+  const uint16_t* wp[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wp[q] = B + (size_t)min(n0 + lr + 32 * q, N - 1) * ldb + kb + 8 * lc;
+  const size_t aoff = (size_t)min(lr, M - 1) * lda + kb + 8 * lc;
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
+  // the ring: slot I holds one step's weight chunks and activation chunk(s); slots
+  // are named statically (E3_SG_*(I) with a literal I) so they stay in registers
+  u32x4 wreg[D][4], areg[D][NSA];  // native vectors: kept in registers
+#define E3_SG_ISSUE(I, ST)                                                                   \
+  {                                                                                          \
+    const int k_ = min((ST), nsteps - 1) * kSgBK;                                            \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) wreg[I][q] =                               \
+        *reinterpret_cast<const u32x4*>(wp[q] + k_);                                         \
+    _Pragma("unroll") for (int h = 0; h < NSA; ++h) areg[I][h] =                             \
+        *reinterpret_cast<const u32x4*>((h ? A2 : A) + aoff + k_);                           \
+  }
+#define E3_SG_STEP(I, T)                                                                     \
+  {                                                                                          \
+    const int buf = (I) & 1;                                                                 \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                          \
+      const int r = lr + 32 * q;                                                             \
+      *reinterpret_cast<u32x4*>(&Ws[buf][r * kSgBK + 8 * (lc ^ tile_swizzle<kSgBK>(r))]) =   \
+          wreg[I][q];                                                                        \
+    }                                                                                        \
+    _Pragma("unroll") for (int h = 0; h < NSA; ++h)                                          \
+        *reinterpret_cast<u32x4*>(&As[buf][h][lr * kSgBK + 8 * (lc ^ tile_swizzle<kSgBK>(lr))]) = \
+        areg[I][h];                                                                          \
+    __syncthreads();                                                                         \
+    E3_SG_ISSUE(I, (T) + D)                                                                  \
+    _Pragma("unroll") for (int kk = 0; kk < kSgBK; kk += 32) {                               \
+      const int c = (kk >> 3) + (lane >> 4);                                                 \
+      bf16x8 bfr[2];                                                                         \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                        \
+        const int r = wv * 32 + j * 16 + (lane & 15);                                        \
+        bfr[j] = *reinterpret_cast<const bf16x8*>(                                           \
+            &Ws[buf][r * kSgBK + 8 * (c ^ tile_swizzle<kSgBK>(r))]);                         \
+      }                                                                                      \
+      _Pragma("unroll") for (int h = 0; h < NSA; ++h) {                                      \
+        bf16x8 af[2];                                                                        \
+        _Pragma("unroll") for (int i2 = 0; i2 < 2; ++i2) {                                   \
+          const int r = i2 * 16 + (lane & 15);                                               \
+          af[i2] = *reinterpret_cast<const bf16x8*>(                                         \
+              &As[buf][h][r * kSgBK + 8 * (c ^ tile_swizzle<kSgBK>(r))]);                    \
+        }                                                                                    \
+        _Pragma("unroll") for (int i2 = 0; i2 < 2; ++i2)                                     \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i2][j] =                           \
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i2], bfr[j], acc[i2][j], 0, 0, 0);    \
+      }                                                                                      \
+    }                                                                                        \
+  }
+  static_assert(kSgDepth == 4, "the ring below names four slots");
+  E3_SG_ISSUE(0, 0)
+  E3_SG_ISSUE(1, 1)
+  E3_SG_ISSUE(2, 2)
+  E3_SG_ISSUE(3, 3)
+  int t0 = 0;
+  for (; t0 + D <= nsteps; t0 += D) {
+    E3_SG_STEP(0, t0)
+    E3_SG_STEP(1, t0 + 1)
+    E3_SG_STEP(2, t0 + 2)
+    E3_SG_STEP(3, t0 + 3)
+  }
+  // the last, partial group of steps (uniform)
+  if (t0 < nsteps) E3_SG_STEP(0, t0)
+  if (t0 + 1 < nsteps) E3_SG_STEP(1, t0 + 1)
+  if (t0 + 2 < nsteps) E3_SG_STEP(2, t0 + 2)
+#undef E3_SG_STEP
+#undef E3_SG_ISSUE
+
+  // D of a 16x16 tile: lane l holds column l % 16, rows 4 (l / 16) + v
+#pragma unroll
+  for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wv * 32 + j * 16 + (lane & 15);
+      if (col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = i2 * 16 + 4 * (lane >> 4) + v;
+        if (row < M) Cz[(size_t)row * N + col] = acc[i2][j][v];
+      }
+    }
+}
+
+static hipError_t launch_sgemm(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
+                               int ldb, float* C, int M, int N, int kper, int splits, hipStream_t s) {
+  if (M > 32 || kper % kSgBK) return hipErrorInvalidValue;
+  const int nt = (N + kSgRows - 1) / kSgRows;
+  dim3 grid((nt + 7) / 8 * 8, 1, splits);
+  if (A_lo)
+    hipLaunchKernelGGL(k_sgemm<true>, grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C, M, N, kper, nt);
+  else
+    hipLaunchKernelGGL(k_sgemm<false>, grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C, M, N, kper, nt);
+  return hipGetLastError();
+}
+
 // K tile: 32 with split activations (three stages fit), 64 otherwise (two stages)
 constexpr int kBKSplit = 32, kBKPlain = 64;
 
 // 256-row tiles once there are 256 rows (256 or 320 columns), 128 x 128 below, and
-// 32 x 128 up to 32 rows (batched drafting, short appends)
+// the skinny GEMM up to 32 rows (batched drafting, short appends)
 static int gemm_bm(int M) { return M >= 256 ? 256 : (M > 32 ? 128 : 32); }
 
 GemmPlan gemm_plan(int M, int N, int K) {
@@ -446,16 +587,16 @@ GemmPlan gemm_plan(int M, int N, int K) {
   const int bm = gemm_bm(M);
   const int max_sp = M <= 256 ? 16 : 4;
   if (bm == 32) {
-    // 32-row blocks (74 KB of LDS, two per CU) stream weights: the smallest split
-    // that gives about one and a half blocks per CU keeps enough weight tiles in
-    // flight without more partials than needed (measured with cold weights at the
-    // 4096-wide shapes: lm_head 2, gate/up 2, qkv 8, down and o_proj 16)
-    const long long tiles = (N + 127) / 128;
-    GemmPlan p{128, 0};
+    // the skinny GEMM (128 weight rows per block, up to three blocks per CU): the
+    // smallest split giving about three blocks for every four CUs; more splits only
+    // add partials (measured with cold weights at the 4096-wide shapes: lm_head and
+    // gate/up 1, qkv 4, down and o_proj 8)
+    const long long tiles = (N + kSgRows - 1) / kSgRows;
+    GemmPlan p{kSgRows, 0};
     for (int sp = 1; sp <= max_sp; sp *= 2) {
       if (K % (kBKPlain * sp) != 0) continue;
       p.splits = sp;
-      if (tiles * sp >= 384) break;
+      if (tiles * sp >= 192) break;
     }
     if (p.splits == 0) p.splits = 1;  // K not a multiple of 64: rejected at launch
     return p;
@@ -509,9 +650,8 @@ hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
   const int kper = K / splits;
   const int bm = gemm_bm(M);
   if (bm == 32) {
-    if (plan.bn != 128) return hipErrorInvalidValue;
-    if (A_lo) return launch_tiles<32, 128, 1, 4, true, kBKPlain, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
-    return launch_tiles<32, 128, 1, 4, false, kBKPlain, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    if (plan.bn != kSgRows) return hipErrorInvalidValue;
+    return launch_sgemm(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
   }
   if (bm == 256 && plan.bn == 320) {
     if (A_lo) return launch_tiles<256, 320, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
