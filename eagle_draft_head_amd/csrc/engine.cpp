@@ -423,7 +423,10 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     c->tp_gu = tplan(2 * ff, n);
     c->tp_d = tplan(n, ff);
     c->tp_lm = tplan(dv, n);
-    c->b_ncand = c->tp_lm.splits ? e3::bcand_count(int(dv)) : c->bp_lm.blocks;
+    // lm_head candidates per row: one per 128 weight rows from the fused epilogue of an
+    // unsplit skinny GEMM, one per 2048 columns from the partials otherwise
+    c->b_ncand = c->tp_lm.splits == 1 ? e3::sgemm_tiles(int(dv))
+                 : c->tp_lm.splits ? e3::bcand_count(int(dv)) : c->bp_lm.blocks;
     c->bld_a = int(3 * n);
     c->bld_b = int(std::max(qd, ff));
     size_t pmax = 0;
@@ -434,8 +437,10 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     pmax = std::max(pmax, planes(c->tp_qkv, c->bp_qkv, false) * kBatchRows * size_t(N_qkv));
     pmax = std::max(pmax, planes(c->tp_o, c->bp_o, false) * kBatchRows * size_t(n));
     pmax = std::max(pmax, planes(c->tp_d, c->bp_d, false) * kBatchRows * size_t(n));
-    pmax = std::max(pmax, planes(c->tp_gu, c->bp_gu, true) * kBatchRows * size_t(2 * ff));
-    pmax = std::max(pmax, planes(c->tp_lm, c->bp_lm, true) * kBatchRows * size_t(dv));
+    // gate/up and lm_head write partials only when split (one split: fused epilogues)
+    auto fused_planes = [](const e3::GemmPlan& tp) { return size_t(tp.splits > 1 ? tp.splits : 0); };
+    pmax = std::max(pmax, fused_planes(c->tp_gu) * kBatchRows * size_t(2 * ff));
+    pmax = std::max(pmax, fused_planes(c->tp_lm) * kBatchRows * size_t(dv));
     const size_t bsp = size_t(e3::attn_batch_max_splits(c->cap, c->hd, c->kv_f32));
     E3_TRY(dalloc(c, &c->bx_a_hi, size_t(kBatchRows) * c->bld_a));
     E3_TRY(dalloc(c, &c->bx_a_lo, size_t(kBatchRows) * c->bld_a));
@@ -826,7 +831,13 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       }
       {
         ProfScope ps(c, 1, s);
-        if (c->tp_gu.splits) {
+        if (c->tp_gu.splits == 1) {
+          e3::BGemmArgs ga{};
+          ga.W = c->w_gu; ga.N = 2 * c->ff; ga.K = n; ga.Xhi = c->bx_z_hi; ga.Xlo = c->bx_z_lo;
+          ga.ldx = n; ga.m = m;
+          ga.act_hi = c->bx_b_hi; ga.act_lo = c->bx_b_lo; ga.ld_act = c->bld_b;
+          E3_HIP(c, e3::launch_sgemm_fused(ga, e3::kBEpiSilu, s), "gate/up");
+        } else if (c->tp_gu.splits) {
           E3_HIP(c, e3::launch_gemm_bf16(c->bx_z_hi, c->bx_z_lo, n, c->w_gu, n, c->b_P, kBatchRows,
                                          2 * c->ff, n, c->tp_gu, s), "gate/up");
           E3_HIP(c, e3::launch_bact(c->b_P, c->tp_gu.splits, c->ff, m, c->bx_b_hi, c->bx_b_lo,
@@ -854,7 +865,14 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       }
       {
         ProfScope ps(c, 0, s);
-        if (c->tp_lm.splits) {
+        if (c->tp_lm.splits == 1) {
+          e3::BGemmArgs ga{};
+          ga.W = c->w_lm; ga.N = c->dv; ga.K = n; ga.Xhi = c->bx_h_hi; ga.Xlo = c->bx_h_lo;
+          ga.ldx = n; ga.m = m;
+          ga.cand_v = c->b_cand_v; ga.cand_i = c->b_cand_i; ga.ncand = c->b_ncand;
+          ga.logits = (dbg && dbg->logits) ? c->b_logits : nullptr;
+          E3_HIP(c, e3::launch_sgemm_fused(ga, e3::kBEpiArgmax, s), "lm_head");
+        } else if (c->tp_lm.splits) {
           E3_HIP(c, e3::launch_gemm_bf16(c->bx_h_hi, c->bx_h_lo, n, c->w_lm, n, c->b_P, kBatchRows,
                                          c->dv, n, c->tp_lm, s), "lm_head");
           E3_HIP(c, e3::launch_bcand(c->b_P, c->tp_lm.splits, c->dv, m, c->b_cand_v, c->b_cand_i,

@@ -173,6 +173,11 @@ struct BGemmPlan {
 };
 BGemmPlan bgemm_plan(int N, int K, int epi);
 hipError_t launch_bgemm(BGemmArgs a, const BGemmPlan& p, int epi, hipStream_t s);
+// The skinny MFMA GEMM over the whole K (32 activation rows, split activations) with
+// the kBEpiSilu or kBEpiArgmax epilogue of the arguments above; the argmax writes
+// sgemm_tiles(N) candidates per row (ncand >= that).  K % 64 == 0.
+int sgemm_tiles(int N);
+hipError_t launch_sgemm_fused(const BGemmArgs& a, int epi, hipStream_t s);
 
 // Row kernels of the batched step: one block of kBRowThreads per sequence row
 // keeps the row in registers (up to kBRowMax values), so a row's sums, its RMS

@@ -443,12 +443,27 @@ constexpr int kSgRows = 128;
 constexpr int kSgBK = 64;
 constexpr int kSgDepth = 4;  // even: a step's LDS buffer is its parity
 
-template <bool SPLIT>
+// Epilogues (one split only, i.e. K whole): kBEpiSilu writes silu(gate) * up of the
+// interleaved (gate, up) rows as (hi, lo) bf16; kBEpiArgmax writes, per activation
+// row, the best (value, index) over the block's 128 weight rows (lowest index on
+// ties) and optionally the logits.  kBEpiPartial stores C[z].
+struct SgEpi {
+  int m;              // activation rows written (<= M)
+  uint16_t* act_hi;   // kBEpiSilu: [m][ld_act]
+  uint16_t* act_lo;
+  int ld_act;
+  float* cand_v;      // kBEpiArgmax: [m][ncand], ncand >= gridDim.x
+  int32_t* cand_i;
+  int ncand;
+  float* logits;      // kBEpiArgmax, optional: [m][N]
+};
+
+template <bool SPLIT, int EPI>
 __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ A2, int lda,
                                                const uint16_t* __restrict__ B, int ldb,
                                                float* __restrict__ C, int M, int N, int kper,
-                                               int nt) {
+                                               int nt, SgEpi e) {
   constexpr int NSA = SPLIT ? 2 : 1;
   constexpr int D = kSgDepth;
   static_assert(D % 2 == 0, "buffer parity follows the ring slot");
@@ -541,18 +556,80 @@ __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
 #undef E3_SG_ISSUE
 
   // D of a 16x16 tile: lane l holds column l % 16, rows 4 (l / 16) + v
+  if constexpr (EPI == kBEpiPartial) {
 #pragma unroll
-  for (int i2 = 0; i2 < 2; ++i2)
+    for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wv * 32 + j * 16 + (lane & 15);
-      if (col >= N) continue;
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wv * 32 + j * 16 + (lane & 15);
+        if (col >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = i2 * 16 + 4 * (lane >> 4) + v;
+          if (row < M) Cz[(size_t)row * N + col] = acc[i2][j][v];
+        }
+      }
+  } else if constexpr (EPI == kBEpiSilu) {
+    // gate row 2i and up row 2i + 1 sit in neighbouring lanes
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wv * 32 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float up = __shfl_xor(acc[i2][j][v], 1, kWave);
+          const int row = i2 * 16 + 4 * (lane >> 4) + v;
+          if (!(col & 1) && col < N && row < e.m) {
+            const float x = silu(acc[i2][j][v]) * up;
+            const uint16_t hi = f32_to_bf16(x);
+            const size_t o = (size_t)row * e.ld_act + (col >> 1);
+            e.act_hi[o] = hi;
+            e.act_lo[o] = f32_to_bf16(x - bf16_to_f32(hi));
+          }
+        }
+      }
+  } else {
+    __shared__ float sbv[4][32];
+    __shared__ int sbi[4][32];
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = i2 * 16 + 4 * (lane >> 4) + v;
-        if (row < M) Cz[(size_t)row * N + col] = acc[i2][j][v];
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = n0 + wv * 32 + j * 16 + (lane & 15);
+          if (col < N) {
+            if (e.logits && row < e.m) e.logits[(size_t)row * N + col] = acc[i2][j][v];
+            if (better(acc[i2][j][v], col, bv, bi)) { bv = acc[i2][j][v]; bi = col; }
+          }
+        }
+        // over the 16 lanes that share this row
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          const float ov = __shfl_xor(bv, o, kWave);
+          const int oi = __shfl_xor(bi, o, kWave);
+          if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        if ((lane & 15) == 0) {
+          sbv[wv][row] = bv;
+          sbi[wv][row] = bi;
+        }
       }
+    __syncthreads();
+    if (tid < e.m) {
+      float bv = sbv[0][tid];
+      int bi = sbi[0][tid];
+#pragma unroll
+      for (int w = 1; w < 4; ++w)
+        if (better(sbv[w][tid], sbi[w][tid], bv, bi)) { bv = sbv[w][tid]; bi = sbi[w][tid]; }
+      e.cand_v[(size_t)tid * e.ncand + n_t] = bv;
+      e.cand_i[(size_t)tid * e.ncand + n_t] = bi;
     }
+  }
 }
 
 static hipError_t launch_sgemm(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
@@ -560,10 +637,37 @@ static hipError_t launch_sgemm(const uint16_t* A_hi, const uint16_t* A_lo, int l
   if (M > 32 || kper % kSgBK) return hipErrorInvalidValue;
   const int nt = (N + kSgRows - 1) / kSgRows;
   dim3 grid((nt + 7) / 8 * 8, 1, splits);
+  const SgEpi e{};
   if (A_lo)
-    hipLaunchKernelGGL(k_sgemm<true>, grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C, M, N, kper, nt);
+    hipLaunchKernelGGL((k_sgemm<true, kBEpiPartial>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C,
+                       M, N, kper, nt, e);
   else
-    hipLaunchKernelGGL(k_sgemm<false>, grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C, M, N, kper, nt);
+    hipLaunchKernelGGL((k_sgemm<false, kBEpiPartial>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C,
+                       M, N, kper, nt, e);
+  return hipGetLastError();
+}
+
+int sgemm_tiles(int N) { return (N + kSgRows - 1) / kSgRows; }
+
+hipError_t launch_sgemm_fused(const BGemmArgs& a, int epi, hipStream_t s) {
+  if (a.m < 1 || a.m > kBatchRows || a.K % kSgBK || (a.ldx & 7) || !a.Xlo) return hipErrorInvalidValue;
+  const int nt = sgemm_tiles(a.N);
+  SgEpi e{};
+  e.m = a.m;
+  e.act_hi = a.act_hi; e.act_lo = a.act_lo; e.ld_act = a.ld_act;
+  e.cand_v = a.cand_v; e.cand_i = a.cand_i; e.ncand = a.ncand; e.logits = a.logits;
+  dim3 grid((nt + 7) / 8 * 8, 1, 1);
+  if (epi == kBEpiSilu) {
+    if (a.N % 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_sgemm<true, kBEpiSilu>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W, a.K,
+                       nullptr, kBatchRows, a.N, a.K, nt, e);
+  } else if (epi == kBEpiArgmax) {
+    if (a.ncand < nt) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_sgemm<true, kBEpiArgmax>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W, a.K,
+                       nullptr, kBatchRows, a.N, a.K, nt, e);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
