@@ -124,8 +124,8 @@ def main():
     if args.kernel is None:
         args.kernel = "lm_head"
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                                   "multi-GPU sharding is not part of this build"}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU (--gpus 1); "
+                                   "the engine has no multi-GPU sharding"}))
         sys.exit(2)
 
     import numpy as np
