@@ -81,6 +81,55 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Reduce-scatter over the wave of NV values per lane (NV a power of two, 2..32):
+// afterwards the 64 / NV consecutive lanes from j * 64 / NV on hold, in v[0], the
+// wave's sum of value j.  Each halving step trades half of the remaining values with
+// a partner lane whose index differs in one more bit and keeps the half that bit
+// selects; the bits left over are then summed whole.  That is NV - 1 + 6 - log2 NV
+// exchanges instead of 6 NV, and the ones inside 16 lanes are DPP moves.  The
+// partners for bits 2 and 3 are lane ^ 7 and lane ^ 15 (the DPP mirrors): they still
+// flip the bit being split and share every bit already split, and the masks used
+// span all 64 lanes, so each lane's value is counted once.
+template <int O>
+__device__ __forceinline__ float lane_exchange(float v) {
+  if constexpr (O == 1) return dpp_move<kDppQuadSwap1>(v);
+  else if constexpr (O == 2) return dpp_move<kDppQuadSwap2>(v);
+  else if constexpr (O == 4) return dpp_move<kDppHalfMirror>(v);  // partner lane ^ 7
+  else if constexpr (O == 8) return dpp_move<kDppMirror>(v);      // partner lane ^ 15
+  else return __shfl_xor(v, O, kWave);
+}
+
+template <int O, int NV>
+__device__ __forceinline__ void rs_step(float (&v)[32], int lane) {
+  constexpr int H = NV / 2;
+  const bool upper = (lane & O) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float send = upper ? v[i] : v[i + H];
+    const float keep = upper ? v[i + H] : v[i];
+    v[i] = keep + lane_exchange<O>(send);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_reduce_scatter(float (&v)[32]) {
+  static_assert(NV >= 2 && NV <= 32 && (NV & (NV - 1)) == 0, "2..32 values, a power of two");
+  const int lane = threadIdx.x & 63;
+  // halving steps on lane bits 5, 4, ... until one value is left per lane
+  if constexpr (NV >= 32) rs_step<32, 32>(v, lane);
+  if constexpr (NV >= 16) rs_step<(NV >= 32 ? 16 : 32), 16>(v, lane);
+  if constexpr (NV >= 8) rs_step<(NV >= 32 ? 8 : NV >= 16 ? 16 : 32), 8>(v, lane);
+  if constexpr (NV >= 4) rs_step<(NV >= 32 ? 4 : NV >= 16 ? 8 : NV >= 8 ? 16 : 32), 4>(v, lane);
+  rs_step<(NV >= 32 ? 2 : NV >= 16 ? 4 : NV >= 8 ? 8 : NV >= 4 ? 16 : 32), 2>(v, lane);
+  // the remaining lane bits are summed whole
+  constexpr int used = NV >= 32 ? 5 : NV >= 16 ? 4 : NV >= 8 ? 3 : NV >= 4 ? 2 : 1;  // bits 5.. consumed
+  if constexpr (used < 5) v[0] += lane_exchange<(used == 1 ? 16 : used == 2 ? 8 : used == 3 ? 4 : 2)>(v[0]);
+  if constexpr (used < 4) v[0] += lane_exchange<(used == 1 ? 8 : used == 2 ? 4 : 2)>(v[0]);
+  if constexpr (used < 3) v[0] += lane_exchange<(used == 1 ? 4 : 2)>(v[0]);
+  if constexpr (used < 2) v[0] += lane_exchange<2>(v[0]);
+  v[0] += lane_exchange<1>(v[0]);
+}
+
 // sum over the block of two values; `red` is LDS with room for 2 * waves floats.
 // Every thread gets the totals.
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {

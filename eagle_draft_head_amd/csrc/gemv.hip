@@ -464,43 +464,44 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
   const int k0 = z * kc;
   const int klen = min(kc, K - k0);
   const int k4 = klen >> 2;
-  for (int m = 0; m < M; ++m) {
-    float4* dst = reinterpret_cast<float4*>(xs + m * kc);
-    if (m >= rows) {
-      for (int i = threadIdx.x; i < k4; i += blockDim.x) dst[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      continue;
-    }
-#pragma unroll 4
-    for (int i = threadIdx.x; i < k4; i += blockDim.x) {
-      const int k = k0 + 4 * i;
-      const float* src;
-      if (x1) {
-        const int sgi = k / seg;
-        src = (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2)) + (size_t)m * seg + (k - sgi * seg);
-      } else {
-        src = x0 + (size_t)m * K + k;
-      }
-      dst[i] = *reinterpret_cast<const float4*>(src);
-    }
-  }
-  __syncthreads();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  if (row0 >= N) return;
+  const int nch = klen >> 3;
   const uint4* wp[R];
 #pragma unroll
   for (int r = 0; r < R; ++r)
     wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * K + k0);
+  // stage the M vectors: one flat loop over all M * k4 float4 of the chunk, so every
+  // thread's loads are in flight together (vectors past `rows` are zero)
+  {
+    float4* dst = reinterpret_cast<float4*>(xs);
+    const int total = M * k4;
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+      const int m = idx / k4, i = idx - m * k4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m < rows) {
+        const int k = k0 + 4 * i;
+        const float* src;
+        if (x1) {
+          const int sgi = k / seg;
+          src = (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2)) + (size_t)m * seg + (k - sgi * seg);
+        } else {
+          src = x0 + (size_t)m * K + k;
+        }
+        v = *reinterpret_cast<const float4*>(src);
+      }
+      dst[(size_t)m * (kc >> 2) + i] = v;
+    }
+  }
+  __syncthreads();
+  if (row0 >= N) return;
   float acc[R][M];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-  const int nch = klen >> 3;
-  for (int c = lane; c < nch; c += 64) {
-    uint4 w[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = ld_stream(wp[r] + c);
+  auto apply = [&](int c, const uint4 (&w)[R]) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const float4* x4 = reinterpret_cast<const float4*>(xs + m * kc);
@@ -508,17 +509,28 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r][m] = dot8(w[r], a, b, acc[r][m]);
     }
+  };
+  for (int c = lane; c < nch; c += 64) {
+    uint4 w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[r] = ld_stream(wp[r] + c);
+    apply(c, w);
   }
+  // the R * M sums: one reduce-scatter over the wave (padded with zeros to a power
+  // of two), then one store per lane group
+  constexpr int NVAL = R * M;
+  static_assert(NVAL <= 32, "accumulators per lane");
+  constexpr int NV = NVAL <= 8 ? 8 : (NVAL <= 16 ? 16 : 32);
+  float v[32];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
-  float* Pz = P + (size_t)z * M * N;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-      if (lane == ((r * M + m) & 63) && row0 + r < N) Pz[(size_t)m * N + row0 + r] = acc[r][m];
+  for (int i = 0; i < 32; ++i) v[i] = i < NVAL ? acc[(i % NVAL) / M][(i % NVAL) % M] : 0.f;
+  wave_reduce_scatter<NV>(v);
+  constexpr int GL = 64 / NV;
+  const int j = lane / GL;
+  if (lane % GL == 0 && j < NVAL) {
+    const int r = j / M, m = j - r * M;
+    if (row0 + r < N) P[((size_t)z * M + m) * N + row0 + r] = v[0];
+  }
 }
 
 // ---------------------------------------------------------------------------
