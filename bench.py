@@ -91,12 +91,15 @@ def kernel_bytes_step(cfg, L: int, gamma: int, kv_bytes: int = 4) -> float:
     return 2.0 * p_step + 8 * n + 2 * n + rows * 2 * kv_bytes * kvd
 
 
-def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4) -> float:
+def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
+               stored: bool = False) -> float:
     """Algorithmic HBM bytes of one round: encode, gamma draft steps, rebuild (K/V
-    elements of kv_bytes bytes)."""
+    elements of kv_bytes bytes).  stored: the encode is the rebuild's extra row (the
+    next boundary: its taps in, the feature and its weighted copy out) on the
+    rebuild's one pass over W_fc."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
-    tot = 6.0 * n * n + 12 * n                         # encode: W_fc + aux
+    tot = 12.0 * n + 8 * n + 4 if stored else 6.0 * n * n + 12 * n   # encode: W_fc + aux
     for j in range(gamma):
         rows = L + j                                      # rows attended before the new one
         tot += 2.0 * p_step + 8 * n + 2 * n + (rows + 1) * 2 * kv_bytes * kvd
@@ -119,6 +122,12 @@ def main():
                     help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
+    ap.add_argument("--boundary", choices=["stored", "taps"], default="stored",
+                    help="stored: each rebuild also encodes the next round's boundary taps (one "
+                         "W_fc pass) and the chain starts from that feature, the context growing "
+                         "by a+1 rows per round around a mean of the workload's length; taps: the "
+                         "chain encodes the boundary taps itself and every round is rewound to "
+                         "the workload's length")
     args = ap.parse_args()
     args.kernel_set = args.kernel is not None
     if args.kernel is None:
@@ -146,7 +155,18 @@ def main():
     wd = gen.drafter_weights(cfg, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    max_ctx = L + 64
+    nsteps = args.steps + args.warmup
+    stored = args.boundary == "stored"
+    accepted = [i % (gamma + 1) for i in range(nsteps)]
+    if stored:
+        # committed rows before step i; the start is chosen so that the mean over
+        # the timed steps is L
+        grow = np.cumsum([0] + [a + 1 for a in accepted])
+        L0 = L - int(round(float(grow[args.warmup:nsteps].mean())))
+        L_at = [L0 + int(g) for g in grow[:nsteps]]
+    else:
+        L_at = [L] * nsteps
+    max_ctx = max(L, max(L_at)) + gamma + 64
     kv_dtype = B.KV_BF16 if args.kv == "bf16" else B.KV_F32
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype)
     stream = torch.cuda.current_stream()
@@ -170,20 +190,40 @@ def main():
     n = cfg.n_embd
     prefill_flop = 2.0 * L * 3 * n * n + 2.0 * L * 2 * n * 2 * cfg.kv_dim
 
-    nsteps = args.steps + args.warmup
-    b_aux = gen.aux_taps(cfg, 1, nsteps, device=dev)
+    b_aux = gen.aux_taps(cfg, 1, nsteps + 1, device=dev)
     b_tok = gen.tokens(cfg, 1, nsteps, device=dev)
     r_aux = gen.aux_taps(cfg, 2, nsteps * (gamma + 1), device=dev)
     r_tok = gen.tokens(cfg, 2, nsteps * (gamma + 1), device=dev)
+    # a rebuild's first row is the round's boundary (taps, token)
+    for i in range(nsteps):
+        for x, b in zip(r_aux, b_aux):
+            x[i * (gamma + 1)].copy_(b[i])
+        r_tok[i * (gamma + 1)] = b_tok[i]
     out = torch.empty((1, gamma), dtype=torch.int32, device=dev)
-    accepted = [i % (gamma + 1) for i in range(nsteps)]
+    torch.cuda.synchronize()
 
-    def step(i):
-        dr.draft_chain([0], b_tok[i:i + 1], [a[i:i + 1] for a in b_aux], gamma, out=out)
+    def reset(i):
+        """The state before step i: L_at[i] committed rows and (stored) the boundary
+        feature of step i (a boundary-only prefill).  Untimed."""
+        dr.rewind(0, L_at[i])
+        if stored:
+            dr.prefill(0, r_tok[:0], [], next_aux=[a[i:i + 1] for a in b_aux])
+
+    def chain(i):
+        dr.draft_chain([0], b_tok[i:i + 1], None if stored else [a[i:i + 1] for a in b_aux], gamma,
+                       out=out)
+
+    def rebuild(i):
         a = accepted[i]
         r0 = i * (gamma + 1)
-        dr.rebuild_after_verify([0], [a], r_tok[r0:r0 + a + 1], [x[r0:r0 + a + 1] for x in r_aux])
-        dr.rewind(0, L)
+        dr.rebuild_after_verify([0], [a], r_tok[r0:r0 + a + 1], [x[r0:r0 + a + 1] for x in r_aux],
+                                next_aux=[x[i + 1:i + 2] for x in b_aux] if stored else None)
+        if not stored:
+            dr.rewind(0, L)
+
+    def step(i):
+        chain(i)
+        rebuild(i)
 
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -192,6 +232,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    reset(0)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -202,6 +243,8 @@ def main():
     elapsed = time.perf_counter() - t_start
     # the same steps again with HIP events around every launch of the measured
     # kernel on its stream (events add gaps, so this pass is not the one timed above)
+    reset(args.warmup)
+    torch.cuda.synchronize()
     B.eagle3_profile_enable(dr.ctx, args.kernel, True)
     for i in range(args.warmup, nsteps):
         step(i)
@@ -213,20 +256,20 @@ def main():
     # every draft_chain call, in a pass of its own), then the encode kernel's time
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    reset(args.warmup)
     for k, i in enumerate(range(args.warmup, nsteps)):
         e0, e1, e2 = ev[k]
         e0.record(stream)
-        dr.draft_chain([0], b_tok[i:i + 1], [a[i:i + 1] for a in b_aux], gamma, out=out)
+        chain(i)
         e1.record(stream)
-        a = accepted[i]
-        r0 = i * (gamma + 1)
-        dr.rebuild_after_verify([0], [a], r_tok[r0:r0 + a + 1], [x[r0:r0 + a + 1] for x in r_aux])
-        dr.rewind(0, L)
+        rebuild(i)
         e2.record(stream)
     torch.cuda.synchronize()
     round_ms = sorted(e0.elapsed_time(e2) for e0, _, e2 in ev)
     chain_ms = sorted(e0.elapsed_time(e1) for e0, e1, _ in ev)
     pct = lambda v, q: v[min(len(v) - 1, int(q * len(v)))]
+    reset(args.warmup)
+    torch.cuda.synchronize()
     B.eagle3_profile_enable(dr.ctx, "encode", True)
     for i in range(args.warmup, nsteps):
         step(i)
@@ -242,7 +285,7 @@ def main():
     kvb = 2 if args.kv == "bf16" else 4
     k_bytes = kernel_bytes(cfg, args.kernel, L, kvb)
     achieved = k_bytes / k_avg_s / 1e9
-    sb = [step_bytes(cfg, L, gamma, accepted[i], kvb) for i in range(args.warmup, nsteps)]
+    sb = [step_bytes(cfg, L_at[i], gamma, accepted[i], kvb, stored) for i in range(args.warmup, nsteps)]
     step_gbs = (sum(sb) / args.steps) / (elapsed / args.steps) / 1e9
 
     cpu = None
@@ -264,9 +307,15 @@ def main():
         "data": "synthetic (seeded; random-init weights of the drafter architecture)",
         "config": {"workload": f"{cfg.name} drafter: n_embd {cfg.n_embd}, {cfg.n_head}/{cfg.n_head_kv} "
                                f"heads x {cfg.head_dim}, n_ff {cfg.n_ff}, draft vocab {cfg.draft_vocab}, "
-                               f"target vocab {cfg.target_vocab}, {L} committed KV rows",
+                               f"target vocab {cfg.target_vocab}, {L} committed KV rows"
+                               + (f" (mean over the timed rounds; {L_at[args.warmup]}.."
+                                  f"{L_at[-1]})" if stored else ""),
                    "batch": 1, "gamma": gamma,
-                   "step": "draft_chain + rebuild_after_verify(a+1 rows, a cycling 0..3) + rewind"},
+                   "step": ("draft_chain from the stored boundary feature + rebuild_after_verify("
+                            f"a+1 rows, a cycling 0..{gamma}, with the next boundary's taps)")
+                   if stored else
+                   f"draft_chain(boundary taps) + rebuild_after_verify(a+1 rows, a cycling 0..{gamma}) "
+                   "+ rewind"},
         "roofline": {"bound": "hbm", "kernel": args.kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": committed_traffic(args.kernel), "avg_launch_us": round(k_avg_s * 1e6, 3),

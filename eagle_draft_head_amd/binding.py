@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libeagle3.so")
 
 OK, E_INVAL, E_SHAPE, E_UNSUPPORTED, E_CAPACITY, E_STATE, E_HIP, E_OOM = 0, -1, -2, -3, -4, -5, -6, -7
 KEEP_SPEC = 1
+STORED_BOUNDARY = 2
 KV_F32, KV_BF16 = 0, 1
 
 ERR_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_SHAPE: "E_SHAPE", E_UNSUPPORTED: "E_UNSUPPORTED",
@@ -69,11 +70,11 @@ def library() -> ctypes.CDLL:
         "eagle3_resolve_rope_dim": ([c_int32, c_float, c_int32, POINTER(c_int32)], ctypes.c_int),
         "eagle3_load": ([POINTER(eagle3_config), POINTER(eagle3_weights), P, POINTER(P)], ctypes.c_int),
         "eagle3_free": ([P], ctypes.c_int),
-        "eagle3_prefill": ([P, c_int32, c_int32, P, P, P, P, P], ctypes.c_int),
+        "eagle3_prefill": ([P, c_int32, c_int32, P, P, P, P, P, P, P, P], ctypes.c_int),
         "eagle3_draft_chain": ([P, c_int32, POINTER(c_int32), P, P, P, P, c_int32, c_uint32, P,
                                 POINTER(c_int32), POINTER(eagle3_debug), P], ctypes.c_int),
         "eagle3_rebuild_after_verify": ([P, c_int32, POINTER(c_int32), POINTER(c_int32), P, P, P,
-                                         P, P], ctypes.c_int),
+                                         P, P, P, P, P], ctypes.c_int),
         "eagle3_rewind": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_kv_len": ([P, c_int32, POINTER(c_int32), POINTER(c_int32)], ctypes.c_int),
         "eagle3_kv_read": ([P, c_int32, c_int32, c_int32, P, P, P], ctypes.c_int),
@@ -82,9 +83,9 @@ def library() -> ctypes.CDLL:
         "eagle3_profile_read": ([P, POINTER(c_double), POINTER(c_int64)], ctypes.c_int),
         "eagle3_ledger_create": ([c_int32, c_int32, c_int32, POINTER(P)], ctypes.c_int),
         "eagle3_ledger_destroy": ([P], None),
-        "eagle3_ledger_prefill": ([P, c_int32, c_int32], ctypes.c_int),
+        "eagle3_ledger_prefill": ([P, c_int32, c_int32, c_int32], ctypes.c_int),
         "eagle3_ledger_chain": ([P, c_int32, c_int32, c_uint32, POINTER(c_int32)], ctypes.c_int),
-        "eagle3_ledger_rebuild": ([P, c_int32, c_int32], ctypes.c_int),
+        "eagle3_ledger_rebuild": ([P, c_int32, c_int32, c_int32], ctypes.c_int),
         "eagle3_ledger_rewind": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_ledger_len": ([P, c_int32, POINTER(c_int32), POINTER(c_int32)], ctypes.c_int),
     }
@@ -177,9 +178,11 @@ def eagle3_free(ctx: int) -> None:
     library().eagle3_free(ctx)
 
 
-def eagle3_prefill(ctx, seq: int, T: int, tok, aux0, aux1, aux2, stream=None) -> None:
+def eagle3_prefill(ctx, seq: int, T: int, tok, aux0, aux1, aux2, next_aux0=None, next_aux1=None,
+                   next_aux2=None, stream=None) -> None:
     _check(ctx, library().eagle3_prefill(ctx, seq, T, _ptr(tok), _ptr(aux0), _ptr(aux1),
-                                         _ptr(aux2), _stream(stream)))
+                                         _ptr(aux2), _ptr(next_aux0), _ptr(next_aux1),
+                                         _ptr(next_aux2), _stream(stream)))
 
 
 def eagle3_draft_chain(ctx, seq_ids: Sequence[int], boundary_tok, aux0, aux1, aux2, gamma: int,
@@ -200,12 +203,15 @@ def eagle3_draft_chain(ctx, seq_ids: Sequence[int], boundary_tok, aux0, aux1, au
 
 
 def eagle3_rebuild_after_verify(ctx, seq_ids: Sequence[int], n_accepted: Sequence[int], tok, aux0,
-                                aux1, aux2, stream=None) -> None:
+                                aux1, aux2, next_aux0=None, next_aux1=None, next_aux2=None,
+                                stream=None) -> None:
     n = len(seq_ids)
     ids = (c_int32 * n)(*seq_ids)
     acc = (c_int32 * n)(*n_accepted)
     _check(ctx, library().eagle3_rebuild_after_verify(ctx, n, ids, acc, _ptr(tok), _ptr(aux0),
-                                                      _ptr(aux1), _ptr(aux2), _stream(stream)))
+                                                      _ptr(aux1), _ptr(aux2), _ptr(next_aux0),
+                                                      _ptr(next_aux1), _ptr(next_aux2),
+                                                      _stream(stream)))
 
 
 def eagle3_rewind(ctx, seq: int, new_len: int) -> None:
@@ -254,16 +260,17 @@ class HostLedger:
             library().eagle3_ledger_destroy(self._h)
             self._h = None
 
-    def prefill(self, seq, T) -> int:
-        return library().eagle3_ledger_prefill(self._h, seq, T)
+    def prefill(self, seq, T, boundary=False) -> int:
+        return library().eagle3_ledger_prefill(self._h, seq, T, int(boundary))
 
-    def chain(self, seq, gamma, keep_spec=False):
+    def chain(self, seq, gamma, keep_spec=False, stored_boundary=False):
         g = c_int32(-1)
-        rc = library().eagle3_ledger_chain(self._h, seq, gamma, KEEP_SPEC if keep_spec else 0, byref(g))
+        flags = (KEEP_SPEC if keep_spec else 0) | (STORED_BOUNDARY if stored_boundary else 0)
+        rc = library().eagle3_ledger_chain(self._h, seq, gamma, flags, byref(g))
         return rc, g.value
 
-    def rebuild(self, seq, a) -> int:
-        return library().eagle3_ledger_rebuild(self._h, seq, a)
+    def rebuild(self, seq, a, boundary=False) -> int:
+        return library().eagle3_ledger_rebuild(self._h, seq, a, int(boundary))
 
     def rewind(self, seq, new_len) -> int:
         return library().eagle3_ledger_rewind(self._h, seq, new_len)

@@ -324,9 +324,13 @@ __global__ __launch_bounds__(kBRowThreads) void k_bprep(const BPrepArgs a) {
     ev[j] = make_float4(bf16_lo(ew.x), bf16_hi(ew.x), bf16_lo(ew.y), bf16_hi(ew.y));
     se += sq4(ev[j]);
     if (a.step == 0) {
-      for (int z = 0; z < a.S_enc; ++z) {
-        const float4 p = reinterpret_cast<const float4*>(a.Penc + ((size_t)z * kBatchRows + r) * n)[v];
-        gv[j].x += p.x; gv[j].y += p.y; gv[j].z += p.z; gv[j].w += p.w;
+      if (a.bnd) {
+        gv[j] = reinterpret_cast<const float4*>(a.bnd + (size_t)a.br.slot[r] * n)[v];
+      } else {
+        for (int z = 0; z < a.S_enc; ++z) {
+          const float4 p = reinterpret_cast<const float4*>(a.Penc + ((size_t)z * kBatchRows + r) * n)[v];
+          gv[j].x += p.x; gv[j].y += p.y; gv[j].z += p.z; gv[j].w += p.w;
+        }
       }
       reinterpret_cast<float4*>(a.G + (size_t)r * n)[v] = gv[j];
       if (a.dbg_hidden) reinterpret_cast<float4*>(a.dbg_hidden + (size_t)orig * (a.gamma + 1) * n)[v] = gv[j];

@@ -74,6 +74,10 @@ struct eagle3_ctx {
         *ao = nullptr, *part_o = nullptr, *part_ml = nullptr, *lm_pv = nullptr;
   int x1_count = 0;
   int32_t *lm_pi = nullptr, *lm_pt = nullptr, *tok_slots = nullptr;
+  // stored boundary features per sequence slot (set by prefill / rebuild when the
+  // next round's boundary taps come with them): f [max_seqs][n], f * hidden_norm
+  // [max_seqs][n] and sum f^2 [max_seqs]
+  float *bnd_y = nullptr, *bnd_w = nullptr, *bnd_ssq = nullptr;
 
   int tf_rows = 0;
   size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
@@ -382,6 +386,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->lm_pi, size_t(c->lm_grid)));
   E3_TRY(dalloc(c, &c->lm_pt, size_t(c->lm_grid)));
   E3_TRY(dalloc(c, &c->tok_slots, size_t(cfg->max_gamma) + 1));
+  E3_TRY(dalloc(c, &c->bnd_y, size_t(cfg->max_seqs) * n));
+  E3_TRY(dalloc(c, &c->bnd_w, size_t(cfg->max_seqs) * n));
+  E3_TRY(dalloc(c, &c->bnd_ssq, size_t(cfg->max_seqs)));
   E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
 
   c->tf_rows = c->cap < 2048 ? c->cap : 2048;
@@ -588,52 +595,89 @@ struct AppendSeg {
   int seq, row0, T, pos0;
 };
 
+// The next rounds' boundary taps that come with an append: count rows of
+// three fp32 streams [count][n]; row j is the boundary of sequence slot slots[j].
+struct BndIn {
+  const float* y[3] = {nullptr, nullptr, nullptr};
+  std::vector<int32_t> slots;
+  int count() const { return int(slots.size()); }
+};
+
+// Teacher-forced rows (segments of `total` packed rows) and then the boundary rows,
+// in passes of up to tf_rows rows (at most kBndRows of them boundary rows): W_fc is
+// streamed once per pass for all of its rows; the K/V projection, rotation and
+// store run for the teacher-forced rows, the boundary rows end in the per-slot
+// boundary features.
 int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, const int32_t* tok,
-                const float* a0, const float* a1, const float* a2, hipStream_t s) {
+                const float* a0, const float* a1, const float* a2, const BndIn& bi, hipStream_t s) {
   const int n = c->n, kvd2 = 2 * c->kvd;
+  const int all = total + bi.count();
   size_t seg_i = 0;
-  for (int c0 = 0; c0 < total; c0 += c->tf_rows) {
-    const int T = std::min(c->tf_rows, total - c0);
+  for (int c0 = 0; c0 < all;) {
+    int P = std::min(c->tf_rows, all - c0);
+    const int T = std::max(0, std::min(total, c0 + P) - c0);  // teacher-forced rows of the pass
+    int Tb = P - T;
+    if (Tb > e3::kBndRows) {
+      Tb = e3::kBndRows;
+      P = T + Tb;
+    }
+    const int b0 = std::max(c0, total) - total;  // first boundary row of the pass
+    e3::TapRowsB yb = e3::no_tap_rows_b();
+    e3::BndOut bo{};
+    const float *x0 = a0 + size_t(c0) * n, *x1 = a1 + size_t(c0) * n, *x2 = a2 + size_t(c0) * n;
+    if (Tb > 0) {
+      for (int k = 0; k < 3; ++k) yb.y[k] = bi.y[k] + size_t(b0) * n;
+      yb.rows_x = T;
+      if (T == 0) {
+        x0 = yb.y[0];
+        x1 = yb.y[1];
+        x2 = yb.y[2];
+      }
+      bo.y = c->bnd_y;
+      bo.yw = c->bnd_w;
+      bo.ssq = c->bnd_ssq;
+      bo.count = Tb;
+      for (int j = 0; j < Tb; ++j) bo.slot[j] = bi.slots[size_t(b0 + j)];
+    }
     int sp1 = 1, sp2 = 1;
     size_t f_split = 0, p_split = 0;
-    if (T <= 16) {
-      // weight-streaming path: every weight chunk applied to all T rows
-      const int M = e3::gemv_multi_width(T);
+    if (P <= 16) {
+      // weight-streaming path: every weight chunk applied to all rows of the pass
       {
         ProfScope ps(c, 7, s);
-        E3_HIP(c, e3::launch_gemv_multi(c->w_fc, n, 3 * n, a0 + size_t(c0) * n, a1 + size_t(c0) * n,
-                                        a2 + size_t(c0) * n, n, T, c->tf_F, &sp1, s), "fc gemv");
+        E3_HIP(c, e3::launch_gemv_multi(c->w_fc, n, 3 * n, x0, x1, x2, n, P, c->tf_F, &sp1, s, yb),
+               "fc gemv");
       }
-      f_split = size_t(M) * n;
+      f_split = size_t(e3::gemv_multi_width(P)) * n;
       E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
-                                  c->nrm_hid, c->cfg.rms_eps, nullptr, nullptr, c->tf_cat32, s),
+                                  c->nrm_hid, c->cfg.rms_eps, nullptr, nullptr, c->tf_cat32, s, &bo),
              "tf cat");
-      {
+      if (T > 0) {
         ProfScope ps(c, 8, s);
         E3_HIP(c, e3::launch_gemv_multi(c->w_qkv + size_t(c->qd) * 2 * n, kvd2, 2 * n, c->tf_cat32,
                                         nullptr, nullptr, 0, T, c->tf_P, &sp2, s), "kv gemv");
       }
-      p_split = size_t(M) * kvd2;
+      p_split = size_t(e3::gemv_multi_width(T > 0 ? T : 1)) * kvd2;
     } else {
       // MFMA path
-      E3_HIP(c, e3::launch_pack_aux(a0 + size_t(c0) * n, a1 + size_t(c0) * n, a2 + size_t(c0) * n,
-                                    T, n, c->tf_A, c->tf_A_lo, s), "pack aux");
-      e3::GemmPlan p1 = e3::gemm_plan(T, n, 3 * n);
-      while (p1.splits > 1 && size_t(p1.splits) * T * n > c->tf_F_cap) p1.splits /= 2;
+      E3_HIP(c, e3::launch_pack_aux(x0, x1, x2, P, n, c->tf_A, c->tf_A_lo, s, yb), "pack aux");
+      e3::GemmPlan p1 = e3::gemm_plan(P, n, 3 * n);
+      while (p1.splits > 1 && size_t(p1.splits) * P * n > c->tf_F_cap) p1.splits /= 2;
       sp1 = p1.splits;
       {
         ProfScope ps(c, 7, s);
-        E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, T, n,
+        E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, P, n,
                                        3 * n, p1, s), "fc gemm");
       }
-      f_split = size_t(T) * n;
+      f_split = size_t(P) * n;
       E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
-                                  c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s),
+                                  c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s,
+                                  &bo),
              "tf cat");
-      e3::GemmPlan p2 = e3::gemm_plan(T, kvd2, 2 * n);
-      while (p2.splits > 1 && size_t(p2.splits) * T * kvd2 > c->tf_P_cap) p2.splits /= 2;
-      sp2 = p2.splits;
-      {
+      if (T > 0) {
+        e3::GemmPlan p2 = e3::gemm_plan(T, kvd2, 2 * n);
+        while (p2.splits > 1 && size_t(p2.splits) * T * kvd2 > c->tf_P_cap) p2.splits /= 2;
+        sp2 = p2.splits;
         ProfScope ps(c, 8, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n,
                                        c->w_qkv + size_t(c->qd) * 2 * n, 2 * n, c->tf_P, T, kvd2,
@@ -641,31 +685,44 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       }
       p_split = size_t(T) * kvd2;
     }
-    // store the rows of this pass into each segment's cache rows, up to
-    // kStoreSegs segments per launch
-    e3::StoreSegs ss{};
-    auto flush = [&]() -> int {
-      if (ss.n == 0) return EAGLE3_OK;
-      E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, ss, c->nkv, c->hd, c->rot, c->inv_freq,
-                                    c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s), "tf store");
-      ss = e3::StoreSegs{};
-      return EAGLE3_OK;
-    };
-    for (; seg_i < segs.size(); ++seg_i) {
-      const AppendSeg& g = segs[seg_i];
-      const int lo = std::max(g.row0, c0), hi = std::min(g.row0 + g.T, c0 + T);
-      if (hi > lo) {
-        if (ss.n == e3::kStoreSegs)
-          if (int rc = flush()) return rc;
-        ss.row0[ss.n] = lo - c0;
-        ss.pos0[ss.n] = g.pos0 + (lo - g.row0);
-        ss.slot[ss.n] = g.seq;
-        ss.row0[++ss.n] = hi - c0;
+    if (T > 0) {
+      // store the rows of this pass into each segment's cache rows, up to
+      // kStoreSegs segments per launch
+      e3::StoreSegs ss{};
+      auto flush = [&]() -> int {
+        if (ss.n == 0) return EAGLE3_OK;
+        E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, ss, c->nkv, c->hd, c->rot, c->inv_freq,
+                                      c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s), "tf store");
+        ss = e3::StoreSegs{};
+        return EAGLE3_OK;
+      };
+      for (; seg_i < segs.size(); ++seg_i) {
+        const AppendSeg& g = segs[seg_i];
+        const int lo = std::max(g.row0, c0), hi = std::min(g.row0 + g.T, c0 + T);
+        if (hi > lo) {
+          if (ss.n == e3::kStoreSegs)
+            if (int rc = flush()) return rc;
+          ss.row0[ss.n] = lo - c0;
+          ss.pos0[ss.n] = g.pos0 + (lo - g.row0);
+          ss.slot[ss.n] = g.seq;
+          ss.row0[++ss.n] = hi - c0;
+        }
+        if (g.row0 + g.T > c0 + T) break;  // continues in the next pass
       }
-      if (g.row0 + g.T > c0 + T) break;  // continues in the next pass
+      if (int rc = flush()) return rc;
     }
-    if (int rc = flush()) return rc;
+    c0 += P;
   }
+  return EAGLE3_OK;
+}
+
+// next-boundary tap pointers: all three or none
+int check_next_taps(eagle3_ctx* c, const float* b0, const float* b1, const float* b2, bool* given) {
+  *given = b0 || b1 || b2;
+  if (*given && !(b0 && b1 && b2))
+    return set_err(c, EAGLE3_E_INVAL, "next-boundary taps: give all three streams or none");
+  if (*given && (!aligned16(b0) || !aligned16(b1) || !aligned16(b2)))
+    return set_err(c, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
   return EAGLE3_OK;
 }
 
@@ -673,28 +730,44 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
 
 int eagle3_prefill(eagle3_ctx* ctx, int32_t seq, int32_t T, const int32_t* tok_dev,
                    const float* aux0_dev, const float* aux1_dev, const float* aux2_dev,
-                   void* stream) {
+                   const float* next_aux0_dev, const float* next_aux1_dev,
+                   const float* next_aux2_dev, void* stream) {
   if (!ctx) return EAGLE3_E_INVAL;
   const char* why = nullptr;
   int rc = ctx->ledger.check_prefill(seq, T, &why);
   if (rc) return set_err(ctx, rc, why);
-  if (T == 0) return EAGLE3_OK;
-  if (!tok_dev || !aux0_dev || !aux1_dev || !aux2_dev)
-    return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
-  if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
-    return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
-  const int32_t start = ctx->ledger.seq(seq).committed;
-  std::vector<AppendSeg> segs{{seq, 0, T, start}};
-  rc = append_rows(ctx, segs, T, tok_dev, aux0_dev, aux1_dev, aux2_dev, as_stream(stream));
+  bool next = false;
+  rc = check_next_taps(ctx, next_aux0_dev, next_aux1_dev, next_aux2_dev, &next);
   if (rc) return rc;
-  ctx->ledger.do_prefill(seq, T);
+  if (T == 0 && !next) return EAGLE3_OK;
+  if (T > 0) {
+    if (!tok_dev || !aux0_dev || !aux1_dev || !aux2_dev)
+      return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
+    if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
+      return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  }
+  const int32_t start = ctx->ledger.seq(seq).committed;
+  std::vector<AppendSeg> segs;
+  if (T > 0) segs.push_back({seq, 0, T, start});
+  BndIn bi;
+  if (next) {
+    bi.y[0] = next_aux0_dev;
+    bi.y[1] = next_aux1_dev;
+    bi.y[2] = next_aux2_dev;
+    bi.slots.push_back(seq);
+  }
+  rc = append_rows(ctx, segs, T, tok_dev, aux0_dev, aux1_dev, aux2_dev, bi, as_stream(stream));
+  if (rc) return rc;
+  ctx->ledger.do_prefill(seq, T, next);
   return EAGLE3_OK;
 }
 
 int eagle3_rebuild_after_verify(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_host,
                                 const int32_t* n_accepted_host, const int32_t* tok_dev,
                                 const float* aux0_dev, const float* aux1_dev,
-                                const float* aux2_dev, void* stream) {
+                                const float* aux2_dev, const float* next_aux0_dev,
+                                const float* next_aux1_dev, const float* next_aux2_dev,
+                                void* stream) {
   if (!ctx) return EAGLE3_E_INVAL;
   if (n_seq < 0 || (n_seq > 0 && (!seq_ids_host || !n_accepted_host)))
     return set_err(ctx, EAGLE3_E_INVAL, "bad sequence list");
@@ -703,21 +776,31 @@ int eagle3_rebuild_after_verify(eagle3_ctx* ctx, int32_t n_seq, const int32_t* s
     return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
   if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
     return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  bool next = false;
+  int rc = check_next_taps(ctx, next_aux0_dev, next_aux1_dev, next_aux2_dev, &next);
+  if (rc) return rc;
   std::vector<AppendSeg> segs;
+  BndIn bi;
   int total = 0;
   for (int b = 0; b < n_seq; ++b) {
     const char* why = nullptr;
     const int s = seq_ids_host[b];
-    int rc = ctx->ledger.check_rebuild(s, n_accepted_host[b], &why);
+    rc = ctx->ledger.check_rebuild(s, n_accepted_host[b], &why);
     if (rc) return set_err(ctx, rc, why);
     for (int j = 0; j < b; ++j)
       if (seq_ids_host[j] == s) return set_err(ctx, EAGLE3_E_INVAL, "duplicate sequence id");
     segs.push_back({s, total, n_accepted_host[b] + 1, ctx->ledger.seq(s).committed});
     total += n_accepted_host[b] + 1;
+    if (next) bi.slots.push_back(s);
   }
-  int rc = append_rows(ctx, segs, total, tok_dev, aux0_dev, aux1_dev, aux2_dev, as_stream(stream));
+  if (next) {
+    bi.y[0] = next_aux0_dev;
+    bi.y[1] = next_aux1_dev;
+    bi.y[2] = next_aux2_dev;
+  }
+  rc = append_rows(ctx, segs, total, tok_dev, aux0_dev, aux1_dev, aux2_dev, bi, as_stream(stream));
   if (rc) return rc;
-  for (int b = 0; b < n_seq; ++b) ctx->ledger.do_rebuild(seq_ids_host[b], n_accepted_host[b]);
+  for (int b = 0; b < n_seq; ++b) ctx->ledger.do_rebuild(seq_ids_host[b], n_accepted_host[b], next);
   return EAGLE3_OK;
 }
 
@@ -729,7 +812,7 @@ namespace {
 // weights once for all rows still drafting.
 int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
                         const int32_t* btok, const float* a0, const float* a1, const float* a2,
-                        int32_t gamma, int32_t* out, const std::vector<int32_t>& geff,
+                        bool stored, int32_t gamma, int32_t* out, const std::vector<int32_t>& geff,
                         const eagle3_debug* dbg, hipStream_t s) {
   using e3::kBatchRows;
   const int n = c->n;
@@ -777,7 +860,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       return gemm(W, N, K, xh, xl, ldx, m, bp, e3::kBEpiPartial);
     };
     int S_enc = 0;
-    {
+    if (!stored) {
       ProfScope ps(c, 6, s);
       E3_HIP(c, e3::launch_bpack_aux(br, a0, a1, a2, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, s), "pack");
       E3_HIP(c, proj(c->w_fc, n, 3 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, br.m, c->tp_enc,
@@ -793,6 +876,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       pa.d2t = c->d2t; pa.dv = c->dv; pa.out_ids = out; pa.embed = c->embed; pa.vocab = c->vt;
       pa.n = n; pa.w_in = c->nrm_in; pa.w_hid = c->nrm_hid; pa.eps = c->cfg.rms_eps;
       pa.G = c->b_G; pa.Penc = c->b_P; pa.S_enc = S_enc;
+      pa.bnd = stored ? c->bnd_y : nullptr;
       pa.Xhi = c->bx_a_hi; pa.Xlo = c->bx_a_lo; pa.ldx = c->bld_a;
       pa.dbg_hidden = dbg ? dbg->hidden : nullptr;
       const int Nqkv = c->qd + 2 * c->kvd;
@@ -907,17 +991,25 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
   if (!ctx) return EAGLE3_E_INVAL;
   if (n_seq < 0 || (n_seq > 0 && (!seq_ids_host || !gamma_eff_host)))
     return set_err(ctx, EAGLE3_E_INVAL, "bad sequence list");
-  if (flags & ~EAGLE3_KEEP_SPEC) return set_err(ctx, EAGLE3_E_INVAL, "unknown flag");
+  if (flags & ~(EAGLE3_KEEP_SPEC | EAGLE3_STORED_BOUNDARY))
+    return set_err(ctx, EAGLE3_E_INVAL, "unknown flag");
   if (n_seq == 0) return EAGLE3_OK;
-  if (!boundary_tok_dev || !aux0_dev || !aux1_dev || !aux2_dev || (gamma > 0 && !out_ids_dev))
+  const bool stored = (flags & EAGLE3_STORED_BOUNDARY) != 0;
+  if (!boundary_tok_dev || (gamma > 0 && !out_ids_dev))
     return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
-  if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
-    return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  if (stored) {
+    if (aux0_dev || aux1_dev || aux2_dev)
+      return set_err(ctx, EAGLE3_E_INVAL, "taps given with EAGLE3_STORED_BOUNDARY");
+  } else {
+    if (!aux0_dev || !aux1_dev || !aux2_dev) return set_err(ctx, EAGLE3_E_INVAL, "null input pointer");
+    if (!aligned16(aux0_dev) || !aligned16(aux1_dev) || !aligned16(aux2_dev))
+      return set_err(ctx, EAGLE3_E_INVAL, "tap pointers must be 16-byte aligned");
+  }
   std::vector<int32_t> geff((size_t)n_seq);
   for (int b = 0; b < n_seq; ++b) {
     const char* why = nullptr;
     const int s = seq_ids_host[b];
-    int rc = ctx->ledger.admit_chain(s, gamma, &geff[size_t(b)], &why);
+    int rc = ctx->ledger.admit_chain(s, gamma, stored, &geff[size_t(b)], &why);
     if (rc) return set_err(ctx, rc, why);
     for (int j = 0; j < b; ++j)
       if (seq_ids_host[j] == s) return set_err(ctx, EAGLE3_E_INVAL, "duplicate sequence id");
@@ -928,7 +1020,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
   const int n = ctx->n;
   if (n_seq > 1) {
     const int rc = draft_chain_batched(ctx, n_seq, seq_ids_host, boundary_tok_dev, aux0_dev,
-                                       aux1_dev, aux2_dev, gamma, out_ids_dev, geff, dbg, s);
+                                       aux1_dev, aux2_dev, stored, gamma, out_ids_dev, geff, dbg, s);
     if (rc) return rc;
     for (int b = 0; b < n_seq; ++b)
       ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
@@ -941,17 +1033,25 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
     int32_t* out_b = out_ids_dev + size_t(b) * gamma;
     if (ge < gamma) E3_HIP(ctx, e3::launch_fill_i32(out_b + ge, -1, gamma - ge, s), "fill");
     if (ge == 0) continue;
-    {
+    // the first step's g: the stored boundary feature of the sequence, or the
+    // encode of the given taps
+    eagle3_ctx::GBuf g_bnd;
+    if (stored) {
+      g_bnd.y = ctx->bnd_y + size_t(sq) * n;
+      g_bnd.w_hid = ctx->bnd_w + size_t(sq) * n;
+      g_bnd.ssq = ctx->bnd_ssq + sq;
+      g_bnd.count = 1;
+    } else {
       e3::VecOut eo{ctx->gb[0].y, ctx->gb[0].w_hid, ctx->nrm_hid, nullptr, nullptr, ctx->gb[0].ssq};
       ProfScope ps(ctx, 6, s);
       E3_HIP(ctx, e3::launch_encode(ctx->w_fc, n, aux0_dev + size_t(b) * n, aux1_dev + size_t(b) * n,
                                     aux2_dev + size_t(b) * n, eo, ctx->gcfg[e3::kGemvEncode], s),
              "encode");
     }
+    const eagle3_ctx::GBuf* g = stored ? &g_bnd : &ctx->gb[0];
     if (dbg && dbg->hidden)
-      E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + size_t(b) * (gamma + 1) * n, ctx->gb[0].y,
+      E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + size_t(b) * (gamma + 1) * n, g->y,
                                  size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
-    const eagle3_ctx::GBuf* g = &ctx->gb[0];
     for (int j = 0; j < ge; ++j) {
       const int pos = L + j;
       const eagle3_ctx::GBuf* gn = &ctx->gb[1 + (j & 1)];
@@ -1069,31 +1169,32 @@ int eagle3_ledger_create(int32_t max_ctx, int32_t max_seqs, int32_t max_gamma, e
 
 void eagle3_ledger_destroy(eagle3_ledger* l) { delete l; }
 
-int eagle3_ledger_prefill(eagle3_ledger* l, int32_t seq, int32_t T) {
+int eagle3_ledger_prefill(eagle3_ledger* l, int32_t seq, int32_t T, int32_t with_boundary) {
   if (!l) return EAGLE3_E_INVAL;
   int rc = l->l.check_prefill(seq, T, nullptr);
   if (rc) return rc;
-  l->l.do_prefill(seq, T);
+  if (T == 0 && !with_boundary) return EAGLE3_OK;
+  l->l.do_prefill(seq, T, with_boundary != 0);
   return EAGLE3_OK;
 }
 
 int eagle3_ledger_chain(eagle3_ledger* l, int32_t seq, int32_t gamma, uint32_t flags,
                         int32_t* gamma_eff) {
   if (!l || !gamma_eff) return EAGLE3_E_INVAL;
-  if (flags & ~EAGLE3_KEEP_SPEC) return EAGLE3_E_INVAL;
+  if (flags & ~(EAGLE3_KEEP_SPEC | EAGLE3_STORED_BOUNDARY)) return EAGLE3_E_INVAL;
   int32_t g = 0;
-  int rc = l->l.admit_chain(seq, gamma, &g, nullptr);
+  int rc = l->l.admit_chain(seq, gamma, (flags & EAGLE3_STORED_BOUNDARY) != 0, &g, nullptr);
   if (rc) return rc;
   l->l.do_chain(seq, g, (flags & EAGLE3_KEEP_SPEC) != 0);
   *gamma_eff = g;
   return EAGLE3_OK;
 }
 
-int eagle3_ledger_rebuild(eagle3_ledger* l, int32_t seq, int32_t n_accepted) {
+int eagle3_ledger_rebuild(eagle3_ledger* l, int32_t seq, int32_t n_accepted, int32_t with_boundary) {
   if (!l) return EAGLE3_E_INVAL;
   int rc = l->l.check_rebuild(seq, n_accepted, nullptr);
   if (rc) return rc;
-  l->l.do_rebuild(seq, n_accepted);
+  l->l.do_rebuild(seq, n_accepted, with_boundary != 0);
   return EAGLE3_OK;
 }
 

@@ -456,7 +456,8 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
                                                     int kc, const float* __restrict__ x0,
                                                     const float* __restrict__ x1,
                                                     const float* __restrict__ x2, int seg,
-                                                    int rows, float* __restrict__ P) {
+                                                    int rows, float* __restrict__ P,
+                                                    const TapRowsB yb) {
   constexpr int R = MultiShape<M>::R;
   constexpr int WAVES = MultiShape<M>::WAVES;
   extern __shared__ float xs[];  // [M][kc]
@@ -485,7 +486,11 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
         const float* src;
         if (x1) {
           const int sgi = k / seg;
-          src = (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2)) + (size_t)m * seg + (k - sgi * seg);
+          // rows from yb.rows_x on come from the second set of streams
+          const bool second = m >= yb.rows_x;
+          const float* base = second ? (sgi == 0 ? yb.y[0] : (sgi == 1 ? yb.y[1] : yb.y[2]))
+                                     : (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2));
+          src = base + (size_t)(second ? m - yb.rows_x : m) * seg + (k - sgi * seg);
         } else {
           src = x0 + (size_t)m * K + k;
         }
@@ -671,9 +676,10 @@ int gemv_multi_splits(int rows, int N, int K) {
 
 hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, const float* x1,
                              const float* x2, int seg, int rows, float* P, int* splits_out,
-                             hipStream_t s) {
+                             hipStream_t s, const TapRowsB& yb) {
   const int m = gemv_multi_width(rows);
   if (m < 0 || (K % 8) || (x1 && (seg % 4))) return hipErrorInvalidValue;
+  if (yb.rows_x < rows && (!x1 || !yb.y[0] || !yb.y[1] || !yb.y[2])) return hipErrorInvalidValue;
   const int kc = multi_kchunk(m, N, K);
   const int splits = ceil_div(K, kc);
   *splits_out = splits;
@@ -683,7 +689,7 @@ hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, c
 #define MCASE(MM)                                                                              \
   case MM:                                                                                     \
     hipLaunchKernelGGL((k_gemv_multi<MM>), grid, block, lds, s, W, N, K, kc, x0, x1, x2, seg,  \
-                       rows, P);                                                               \
+                       rows, P, yb);                                                           \
     break;
     MCASE(1) MCASE(2) MCASE(3) MCASE(4) MCASE(5) MCASE(6) MCASE(8) MCASE(9) MCASE(12) MCASE(16)
 #undef MCASE

@@ -98,14 +98,24 @@ hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, const int3
                                   const int32_t* d2t, int dv, int32_t* out_id, int32_t* tok_store,
                                   hipStream_t s);
 
+// A second set of tap streams for a teacher-forced pass: rows [rows_x, rows) of the
+// pass read y[0..2] (row rows_x is y's row 0); rows_x >= rows means none.  Passed by
+// value.
+struct TapRowsB {
+  const float* y[3];
+  int rows_x;
+};
+inline TapRowsB no_tap_rows_b() { return TapRowsB{{nullptr, nullptr, nullptr}, 1 << 30}; }
+
 // Multi-vector split-K GEMV for teacher-forced rows: P[z][m][r] (fp32) over K chunks z.
-// Input: three fp32 streams x0|x1|x2 of row length seg concatenated along K, or (x1 ==
-// NULL) one fp32 matrix x0 [rows, K].  rows <= 16; *splits_out receives the chunk count.
+// Input: three fp32 streams x0|x1|x2 of row length seg concatenated along K (rows from
+// yb.rows_x on taken from yb's streams), or (x1 == NULL) one fp32 matrix x0 [rows, K].
+// rows <= 16; *splits_out receives the chunk count.
 int gemv_multi_width(int rows);
 int gemv_multi_splits(int rows, int N, int K);  // chunk count the launch will use
 hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, const float* x1,
                              const float* x2, int seg, int rows, float* P, int* splits_out,
-                             hipStream_t s);
+                             hipStream_t s, const TapRowsB& yb = no_tap_rows_b());
 
 // ---- batched drafting: up to kBatchRows sequences per pass ----
 constexpr int kBatchRows = 32;
@@ -191,9 +201,9 @@ hipError_t launch_bpack_aux(const BatchRows& br, const float* a0, const float* a
 // Start of step `step` for rows [0, m): the token (boundary token at step 0, else the
 // argmax of the previous lm_head candidates through d2t, also stored to
 // out_ids[orig * gamma + step - 1]), then X[r][0:n] = RMSNorm(E[tok], w_in) as
-// (hi, lo).  At step 0 also g = sum of the encode partials -> G and X[r][n:2n] =
-// RMSNorm(g, w_hid) (later steps receive that half from the down projection's
-// row kernel).
+// (hi, lo).  At step 0 also g = sum of the encode partials (or, with bnd set, the
+// stored boundary feature bnd[slot * n ..]) -> G and X[r][n:2n] = RMSNorm(g, w_hid)
+// (later steps receive that half from the down projection's row kernel).
 struct BPrepArgs {
   BatchRows br;
   int m, step, gamma;
@@ -212,6 +222,7 @@ struct BPrepArgs {
   float* G;                // [32][n]
   const float* Penc;       // step 0: encode partials [S][32][n]
   int S_enc;
+  const float* bnd;        // step 0: stored boundary features [slots][n], or NULL
   uint16_t* Xhi;           // [32][ldx]
   uint16_t* Xlo;
   int ldx;
@@ -272,17 +283,31 @@ hipError_t launch_bfinal(const BatchRows& br, int m, int gamma, const float* can
                          int32_t* out_ids, hipStream_t s);
 
 // ---- teacher-forced append (prefill / rebuild) ----
-// A[t, 0:3n] = [aux0[t]; aux1[t]; aux2[t]] as bf16 (A_hi); with A_lo given, also the
-// bf16 remainder A_lo = bf16(a - A_hi), so A_hi + A_lo carries ~16 mantissa bits.
+// A[t, 0:3n] = [aux0[t]; aux1[t]; aux2[t]] as bf16 (A_hi), rows from yb.rows_x on
+// taken from yb's streams; with A_lo given, also the bf16 remainder
+// A_lo = bf16(a - A_hi), so A_hi + A_lo carries ~16 mantissa bits.
 hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
-                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s);
-// cat[t] = [RMSNorm(E[tok[t]], w_in); RMSNorm(sum_z F[z][t], w_hid)], F row stride n,
-// split stride f_split (elements); written as fp32 (cat32) or as bf16 (cat16, plus the
-// bf16 remainder in cat16_lo when given).
+                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s,
+                           const TapRowsB& yb = no_tap_rows_b());
+// Boundary features of a teacher-forced pass: fc rows [T_cat, T_cat + count) are the
+// next rounds' boundary rows; row T_cat + j goes to sequence slot slot[j]:
+// y[slot] = f [n], yw[slot] = f * w_hid [n], ssq[slot] = sum f^2.
+constexpr int kBndRows = 32;
+struct BndOut {
+  float* y;
+  float* yw;
+  float* ssq;
+  int count;
+  int32_t slot[kBndRows];
+};
+// cat[t] = [RMSNorm(E[tok[t]], w_in); RMSNorm(sum_z F[z][t], w_hid)] for t < T, F row
+// stride n, split stride f_split (elements); written as fp32 (cat32) or as bf16
+// (cat16, plus the bf16 remainder in cat16_lo when given).  Rows T .. T + bnd.count - 1
+// of F are boundary rows, summed into bnd's slots.
 hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int n,
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
-                         float* cat32, hipStream_t s);
+                         float* cat32, hipStream_t s, const BndOut* bnd = nullptr);
 // Up to kStoreSegs runs of consecutive rows of one append pass: rows
 // [row0[s], row0[s + 1]) go to sequence slot[s] from position pos0[s] on.
 constexpr int kStoreSegs = 32;

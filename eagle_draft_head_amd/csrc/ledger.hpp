@@ -11,6 +11,10 @@
 //   prefill of T rows                committed + T <= max_ctx
 // A chain round writes rows committed .. committed + gamma_eff - 1 and is
 // rewound afterwards (its rows become dead) unless the caller keeps them.
+// Boundary feature: prefill and rebuild may also encode the taps of the next
+// round's boundary (the pages' prefill and rebuild_after_verify set the boundary
+// target feature); the sequence then holds a stored feature until the next
+// prefill, rebuild or rewind, and a chain round may start from it.
 #pragma once
 
 #include <stdint.h>
@@ -27,6 +31,7 @@ class Ledger {
     int32_t committed = 0;
     int32_t spec = 0;
     int32_t last_gamma = -1;  // -1: no chain since the last commit
+    bool boundary = false;    // a stored boundary feature for the current length
   };
 
   Ledger() = default;
@@ -50,11 +55,14 @@ class Ledger {
     return EAGLE3_OK;
   }
 
-  int admit_chain(int32_t s, int32_t gamma, int32_t* gamma_eff, const char** why) const {
+  int admit_chain(int32_t s, int32_t gamma, bool stored_boundary, int32_t* gamma_eff,
+                  const char** why) const {
     if (!valid_seq(s)) return fail(why, "bad sequence id", EAGLE3_E_INVAL);
     if (gamma < 0 || gamma > max_gamma_) return fail(why, "gamma out of range", EAGLE3_E_INVAL);
     const Seq& q = seq(s);
     if (q.spec) return fail(why, "speculative rows are live", EAGLE3_E_STATE);
+    if (stored_boundary && !q.boundary)
+      return fail(why, "no stored boundary feature for this sequence", EAGLE3_E_STATE);
     int32_t room = max_ctx_ - q.committed;
     if (room < 0) room = 0;
     *gamma_eff = gamma < room ? gamma : room;
@@ -81,11 +89,12 @@ class Ledger {
   }
 
   // ---- transitions: call only after the matching check succeeded ----
-  int32_t do_prefill(int32_t s, int32_t T) {
+  int32_t do_prefill(int32_t s, int32_t T, bool boundary) {
     Seq& q = seqs_[size_t(s)];
     const int32_t start = q.committed;
     q.committed += T;
     q.last_gamma = -1;
+    q.boundary = boundary;
     return start;
   }
   void do_chain(int32_t s, int32_t gamma_eff, bool keep_spec) {
@@ -93,11 +102,12 @@ class Ledger {
     q.spec = keep_spec ? gamma_eff : 0;
     q.last_gamma = gamma_eff;
   }
-  int32_t do_rebuild(int32_t s, int32_t a) {
+  int32_t do_rebuild(int32_t s, int32_t a, bool boundary) {
     Seq& q = seqs_[size_t(s)];
     const int32_t start = q.committed;
     q.committed += a + 1;
     q.last_gamma = -1;
+    q.boundary = boundary;
     return start;
   }
   void do_rewind(int32_t s, int32_t new_len) {
@@ -105,6 +115,7 @@ class Ledger {
     q.committed = new_len;
     q.spec = 0;
     q.last_gamma = -1;
+    q.boundary = false;
   }
 
  private:

@@ -22,12 +22,15 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
                                                   const float* __restrict__ a1,
                                                   const float* __restrict__ a2, int T, int n,
                                                   uint16_t* __restrict__ A_hi,
-                                                  uint16_t* __restrict__ A_lo) {
+                                                  uint16_t* __restrict__ A_lo, const TapRowsB yb) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (t >= T || c >= 3 * n) return;
   const int j = c / n, k = c - j * n;
-  const float4* src = reinterpret_cast<const float4*>((j == 0 ? a0 : (j == 1 ? a1 : a2)) + (size_t)t * n + k);
+  const bool second = t >= yb.rows_x;  // rows from yb.rows_x on: the second set of streams
+  const float* base = second ? (j == 0 ? yb.y[0] : (j == 1 ? yb.y[1] : yb.y[2]))
+                             : (j == 0 ? a0 : (j == 1 ? a1 : a2));
+  const float4* src = reinterpret_cast<const float4*>(base + (size_t)(second ? t - yb.rows_x : t) * n + k);
   const float4 v0 = src[0], v1 = src[1];
   const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   uint16_t h[8], l[8];
@@ -47,11 +50,12 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
 }
 
 hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
-                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s) {
+                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s, const TapRowsB& yb) {
   if (T <= 0) return hipSuccess;
   if ((n & 7) || T > 65535) return hipErrorInvalidValue;
+  if (yb.rows_x < T && (!yb.y[0] || !yb.y[1] || !yb.y[2])) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_pack_aux, dim3((3 * n + 2047) / 2048, T), dim3(256), 0, s, a0, a1, a2, T, n,
-                     A_hi, A_lo);
+                     A_hi, A_lo, yb);
   return hipGetLastError();
 }
 
@@ -96,10 +100,29 @@ __global__ __launch_bounds__(512) void k_tf_cat(const float* __restrict__ F, int
                                                 const float* __restrict__ w_hid, float eps,
                                                 uint16_t* __restrict__ cat16,
                                                 uint16_t* __restrict__ cat16_lo,
-                                                float* __restrict__ cat32) {
+                                                float* __restrict__ cat32, const BndOut bnd) {
   extern __shared__ float fs[];  // [n]
   __shared__ float red[32];
   const int t = blockIdx.x;
+  if (t >= T) {
+    // a boundary row: f = sum of the partials, kept with f * w_hid and sum f^2 for the
+    // next round's first step
+    const int j = t - T;
+    float* y = bnd.y + (size_t)bnd.slot[j] * n;
+    float* yw = bnd.yw + (size_t)bnd.slot[j] * n;
+    const float4* wh4 = reinterpret_cast<const float4*>(w_hid);
+    float sf = 0.f, unused = 0.f;
+    for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) {
+      const float4 f = sum_splits4(F + (size_t)t * n + 4 * i, splits, f_split);
+      const float4 wh = wh4[i];
+      reinterpret_cast<float4*>(y)[i] = f;
+      reinterpret_cast<float4*>(yw)[i] = make_float4(f.x * wh.x, f.y * wh.y, f.z * wh.z, f.w * wh.w);
+      sf = fmaf(f.x, f.x, fmaf(f.y, f.y, fmaf(f.z, f.z, fmaf(f.w, f.w, sf))));
+    }
+    block_sum2(sf, unused, red);
+    if (threadIdx.x == 0) bnd.ssq[bnd.slot[j]] = sf;
+    return;
+  }
   const int tk = min(max(tok[t], 0), vocab - 1);  // out-of-range ids are clamped
   const uint2* e4 = reinterpret_cast<const uint2*>(embed + (size_t)tk * n);
   float4* f4 = reinterpret_cast<float4*>(fs);
@@ -162,10 +185,16 @@ __global__ __launch_bounds__(512) void k_tf_cat(const float* __restrict__ F, int
 hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int n,
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
-                         float* cat32, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tf_cat, dim3(T), dim3(512), size_t(n) * sizeof(float), s, F, splits,
-                     f_split, T, n, embed, vocab, tok, w_in, w_hid, eps, cat16, cat16_lo, cat32);
+                         float* cat32, hipStream_t s, const BndOut* bnd) {
+  BndOut b{};
+  if (bnd) {
+    if (bnd->count < 0 || bnd->count > kBndRows || (bnd->count > 0 && (!bnd->y || !bnd->yw || !bnd->ssq)))
+      return hipErrorInvalidValue;
+    b = *bnd;
+  }
+  if (T < 0 || T + b.count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tf_cat, dim3(T + b.count), dim3(512), size_t(n) * sizeof(float), s, F, splits,
+                     f_split, T, n, embed, vocab, tok, w_in, w_hid, eps, cat16, cat16_lo, cat32, b);
   return hipGetLastError();
 }
 

@@ -38,13 +38,22 @@ class Drafter:
             pass
 
     # -- entry points ---------------------------------------------------------
-    def prefill(self, seq: int, tok: torch.Tensor, aux: Sequence[torch.Tensor], stream=None):
+    def prefill(self, seq: int, tok: torch.Tensor, aux: Sequence[torch.Tensor],
+                next_aux: Optional[Sequence[torch.Tensor]] = None, stream=None):
+        """Append the teacher-forced rows; with next_aux (three [n] fp32 taps) also
+        store the boundary feature a chain with aux=None starts from."""
         T = int(tok.numel())
-        B.eagle3_prefill(self.ctx, seq, T, tok, aux[0], aux[1], aux[2], stream)
+        a = aux if T > 0 else (None, None, None)
+        na = next_aux if next_aux is not None else (None, None, None)
+        B.eagle3_prefill(self.ctx, seq, T, tok if T > 0 else None, a[0], a[1], a[2], na[0], na[1],
+                         na[2], stream)
 
     def draft_chain(self, seq_ids: Sequence[int], boundary_tok: torch.Tensor,
-                    aux: Sequence[torch.Tensor], gamma: int, out: Optional[torch.Tensor] = None,
-                    keep_spec: bool = False, debug: bool = False, stream=None):
+                    aux: Optional[Sequence[torch.Tensor]], gamma: int,
+                    out: Optional[torch.Tensor] = None, keep_spec: bool = False,
+                    debug: bool = False, stream=None):
+        """One chain round per sequence; aux=None starts from the stored boundary
+        features (set by prefill / rebuild_after_verify with next_aux)."""
         n_seq = len(seq_ids)
         dev = boundary_tok.device
         if out is None:
@@ -53,15 +62,20 @@ class Drafter:
         if debug:
             logits = torch.zeros((n_seq, max(gamma, 1), self.dv), dtype=torch.float32, device=dev)
             hidden = torch.zeros((n_seq, gamma + 1, self.n), dtype=torch.float32, device=dev)
-        geff = B.eagle3_draft_chain(self.ctx, list(seq_ids), boundary_tok, aux[0], aux[1], aux[2],
-                                    gamma, out, B.KEEP_SPEC if keep_spec else 0, logits, hidden,
-                                    stream)
+        flags = (B.KEEP_SPEC if keep_spec else 0) | (B.STORED_BOUNDARY if aux is None else 0)
+        a = aux if aux is not None else (None, None, None)
+        geff = B.eagle3_draft_chain(self.ctx, list(seq_ids), boundary_tok, a[0], a[1], a[2],
+                                    gamma, out, flags, logits, hidden, stream)
         return out, geff, logits, hidden
 
     def rebuild_after_verify(self, seq_ids: Sequence[int], n_accepted: Sequence[int],
-                             tok: torch.Tensor, aux: Sequence[torch.Tensor], stream=None):
+                             tok: torch.Tensor, aux: Sequence[torch.Tensor],
+                             next_aux: Optional[Sequence[torch.Tensor]] = None, stream=None):
+        """Commit the accepted rows; with next_aux (three [n_seq, n] fp32 taps) also
+        store each sequence's next boundary feature."""
+        na = next_aux if next_aux is not None else (None, None, None)
         B.eagle3_rebuild_after_verify(self.ctx, list(seq_ids), list(n_accepted), tok, aux[0],
-                                      aux[1], aux[2], stream)
+                                      aux[1], aux[2], na[0], na[1], na[2], stream)
 
     def rewind(self, seq: int, new_len: int):
         B.eagle3_rewind(self.ctx, seq, new_len)

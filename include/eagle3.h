@@ -45,6 +45,10 @@ enum {
 /* eagle3_draft_chain flag: keep the speculative rows (spec > 0) instead of
    rewinding at the end of the round; only eagle3_rewind clears them. */
 #define EAGLE3_KEEP_SPEC 1u
+/* eagle3_draft_chain flag: start each listed sequence from its stored boundary
+   feature (set by eagle3_prefill / eagle3_rebuild_after_verify from next-boundary
+   taps) instead of encoding taps; the tap pointers must then be NULL. */
+#define EAGLE3_STORED_BOUNDARY 2u
 
 typedef struct eagle3_ctx eagle3_ctx;
 
@@ -130,17 +134,27 @@ int eagle3_free(eagle3_ctx *ctx);
    taps of target position p_t (aux*_dev[t], fp32 [T, n] each, ascending tap
    order) with tok_dev[t] (int32 [T]) = the target token at p_t + 1 (the shifted
    pairing of ExecuTorch PR #20153).  Only K and V of the rows are computed.
-   Requires spec == 0 and committed + T <= max_ctx. T == 0 is a no-op. */
+   Next boundary (the page's prefill also builds the boundary target feature):
+   with next_aux*_dev given (fp32 [n] each: the taps of the last prompt position,
+   all three or none), fc of those taps is computed in the same pass over W_fc
+   and stored as the sequence's boundary feature, which a following
+   eagle3_draft_chain with EAGLE3_STORED_BOUNDARY starts from; without them any
+   stored feature of the sequence is dropped.
+   Requires spec == 0 and committed + T <= max_ctx.  T == 0 without next taps is
+   a no-op; T == 0 with them only stores the boundary feature. */
 int eagle3_prefill(eagle3_ctx *ctx, int32_t seq, int32_t T, const int32_t *tok_dev,
                    const float *aux0_dev, const float *aux1_dev, const float *aux2_dev,
-                   void *stream);
+                   const float *next_aux0_dev, const float *next_aux1_dev,
+                   const float *next_aux2_dev, void *stream);
 
 /* One chain round per listed sequence (pegainfer PR #707 `chain_round`):
    g = fc(boundary taps), then gamma_eff greedy draft steps over the persistent
    draft KV, then rewind (unless flags & EAGLE3_KEEP_SPEC).
      seq_ids_host[n_seq]: distinct sequence slots;
      boundary_tok_dev[n_seq] (int32): the token at the boundary position;
-     aux*_dev [n_seq, n] fp32: taps of the position before it;
+     aux*_dev [n_seq, n] fp32: taps of the position before it; NULL with
+       flags & EAGLE3_STORED_BOUNDARY, where g is each sequence's stored boundary
+       feature instead (EAGLE3_E_STATE if a sequence holds none);
      out_ids_dev [n_seq, gamma] int32: target id of draft j+1, -1 beyond gamma_eff;
      gamma_eff_host[n_seq]: filled before any device work is queued,
        gamma_eff = clamp(max_ctx - committed, 0, gamma) (reserve for the k+1 commit);
@@ -157,16 +171,24 @@ int eagle3_draft_chain(eagle3_ctx *ctx, int32_t n_seq, const int32_t *seq_ids_ho
    and a_b + 1 rows are appended: (boundary taps, boundary token),
    (taps before d_1, d_1) ... (taps before d_a, d_a).  Rows are packed over
    sequences in list order: tok_dev [sum(a_b+1)] int32, aux*_dev [sum(a_b+1), n].
+   Next boundary (the page's rebuild also sets the boundary target feature for
+   the next round): with next_aux*_dev given ([n_seq, n] fp32 each, list order:
+   the taps of each sequence's new boundary position; all three or none), their
+   fc rows ride along in the same pass over W_fc and are stored as the
+   sequences' boundary features for a following chain with
+   EAGLE3_STORED_BOUNDARY; without them the stored features are dropped.
    Requires spec == 0, a preceding chain round on the sequence since its last
    commit, and a_b <= that round's gamma_eff. */
 int eagle3_rebuild_after_verify(eagle3_ctx *ctx, int32_t n_seq, const int32_t *seq_ids_host,
                                 const int32_t *n_accepted_host, const int32_t *tok_dev,
                                 const float *aux0_dev, const float *aux1_dev,
-                                const float *aux2_dev, void *stream);
+                                const float *aux2_dev, const float *next_aux0_dev,
+                                const float *next_aux1_dev, const float *next_aux2_dev,
+                                void *stream);
 
 /* Drop speculative rows and truncate the committed rows to new_len
-   (abort / cleanup).  Requires 0 <= new_len <= committed.  Host bookkeeping
-   only: no device work. */
+   (abort / cleanup); the sequence's stored boundary feature is dropped too.
+   Requires 0 <= new_len <= committed.  Host bookkeeping only: no device work. */
 int eagle3_rewind(eagle3_ctx *ctx, int32_t seq, int32_t new_len);
 
 /* Lengths of a sequence: committed rows and live speculative rows. */

@@ -14,6 +14,10 @@
  *          0 <= a <= its gamma_eff, committed + a + 1 <= max_ctx + 1;
  *          committed += a + 1;
  *   rewind to new_len: 0 <= new_len <= committed; spec := 0.
+ * Boundary feature: prefill / rebuild with_boundary != 0 leave a stored
+ *   boundary feature, without it they drop it, rewind drops it; a chain with
+ *   flags & EAGLE3_STORED_BOUNDARY needs one (else EAGLE3_E_STATE).  A prefill
+ *   of T == 0 without a boundary changes nothing.
  * Every call returns EAGLE3_OK or an EAGLE3_E_* code and changes nothing on
  * error.  Host memory only.
  */
@@ -31,10 +35,11 @@ typedef struct eagle3_ledger eagle3_ledger;
 int eagle3_ledger_create(int32_t max_ctx, int32_t max_seqs, int32_t max_gamma,
                          eagle3_ledger **out);
 void eagle3_ledger_destroy(eagle3_ledger *l);
-int eagle3_ledger_prefill(eagle3_ledger *l, int32_t seq, int32_t T);
+int eagle3_ledger_prefill(eagle3_ledger *l, int32_t seq, int32_t T, int32_t with_boundary);
 int eagle3_ledger_chain(eagle3_ledger *l, int32_t seq, int32_t gamma, uint32_t flags,
                         int32_t *gamma_eff);
-int eagle3_ledger_rebuild(eagle3_ledger *l, int32_t seq, int32_t n_accepted);
+int eagle3_ledger_rebuild(eagle3_ledger *l, int32_t seq, int32_t n_accepted,
+                          int32_t with_boundary);
 int eagle3_ledger_rewind(eagle3_ledger *l, int32_t seq, int32_t new_len);
 int eagle3_ledger_len(const eagle3_ledger *l, int32_t seq, int32_t *committed, int32_t *spec);
 

@@ -245,8 +245,8 @@ class DrafterOracle:
 class StatelessChain:
     """The same chain computed from scratch at every step: all committed rows
     and all chain rows so far are run through the full layer with causal
-    attention and the last row is read (ExecuTorch PR #20153 description:
-    "a cached draft chain matching the stateless recompute")."""
+    attention and the last row is read (ExecuTorch PR #20153 description: the
+    cached chain must equal this recompute)."""
 
     def __init__(self, drafter: DrafterOracle):
         self.d = drafter

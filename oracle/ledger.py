@@ -1,13 +1,12 @@
 """Draft-KV length bookkeeping (test infrastructure).
 
 Per sequence the draft KV holds `committed` teacher-forced rows; a chain round
-writes speculative rows after them and rewinds, so a round leaves no trace
-(pegainfer PR #707, PR description: `chain_round` "rewind[s] the speculative KV
-so the round is side-effect-free except for the returned span").
+writes speculative rows after them and rewinds, so a round leaves nothing behind
+but the drafted ids (pegainfer PR #707, PR description, `chain_round`).
 
-Capacity (PR #707, review: "account for the extra committed token ... start=97,
-k=3, max=100 passes drafting but overflows during rebuild ... reserve space for
-k + 1 or shrink k near the boundary"):
+Capacity (PR #707, review of the capacity check: a fully accepted chain of k
+drafts commits k + 1 rows, so the extra row must be reserved or k shrunk at the
+edge; the review's example is start 97, k 3, max 100):
   * `max_ctx` is the admission bound; the store holds max_ctx + 1 rows, the
     extra row being the reserve for the (k+1)-th commit of a fully accepted
     chain;
@@ -17,7 +16,14 @@ k + 1 or shrink k near the boundary"):
   * prefill needs committed + T <= max_ctx.
 At start=97, k=3, max=100 the chain drafts 3, full acceptance commits 4 rows
 (97..100), committed becomes 101 and the next chain is admitted with
-gamma_eff = 0 ("shrink k" seen from the next round).
+gamma_eff = 0 (k shrunk, as seen from the next round).
+
+Boundary feature (PR #707, PR description: prefill also builds the boundary
+target feature, and rebuild_after_verify sets the one for the next round): a
+prefill or rebuild that is given the next boundary's taps leaves a stored
+feature, one without them drops it, and a rewind drops it; a chain may start
+from the stored feature only while one is held.  A prefill of zero rows without
+taps changes nothing (our reading; the pages are silent).
 """
 from __future__ import annotations
 
@@ -42,6 +48,7 @@ class _Seq:
     committed: int = 0
     spec: int = 0
     last_gamma: int = -1      # gamma_eff of the chain since the last commit; -1 none
+    boundary: bool = False    # a stored boundary feature for the current length
 
 
 class Ledger:
@@ -74,12 +81,14 @@ class Ledger:
         if q.committed + T > self.max_ctx:
             raise LedgerError(E_CAPACITY, "prefill past max_ctx")
 
-    def admit_chain(self, s: int, gamma: int) -> int:
+    def admit_chain(self, s: int, gamma: int, stored_boundary: bool = False) -> int:
         q = self._seq(s)
         if gamma < 0 or gamma > self.max_gamma:
             raise LedgerError(E_INVAL, "gamma out of range")
         if q.spec:
             raise LedgerError(E_STATE, "speculative rows are live")
+        if stored_boundary and not q.boundary:
+            raise LedgerError(E_STATE, "no stored boundary feature")
         return max(0, min(gamma, self.max_ctx - q.committed))
 
     def check_rebuild(self, s: int, a: int) -> None:
@@ -94,27 +103,32 @@ class Ledger:
             raise LedgerError(E_CAPACITY, "rebuild past the reserved row")
 
     # -- transitions -------------------------------------------------------
-    def prefill(self, s: int, T: int) -> int:
+    def prefill(self, s: int, T: int, boundary: bool = False) -> int:
         self.check_prefill(s, T)
         q = self.seqs[s]
         start = q.committed
+        if T == 0 and not boundary:
+            return start
         q.committed += T
         q.last_gamma = -1
+        q.boundary = boundary
         return start
 
-    def chain(self, s: int, gamma: int, keep_spec: bool = False) -> int:
-        g = self.admit_chain(s, gamma)
+    def chain(self, s: int, gamma: int, keep_spec: bool = False,
+              stored_boundary: bool = False) -> int:
+        g = self.admit_chain(s, gamma, stored_boundary)
         q = self.seqs[s]
         q.spec = g if keep_spec else 0
         q.last_gamma = g
         return g
 
-    def rebuild(self, s: int, a: int) -> int:
+    def rebuild(self, s: int, a: int, boundary: bool = False) -> int:
         self.check_rebuild(s, a)
         q = self.seqs[s]
         start = q.committed
         q.committed += a + 1
         q.last_gamma = -1
+        q.boundary = boundary
         return start
 
     def rewind(self, s: int, new_len: int) -> None:
@@ -124,3 +138,4 @@ class Ledger:
         q.committed = new_len
         q.spec = 0
         q.last_gamma = -1
+        q.boundary = False

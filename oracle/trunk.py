@@ -2,8 +2,8 @@
 
 It stands in for the target model of the greedy speculative loop.  The loop's
 invariant (memra_engine `eagle.rs` module doc: greedy speculative decoding is
-token-for-token identical to plain greedy generation; ExecuTorch PR #20153:
-"the full shifted speculative loop reproducing greedy decoding") is only exact
+token-for-token identical to plain greedy generation; ExecuTorch PR #20153 tests
+that the whole shifted speculative loop gives the greedy tokens) is only exact
 if a row's result does not depend on whether it was computed alone or inside a
 verify batch.  So every token goes through the same one-row code path, in the
 same order, whichever way it is fed.

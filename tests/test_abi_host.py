@@ -59,21 +59,22 @@ def test_ledger_matches_oracle_on_random_histories(seed):
     for _ in range(400):
         op = rnd.randrange(5)
         s = rnd.randrange(-1, seqs + 1)
+        bnd = rnd.random() < 0.5
         if op == 0:
             T = rnd.randrange(-1, 8)
-            rc = ours.prefill(s, T)
-            rrc, _ = _oracle_rc(ref.prefill, s, T)
+            rc = ours.prefill(s, T, bnd)
+            rrc, _ = _oracle_rc(ref.prefill, s, T, bnd)
         elif op == 1:
             g = rnd.randrange(-1, mg + 2)
             keep = rnd.random() < 0.2
-            rc, ge = ours.chain(s, g, keep)
-            rrc, rge = _oracle_rc(lambda: ref.chain(s, g, keep_spec=keep))
+            rc, ge = ours.chain(s, g, keep, bnd)
+            rrc, rge = _oracle_rc(lambda: ref.chain(s, g, keep_spec=keep, stored_boundary=bnd))
             if rc == 0:
                 assert ge == rge
         elif op == 2:
             a = rnd.randrange(-1, mg + 2)
-            rc = ours.rebuild(s, a)
-            rrc, _ = _oracle_rc(ref.rebuild, s, a)
+            rc = ours.rebuild(s, a, bnd)
+            rrc, _ = _oracle_rc(ref.rebuild, s, a, bnd)
         elif op == 3:
             nl = rnd.randrange(-1, max_ctx + 3)
             rc = ours.rewind(s, nl)
@@ -84,6 +85,25 @@ def test_ledger_matches_oracle_on_random_histories(seed):
         for q in range(seqs):
             _, c, sp = ours.length(q)
             assert (c, sp) == (ref.committed(q), ref.spec(q))
+
+
+def test_ledger_stored_boundary_rules():
+    L = B.HostLedger(100, 2, 8)
+    assert L.chain(0, 3, stored_boundary=True) == (B.E_STATE, -1)
+    assert L.prefill(0, 10) == 0
+    assert L.chain(0, 3, stored_boundary=True)[0] == B.E_STATE   # prefill without taps
+    assert L.prefill(0, 0, boundary=True) == 0                    # boundary only
+    assert L.length(0) == (0, 10, 0)
+    assert L.chain(0, 3, stored_boundary=True) == (0, 3)
+    assert L.chain(0, 3, stored_boundary=True) == (0, 3)          # a round leaves it
+    assert L.chain(1, 3, stored_boundary=True)[0] == B.E_STATE    # per sequence
+    assert L.rebuild(0, 2, boundary=True) == 0
+    assert L.chain(0, 3, stored_boundary=True) == (0, 3)
+    assert L.rebuild(0, 1) == 0                                   # rebuild without taps
+    assert L.chain(0, 3, stored_boundary=True)[0] == B.E_STATE
+    assert L.prefill(0, 1, boundary=True) == 0
+    assert L.rewind(0, 14) == 0                                   # rewind drops it
+    assert L.chain(0, 3, stored_boundary=True)[0] == B.E_STATE
 
 
 def test_ledger_capacity_edge_97_3_100():

@@ -21,9 +21,12 @@ def _tok(x):
     return torch.as_tensor(np.asarray(x), dtype=torch.int32).reshape(-1).cuda()
 
 
-def _rounds(cfg, lens, gamma, rounds, max_ctx, seed, min_pinned=None, kv_bf16=False):
+def _rounds(cfg, lens, gamma, rounds, max_ctx, seed, min_pinned=None, kv_bf16=False,
+            stored=False):
+    """stored: the boundary features come from the prefills and the packed rebuilds
+    (given the next round's boundary taps) and every chain starts from them."""
     say(f"[batched] {cfg.name}: {len(lens)} sequences, gamma={gamma}, rounds={rounds}, "
-        f"{'bf16' if kv_bf16 else 'fp32'} KV")
+        f"{'bf16' if kv_bf16 else 'fp32'} KV, stored={stored}")
     wd, wh = weights_both(cfg)
     S = len(lens)
     if kv_bf16:
@@ -36,16 +39,21 @@ def _rounds(cfg, lens, gamma, rounds, max_ctx, seed, min_pinned=None, kv_bf16=Fa
     total = sum(lens)
     aux, toks = aux_np(cfg, 30, max(total, 1)), toks_np(cfg, 30, max(total, 1))
     r0 = 0
+    b0 = aux_np(cfg, 40, S)
     for s, L in enumerate(lens):
+        nxt = to_dev_aux(b0, slice(s, s + 1)) if stored else None
         if L:
             orc.prefill(s, row_slice(aux, r0, r0 + L), toks[r0:r0 + L])
-            dr.prefill(s, _tok(toks[r0:r0 + L]), to_dev_aux(row_slice(aux, r0, r0 + L)))
+            dr.prefill(s, _tok(toks[r0:r0 + L]), to_dev_aux(row_slice(aux, r0, r0 + L)), next_aux=nxt)
+        elif stored:
+            dr.prefill(s, _tok([]), [], next_aux=nxt)
         r0 += L
     rng = np.random.default_rng(seed)
     steps = pinned = 0
     for rd in range(rounds):
         baux, btok = aux_np(cfg, 40 + rd, S), toks_np(cfg, 40 + rd, S)
-        out, geff, logits, hidden = dr.draft_chain(list(range(S)), _tok(btok), to_dev_aux(baux),
+        out, geff, logits, hidden = dr.draft_chain(list(range(S)), _tok(btok),
+                                                   None if stored else to_dev_aux(baux),
                                                    gamma, debug=True)
         torch.cuda.synchronize()
         drafts = []
@@ -82,8 +90,14 @@ def _rounds(cfg, lens, gamma, rounds, max_ctx, seed, min_pinned=None, kv_bf16=Fa
                 aux_rows[j].append(rows_s[j])
             q += a
         if live:
+            nxt = None
+            if stored:  # the next round's boundary taps of the rebuilt sequences
+                nb = aux_np(cfg, 40 + rd + 1, S)
+                nxt = to_dev_aux([x[live] for x in nb])
             dr.rebuild_after_verify(live, acc, _tok(tok_rows),
-                                    to_dev_aux([np.concatenate(x) for x in aux_rows]))
+                                    to_dev_aux([np.concatenate(x) for x in aux_rows]), next_aux=nxt)
+        # (a sequence that drafted nothing is not rebuilt and keeps an older stored
+        # feature; its committed length does not change, so it never drafts again)
         for s in range(S):
             assert dr.kv_len(s) == (orc.ledger.committed(s), 0)
     say(f"[batched] {cfg.name}: {pinned}/{steps} steps pinned")
@@ -102,6 +116,16 @@ def test_batched_ragged_lengths_and_capacity_edge():
 def test_batched_more_sequences_than_one_pass():
     _rounds(TINY, [int(x) for x in gen.lengths(TINY, 7, 35, 1, 120)], gamma=3, rounds=2,
             max_ctx=160, seed=6)
+
+
+def test_batched_stored_boundaries():
+    """Boundary features from prefill (one of them a boundary-only prefill of an
+    empty cache) and from packed rebuilds: 35 sequences, so the rebuild's boundary
+    rows span two passes of at most 32."""
+    _rounds(TINY, [0] + [int(x) for x in gen.lengths(TINY, 8, 34, 1, 120)], gamma=3, rounds=3,
+            max_ctx=160, seed=7, stored=True)
+    _rounds(small_variant(), [0, 1, 37, 130, 300, 511], gamma=4, rounds=3, max_ctx=700, seed=8,
+            stored=True)
 
 
 def test_batched_wide_heads_partial_rope():

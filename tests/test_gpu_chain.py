@@ -20,27 +20,32 @@ def _tok(x):
     return torch.as_tensor(np.asarray(x), dtype=torch.int32).reshape(-1).cuda()
 
 
-def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None):
-    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds}")
+def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None, stored=False):
+    """stored: every round starts from the boundary feature stored by the prefill
+    or the previous rebuild (given the round's boundary taps as next taps), and
+    every round is followed by a rebuild."""
+    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds} stored={stored}")
+    if stored:
+        rebuild_every = 1
     wd, wh = weights_both(cfg)
     max_ctx = max_ctx or (L + rounds * (gamma + 1) + gamma + 8)
     dr = gpu_drafter(cfg, wd, max_ctx=max_ctx)
     orc = make_oracle(cfg, wh, max_ctx=max_ctx)
     aux = aux_np(cfg, 0, L)
     toks = toks_np(cfg, 0, L)
-    orc.prefill(0, aux, toks)
-    dr.prefill(0, _tok(toks), to_dev_aux(aux))
-    baux = aux_np(cfg, 1, rounds)
+    baux = aux_np(cfg, 1, rounds + 1)
     btok = toks_np(cfg, 1, rounds)
     raux = aux_np(cfg, 2, rounds * (gamma + 1))
+    orc.prefill(0, aux, toks)
+    dr.prefill(0, _tok(toks), to_dev_aux(aux), next_aux=to_dev_aux(baux, slice(0, 1)) if stored else None)
     steps = pinned = 0
     worst_logit = worst_hidden = 0.0
     for r in range(rounds):
         b_aux = [a[r] for a in baux]
         recs = orc.draft_chain(0, b_aux, btok[r], gamma)
         out, geff, logits, hidden = dr.draft_chain([0], _tok([btok[r]]),
-                                                   [torch.as_tensor(a[r:r + 1], dtype=torch.float32).cuda()
-                                                    for a in baux], gamma, debug=True)
+                                                   None if stored else to_dev_aux(baux, slice(r, r + 1)),
+                                                   gamma, debug=True)
         torch.cuda.synchronize()
         # the encoded boundary feature
         f_ref = orc.encode([a for a in b_aux])
@@ -63,7 +68,8 @@ def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None):
             new_aux = [np.concatenate([ba[r:r + 1], ra[rows]]) for ba, ra in zip(baux, raux)]
             new_tok = np.array([btok[r]] + [x.target_id for x in recs[:a]], dtype=np.int32)
             orc.rebuild_after_verify(0, a, new_aux, new_tok)
-            dr.rebuild_after_verify([0], [a], _tok(new_tok), to_dev_aux(new_aux))
+            dr.rebuild_after_verify([0], [a], _tok(new_tok), to_dev_aux(new_aux),
+                                    next_aux=to_dev_aux(baux, slice(r + 1, r + 2)) if stored else None)
         assert dr.kv_len(0) == (orc.ledger.committed(0), 0)
     say(f"[parity] {cfg.name}: {pinned}/{steps} steps pinned; worst logit {worst_logit:.2e}, "
         f"hidden {worst_hidden:.2e}")
@@ -84,6 +90,49 @@ def test_ragged_shape_chain_parity():
 def test_chain_from_empty_cache():
     pinned, steps = _run_rounds(TINY, rounds=10, L=0, gamma=5)
     assert steps == 50
+
+
+def test_stored_boundary_rounds_tiny():
+    """Boundary features stored by prefill and by every rebuild (one fc pass over
+    the accepted rows and the next boundary), chains starting from them."""
+    pinned, steps = _run_rounds(TINY, rounds=60, L=63, gamma=3, stored=True)
+    assert pinned >= 0.25 * steps
+
+
+def test_stored_boundary_rounds_ragged_and_empty():
+    pinned, steps = _run_rounds(small_variant(), rounds=12, L=300, gamma=4, stored=True)
+    assert pinned >= 0.25 * steps
+    _run_rounds(TINY, rounds=5, L=0, gamma=5, stored=True)  # boundary-only prefill
+
+
+def test_stored_boundary_state_errors(tiny):
+    wd, _ = tiny
+    dr = gpu_drafter(TINY, wd, max_ctx=200)
+    aux, toks = aux_np(TINY, 0, 20), toks_np(TINY, 0, 20)
+    dr.prefill(0, _tok(toks), to_dev_aux(aux))
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.draft_chain([0], _tok([1]), None, 3)
+    assert e.value.code == B.E_STATE
+    assert dr.kv_len(0) == (20, 0)
+    baux = to_dev_aux(aux_np(TINY, 1, 1))
+    # taps together with the stored-boundary flag are rejected
+    with pytest.raises(B.Eagle3Error) as e:
+        B.eagle3_draft_chain(dr.ctx, [0], _tok([1]), baux[0], baux[1], baux[2], 3,
+                             torch.empty((1, 3), dtype=torch.int32, device="cuda"),
+                             flags=B.STORED_BOUNDARY)
+    assert e.value.code == B.E_INVAL
+    # only some of the three next-boundary streams
+    with pytest.raises(B.Eagle3Error) as e:
+        B.eagle3_prefill(dr.ctx, 0, 0, None, None, None, None, baux[0], None, baux[2])
+    assert e.value.code == B.E_INVAL
+    dr.prefill(0, _tok([]), [], next_aux=baux)  # boundary only
+    out, geff, _, _ = dr.draft_chain([0], _tok([1]), None, 3)
+    assert geff == [3] and dr.kv_len(0) == (20, 0)
+    dr.rewind(0, 20)  # drops the stored feature
+    with pytest.raises(B.Eagle3Error) as e:
+        dr.draft_chain([0], _tok([1]), None, 3)
+    assert e.value.code == B.E_STATE
+    dr.close()
 
 
 @pytest.fixture(scope="module")
