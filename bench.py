@@ -92,7 +92,7 @@ def kernel_bytes_step(cfg, L: int, gamma: int, kv_bytes: int = 4) -> float:
 
 
 def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
-               stored: bool = False) -> float:
+               stored: bool = False, rebuild: bool = True) -> float:
     """Algorithmic HBM bytes of one round: encode, gamma draft steps, rebuild (K/V
     elements of kv_bytes bytes).  stored: the encode is the rebuild's extra row (the
     next boundary: its taps in, the feature and its weighted copy out) on the
@@ -103,8 +103,9 @@ def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
     for j in range(gamma):
         rows = L + j                                      # rows attended before the new one
         tot += 2.0 * p_step + 8 * n + 2 * n + (rows + 1) * 2 * kv_bytes * kvd
-    T = accepted + 1                                      # rebuild rows
-    tot += 6.0 * n * n + 2.0 * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 2 * kv_bytes * kvd)
+    if rebuild:
+        T = accepted + 1                                  # rebuild rows
+        tot += 6.0 * n * n + 2.0 * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 2 * kv_bytes * kvd)
     return tot
 
 
@@ -122,6 +123,9 @@ def main():
                     help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
+    ap.add_argument("--drafter", choices=["persistent", "round-local"], default="persistent",
+                    help="round-local: the scratch-KV drafter (each round attends over its own rows "
+                         "only; a step is one chain round from encoded taps, no rebuild)")
     ap.add_argument("--boundary", choices=["stored", "taps"], default="stored",
                     help="stored: each rebuild also encodes the next round's boundary taps (one "
                          "W_fc pass) and the chain starts from that feature, the context growing "
@@ -156,7 +160,8 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     nsteps = args.steps + args.warmup
-    stored = args.boundary == "stored"
+    local = args.drafter == "round-local"
+    stored = args.boundary == "stored" and not local
     accepted = [i % (gamma + 1) for i in range(nsteps)]
     if stored:
         # committed rows before step i; the start is chosen so that the mean over
@@ -211,9 +216,11 @@ def main():
 
     def chain(i):
         dr.draft_chain([0], b_tok[i:i + 1], None if stored else [a[i:i + 1] for a in b_aux], gamma,
-                       out=out)
+                       out=out, round_local=local)
 
     def rebuild(i):
+        if local:
+            return
         a = accepted[i]
         r0 = i * (gamma + 1)
         dr.rebuild_after_verify([0], [a], r_tok[r0:r0 + a + 1], [x[r0:r0 + a + 1] for x in r_aux],
@@ -283,9 +290,12 @@ def main():
     tokens_per_s = gamma * args.steps / elapsed
     k_avg_s = (k_ms / 1e3) / max(k_launches, 1)
     kvb = 2 if args.kv == "bf16" else 4
-    k_bytes = kernel_bytes(cfg, args.kernel, L, kvb)
+    k_bytes = kernel_bytes(cfg, args.kernel, 0 if local else L, kvb)
     achieved = k_bytes / k_avg_s / 1e9
-    sb = [step_bytes(cfg, L_at[i], gamma, accepted[i], kvb, stored) for i in range(args.warmup, nsteps)]
+    if local:
+        sb = [step_bytes(cfg, 0, gamma, 0, kvb, rebuild=False) for i in range(args.warmup, nsteps)]
+    else:
+        sb = [step_bytes(cfg, L_at[i], gamma, accepted[i], kvb, stored) for i in range(args.warmup, nsteps)]
     step_gbs = (sum(sb) / args.steps) / (elapsed / args.steps) / 1e9
 
     cpu = None
@@ -308,12 +318,15 @@ def main():
         "config": {"workload": f"{cfg.name} drafter: n_embd {cfg.n_embd}, {cfg.n_head}/{cfg.n_head_kv} "
                                f"heads x {cfg.head_dim}, n_ff {cfg.n_ff}, draft vocab {cfg.draft_vocab}, "
                                f"target vocab {cfg.target_vocab}, {L} committed KV rows"
+                               + (" (not attended: round-local drafter)" if local else "")
                                + (f" (mean over the timed rounds; {L_at[args.warmup]}.."
                                   f"{L_at[-1]})" if stored else ""),
                    "batch": 1, "gamma": gamma,
                    "step": ("draft_chain from the stored boundary feature + rebuild_after_verify("
                             f"a+1 rows, a cycling 0..{gamma}, with the next boundary's taps)")
                    if stored else
+                   "round-local draft_chain (boundary taps; attention over the round's own rows; "
+                   "no rebuild)" if local else
                    f"draft_chain(boundary taps) + rebuild_after_verify(a+1 rows, a cycling 0..{gamma}) "
                    "+ rewind"},
         "roofline": {"bound": "hbm", "kernel": args.kernel, "achieved": round(achieved, 1),
@@ -327,7 +340,8 @@ def main():
         "chain_ms_p50": round(pct(chain_ms, 0.5), 4),
         "encode_us": round(encode_us, 2),
         "draft_step_us": round(per_step_us, 2),
-        "draft_step_hbm_frac": round(kernel_bytes_step(cfg, L, gamma, kvb) / (per_step_us * 1e-6) / 1e9
+        "draft_step_hbm_frac": round(kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
+                                     / (per_step_us * 1e-6) / 1e9
                                      / HBM_PEAK_GBS, 4),
         "prefill": {"rows": L, "ms": round(prefill_s * 1e3, 3),
                     "tflops": round(prefill_flop / prefill_s / 1e12, 2)},

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libeagle3.so")
 OK, E_INVAL, E_SHAPE, E_UNSUPPORTED, E_CAPACITY, E_STATE, E_HIP, E_OOM = 0, -1, -2, -3, -4, -5, -6, -7
 KEEP_SPEC = 1
 STORED_BOUNDARY = 2
+ROUND_LOCAL = 4
 KV_F32, KV_BF16 = 0, 1
 
 ERR_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_SHAPE: "E_SHAPE", E_UNSUPPORTED: "E_UNSUPPORTED",
@@ -263,9 +264,10 @@ class HostLedger:
     def prefill(self, seq, T, boundary=False) -> int:
         return library().eagle3_ledger_prefill(self._h, seq, T, int(boundary))
 
-    def chain(self, seq, gamma, keep_spec=False, stored_boundary=False):
+    def chain(self, seq, gamma, keep_spec=False, stored_boundary=False, round_local=False):
         g = c_int32(-1)
-        flags = (KEEP_SPEC if keep_spec else 0) | (STORED_BOUNDARY if stored_boundary else 0)
+        flags = ((KEEP_SPEC if keep_spec else 0) | (STORED_BOUNDARY if stored_boundary else 0)
+                 | (ROUND_LOCAL if round_local else 0))
         rc = library().eagle3_ledger_chain(self._h, seq, gamma, flags, byref(g))
         return rc, g.value
 

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   float* part_ml = a.part_ml;
   if (a.batched) {
     const int rb = blockIdx.z;
-    T = a.br.pos0[rb] + a.step + 1;
+    T = a.br.row0[rb] + a.step + 1;
     kv_off = (size_t)a.br.slot[rb] * a.seq_elems;
     qrow += (size_t)rb * a.n_head * HD;
     part_o += (size_t)rb * a.n_head * S * HD;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(128) void k_attn_combine_b(const float* __restrict_
   extern __shared__ float w[];  // [Smax]
   __shared__ float red[32];
   const int h = blockIdx.x, r = blockIdx.y;
-  const int T = br.pos0[r] + step + 1;
+  const int T = br.row0[r] + step + 1;
   const int S = (T + chunk - 1) / chunk;
   const float* ml = part_ml + ((size_t)r * n_head + h) * Smax * 2;
   float M = -INFINITY;
@@ -419,7 +419,7 @@ static int attn_batch_target() {
 
 int attn_batch_chunk(const BatchRows& br, int m, int step, int n_head_kv, int head_dim, int kv_f32) {
   long long rows = 0;
-  for (int r = 0; r < m; ++r) rows += br.pos0[r] + step + 1;
+  for (int r = 0; r < m; ++r) rows += br.row0[r] + step + 1;
   const int rpb = rows_per_block(head_dim, kv_f32);
   const long long target = attn_batch_target();
   long long c = (rows * n_head_kv + target - 1) / target;
@@ -440,7 +440,7 @@ hipError_t launch_attn_batched(const AttnArgs& a, int m, uint16_t* out_hi, uint1
   if (!a.batched || m < 1 || m > kBatchRows) return hipErrorInvalidValue;
   const int chunk = attn_batch_chunk(a.br, m, a.step, a.n_head_kv, a.head_dim, a.kv_f32);
   int Tmax = 0;
-  for (int r = 0; r < m; ++r) Tmax = std::max(Tmax, a.br.pos0[r] + a.step + 1);
+  for (int r = 0; r < m; ++r) Tmax = std::max(Tmax, a.br.row0[r] + a.step + 1);
   const int Smax = (Tmax + chunk - 1) / chunk;
   if (Smax > attn_batch_max_splits(a.cap, a.head_dim, a.kv_f32) || Tmax > a.cap)
     return hipErrorInvalidValue;

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(128) void k_bqkv(const BQkvArgs a) {
       const size_t esz = a.kv_f32 ? 4 : 2;
       char* base = static_cast<char*>(a.kv) +
                    ((size_t)a.br.slot[r] * a.seq_elems + (seg == 2 ? a.seq_elems / 2 : 0)) * esz;
-      const size_t at = ((size_t)head * a.cap + pos) * hd;
+      const size_t at = ((size_t)head * a.cap + a.br.row0[r] + a.step) * hd;
       kv_store(base, at + d0, y0, a.kv_f32);
       kv_store(base, at + d1, y1, a.kv_f32);
     }

@@ -78,6 +78,11 @@ struct eagle3_ctx {
   // next round's boundary taps come with them): f [max_seqs][n], f * hidden_norm
   // [max_seqs][n] and sum f^2 [max_seqs]
   float *bnd_y = nullptr, *bnd_w = nullptr, *bnd_ssq = nullptr;
+  // round-local scratch KV (EAGLE3_ROUND_LOCAL): per slot K then V, each
+  // [n_head_kv][max_gamma][head_dim]
+  char* kv_local = nullptr;
+  int cap_local = 0;
+  size_t kv_local_elems = 0;  // K + V elements per slot
 
   int tf_rows = 0;
   size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
@@ -105,6 +110,8 @@ struct eagle3_ctx {
   Profiler prof;
 
   void* k_of(int s) { return kv + size_t(s) * kv_seq_elems * kv_esize; }
+  void* k_local(int s) { return kv_local + size_t(s) * kv_local_elems * kv_esize; }
+  void* v_local(int s) { return kv_local + (size_t(s) * kv_local_elems + kv_local_elems / 2) * kv_esize; }
   void* v_of(int s) { return kv + (size_t(s) * kv_seq_elems + kv_seq_elems / 2) * kv_esize; }
 };
 
@@ -389,6 +396,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->bnd_y, size_t(cfg->max_seqs) * n));
   E3_TRY(dalloc(c, &c->bnd_w, size_t(cfg->max_seqs) * n));
   E3_TRY(dalloc(c, &c->bnd_ssq, size_t(cfg->max_seqs)));
+  c->cap_local = cfg->max_gamma;
+  c->kv_local_elems = size_t(2) * c->nkv * c->cap_local * c->hd;
+  E3_TRY(dalloc(c, &c->kv_local, size_t(cfg->max_seqs) * c->kv_local_elems * c->kv_esize));
   E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
 
   c->tf_rows = c->cap < 2048 ? c->cap : 2048;
@@ -812,8 +822,8 @@ namespace {
 // weights once for all rows still drafting.
 int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
                         const int32_t* btok, const float* a0, const float* a1, const float* a2,
-                        bool stored, int32_t gamma, int32_t* out, const std::vector<int32_t>& geff,
-                        const eagle3_debug* dbg, hipStream_t s) {
+                        bool stored, bool local, int32_t gamma, int32_t* out,
+                        const std::vector<int32_t>& geff, const eagle3_debug* dbg, hipStream_t s) {
   using e3::kBatchRows;
   const int n = c->n;
   for (int g0 = 0; g0 < n_seq; g0 += kBatchRows) {
@@ -835,6 +845,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       br.orig[r] = b;
       br.slot[r] = seq_ids[b];
       br.pos0[r] = c->ledger.seq(seq_ids[b]).committed;
+      br.row0[r] = local ? 0 : br.pos0[r];
       br.geff[r] = geff[size_t(b)];
     }
     auto gemm = [&](const uint16_t* W, int N, int K, const uint16_t* xh, const uint16_t* xl, int ldx,
@@ -889,16 +900,21 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
         e3::BQkvArgs qa{};
         qa.P = c->b_P; qa.S = S_qkv; qa.N = Nqkv; qa.br = br; qa.m = m; qa.step = j;
         qa.n_head = c->nh; qa.n_head_kv = c->nkv; qa.head_dim = c->hd; qa.rope_dim = c->rot;
-        qa.inv_freq = c->inv_freq; qa.q = c->b_q; qa.kv = c->kv; qa.seq_elems = c->kv_seq_elems;
-        qa.kv_f32 = c->kv_f32; qa.cap = c->cap;
+        qa.inv_freq = c->inv_freq; qa.q = c->b_q;
+        qa.kv = local ? c->kv_local : c->kv;
+        qa.seq_elems = local ? c->kv_local_elems : c->kv_seq_elems;
+        qa.kv_f32 = c->kv_f32; qa.cap = local ? c->cap_local : c->cap;
         E3_HIP(c, e3::launch_bqkv(qa, s), "qkv rows");
       }
       {
         e3::AttnArgs aa{};
-        aa.q = c->b_q; aa.k_cache = c->k_of(0); aa.v_cache = c->v_of(0); aa.kv_f32 = c->kv_f32;
-        aa.cap = c->cap; aa.n_head = c->nh; aa.n_head_kv = c->nkv; aa.head_dim = c->hd;
+        aa.q = c->b_q; aa.kv_f32 = c->kv_f32;
+        aa.k_cache = local ? c->k_local(0) : c->k_of(0);
+        aa.v_cache = local ? c->v_local(0) : c->v_of(0);
+        aa.cap = local ? c->cap_local : c->cap;
+        aa.n_head = c->nh; aa.n_head_kv = c->nkv; aa.head_dim = c->hd;
         aa.part_o = c->b_po; aa.part_ml = c->b_pml; aa.batched = 1; aa.step = j;
-        aa.seq_elems = c->kv_seq_elems; aa.br = br;
+        aa.seq_elems = local ? c->kv_local_elems : c->kv_seq_elems; aa.br = br;
         ProfScope ps(c, 5, s);
         E3_HIP(c, e3::launch_attn_batched(aa, m, c->bx_b_hi, c->bx_b_lo, c->bld_b, s), "attention");
       }
@@ -991,8 +1007,11 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
   if (!ctx) return EAGLE3_E_INVAL;
   if (n_seq < 0 || (n_seq > 0 && (!seq_ids_host || !gamma_eff_host)))
     return set_err(ctx, EAGLE3_E_INVAL, "bad sequence list");
-  if (flags & ~(EAGLE3_KEEP_SPEC | EAGLE3_STORED_BOUNDARY))
+  if (flags & ~(EAGLE3_KEEP_SPEC | EAGLE3_STORED_BOUNDARY | EAGLE3_ROUND_LOCAL))
     return set_err(ctx, EAGLE3_E_INVAL, "unknown flag");
+  const bool local = (flags & EAGLE3_ROUND_LOCAL) != 0;
+  if (local && (flags & EAGLE3_KEEP_SPEC))
+    return set_err(ctx, EAGLE3_E_INVAL, "a round-local chain keeps no speculative rows");
   if (n_seq == 0) return EAGLE3_OK;
   const bool stored = (flags & EAGLE3_STORED_BOUNDARY) != 0;
   if (!boundary_tok_dev || (gamma > 0 && !out_ids_dev))
@@ -1009,7 +1028,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
   for (int b = 0; b < n_seq; ++b) {
     const char* why = nullptr;
     const int s = seq_ids_host[b];
-    int rc = ctx->ledger.admit_chain(s, gamma, stored, &geff[size_t(b)], &why);
+    int rc = ctx->ledger.admit_chain(s, gamma, stored, local, &geff[size_t(b)], &why);
     if (rc) return set_err(ctx, rc, why);
     for (int j = 0; j < b; ++j)
       if (seq_ids_host[j] == s) return set_err(ctx, EAGLE3_E_INVAL, "duplicate sequence id");
@@ -1020,10 +1039,12 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
   const int n = ctx->n;
   if (n_seq > 1) {
     const int rc = draft_chain_batched(ctx, n_seq, seq_ids_host, boundary_tok_dev, aux0_dev,
-                                       aux1_dev, aux2_dev, stored, gamma, out_ids_dev, geff, dbg, s);
+                                       aux1_dev, aux2_dev, stored, local, gamma, out_ids_dev, geff,
+                                       dbg, s);
     if (rc) return rc;
-    for (int b = 0; b < n_seq; ++b)
-      ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
+    if (!local)
+      for (int b = 0; b < n_seq; ++b)
+        ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
     return EAGLE3_OK;
   }
   for (int b = 0; b < n_seq; ++b) {
@@ -1054,6 +1075,10 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
                                  size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
     for (int j = 0; j < ge; ++j) {
       const int pos = L + j;
+      const int row = local ? j : pos;  // KV row written (and rows 0..row attended)
+      void* kc = local ? ctx->k_local(sq) : ctx->k_of(sq);
+      void* vc = local ? ctx->v_local(sq) : ctx->v_of(sq);
+      const int cap = local ? ctx->cap_local : ctx->cap;
       const eagle3_ctx::GBuf* gn = &ctx->gb[1 + (j & 1)];
       e3::QkvArgs qa{};
       qa.w_qkv = ctx->w_qkv; qa.n = n; qa.n_head = ctx->nh; qa.n_head_kv = ctx->nkv;
@@ -1068,17 +1093,17 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
         qa.prev_out_id = out_b + (j - 1); qa.tok_store = ctx->tok_slots + (j - 1);
       }
       qa.gw = g->w_hid; qa.g_ssq = g->ssq; qa.g_ssq_count = g->count;
-      qa.w_in = ctx->nrm_in; qa.pos = pos; qa.q_out = ctx->q;
-      qa.k_cache = ctx->k_of(sq); qa.v_cache = ctx->v_of(sq); qa.cap = ctx->cap;
+      qa.w_in = ctx->nrm_in; qa.pos = pos; qa.row = row; qa.q_out = ctx->q;
+      qa.k_cache = kc; qa.v_cache = vc; qa.cap = cap;
       qa.kv_f32 = ctx->kv_f32;
       {
         ProfScope ps(ctx, 2, s);
         E3_HIP(ctx, e3::launch_qkv(qa, ctx->gcfg[e3::kGemvQkv], s), "qkv");
       }
       e3::AttnArgs aa{};
-      aa.q = ctx->q; aa.k_cache = ctx->k_of(sq); aa.v_cache = ctx->v_of(sq); aa.cap = ctx->cap;
+      aa.q = ctx->q; aa.k_cache = kc; aa.v_cache = vc; aa.cap = cap;
       aa.kv_f32 = ctx->kv_f32;
-      aa.T = pos + 1; aa.n_head = ctx->nh; aa.n_head_kv = ctx->nkv; aa.head_dim = ctx->hd;
+      aa.T = row + 1; aa.n_head = ctx->nh; aa.n_head_kv = ctx->nkv; aa.head_dim = ctx->hd;
       aa.part_o = ctx->part_o; aa.part_ml = ctx->part_ml; aa.out = ctx->ao;
       {
         ProfScope ps(ctx, 5, s);
@@ -1121,8 +1146,9 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
                                            ctx->dv, out_b + (ge - 1), ctx->tok_slots + (ge - 1), s),
            "argmax");
   }
-  for (int b = 0; b < n_seq; ++b)
-    ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
+  if (!local)
+    for (int b = 0; b < n_seq; ++b)
+      ctx->ledger.do_chain(seq_ids_host[b], geff[size_t(b)], (flags & EAGLE3_KEEP_SPEC) != 0);
   return EAGLE3_OK;
 }
 
@@ -1181,11 +1207,14 @@ int eagle3_ledger_prefill(eagle3_ledger* l, int32_t seq, int32_t T, int32_t with
 int eagle3_ledger_chain(eagle3_ledger* l, int32_t seq, int32_t gamma, uint32_t flags,
                         int32_t* gamma_eff) {
   if (!l || !gamma_eff) return EAGLE3_E_INVAL;
-  if (flags & ~(EAGLE3_KEEP_SPEC | EAGLE3_STORED_BOUNDARY)) return EAGLE3_E_INVAL;
+  if (flags & ~(EAGLE3_KEEP_SPEC | EAGLE3_STORED_BOUNDARY | EAGLE3_ROUND_LOCAL))
+    return EAGLE3_E_INVAL;
+  const bool local = (flags & EAGLE3_ROUND_LOCAL) != 0;
+  if (local && (flags & EAGLE3_KEEP_SPEC)) return EAGLE3_E_INVAL;
   int32_t g = 0;
-  int rc = l->l.admit_chain(seq, gamma, (flags & EAGLE3_STORED_BOUNDARY) != 0, &g, nullptr);
+  int rc = l->l.admit_chain(seq, gamma, (flags & EAGLE3_STORED_BOUNDARY) != 0, local, &g, nullptr);
   if (rc) return rc;
-  l->l.do_chain(seq, g, (flags & EAGLE3_KEEP_SPEC) != 0);
+  if (!local) l->l.do_chain(seq, g, (flags & EAGLE3_KEEP_SPEC) != 0);
   *gamma_eff = g;
   return EAGLE3_OK;
 }

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
       a.q_out[head * hd + d1] = y1;
     } else {
       void* base = seg == 1 ? a.k_cache : a.v_cache;
-      const size_t row = ((size_t)head * a.cap + a.pos) * hd;
+      const size_t row = ((size_t)head * a.cap + a.row) * hd;
       kv_store(base, row + d0, y0, a.kv_f32);
       kv_store(base, row + d1, y1, a.kv_f32);
     }

@@ -54,7 +54,8 @@ struct QkvArgs {
   const float* g_ssq;      // per-block partial sums of g^2
   int g_ssq_count;
   const float* w_in;       // input_layernorm
-  int pos;
+  int pos;                 // rotary position of the row
+  int row;                 // KV row written (pos, or the step in a round-local scratch)
   float* q_out;
   void* k_cache;           // this sequence's [n_head_kv][cap][head_dim]
   void* v_cache;
@@ -124,7 +125,8 @@ constexpr int kBatchRows = 32;
 struct BatchRows {
   int m;                      // rows in the pass
   int32_t orig[kBatchRows];   // row -> index in the caller's sequence list
-  int32_t pos0[kBatchRows];   // committed rows = position written by step 0
+  int32_t pos0[kBatchRows];   // committed rows = rotary position of step 0
+  int32_t row0[kBatchRows];   // KV row of step 0: pos0, or 0 in a round-local scratch
   int32_t slot[kBatchRows];   // sequence id (draft-KV slot)
   int32_t geff[kBatchRows];   // admitted chain length (>= 1)
 };
@@ -140,7 +142,7 @@ struct AttnArgs {
   float* part_o;           // [n_head][S][hd]
   float* part_ml;          // [n_head][S][2]
   float* out;              // [n_head * hd]
-  // batched form (batched != 0): row r of blockIdx.z attends rows 0..pos0[r]+step of
+  // batched form (batched != 0): row r of blockIdx.z attends rows 0..row0[r]+step of
   // slot[r], whose K/V start seq_elems * slot elements past k_cache / v_cache; q and
   // the partials are per row ([row][n_head][hd], [row][n_head][S][...])
   int batched;
@@ -230,7 +232,7 @@ struct BPrepArgs {
 };
 hipError_t launch_bprep(const BPrepArgs& a, hipStream_t s);
 // q|k|v of rows [0, m) from the QKV partials: rotate q, k at pos0 + step; q -> [32][qd],
-// k, v -> row pos0 + step of each row's cache slot.
+// k, v -> row row0 + step of each row's cache slot.
 struct BQkvArgs {
   const float* P;
   int S, N;

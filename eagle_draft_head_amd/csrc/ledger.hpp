@@ -15,6 +15,9 @@
 // round's boundary (the pages' prefill and rebuild_after_verify set the boundary
 // target feature); the sequence then holds a stored feature until the next
 // prefill, rebuild or rewind, and a chain round may start from it.
+// Round-local chains (the scratch-KV drafter of memra_engine `eagle.rs`: a draft KV
+// emptied every round) attend only over their own rows: gamma_eff = gamma, and no
+// length, speculative count or rebuild permission changes.
 #pragma once
 
 #include <stdint.h>
@@ -55,14 +58,18 @@ class Ledger {
     return EAGLE3_OK;
   }
 
-  int admit_chain(int32_t s, int32_t gamma, bool stored_boundary, int32_t* gamma_eff,
-                  const char** why) const {
+  int admit_chain(int32_t s, int32_t gamma, bool stored_boundary, bool round_local,
+                  int32_t* gamma_eff, const char** why) const {
     if (!valid_seq(s)) return fail(why, "bad sequence id", EAGLE3_E_INVAL);
     if (gamma < 0 || gamma > max_gamma_) return fail(why, "gamma out of range", EAGLE3_E_INVAL);
     const Seq& q = seq(s);
     if (q.spec) return fail(why, "speculative rows are live", EAGLE3_E_STATE);
     if (stored_boundary && !q.boundary)
       return fail(why, "no stored boundary feature for this sequence", EAGLE3_E_STATE);
+    if (round_local) {
+      *gamma_eff = gamma;
+      return EAGLE3_OK;
+    }
     int32_t room = max_ctx_ - q.committed;
     if (room < 0) room = 0;
     *gamma_eff = gamma < room ? gamma : room;

@@ -51,9 +51,10 @@ class Drafter:
     def draft_chain(self, seq_ids: Sequence[int], boundary_tok: torch.Tensor,
                     aux: Optional[Sequence[torch.Tensor]], gamma: int,
                     out: Optional[torch.Tensor] = None, keep_spec: bool = False,
-                    debug: bool = False, stream=None):
+                    debug: bool = False, stream=None, round_local: bool = False):
         """One chain round per sequence; aux=None starts from the stored boundary
-        features (set by prefill / rebuild_after_verify with next_aux)."""
+        features (set by prefill / rebuild_after_verify with next_aux); round_local
+        attends over the round's own rows only (a scratch KV emptied every round)."""
         n_seq = len(seq_ids)
         dev = boundary_tok.device
         if out is None:
@@ -62,7 +63,8 @@ class Drafter:
         if debug:
             logits = torch.zeros((n_seq, max(gamma, 1), self.dv), dtype=torch.float32, device=dev)
             hidden = torch.zeros((n_seq, gamma + 1, self.n), dtype=torch.float32, device=dev)
-        flags = (B.KEEP_SPEC if keep_spec else 0) | (B.STORED_BOUNDARY if aux is None else 0)
+        flags = ((B.KEEP_SPEC if keep_spec else 0) | (B.STORED_BOUNDARY if aux is None else 0)
+                 | (B.ROUND_LOCAL if round_local else 0))
         a = aux if aux is not None else (None, None, None)
         geff = B.eagle3_draft_chain(self.ctx, list(seq_ids), boundary_tok, a[0], a[1], a[2],
                                     gamma, out, flags, logits, hidden, stream)

@@ -49,6 +49,14 @@ enum {
    feature (set by eagle3_prefill / eagle3_rebuild_after_verify from next-boundary
    taps) instead of encoding taps; the tap pointers must then be NULL. */
 #define EAGLE3_STORED_BOUNDARY 2u
+/* eagle3_draft_chain flag: the round-local drafter (memra_engine `eagle.rs`,
+   `Eagle3Scratch`: the draft KV is a small scratch emptied every round).  Step j
+   attends over the round's own rows 0..j only, held in a per-sequence scratch of
+   max_gamma rows; rotary positions still continue from the committed length; the
+   committed rows are neither read nor written, gamma_eff = gamma, and the call
+   changes no length (a rebuild still needs a persistent chain round first).  Not
+   combinable with EAGLE3_KEEP_SPEC. */
+#define EAGLE3_ROUND_LOCAL 4u
 
 typedef struct eagle3_ctx eagle3_ctx;
 

@@ -18,6 +18,9 @@
  *   boundary feature, without it they drop it, rewind drops it; a chain with
  *   flags & EAGLE3_STORED_BOUNDARY needs one (else EAGLE3_E_STATE).  A prefill
  *   of T == 0 without a boundary changes nothing.
+ * Round-local chain (flags & EAGLE3_ROUND_LOCAL): spec == 0 and the gamma range
+ *   as above; gamma_eff = gamma; nothing changes (EAGLE3_KEEP_SPEC with it is
+ *   EAGLE3_E_INVAL).
  * Every call returns EAGLE3_OK or an EAGLE3_E_* code and changes nothing on
  * error.  Host memory only.
  */

@@ -180,11 +180,14 @@ class DrafterOracle:
     # one cached step: row at `pos` over K/V rows [0, pos)
     # ------------------------------------------------------------------
     def step(self, g: np.ndarray, tok: int, pos: int, Kctx: np.ndarray,
-             Vctx: np.ndarray) -> StepRecord:
+             Vctx: np.ndarray, nctx: int = None) -> StepRecord:
+        """nctx: context rows Kctx[:nctx] attended before the new row (default pos,
+        the persistent KV; a round-local scratch passes the round's own rows)."""
+        nctx = pos if nctx is None else nctx
         cat = self.input_cat(g[None, :], [tok])[0]
         q, k, v = self.qkv(cat, pos)
-        K = np.concatenate([Kctx[:pos], k[None]], axis=0)
-        V = np.concatenate([Vctx[:pos], v[None]], axis=0)
+        K = np.concatenate([Kctx[:nctx], k[None]], axis=0)
+        V = np.concatenate([Vctx[:nctx], v[None]], axis=0)
         o = attention_decode(q, K, V).reshape(-1)
         gsum = self.after_attention(o, g)
         logits = self.head(gsum)
@@ -241,6 +244,27 @@ class DrafterOracle:
             g, tok = r.gsum, r.target_id
         return recs
 
+    def draft_chain_round_local(self, s: int, boundary_aux, boundary_tok: int,
+                                gamma: int) -> List[StepRecord]:
+        """The scratch-KV drafter (memra_engine `eagle.rs`, `Eagle3Scratch`: a small
+        draft KV emptied at the start of every round): step j attends over the
+        round's own rows 0..j only; rope positions still continue from the
+        committed length; the persistent KV and the ledger lengths are untouched."""
+        L = self.ledger.committed(s)
+        g_eff = self.ledger.chain(s, gamma, round_local=True)
+        g = self.encode([np.asarray(a, dtype=np.float64).reshape(self.n)
+                         for a in boundary_aux])
+        tok = int(boundary_tok)
+        Ks = np.zeros((max(g_eff, 1), self.nkv, self.hd))
+        Vs = np.zeros((max(g_eff, 1), self.nkv, self.hd))
+        recs: List[StepRecord] = []
+        for j in range(g_eff):
+            r = self.step(g, tok, L + j, Ks, Vs, nctx=j)
+            Ks[j], Vs[j] = r.k, r.v
+            recs.append(r)
+            g, tok = r.gsum, r.target_id
+        return recs
+
 
 class StatelessChain:
     """The same chain computed from scratch at every step: all committed rows
@@ -252,7 +276,10 @@ class StatelessChain:
         self.d = drafter
 
     def run(self, committed_aux, committed_toks, boundary_aux, boundary_tok,
-            gamma: int) -> List[StepRecord]:
+            gamma: int, position0: int = 0) -> List[StepRecord]:
+        """position0: position of the first row (the committed rows, else the first
+        chain row); a round-local chain is the recompute over its own rows only,
+        placed at the committed length."""
         d = self.d
         toks_c = np.asarray(committed_toks, dtype=np.int64).reshape(-1)
         L = toks_c.shape[0]
@@ -271,10 +298,10 @@ class StatelessChain:
             chain_T.append(tok)
             G = np.concatenate([G_c, np.stack(chain_G)], axis=0)
             T = np.concatenate([toks_c, np.asarray(chain_T, dtype=np.int64)])
-            logits, gsum = d.layer_full(G, T)
+            logits, gsum = d.layer_full(G, T, position0 + np.arange(G.shape[0]))
             lg, gs = logits[-1], gsum[-1]
             i, t = d.pick(lg)
-            recs.append(StepRecord(L + j, g.copy(), tok, lg, gs, i, t,
+            recs.append(StepRecord(position0 + L + j, g.copy(), tok, lg, gs, i, t,
                                    top2_margin(lg)))
             g, tok = gs, t
         return recs

@@ -24,6 +24,11 @@ prefill or rebuild that is given the next boundary's taps leaves a stored
 feature, one without them drops it, and a rewind drops it; a chain may start
 from the stored feature only while one is held.  A prefill of zero rows without
 taps changes nothing (our reading; the pages are silent).
+
+Round-local chains (the scratch-KV drafter of memra_engine `eagle.rs`, whose draft
+KV is emptied every round) attend only over their own rows, so no capacity rule
+applies: gamma_eff = gamma, and they change no length, no speculative count and
+enable no rebuild.
 """
 from __future__ import annotations
 
@@ -81,7 +86,8 @@ class Ledger:
         if q.committed + T > self.max_ctx:
             raise LedgerError(E_CAPACITY, "prefill past max_ctx")
 
-    def admit_chain(self, s: int, gamma: int, stored_boundary: bool = False) -> int:
+    def admit_chain(self, s: int, gamma: int, stored_boundary: bool = False,
+                    round_local: bool = False) -> int:
         q = self._seq(s)
         if gamma < 0 or gamma > self.max_gamma:
             raise LedgerError(E_INVAL, "gamma out of range")
@@ -89,6 +95,8 @@ class Ledger:
             raise LedgerError(E_STATE, "speculative rows are live")
         if stored_boundary and not q.boundary:
             raise LedgerError(E_STATE, "no stored boundary feature")
+        if round_local:
+            return gamma
         return max(0, min(gamma, self.max_ctx - q.committed))
 
     def check_rebuild(self, s: int, a: int) -> None:
@@ -115,8 +123,12 @@ class Ledger:
         return start
 
     def chain(self, s: int, gamma: int, keep_spec: bool = False,
-              stored_boundary: bool = False) -> int:
-        g = self.admit_chain(s, gamma, stored_boundary)
+              stored_boundary: bool = False, round_local: bool = False) -> int:
+        if round_local and keep_spec:
+            raise LedgerError(E_INVAL, "a round-local chain keeps no speculative rows")
+        g = self.admit_chain(s, gamma, stored_boundary, round_local)
+        if round_local:
+            return g
         q = self.seqs[s]
         q.spec = g if keep_spec else 0
         q.last_gamma = g

@@ -67,8 +67,10 @@ def test_ledger_matches_oracle_on_random_histories(seed):
         elif op == 1:
             g = rnd.randrange(-1, mg + 2)
             keep = rnd.random() < 0.2
-            rc, ge = ours.chain(s, g, keep, bnd)
-            rrc, rge = _oracle_rc(lambda: ref.chain(s, g, keep_spec=keep, stored_boundary=bnd))
+            loc = rnd.random() < 0.25
+            rc, ge = ours.chain(s, g, keep, bnd, loc)
+            rrc, rge = _oracle_rc(lambda: ref.chain(s, g, keep_spec=keep, stored_boundary=bnd,
+                                                    round_local=loc))
             if rc == 0:
                 assert ge == rge
         elif op == 2:
@@ -104,6 +106,18 @@ def test_ledger_stored_boundary_rules():
     assert L.prefill(0, 1, boundary=True) == 0
     assert L.rewind(0, 14) == 0                                   # rewind drops it
     assert L.chain(0, 3, stored_boundary=True)[0] == B.E_STATE
+
+
+def test_ledger_round_local_rules():
+    L = B.HostLedger(100, 1, 8)
+    assert L.prefill(0, 98) == 0
+    assert L.chain(0, 8, round_local=True) == (0, 8)       # no capacity clamp
+    assert L.length(0) == (0, 98, 0)
+    assert L.rebuild(0, 0) == B.E_STATE                     # no persistent round since the commit
+    assert L.chain(0, 9, round_local=True)[0] == B.E_INVAL  # gamma range still applies
+    assert L.chain(0, 3, keep_spec=True, round_local=True)[0] == B.E_INVAL
+    assert L.chain(0, 3, keep_spec=True) == (0, 2)          # persistent: clamped, spec kept
+    assert L.chain(0, 3, round_local=True)[0] == B.E_STATE  # speculative rows are live
 
 
 def test_ledger_capacity_edge_97_3_100():

@@ -118,6 +118,41 @@ def test_batched_more_sequences_than_one_pass():
             max_ctx=160, seed=6)
 
 
+def test_batched_round_local():
+    """Round-local batched chains (each sequence attends over its own round only):
+    ragged committed lengths, sequences at the capacity edge draft the full gamma,
+    and the committed rows and lengths are untouched."""
+    cfg = small_variant()
+    lens = [0, 1, 37, 300, 699, 700]
+    S, gamma, max_ctx = len(lens), 5, 700
+    wd, wh = weights_both(cfg)
+    dr = gpu_drafter(cfg, wd, max_ctx=max_ctx, max_seqs=S)
+    orc = make_oracle(cfg, wh, max_ctx=max_ctx, max_seqs=S)
+    aux, toks = aux_np(cfg, 30, sum(lens)), toks_np(cfg, 30, sum(lens))
+    r0 = 0
+    for s, L in enumerate(lens):
+        if L:
+            orc.prefill(s, row_slice(aux, r0, r0 + L), toks[r0:r0 + L])
+            dr.prefill(s, _tok(toks[r0:r0 + L]), to_dev_aux(row_slice(aux, r0, r0 + L)))
+        r0 += L
+    kv0 = {s: [t.clone() for t in dr.kv_read(s, 0, L)] for s, L in enumerate(lens) if L}
+    for rd in range(3):
+        baux, btok = aux_np(cfg, 40 + rd, S), toks_np(cfg, 40 + rd, S)
+        out, geff, logits, hidden = dr.draft_chain(list(range(S)), _tok(btok), to_dev_aux(baux), gamma,
+                                                   debug=True, round_local=True)
+        torch.cuda.synchronize()
+        assert geff == [gamma] * S
+        for s in range(S):
+            recs = orc.draft_chain_round_local(s, [a[s] for a in baux], btok[s], gamma)
+            check_round(compare_round(recs, out, geff[s], logits, hidden, b=s),
+                        f"round-local round {rd} seq {s}")
+            assert dr.kv_len(s) == (lens[s], 0)
+    for s, (k0, v0) in kv0.items():
+        k1, v1 = dr.kv_read(s, 0, lens[s])
+        assert torch.equal(k0, k1) and torch.equal(v0, v1)
+    dr.close()
+
+
 def test_batched_stored_boundaries():
     """Boundary features from prefill (one of them a boundary-only prefill of an
     empty cache) and from packed rebuilds: 35 sequences, so the rebuild's boundary

@@ -105,6 +105,44 @@ def test_stored_boundary_rounds_ragged_and_empty():
     _run_rounds(TINY, rounds=5, L=0, gamma=5, stored=True)  # boundary-only prefill
 
 
+@pytest.mark.parametrize("cfg,L,gamma,rounds", [(TINY, 63, 3, 30), (TINY, 0, 8, 5),
+                                                (small_variant(), 300, 5, 8)],
+                         ids=["tiny", "empty", "ragged"])
+def test_round_local_chain_parity(cfg, L, gamma, rounds):
+    """The scratch-KV drafter: each round attends over its own rows only; the
+    committed rows stay bit-identical and no length changes."""
+    say(f"[parity] round-local cfg={cfg.name} L={L} gamma={gamma} rounds={rounds}")
+    wd, wh = weights_both(cfg)
+    dr = gpu_drafter(cfg, wd, max_ctx=L + 16, max_gamma=max(8, gamma))
+    orc = make_oracle(cfg, wh, max_ctx=L + 16)
+    aux, toks = aux_np(cfg, 0, L), toks_np(cfg, 0, L)
+    orc.prefill(0, aux, toks)
+    dr.prefill(0, _tok(toks), to_dev_aux(aux))
+    if L:
+        k0, v0 = (t.clone() for t in dr.kv_read(0, 0, L))
+    baux, btok = aux_np(cfg, 1, rounds), toks_np(cfg, 1, rounds)
+    steps = pinned = 0
+    for r in range(rounds):
+        recs = orc.draft_chain_round_local(0, [a[r] for a in baux], btok[r], gamma)
+        out, geff, logits, hidden = dr.draft_chain([0], _tok([btok[r]]), to_dev_aux(baux, slice(r, r + 1)),
+                                                   gamma, debug=True, round_local=True)
+        torch.cuda.synchronize()
+        assert geff == [gamma] and len(recs) == gamma
+        cmp = compare_round(recs, out, geff[0], logits, hidden)
+        check_round(cmp, f"round-local round {r}")
+        steps += len(cmp)
+        for c in cmp:
+            if not c.pinned:
+                break
+            pinned += 1
+        assert dr.kv_len(0) == (L, 0)
+    if L:
+        k1, v1 = dr.kv_read(0, 0, L)
+        assert torch.equal(k0, k1) and torch.equal(v0, v1)
+    say(f"[parity] round-local {cfg.name}: {pinned}/{steps} steps pinned")
+    assert pinned >= max(1, rounds // 2)  # the comparison is not vacuous
+
+
 def test_stored_boundary_state_errors(tiny):
     wd, _ = tiny
     dr = gpu_drafter(TINY, wd, max_ctx=200)

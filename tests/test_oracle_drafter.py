@@ -94,6 +94,44 @@ def test_cached_chain_equals_stateless_recompute(cfg, L, gamma, rounds):
             assert a.position == b.position
 
 
+@pytest.mark.parametrize("cfg,L,gamma", [(TINY, 63, 3), (TINY, 0, 5), (small_variant(), 40, 4)])
+def test_round_local_chain_equals_recompute_over_its_own_rows(cfg, L, gamma):
+    """The scratch-KV drafter: each step is the full layer recomputed over the
+    round's rows only, placed at positions L, L + 1, ..."""
+    d = make_oracle(cfg)
+    aux, toks = aux_np(cfg, 0, L + 1), toks_np(cfg, 0, L + 1)
+    d.prefill(0, row_slice(aux, 0, L), toks[:L])
+    K0, V0 = d.K[0][:L].copy(), d.V[0][:L].copy()
+    b_aux = [a[L] for a in aux]
+    recs = d.draft_chain_round_local(0, b_aux, toks[L], gamma)
+    ref = StatelessChain(d).run(row_slice(aux, 0, 0), toks[:0], b_aux, toks[L], gamma, position0=L)
+    assert len(recs) == gamma
+    assert [x.target_id for x in recs] == [x.target_id for x in ref]
+    for a, b in zip(recs, ref):
+        assert np.allclose(a.logits, b.logits, **TOL)
+        assert np.allclose(a.gsum, b.gsum, **TOL)
+        assert a.position == b.position
+    # the persistent rows and the lengths are untouched
+    assert d.ledger.committed(0) == L and d.ledger.spec(0) == 0
+    assert np.array_equal(d.K[0][:L], K0) and np.array_equal(d.V[0][:L], V0)
+
+
+def test_round_local_chain_depends_on_relative_positions_only(tiny_w):
+    """Rotary attention sees only position differences: the round-local chain at
+    L equals the persistent chain of an empty cache (positions from 0)."""
+    d = make_oracle(TINY, tiny_w, max_seqs=2)
+    L = 50
+    aux, toks = aux_np(TINY, 2, L + 1), toks_np(TINY, 2, L + 1)
+    d.prefill(0, row_slice(aux, 0, L), toks[:L])
+    b_aux = [a[L] for a in aux]
+    loc = d.draft_chain_round_local(0, b_aux, toks[L], 4)
+    emp = d.draft_chain(1, b_aux, toks[L], 4)
+    assert [x.target_id for x in loc] == [x.target_id for x in emp]
+    for a, b in zip(loc, emp):
+        assert np.allclose(a.logits, b.logits, rtol=1e-9, atol=1e-11)
+        assert a.position == b.position + L
+
+
 def test_chain_round_leaves_kv_bit_identical(tiny_w):
     d = make_oracle(TINY, tiny_w)
     L = 63
