@@ -23,6 +23,9 @@ namespace e3 {
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnMaxChunk = 512;
+// 256 rather than 512: a 4096-row context over 4 KV heads then splits 64 ways, and its
+// combine loads every split in one round trip (128 splits took two)
+constexpr int kAttnSingleBlocks = 256;
 
 // 16 bytes of a KV row as floats: 8 bf16 or 4 fp32 values
 template <typename KT>
@@ -343,9 +346,21 @@ static inline int rows_per_block(int hd, int kv_f32) {
   return kAttnWaves * (64 / (hd / kAttnLaneElems));
 }
 
+// (kv head, split) blocks aimed at by the single-row attention; EAGLE3_ATTN_BLOCKS
+// overrides it (8..512) for tuning
+static int attn_single_blocks() {
+  static const int t = [] {
+    const char* e = std::getenv("EAGLE3_ATTN_BLOCKS");
+    const int v = e ? std::atoi(e) : 0;
+    return (v >= 8 && v <= 512) ? v : kAttnSingleBlocks;
+  }();
+  return t;
+}
+
 static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S) {
   const int rpb = rows_per_block(hd, kv_f32);
-  const int target = n_head_kv >= 512 ? 1 : 512 / n_head_kv;
+  const int blocks = attn_single_blocks();
+  const int target = n_head_kv >= blocks ? 1 : blocks / n_head_kv;
   int c = (T + target - 1) / target;
   c = ((c + rpb - 1) / rpb) * rpb;
   if (c < rpb) c = rpb;
