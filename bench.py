@@ -3,17 +3,23 @@
 A step is one speculative round of the drafter at batch 1 on the Qwen3-8B-shaped
 workload (n_embd 4096, 32/8 heads x 128, n_ff 12288, draft vocab 32000,
 target vocab 151936, 1024 committed KV rows):
-  draft_chain (encode + gamma = 3 greedy draft steps + rewind) followed by
-  rebuild_after_verify of a + 1 teacher-forced rows (a cycles 0..3), then a
-  rewind back to 1024 committed rows so every step sees the same context.
+  draft_chain (gamma = 3 greedy draft steps from the boundary feature, then the
+  rewind of its speculative rows) followed by rebuild_after_verify of a + 1
+  teacher-forced rows (a cycles 0..3) that also encodes the next round's
+  boundary taps in the same pass over W_fc.  The committed context grows by
+  a + 1 rows a step, starting where its mean over the timed steps is 1024.
+  --boundary taps: the chain encodes the boundary taps itself and each step ends
+  with a rewind to exactly 1024 rows (the default for page4, whose rounds are
+  rewound).
 Inputs are seeded synthetic tensors already resident in HBM.  `value` is draft
 tokens per second over the timed steps.  The dominant kernel (the lm_head GEMV
 with fused final norm and argmax) is timed with HIP events on the launching
-stream during the same timed region; its algorithmic bytes per launch over its
+stream in a pass over the same steps; its algorithmic bytes per launch over its
 average duration give `roofline.achieved`.  The CPU oracle is timed on a bounded
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--boundary stored|taps] [--drafter persistent|round-local] [--kv f32|bf16]
        [--no-cpu] [--kernel lm_head|gate_up|qkv|down|o_proj|attention|encode]
 """
 from __future__ import annotations
@@ -126,12 +132,13 @@ def main():
     ap.add_argument("--drafter", choices=["persistent", "round-local"], default="persistent",
                     help="round-local: the scratch-KV drafter (each round attends over its own rows "
                          "only; a step is one chain round from encoded taps, no rebuild)")
-    ap.add_argument("--boundary", choices=["stored", "taps"], default="stored",
+    ap.add_argument("--boundary", choices=["stored", "taps"], default=None,
                     help="stored: each rebuild also encodes the next round's boundary taps (one "
                          "W_fc pass) and the chain starts from that feature, the context growing "
                          "by a+1 rows per round around a mean of the workload's length; taps: the "
                          "chain encodes the boundary taps itself and every round is rewound to "
-                         "the workload's length")
+                         "the workload's length (the default for page4, whose rounds are rewound; "
+                         "stored elsewhere)")
     args = ap.parse_args()
     args.kernel_set = args.kernel is not None
     if args.kernel is None:
@@ -161,6 +168,8 @@ def main():
     print(f"[bench] weights generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     nsteps = args.steps + args.warmup
     local = args.drafter == "round-local"
+    if args.boundary is None:
+        args.boundary = "taps" if args.workload == "page4" else "stored"
     stored = args.boundary == "stored" and not local
     accepted = [i % (gamma + 1) for i in range(nsteps)]
     if stored:
