@@ -31,15 +31,23 @@ def _setup(cfg, L, max_ctx):
     return dr, orc
 
 
-def _rounds(cfg, dr, orc, gammas, rebuild_pattern):
+def _rounds(cfg, dr, orc, gammas, rebuild_pattern, stored=False):
+    """stored: the benchmark's protocol; every round starts from the boundary feature
+    stored by the previous rebuild (the first by a boundary-only prefill), and every
+    rebuild (rebuild_pattern then has no None) also takes the next round's taps."""
     steps = pinned = 0
+    b_auxs = [gen.aux_taps(cfg, 101 + i, 1, device="cuda") for i in range(len(gammas) + 1)]
+    if stored:
+        assert None not in rebuild_pattern
+        dr.prefill(0, gen.tokens(cfg, 0, 0, device="cuda"), [], next_aux=b_auxs[0])
     stream = 1
     for gi, gamma in enumerate(gammas):
-        b_aux = gen.aux_taps(cfg, 100 + stream, 1, device="cuda")
+        b_aux = b_auxs[gi]
         b_tok = gen.tokens(cfg, 100 + stream, 1, device="cuda")
         stream += 1
         recs = orc.draft_chain(0, [a[0].double().cpu().numpy() for a in b_aux], int(b_tok[0]), gamma)
-        out, geff, logits, hidden = dr.draft_chain([0], b_tok, b_aux, gamma, debug=True)
+        out, geff, logits, hidden = dr.draft_chain([0], b_tok, None if stored else b_aux, gamma,
+                                                   debug=True)
         torch.cuda.synchronize()
         cmp = compare_round(recs, out, geff[0], logits, hidden)
         check_round(cmp, f"{cfg.name} gamma={gamma}")
@@ -60,7 +68,8 @@ def _rounds(cfg, dr, orc, gammas, rebuild_pattern):
                                     dtype=torch.int32, device="cuda")
             orc.rebuild_after_verify(0, a, [x.double().cpu().numpy() for x in rows_aux],
                                      rows_tok.cpu().numpy())
-            dr.rebuild_after_verify([0], [a], rows_tok, rows_aux)
+            dr.rebuild_after_verify([0], [a], rows_tok, rows_aux,
+                                    next_aux=b_auxs[gi + 1] if stored else None)
             assert dr.kv_len(0) == (orc.ledger.committed(0), 0)
     return pinned, steps
 
@@ -80,6 +89,18 @@ def test_qwen3_8b_shape_chain_parity():
     _kv_check(dr, orc, None)
     pinned, steps = _rounds(cfg, dr, orc, [3] * 6, [3, None, 0, 2])
     say(f"[fullsize] {cfg.name}: {pinned}/{steps} steps pinned")
+    assert pinned >= steps // 2
+    _kv_check(dr, orc, None)
+    dr.close()
+
+
+def test_qwen3_8b_shape_stored_boundary_rounds():
+    """The benchmark's default protocol at full size: chains from the boundary
+    feature the rebuild stored (its fc row rode on the rebuild's W_fc pass)."""
+    cfg = QWEN3_8B
+    dr, orc = _setup(cfg, cfg.context, cfg.context + 64)
+    pinned, steps = _rounds(cfg, dr, orc, [3] * 6, [3, 0, 2, 1], stored=True)
+    say(f"[fullsize] {cfg.name} stored boundary: {pinned}/{steps} steps pinned")
     assert pinned >= steps // 2
     _kv_check(dr, orc, None)
     dr.close()
