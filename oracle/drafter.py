@@ -88,7 +88,10 @@ class DrafterOracle:
         self.rot = geom.rope_dim
         self.theta = float(geom.rope_theta)
         self.eps = float(geom.rms_eps)
-        W = {k: bf16_bits_to_f64(_bits(weights[k])) for k in WEIGHT_NAMES}
+        # bf16 weights (bit patterns or tensors), or fp64 arrays used as given (the
+        # int4 weights' exact values, oracle.int4)
+        W = {k: (weights[k] if isinstance(weights[k], np.ndarray) and weights[k].dtype == np.float64
+                 else bf16_bits_to_f64(_bits(weights[k]))) for k in WEIGHT_NAMES}
         self.W = W
         assert W["fc"].shape == (self.n, 3 * self.n), "fc in != 3 n_embd"
         assert W["q_proj"].shape == (self.nh * self.hd, 2 * self.n), "q_proj shape"
