@@ -20,6 +20,7 @@ KEEP_SPEC = 1
 STORED_BOUNDARY = 2
 ROUND_LOCAL = 4
 KV_F32, KV_BF16 = 0, 1
+WEIGHTS_BF16, WEIGHTS_I4 = 0, 1
 
 ERR_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_SHAPE: "E_SHAPE", E_UNSUPPORTED: "E_UNSUPPORTED",
              E_CAPACITY: "E_CAPACITY", E_STATE: "E_STATE", E_HIP: "E_HIP", E_OOM: "E_OOM"}
@@ -43,7 +44,8 @@ class eagle3_config(ctypes.Structure):
                 ("head_dim", c_int32), ("n_ff", c_int32), ("draft_vocab", c_int32),
                 ("target_vocab", c_int32), ("n_aux", c_int32), ("rope_dim", c_int32),
                 ("rope_theta", c_float), ("rms_eps", c_float), ("max_ctx", c_int32),
-                ("max_gamma", c_int32), ("max_seqs", c_int32), ("kv_dtype", c_int32)]
+                ("max_gamma", c_int32), ("max_seqs", c_int32), ("kv_dtype", c_int32),
+                ("weight_format", c_int32)]
 
 
 class eagle3_weights(ctypes.Structure):
@@ -79,6 +81,7 @@ def library() -> ctypes.CDLL:
         "eagle3_rewind": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_kv_len": ([P, c_int32, POINTER(c_int32), POINTER(c_int32)], ctypes.c_int),
         "eagle3_kv_read": ([P, c_int32, c_int32, c_int32, P, P, P], ctypes.c_int),
+        "eagle3_weights_i4_read": ([P, c_int32, P, P, P], ctypes.c_int),
         "eagle3_last_error": ([P], c_char_p),
         "eagle3_profile_enable": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_profile_read": ([P, POINTER(c_double), POINTER(c_int64)], ctypes.c_int),
@@ -141,13 +144,13 @@ def eagle3_resolve_rope_dim(rotary_dim: Optional[int], partial_factor: Optional[
 
 
 def make_config(geom, max_ctx: int, max_gamma: int = 16, max_seqs: int = 1,
-                kv_dtype: int = KV_F32) -> eagle3_config:
+                kv_dtype: int = KV_F32, weight_format: int = WEIGHTS_BF16) -> eagle3_config:
     return eagle3_config(
         n_embd=geom.n_embd, n_head=geom.n_head, n_head_kv=geom.n_head_kv, head_dim=geom.head_dim,
         n_ff=geom.n_ff, draft_vocab=geom.draft_vocab, target_vocab=geom.target_vocab,
         n_aux=getattr(geom, "n_aux", 3), rope_dim=geom.rope_dim, rope_theta=float(geom.rope_theta),
         rms_eps=float(geom.rms_eps), max_ctx=int(max_ctx), max_gamma=int(max_gamma),
-        max_seqs=int(max_seqs), kv_dtype=int(kv_dtype))
+        max_seqs=int(max_seqs), kv_dtype=int(kv_dtype), weight_format=int(weight_format))
 
 
 def make_weights(tensors: Dict[str, object], d2t_host) -> eagle3_weights:
@@ -228,6 +231,14 @@ def eagle3_kv_len(ctx, seq: int):
 def eagle3_kv_read(ctx, seq: int, row0: int, nrows: int, k_out, v_out, stream=None) -> None:
     _check(ctx, library().eagle3_kv_read(ctx, seq, row0, nrows, _ptr(k_out), _ptr(v_out),
                                          _stream(stream)))
+
+
+I4_MATRICES = {"fc": 0, "qkv": 1, "o_proj": 2, "gate_up": 3, "down_proj": 4, "lm_head": 5}
+
+
+def eagle3_weights_i4_read(ctx, matrix: str, codes, scales, stream=None) -> None:
+    _check(ctx, library().eagle3_weights_i4_read(ctx, I4_MATRICES[matrix], _ptr(codes),
+                                                 _ptr(scales), _stream(stream)))
 
 
 def eagle3_last_error(ctx) -> str:

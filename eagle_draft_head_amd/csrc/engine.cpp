@@ -51,6 +51,20 @@ struct eagle3_ctx {
   int n = 0, nh = 0, nkv = 0, hd = 0, qd = 0, kvd = 0, ff = 0, dv = 0, vt = 0, rot = 0, cap = 0;
   std::vector<void*> allocs;
 
+  // int4 projection weights (weight_format EAGLE3_WEIGHTS_I4): codes and scales of
+  // each matrix, rows in the same (repacked) order as the bf16 copies
+  struct I4W {
+    uint8_t* q = nullptr;
+    uint16_t* s = nullptr;
+  } i4_fc, i4_qkv, i4_o, i4_gu, i4_d, i4_lm;
+  bool i4 = false;
+  // the weight stream a GEMV reads: the bf16 rows or the int4 codes, and the scales
+  const uint16_t* wq(const uint16_t* bf16, const I4W& m, size_t row0 = 0, size_t K = 0) const {
+    return i4 ? reinterpret_cast<const uint16_t*>(m.q + row0 * (K / 2)) : bf16 + row0 * K;
+  }
+  const uint16_t* ws(const I4W& m, size_t row0 = 0, size_t K = 0) const {
+    return i4 ? m.s + row0 * (K / 32) : nullptr;
+  }
   uint16_t *w_fc = nullptr, *w_qkv = nullptr, *w_o = nullptr, *w_gu = nullptr, *w_d = nullptr,
            *w_lm = nullptr, *embed = nullptr;
   float *nrm_in = nullptr, *nrm_hid = nullptr, *nrm_post = nullptr, *nrm_fin = nullptr;
@@ -232,6 +246,13 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (cfg->max_gamma > 64) return bad("max_gamma above 64", EAGLE3_E_UNSUPPORTED);
   if (cfg->kv_dtype != EAGLE3_KV_F32 && cfg->kv_dtype != EAGLE3_KV_BF16)
     return bad("unknown kv_dtype", EAGLE3_E_INVAL);
+  if (cfg->weight_format != EAGLE3_WEIGHTS_BF16 && cfg->weight_format != EAGLE3_WEIGHTS_I4)
+    return bad("unknown weight_format", EAGLE3_E_INVAL);
+  if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
+    if (cfg->max_seqs != 1) return bad("int4 weights: batch-1 drafting only (max_seqs 1)", EAGLE3_E_UNSUPPORTED);
+    if (cfg->n_embd % 32 || (int64_t(cfg->n_head) * cfg->head_dim) % 32 || cfg->n_ff % 32)
+      return bad("int4 weights need input widths that are multiples of 32", EAGLE3_E_UNSUPPORTED);
+  }
   {  // the GEMV kernels stage a whole fp32 activation vector in LDS
     const int64_t n = cfg->n_embd, kmax = std::max<int64_t>(
         {3 * n, 2 * n, int64_t(cfg->n_head) * cfg->head_dim, int64_t(cfg->n_ff)});
@@ -537,6 +558,21 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     for (int64_t i = 0; i < ff; ++i) dst[size_t(i)] = int32_t(2 * i + 1);
     E3_TRY(gather(c->w_gu, w->up_proj, int(n)));
   }
+  if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
+    c->i4 = true;
+    auto quant = [&](const uint16_t* W, int64_t rows, int64_t K, eagle3_ctx::I4W* m) -> int {
+      E3_TRY(dalloc(c, &m->q, size_t(rows) * size_t(K) / 2));
+      E3_TRY(dalloc(c, &m->s, size_t(rows) * size_t(K) / 32));
+      E3_TRYH(e3::launch_quant_i4(W, int(rows), int(K), m->q, m->s, s), "int4 quantize");
+      return EAGLE3_OK;
+    };
+    E3_TRY(quant(c->w_fc, n, 3 * n, &c->i4_fc));
+    E3_TRY(quant(c->w_qkv, N_qkv, 2 * n, &c->i4_qkv));
+    E3_TRY(quant(c->w_o, n, qd, &c->i4_o));
+    E3_TRY(quant(c->w_gu, 2 * ff, n, &c->i4_gu));
+    E3_TRY(quant(c->w_d, n, ff, &c->i4_d));
+    E3_TRY(quant(c->w_lm, dv, n, &c->i4_lm));
+  }
   E3_TRYH(hipStreamSynchronize(s), "load sync");
 #undef E3_TRY
 #undef E3_TRYH
@@ -598,6 +634,31 @@ int eagle3_kv_read(const eagle3_ctx* cctx, int32_t seq, int32_t row0, int32_t nr
   return EAGLE3_OK;
 }
 
+int eagle3_weights_i4_read(const eagle3_ctx* cctx, int32_t matrix, void* codes_dev,
+                           void* scales_dev, void* stream) {
+  eagle3_ctx* ctx = const_cast<eagle3_ctx*>(cctx);
+  if (!ctx || !codes_dev || !scales_dev) return EAGLE3_E_INVAL;
+  if (!ctx->i4) return set_err(ctx, EAGLE3_E_STATE, "the weights are not int4");
+  const int64_t n = ctx->n;
+  const eagle3_ctx::I4W* m = nullptr;
+  int64_t rows = 0, K = 0;
+  switch (matrix) {
+    case EAGLE3_I4_FC: m = &ctx->i4_fc; rows = n; K = 3 * n; break;
+    case EAGLE3_I4_QKV: m = &ctx->i4_qkv; rows = ctx->qd + 2 * ctx->kvd; K = 2 * n; break;
+    case EAGLE3_I4_O: m = &ctx->i4_o; rows = n; K = ctx->qd; break;
+    case EAGLE3_I4_GATE_UP: m = &ctx->i4_gu; rows = 2 * ctx->ff; K = n; break;
+    case EAGLE3_I4_DOWN: m = &ctx->i4_d; rows = n; K = ctx->ff; break;
+    case EAGLE3_I4_LM_HEAD: m = &ctx->i4_lm; rows = ctx->dv; K = n; break;
+    default: return set_err(ctx, EAGLE3_E_INVAL, "unknown matrix");
+  }
+  hipStream_t s = as_stream(stream);
+  E3_HIP(ctx, hipMemcpyAsync(codes_dev, m->q, size_t(rows * K / 2), hipMemcpyDeviceToDevice, s),
+         "int4 read");
+  E3_HIP(ctx, hipMemcpyAsync(scales_dev, m->s, size_t(rows * K / 32) * 2, hipMemcpyDeviceToDevice, s),
+         "int4 read");
+  return EAGLE3_OK;
+}
+
 // ---- teacher-forced append over packed rows ----------------------------------
 namespace {
 
@@ -623,8 +684,10 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
   const int n = c->n, kvd2 = 2 * c->kvd;
   const int all = total + bi.count();
   size_t seg_i = 0;
+  // int4 weights: every pass on the multi-vector GEMV (at most 16 rows)
+  const int pass_rows = c->i4 ? std::min(16, c->tf_rows) : c->tf_rows;
   for (int c0 = 0; c0 < all;) {
-    int P = std::min(c->tf_rows, all - c0);
+    int P = std::min(pass_rows, all - c0);
     const int T = std::max(0, std::min(total, c0 + P) - c0);  // teacher-forced rows of the pass
     int Tb = P - T;
     if (Tb > e3::kBndRows) {
@@ -655,7 +718,8 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       // weight-streaming path: every weight chunk applied to all rows of the pass
       {
         ProfScope ps(c, 7, s);
-        E3_HIP(c, e3::launch_gemv_multi(c->w_fc, n, 3 * n, x0, x1, x2, n, P, c->tf_F, &sp1, s, yb),
+        E3_HIP(c, e3::launch_gemv_multi(c->wq(c->w_fc, c->i4_fc), c->ws(c->i4_fc), n, 3 * n, x0, x1,
+                                        x2, n, P, c->tf_F, &sp1, s, yb),
                "fc gemv");
       }
       f_split = size_t(e3::gemv_multi_width(P)) * n;
@@ -664,8 +728,11 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
              "tf cat");
       if (T > 0) {
         ProfScope ps(c, 8, s);
-        E3_HIP(c, e3::launch_gemv_multi(c->w_qkv + size_t(c->qd) * 2 * n, kvd2, 2 * n, c->tf_cat32,
-                                        nullptr, nullptr, 0, T, c->tf_P, &sp2, s), "kv gemv");
+        // the K and V rows of the fused QKV matrix
+        E3_HIP(c, e3::launch_gemv_multi(c->wq(c->w_qkv, c->i4_qkv, size_t(c->qd), 2 * n),
+                                        c->ws(c->i4_qkv, size_t(c->qd), 2 * n), kvd2, 2 * n,
+                                        c->tf_cat32, nullptr, nullptr, 0, T, c->tf_P, &sp2, s),
+               "kv gemv");
       }
       p_split = size_t(e3::gemv_multi_width(T > 0 ? T : 1)) * kvd2;
     } else {
@@ -1065,7 +1132,8 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
     } else {
       e3::VecOut eo{ctx->gb[0].y, ctx->gb[0].w_hid, ctx->nrm_hid, nullptr, nullptr, ctx->gb[0].ssq};
       ProfScope ps(ctx, 6, s);
-      E3_HIP(ctx, e3::launch_encode(ctx->w_fc, n, aux0_dev + size_t(b) * n, aux1_dev + size_t(b) * n,
+      E3_HIP(ctx, e3::launch_encode(ctx->wq(ctx->w_fc, ctx->i4_fc), ctx->ws(ctx->i4_fc), n,
+                                    aux0_dev + size_t(b) * n, aux1_dev + size_t(b) * n,
                                     aux2_dev + size_t(b) * n, eo, ctx->gcfg[e3::kGemvEncode], s),
              "encode");
     }
@@ -1081,7 +1149,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       const int cap = local ? ctx->cap_local : ctx->cap;
       const eagle3_ctx::GBuf* gn = &ctx->gb[1 + (j & 1)];
       e3::QkvArgs qa{};
-      qa.w_qkv = ctx->w_qkv; qa.n = n; qa.n_head = ctx->nh; qa.n_head_kv = ctx->nkv;
+      qa.w_qkv = ctx->wq(ctx->w_qkv, ctx->i4_qkv); qa.s_qkv = ctx->ws(ctx->i4_qkv); qa.n = n; qa.n_head = ctx->nh; qa.n_head_kv = ctx->nkv;
       qa.head_dim = ctx->hd; qa.rope_dim = ctx->rot; qa.inv_freq = ctx->inv_freq;
       qa.eps = ctx->cfg.rms_eps; qa.embed = ctx->embed; qa.vocab = ctx->vt;
       if (j == 0) {
@@ -1112,23 +1180,26 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       {
         e3::VecOut oo{ctx->x1, ctx->x1w, ctx->nrm_post, nullptr, nullptr, ctx->x1_ssq};
         ProfScope ps(ctx, 4, s);
-        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_o, n, ctx->qd, ctx->ao, g->y, oo,
+        E3_HIP(ctx, e3::launch_gemv_resid(ctx->wq(ctx->w_o, ctx->i4_o), ctx->ws(ctx->i4_o), n, ctx->qd,
+                                          ctx->ao, g->y, oo,
                                           ctx->gcfg[e3::kGemvO], s), "o_proj");
       }
       {
         ProfScope ps(ctx, 1, s);
-        E3_HIP(ctx, e3::launch_gateup(ctx->w_gu, ctx->ff, n, ctx->x1w, ctx->x1_ssq, ctx->x1_count,
+        E3_HIP(ctx, e3::launch_gateup(ctx->wq(ctx->w_gu, ctx->i4_gu), ctx->ws(ctx->i4_gu), ctx->ff, n,
+                                      ctx->x1w, ctx->x1_ssq, ctx->x1_count,
                                       ctx->cfg.rms_eps, ctx->act, ctx->gcfg[e3::kGemvGateUp], s),
                "gate/up");
       }
       {
         e3::VecOut dn{gn->y, gn->w_norm, ctx->nrm_fin, gn->w_hid, ctx->nrm_hid, gn->ssq};
         ProfScope ps(ctx, 3, s);
-        E3_HIP(ctx, e3::launch_gemv_resid(ctx->w_d, n, ctx->ff, ctx->act, ctx->x1, dn,
+        E3_HIP(ctx, e3::launch_gemv_resid(ctx->wq(ctx->w_d, ctx->i4_d), ctx->ws(ctx->i4_d), n, ctx->ff,
+                                          ctx->act, ctx->x1, dn,
                                           ctx->gcfg[e3::kGemvDown], s), "down");
       }
       e3::LmHeadArgs la{};
-      la.w_lm = ctx->w_lm; la.dv = ctx->dv; la.n = n; la.hw = gn->w_norm; la.h_ssq = gn->ssq;
+      la.w_lm = ctx->wq(ctx->w_lm, ctx->i4_lm); la.s_lm = ctx->ws(ctx->i4_lm); la.dv = ctx->dv; la.n = n; la.hw = gn->w_norm; la.h_ssq = gn->ssq;
       la.h_ssq_count = gn->count; la.eps = ctx->cfg.rms_eps;
       la.logits_dbg = (dbg && dbg->logits) ? dbg->logits + (size_t(b) * gamma + j) * ctx->dv : nullptr;
       la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;

@@ -115,6 +115,156 @@ __device__ __forceinline__ void rows_dot_issued(const uint16_t* __restrict__ W, 
   rows_dot_from<R, U>(wp, lane + 64 * U, K >> 3, x4, acc);
 }
 
+// ---------------------------------------------------------------------------
+// int4 weights (kernels.hpp, I4 weights): a row of K weights is K / 2 bytes of
+// codes (element 2i in the low nibble, stored as q + 8) and K / 32 bf16 scales, one
+// per group of 32.  A lane's 16-byte chunk is one whole group, so its dot product
+// is scale * (sum of nibble * x - 8 * sum of x), the x sum shared by the rows.
+
+// sum over the 32 elements of a group of nibble * x (x: the group's 8 float4)
+__device__ __forceinline__ float nib_dot(const uint4 w, const float4 (&x)[8]) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // byte j of the word holds elements 8i + 2j (low nibble) and 8i + 2j + 1
+    const uint32_t lo = ws[i] & 0x0F0F0F0Fu, hi = (ws[i] >> 4) & 0x0F0F0F0Fu;
+    const float4 a = x[2 * i], b = x[2 * i + 1];
+    acc = fmaf(float(lo & 0xFFu), a.x, acc);
+    acc = fmaf(float(hi & 0xFFu), a.y, acc);
+    acc = fmaf(float((lo >> 8) & 0xFFu), a.z, acc);
+    acc = fmaf(float((hi >> 8) & 0xFFu), a.w, acc);
+    acc = fmaf(float((lo >> 16) & 0xFFu), b.x, acc);
+    acc = fmaf(float((hi >> 16) & 0xFFu), b.y, acc);
+    acc = fmaf(float(lo >> 24), b.z, acc);
+    acc = fmaf(float(hi >> 24), b.w, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float sum32(const float4 (&x)[8]) {
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    s0 += (x[i].x + x[i].y) + (x[i].z + x[i].w);
+    s1 += (x[i + 1].x + x[i + 1].y) + (x[i + 1].z + x[i + 1].w);
+  }
+  return s0 + s1;
+}
+
+// group c of the lane (x4: the whole staged vector) applied to the R rows
+template <int R>
+__device__ __forceinline__ void i4_group(const uint4 (&w)[R], const uint16_t (&sc)[R], int c,
+                                         const float4* __restrict__ x4, float (&acc)[R]) {
+  float4 x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x4[8 * c + i];
+  const float m8 = -8.f * sum32(x);
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = fmaf(bf16_to_f32(sc[r]), nib_dot(w[r], x) + m8, acc[r]);
+}
+
+// rows_dot for int4 rows: codes Q and scales S of a matrix of row length ldw,
+// columns [k0, k0 + K) (k0 and K multiples of 32), against xs[0, K)
+template <int R, int U>
+__device__ __forceinline__ void rows_dot_i4(const uint8_t* __restrict__ Q,
+                                            const uint16_t* __restrict__ S, size_t ldw, int row0,
+                                            int N, int k0, int K, const float* __restrict__ xs,
+                                            float (&acc)[R]) {
+  const uint4* wp[R];
+  const uint16_t* sp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t row = (size_t)min(row0 + r, N - 1);
+    wp[r] = reinterpret_cast<const uint4*>(Q + row * (ldw / 2) + k0 / 2);
+    sp[r] = S + row * (ldw / 32) + k0 / 32;
+  }
+  const float4* x4 = reinterpret_cast<const float4*>(xs);
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  const int nch = K >> 5;
+  int c = threadIdx.x & 63;
+  for (; c + 64 * (U - 1) < nch; c += 64 * U) {
+    uint4 w[U][R];
+    uint16_t sc[U][R];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        w[u][r] = ld_stream(wp[r] + c + 64 * u);
+        sc[u][r] = sp[r][c + 64 * u];
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) i4_group<R>(w[u], sc[u], c + 64 * u, x4, acc);
+  }
+  for (; c < nch; c += 64) {
+    uint4 w[R];
+    uint16_t sc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      w[r] = ld_stream(wp[r] + c);
+      sc[r] = sp[r][c];
+    }
+    i4_group<R>(w, sc, c, x4, acc);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+}
+
+// the weight stream of a kernel: bf16 rows (I4 false) or int4 rows (W the codes,
+// S the scales)
+template <int R, int U, bool I4>
+__device__ __forceinline__ void rows_dot_w(const uint16_t* __restrict__ W,
+                                           const uint16_t* __restrict__ S, size_t ldw, int row0,
+                                           int N, int k0, int K, const float* __restrict__ xs,
+                                           float (&acc)[R]) {
+  if constexpr (I4)
+    rows_dot_i4<R, U>(reinterpret_cast<const uint8_t*>(W), S, ldw, row0, N, k0, K, xs, acc);
+  else
+    rows_dot<R, U>(W, ldw, row0, N, k0, K, xs, acc);
+}
+
+// One thread per group of 32: scale = bf16(max|w| / 7), codes rint(w / scale)
+// clamped to [-7, 7] (both divisions IEEE fp32), stored as nibbles q + 8.
+__global__ __launch_bounds__(256) void k_quant_i4(const uint16_t* __restrict__ W, int rows, int K,
+                                                  uint8_t* __restrict__ Q, uint16_t* __restrict__ S) {
+  const int gpr = K >> 5;
+  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= (size_t)rows * gpr) return;
+  const size_t row = g / gpr, gi = g - row * gpr;
+  const uint4* src = reinterpret_cast<const uint4*>(W + row * K + gi * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    v[8 * i + 0] = bf16_lo(u.x); v[8 * i + 1] = bf16_hi(u.x);
+    v[8 * i + 2] = bf16_lo(u.y); v[8 * i + 3] = bf16_hi(u.y);
+    v[8 * i + 4] = bf16_lo(u.z); v[8 * i + 5] = bf16_hi(u.z);
+    v[8 * i + 6] = bf16_lo(u.w); v[8 * i + 7] = bf16_hi(u.w);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint16_t sb = f32_to_bf16(__fdiv_rn(amax, 7.0f));
+  const float sc = bf16_to_f32(sb);
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int q = 0;
+    if (sc > 0.f) q = (int)fminf(fmaxf(rintf(__fdiv_rn(v[i], sc)), -7.f), 7.f);
+    words[i >> 3] |= uint32_t(q + 8) << (4 * (i & 7));
+  }
+  *reinterpret_cast<uint4*>(Q + row * (K / 2) + gi * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+  S[row * gpr + gi] = sb;
+}
+
+hipError_t launch_quant_i4(const uint16_t* W, int rows, int K, uint8_t* Q, uint16_t* S, hipStream_t s) {
+  if (rows <= 0 || K <= 0 || (K % 32)) return hipErrorInvalidValue;
+  const size_t groups = (size_t)rows * (K / 32);
+  hipLaunchKernelGGL(k_quant_i4, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, W, rows, K, Q, S);
+  return hipGetLastError();
+}
+
 // sum of `count` per-block partial sums (this thread's share)
 __device__ __forceinline__ float sum_partials(const float* __restrict__ p, int count) {
   float s = 0.f;
@@ -180,8 +330,9 @@ __device__ __forceinline__ void stage_plain(float* xs, const float* __restrict__
 
 
 // ---------------------------------------------------------------------------
-template <int WAVES, int R, int U>
-__global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restrict__ W, int n,
+template <int WAVES, int R, int U, bool I4>
+__global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ S, int n,
                                                        const float* __restrict__ a0,
                                                        const float* __restrict__ a1,
                                                        const float* __restrict__ a2, VecOut out) {
@@ -194,7 +345,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restric
   const int wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
   float acc[R];
-  if (row0 < n) rows_dot<R, U>(W, size_t(3) * n, row0, n, 0, 3 * n, xs, acc);
+  if (row0 < n) rows_dot_w<R, U, I4>(W, S, size_t(3) * n, row0, n, 0, 3 * n, xs, acc);
   else
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
@@ -204,7 +355,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restric
 // ---------------------------------------------------------------------------
 constexpr int kQkvERegs = 8;  // float4 chunks of the embedding row held per thread
 
-template <int WAVES, int R, int U>
+template <int WAVES, int R, int U, bool I4>
 __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
   extern __shared__ float xs[];  // [0, n): embedding half; [n, 2n): hidden half
@@ -222,7 +373,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   // the prologue below (staging, the previous step's argmax, the embedding row)
   // overlaps the weight stream
   uint4 wpf[U][R];
-  const bool issued = row0 < N && (n >> 3) >= 64 * U;
+  const bool issued = !I4 && row0 < N && (n >> 3) >= 64 * U;
   if (issued) rows_issue<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, wpf);
   // hidden half: already weighted by hidden_norm; its sum of squares from partials
   stage_plain(xs + n, a.gw, n);
@@ -262,7 +413,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   }
   float acc_g[R], acc_e[R];
   if (issued) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, wpf, acc_g);
-  else if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
+  else if (row0 < N) rows_dot_w<R, U, I4>(a.w_qkv, a.s_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
   float se = 0.f;
   float4* x4 = reinterpret_cast<float4*>(xs);
   if (in_regs) {
@@ -280,7 +431,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
     se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
   }
   __syncthreads();
-  if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, 0, n, xs, acc_e);
+  if (row0 < N) rows_dot_w<R, U, I4>(a.w_qkv, a.s_qkv, size_t(2) * n, row0, N, 0, n, xs, acc_e);
   block_sum2(se, sg, red);  // every wave takes part
   if (row0 >= N) return;
   const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
@@ -322,8 +473,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int WAVES, int R, int U>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __restrict__ W, int N,
+template <int WAVES, int R, int U, bool I4>
+__global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __restrict__ W,
+                                                           const uint16_t* __restrict__ S, int N,
                                                            int K, const float* __restrict__ x,
                                                            const float* __restrict__ resid,
                                                            VecOut out) {
@@ -335,7 +487,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __res
   const int row0 = (blockIdx.x * WAVES + wv) * R;
   float acc[R];
   if (row0 < N) {
-    rows_dot<R, U>(W, size_t(K), row0, N, 0, K, xs, acc);
+    rows_dot_w<R, U, I4>(W, S, size_t(K), row0, N, 0, K, xs, acc);
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] += resid[min(row0 + r, N - 1)];
   } else {
@@ -346,8 +498,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-template <int WAVES, int R, int U>
-__global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restrict__ W, int n_ff,
+template <int WAVES, int R, int U, bool I4>
+__global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ S, int n_ff,
                                                        int n, const float* __restrict__ xw,
                                                        const float* __restrict__ x_ssq,
                                                        int ssq_count, float eps,
@@ -362,7 +515,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restric
   float ss = sum_partials(x_ssq, ssq_count), dummy = 0.f;
   __syncthreads();
   float acc[R];
-  if (row0 < N) rows_dot<R, U>(W, size_t(n), row0, N, 0, n, xs, acc);
+  if (row0 < N) rows_dot_w<R, U, I4>(W, S, size_t(n), row0, N, 0, n, xs, acc);
   block_sum2(ss, dummy, red);
   if (row0 >= N) return;
   const float inv = 1.0f / sqrtf(ss / float(n) + eps);
@@ -377,7 +530,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-template <int WAVES, int R, int U>
+template <int WAVES, int R, int U, bool I4>
 __global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
   extern __shared__ float xs[];
   __shared__ float red[32];
@@ -391,7 +544,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
   float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
   __syncthreads();
   float acc[R];
-  if (row0 < a.dv) rows_dot<R, U>(a.w_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
+  if (row0 < a.dv) rows_dot_w<R, U, I4>(a.w_lm, a.s_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
   block_sum2(ss, dummy, red);
   const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
   float bv = -INFINITY;
@@ -451,8 +604,9 @@ struct MultiShape {
   static constexpr int ROWS = WAVES * R;
 };
 
-template <int M>
-__global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__ W, int N, int K,
+template <int M, bool I4>
+__global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__ W,
+                                                    const uint16_t* __restrict__ S, int N, int K,
                                                     int kc, const float* __restrict__ x0,
                                                     const float* __restrict__ x1,
                                                     const float* __restrict__ x2, int seg,
@@ -467,11 +621,20 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
   const int k4 = klen >> 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  const int nch = klen >> 3;
+  const int nch = I4 ? (klen >> 5) : (klen >> 3);  // 16-byte chunks of the K range
   const uint4* wp[R];
+  const uint16_t* sp[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    wp[r] = reinterpret_cast<const uint4*>(W + (size_t)min(row0 + r, N - 1) * K + k0);
+  for (int r = 0; r < R; ++r) {
+    const size_t row = (size_t)min(row0 + r, N - 1);
+    if constexpr (I4) {
+      wp[r] = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(W) + row * (K / 2) + k0 / 2);
+      sp[r] = S + row * (K / 32) + k0 / 32;
+    } else {
+      wp[r] = reinterpret_cast<const uint4*>(W + row * K + k0);
+      sp[r] = nullptr;
+    }
+  }
   // stage the M vectors: one flat loop over all M * k4 float4 of the chunk, so every
   // thread's loads are in flight together (vectors past `rows` are zero)
   {
@@ -515,11 +678,61 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
       for (int r = 0; r < R; ++r) acc[r][m] = dot8(w[r], a, b, acc[r][m]);
     }
   };
-  for (int c = lane; c < nch; c += 64) {
-    uint4 w[R];
+  if constexpr (I4) {
+    // group c: each row's 32 codes are converted and scaled once and applied to
+    // the M vectors; the -8 * scale * sum(x) term per group at the end
+    for (int c = lane; c < nch; c += 64) {
+      uint4 w[R];
+      float sr[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) w[r] = ld_stream(wp[r] + c);
-    apply(c, w);
+      for (int r = 0; r < R; ++r) {
+        w[r] = ld_stream(wp[r] + c);
+        sr[r] = bf16_to_f32(sp[r][c]);
+      }
+      float xsum[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) xsum[m] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 xa[M], xb[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const float4* x4 = reinterpret_cast<const float4*>(xs + m * kc);
+          xa[m] = x4[8 * c + 2 * i];
+          xb[m] = x4[8 * c + 2 * i + 1];
+          xsum[m] += ((xa[m].x + xa[m].y) + (xa[m].z + xa[m].w)) + ((xb[m].x + xb[m].y) + (xb[m].z + xb[m].w));
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t wd = i == 0 ? w[r].x : (i == 1 ? w[r].y : (i == 2 ? w[r].z : w[r].w));
+          const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;
+          const float f0 = float(lo & 0xFFu) * sr[r], f1 = float(hi & 0xFFu) * sr[r];
+          const float f2 = float((lo >> 8) & 0xFFu) * sr[r], f3 = float((hi >> 8) & 0xFFu) * sr[r];
+          const float f4 = float((lo >> 16) & 0xFFu) * sr[r], f5 = float((hi >> 16) & 0xFFu) * sr[r];
+          const float f6 = float(lo >> 24) * sr[r], f7 = float(hi >> 24) * sr[r];
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float t = acc[r][m];
+            t = fmaf(f0, xa[m].x, t); t = fmaf(f1, xa[m].y, t);
+            t = fmaf(f2, xa[m].z, t); t = fmaf(f3, xa[m].w, t);
+            t = fmaf(f4, xb[m].x, t); t = fmaf(f5, xb[m].y, t);
+            t = fmaf(f6, xb[m].z, t); t = fmaf(f7, xb[m].w, t);
+            acc[r][m] = t;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(-8.f * sr[r], xsum[m], acc[r][m]);
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) {
+      uint4 w[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[r] = ld_stream(wp[r] + c);
+      apply(c, w);
+    }
   }
   // the R * M sums: one reduce-scatter over the wave (padded with zeros to a power
   // of two), then one store per lane group
@@ -562,12 +775,18 @@ int gemv_grid(int N, int cfg) {
   }
 }
 
-hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const float* a1,
-                         const float* a2, const VecOut& out, int cfg, hipStream_t s) {
-#define CASE(ID, WV, RR, UU)                                                               \
-  case ID:                                                                                 \
-    hipLaunchKernelGGL((k_encode<WV, RR, UU>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
-                       size_t(3 * n) * sizeof(float), s, w_fc, n, a0, a1, a2, out);        \
+// (S non-null: W holds int4 codes and S their scales)
+hipError_t launch_encode(const uint16_t* w_fc, const uint16_t* S, int n, const float* a0,
+                         const float* a1, const float* a2, const VecOut& out, int cfg,
+                         hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                                    \
+  case ID:                                                                                      \
+    if (S)                                                                                      \
+      hipLaunchKernelGGL((k_encode<WV, RR, UU, true>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
+                         size_t(3 * n) * sizeof(float), s, w_fc, S, n, a0, a1, a2, out);       \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_encode<WV, RR, UU, false>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
+                         size_t(3 * n) * sizeof(float), s, w_fc, S, n, a0, a1, a2, out);       \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -579,35 +798,48 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                               \
   case ID:                                                                                 \
     if (RR % 2) return hipErrorInvalidValue;                                               \
-    hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(N, WV * RR)),    \
-                       dim3(64 * WV), size_t(2 * a.n) * sizeof(float), s, a);              \
+    if (a.s_qkv)                                                                           \
+      hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU, true>), dim3(ceil_div(N, WV * RR)), \
+                         dim3(64 * WV), size_t(2 * a.n) * sizeof(float), s, a);            \
+    else                                                                                   \
+      hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU, false>), dim3(ceil_div(N, WV * RR)), \
+                         dim3(64 * WV), size_t(2 * a.n) * sizeof(float), s, a);            \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_resid(const uint16_t* w, int N, int K, const float* x, const float* resid,
-                             const VecOut& out, int cfg, hipStream_t s) {
-#define CASE(ID, WV, RR, UU)                                                                 \
-  case ID:                                                                                   \
-    hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU>), dim3(ceil_div(N, WV * RR)),              \
-                       dim3(64 * WV), size_t(K) * sizeof(float), s, w, N, K, x, resid, out); \
+hipError_t launch_gemv_resid(const uint16_t* w, const uint16_t* S, int N, int K, const float* x,
+                             const float* resid, const VecOut& out, int cfg, hipStream_t s) {
+#define CASE(ID, WV, RR, UU)                                                                    \
+  case ID:                                                                                      \
+    if (S)                                                                                      \
+      hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, true>), dim3(ceil_div(N, WV * RR)),         \
+                         dim3(64 * WV), size_t(K) * sizeof(float), s, w, S, N, K, x, resid, out); \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, false>), dim3(ceil_div(N, WV * RR)),        \
+                         dim3(64 * WV), size_t(K) * sizeof(float), s, w, S, N, K, x, resid, out); \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
   return hipGetLastError();
 }
 
-hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* xw,
+hipError_t launch_gateup(const uint16_t* w_gu, const uint16_t* S, int n_ff, int n, const float* xw,
                          const float* x_ssq, int ssq_count, float eps, float* act, int cfg,
                          hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                                \
   case ID:                                                                                  \
     if (RR % 2) return hipErrorInvalidValue;                                                \
-    hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(2 * n_ff, WV * RR)), \
-                       dim3(64 * WV), size_t(n) * sizeof(float), s, w_gu, n_ff, n, xw, x_ssq, \
-                       ssq_count, eps, act);                                                \
+    if (S)                                                                                  \
+      hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU, true>),                       \
+                         dim3(ceil_div(2 * n_ff, WV * RR)), dim3(64 * WV), size_t(n) * sizeof(float), \
+                         s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act);              \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU, false>),                      \
+                         dim3(ceil_div(2 * n_ff, WV * RR)), dim3(64 * WV), size_t(n) * sizeof(float), \
+                         s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act);              \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -619,8 +851,12 @@ int lmhead_grid(int dv, int cfg) { return gemv_grid(dv, cfg); }
 hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                                  \
   case ID:                                                                                    \
-    hipLaunchKernelGGL((k_lmhead<WV, RR, UU>), dim3(ceil_div(a.dv, WV * RR)), dim3(64 * WV), \
-                       size_t(a.n) * sizeof(float), s, a);                                    \
+    if (a.s_lm)                                                                               \
+      hipLaunchKernelGGL((k_lmhead<WV, RR, UU, true>), dim3(ceil_div(a.dv, WV * RR)),          \
+                         dim3(64 * WV), size_t(a.n) * sizeof(float), s, a);                   \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_lmhead<WV, RR, UU, false>), dim3(ceil_div(a.dv, WV * RR)),         \
+                         dim3(64 * WV), size_t(a.n) * sizeof(float), s, a);                   \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -674,11 +910,11 @@ int gemv_multi_splits(int rows, int N, int K) {
   return ceil_div(K, multi_kchunk(m, N, K));
 }
 
-hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, const float* x1,
-                             const float* x2, int seg, int rows, float* P, int* splits_out,
-                             hipStream_t s, const TapRowsB& yb) {
+hipError_t launch_gemv_multi(const uint16_t* W, const uint16_t* S, int N, int K, const float* x0,
+                             const float* x1, const float* x2, int seg, int rows, float* P,
+                             int* splits_out, hipStream_t s, const TapRowsB& yb) {
   const int m = gemv_multi_width(rows);
-  if (m < 0 || (K % 8) || (x1 && (seg % 4))) return hipErrorInvalidValue;
+  if (m < 0 || (K % (S ? 32 : 8)) || (x1 && (seg % 4))) return hipErrorInvalidValue;
   if (yb.rows_x < rows && (!x1 || !yb.y[0] || !yb.y[1] || !yb.y[2])) return hipErrorInvalidValue;
   const int kc = multi_kchunk(m, N, K);
   const int splits = ceil_div(K, kc);
@@ -688,8 +924,12 @@ hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, c
   switch (m) {
 #define MCASE(MM)                                                                              \
   case MM:                                                                                     \
-    hipLaunchKernelGGL((k_gemv_multi<MM>), grid, block, lds, s, W, N, K, kc, x0, x1, x2, seg,  \
-                       rows, P, yb);                                                           \
+    if (S)                                                                                     \
+      hipLaunchKernelGGL((k_gemv_multi<MM, true>), grid, block, lds, s, W, S, N, K, kc, x0, x1, x2, \
+                         seg, rows, P, yb);                                                    \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_gemv_multi<MM, false>), grid, block, lds, s, W, S, N, K, kc, x0, x1,  \
+                         x2, seg, rows, P, yb);                                                \
     break;
     MCASE(1) MCASE(2) MCASE(3) MCASE(4) MCASE(5) MCASE(6) MCASE(8) MCASE(9) MCASE(12) MCASE(16)
 #undef MCASE

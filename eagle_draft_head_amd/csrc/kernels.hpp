@@ -22,9 +22,19 @@ struct VecOut {
 };
 int gemv_grid(int N, int cfg);  // blocks (= partial sums) of a launch over N rows
 
+// Weights of the GEMVs: bf16 rows [N][K], or (a non-null scale pointer S) int4 rows:
+// codes [N][K / 2] bytes (element 2i in the low nibble, stored as q + 8, q in
+// [-7, 7]) and one bf16 scale per group of 32 weights, [N][K / 32]; the weight is
+// scale * q.  K must then be a multiple of 32.  launch_quant_i4 makes them from
+// bf16 rows: scale = bf16(max|w| / 7), q = clamp(rint(w / scale), -7, 7), both
+// divisions IEEE fp32.
+hipError_t launch_quant_i4(const uint16_t* W, int rows, int K, uint8_t* Q, uint16_t* S,
+                           hipStream_t s);
+
 // g[r] = fc[r,:] . [aux0; aux1; aux2]
-hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const float* a1,
-                         const float* a2, const VecOut& out, int cfg, hipStream_t s);
+hipError_t launch_encode(const uint16_t* w_fc, const uint16_t* S, int n, const float* a0,
+                         const float* a1, const float* a2, const VecOut& out, int cfg,
+                         hipStream_t s);
 
 // Fused: [finish the previous step's argmax] -> cat = [RMSNorm(E[tok]); RMSNorm(g)] ->
 // (the hidden half arrives pre-weighted as gw = g * hidden_norm with the partial
@@ -34,6 +44,7 @@ hipError_t launch_encode(const uint16_t* w_fc, int n, const float* a0, const flo
 // of the cache (bf16, head-major).
 struct QkvArgs {
   const uint16_t* w_qkv;
+  const uint16_t* s_qkv;   // int4 scales (w_qkv then holds codes), or NULL
   int n, n_head, n_head_kv, head_dim, rope_dim;
   const double* inv_freq;  // [rope_dim / 2]: theta^(-2i / rope_dim)
   float eps;
@@ -65,12 +76,12 @@ struct QkvArgs {
 hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s);
 
 // y[r] = W[r,:] . x + resid[r]   (o_proj, down_proj)
-hipError_t launch_gemv_resid(const uint16_t* w, int N, int K, const float* x,
+hipError_t launch_gemv_resid(const uint16_t* w, const uint16_t* S, int N, int K, const float* x,
                              const float* resid, const VecOut& out, int cfg, hipStream_t s);
 
 // act[i] = silu(gate_i . z) * (up_i . z), z = xw / rms with xw = x1 * w_post and the
 // rms from per-block partial sums of x1^2; W_gu rows interleaved
-hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* xw,
+hipError_t launch_gateup(const uint16_t* w_gu, const uint16_t* S, int n_ff, int n, const float* xw,
                          const float* x_ssq, int ssq_count, float eps, float* act, int cfg,
                          hipStream_t s);
 
@@ -80,6 +91,7 @@ hipError_t launch_gateup(const uint16_t* w_gu, int n_ff, int n, const float* xw,
 // may be NULL.
 struct LmHeadArgs {
   const uint16_t* w_lm;
+  const uint16_t* s_lm;    // int4 scales (w_lm then holds codes), or NULL
   int dv, n;
   const float* hw;
   const float* h_ssq;
@@ -114,9 +126,9 @@ inline TapRowsB no_tap_rows_b() { return TapRowsB{{nullptr, nullptr, nullptr}, 1
 // rows <= 16; *splits_out receives the chunk count.
 int gemv_multi_width(int rows);
 int gemv_multi_splits(int rows, int N, int K);  // chunk count the launch will use
-hipError_t launch_gemv_multi(const uint16_t* W, int N, int K, const float* x0, const float* x1,
-                             const float* x2, int seg, int rows, float* P, int* splits_out,
-                             hipStream_t s, const TapRowsB& yb = no_tap_rows_b());
+hipError_t launch_gemv_multi(const uint16_t* W, const uint16_t* S, int N, int K, const float* x0,
+                             const float* x1, const float* x2, int seg, int rows, float* P,
+                             int* splits_out, hipStream_t s, const TapRowsB& yb = no_tap_rows_b());
 
 // ---- batched drafting: up to kBatchRows sequences per pass ----
 constexpr int kBatchRows = 32;

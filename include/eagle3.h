@@ -77,6 +77,7 @@ typedef struct {
   int32_t max_gamma;     /* largest chain length accepted */
   int32_t max_seqs;      /* sequence slots */
   int32_t kv_dtype;      /* EAGLE3_KV_F32 (default) or EAGLE3_KV_BF16, see below */
+  int32_t weight_format; /* EAGLE3_WEIGHTS_BF16 (default) or EAGLE3_WEIGHTS_I4, see below */
 } eagle3_config;
 
 /* Draft-KV precision.  EAGLE3_KV_F32 stores K/V rows in fp32 and feeds the
@@ -86,6 +87,17 @@ typedef struct {
    that alone moves draft logits by about 1-2e-2 relative to exact arithmetic. */
 #define EAGLE3_KV_F32 0
 #define EAGLE3_KV_BF16 1
+
+/* Projection-weight format (ExecuTorch PR #20154 names a weight-stationary INT4
+   GEMM for small M; the format is our reading).  EAGLE3_WEIGHTS_I4: eagle3_load
+   quantizes fc, q/k/v, o, gate/up, down and lm_head to symmetric int4 in groups of
+   32 along the input dimension with one bf16 scale per group (scale =
+   bf16(max|w| / 7), q = clamp(rint(w / scale), -7, 7), IEEE fp32 divisions) and
+   every draft step and append streams those (about 4.5 bits a weight).  Requires
+   max_seqs == 1 and input widths (n_embd, n_head * head_dim, n_ff) that are
+   multiples of 32; appends run in passes of at most 16 rows. */
+#define EAGLE3_WEIGHTS_BF16 0
+#define EAGLE3_WEIGHTS_I4 1
 
 /* Weights: device pointers, bf16, PyTorch [out, in] row-major (in contiguous).
    They are copied (and repacked) at load; the caller may free them afterwards.
@@ -207,6 +219,24 @@ int eagle3_kv_len(const eagle3_ctx *ctx, int32_t seq, int32_t *committed, int32_
    bf16 per kv_dtype; K rows roped).  Inspection and tests; rows need not be live. */
 int eagle3_kv_read(const eagle3_ctx *ctx, int32_t seq, int32_t row0, int32_t nrows,
                    void *k_dev, void *v_dev, void *stream);
+
+/* Copy one int4 projection matrix (weight_format EAGLE3_WEIGHTS_I4) into caller
+   buffers: codes_dev [rows][K / 2] bytes and scales_dev [rows][K / 32] bf16, in the
+   layout of EAGLE3_WEIGHTS_I4.  Row order as stored: fc, o_proj, down_proj and
+   lm_head as given; QKV is q rows then k rows then v rows, with the q and k rows of
+   each head ordered so that rotary partners are adjacent; gate/up interleaves
+   gate row i (row 2i) and up row i (row 2i + 1).  Inspection and tests;
+   EAGLE3_E_STATE when the weights are bf16. */
+enum {
+  EAGLE3_I4_FC = 0,
+  EAGLE3_I4_QKV = 1,
+  EAGLE3_I4_O = 2,
+  EAGLE3_I4_GATE_UP = 3,
+  EAGLE3_I4_DOWN = 4,
+  EAGLE3_I4_LM_HEAD = 5
+};
+int eagle3_weights_i4_read(const eagle3_ctx *ctx, int32_t matrix, void *codes_dev,
+                           void *scales_dev, void *stream);
 
 /* Message of the last failing call on this handle (or of the last failing
    eagle3_load when ctx is NULL). */

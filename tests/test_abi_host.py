@@ -191,7 +191,10 @@ def test_load_rejects_d2t_problems(d2t_tiny):
                                          (dict(n_head_kv=3), B.E_SHAPE),
                                          (dict(n_aux=2), B.E_UNSUPPORTED),
                                          (dict(n_embd=200), B.E_UNSUPPORTED),
-                                         (dict(max_ctx=0), B.E_INVAL)])
+                                         (dict(max_ctx=0), B.E_INVAL),
+                                         (dict(weight_format=7), B.E_INVAL),
+                                         (dict(weight_format=B.WEIGHTS_I4, max_seqs=2), B.E_UNSUPPORTED),
+                                         (dict(weight_format=B.WEIGHTS_I4, n_ff=776), B.E_UNSUPPORTED)])
 def test_load_rejects_unsupported_geometry(d2t_tiny, change, code):
     cfg = B.make_config(TINY, 100)
     for k, v in change.items():
