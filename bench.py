@@ -66,22 +66,27 @@ def committed_traffic(kernel: str):
     return float(vals["bytes_per_launch"])
 
 
+# HBM bytes per projection weight: bf16, or int4 codes plus one bf16 scale per 32
+WB_BF16, WB_I4 = 2.0, 0.5 + 2.0 / 32
+WB = WB_BF16
+
+
 def kernel_bytes(cfg, kernel: str, L: int, kv_bytes: int = 4) -> float:
     """Algorithmic HBM bytes of one launch of a kernel family (K/V elements of
     kv_bytes bytes)."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     if kernel == "lm_head":
-        return 2.0 * dv * n + 4 * n + 4 * n
+        return WB * dv * n + 4 * n + 4 * n
     if kernel == "gate_up":
-        return 2.0 * 2 * ff * n + 4 * n + 4 * n + 4 * ff
+        return WB * 2 * ff * n + 4 * n + 4 * n + 4 * ff
     if kernel == "qkv":
-        return 2.0 * (qd + 2 * kvd) * 2 * n + 2 * n + 4 * n + 8 * n + 4 * qd + 2 * 2 * kvd
+        return WB * (qd + 2 * kvd) * 2 * n + 2 * n + 4 * n + 8 * n + 4 * qd + 2 * 2 * kvd
     if kernel == "down":
-        return 2.0 * n * ff + 4 * ff + 4 * n + 4 * n
+        return WB * n * ff + 4 * ff + 4 * n + 4 * n
     if kernel == "o_proj":
-        return 2.0 * n * qd + 4 * qd + 4 * n + 4 * n
+        return WB * n * qd + 4 * qd + 4 * n + 4 * n
     if kernel == "encode":
-        return 2.0 * 3 * n * n + 12 * n + 4 * n
+        return WB * 3 * n * n + 12 * n + 4 * n
     if kernel == "attention":
         return 2.0 * kv_bytes * kvd * (L + 1) + 8 * qd
     raise KeyError(kernel)
@@ -94,7 +99,7 @@ def kernel_bytes_step(cfg, L: int, gamma: int, kv_bytes: int = 4) -> float:
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
     rows = L + 1 + (gamma - 1) / 2 + 1
-    return 2.0 * p_step + 8 * n + 2 * n + rows * 2 * kv_bytes * kvd
+    return WB * p_step + 8 * n + 2 * n + rows * 2 * kv_bytes * kvd
 
 
 def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
@@ -105,13 +110,13 @@ def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
     rebuild's one pass over W_fc."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
-    tot = 12.0 * n + 8 * n + 4 if stored else 6.0 * n * n + 12 * n   # encode: W_fc + aux
+    tot = 12.0 * n + 8 * n + 4 if stored else WB * 3 * n * n + 12 * n   # encode: W_fc + aux
     for j in range(gamma):
         rows = L + j                                      # rows attended before the new one
-        tot += 2.0 * p_step + 8 * n + 2 * n + (rows + 1) * 2 * kv_bytes * kvd
+        tot += WB * p_step + 8 * n + 2 * n + (rows + 1) * 2 * kv_bytes * kvd
     if rebuild:
         T = accepted + 1                                  # rebuild rows
-        tot += 6.0 * n * n + 2.0 * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 2 * kv_bytes * kvd)
+        tot += WB * 3 * n * n + WB * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 2 * kv_bytes * kvd)
     return tot
 
 
@@ -129,6 +134,8 @@ def main():
                     help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
+    ap.add_argument("--weights", choices=["bf16", "int4"], default="bf16",
+                    help="int4: projection weights quantized at load (groups of 32, bf16 scales)")
     ap.add_argument("--drafter", choices=["persistent", "round-local"], default="persistent",
                     help="round-local: the scratch-KV drafter (each round attends over its own rows "
                          "only; a step is one chain round from encoded taps, no rebuild)")
@@ -182,7 +189,11 @@ def main():
         L_at = [L] * nsteps
     max_ctx = max(L, max(L_at)) + gamma + 64
     kv_dtype = B.KV_BF16 if args.kv == "bf16" else B.KV_F32
-    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype)
+    i4 = args.weights == "int4"
+    global WB
+    WB = WB_I4 if i4 else WB_BF16
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype,
+                 weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16)
     stream = torch.cuda.current_stream()
 
     # committed context
@@ -309,7 +320,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, args.cpu_rounds)
+        cpu = cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, args.cpu_rounds, int4_weights=i4)
 
     line = {
         "metric": "draft tokens/sec (gamma=3 chain, batch 1) and achieved HBM GB/s per draft step",
@@ -322,7 +333,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"bf16 weights, fp32 accumulate, {args.kv} draft KV",
+        "dtype": (f"int4 weights (groups of 32, bf16 scales)" if i4 else "bf16 weights")
+                 + f", fp32 accumulate, {args.kv} draft KV",
         "data": "synthetic (seeded; random-init weights of the drafter architecture)",
         "config": {"workload": f"{cfg.name} drafter: n_embd {cfg.n_embd}, {cfg.n_head}/{cfg.n_head_kv} "
                                f"heads x {cfg.head_dim}, n_ff {cfg.n_ff}, draft vocab {cfg.draft_vocab}, "
@@ -340,7 +352,8 @@ def main():
                    "+ rewind"},
         "roofline": {"bound": "hbm", "kernel": args.kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": committed_traffic(args.kernel), "avg_launch_us": round(k_avg_s * 1e6, 3),
+                     "traffic": None if i4 else committed_traffic(args.kernel),
+                     "avg_launch_us": round(k_avg_s * 1e6, 3),
                      "launches": k_launches, "bytes_per_launch": k_bytes},
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
@@ -378,6 +391,9 @@ def run_batched(args, cfg):
     """Batched drafting: one draft_chain over all sequences per step, then a packed
     rebuild of a_b + 1 rows per sequence (a_b seeded on [0, gamma]) and a rewind of
     every sequence to its seeded length."""
+    if args.weights != "bf16":
+        print(json.dumps({"error": "int4 weights are a batch-1 mode (the batched GEMMs stream bf16)"}))
+        sys.exit(2)
     import numpy as np
     import torch
 
@@ -514,7 +530,7 @@ def cpu_baseline_batched(cfg, wd, lens, b_aux, b_tok, gamma):
                       f"{pick} (committed rows {[lens[s] for s in pick]}), sequentially; prefill untimed"}
 
 
-def cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, rounds):
+def cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, rounds, int4_weights=False):
     """The oracle as it stands (fp64 numpy) on the host: prefill of the committed
     rows (untimed setup), then `rounds` chain rounds of gamma steps, timed."""
     import numpy as np
@@ -527,6 +543,9 @@ def cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, rounds):
     except Exception:
         threads = os.cpu_count() or 1
     wh = {k: v.cpu() for k, v in wd.items() if k != "embed"}
+    if int4_weights:  # the same int4 weights the GPU streams (untimed setup)
+        from oracle import int4
+        wh = int4.int4_weights(wh)
     L = int(tok_c.numel())
     orc = make_oracle(cfg, wh, max_ctx=L + 64, lazy_embed=True)
     t0 = time.perf_counter()
@@ -541,7 +560,8 @@ def cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, rounds):
     med = sorted(times)[len(times) // 2]
     return {"value": round(gamma / med, 4), "unit": "draft tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle: {rounds} chain rounds of gamma={gamma} over {L} committed "
+            "sample": f"fp64 numpy oracle{' (int4 weights)' if int4_weights else ''}: {rounds} chain "
+                      f"rounds of gamma={gamma} over {L} committed "
                       f"rows (median round {med:.2f}s; untimed setup prefill {setup_s:.1f}s)"}
 
 
