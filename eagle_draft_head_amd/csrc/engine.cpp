@@ -36,6 +36,7 @@ constexpr int kProfKernels = 9;
 // gfx950 gives a workgroup up to 160 KB of LDS; the GEMVs keep one fp32
 // activation vector there (the down projection of a 5120-wide drafter: 68 KB)
 constexpr int64_t kMaxStageBytes = 128 * 1024;
+constexpr int64_t kMaxLdsBytes = 160 * 1024;  // a workgroup's LDS on gfx950
 
 struct Profiler {
   int kernel = -1;
@@ -252,6 +253,11 @@ int validate_config(const eagle3_config* cfg, const char** why) {
     if (cfg->max_seqs != 1) return bad("int4 weights: batch-1 drafting only (max_seqs 1)", EAGLE3_E_UNSUPPORTED);
     if (cfg->n_embd % 32 || (int64_t(cfg->n_head) * cfg->head_dim) % 32 || cfg->n_ff % 32)
       return bad("int4 weights need input widths that are multiples of 32", EAGLE3_E_UNSUPPORTED);
+    // the int4 GEMVs stage fp32 x and its fixed-point planes: 6.125 bytes per input
+    const int64_t n = cfg->n_embd, kmax = std::max<int64_t>(
+        {3 * n, int64_t(cfg->n_head) * cfg->head_dim, int64_t(cfg->n_ff)});
+    if (kmax * 49 / 8 > kMaxLdsBytes || n * 98 / 8 > kMaxLdsBytes)
+      return bad("int4 weights: an activation vector exceeds the LDS staging limit", EAGLE3_E_UNSUPPORTED);
   }
   {  // the GEMV kernels stage a whole fp32 activation vector in LDS
     const int64_t n = cfg->n_embd, kmax = std::max<int64_t>(
@@ -392,12 +398,13 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   const size_t smax = size_t(e3::attn_max_splits(c->cap, c->hd, c->nkv));
   E3_TRY(dalloc(c, &c->part_o, size_t(nh) * smax * hd));
   E3_TRY(dalloc(c, &c->part_ml, size_t(nh) * smax * 2));
-  c->gcfg[e3::kGemvEncode] = e3::gemv_pick(e3::kGemvEncode, int(n), int(3 * n));
-  c->gcfg[e3::kGemvQkv] = e3::gemv_pick(e3::kGemvQkv, int(qd + 2 * kvd), int(2 * n));
-  c->gcfg[e3::kGemvO] = e3::gemv_pick(e3::kGemvO, int(n), int(qd));
-  c->gcfg[e3::kGemvGateUp] = e3::gemv_pick(e3::kGemvGateUp, int(2 * ff), int(n));
-  c->gcfg[e3::kGemvDown] = e3::gemv_pick(e3::kGemvDown, int(n), int(ff));
-  c->gcfg[e3::kGemvLmHead] = e3::gemv_pick(e3::kGemvLmHead, int(dv), int(n));
+  const bool wi4 = cfg->weight_format == EAGLE3_WEIGHTS_I4;
+  c->gcfg[e3::kGemvEncode] = e3::gemv_pick(e3::kGemvEncode, int(n), int(3 * n), wi4);
+  c->gcfg[e3::kGemvQkv] = e3::gemv_pick(e3::kGemvQkv, int(qd + 2 * kvd), int(n), wi4);
+  c->gcfg[e3::kGemvO] = e3::gemv_pick(e3::kGemvO, int(n), int(qd), wi4);
+  c->gcfg[e3::kGemvGateUp] = e3::gemv_pick(e3::kGemvGateUp, int(2 * ff), int(n), wi4);
+  c->gcfg[e3::kGemvDown] = e3::gemv_pick(e3::kGemvDown, int(n), int(ff), wi4);
+  c->gcfg[e3::kGemvLmHead] = e3::gemv_pick(e3::kGemvLmHead, int(dv), int(n), wi4);
   E3_TRY(gemv_config_override(c));
   c->lm_grid = e3::lmhead_grid(int(dv), c->gcfg[e3::kGemvLmHead]);
   for (int i = 0; i < 3; ++i) {

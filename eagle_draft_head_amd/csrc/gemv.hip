@@ -24,6 +24,8 @@
 // are issued before their FMAs so each lane keeps U*R loads in flight.  The
 // per-row sums are reduced across the wave at the end.  No block ever waits
 // for another block: cross-block reductions happen in the next kernel.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "gemv_cfg.hpp"
 #include "kernels.hpp"
@@ -118,110 +120,202 @@ __device__ __forceinline__ void rows_dot_issued(const uint16_t* __restrict__ W, 
 // ---------------------------------------------------------------------------
 // int4 weights (kernels.hpp, I4 weights): a row of K weights is K / 2 bytes of
 // codes (element 2i in the low nibble, stored as q + 8) and K / 32 bf16 scales, one
-// per group of 32.  A lane's 16-byte chunk is one whole group, so its dot product
-// is scale * (sum of nibble * x - 8 * sum of x), the x sum shared by the rows.
+// per group of 32.  A lane's 16-byte chunk is one whole group.
+//
+// The activation vector is turned once per block into fixed point per group of 32:
+// a power-of-two exponent e from the group's largest magnitude m (2^(E-1) <= m < 2^E,
+// e = 14 - E) and x_q = rint(x * 2^e), so |x_q| <= 2^14 and x_q is off from x * 2^e
+// by at most 1/2, i.e. x by at most m * 2^-14.  x_q + 0x8888 has four base-16
+// digits u_t, and x_q = sum_t 16^t (u_t - 8); the digits (u_t - 8) are stored as
+// signed nibbles, one plane per t, in the element order of the codes.  A code XOR 8
+// is q as a signed nibble, so sixteen v_dot8_i32_i4 give the four per-digit sums of
+// a group exactly, and sum_t 16^t s_t = sum q x_q (|.| < 2^22, exact in fp32) is
+// scaled by scale * 2^-e once per group and row.
 
-// sum over the 32 elements of a group of nibble * x (x: the group's 8 float4)
-__device__ __forceinline__ float nib_dot(const uint4 w, const float4 (&x)[8]) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    // byte j of the word holds elements 8i + 2j (low nibble) and 8i + 2j + 1
-    const uint32_t lo = ws[i] & 0x0F0F0F0Fu, hi = (ws[i] >> 4) & 0x0F0F0F0Fu;
-    const float4 a = x[2 * i], b = x[2 * i + 1];
-    acc = fmaf(float(lo & 0xFFu), a.x, acc);
-    acc = fmaf(float(hi & 0xFFu), a.y, acc);
-    acc = fmaf(float((lo >> 8) & 0xFFu), a.z, acc);
-    acc = fmaf(float((hi >> 8) & 0xFFu), a.w, acc);
-    acc = fmaf(float((lo >> 16) & 0xFFu), b.x, acc);
-    acc = fmaf(float((hi >> 16) & 0xFFu), b.y, acc);
-    acc = fmaf(float(lo >> 24), b.z, acc);
-    acc = fmaf(float(hi >> 24), b.w, acc);
-  }
-  return acc;
+// LDS layout of a vector of G groups: planes [4][G] uint4 (entry i * G + g holds
+// digit planes 0..3 of elements 8i..8i+7 of group g) and exponents [G] int.
+constexpr size_t q_vec_bytes(int K) { return size_t(K / 8) * 16 + size_t(K / 32) * 4; }
+
+// swap nibbles 1 <-> 2 and 5 <-> 6 of a word
+__device__ __forceinline__ uint32_t swap_mid_nibbles(uint32_t x) {
+  const uint32_t t = ((x >> 4) ^ x) & 0x00F000F0u;
+  return x ^ t ^ (t << 4);
 }
 
-__device__ __forceinline__ float sum32(const float4 (&x)[8]) {
-  float s0 = 0.f, s1 = 0.f;
+// xs[0, K) (fp32, LDS) -> digit planes xp and exponents xe (LDS).  Every thread of
+// the block calls it; K % 32 == 0 and blockDim.x % 64 == 0.  One thread per 8
+// elements; the four threads of a group are the four lanes of a DPP quad.
+__device__ __forceinline__ void quant_x_i4(const float* __restrict__ xs, int K,
+                                           uint4* __restrict__ xp, int* __restrict__ xe) {
+  const int G = K >> 5, nchunk = K >> 3;
+  const float4* x4 = reinterpret_cast<const float4*>(xs);
+  for (int j0 = 0; j0 < nchunk; j0 += blockDim.x) {  // same trip count for every lane
+    const int j = j0 + int(threadIdx.x);
+    const bool on = j < nchunk;  // whole quads are on or off (nchunk % 4 == 0)
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (on) {
+      a = x4[2 * j];
+      b = x4[2 * j + 1];
+    }
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    s0 += (x[i].x + x[i].y) + (x[i].z + x[i].w);
-    s1 += (x[i + 1].x + x[i + 1].y) + (x[i + 1].z + x[i + 1].w);
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+    m = fmaxf(m, dpp_move<kDppQuadSwap1>(m));
+    m = fmaxf(m, dpp_move<kDppQuadSwap2>(m));
+    const int e = 14 - (int((__float_as_uint(m) >> 23) & 0xFFu) - 126);
+    uint32_t u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float t = __builtin_amdgcn_fmed3f(rintf(ldexpf(v[k], e)), -16384.f, 16384.f);
+      u[k] = uint32_t(int(t) + 0x8888);  // 16 bits
+    }
+    // d_i: byte t = digit t of element 2i (low nibble) and of element 2i + 1 (high)
+    uint32_t d[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d[i] = swap_mid_nibbles(__builtin_amdgcn_perm(u[2 * i + 1], u[2 * i], 0x05010400u));
+    // byte transpose: plane t = byte t of d_0..d_3
+    const uint32_t t01l = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);
+    const uint32_t t01h = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);
+    const uint32_t t23l = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+    const uint32_t t23h = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+    const uint4 pl = make_uint4(__builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x88888888u,
+                                __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x88888888u,
+                                __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x88888888u,
+                                __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x88888888u);
+    if (on) {
+      xp[(j & 3) * G + (j >> 2)] = pl;
+      if ((j & 3) == 0) xe[j >> 2] = e;
+    }
   }
-  return s0 + s1;
 }
 
-// group c of the lane (x4: the whole staged vector) applied to the R rows
+// group g of the lane (of G in the vector) applied to the R rows
 template <int R>
-__device__ __forceinline__ void i4_group(const uint4 (&w)[R], const uint16_t (&sc)[R], int c,
-                                         const float4* __restrict__ x4, float (&acc)[R]) {
-  float4 x[8];
+__device__ __forceinline__ void q_group(const uint4 (&w)[R], const uint16_t (&sc)[R], int g, int G,
+                                        const uint4* __restrict__ xp, const int* __restrict__ xe,
+                                        float (&acc)[R]) {
+  const uint4 p0 = xp[g], p1 = xp[G + g], p2 = xp[2 * G + g], p3 = xp[3 * G + g];
+  const int e = xe[g];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = x4[8 * c + i];
-  const float m8 = -8.f * sum32(x);
+  for (int r = 0; r < R; ++r) {
+    const int w0 = int(w[r].x ^ 0x88888888u), w1 = int(w[r].y ^ 0x88888888u);
+    const int w2 = int(w[r].z ^ 0x88888888u), w3 = int(w[r].w ^ 0x88888888u);
+    const uint32_t pp[4][4] = {{p0.x, p1.x, p2.x, p3.x}, {p0.y, p1.y, p2.y, p3.y},
+                               {p0.z, p1.z, p2.z, p3.z}, {p0.w, p1.w, p2.w, p3.w}};
+    // Horner over the digit planes, most significant first: one chain of 16 dots
+    int gs = 0;
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = fmaf(bf16_to_f32(sc[r]), nib_dot(w[r], x) + m8, acc[r]);
+    for (int t = 3; t >= 0; --t) {
+      if (t < 3) gs <<= 4;
+      gs = __builtin_amdgcn_sdot8(w0, int(pp[t][0]), gs, false);
+      gs = __builtin_amdgcn_sdot8(w1, int(pp[t][1]), gs, false);
+      gs = __builtin_amdgcn_sdot8(w2, int(pp[t][2]), gs, false);
+      gs = __builtin_amdgcn_sdot8(w3, int(pp[t][3]), gs, false);
+    }
+    acc[r] = fmaf(ldexpf(float(gs), -e), bf16_to_f32(sc[r]), acc[r]);
+  }
 }
 
-// rows_dot for int4 rows: codes Q and scales S of a matrix of row length ldw,
-// columns [k0, k0 + K) (k0 and K multiples of 32), against xs[0, K)
+// The first U chunk steps (codes and scales) of the R int4 rows a wave owns, from
+// codes Q and scales S of a matrix of row length ldw, columns [k0, k0 + K) (k0 and
+// K multiples of 32): issued before the prologue that stages the vector, so that
+// the weight stream overlaps it.
 template <int R, int U>
-__device__ __forceinline__ void rows_dot_i4(const uint8_t* __restrict__ Q,
-                                            const uint16_t* __restrict__ S, size_t ldw, int row0,
-                                            int N, int k0, int K, const float* __restrict__ xs,
-                                            float (&acc)[R]) {
-  const uint4* wp[R];
-  const uint16_t* sp[R];
+struct QLoad {
+  uint4 w[U][R];
+  uint16_t sc[U][R];
+};
+
+template <int R>
+__device__ __forceinline__ void q_row_ptrs(const uint8_t* __restrict__ Q, const uint16_t* __restrict__ S,
+                                           size_t ldw, int row0, int N, int k0,
+                                           const uint4* (&wp)[R], const uint16_t* (&sp)[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const size_t row = (size_t)min(row0 + r, N - 1);
     wp[r] = reinterpret_cast<const uint4*>(Q + row * (ldw / 2) + k0 / 2);
     sp[r] = S + row * (ldw / 32) + k0 / 32;
   }
-  const float4* x4 = reinterpret_cast<const float4*>(xs);
+}
+
+template <int R, int U>
+__device__ __forceinline__ void q_issue(const uint8_t* __restrict__ Q, const uint16_t* __restrict__ S,
+                                        size_t ldw, int row0, int N, int k0, int K, QLoad<R, U>& L) {
+  const uint4* wp[R];
+  const uint16_t* sp[R];
+  q_row_ptrs<R>(Q, S, ldw, row0, N, k0, wp, sp);
+  const int G = K >> 5, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  const int nch = K >> 5;
-  int c = threadIdx.x & 63;
-  for (; c + 64 * (U - 1) < nch; c += 64 * U) {
-    uint4 w[U][R];
-    uint16_t sc[U][R];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    const int c = lane + 64 * u;
+    if (c < G) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        w[u][r] = ld_stream(wp[r] + c + 64 * u);
-        sc[u][r] = sp[r][c + 64 * u];
+        L.w[u][r] = ld_stream(wp[r] + c);
+        L.sc[u][r] = sp[r][c];
       }
-#pragma unroll
-    for (int u = 0; u < U; ++u) i4_group<R>(w[u], sc[u], c + 64 * u, x4, acc);
-  }
-  for (; c < nch; c += 64) {
-    uint4 w[R];
-    uint16_t sc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      w[r] = ld_stream(wp[r] + c);
-      sc[r] = sp[r][c];
     }
-    i4_group<R>(w, sc, c, x4, acc);
+  }
+}
+
+// the dot products of those rows against the quantised vector (xp, xe) of the K
+// columns: the issued steps, then the rest of the row one step at a time
+template <int R, int U>
+__device__ __forceinline__ void q_dot_issued(const uint8_t* __restrict__ Q,
+                                             const uint16_t* __restrict__ S, size_t ldw, int row0,
+                                             int N, int k0, int K, const QLoad<R, U>& L,
+                                             const uint4* __restrict__ xp, const int* __restrict__ xe,
+                                             float (&acc)[R]) {
+  const int G = K >> 5, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (lane + 64 * u < G) q_group<R>(L.w[u], L.sc[u], lane + 64 * u, G, xp, xe, acc);
+  if (64 * U < G) {
+    const uint4* wp[R];
+    const uint16_t* sp[R];
+    q_row_ptrs<R>(Q, S, ldw, row0, N, k0, wp, sp);
+    for (int c = lane + 64 * U; c < G; c += 64) {
+      uint4 w[R];
+      uint16_t sc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        w[r] = ld_stream(wp[r] + c);
+        sc[r] = sp[r][c];
+      }
+      q_group<R>(w, sc, c, G, xp, xe, acc);
+    }
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
 }
 
-// the weight stream of a kernel: bf16 rows (I4 false) or int4 rows (W the codes,
-// S the scales)
-template <int R, int U, bool I4>
-__device__ __forceinline__ void rows_dot_w(const uint16_t* __restrict__ W,
-                                           const uint16_t* __restrict__ S, size_t ldw, int row0,
-                                           int N, int k0, int K, const float* __restrict__ xs,
-                                           float (&acc)[R]) {
-  if constexpr (I4)
-    rows_dot_i4<R, U>(reinterpret_cast<const uint8_t*>(W), S, ldw, row0, N, k0, K, xs, acc);
-  else
-    rows_dot<R, U>(W, ldw, row0, N, k0, K, xs, acc);
+// int4 kernels keep 4 waves per SIMD resident (at most 128 VGPRs): a wave's loads
+// are one row set's worth, so the loads of other waves hide its arithmetic
+constexpr int kI4WavesPerSimd = 4;
+
+// int4 kernels run a grid of at most this many blocks (each stages and quantises
+// the vector once, then covers ceil(virtual blocks / grid) virtual blocks of rows);
+// EAGLE3_I4_BLOCKS overrides it
+constexpr int kI4Blocks = 512;
+int i4_blocks() {
+  static const int v = [] {
+    const char* s = std::getenv("EAGLE3_I4_BLOCKS");
+    const int b = s ? std::atoi(s) : 0;
+    return b > 0 ? b : kI4Blocks;
+  }();
+  return v;
+}
+// the launched grid for nvb virtual blocks: the fewest blocks that keep the
+// per-block count of virtual blocks at ceil(nvb / cap)
+static inline int i4_grid(int nvb) {
+  const int cap = i4_blocks();
+  if (nvb <= cap) return nvb;
+  const int per = (nvb + cap - 1) / cap;
+  return (nvb + per - 1) / per;
 }
 
 // One thread per group of 32: scale = bf16(max|w| / 7), codes rint(w / scale)
@@ -272,11 +366,11 @@ __device__ __forceinline__ float sum_partials(const float* __restrict__ p, int c
   return s;
 }
 
-// Emit the R rows of a wave: y, y*w1, y*w2 (when given) and this block's sum
-// of y^2 (when given).  Every thread of the block must call it.
+// Emit the R rows of a wave: y, y*w1, y*w2 (when given) and the block's sum of
+// y^2 (when given) as partial `slot`.  Every thread of the block must call it.
 template <int R, int WAVES>
 __device__ __forceinline__ void emit_rows(const float (&y)[R], int row0, int N, const VecOut& o,
-                                          float* red) {
+                                          float* red, int slot) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   float ss = 0.f;
 #pragma unroll
@@ -298,7 +392,7 @@ __device__ __forceinline__ void emit_rows(const float (&y)[R], int row0, int N, 
     float t = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) t += red[w];
-    o.ssq[blockIdx.x] = t;
+    o.ssq[slot] = t;
   }
 }
 
@@ -331,57 +425,67 @@ __device__ __forceinline__ void stage_plain(float* xs, const float* __restrict__
 
 // ---------------------------------------------------------------------------
 template <int WAVES, int R, int U, bool I4>
-__global__ __launch_bounds__(64 * WAVES) void k_encode(const uint16_t* __restrict__ W,
-                                                       const uint16_t* __restrict__ S, int n,
-                                                       const float* __restrict__ a0,
-                                                       const float* __restrict__ a1,
-                                                       const float* __restrict__ a2, VecOut out) {
-  extern __shared__ float xs[];
+__global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_encode(
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ S, int n,
+    const float* __restrict__ a0, const float* __restrict__ a1, const float* __restrict__ a2,
+    VecOut out) {
+  extern __shared__ float xs[];  // [3n]; int4: then the quantised vector
   __shared__ float red[16];
-  stage_plain(xs, a0, n);
-  stage_plain(xs + n, a1, n);
-  stage_plain(xs + 2 * n, a2, n);
-  __syncthreads();
   const int wv = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wv) * R;
-  float acc[R];
-  if (row0 < n) rows_dot_w<R, U, I4>(W, S, size_t(3) * n, row0, n, 0, 3 * n, xs, acc);
-  else
+  if constexpr (!I4) {
+    stage_plain(xs, a0, n);
+    stage_plain(xs + n, a1, n);
+    stage_plain(xs + 2 * n, a2, n);
+    __syncthreads();
+    const int row0 = (blockIdx.x * WAVES + wv) * R;
+    float acc[R];
+    if (row0 < n) rows_dot<R, U>(W, size_t(3) * n, row0, n, 0, 3 * n, xs, acc);
+    else
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  emit_rows<R, WAVES>(acc, row0, n, out, red);
+      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    emit_rows<R, WAVES>(acc, row0, n, out, red, blockIdx.x);
+  } else {
+    const uint8_t* Q = reinterpret_cast<const uint8_t*>(W);
+    const int K = 3 * n;
+    const int nvb = (n + WAVES * R - 1) / (WAVES * R);
+    QLoad<R, U> L;
+    int row0 = (blockIdx.x * WAVES + wv) * R;
+    if (row0 < n) q_issue<R, U>(Q, S, size_t(K), row0, n, 0, K, L);
+    stage_plain(xs, a0, n);
+    stage_plain(xs + n, a1, n);
+    stage_plain(xs + 2 * n, a2, n);
+    __syncthreads();
+    uint4* xp = reinterpret_cast<uint4*>(xs + K);
+    int* xe = reinterpret_cast<int*>(xp + K / 8);
+    quant_x_i4(xs, K, xp, xe);
+    __syncthreads();
+    // (the whole row is one issue for the drafter widths and the grid covers every
+    // row set, so the loop body runs once; later row sets load at their turn)
+    for (int vb = blockIdx.x;; vb += gridDim.x) {
+      float acc[R];
+      if (row0 < n) q_dot_issued<R, U>(Q, S, size_t(K), row0, n, 0, K, L, xp, xe, acc);
+      else
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.f;
+      emit_rows<R, WAVES>(acc, row0, n, out, red, vb);
+      const int vn = vb + int(gridDim.x);
+      if (vn >= nvb) break;
+      __syncthreads();  // red is reused by the next virtual block
+      row0 = (vn * WAVES + wv) * R;
+      if (row0 < n) q_issue<R, U>(Q, S, size_t(K), row0, n, 0, K, L);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 constexpr int kQkvERegs = 8;  // float4 chunks of the embedding row held per thread
 
-template <int WAVES, int R, int U, bool I4>
-__global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
-  static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
-  extern __shared__ float xs[];  // [0, n): embedding half; [n, 2n): hidden half
-  __shared__ float red[32];
-  __shared__ float sv[16];
-  __shared__ int si[16], st[16];
-  const int n = a.n;
-  const int hd = a.head_dim;
-  const int qd = a.n_head * hd, kvd = a.n_head_kv * hd;
-  const int N = qd + 2 * kvd;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wv) * R;
-
-  // the first weight loads of the hidden half go out before anything else, so
-  // the prologue below (staging, the previous step's argmax, the embedding row)
-  // overlaps the weight stream
-  uint4 wpf[U][R];
-  const bool issued = !I4 && row0 < N && (n >> 3) >= 64 * U;
-  if (issued) rows_issue<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, wpf);
-  // hidden half: already weighted by hidden_norm; its sum of squares from partials
-  stage_plain(xs + n, a.gw, n);
-  float sg = sum_partials(a.g_ssq, a.g_ssq_count);
+// finish the previous step (argmax over the lm_head candidates, d2t; the
+// candidates' target ids come with them when prev_tok is given) or read the
+// token; every thread of the block calls it and gets the token
+__device__ __forceinline__ int qkv_token(const QkvArgs& a, float* sv, int* si, int* st) {
   int tok;
   if (a.prev_count > 0) {
-    // finish the previous step: argmax over the lm_head candidates, d2t (the
-    // candidates' target ids come with them when prev_tok is given)
     int bt;
     int bi = block_argmax_carry(a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, sv, si, st, &bt);
     if (bi < 0 || bi >= a.dv) tok = a.d2t[0];  // only reachable with NaN logits
@@ -393,50 +497,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   } else {
     tok = *a.tok;
   }
-  tok = min(max(tok, 0), a.vocab - 1);  // out-of-range ids are clamped
-  __syncthreads();  // hidden half staged
-  // the embedding row and input_layernorm go to registers; they land while the
-  // hidden half streams
-  const uint2* e4 = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);
-  const float4* w4 = reinterpret_cast<const float4*>(a.w_in);
-  const int n4 = n >> 2;
-  uint2 er[kQkvERegs];
-  float4 wr[kQkvERegs];
-  const bool in_regs = n4 <= kQkvERegs * int(blockDim.x);
-#pragma unroll
-  for (int j = 0; j < kQkvERegs; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (in_regs && i < n4) {
-      er[j] = e4[i];
-      wr[j] = w4[i];
-    }
-  }
-  float acc_g[R], acc_e[R];
-  if (issued) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, wpf, acc_g);
-  else if (row0 < N) rows_dot_w<R, U, I4>(a.w_qkv, a.s_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
-  float se = 0.f;
-  float4* x4 = reinterpret_cast<float4*>(xs);
-  if (in_regs) {
-#pragma unroll
-    for (int j = 0; j < kQkvERegs; ++j) {
-      const int i = threadIdx.x + j * blockDim.x;
-      if (i < n4) {
-        const float e0 = bf16_lo(er[j].x), e1 = bf16_hi(er[j].x), e2 = bf16_lo(er[j].y),
-                    e3 = bf16_hi(er[j].y);
-        x4[i] = make_float4(e0 * wr[j].x, e1 * wr[j].y, e2 * wr[j].z, e3 * wr[j].w);
-        se = fmaf(e0, e0, fmaf(e1, e1, fmaf(e2, e2, fmaf(e3, e3, se))));
-      }
-    }
-  } else {
-    se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
-  }
-  __syncthreads();
-  if (row0 < N) rows_dot_w<R, U, I4>(a.w_qkv, a.s_qkv, size_t(2) * n, row0, N, 0, n, xs, acc_e);
-  block_sum2(se, sg, red);  // every wave takes part
-  if (row0 >= N) return;
-  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
-  const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+  return min(max(tok, 0), a.vocab - 1);  // out-of-range ids are clamped
+}
 
+// the fused epilogue of a wave's R rows: 1/rms per half, NeoX rotation of q/k
+// pairs, q to fp32, k/v rows to the KV cache
+template <int R>
+__device__ __forceinline__ void qkv_epilogue(const QkvArgs& a, int row0, const float (&acc_e)[R],
+                                             const float (&acc_g)[R], float ie, float ig) {
+  const int lane = threadIdx.x & 63;
+  const int hd = a.head_dim;
+  const int qd = a.n_head * hd, kvd = a.n_head_kv * hd;
+  const int N = qd + 2 * kvd;
 #pragma unroll
   for (int p = 0; p < R / 2; ++p) {
     const int r = row0 + 2 * p;
@@ -472,102 +544,318 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-template <int WAVES, int R, int U, bool I4>
-__global__ __launch_bounds__(64 * WAVES) void k_gemv_resid(const uint16_t* __restrict__ W,
-                                                           const uint16_t* __restrict__ S, int N,
-                                                           int K, const float* __restrict__ x,
-                                                           const float* __restrict__ resid,
-                                                           VecOut out) {
-  extern __shared__ float xs[];
-  __shared__ float red[16];
-  stage_plain(xs, x, K);
-  __syncthreads();
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
+  static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
+  extern __shared__ float xs[];  // [0, n): embedding half; [n, 2n): hidden half
+  __shared__ float red[32];
+  __shared__ float sv[16];
+  __shared__ int si[16], st[16];
+  const int n = a.n;
+  const int N = (a.n_head + 2 * a.n_head_kv) * a.head_dim;
   const int wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
-  float acc[R];
-  if (row0 < N) {
-    rows_dot_w<R, U, I4>(W, S, size_t(K), row0, N, 0, K, xs, acc);
+
+  // the first weight loads of the hidden half go out before anything else, so
+  // the prologue below (staging, the previous step's argmax, the embedding row)
+  // overlaps the weight stream
+  uint4 wpf[U][R];
+  const bool issued = row0 < N && (n >> 3) >= 64 * U;
+  if (issued) rows_issue<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, wpf);
+  // hidden half: already weighted by hidden_norm; its sum of squares from partials
+  stage_plain(xs + n, a.gw, n);
+  float sg = sum_partials(a.g_ssq, a.g_ssq_count);
+  const int tok = qkv_token(a, sv, si, st);
+  __syncthreads();  // hidden half staged
+  // the embedding row and input_layernorm go to registers; they land while the
+  // hidden half streams
+  const uint2* e4 = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);
+  const float4* w4 = reinterpret_cast<const float4*>(a.w_in);
+  const int n4 = n >> 2;
+  uint2 er[kQkvERegs];
+  float4 wr[kQkvERegs];
+  const bool in_regs = n4 <= kQkvERegs * int(blockDim.x);
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] += resid[min(row0 + r, N - 1)];
-  } else {
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  for (int j = 0; j < kQkvERegs; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (in_regs && i < n4) {
+      er[j] = e4[i];
+      wr[j] = w4[i];
+    }
   }
-  emit_rows<R, WAVES>(acc, row0, N, out, red);
+  float acc_g[R], acc_e[R];
+  if (issued) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, wpf, acc_g);
+  else if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
+  float se = 0.f;
+  float4* x4 = reinterpret_cast<float4*>(xs);
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kQkvERegs; ++j) {
+      const int i = threadIdx.x + j * blockDim.x;
+      if (i < n4) {
+        const float e0 = bf16_lo(er[j].x), e1 = bf16_hi(er[j].x), e2 = bf16_lo(er[j].y),
+                    e3 = bf16_hi(er[j].y);
+        x4[i] = make_float4(e0 * wr[j].x, e1 * wr[j].y, e2 * wr[j].z, e3 * wr[j].w);
+        se = fmaf(e0, e0, fmaf(e1, e1, fmaf(e2, e2, fmaf(e3, e3, se))));
+      }
+    }
+  } else {
+    se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
+  }
+  __syncthreads();
+  if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, 0, n, xs, acc_e);
+  block_sum2(se, sg, red);  // every wave takes part
+  if (row0 >= N) return;
+  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
+  const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+  qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+}
+
+// k_qkv with int4 weights: the first row set's codes of both halves go out first;
+// both halves are then staged and quantised once per block, and the block covers
+// its virtual blocks of rows
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_qkv_q(QkvArgs a) {
+  static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
+  extern __shared__ float xs[];  // [0, n) embedding half, [n, 2n) hidden half, then
+                                 // the two quantised halves
+  __shared__ float red[32];
+  __shared__ float sv[16];
+  __shared__ int si[16], st[16];
+  const int n = a.n;
+  const int N = (a.n_head + 2 * a.n_head_kv) * a.head_dim;
+  const int wv = threadIdx.x >> 6;
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.w_qkv);
+  const size_t ldw = size_t(2) * n;
+  const int nvb = (N + WAVES * R - 1) / (WAVES * R);
+  QLoad<R, U> Lg, Le;
+  int row0 = (blockIdx.x * WAVES + wv) * R;
+  if (row0 < N) {
+    q_issue<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg);
+    q_issue<R, U>(Q, a.s_qkv, ldw, row0, N, 0, n, Le);
+  }
+  uint4* xpe = reinterpret_cast<uint4*>(xs + 2 * n);
+  int* xee = reinterpret_cast<int*>(xpe + n / 8);
+  uint4* xpg = reinterpret_cast<uint4*>(xee + n / 32);
+  int* xeg = reinterpret_cast<int*>(xpg + n / 8);
+  stage_plain(xs + n, a.gw, n);
+  float sg = sum_partials(a.g_ssq, a.g_ssq_count);
+  const int tok = qkv_token(a, sv, si, st);
+  float se = stage_weighted_bf16(xs, a.embed + (size_t)tok * n, a.w_in, n);
+  __syncthreads();
+  quant_x_i4(xs, n, xpe, xee);
+  quant_x_i4(xs + n, n, xpg, xeg);
+  block_sum2(se, sg, red);  // its barriers also publish the quantised halves
+  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
+  const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+  for (int vb = blockIdx.x;; vb += gridDim.x) {
+    if (row0 < N) {
+      float acc_g[R], acc_e[R];
+      q_dot_issued<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg, xpg, xeg, acc_g);
+      q_dot_issued<R, U>(Q, a.s_qkv, ldw, row0, N, 0, n, Le, xpe, xee, acc_e);
+      qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+    }
+    const int vn = vb + int(gridDim.x);
+    if (vn >= nvb) break;
+    row0 = (vn * WAVES + wv) * R;
+    if (row0 < N) {
+      q_issue<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg);
+      q_issue<R, U>(Q, a.s_qkv, ldw, row0, N, 0, n, Le);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 template <int WAVES, int R, int U, bool I4>
-__global__ __launch_bounds__(64 * WAVES) void k_gateup(const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_gemv_resid(
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ S, int N, int K,
+    const float* __restrict__ x, const float* __restrict__ resid, VecOut out) {
+  extern __shared__ float xs[];  // [K]; int4: then the quantised vector
+  __shared__ float red[16];
+  const int wv = threadIdx.x >> 6;
+  auto finish = [&](float (&acc)[R], int row0) {
+    if (row0 < N) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] += resid[min(row0 + r, N - 1)];
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    }
+  };
+  if constexpr (!I4) {
+    stage_plain(xs, x, K);
+    __syncthreads();
+    const int row0 = (blockIdx.x * WAVES + wv) * R;
+    float acc[R];
+    if (row0 < N) rows_dot<R, U>(W, size_t(K), row0, N, 0, K, xs, acc);
+    finish(acc, row0);
+    emit_rows<R, WAVES>(acc, row0, N, out, red, blockIdx.x);
+  } else {
+    const uint8_t* Q = reinterpret_cast<const uint8_t*>(W);
+    const int nvb = (N + WAVES * R - 1) / (WAVES * R);
+    QLoad<R, U> L;
+    int row0 = (blockIdx.x * WAVES + wv) * R;
+    if (row0 < N) q_issue<R, U>(Q, S, size_t(K), row0, N, 0, K, L);
+    stage_plain(xs, x, K);
+    __syncthreads();
+    uint4* xp = reinterpret_cast<uint4*>(xs + K);
+    int* xe = reinterpret_cast<int*>(xp + K / 8);
+    quant_x_i4(xs, K, xp, xe);
+    __syncthreads();
+    for (int vb = blockIdx.x;; vb += gridDim.x) {
+      float acc[R];
+      if (row0 < N) q_dot_issued<R, U>(Q, S, size_t(K), row0, N, 0, K, L, xp, xe, acc);
+      finish(acc, row0);
+      emit_rows<R, WAVES>(acc, row0, N, out, red, vb);
+      const int vn = vb + int(gridDim.x);
+      if (vn >= nvb) break;
+      __syncthreads();  // red is reused by the next virtual block
+      row0 = (vn * WAVES + wv) * R;
+      if (row0 < N) q_issue<R, U>(Q, S, size_t(K), row0, N, 0, K, L);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int WAVES, int R, int U, bool I4>
+__global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_gateup(const uint16_t* __restrict__ W,
                                                        const uint16_t* __restrict__ S, int n_ff,
                                                        int n, const float* __restrict__ xw,
                                                        const float* __restrict__ x_ssq,
                                                        int ssq_count, float eps,
                                                        float* __restrict__ act) {
   static_assert(R % 2 == 0, "gate/up pairs need an even row count per wave");
-  extern __shared__ float xs[];
+  extern __shared__ float xs[];  // [n]; int4: then the quantised vector
   __shared__ float red[32];
   const int N = 2 * n_ff;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  QLoad<(I4 ? R : 1), (I4 ? U : 1)> L0;  // int4: the first row set, loaded before the stage
+  if constexpr (I4) {
+    const int row0 = (blockIdx.x * WAVES + wv) * R;
+    if (row0 < N) q_issue<R, U>(reinterpret_cast<const uint8_t*>(W), S, size_t(n), row0, N, 0, n, L0);
+  }
   stage_plain(xs, xw, n);
   float ss = sum_partials(x_ssq, ssq_count), dummy = 0.f;
   __syncthreads();
-  float acc[R];
-  if (row0 < N) rows_dot_w<R, U, I4>(W, S, size_t(n), row0, N, 0, n, xs, acc);
-  block_sum2(ss, dummy, red);
-  if (row0 >= N) return;
-  const float inv = 1.0f / sqrtf(ss / float(n) + eps);
+  auto epilogue = [&](int row0, const float (&acc)[R], float inv) {
 #pragma unroll
-  for (int p = 0; p < R / 2; ++p) {
-    const int r = row0 + 2 * p;
-    if (lane == p && r < N) {
-      const float gt = acc[2 * p] * inv, up = acc[2 * p + 1] * inv;
-      act[r >> 1] = (gt / (1.0f + expf(-gt))) * up;
+    for (int p = 0; p < R / 2; ++p) {
+      const int r = row0 + 2 * p;
+      if (lane == p && r < N) {
+        const float gt = acc[2 * p] * inv, up = acc[2 * p + 1] * inv;
+        act[r >> 1] = (gt / (1.0f + expf(-gt))) * up;
+      }
+    }
+  };
+  if constexpr (!I4) {
+    const int row0 = (blockIdx.x * WAVES + wv) * R;
+    float acc[R];
+    if (row0 < N) rows_dot<R, U>(W, size_t(n), row0, N, 0, n, xs, acc);
+    block_sum2(ss, dummy, red);
+    if (row0 >= N) return;
+    epilogue(row0, acc, 1.0f / sqrtf(ss / float(n) + eps));
+  } else {
+    uint4* xp = reinterpret_cast<uint4*>(xs + n);
+    int* xe = reinterpret_cast<int*>(xp + n / 8);
+    quant_x_i4(xs, n, xp, xe);
+    block_sum2(ss, dummy, red);  // its barriers also publish the quantised vector
+    const float inv = 1.0f / sqrtf(ss / float(n) + eps);
+    const uint8_t* Q = reinterpret_cast<const uint8_t*>(W);
+    const int nvb = (N + WAVES * R - 1) / (WAVES * R);
+    int row0 = (blockIdx.x * WAVES + wv) * R;
+    for (int vb = blockIdx.x;; vb += gridDim.x) {
+      const int vn = vb + int(gridDim.x), rn = (vn * WAVES + wv) * R;
+      QLoad<R, U> Ln;
+      if (vn < nvb && rn < N) q_issue<R, U>(Q, S, size_t(n), rn, N, 0, n, Ln);
+      if (row0 < N) {
+        float acc[R];
+        q_dot_issued<R, U>(Q, S, size_t(n), row0, N, 0, n, L0, xp, xe, acc);
+        epilogue(row0, acc, inv);
+      }
+      if (vn >= nvb) break;
+      L0 = Ln;
+      row0 = rn;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 template <int WAVES, int R, int U, bool I4>
-__global__ __launch_bounds__(64 * WAVES) void k_lmhead(LmHeadArgs a) {
-  extern __shared__ float xs[];
+__global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead(LmHeadArgs a) {
+  extern __shared__ float xs[];  // [n]; int4: then the quantised vector
   __shared__ float red[32];
   __shared__ float bv_s[16];
   __shared__ int bi_s[16], bt_s[16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wv) * R;
-  // d2t of this wave's rows (lane r holds row0 + r's), loaded before the stream
-  const int dt = (a.d2t && lane < R && row0 + lane < a.dv) ? a.d2t[row0 + lane] : 0;
-  stage_plain(xs, a.hw, a.n);
-  float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
-  __syncthreads();
-  float acc[R];
-  if (row0 < a.dv) rows_dot_w<R, U, I4>(a.w_lm, a.s_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
-  block_sum2(ss, dummy, red);
-  const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
-  float bv = -INFINITY;
-  int bi = 0x7FFFFFFF, br = 0;
-  if (row0 < a.dv) {
+  // d2t of a wave's rows (lane r holds row0 + r's)
+  auto d2t_of = [&](int row0) { return (a.d2t && lane < R && row0 + lane < a.dv) ? a.d2t[row0 + lane] : 0; };
+  // the block's candidate for virtual block vb from the waves' R logits each
+  auto candidates = [&](const float (&acc)[R], int row0, float inv, int dt, int vb) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF, br = 0;
+    if (row0 < a.dv) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (row0 + r < a.dv) {
-        const float v = acc[r] * inv;
-        if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; br = r; }
-        if (a.logits_dbg && lane == r) a.logits_dbg[row0 + r] = v;
+      for (int r = 0; r < R; ++r) {
+        if (row0 + r < a.dv) {
+          const float v = acc[r] * inv;
+          if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; br = r; }
+          if (a.logits_dbg && lane == r) a.logits_dbg[row0 + r] = v;
+        }
       }
     }
-  }
-  int bt = bi + __shfl(dt, br, kWave);
-  if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; bt_s[wv] = bt; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < WAVES; ++w)
-      if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; bt = bt_s[w]; }
-    a.part_val[blockIdx.x] = bv;
-    a.part_idx[blockIdx.x] = bi;
-    if (a.d2t) a.part_tok[blockIdx.x] = bt;
+    int bt = bi + __shfl(dt, br, kWave);
+    if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; bt_s[wv] = bt; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < WAVES; ++w)
+        if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; bt = bt_s[w]; }
+      a.part_val[vb] = bv;
+      a.part_idx[vb] = bi;
+      if (a.d2t) a.part_tok[vb] = bt;
+    }
+  };
+  int row0 = (blockIdx.x * WAVES + wv) * R;
+  if constexpr (!I4) {
+    const int dt = d2t_of(row0);  // loaded before the stream
+    stage_plain(xs, a.hw, a.n);
+    float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
+    __syncthreads();
+    float acc[R];
+    if (row0 < a.dv) rows_dot<R, U>(a.w_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
+    block_sum2(ss, dummy, red);
+    candidates(acc, row0, 1.0f / sqrtf(ss / float(a.n) + a.eps), dt, blockIdx.x);
+  } else {
+    const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.w_lm);
+    const size_t ldw = size_t(a.n);
+    const int nvb = (a.dv + WAVES * R - 1) / (WAVES * R);
+    QLoad<R, U> L;
+    if (row0 < a.dv) q_issue<R, U>(Q, a.s_lm, ldw, row0, a.dv, 0, a.n, L);
+    int dt = d2t_of(row0);
+    stage_plain(xs, a.hw, a.n);
+    float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
+    __syncthreads();
+    uint4* xp = reinterpret_cast<uint4*>(xs + a.n);
+    int* xe = reinterpret_cast<int*>(xp + a.n / 8);
+    quant_x_i4(xs, a.n, xp, xe);
+    block_sum2(ss, dummy, red);  // its barriers also publish the quantised vector
+    const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
+    for (int vb = blockIdx.x;; vb += gridDim.x) {
+      const int vn = vb + int(gridDim.x), rn = (vn * WAVES + wv) * R;
+      QLoad<R, U> Ln;
+      int dtn = 0;
+      if (vn < nvb) {
+        if (rn < a.dv) q_issue<R, U>(Q, a.s_lm, ldw, rn, a.dv, 0, a.n, Ln);
+        dtn = d2t_of(rn);
+      }
+      float acc[R];
+      if (row0 < a.dv) q_dot_issued<R, U>(Q, a.s_lm, ldw, row0, a.dv, 0, a.n, L, xp, xe, acc);
+      candidates(acc, row0, inv, dt, vb);
+      if (vn >= nvb) break;
+      __syncthreads();  // the candidate slots are reused
+      L = Ln;
+      row0 = rn;
+      dt = dtn;
+    }
   }
 }
 
@@ -763,6 +1051,23 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
 
 static inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// raise a kernel's dynamic LDS limit to `bytes` (once per kernel and size; the int4
+// kernels stage the vector and its quantised form, which can pass 64 KB)
+template <auto F>
+static hipError_t lds_allow(size_t bytes) {
+  static size_t allowed = 64 * 1024;
+  if (bytes <= allowed) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(F),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+  if (e == hipSuccess) allowed = bytes;
+  return e;
+}
+#define E3_LDS_ALLOW(KERNEL, BYTES)                                \
+  do {                                                             \
+    const hipError_t _e = lds_allow<KERNEL>(BYTES);                \
+    if (_e != hipSuccess) return _e;                               \
+  } while (0)
+
 int gemv_grid(int N, int cfg) {
   switch (cfg) {
 #define CASE(ID, WV, RR, UU) \
@@ -779,14 +1084,16 @@ int gemv_grid(int N, int cfg) {
 hipError_t launch_encode(const uint16_t* w_fc, const uint16_t* S, int n, const float* a0,
                          const float* a1, const float* a2, const VecOut& out, int cfg,
                          hipStream_t s) {
+  const size_t xb = size_t(3 * n) * sizeof(float);
 #define CASE(ID, WV, RR, UU)                                                                    \
   case ID:                                                                                      \
-    if (S)                                                                                      \
-      hipLaunchKernelGGL((k_encode<WV, RR, UU, true>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
-                         size_t(3 * n) * sizeof(float), s, w_fc, S, n, a0, a1, a2, out);       \
-    else                                                                                        \
+    if (S) {                                                                                    \
+      E3_LDS_ALLOW((k_encode<WV, RR, UU, true>), xb + q_vec_bytes(3 * n));                      \
+      hipLaunchKernelGGL((k_encode<WV, RR, UU, true>), dim3(i4_grid(ceil_div(n, WV * RR))),     \
+                         dim3(64 * WV), xb + q_vec_bytes(3 * n), s, w_fc, S, n, a0, a1, a2, out); \
+    } else                                                                                      \
       hipLaunchKernelGGL((k_encode<WV, RR, UU, false>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
-                         size_t(3 * n) * sizeof(float), s, w_fc, S, n, a0, a1, a2, out);       \
+                         xb, s, w_fc, S, n, a0, a1, a2, out);                                   \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -795,15 +1102,17 @@ hipError_t launch_encode(const uint16_t* w_fc, const uint16_t* S, int n, const f
 
 hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
   const int N = (a.n_head + 2 * a.n_head_kv) * a.head_dim;
+  const size_t xb = size_t(2 * a.n) * sizeof(float);
 #define CASE(ID, WV, RR, UU)                                                               \
   case ID:                                                                                 \
     if (RR % 2) return hipErrorInvalidValue;                                               \
-    if (a.s_qkv)                                                                           \
-      hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU, true>), dim3(ceil_div(N, WV * RR)), \
-                         dim3(64 * WV), size_t(2 * a.n) * sizeof(float), s, a);            \
-    else                                                                                   \
-      hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU, false>), dim3(ceil_div(N, WV * RR)), \
-                         dim3(64 * WV), size_t(2 * a.n) * sizeof(float), s, a);            \
+    if (a.s_qkv) {                                                                         \
+      E3_LDS_ALLOW((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), xb + 2 * q_vec_bytes(a.n));        \
+      hipLaunchKernelGGL((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), dim3(i4_grid(ceil_div(N, WV * RR))), \
+                         dim3(64 * WV), xb + 2 * q_vec_bytes(a.n), s, a);                  \
+    } else                                                                                 \
+      hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(N, WV * RR)),   \
+                         dim3(64 * WV), xb, s, a);                                         \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -812,14 +1121,16 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
 
 hipError_t launch_gemv_resid(const uint16_t* w, const uint16_t* S, int N, int K, const float* x,
                              const float* resid, const VecOut& out, int cfg, hipStream_t s) {
+  const size_t xb = size_t(K) * sizeof(float);
 #define CASE(ID, WV, RR, UU)                                                                    \
   case ID:                                                                                      \
-    if (S)                                                                                      \
-      hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, true>), dim3(ceil_div(N, WV * RR)),         \
-                         dim3(64 * WV), size_t(K) * sizeof(float), s, w, S, N, K, x, resid, out); \
-    else                                                                                        \
+    if (S) {                                                                                    \
+      E3_LDS_ALLOW((k_gemv_resid<WV, RR, UU, true>), xb + q_vec_bytes(K));                      \
+      hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, true>), dim3(i4_grid(ceil_div(N, WV * RR))), \
+                         dim3(64 * WV), xb + q_vec_bytes(K), s, w, S, N, K, x, resid, out);    \
+    } else                                                                                      \
       hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, false>), dim3(ceil_div(N, WV * RR)),        \
-                         dim3(64 * WV), size_t(K) * sizeof(float), s, w, S, N, K, x, resid, out); \
+                         dim3(64 * WV), xb, s, w, S, N, K, x, resid, out);                     \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
@@ -829,16 +1140,18 @@ hipError_t launch_gemv_resid(const uint16_t* w, const uint16_t* S, int N, int K,
 hipError_t launch_gateup(const uint16_t* w_gu, const uint16_t* S, int n_ff, int n, const float* xw,
                          const float* x_ssq, int ssq_count, float eps, float* act, int cfg,
                          hipStream_t s) {
+  const size_t xb = size_t(n) * sizeof(float);
 #define CASE(ID, WV, RR, UU)                                                                \
   case ID:                                                                                  \
     if (RR % 2) return hipErrorInvalidValue;                                                \
-    if (S)                                                                                  \
+    if (S) {                                                                                \
+      E3_LDS_ALLOW((k_gateup<WV, (RR < 2 ? 2 : RR), UU, true>), xb + q_vec_bytes(n));       \
       hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU, true>),                       \
-                         dim3(ceil_div(2 * n_ff, WV * RR)), dim3(64 * WV), size_t(n) * sizeof(float), \
-                         s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act);              \
-    else                                                                                    \
+                         dim3(i4_grid(ceil_div(2 * n_ff, WV * RR))), dim3(64 * WV),          \
+                         xb + q_vec_bytes(n), s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act); \
+    } else                                                                                  \
       hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU, false>),                      \
-                         dim3(ceil_div(2 * n_ff, WV * RR)), dim3(64 * WV), size_t(n) * sizeof(float), \
+                         dim3(ceil_div(2 * n_ff, WV * RR)), dim3(64 * WV), xb,              \
                          s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act);              \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
@@ -846,17 +1159,20 @@ hipError_t launch_gateup(const uint16_t* w_gu, const uint16_t* S, int n_ff, int 
   return hipGetLastError();
 }
 
+// number of candidate partials (virtual blocks, also with int4 weights)
 int lmhead_grid(int dv, int cfg) { return gemv_grid(dv, cfg); }
 
 hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
+  const size_t xb = size_t(a.n) * sizeof(float);
 #define CASE(ID, WV, RR, UU)                                                                  \
   case ID:                                                                                    \
-    if (a.s_lm)                                                                               \
-      hipLaunchKernelGGL((k_lmhead<WV, RR, UU, true>), dim3(ceil_div(a.dv, WV * RR)),          \
-                         dim3(64 * WV), size_t(a.n) * sizeof(float), s, a);                   \
-    else                                                                                      \
+    if (a.s_lm) {                                                                             \
+      E3_LDS_ALLOW((k_lmhead<WV, RR, UU, true>), xb + q_vec_bytes(a.n));                      \
+      hipLaunchKernelGGL((k_lmhead<WV, RR, UU, true>), dim3(i4_grid(ceil_div(a.dv, WV * RR))), \
+                         dim3(64 * WV), xb + q_vec_bytes(a.n), s, a);                         \
+    } else                                                                                    \
       hipLaunchKernelGGL((k_lmhead<WV, RR, UU, false>), dim3(ceil_div(a.dv, WV * RR)),         \
-                         dim3(64 * WV), size_t(a.n) * sizeof(float), s, a);                   \
+                         dim3(64 * WV), xb, s, a);                                            \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
