@@ -33,12 +33,12 @@ from .drafter import DrafterOracle, StatelessChain
 from .ledger import Ledger, LedgerError
 from .rope_width import resolve_rope_dim
 from .trunk import TrunkOracle
-from . import int4
+from . import int4, kvquant
 from .loop import greedy_plain, greedy_speculative
 
 __all__ = [
     "argmax_first", "attention_causal", "attention_decode", "bf16_bits_to_f64",
     "rms_norm", "rope_neox_partial", "silu", "DrafterOracle", "StatelessChain",
     "Ledger", "LedgerError", "resolve_rope_dim", "TrunkOracle", "greedy_plain",
-    "greedy_speculative", "int4",
+    "greedy_speculative", "int4", "kvquant",
 ]

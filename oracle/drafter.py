@@ -31,6 +31,7 @@ from typing import Callable, Dict, List, Optional, Sequence, Union
 
 import numpy as np
 
+from . import kvquant
 from .ledger import Ledger
 from .numerics import (argmax_first, attention_causal, attention_decode,
                        bf16_bits_to_f64, rms_norm, rope_neox_partial, silu)
@@ -77,7 +78,13 @@ class DrafterOracle:
 
     def __init__(self, geom, weights: Dict[str, object],
                  embed: Union[np.ndarray, Callable[[np.ndarray], np.ndarray], object],
-                 d2t, max_ctx: int = 0, max_seqs: int = 1, max_gamma: int = 16):
+                 d2t, max_ctx: int = 0, max_seqs: int = 1, max_gamma: int = 16,
+                 kv_format: str = "exact"):
+        """kv_format: "exact" keeps K/V rows as computed; "q8q5" stores each row
+        in its quantized form (oracle.kvquant: q8_0 K, q5_1 V) and every read of
+        the cache, the new row's included, sees those values."""
+        assert kv_format in ("exact", "q8q5"), kv_format
+        self.kv_q = kv_format == "q8q5"
         self.n = geom.n_embd
         self.nh = geom.n_head
         self.nkv = geom.n_head_kv
@@ -189,6 +196,7 @@ class DrafterOracle:
         nctx = pos if nctx is None else nctx
         cat = self.input_cat(g[None, :], [tok])[0]
         q, k, v = self.qkv(cat, pos)
+        k, v = self._kv_rows(k, v)
         K = np.concatenate([Kctx[:nctx], k[None]], axis=0)
         V = np.concatenate([Vctx[:nctx], v[None]], axis=0)
         o = attention_decode(q, K, V).reshape(-1)
@@ -201,6 +209,12 @@ class DrafterOracle:
     # ------------------------------------------------------------------
     # stateful entry points (pegainfer PR #707 description)
     # ------------------------------------------------------------------
+    def _kv_rows(self, k, v):
+        """The K/V rows as the cache stores them."""
+        if not self.kv_q:
+            return k, v
+        return kvquant.k_stored(k), kvquant.v_stored(v)
+
     def _append(self, s: int, start: int, aux, toks) -> None:
         toks = np.asarray(toks, dtype=np.int64).reshape(-1)
         T = toks.shape[0]
@@ -209,6 +223,7 @@ class DrafterOracle:
         f = self.encode([np.asarray(a, dtype=np.float64).reshape(T, self.n) for a in aux])
         cat = self.input_cat(f, toks)
         _, k, v = self.qkv(cat, start + np.arange(T))
+        k, v = self._kv_rows(k, v)
         self.K[s][start:start + T] = k
         self.V[s][start:start + T] = v
 
