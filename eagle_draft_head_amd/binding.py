@@ -19,7 +19,7 @@ OK, E_INVAL, E_SHAPE, E_UNSUPPORTED, E_CAPACITY, E_STATE, E_HIP, E_OOM = 0, -1, 
 KEEP_SPEC = 1
 STORED_BOUNDARY = 2
 ROUND_LOCAL = 4
-KV_F32, KV_BF16 = 0, 1
+KV_F32, KV_BF16, KV_Q8Q5 = 0, 1, 2
 WEIGHTS_BF16, WEIGHTS_I4 = 0, 1
 
 ERR_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_SHAPE: "E_SHAPE", E_UNSUPPORTED: "E_UNSUPPORTED",

@@ -241,6 +241,213 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_attn over quantized regions (q8_0 K, q5_1 V; layout in kernels.hpp).  A lane
+// holds 8 consecutive dims of a row, inside one block of 32: per row it loads 8 K
+// codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and its
+// V block's (D, M).  The K dot product is D_k * (sum_e code_e q_e - 128 sum_e q_e)
+// (codes are stored + 128, sum_e q_e per lane precomputed); V enters as
+// p D_v q_e per element plus p M_v once per row, added to every element at the end.
+// The block whose split holds row T - 1 first quantizes that row from kv_new into
+// the cache (other blocks never read it).
+template <int HD, int G>
+__global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
+  constexpr int LPR = HD / kAttnLaneElems;  // lanes per row
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * kAttnWaves;
+  constexpr int kDepth = 4;
+  __shared__ float obuf[kAttnWaves][G][HD];
+  __shared__ float s_M[kAttnWaves][G], s_L[kAttnWaves][G];
+
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int slot = lane / LPR, sub = lane % LPR;
+  const int T = a.T, nkv = a.n_head_kv, cap = a.cap;
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  if (r0 >= T) return;
+  const uint8_t* kreg = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vreg = static_cast<const uint8_t*>(a.v_cache);
+  if (a.kv_new && r1 == T) {
+    // quantize the new row of this KV head: K dims then V dims, one per lane
+    for (int i0 = 0; i0 < 2 * HD; i0 += blockDim.x) {
+      const int i = i0 + threadIdx.x;
+      const bool on = i < 2 * HD;  // whole groups of 32
+      const bool is_k = i < HD;
+      const int dim = is_k ? i : i - HD;
+      const float x = on ? a.kv_new[(is_k ? 0 : nkv * HD) + kvh * HD + dim] : 0.f;
+      const KvqAt at(nkv, cap, HD, kvh, T - 1);
+      kvq_store(x, is_k, dim, const_cast<uint8_t*>(kreg), const_cast<uint8_t*>(vreg), at, on);
+    }
+    __threadfence();
+    __syncthreads();
+  }
+  const bool direct = S == 1;
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  // per-lane bases: row r of this head at kc + r * HD etc.
+  const size_t hr0 = (size_t)kvh * cap, all = (size_t)nkv * cap;
+  const uint8_t* kc = kreg + hr0 * HD + sub * 8;
+  const uint8_t* ks = kreg + all * HD + hr0 * (HD / 32) * 2 + (sub >> 2) * 2;
+  const uint8_t* vn = vreg + hr0 * (HD / 2) + sub * 4;
+  const uint8_t* vh = vreg + all * (HD / 2) + hr0 * (HD / 8) + sub;
+  const uint8_t* vd = vreg + all * (HD / 2 + HD / 8) + hr0 * (HD / 32) * 4 + (sub >> 2) * 4;
+
+  const int off = wv * RPW + slot;
+  const int rlast = r1 - 1;
+  uint2 kq[kDepth];
+  uint32_t kd[kDepth], vq[kDepth], vb[kDepth], vm[kDepth];
+  auto load_row = [&](int i, int row) {
+    row = min(row, rlast);
+    kq[i] = *reinterpret_cast<const uint2*>(kc + (size_t)row * HD);
+    kd[i] = *reinterpret_cast<const uint16_t*>(ks + (size_t)row * (HD / 32) * 2);
+    vq[i] = *reinterpret_cast<const uint32_t*>(vn + (size_t)row * (HD / 2));
+    vb[i] = vh[(size_t)row * (HD / 8)];
+    vm[i] = *reinterpret_cast<const uint32_t*>(vd + (size_t)row * (HD / 32) * 4);
+  };
+  int rb = r0;
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) load_row(i, rb + off + i * RPB);
+  float qv[G][kAttnLaneElems], qs[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qs[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e) {
+      qv[g][e] = a.q[(size_t)(kvh * G + g) * HD + sub * 8 + e] * scale;
+      qs[g] += qv[g][e];
+    }
+    qs[g] *= -128.f;
+  }
+  float m[G], mr[G], l[G], sm[G], acc[G][kAttnLaneElems];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    mr[g] = -INFINITY;
+    l[g] = 0.f;
+    sm[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = 0.f;
+  }
+  auto step = [&](int i, int row) {
+    // K codes (stored + 128) and V codes (low nibbles; the high bits moved to bit 4
+    // of each byte: byte j of (b & mask) + (0x80 - 2^j) carries bit j into bit 7)
+    uint32_t k0 = kq[i].x, k1 = kq[i].y;
+    uint32_t nb = vq[i];
+    const uint32_t hr = vb[i] * 0x01010101u;
+    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(nb));  // one v_cvt_f32_ubyteN per byte
+    const uint32_t c_lo = (nb & 0x0F0F0F0Fu) | ((((hr & 0x08040201u) + 0x787C7E7Fu) & 0x80808080u) >> 3);
+    const uint32_t c_hi = ((nb >> 4) & 0x0F0F0F0Fu) | ((((hr & 0x80402010u) + 0x00406070u) & 0x80808080u) >> 3);
+    const float Dk = f16_bits_to_f32(uint16_t(kd[i]));
+    const float Dv = f16_bits_to_f32(uint16_t(vm[i] & 0xFFFFu)), Mv = f16_bits_to_f32(uint16_t(vm[i] >> 16));
+    const float kf[8] = {float(k0 & 0xFFu), float((k0 >> 8) & 0xFFu), float((k0 >> 16) & 0xFFu), float(k0 >> 24),
+                         float(k1 & 0xFFu), float((k1 >> 8) & 0xFFu), float((k1 >> 16) & 0xFFu), float(k1 >> 24)};
+    const float vf[8] = {float(c_lo & 0xFFu), float((c_lo >> 8) & 0xFFu), float((c_lo >> 16) & 0xFFu), float(c_lo >> 24),
+                         float(c_hi & 0xFFu), float((c_hi >> 8) & 0xFFu), float((c_hi >> 16) & 0xFFu), float(c_hi >> 24)};
+    load_row(i, row + kDepth * RPB);
+    float d[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float t = qs[g];
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) t = fmaf(kf[e], qv[g][e], t);
+      d[g] = t * Dk;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float sc = d[g];
+      if (sc > mr[g]) {
+        const float fo = __builtin_amdgcn_exp2f(m[g] - sc);
+        l[g] *= fo;
+        sm[g] *= fo;
+#pragma unroll
+        for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
+        m[g] = sc;
+        mr[g] = sc + kRescale;
+      }
+      const float p = __builtin_amdgcn_exp2f(sc - m[g]);
+      l[g] += p;
+      sm[g] = fmaf(p, Mv, sm[g]);
+      const float pd = p * Dv;
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(pd, vf[e], acc[g][e]);
+    }
+  };
+  for (; rb + kDepth * RPB <= r1; rb += kDepth * RPB) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) step(i, rb + off + i * RPB);
+  }
+  if (rb < r1) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int rr = rb + off + i * RPB;
+      if (rr >= r1) break;
+      step(i, rr);
+    }
+  }
+  // the V minimum's share goes to every element of the lane
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] += sm[g];
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mw = wave_max(m[g]);
+    if (lane == 0) s_M[wv][g] = mw;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float Mb = s_M[0][g];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    const float f = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - Mb);
+    l[g] *= f;
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= f;
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      l[g] += __shfl_xor(l[g], o, kWave);
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, kWave);
+    }
+  if (slot == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][sub * 8 + e] = acc[g][e];
+      if (sub == 0) s_L[wv][g] = l[g];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
+    const int g = i / HD, dd = i - g * HD;
+    float v = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      v += obuf[w][g][dd];
+      L += s_L[w][g];
+    }
+    const int h = kvh * G + g;
+    if (direct) a.out[(size_t)h * HD + dd] = v / L;
+    else a.part_o[((size_t)h * S + s) * HD + dd] = v;
+  }
+  if (direct) return;
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float Mb = s_M[0][g], L = 0.f;
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    for (int w = 0; w < kAttnWaves; ++w) L += s_L[w][g];
+    const int h = kvh * G + g;
+    a.part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
+    a.part_ml[((size_t)h * S + s) * 2 + 1] = L;
+  }
+}
+
 // One block of hd threads per query head: o = sum_s w_s o_s with
 // w_s = 2^(m_s - M) / sum_z l_z 2^(m_z - M) (m in base 2, M the largest m_s).
 // Splits are taken kCombineRegs at a time: this thread's column of the group's
@@ -471,11 +678,46 @@ hipError_t launch_attn_batched(const AttnArgs& a, int m, uint16_t* out_hi, uint1
   return hipGetLastError();
 }
 
+template <int HD>
+static hipError_t launch_q_hd(const AttnArgs& a, int G, int chunk, int S, hipStream_t s) {
+  dim3 grid(S, a.n_head_kv), block(64 * kAttnWaves);
+#define E3_ATTN_CASE(GG)                                                      \
+  case GG:                                                                  \
+    hipLaunchKernelGGL((k_attn_q<HD, GG>), grid, block, 0, s, a, chunk, S); \
+    break;
+  switch (G) {
+    E3_ATTN_CASE(1)
+    E3_ATTN_CASE(2)
+    E3_ATTN_CASE(3)
+    E3_ATTN_CASE(4)
+    E3_ATTN_CASE(5)
+    E3_ATTN_CASE(6)
+    E3_ATTN_CASE(7)
+    E3_ATTN_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef E3_ATTN_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S, HD,
+                     a.out);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batched) return hipErrorInvalidValue;
   int chunk, S;
   pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   const int G = a.n_head / a.n_head_kv;
+  if (a.kv_q) {
+    switch (a.head_dim) {
+      case 64: return launch_q_hd<64>(a, G, chunk, S, s);
+      case 128: return launch_q_hd<128>(a, G, chunk, S, s);
+      case 256: return launch_q_hd<256>(a, G, chunk, S, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   return a.kv_f32 ? launch_kt<float>(a, G, chunk, S, s) : launch_kt<uint16_t>(a, G, chunk, S, s);
 }
 

@@ -1,6 +1,7 @@
 // Shared device/host helpers of the gfx950 drafter engine.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -235,5 +236,67 @@ __device__ __forceinline__ void kv_store(void* base, size_t idx, float v, int f3
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---- quantized draft KV (q8_0 K rows, q5_1 V rows; layout in kernels.hpp KvqRef) ----
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// byte offsets of row `pos` of KV head `head` in a region of nkv heads x cap rows
+struct KvqAt {
+  size_t k_code, k_scale, v_nib, v_hi, v_dm;
+  __device__ KvqAt(int nkv, int cap, int hd, int head, int pos) {
+    const size_t hr = (size_t)head * cap + pos, all = (size_t)nkv * cap;
+    k_code = hr * hd;
+    k_scale = all * hd + hr * (hd / 32) * 2;
+    v_nib = hr * (hd / 2);
+    v_hi = all * (hd / 2) + hr * (hd / 8);
+    v_dm = all * (hd / 2 + hd / 8) + hr * (hd / 32) * 4;
+  }
+};
+
+// Quantize and store one value per lane.  The lanes come in aligned groups of 32
+// holding dims [32b, 32b + 32) of one head row, K (q8_0) or V (q5_1); every lane of
+// the wave calls it (the group reductions are shuffles); `on` lanes store.
+// q8_0: D = fp16(max|x| / 127), q = clamp(rint(x / D), -127, 127), stored q + 128;
+// q5_1: D = fp16((max - min) / 31), M = fp16(min), q = clamp(rint((x - M) / D), 0, 31);
+// D == 0 gives code 0.  Subtraction and divisions are IEEE fp32.
+__device__ __forceinline__ void kvq_store(float x, bool is_k, int dim, uint8_t* kreg, uint8_t* vreg,
+                                          const KvqAt& at, bool on) {
+  float amax = fabsf(x), mn = x, mx = x;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    mn = fminf(mn, __shfl_xor(mn, o, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  }
+  const int j = dim & 7;
+  if (is_k) {
+    const uint16_t Db = f32_to_f16_bits(__fdiv_rn(amax, 127.f));
+    const float D = f16_bits_to_f32(Db);
+    const float q = D > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x, D)), -127.f), 127.f) : 0.f;
+    if (on) {
+      kreg[at.k_code + dim] = uint8_t(int(q) + 128);
+      if ((dim & 31) == 0) *reinterpret_cast<uint16_t*>(kreg + at.k_scale + (dim >> 5) * 2) = Db;
+    }
+  } else {
+    const uint16_t Db = f32_to_f16_bits(__fdiv_rn(mx - mn, 31.f));
+    const uint16_t Mb = f32_to_f16_bits(mn);
+    const float D = f16_bits_to_f32(Db), M = f16_bits_to_f32(Mb);
+    const float qf = D > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x - M, D)), 0.f), 31.f) : 0.f;
+    const uint32_t q = uint32_t(qf);
+    // dims j and j + 4 of a group of 8 share a nibble byte; the 8 high bits one byte
+    const uint32_t partner = __shfl_xor(q, 4, kWave);
+    uint32_t hb = (q >> 4) << j;
+    hb |= __shfl_xor(hb, 1, kWave);
+    hb |= __shfl_xor(hb, 2, kWave);
+    hb |= __shfl_xor(hb, 4, kWave);
+    if (on) {
+      if (j < 4) vreg[at.v_nib + (dim >> 3) * 4 + j] = uint8_t((q & 15u) | ((partner & 15u) << 4));
+      if (j == 0) vreg[at.v_hi + (dim >> 3)] = uint8_t(hb);
+      if ((dim & 31) == 0)
+        *reinterpret_cast<uint32_t*>(vreg + at.v_dm + (dim >> 5) * 4) = uint32_t(Db) | (uint32_t(Mb) << 16);
+    }
+  }
+}
 
 }  // namespace e3

@@ -75,6 +75,8 @@ struct eagle3_ctx {
   int lm_grid = 0;
   char* kv = nullptr;
   int kv_f32 = 1;
+  int kv_q = 0;             // quantized K/V regions (q8_0 K, q5_1 V); elements are bytes
+  float* kv_stage = nullptr;  // kv_q: the chain step's new K/V row in fp32 [2][kvd]
   size_t kv_esize = 4;      // bytes per cache element
   size_t kv_seq_elems = 0;  // K + V elements per sequence
 
@@ -245,8 +247,10 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (!(cfg->rms_eps >= 0.f) || !std::isfinite(cfg->rms_eps)) return bad("rms_eps must be >= 0", EAGLE3_E_INVAL);
   if (int64_t(cfg->max_ctx) + 1 > (int64_t(1) << 30)) return bad("max_ctx too large", EAGLE3_E_UNSUPPORTED);
   if (cfg->max_gamma > 64) return bad("max_gamma above 64", EAGLE3_E_UNSUPPORTED);
-  if (cfg->kv_dtype != EAGLE3_KV_F32 && cfg->kv_dtype != EAGLE3_KV_BF16)
+  if (cfg->kv_dtype != EAGLE3_KV_F32 && cfg->kv_dtype != EAGLE3_KV_BF16 && cfg->kv_dtype != EAGLE3_KV_Q8Q5)
     return bad("unknown kv_dtype", EAGLE3_E_INVAL);
+  if (cfg->kv_dtype == EAGLE3_KV_Q8Q5 && cfg->max_seqs != 1)
+    return bad("quantized KV: batch-1 drafting only (max_seqs 1)", EAGLE3_E_UNSUPPORTED);
   if (cfg->weight_format != EAGLE3_WEIGHTS_BF16 && cfg->weight_format != EAGLE3_WEIGHTS_I4)
     return bad("unknown weight_format", EAGLE3_E_INVAL);
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
@@ -386,8 +390,11 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->nrm_fin, size_t(n)));
   E3_TRY(dalloc(c, &c->d2t, size_t(dv)));
   c->kv_f32 = cfg->kv_dtype == EAGLE3_KV_F32;
-  c->kv_esize = c->kv_f32 ? 4 : 2;
-  c->kv_seq_elems = size_t(2) * kvd * size_t(c->cap);
+  c->kv_q = cfg->kv_dtype == EAGLE3_KV_Q8Q5;
+  c->kv_esize = c->kv_f32 ? 4 : (c->kv_q ? 1 : 2);
+  c->kv_seq_elems = c->kv_q ? 2 * e3::kvq_region_bytes(int(c->nkv), c->cap, int(c->hd))
+                            : size_t(2) * kvd * size_t(c->cap);
+  if (c->kv_q) E3_TRY(dalloc(c, &c->kv_stage, size_t(2) * kvd));
   E3_TRY(dalloc(c, &c->kv, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize));
 
   E3_TRY(dalloc(c, &c->x1, size_t(n)));
@@ -425,7 +432,8 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->bnd_w, size_t(cfg->max_seqs) * n));
   E3_TRY(dalloc(c, &c->bnd_ssq, size_t(cfg->max_seqs)));
   c->cap_local = cfg->max_gamma;
-  c->kv_local_elems = size_t(2) * c->nkv * c->cap_local * c->hd;
+  c->kv_local_elems = c->kv_q ? 2 * e3::kvq_region_bytes(int(c->nkv), c->cap_local, int(c->hd))
+                             : size_t(2) * c->nkv * c->cap_local * c->hd;
   E3_TRY(dalloc(c, &c->kv_local, size_t(cfg->max_seqs) * c->kv_local_elems * c->kv_esize));
   E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
 
@@ -441,7 +449,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
   E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
   E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));
-  if (c->kv_f32) {
+  if (c->kv_f32 || c->kv_q) {  // fp32-grade K/V rows (quantized ones are decided from them)
     E3_TRY(dalloc(c, &c->tf_A_lo, size_t(c->tf_rows) * 3 * n));
     E3_TRY(dalloc(c, &c->tf_cat16_lo, size_t(c->tf_rows) * 2 * n));
   }
@@ -625,6 +633,12 @@ int eagle3_kv_read(const eagle3_ctx* cctx, int32_t seq, int32_t row0, int32_t nr
     return set_err(ctx, EAGLE3_E_INVAL, "rows outside the allocation");
   if (nrows == 0) return EAGLE3_OK;
   hipStream_t s = as_stream(stream);
+  if (ctx->kv_q) {  // quantized regions: dequantized to fp32
+    E3_HIP(ctx, e3::launch_kvq_read(ctx->k_of(seq), ctx->v_of(seq), int(ctx->nkv), ctx->cap, int(ctx->hd),
+                                    row0, nrows, static_cast<float*>(k_dev), static_cast<float*>(v_dev), s),
+           "kv_read");
+    return EAGLE3_OK;
+  }
   // cache is [nkv][cap][hd]; output is [nrows][nkv][hd], same element type
   const size_t rowb = size_t(ctx->hd) * ctx->kv_esize;
   for (int half = 0; half < 2; ++half) {
@@ -776,7 +790,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       auto flush = [&]() -> int {
         if (ss.n == 0) return EAGLE3_OK;
         E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, ss, c->nkv, c->hd, c->rot, c->inv_freq,
-                                      c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s), "tf store");
+                                      c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s, c->kv_q), "tf store");
         ss = e3::StoreSegs{};
         return EAGLE3_OK;
       };
@@ -1171,6 +1185,10 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       qa.w_in = ctx->nrm_in; qa.pos = pos; qa.row = row; qa.q_out = ctx->q;
       qa.k_cache = kc; qa.v_cache = vc; qa.cap = cap;
       qa.kv_f32 = ctx->kv_f32;
+      if (ctx->kv_q) {  // the new row goes to the fp32 stage; attention quantizes it
+        qa.k_cache = ctx->kv_stage; qa.v_cache = ctx->kv_stage + ctx->kvd;
+        qa.cap = 1; qa.row = 0; qa.kv_f32 = 1;
+      }
       {
         ProfScope ps(ctx, 2, s);
         E3_HIP(ctx, e3::launch_qkv(qa, ctx->gcfg[e3::kGemvQkv], s), "qkv");
@@ -1178,6 +1196,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       e3::AttnArgs aa{};
       aa.q = ctx->q; aa.k_cache = kc; aa.v_cache = vc; aa.cap = cap;
       aa.kv_f32 = ctx->kv_f32;
+      aa.kv_q = ctx->kv_q; aa.kv_new = ctx->kv_q ? ctx->kv_stage : nullptr;
       aa.T = row + 1; aa.n_head = ctx->nh; aa.n_head_kv = ctx->nkv; aa.head_dim = ctx->hd;
       aa.part_o = ctx->part_o; aa.part_ml = ctx->part_ml; aa.out = ctx->ao;
       {

@@ -144,11 +144,24 @@ struct BatchRows {
 };
 
 // ---- attention over the draft KV (split over context, LSE combine) ----
+// ---- quantized draft KV (EAGLE3_KV_Q8Q5) ----
+// A sequence's K region holds, in bytes: codes [nkv][cap][hd] (q8_0 code + 128), then
+// fp16 scales [nkv][cap][hd / 32].  Its V region: code nibbles [nkv][cap][hd / 2] (per
+// 8 dims, byte j holds dim j's low 4 bits and dim j + 4's in its high half), high bits
+// [nkv][cap][hd / 8] (bit j of byte c is bit 4 of dim 8c + j), then (D, M) fp16 pairs
+// [nkv][cap][hd / 32] (one u32, D in the low half).  Both regions are
+// kvq_region_bytes long: 34 bytes per 32 K values and 24 per 32 V values, as in the
+// pages' block formats, with the V region padded to the K region's size.
+inline size_t kvq_region_bytes(int nkv, int cap, int hd) { return size_t(nkv) * cap * (hd / 32) * 34; }
+
 struct AttnArgs {
   const float* q;          // [n_head * hd], roped
-  const void* k_cache;     // [n_head_kv][cap][hd], fp32 or bf16
+  const void* k_cache;     // [n_head_kv][cap][hd], fp32 or bf16 (or a quantized K region)
   const void* v_cache;
   int kv_f32;
+  int kv_q;                // quantized regions (q8_0 K, q5_1 V)
+  const float* kv_new;     // kv_q: the new row T - 1 in fp32, K [nkv][hd] then V; the
+                           // block of its split quantizes it into the cache first
   int cap, T;              // rows 0..T-1 attended
   int n_head, n_head_kv, head_dim;
   float* part_o;           // [n_head][S][hd]
@@ -335,9 +348,13 @@ struct StoreSegs {
 // repacked, row stride 2*kvd, split stride p_split); rotate k at the row's position
 // and store it into that cache row of its slot (slot s starts s * seq_elems
 // elements past kv; K then V, each [n_head_kv][cap][head_dim]).
+// (kv_q: quantized regions; seq_elems is then the bytes per slot, K region then V)
 hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const StoreSegs& segs,
                            int n_head_kv, int head_dim, int rope_dim, const double* inv_freq, void* kv,
-                           size_t seq_elems, int cap, int kv_f32, hipStream_t s);
+                           size_t seq_elems, int cap, int kv_f32, hipStream_t s, int kv_q = 0);
+// rows [row0, row0 + nrows) of quantized K/V regions as fp32 [nrows][nkv][hd]
+hipError_t launch_kvq_read(const void* kreg, const void* vreg, int nkv, int cap, int hd, int row0,
+                           int nrows, float* k_out, float* v_out, hipStream_t s);
 
 // C[z][M][N] (fp32) = (A_hi + A_lo)[M, kz-range] . B[N, kz-range]^T on bf16 MFMA
 // (A_lo may be NULL: one product).  Row strides lda, ldb (elements); K split

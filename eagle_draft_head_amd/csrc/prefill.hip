@@ -243,15 +243,108 @@ __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, i
   }
 }
 
+// k_tf_store for quantized regions: a block's 256 pairs are 512 consecutive values of
+// the [k | v] row, i.e. whole heads (head_dim divides 512); they are rotated into
+// LDS at their final dims, then quantized 32 dims at a time (one value per lane).
+__global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P, int splits,
+                                                    size_t p_split, const StoreSegs segs, int nkv,
+                                                    int hd, int rope_dim,
+                                                    const double* __restrict__ inv_freq,
+                                                    uint8_t* __restrict__ kv, size_t seq_bytes,
+                                                    int cap) {
+  __shared__ float srow[512];
+  const int t = segs.row0[0] + blockIdx.x;
+  int sg = 0;
+  while (sg + 1 < segs.n && t >= segs.row0[sg + 1]) ++sg;
+  const int kvd = nkv * hd;
+  const int pos = segs.pos0[sg] + (t - segs.row0[sg]);
+  uint8_t* kreg = kv + (size_t)segs.slot[sg] * seq_bytes;
+  uint8_t* vreg = kreg + seq_bytes / 2;
+  const float* row = P + (size_t)t * 2 * kvd;
+  const int v0 = blockIdx.y * 512;  // this block's first value of the [k | v] row
+  {
+    const int r = v0 + 2 * threadIdx.x;
+    if (r < 2 * kvd) {
+      float y0 = sum_splits(row + r, splits, p_split);
+      float y1 = sum_splits(row + r + 1, splits, p_split);
+      const bool is_k = r < kvd;
+      const int rr = is_k ? r : r - kvd;
+      const int li = rr % hd;
+      int d0 = li, d1 = li + 1;
+      if (is_k && li < rope_dim) {
+        const int i = li >> 1;
+        d0 = i;
+        d1 = i + (rope_dim >> 1);
+        float c, sv;
+        rope_cs(pos, inv_freq[i], &c, &sv);
+        const float t0 = y0 * c - y1 * sv, t1 = y1 * c + y0 * sv;
+        y0 = t0;
+        y1 = t1;
+      }
+      const int hb = r - li - v0;  // the head's first value within the block
+      srow[hb + d0] = y0;
+      srow[hb + d1] = y1;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += blockDim.x) {  // two rounds, every lane
+    const int v = v0 + i;
+    const bool on = v < 2 * kvd;  // whole groups of 32 are on or off
+    const bool is_k = v < kvd;
+    const int rr = is_k ? v : v - kvd;
+    const int head = rr / hd, dim = rr - head * hd;
+    const KvqAt at(nkv, cap, hd, on ? head : 0, pos);
+    kvq_store(on ? srow[i] : 0.f, is_k, dim, kreg, vreg, at, on);
+  }
+}
+
 hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const StoreSegs& segs,
                            int n_head_kv, int head_dim, int rope_dim, const double* inv_freq, void* kv,
-                           size_t seq_elems, int cap, int kv_f32, hipStream_t s) {
+                           size_t seq_elems, int cap, int kv_f32, hipStream_t s, int kv_q) {
   if (segs.n < 1 || segs.n > kStoreSegs) return hipErrorInvalidValue;
   const int rows = segs.row0[segs.n] - segs.row0[0];
   if (rows <= 0) return hipSuccess;
+  if (kv_q) {
+    if (head_dim % 32 || 512 % head_dim) return hipErrorInvalidValue;
+    const int blocks = (2 * n_head_kv * head_dim + 511) / 512;
+    hipLaunchKernelGGL(k_tf_store_q, dim3(rows, blocks), dim3(256), 0, s, P, splits, p_split, segs,
+                       n_head_kv, head_dim, rope_dim, inv_freq, static_cast<uint8_t*>(kv), seq_elems, cap);
+    return hipGetLastError();
+  }
   const int pair_blocks = (n_head_kv * head_dim + 255) / 256;
   hipLaunchKernelGGL(k_tf_store, dim3(rows, pair_blocks), dim3(256), 0, s, P, splits, p_split, segs, n_head_kv,
                      head_dim, rope_dim, inv_freq, static_cast<char*>(kv), seq_elems, cap, kv_f32);
+  return hipGetLastError();
+}
+
+// One thread per value: rows [row0, row0 + nrows) of quantized regions to fp32
+// [row][nkv][hd] (K: D * (code - 128); V: fmaf(D, q, M)).
+__global__ __launch_bounds__(256) void k_kvq_read(const uint8_t* __restrict__ kreg,
+                                                  const uint8_t* __restrict__ vreg, int nkv, int cap,
+                                                  int hd, int row0, int nrows, float* __restrict__ ko,
+                                                  float* __restrict__ vo) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t per = (size_t)nkv * hd;
+  if (i >= per * nrows) return;
+  const int r = int(i / per), rem = int(i - (size_t)r * per);
+  const int head = rem / hd, dim = rem - head * hd;
+  const KvqAt at(nkv, cap, hd, head, row0 + r);
+  const float Dk = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(kreg + at.k_scale + (dim >> 5) * 2));
+  ko[i] = Dk * float(int(kreg[at.k_code + dim]) - 128);
+  const int j = dim & 7;
+  const uint8_t nb = vreg[at.v_nib + (dim >> 3) * 4 + (j & 3)];
+  const uint32_t q = uint32_t(j < 4 ? (nb & 15) : (nb >> 4)) | (((uint32_t(vreg[at.v_hi + (dim >> 3)]) >> j) & 1u) << 4);
+  const uint32_t dm = *reinterpret_cast<const uint32_t*>(vreg + at.v_dm + (dim >> 5) * 4);
+  vo[i] = fmaf(f16_bits_to_f32(uint16_t(dm & 0xFFFFu)), float(q), f16_bits_to_f32(uint16_t(dm >> 16)));
+}
+
+hipError_t launch_kvq_read(const void* kreg, const void* vreg, int nkv, int cap, int hd, int row0,
+                           int nrows, float* k_out, float* v_out, hipStream_t s) {
+  const size_t total = (size_t)nkv * hd * nrows;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_kvq_read, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(kreg), static_cast<const uint8_t*>(vreg), nkv, cap, hd,
+                     row0, nrows, k_out, v_out);
   return hipGetLastError();
 }
 

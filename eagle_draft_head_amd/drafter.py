@@ -88,7 +88,7 @@ class Drafter:
 
     def kv_read(self, seq: int, row0: int, nrows: int):
         g = self.geom
-        dt = torch.float32 if self.kv_dtype == B.KV_F32 else torch.bfloat16
+        dt = torch.bfloat16 if self.kv_dtype == B.KV_BF16 else torch.float32
         k = torch.empty((nrows, g.n_head_kv, g.head_dim), dtype=dt, device="cuda")
         v = torch.empty_like(k)
         B.eagle3_kv_read(self.ctx, seq, row0, nrows, k, v)

@@ -76,7 +76,7 @@ typedef struct {
   int32_t max_ctx;       /* admission bound per sequence; max_ctx + 1 rows are allocated */
   int32_t max_gamma;     /* largest chain length accepted */
   int32_t max_seqs;      /* sequence slots */
-  int32_t kv_dtype;      /* EAGLE3_KV_F32 (default) or EAGLE3_KV_BF16, see below */
+  int32_t kv_dtype;      /* EAGLE3_KV_F32 (default), EAGLE3_KV_BF16 or EAGLE3_KV_Q8Q5 */
   int32_t weight_format; /* EAGLE3_WEIGHTS_BF16 (default) or EAGLE3_WEIGHTS_I4, see below */
 } eagle3_config;
 
@@ -87,6 +87,18 @@ typedef struct {
    that alone moves draft logits by about 1-2e-2 relative to exact arithmetic. */
 #define EAGLE3_KV_F32 0
 #define EAGLE3_KV_BF16 1
+/* EAGLE3_KV_Q8Q5: K rows in q8_0 and V rows in q5_1, blocks of 32 values along
+   head_dim (memra_engine `eagle.rs`, `Eagle3Scratch` doc and `attn`: the draft
+   layer appends quantized K/V rows and decode attention reads the quantized views;
+   34 and 24 bytes per block by default).  The formulas are our reading: q8_0
+   D = fp16(max|x| / 127), q = clamp(rint(x / D), -127, 127), value D q; q5_1
+   D = fp16((max - min) / 31), M = fp16(min), q = clamp(rint((x - M) / D), 0, 31),
+   value D q + M; every decision in fp32 on the fp32 row.  Rows are quantized once,
+   when appended (teacher-forced rows as they are stored, a chain step's row by the
+   attention block that owns it), and every read sees the quantized values, the new
+   row's included.  Batch-1 drafting only (max_seqs 1); prefill activations keep the
+   fp32-grade path of EAGLE3_KV_F32. */
+#define EAGLE3_KV_Q8Q5 2
 
 /* Projection-weight format (ExecuTorch PR #20154 names a weight-stationary INT4
    GEMM for small M; the format is our reading).  EAGLE3_WEIGHTS_I4: eagle3_load
@@ -216,7 +228,8 @@ int eagle3_kv_len(const eagle3_ctx *ctx, int32_t seq, int32_t *committed, int32_
 
 /* Copy draft-KV rows [row0, row0 + nrows) of a sequence into caller buffers
    (dev [nrows, n_head_kv, head_dim] each in the cache's element type, fp32 or
-   bf16 per kv_dtype; K rows roped).  Inspection and tests; rows need not be live. */
+   bf16 per kv_dtype, and fp32 dequantized values for EAGLE3_KV_Q8Q5; K rows
+   roped).  Inspection and tests; rows need not be live. */
 int eagle3_kv_read(const eagle3_ctx *ctx, int32_t seq, int32_t row0, int32_t nrows,
                    void *k_dev, void *v_dev, void *stream);
 

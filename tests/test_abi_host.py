@@ -194,7 +194,9 @@ def test_load_rejects_d2t_problems(d2t_tiny):
                                          (dict(max_ctx=0), B.E_INVAL),
                                          (dict(weight_format=7), B.E_INVAL),
                                          (dict(weight_format=B.WEIGHTS_I4, max_seqs=2), B.E_UNSUPPORTED),
-                                         (dict(weight_format=B.WEIGHTS_I4, n_ff=776), B.E_UNSUPPORTED)])
+                                         (dict(weight_format=B.WEIGHTS_I4, n_ff=776), B.E_UNSUPPORTED),
+                                         (dict(kv_dtype=3), B.E_INVAL),
+                                         (dict(kv_dtype=B.KV_Q8Q5, max_seqs=2), B.E_UNSUPPORTED)])
 def test_load_rejects_unsupported_geometry(d2t_tiny, change, code):
     cfg = B.make_config(TINY, 100)
     for k, v in change.items():
