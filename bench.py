@@ -19,7 +19,7 @@ average duration give `roofline.achieved`.  The CPU oracle is timed on a bounded
 sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--boundary stored|taps] [--drafter persistent|round-local] [--kv f32|bf16]
+       [--boundary stored|taps] [--drafter persistent|round-local] [--kv f32|bf16|q8q5]
        [--no-cpu] [--kernel lm_head|gate_up|qkv|down|o_proj|attention|encode]
 """
 from __future__ import annotations
@@ -68,6 +68,8 @@ def committed_traffic(kernel: str):
 
 # HBM bytes per projection weight: bf16, or int4 codes plus one bf16 scale per 32
 WB_BF16, WB_I4 = 2.0, 0.5 + 2.0 / 32
+# KV bytes per element, K and V averaged: q8_0 K is 34 bytes per 32 values, q5_1 V 24
+KV_BYTES = {"f32": 4.0, "bf16": 2.0, "q8q5": (34.0 + 24.0) / 64}
 WB = WB_BF16
 
 
@@ -130,7 +132,7 @@ def main():
     ap.add_argument("--kernel", default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=3)
-    ap.add_argument("--kv", choices=["f32", "bf16"], default="f32",
+    ap.add_argument("--kv", choices=["f32", "bf16", "q8q5"], default="f32",
                     help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
@@ -188,7 +190,7 @@ def main():
     else:
         L_at = [L] * nsteps
     max_ctx = max(L, max(L_at)) + gamma + 64
-    kv_dtype = B.KV_BF16 if args.kv == "bf16" else B.KV_F32
+    kv_dtype = {"bf16": B.KV_BF16, "q8q5": B.KV_Q8Q5}.get(args.kv, B.KV_F32)
     i4 = args.weights == "int4"
     global WB
     WB = WB_I4 if i4 else WB_BF16
@@ -309,7 +311,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = gamma * args.steps / elapsed
     k_avg_s = (k_ms / 1e3) / max(k_launches, 1)
-    kvb = 2 if args.kv == "bf16" else 4
+    kvb = KV_BYTES[args.kv]
     k_bytes = kernel_bytes(cfg, args.kernel, 0 if local else L, kvb)
     achieved = k_bytes / k_avg_s / 1e9
     if local:
@@ -391,8 +393,8 @@ def run_batched(args, cfg):
     """Batched drafting: one draft_chain over all sequences per step, then a packed
     rebuild of a_b + 1 rows per sequence (a_b seeded on [0, gamma]) and a rewind of
     every sequence to its seeded length."""
-    if args.weights != "bf16":
-        print(json.dumps({"error": "int4 weights are a batch-1 mode (the batched GEMMs stream bf16)"}))
+    if args.weights != "bf16" or args.kv == "q8q5":
+        print(json.dumps({"error": "int4 weights and q8q5 KV are batch-1 modes"}))
         sys.exit(2)
     import numpy as np
     import torch
