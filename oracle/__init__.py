@@ -27,7 +27,7 @@ pages' own text (which norm goes where, the concat order, the pre-norm
 residual, the token/feature pairing) — no golden tensors, checkpoints or the
 vLLM code the memra module doc calls authoritative are available.
 """
-from .numerics import (argmax_first, attention_causal, attention_decode,
+from .numerics import (argmax_first, attention_causal, attention_decode, attention_verify,
                        bf16_bits_to_f64, rms_norm, rope_neox_partial, silu)
 from .drafter import DrafterOracle, StatelessChain
 from .ledger import Ledger, LedgerError
@@ -37,7 +37,7 @@ from . import int4, kvquant
 from .loop import greedy_plain, greedy_speculative
 
 __all__ = [
-    "argmax_first", "attention_causal", "attention_decode", "bf16_bits_to_f64",
+    "argmax_first", "attention_causal", "attention_decode", "attention_verify", "bf16_bits_to_f64",
     "rms_norm", "rope_neox_partial", "silu", "DrafterOracle", "StatelessChain",
     "Ledger", "LedgerError", "resolve_rope_dim", "TrunkOracle", "greedy_plain",
     "greedy_speculative", "int4", "kvquant",

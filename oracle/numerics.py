@@ -92,3 +92,18 @@ def attention_causal(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     for t in range(T):
         out[t] = attention_decode(Q[t], K[: t + 1], V[: t + 1])
     return out
+
+
+def attention_verify(Q: np.ndarray, K: np.ndarray, V: np.ndarray, ctx: int) -> np.ndarray:
+    """Verify-window attention (ExecuTorch PR #20344 "split-K mid-M SDPA ... for
+    EAGLE-3 target_verify at long context"; PR #20156 description: one target
+    forward per round over the K-token verify window): M query rows whose K/V are
+    rows ctx..ctx+M-1 of the cache; query row m sees rows 0..ctx+m inclusive.
+
+    Q [M, n_head, hd]; K, V [>= ctx + M, n_head_kv, hd]  ->  O [M, n_head, hd]
+    """
+    M = Q.shape[0]
+    out = np.empty_like(Q, dtype=np.float64)
+    for m in range(M):
+        out[m] = attention_decode(Q[m], K[: ctx + m + 1], V[: ctx + m + 1])
+    return out

@@ -128,3 +128,25 @@ def test_attention_closed_forms():
 def test_argmax_lowest_index_on_ties():
     assert argmax_first(np.array([1.0, 3.0, 3.0, 2.0])) == 1
     assert argmax_first(np.array([-1.0])) == 0
+
+
+@pytest.mark.parametrize("nh,nkv,hd,ctx,M", [(4, 2, 64, 0, 4), (4, 2, 64, 37, 1), (8, 2, 32, 50, 5),
+                                             (6, 3, 16, 9, 8)])
+def test_verify_attention_against_torch_sdpa_with_a_window_mask(nh, nkv, hd, ctx, M):
+    # the verify window: query row m sees rows 0..ctx+m (torch SDPA, explicit mask)
+    from oracle import attention_verify
+    T = ctx + M
+    Q = rng.normal(0, 1, (M, nh, hd))
+    K = rng.normal(0, 1, (T + 3, nkv, hd))  # rows past the window are never read
+    V = rng.normal(0, 1, (T + 3, nkv, hd))
+    O = attention_verify(Q, K, V, ctx)
+    rep = nh // nkv
+    Kr = torch.from_numpy(np.repeat(K[:T], rep, axis=1)).permute(1, 0, 2)
+    Vr = torch.from_numpy(np.repeat(V[:T], rep, axis=1)).permute(1, 0, 2)
+    mask = torch.from_numpy(np.arange(T)[None, :] <= ctx + np.arange(M)[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(Q).permute(1, 0, 2), Kr, Vr,
+                                                           attn_mask=mask).permute(1, 0, 2).numpy()
+    assert np.allclose(O, ref, rtol=1e-10, atol=1e-12)
+    # and the window is the tail of causal self-attention over all T rows
+    Qf = np.concatenate([rng.normal(0, 1, (ctx, nh, hd)), Q])
+    assert np.allclose(attention_causal(Qf, K[:T], V[:T])[ctx:], O, rtol=1e-12, atol=1e-14)
