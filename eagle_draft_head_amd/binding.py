@@ -82,6 +82,10 @@ def library() -> ctypes.CDLL:
         "eagle3_kv_len": ([P, c_int32, POINTER(c_int32), POINTER(c_int32)], ctypes.c_int),
         "eagle3_kv_read": ([P, c_int32, c_int32, c_int32, P, P, P], ctypes.c_int),
         "eagle3_weights_i4_read": ([P, c_int32, P, P, P], ctypes.c_int),
+        "eagle3_verify_attention_workspace": ([c_int32, c_int32, c_int32, c_int32, c_int32, c_int32],
+                                              ctypes.c_size_t),
+        "eagle3_verify_attention": ([P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                     c_int32, P, P, ctypes.c_size_t, P], ctypes.c_int),
         "eagle3_last_error": ([P], c_char_p),
         "eagle3_profile_enable": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_profile_read": ([P, POINTER(c_double), POINTER(c_int64)], ctypes.c_int),
@@ -239,6 +243,22 @@ I4_MATRICES = {"fc": 0, "qkv": 1, "o_proj": 2, "gate_up": 3, "down_proj": 4, "lm
 def eagle3_weights_i4_read(ctx, matrix: str, codes, scales, stream=None) -> None:
     _check(ctx, library().eagle3_weights_i4_read(ctx, I4_MATRICES[matrix], _ptr(codes),
                                                  _ptr(scales), _stream(stream)))
+
+
+def eagle3_verify_attention_workspace(M: int, n_head: int, n_head_kv: int, head_dim: int,
+                                      ctx_rows: int, kv_dtype: int = KV_F32) -> int:
+    return int(library().eagle3_verify_attention_workspace(M, n_head, n_head_kv, head_dim,
+                                                           ctx_rows, kv_dtype))
+
+
+def eagle3_verify_attention(q, k, v, kv_dtype: int, cap: int, ctx_rows: int, M: int, n_head: int,
+                            n_head_kv: int, head_dim: int, out, workspace=None,
+                            workspace_bytes: int = 0, stream=None) -> None:
+    rc = library().eagle3_verify_attention(_ptr(q), _ptr(k), _ptr(v), kv_dtype, cap, ctx_rows, M,
+                                           n_head, n_head_kv, head_dim, _ptr(out), _ptr(workspace),
+                                           workspace_bytes, _stream(stream))
+    if rc != OK:
+        raise Eagle3Error(rc, "eagle3_verify_attention")
 
 
 def eagle3_last_error(ctx) -> str:

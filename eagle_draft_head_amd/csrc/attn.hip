@@ -242,6 +242,184 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 }
 
 // ---------------------------------------------------------------------------
+// Verify-window attention (mid M): M query rows per head, query row m seeing cache
+// rows 0..ctx+m (the window's own K/V are rows ctx..ctx+M-1).  The M * G query
+// vectors of a KV head are taken GQ at a time by "query group" blocks that walk the
+// same split of K/V rows as k_attn does for G heads, with a per-vector row limit.
+// The blocks of one (KV head, split) tile are placed on one XCD (workgroups go to
+// the XCDs round robin by linear id, so tile t's groups get ids t % 8 + 8 k), where
+// they read the tile's rows through the same L2: the rows come from HBM about once
+// for all M * G vectors.
+template <int HD, int GQ, typename KT>
+__global__ __launch_bounds__(256) void k_attn_mid(VerifyArgs a, int chunk, int S, int QG) {
+  constexpr int E = KvVec<KT>::E;
+  constexpr int NV = kAttnLaneElems / E;
+  constexpr int LPR = HD / kAttnLaneElems;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * kAttnWaves;
+  constexpr int kDepth = NV == 1 ? 4 : 3;
+  __shared__ float obuf[kAttnWaves][GQ][HD];
+  __shared__ float s_M[kAttnWaves][GQ], s_L[kAttnWaves][GQ];
+
+  const int nkv = a.n_head_kv, G = a.n_head / nkv;
+  const int tiles = S * nkv;
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int tile = (slot / QG) * 8 + xcd, qg = slot % QG;
+  if (tile >= tiles) return;
+  const int s = tile % S, kvh = tile / S;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int rs = lane / LPR, sub = lane % LPR;
+  auto dim = [&](int e) { return (e / E) * (HD / NV) + sub * E + (e % E); };
+  const int T = a.ctx + a.M;
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  // this group's query vectors: j = qg * GQ + jj over (m, g), m-major
+  int lim[GQ], qrow[GQ];
+#pragma unroll
+  for (int jj = 0; jj < GQ; ++jj) {
+    const int j = qg * GQ + jj;
+    const int m = j / G, g = j - m * G;
+    const bool ok = m < a.M;
+    lim[jj] = ok ? a.ctx + m : -1;                    // last row seen (inclusive)
+    qrow[jj] = ok ? m * a.n_head + kvh * G + g : -1;  // (m, head) index
+  }
+  const bool direct = S == 1;
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  const KT* Kb = static_cast<const KT*>(a.k) + (size_t)kvh * a.cap * HD + sub * E;
+  const KT* Vb = static_cast<const KT*>(a.v) + (size_t)kvh * a.cap * HD + sub * E;
+  const int off = wv * RPW + rs;
+  const int rlast = r1 - 1;
+  uint4 kw[kDepth][NV], vw[kDepth][NV];
+  auto load_row = [&](int i, int row) {
+    row = min(row, rlast);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      kw[i][j] = *reinterpret_cast<const uint4*>(Kb + (size_t)row * HD + j * (HD / NV));
+      vw[i][j] = *reinterpret_cast<const uint4*>(Vb + (size_t)row * HD + j * (HD / NV));
+    }
+  };
+  int rb = r0;
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) load_row(i, rb + off + i * RPB);
+  float qv[GQ][kAttnLaneElems];
+#pragma unroll
+  for (int g = 0; g < GQ; ++g)
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e)
+      qv[g][e] = qrow[g] >= 0 ? a.q[(size_t)qrow[g] * HD + dim(e)] * scale : 0.f;
+  float m[GQ], mr[GQ], l[GQ], acc[GQ][kAttnLaneElems];
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    m[g] = -INFINITY;
+    mr[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = 0.f;
+  }
+  auto step = [&](int i, int row) {
+    float kf[kAttnLaneElems], vf[kAttnLaneElems];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      KvVec<KT>::unpack(kw[i][j], kf + j * E);
+      KvVec<KT>::unpack(vw[i][j], vf + j * E);
+    }
+    load_row(i, row + kDepth * RPB);
+    float d[GQ];
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) t = fmaf(kf[e], qv[g][e], t);
+      d[g] = t;
+    }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) d[g] = group_sum<LPR>(d[g]);
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      if (row > lim[g]) continue;  // past this query row's window position
+      const float sc = d[g];
+      if (sc > mr[g]) {
+        const float fo = __builtin_amdgcn_exp2f(m[g] - sc);
+        l[g] *= fo;
+#pragma unroll
+        for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
+        m[g] = sc;
+        mr[g] = sc + kRescale;
+      }
+      const float p = __builtin_amdgcn_exp2f(sc - m[g]);
+      l[g] += p;
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+    }
+  };
+  for (; rb + kDepth * RPB <= r1; rb += kDepth * RPB) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) step(i, rb + off + i * RPB);
+  }
+  if (rb < r1) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int rr = rb + off + i * RPB;
+      if (rr >= r1) break;
+      step(i, rr);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    const float mw = wave_max(m[g]);
+    if (lane == 0) s_M[wv][g] = mw;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < GQ; ++g) {
+    float Mb = s_M[0][g];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    const float f = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - Mb);
+    l[g] *= f;
+#pragma unroll
+    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= f;
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      l[g] += __shfl_xor(l[g], o, kWave);
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, kWave);
+    }
+  if (rs == 0) {
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+#pragma unroll
+      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][dim(e)] = acc[g][e];
+      if (sub == 0) s_L[wv][g] = l[g];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < GQ * HD; i += blockDim.x) {
+    const int g = i / HD, dd = i - g * HD;
+    if (qrow[g] < 0) continue;
+    float v = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      v += obuf[w][g][dd];
+      Ls += s_L[w][g];
+    }
+    if (direct) a.out[(size_t)qrow[g] * HD + dd] = v / Ls;
+    else a.part_o[((size_t)qrow[g] * S + s) * HD + dd] = v;
+  }
+  if (direct) return;
+  if (threadIdx.x < GQ && qrow[threadIdx.x] >= 0) {
+    const int g = threadIdx.x;
+    float Mb = s_M[0][g], Ls = 0.f;
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    for (int w = 0; w < kAttnWaves; ++w) Ls += s_L[w][g];
+    a.part_ml[((size_t)qrow[g] * S + s) * 2 + 0] = Mb;
+    a.part_ml[((size_t)qrow[g] * S + s) * 2 + 1] = Ls;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_attn over quantized regions (q8_0 K, q5_1 V; layout in kernels.hpp).  A lane
 // holds 8 consecutive dims of a row, inside one block of 32: per row it loads 8 K
 // codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and its
@@ -703,6 +881,52 @@ static hipError_t launch_q_hd(const AttnArgs& a, int G, int chunk, int S, hipStr
   hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S, HD,
                      a.out);
   return hipGetLastError();
+}
+
+// query vectors per block of the verify attention: the decode kernel's largest G
+constexpr int kVerifyGroup = 8;
+
+static int verify_group(int MG) { return MG <= 1 ? 1 : MG <= 2 ? 2 : MG <= 4 ? 4 : kVerifyGroup; }
+
+size_t attn_verify_workspace(int M, int n_head, int n_head_kv, int head_dim, int ctx, int kv_f32) {
+  int chunk, S;
+  pick_split(ctx + M, n_head_kv, head_dim, kv_f32, &chunk, &S);
+  return size_t(M) * n_head * S * (head_dim + 2) * sizeof(float);
+}
+
+template <int HD, typename KT>
+static hipError_t launch_mid_hd(const VerifyArgs& a, int chunk, int S, hipStream_t s) {
+  const int MG = a.M * (a.n_head / a.n_head_kv);
+  const int GQ = verify_group(MG);
+  const int QG = (MG + GQ - 1) / GQ;
+  const int tiles = S * a.n_head_kv;
+  const dim3 grid(unsigned((tiles + 7) / 8 * 8 * QG)), block(64 * kAttnWaves);
+  switch (GQ) {
+    case 1: hipLaunchKernelGGL((k_attn_mid<HD, 1, KT>), grid, block, 0, s, a, chunk, S, QG); break;
+    case 2: hipLaunchKernelGGL((k_attn_mid<HD, 2, KT>), grid, block, 0, s, a, chunk, S, QG); break;
+    case 4: hipLaunchKernelGGL((k_attn_mid<HD, 4, KT>), grid, block, 0, s, a, chunk, S, QG); break;
+    default: hipLaunchKernelGGL((k_attn_mid<HD, kVerifyGroup, KT>), grid, block, 0, s, a, chunk, S, QG); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.M * a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S, HD,
+                     a.out);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipStream_t s) {
+  if (a.M < 1 || a.ctx < 0 || int64_t(a.ctx) + a.M > a.cap || a.n_head % a.n_head_kv)
+    return hipErrorInvalidValue;
+  int chunk, S;
+  pick_split(a.ctx + a.M, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
+  if (S > 1 && workspace_bytes < attn_verify_workspace(a.M, a.n_head, a.n_head_kv, a.head_dim, a.ctx, a.kv_f32))
+    return hipErrorInvalidValue;
+  switch (a.head_dim) {
+    case 64: return a.kv_f32 ? launch_mid_hd<64, float>(a, chunk, S, s) : launch_mid_hd<64, uint16_t>(a, chunk, S, s);
+    case 128: return a.kv_f32 ? launch_mid_hd<128, float>(a, chunk, S, s) : launch_mid_hd<128, uint16_t>(a, chunk, S, s);
+    case 256: return a.kv_f32 ? launch_mid_hd<256, float>(a, chunk, S, s) : launch_mid_hd<256, uint16_t>(a, chunk, S, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {

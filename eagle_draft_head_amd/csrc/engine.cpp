@@ -607,6 +607,38 @@ const char* eagle3_last_error(const eagle3_ctx* ctx) {
   return ctx ? ctx->err.c_str() : g_load_error.c_str();
 }
 
+size_t eagle3_verify_attention_workspace(int32_t M, int32_t n_head, int32_t n_head_kv,
+                                         int32_t head_dim, int32_t ctx_rows, int32_t kv_dtype) {
+  if (M < 1 || ctx_rows < 0 || n_head_kv < 1 || n_head < n_head_kv) return 0;
+  return e3::attn_verify_workspace(M, n_head, n_head_kv, head_dim, ctx_rows, kv_dtype == EAGLE3_KV_F32);
+}
+
+int eagle3_verify_attention(const float* q_dev, const void* k_dev, const void* v_dev, int32_t kv_dtype,
+                            int32_t cap, int32_t ctx_rows, int32_t M, int32_t n_head, int32_t n_head_kv,
+                            int32_t head_dim, float* out_dev, void* workspace_dev, size_t workspace_bytes,
+                            void* stream) {
+  if (!q_dev || !k_dev || !v_dev || !out_dev || M < 1 || ctx_rows < 0 || cap < 1 ||
+      int64_t(ctx_rows) + M > cap || n_head < 1 || n_head_kv < 1)
+    return EAGLE3_E_INVAL;
+  if (n_head % n_head_kv) return EAGLE3_E_SHAPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return EAGLE3_E_UNSUPPORTED;
+  if (kv_dtype != EAGLE3_KV_F32 && kv_dtype != EAGLE3_KV_BF16) return EAGLE3_E_UNSUPPORTED;
+  const int f32 = kv_dtype == EAGLE3_KV_F32;
+  const size_t need = e3::attn_verify_workspace(M, n_head, n_head_kv, head_dim, ctx_rows, f32);
+  e3::VerifyArgs a{};
+  a.q = q_dev; a.k = k_dev; a.v = v_dev; a.kv_f32 = f32;
+  a.cap = cap; a.ctx = ctx_rows; a.M = M;
+  a.n_head = n_head; a.n_head_kv = n_head_kv; a.head_dim = head_dim;
+  float* ws = static_cast<float*>(workspace_dev);
+  const size_t po = need / sizeof(float) / size_t(head_dim + 2) * size_t(head_dim);  // part_o floats
+  a.part_o = ws;
+  a.part_ml = ws ? ws + po : nullptr;
+  a.out = out_dev;
+  const hipError_t e = e3::launch_attn_verify(a, ws ? workspace_bytes : 0, as_stream(stream));
+  if (e == hipErrorInvalidValue) return EAGLE3_E_INVAL;
+  return e == hipSuccess ? EAGLE3_OK : EAGLE3_E_HIP;
+}
+
 int eagle3_kv_len(const eagle3_ctx* ctx, int32_t seq, int32_t* committed, int32_t* spec) {
   if (!ctx || !committed || !spec) return EAGLE3_E_INVAL;
   if (!ctx->ledger.valid_seq(seq)) return EAGLE3_E_INVAL;

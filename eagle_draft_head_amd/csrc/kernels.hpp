@@ -176,6 +176,24 @@ struct AttnArgs {
   BatchRows br;
 };
 int attn_max_splits(int cap, int head_dim, int n_head_kv);
+
+// Verify-window attention: M query rows per head ([M][n_head][hd], roped), cache rows
+// 0..ctx+M-1 ([n_head_kv][cap][hd], fp32 or bf16), query row m sees rows 0..ctx+m;
+// out [M][n_head][hd].  Split partials go to part_o [M*n_head][S][hd] and part_ml
+// [M*n_head][S][2] (attn_verify_workspace bytes in all, unused when S == 1).
+struct VerifyArgs {
+  const float* q;
+  const void* k;
+  const void* v;
+  int kv_f32;
+  int cap, ctx, M;
+  int n_head, n_head_kv, head_dim;
+  float* part_o;
+  float* part_ml;
+  float* out;
+};
+size_t attn_verify_workspace(int M, int n_head, int n_head_kv, int head_dim, int ctx, int kv_f32);
+hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipStream_t s);
 // Splits the context, then (when more than one split) runs the combine kernel.
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 // Batched: split every row's context in chunks of one size, then combine per (row,

@@ -233,6 +233,28 @@ int eagle3_kv_len(const eagle3_ctx *ctx, int32_t seq, int32_t *committed, int32_
 int eagle3_kv_read(const eagle3_ctx *ctx, int32_t seq, int32_t row0, int32_t nrows,
                    void *k_dev, void *v_dev, void *stream);
 
+/* Verify-window attention (the target-verify side of a round: ExecuTorch PR #20344
+   "split-K mid-M SDPA ... for EAGLE-3 target_verify at long context"; PR #20156:
+   one target forward per round over the K-token window).  M query rows per head,
+   q_dev [M][n_head][head_dim] fp32 (roped); k_dev, v_dev [n_head_kv][cap][head_dim]
+   in kv_dtype EAGLE3_KV_F32 or EAGLE3_KV_BF16 (K roped), whose rows ctx_rows ..
+   ctx_rows + M - 1 hold the window's own K/V; query row m attends rows
+   0 .. ctx_rows + m (scale 1/sqrt(head_dim), query head h reads KV head
+   h / (n_head / n_head_kv)); out_dev [M][n_head][head_dim] fp32.  The context is
+   split across blocks and the splits combined; workspace_dev must hold
+   eagle3_verify_attention_workspace(...) bytes (device memory owned by the caller;
+   0 bytes needed when the context fits one split).  All pointers are device
+   pointers; stream is a hipStream_t (NULL: the default stream); the call is
+   asynchronous.  Errors: EAGLE3_E_INVAL (null pointers, M < 1, ctx_rows < 0,
+   ctx_rows + M > cap, too small a workspace), EAGLE3_E_SHAPE (n_head not a multiple
+   of n_head_kv), EAGLE3_E_UNSUPPORTED (head_dim not 64/128/256, other kv_dtype). */
+size_t eagle3_verify_attention_workspace(int32_t M, int32_t n_head, int32_t n_head_kv,
+                                         int32_t head_dim, int32_t ctx_rows, int32_t kv_dtype);
+int eagle3_verify_attention(const float *q_dev, const void *k_dev, const void *v_dev,
+                            int32_t kv_dtype, int32_t cap, int32_t ctx_rows, int32_t M,
+                            int32_t n_head, int32_t n_head_kv, int32_t head_dim, float *out_dev,
+                            void *workspace_dev, size_t workspace_bytes, void *stream);
+
 /* Copy one int4 projection matrix (weight_format EAGLE3_WEIGHTS_I4) into caller
    buffers: codes_dev [rows][K / 2] bytes and scales_dev [rows][K / 32] bf16, in the
    layout of EAGLE3_WEIGHTS_I4.  Row order as stored: fc, o_proj, down_proj and
