@@ -148,6 +148,9 @@ def main():
                          "chain encodes the boundary taps itself and every round is rewound to "
                          "the workload's length (the default for page4, whose rounds are rewound; "
                          "stored elsewhere)")
+    ap.add_argument("--verify-attn", action="store_true",
+                    help="time eagle3_verify_attention alone: the workload's KV heads over its "
+                         "context plus a gamma+1-row window, against gamma+1 single-row calls")
     args = ap.parse_args()
     args.kernel_set = args.kernel is not None
     if args.kernel is None:
@@ -165,6 +168,8 @@ def main():
     from synth import ALL, gen
 
     cfg = ALL[args.workload]
+    if args.verify_attn:
+        return run_verify_attn(args, cfg)
     if cfg.max_seqs > 1:
         return run_batched(args, cfg)
     gamma = args.gamma or cfg.gamma
@@ -387,6 +392,75 @@ def batched_kernel_bytes(cfg, kernel: str, lens, gamma: int, kv_bytes: int = 4) 
     act = {"lm_head": (dv, n), "gate_up": (2 * ff, n), "qkv": (qd + 2 * kvd, 2 * n),
            "down": (n, ff), "o_proj": (n, qd)}[kernel]
     return 2.0 * act[0] * act[1] + m * 4 * act[1]
+
+
+def run_verify_attn(args, cfg):
+    """The verify-window attention alone: the workload's heads (the drafter's, as a
+    stand-in for a target of that shape) over its context plus a window of gamma + 1
+    rows, fp32 or bf16 K/V resident in HBM.  One step = one eagle3_verify_attention
+    call; bytes = the K/V rows read once + q + out.  Also times the same window as
+    gamma + 1 single-row calls (row m over ctx + m + 1 rows), which read the rows
+    gamma + 1 times."""
+    import numpy as np
+    import torch
+
+    from eagle_draft_head_amd import binding as B
+    from synth import gen
+
+    gamma = args.gamma or cfg.gamma
+    M = gamma + 1
+    ctx = cfg.context
+    nh, nkv, hd = cfg.n_head, cfg.n_head_kv, cfg.head_dim
+    kv = B.KV_BF16 if args.kv == "bf16" else B.KV_F32
+    if args.kv == "q8q5":
+        print(json.dumps({"error": "verify attention takes fp32 or bf16 K/V"}))
+        sys.exit(2)
+    esz = 2 if kv == B.KV_BF16 else 4
+    cap = ctx + M
+    dt = torch.bfloat16 if kv == B.KV_BF16 else torch.float32
+    q = gen.normal(98, 1, (M, nh, hd), 1.0, device="cuda")
+    k = gen.normal(98, 2, (nkv, cap, hd), 1.0, device="cuda").to(dt)
+    v = gen.normal(98, 3, (nkv, cap, hd), 1.0, device="cuda").to(dt)
+    out = torch.empty((M, nh, hd), dtype=torch.float32, device="cuda")
+    ws_bytes = max(B.eagle3_verify_attention_workspace(M, nh, nkv, hd, ctx + M - 1, kv), 4)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def window():
+        B.eagle3_verify_attention(q, k, v, kv, cap, ctx, M, nh, nkv, hd, out, ws, ws_bytes, stream)
+
+    def singles():
+        for m in range(M):
+            B.eagle3_verify_attention(q[m:m + 1], k, v, kv, cap, ctx + m, 1, nh, nkv, hd, out[m:m + 1],
+                                      ws, ws_bytes, stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3  # us per call
+
+    us = timed(window)
+    us_single = timed(singles)
+    bytes_w = 2.0 * esz * nkv * hd * (ctx + M) + 4.0 * 2 * M * nh * hd
+    gbs = bytes_w / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "verify-window attention GB/s (K/V rows read once)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "us_per_call": round(us, 3), "us_per_window_as_single_rows": round(us_single, 3),
+        "higher_is_better": True, "dtype": f"{args.kv} K/V, fp32 q and accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{cfg.name} heads {nh}/{nkv} x {hd}, {ctx} context rows + a "
+                               f"{M}-row window"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "bytes_per_call": bytes_w},
+    }))
 
 
 def run_batched(args, cfg):

@@ -883,10 +883,22 @@ static hipError_t launch_q_hd(const AttnArgs& a, int G, int chunk, int S, hipStr
   return hipGetLastError();
 }
 
-// query vectors per block of the verify attention: the decode kernel's largest G
+// query vectors per block of the verify attention: at most the decode kernel's
+// largest G; 4 by default (at 32K rows, 40/8 heads and a 4-row window: 154 us fp32
+// and 121 us bf16 against 160 and 161 with 8, whose 254 VGPRs leave 2 waves a SIMD)
 constexpr int kVerifyGroup = 8;
+constexpr int kVerifyGroupDefault = 4;
 
-static int verify_group(int MG) { return MG <= 1 ? 1 : MG <= 2 ? 2 : MG <= 4 ? 4 : kVerifyGroup; }
+// EAGLE3_VERIFY_GROUP (1, 2, 4 or 8) caps it for tuning
+static int verify_group(int MG) {
+  static const int cap = [] {
+    const char* e = std::getenv("EAGLE3_VERIFY_GROUP");
+    const int v = e ? std::atoi(e) : 0;
+    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : kVerifyGroupDefault;
+  }();
+  const int g = MG <= 1 ? 1 : MG <= 2 ? 2 : MG <= 4 ? 4 : kVerifyGroup;
+  return g < cap ? g : cap;
+}
 
 size_t attn_verify_workspace(int M, int n_head, int n_head_kv, int head_dim, int ctx, int kv_f32) {
   int chunk, S;
