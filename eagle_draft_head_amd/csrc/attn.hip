@@ -420,6 +420,199 @@ __global__ __launch_bounds__(256) void k_attn_mid(VerifyArgs a, int chunk, int S
 }
 
 // ---------------------------------------------------------------------------
+// Verify-window attention on MFMA.  A block takes 16 query vectors of one KV head
+// (a query group) over one split of rows; each wave walks 32-row tiles of the split.
+// Per tile, S^T = K Q^T as two 16x16 outputs of v_mfma_f32_16x16x32_bf16 (A = 16 K
+// rows, B = the 16 query vectors; lane l holds row l % 16 and dims 8 (l / 16) .. + 7
+// of a 32-wide k step, and gets S^T[rows 4 (l / 16) + v][query l % 16]).  A lane thus
+// holds 8 scores of one query (rows 4g + v and 16 + 4g + v, g = l / 16): exactly an A
+// operand of O += P V over the 32 rows, when the MFMA's k slot 8g + v stands for row
+// 4g + v and slot 8g + 4 + v for row 16 + 4g + v; V's B operand (dim 16t + l % 16)
+// is loaded in that row order.  O's D layout holds queries 4g + v, so the online
+// softmax rescale factors move there by shuffles.  fp32 operands enter as bf16
+// (hi, lo) pairs, x = hi + lo to 2^-18, and hi*hi + hi*lo + lo*hi is summed.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 8 fp32 -> bf16 (hi, lo), both rounded to nearest even (v_cvt_pk_bf16_f32):
+// |x - hi - lo| <= 2^-18 |x|
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = (__bf16)x[i];
+    lo[i] = (__bf16)(x[i] - (float)hi[i]);
+  }
+}
+
+__device__ __forceinline__ float kv_elem(const float* p) { return *p; }
+__device__ __forceinline__ float kv_elem(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <int HD, typename KT>
+__global__ __launch_bounds__(256) void k_attn_mid_mfma(VerifyArgs a, int chunk, int S, int QG) {
+  constexpr int NT = HD / 16;  // 16-wide output dim tiles
+  constexpr int KS = HD / 32;  // k steps of S
+  constexpr bool F32 = sizeof(KT) == 4;
+  __shared__ float so[kAttnWaves][16][HD + 4];
+  __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
+
+  const int nkv = a.n_head_kv, G = a.n_head / nkv;
+  const int tiles = S * nkv;
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int tile = (slot / QG) * 8 + xcd, qg = slot % QG;
+  if (tile >= tiles) return;
+  const int s = tile % S, kvh = tile / S;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int T = a.ctx + a.M;
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  // this lane's query (S layout): vector j = qg * 16 + c16 over (m, g), m-major
+  const int jq = qg * 16 + c16, mq = jq / G;
+  const bool qok = mq < a.M;
+  const int lim = qok ? a.ctx + mq : -1;
+  const int qrow = qok ? mq * a.n_head + kvh * G + (jq - mq * G) : -1;
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  bf16x8_t qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = qok ? a.q[(size_t)qrow * HD + 32 * ks + 8 * g4 + e] * scale : 0.f;
+    split8(x, qh[ks], ql[ks]);
+  }
+  const KT* Kb = static_cast<const KT*>(a.k) + (size_t)kvh * a.cap * HD;
+  const KT* Vb = static_cast<const KT*>(a.v) + (size_t)kvh * a.cap * HD;
+  f32x4_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  const int rlast = r1 - 1;
+  for (int tb = r0 + 32 * wv; tb < r1; tb += 32 * kAttnWaves) {
+    // V's B operands (rows in slot order, dim 16 t + c16) are requested first, so
+    // they arrive with K's
+    float vx[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        vx[t][v] = kv_elem(Vb + (size_t)min(tb + 4 * g4 + v, rlast) * HD + 16 * t + c16);
+        vx[t][4 + v] = kv_elem(Vb + (size_t)min(tb + 16 + 4 * g4 + v, rlast) * HD + 16 * t + c16);
+      }
+    // S^T for rows tb + 16 h + (0..15): A = K rows, B = queries
+    f32x4_t st[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const KT* kr = Kb + (size_t)min(tb + 16 * h + c16, rlast) * HD + 8 * g4;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (F32) {
+          const float4 u = *reinterpret_cast<const float4*>(kr + 32 * ks);
+          const float4 w = *reinterpret_cast<const float4*>(kr + 32 * ks + 4);
+          const float x[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+          bf16x8_t kh, kl;
+          split8(x, kh, kl);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[ks], acc, 0, 0, 0);
+        } else {
+          const bf16x8_t kh = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(kr + 32 * ks));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], acc, 0, 0, 0);
+        }
+      }
+      st[h] = acc;
+    }
+    // mask, tile maximum and sum per query (the 4 lanes c16, c16 + 16, ...)
+    float sc[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ra = tb + 4 * g4 + v, rb = tb + 16 + 4 * g4 + v;
+      sc[v] = (ra < r1 && ra <= lim) ? st[0][v] : -INFINITY;
+      sc[4 + v] = (rb < r1 && rb <= lim) ? st[1][v] : -INFINITY;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int v = 1; v < 8; ++v) mx = fmaxf(mx, sc[v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float mn = fmaxf(m, mx);
+    const float fo = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);  // m = -inf: 0
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      p[v] = sc[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[v] - mn);
+      ps += p[v];
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * fo + ps;
+    m = mn;
+    // rescale O (D layout: queries 4 g4 + v) by those queries' factors
+    float fv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) fv[v] = __shfl(fo, 4 * g4 + v, kWave);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[t][v] *= fv[v];
+    bf16x8_t ph, pl;
+    split8(p, ph, pl);
+    // O += P V: B = V[rows (slot order)][dim 16 t + c16]
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float (&x)[8] = vx[t];
+      if constexpr (F32) {
+        bf16x8_t vh, vl;
+        split8(x, vh, vl);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vh, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vl, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vh, o[t], 0, 0, 0);
+      } else {
+        bf16x8_t vh, vl;
+        split8(x, vh, vl);  // exact: lo is zero for bf16 values
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vh, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vh, o[t], 0, 0, 0);
+      }
+    }
+  }
+  // merge the waves
+  if (g4 == 0) {
+    sm[wv][c16] = m;
+    sl[wv][c16] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) so[wv][4 * g4 + v][16 * t + c16] = o[t][v];
+  __syncthreads();
+  const bool direct = S == 1;
+  for (int i = threadIdx.x; i < 16 * HD; i += blockDim.x) {
+    const int q = i / HD, dd = i - q * HD;
+    const int j = qg * 16 + q, mm = j / G;
+    if (mm >= a.M) continue;
+    const int qr = mm * a.n_head + kvh * G + (j - mm * G);
+    float Mb = sm[0][q];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, sm[w][q]);
+    float v = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = (Mb == -INFINITY || sm[w][q] == -INFINITY) ? 0.f : exp2f(sm[w][q] - Mb);
+      v = fmaf(f, so[w][q][dd], v);
+      Ls = fmaf(f, sl[w][q], Ls);
+    }
+    if (direct) a.out[(size_t)qr * HD + dd] = v / Ls;
+    else {
+      a.part_o[((size_t)qr * S + s) * HD + dd] = v;
+      if (dd == 0) {
+        a.part_ml[((size_t)qr * S + s) * 2 + 0] = Mb;
+        a.part_ml[((size_t)qr * S + s) * 2 + 1] = Ls;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_attn over quantized regions (q8_0 K, q5_1 V; layout in kernels.hpp).  A lane
 // holds 8 consecutive dims of a row, inside one block of 32: per row it loads 8 K
 // codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and its
@@ -744,9 +937,10 @@ static int attn_single_blocks() {
   return t;
 }
 
-static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S) {
-  const int rpb = rows_per_block(hd, kv_f32);
-  const int blocks = attn_single_blocks();
+static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S, int blocks = 0,
+                       int rpb = 0) {
+  if (rpb <= 0) rpb = rows_per_block(hd, kv_f32);
+  if (blocks <= 0) blocks = attn_single_blocks();
   const int target = n_head_kv >= blocks ? 1 : blocks / n_head_kv;
   int c = (T + target - 1) / target;
   c = ((c + rpb - 1) / rpb) * rpb;
@@ -900,15 +1094,56 @@ static int verify_group(int MG) {
   return g < cap ? g : cap;
 }
 
+// EAGLE3_VERIFY_VALU=1 selects the VALU kernel (k_attn_mid) for comparison
+static bool verify_valu() {
+  static const bool v = [] {
+    const char* e = std::getenv("EAGLE3_VERIFY_VALU");
+    return e && e[0] == '1';
+  }();
+  return v;
+}
+
+// (KV head, split) tiles aimed at by the MFMA verify kernel (EAGLE3_VERIFY_BLOCKS
+// overrides it): more than the decode kernel's, since a wave holds one 32-row tile's
+// loads at a time
+static int verify_blocks() {
+  static const int t = [] {
+    const char* e = std::getenv("EAGLE3_VERIFY_BLOCKS");
+    const int v = e ? std::atoi(e) : 0;
+    return (v >= 8 && v <= 8192) ? v : 1024;
+  }();
+  return t;
+}
+
+static bool verify_mfma(int hd) { return hd <= 128 && !verify_valu(); }
+
+static void verify_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S) {
+  if (verify_mfma(hd)) pick_split(T, n_head_kv, hd, kv_f32, chunk, S, verify_blocks(), 32 * kAttnWaves);
+  else pick_split(T, n_head_kv, hd, kv_f32, chunk, S);
+}
+
 size_t attn_verify_workspace(int M, int n_head, int n_head_kv, int head_dim, int ctx, int kv_f32) {
   int chunk, S;
-  pick_split(ctx + M, n_head_kv, head_dim, kv_f32, &chunk, &S);
+  verify_split(ctx + M, n_head_kv, head_dim, kv_f32, &chunk, &S);
   return size_t(M) * n_head * S * (head_dim + 2) * sizeof(float);
 }
 
 template <int HD, typename KT>
 static hipError_t launch_mid_hd(const VerifyArgs& a, int chunk, int S, hipStream_t s) {
   const int MG = a.M * (a.n_head / a.n_head_kv);
+  // (head_dim 256 stays on the VALU kernel: the MFMA kernel's wave merge would need
+  // more than 64 KB of LDS)
+  if (verify_mfma(HD)) {
+    const int QG = (MG + 15) / 16;
+    const int tiles = S * a.n_head_kv;
+    hipLaunchKernelGGL((k_attn_mid_mfma<(HD <= 128 ? HD : 128), KT>), dim3(unsigned((tiles + 7) / 8 * 8 * QG)),
+                       dim3(64 * kAttnWaves), 0, s, a, chunk, S, QG);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    hipLaunchKernelGGL(k_attn_combine, dim3(a.M * a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S,
+                       HD, a.out);
+    return hipGetLastError();
+  }
   const int GQ = verify_group(MG);
   const int QG = (MG + GQ - 1) / GQ;
   const int tiles = S * a.n_head_kv;
@@ -930,7 +1165,7 @@ hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipSt
   if (a.M < 1 || a.ctx < 0 || int64_t(a.ctx) + a.M > a.cap || a.n_head % a.n_head_kv)
     return hipErrorInvalidValue;
   int chunk, S;
-  pick_split(a.ctx + a.M, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
+  verify_split(a.ctx + a.M, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   if (S > 1 && workspace_bytes < attn_verify_workspace(a.M, a.n_head, a.n_head_kv, a.head_dim, a.ctx, a.kv_f32))
     return hipErrorInvalidValue;
   switch (a.head_dim) {
