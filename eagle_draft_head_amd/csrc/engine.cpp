@@ -59,6 +59,10 @@ struct eagle3_ctx {
     uint16_t* s = nullptr;
   } i4_fc, i4_qkv, i4_o, i4_gu, i4_d, i4_lm;
   bool i4 = false;
+  // int4: the teacher-forced MFMA passes multiply by the int4 weights of fc and of the
+  // K/V rows of QKV as exact bf16 (hi, lo) pairs: hi overwrites those rows of w_fc /
+  // w_qkv, lo lives here
+  uint16_t *i4_fc_lo = nullptr, *i4_kv_lo = nullptr;
   // the weight stream a GEMV reads: the bf16 rows or the int4 codes, and the scales
   const uint16_t* wq(const uint16_t* bf16, const I4W& m, size_t row0 = 0, size_t K = 0) const {
     return i4 ? reinterpret_cast<const uint16_t*>(m.q + row0 * (K / 2)) : bf16 + row0 * K;
@@ -587,6 +591,13 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     E3_TRY(quant(c->w_gu, 2 * ff, n, &c->i4_gu));
     E3_TRY(quant(c->w_d, n, ff, &c->i4_d));
     E3_TRY(quant(c->w_lm, dv, n, &c->i4_lm));
+    E3_TRY(dalloc(c, &c->i4_fc_lo, size_t(n) * 3 * n));
+    E3_TRY(dalloc(c, &c->i4_kv_lo, size_t(2 * kvd) * 2 * n));
+    E3_TRYH(e3::launch_dequant_i4_split(c->i4_fc.q, c->i4_fc.s, int(n), int(3 * n), c->w_fc, c->i4_fc_lo, s),
+            "int4 fc split");
+    E3_TRYH(e3::launch_dequant_i4_split(c->i4_qkv.q + size_t(qd) * n, c->i4_qkv.s + size_t(qd) * (2 * n / 32),
+                                        int(2 * kvd), int(2 * n), c->w_qkv + size_t(qd) * 2 * n, c->i4_kv_lo, s),
+            "int4 kv split");
   }
   E3_TRYH(hipStreamSynchronize(s), "load sync");
 #undef E3_TRY
@@ -737,8 +748,8 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
   const int n = c->n, kvd2 = 2 * c->kvd;
   const int all = total + bi.count();
   size_t seg_i = 0;
-  // int4 weights: every pass on the multi-vector GEMV (at most 16 rows)
-  const int pass_rows = c->i4 ? std::min(16, c->tf_rows) : c->tf_rows;
+  const int pass_rows = c->tf_rows;
+  const int wsp = c->i4 ? 2 : 1;  // int4: each MFMA product twice, weights hi and lo
   for (int c0 = 0; c0 < all;) {
     int P = std::min(pass_rows, all - c0);
     const int T = std::max(0, std::min(total, c0 + P) - c0);  // teacher-forced rows of the pass
@@ -792,12 +803,16 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       // MFMA path
       E3_HIP(c, e3::launch_pack_aux(x0, x1, x2, P, n, c->tf_A, c->tf_A_lo, s, yb), "pack aux");
       e3::GemmPlan p1 = e3::gemm_plan(P, n, 3 * n);
-      while (p1.splits > 1 && size_t(p1.splits) * P * n > c->tf_F_cap) p1.splits /= 2;
-      sp1 = p1.splits;
+      while (p1.splits > 1 && size_t(wsp) * p1.splits * P * n > c->tf_F_cap) p1.splits /= 2;
+      sp1 = p1.splits * wsp;
       {
         ProfScope ps(c, 7, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, P, n,
                                        3 * n, p1, s), "fc gemm");
+        if (c->i4)  // the weights' low halves into the next split slots
+          E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->i4_fc_lo, 3 * n,
+                                         c->tf_F + size_t(p1.splits) * P * n, P, n, 3 * n, p1, s),
+                 "fc gemm lo");
       }
       f_split = size_t(P) * n;
       E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
@@ -806,12 +821,16 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
              "tf cat");
       if (T > 0) {
         e3::GemmPlan p2 = e3::gemm_plan(T, kvd2, 2 * n);
-        while (p2.splits > 1 && size_t(p2.splits) * T * kvd2 > c->tf_P_cap) p2.splits /= 2;
-        sp2 = p2.splits;
+        while (p2.splits > 1 && size_t(wsp) * p2.splits * T * kvd2 > c->tf_P_cap) p2.splits /= 2;
+        sp2 = p2.splits * wsp;
         ProfScope ps(c, 8, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n,
                                        c->w_qkv + size_t(c->qd) * 2 * n, 2 * n, c->tf_P, T, kvd2,
                                        2 * n, p2, s), "kv gemm");
+        if (c->i4)
+          E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n, c->i4_kv_lo, 2 * n,
+                                         c->tf_P + size_t(p2.splits) * T * kvd2, T, kvd2, 2 * n, p2, s),
+                 "kv gemm lo");
       }
       p_split = size_t(T) * kvd2;
     }

@@ -352,6 +352,32 @@ __global__ __launch_bounds__(256) void k_quant_i4(const uint16_t* __restrict__ W
   S[row * gpr + gi] = sb;
 }
 
+// One thread per weight: w = scale * q (at most 11 significant bits) as bf16 hi (round
+// to nearest even) and lo = w - hi, which is exact in bf16, so hi + lo == w.
+__global__ __launch_bounds__(256) void k_dequant_i4_split(const uint8_t* __restrict__ Q,
+                                                          const uint16_t* __restrict__ S, int rows,
+                                                          int K, uint16_t* __restrict__ hi,
+                                                          uint16_t* __restrict__ lo) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)rows * K) return;
+  const size_t row = i / K, k = i - row * K;
+  const uint8_t b = Q[row * (K / 2) + k / 2];
+  const int q = int((k & 1) ? (b >> 4) : (b & 15)) - 8;
+  const float w = bf16_to_f32(S[row * (K / 32) + k / 32]) * float(q);
+  const uint16_t h = f32_to_bf16(w);
+  hi[i] = h;
+  lo[i] = f32_to_bf16(w - bf16_to_f32(h));
+}
+
+hipError_t launch_dequant_i4_split(const uint8_t* Q, const uint16_t* S, int rows, int K, uint16_t* hi,
+                                   uint16_t* lo, hipStream_t s) {
+  if (rows <= 0 || K <= 0 || (K % 32)) return hipErrorInvalidValue;
+  const size_t n = (size_t)rows * K;
+  hipLaunchKernelGGL(k_dequant_i4_split, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Q, S, rows, K,
+                     hi, lo);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_i4(const uint16_t* W, int rows, int K, uint8_t* Q, uint16_t* S, hipStream_t s) {
   if (rows <= 0 || K <= 0 || (K % 32)) return hipErrorInvalidValue;
   const size_t groups = (size_t)rows * (K / 32);

@@ -30,6 +30,10 @@ int gemv_grid(int N, int cfg);  // blocks (= partial sums) of a launch over N ro
 // divisions IEEE fp32.
 hipError_t launch_quant_i4(const uint16_t* W, int rows, int K, uint8_t* Q, uint16_t* S,
                            hipStream_t s);
+// The int4 matrix (Q, S) [rows][K] as bf16 (hi, lo) with hi + lo == scale * q exactly
+// (the weights of the teacher-forced MFMA passes).
+hipError_t launch_dequant_i4_split(const uint8_t* Q, const uint16_t* S, int rows, int K, uint16_t* hi,
+                                   uint16_t* lo, hipStream_t s);
 
 // g[r] = fc[r,:] . [aux0; aux1; aux2]
 hipError_t launch_encode(const uint16_t* w_fc, const uint16_t* S, int n, const float* a0,
