@@ -427,8 +427,8 @@ __global__ __launch_bounds__(256) void k_attn_mid(VerifyArgs a, int chunk, int S
 // of a 32-wide k step, and gets S^T[rows 4 (l / 16) + v][query l % 16]).  A lane thus
 // holds 8 scores of one query (rows 4g + v and 16 + 4g + v, g = l / 16): exactly an A
 // operand of O += P V over the 32 rows, when the MFMA's k slot 8g + v stands for row
-// 4g + v and slot 8g + 4 + v for row 16 + 4g + v; V's B operand (dim 16t + l % 16)
-// is loaded in that row order.  O's D layout holds queries 4g + v, so the online
+// 4g + v and slot 8g + 4 + v for row 16 + 4g + v; V's B operand is loaded in that
+// row order, 16 bytes of a row per lane (the output tiles' dims interleaved to match).  O's D layout holds queries 4g + v, so the online
 // softmax rescale factors move there by shuffles.  fp32 operands enter as bf16
 // (hi, lo) pairs, x = hi + lo to 2^-18, and hi*hi + hi*lo + lo*hi is summed.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -452,6 +452,11 @@ __global__ __launch_bounds__(256) void k_attn_mid_mfma(VerifyArgs a, int chunk, 
   constexpr int NT = HD / 16;  // 16-wide output dim tiles
   constexpr int KS = HD / 32;  // k steps of S
   constexpr bool F32 = sizeof(KT) == 4;
+  // V elements per load (bf16: 16 bytes, or 8 at head_dim 64; fp32: one element,
+  // which measured faster at 32K rows than 16-byte loads, 96.5 against 110.8 us)
+  // and dims per group of output tiles
+  constexpr int VE = F32 ? 1 : (KvVec<KT>::E < NT ? KvVec<KT>::E : NT);
+  constexpr int VD = 16 * VE;
   __shared__ float so[kAttnWaves][16][HD + 4];
   __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
 
@@ -489,13 +494,27 @@ __global__ __launch_bounds__(256) void k_attn_mid_mfma(VerifyArgs a, int chunk, 
   for (int tb = r0 + 32 * wv; tb < r1; tb += 32 * kAttnWaves) {
     // V's B operands (rows in slot order, dim 16 t + c16) are requested first, so
     // they arrive with K's
+    // Output tile t = VE * grp + k holds dim VD * grp + VE * c16 + k (VE elements per
+    // load, VD = 16 VE dims per group): one load per row and group gives a lane VE
+    // tiles' operands, 16 lanes reading 16 VE contiguous elements.
     float vx[NT][8];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int grp = 0; grp < HD / VD; ++grp)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        vx[t][v] = kv_elem(Vb + (size_t)min(tb + 4 * g4 + v, rlast) * HD + 16 * t + c16);
-        vx[t][4 + v] = kv_elem(Vb + (size_t)min(tb + 16 + 4 * g4 + v, rlast) * HD + 16 * t + c16);
+      for (int v = 0; v < 8; ++v) {
+        const int row = min(tb + (v < 4 ? 4 * g4 + v : 16 + 4 * g4 + (v - 4)), rlast);
+        const KT* vp = Vb + (size_t)row * HD + VD * grp + VE * c16;
+        float e[8];
+        if constexpr (VE == 1) {
+          e[0] = kv_elem(vp);
+        } else if constexpr (VE * sizeof(KT) == 16) {
+          KvVec<KT>::unpack(*reinterpret_cast<const uint4*>(vp), e);
+        } else {  // 4 bf16
+          const uint2 w = *reinterpret_cast<const uint2*>(vp);
+          e[0] = bf16_lo(w.x); e[1] = bf16_hi(w.x); e[2] = bf16_lo(w.y); e[3] = bf16_hi(w.y);
+        }
+#pragma unroll
+        for (int k = 0; k < VE; ++k) vx[VE * grp + k][v] = e[k];
       }
     // S^T for rows tb + 16 h + (0..15): A = K rows, B = queries
     f32x4_t st[2];
@@ -583,7 +602,7 @@ __global__ __launch_bounds__(256) void k_attn_mid_mfma(VerifyArgs a, int chunk, 
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) so[wv][4 * g4 + v][16 * t + c16] = o[t][v];
+    for (int v = 0; v < 4; ++v) so[wv][4 * g4 + v][VD * (t / VE) + VE * c16 + (t % VE)] = o[t][v];
   __syncthreads();
   const bool direct = S == 1;
   for (int i = threadIdx.x; i < 16 * HD; i += blockDim.x) {

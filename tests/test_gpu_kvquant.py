@@ -17,7 +17,7 @@ import torch
 
 from eagle_draft_head_amd import binding as B
 from eagle_draft_head_amd.drafter import Drafter
-from oracle import kvquant
+from oracle import int4, kvquant
 from synth import TINY, gen, small_variant
 from tests.common import aux_np, make_oracle, toks_np
 from tests.gpu_harness import check_round, compare_round, say, to_dev_aux
@@ -81,15 +81,20 @@ def _kv_close(dr, orc, R):
         assert off.mean() < 1e-2, off.mean()
 
 
-@pytest.mark.parametrize("cfg,L,rounds,gamma,local", [(TINY, 63, 24, 3, False), (HD128, 200, 12, 4, False),
-                                                      (TINY, 63, 8, 4, True), (TINY, 0, 4, 5, False)],
-                         ids=["tiny", "hd128", "tiny-round-local", "empty"])
-def test_kvq_chain_parity(cfg, L, rounds, gamma, local):
-    say(f"[kvq] {cfg.name} L={L} rounds={rounds} gamma={gamma} local={local}")
+@pytest.mark.parametrize("cfg,L,rounds,gamma,local,i4", [(TINY, 63, 24, 3, False, False),
+                                                         (HD128, 200, 12, 4, False, False),
+                                                         (TINY, 63, 8, 4, True, False),
+                                                         (TINY, 0, 4, 5, False, False),
+                                                         (TINY, 63, 12, 3, False, True)],
+                         ids=["tiny", "hd128", "tiny-round-local", "empty", "tiny-int4-weights"])
+def test_kvq_chain_parity(cfg, L, rounds, gamma, local, i4):
+    say(f"[kvq] {cfg.name} L={L} rounds={rounds} gamma={gamma} local={local} int4={i4}")
     wd = gen.drafter_weights(cfg, device="cuda")
     max_ctx = L + rounds * (gamma + 1) + 16
-    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, kv_dtype=B.KV_Q8Q5)
-    orc = make_oracle(cfg, {k: v.cpu() for k, v in wd.items()}, max_ctx=max_ctx, kv_format="q8q5")
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, kv_dtype=B.KV_Q8Q5,
+                 weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16)
+    wh = {k: v.cpu() for k, v in wd.items()}
+    orc = make_oracle(cfg, int4.int4_weights(wh) if i4 else wh, max_ctx=max_ctx, kv_format="q8q5")
     aux, toks = aux_np(cfg, 0, L), toks_np(cfg, 0, L)
     orc.prefill(0, aux, toks)
     dr.prefill(0, torch.as_tensor(toks, dtype=torch.int32).cuda(), to_dev_aux(aux))

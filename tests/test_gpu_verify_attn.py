@@ -43,6 +43,7 @@ def _oracle(q, k, v, ctx, M):
 @pytest.mark.parametrize("nh,nkv,hd,ctx,M,kv", [
     (4, 2, 64, 0, 4, B.KV_F32),        # empty context: the window alone
     (4, 2, 64, 37, 1, B.KV_F32),       # one query row (decode)
+    (4, 2, 64, 513, 3, B.KV_BF16),     # head_dim 64 bf16: 8-byte V operand loads
     (8, 2, 128, 300, 5, B.KV_BF16),    # 4 heads per KV head, 20 query vectors
     (16, 4, 256, 50, 8, B.KV_F32),
     (6, 2, 64, 1000, 4, B.KV_F32),     # 3 heads per KV head: ragged query groups
