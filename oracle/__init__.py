@@ -21,14 +21,17 @@ Sources (page titles as published):
            (CUDA)" (description)
 
 Parity pins: every function is pinned by a `-m "not gpu"` test against closed
-forms, library routines, invariants the pages state, or brute force.  One part
-is "parity unpinned": the op order and structure of the layer beyond the
-pages' own text (which norm goes where, the concat order, the pre-norm
-residual, the token/feature pairing) — no golden tensors, checkpoints or the
-vLLM code the memra module doc calls authoritative are available.
+forms, library routines, invariants the pages state, or brute force.  The layer's
+structure (concat order, which norm sits where, the pre-norm residual, the MLP's
+gate/up roles, rotary placement) is pinned by exact consequences of the memra
+module doc's op sequence, each shown to fail under a planted mistake
+(tests/test_oracle_structure.py).  One reading has no numerical pin ("parity
+unpinned"): the token/feature pairing of committed rows (taps of position r with
+the token at r + 1), taken from the ExecuTorch PR #20153 description and fixed by
+the entry points' semantics rather than by a value any test can derive.
 """
 from .numerics import (argmax_first, attention_causal, attention_decode, attention_verify,
-                       bf16_bits_to_f64, rms_norm, rope_neox_partial, silu)
+                       bf16_bits_to_f64, rms_norm, rope_neox_partial, round_bf16, silu)
 from .drafter import DrafterOracle, StatelessChain
 from .ledger import Ledger, LedgerError
 from .rope_width import resolve_rope_dim
@@ -38,7 +41,7 @@ from .loop import greedy_plain, greedy_speculative
 
 __all__ = [
     "argmax_first", "attention_causal", "attention_decode", "attention_verify", "bf16_bits_to_f64",
-    "rms_norm", "rope_neox_partial", "silu", "DrafterOracle", "StatelessChain",
+    "rms_norm", "rope_neox_partial", "round_bf16", "silu", "DrafterOracle", "StatelessChain",
     "Ledger", "LedgerError", "resolve_rope_dim", "TrunkOracle", "greedy_plain",
     "greedy_speculative", "int4", "kvquant",
 ]

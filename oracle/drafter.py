@@ -34,7 +34,7 @@ import numpy as np
 from . import kvquant
 from .ledger import Ledger
 from .numerics import (argmax_first, attention_causal, attention_decode,
-                       bf16_bits_to_f64, rms_norm, rope_neox_partial, silu)
+                       bf16_bits_to_f64, rms_norm, rope_neox_partial, round_bf16, silu)
 
 WEIGHT_NAMES = ("fc", "input_layernorm", "hidden_norm", "q_proj", "k_proj",
                 "v_proj", "o_proj", "post_attention_layernorm", "gate_proj",
@@ -80,10 +80,13 @@ class DrafterOracle:
                  embed: Union[np.ndarray, Callable[[np.ndarray], np.ndarray], object],
                  d2t, max_ctx: int = 0, max_seqs: int = 1, max_gamma: int = 16,
                  kv_format: str = "exact"):
-        """kv_format: "exact" keeps K/V rows as computed; "q8q5" stores each row
-        in its quantized form (oracle.kvquant: q8_0 K, q5_1 V) and every read of
-        the cache, the new row's included, sees those values."""
-        assert kv_format in ("exact", "q8q5"), kv_format
+        """kv_format: "exact" keeps K/V rows as computed; "bf16" stores every
+        element of a row rounded to the nearest bfloat16 (ties to even); "q8q5"
+        stores each row in its quantized form (oracle.kvquant: q8_0 K, q5_1 V).
+        With "bf16" and "q8q5" every read of the cache, the new row's own
+        attention included, sees the stored values."""
+        assert kv_format in ("exact", "bf16", "q8q5"), kv_format
+        self.kv_format = kv_format
         self.kv_q = kv_format == "q8q5"
         self.n = geom.n_embd
         self.nh = geom.n_head
@@ -211,6 +214,8 @@ class DrafterOracle:
     # ------------------------------------------------------------------
     def _kv_rows(self, k, v):
         """The K/V rows as the cache stores them."""
+        if self.kv_format == "bf16":
+            return round_bf16(k), round_bf16(v)
         if not self.kv_q:
             return k, v
         return kvquant.k_stored(k), kvquant.v_stored(v)

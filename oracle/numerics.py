@@ -27,6 +27,16 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def round_bf16(x) -> np.ndarray:
+    """Round fp64 values to the nearest bfloat16 (8 significant bits), ties to
+    even, returned as fp64.  Exact for the normal bf16 range: with x = m * 2^e and
+    0.5 <= |m| < 1, the kept significand is rint(m * 2^8) (rint rounds half to
+    even) and the value is that times 2^(e - 8)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis (memra module doc: the four RMSNorms of the
     op-sequence; formula per the reading in the module docstring)."""

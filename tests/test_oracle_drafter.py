@@ -233,3 +233,27 @@ def test_page4_drafter_is_about_0p8_gb():
     assert s["fc"] == (4096, 12288) and s["q_proj"] == (4096, 8192)
     assert s["k_proj"] == (1024, 8192) and s["lm_head"] == (32000, 4096)
     assert s["gate_proj"] == (12288, 4096) and s["down_proj"] == (4096, 12288)
+
+
+def test_bf16_kv_cache_holds_the_rounded_exact_rows(tiny_w):
+    """kv_format="bf16": every stored K/V element is the exact row rounded to the
+    nearest bfloat16, teacher-forced and chain rows alike, and the chain stays
+    close to the exact-KV chain."""
+    from oracle import round_bf16
+    L = 40
+    aux, toks = aux_np(TINY, 3, L + 1), toks_np(TINY, 3, L + 1)
+    de = make_oracle(TINY, tiny_w)
+    db = make_oracle(TINY, tiny_w, kv_format="bf16")
+    for d in (de, db):
+        d.prefill(0, row_slice(aux, 0, L), toks[:L])
+    assert np.array_equal(db.K[0][:L], round_bf16(de.K[0][:L]))
+    assert np.array_equal(db.V[0][:L], round_bf16(de.V[0][:L]))
+    kb = torch.from_numpy(db.K[0][:L].copy()).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(kb, db.K[0][:L])          # representable in bf16
+    b_aux = [a[L] for a in aux]
+    re = de.draft_chain(0, b_aux, toks[L], 3, keep_spec=True)
+    rb = db.draft_chain(0, b_aux, toks[L], 3, keep_spec=True)
+    # the chain's first row: the rounded form of what the exact mode computed
+    assert np.array_equal(db.K[0][L], round_bf16(re[0].k)) and np.array_equal(rb[0].k, db.K[0][L])
+    assert not np.array_equal(rb[0].logits, re[0].logits)   # the rounding is seen
+    assert np.abs(rb[0].logits - re[0].logits).max() < 5e-3

@@ -150,3 +150,23 @@ def test_verify_attention_against_torch_sdpa_with_a_window_mask(nh, nkv, hd, ctx
     # and the window is the tail of causal self-attention over all T rows
     Qf = np.concatenate([rng.normal(0, 1, (ctx, nh, hd)), Q])
     assert np.allclose(attention_causal(Qf, K[:T], V[:T])[ctx:], O, rtol=1e-12, atol=1e-14)
+
+
+def test_round_bf16_against_torch_and_ties():
+    from oracle import round_bf16
+    # fp32 inputs: torch's float32 -> bfloat16 conversion rounds to nearest even
+    x = torch.randn(20000, dtype=torch.float32) * torch.exp(torch.randn(20000) * 4)
+    want = x.to(torch.bfloat16).double().numpy()
+    assert np.array_equal(round_bf16(x.double().numpy()), want)
+    # hand-made ties: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> 1 (even);
+    # 1 + 3 * 2^-8 between 1 + 2^-7 (odd) and 1 + 2^-6 (even) -> 1 + 2^-6
+    assert round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    assert round_bf16(np.array([-(1 + 3 * 2.0 ** -8)]))[0] == -(1 + 2.0 ** -6)
+    # just past a tie rounds up; representable values and zero are unchanged
+    assert round_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1 + 2.0 ** -7
+    v = np.array([0.0, -0.0, 1.5, -3.0 * 2.0 ** -20, 2.0 ** 100])
+    assert np.array_equal(round_bf16(v), v)
+    # error at most half an ulp: 2^(e-8) <= |y| 2^-8 for y in [2^e, 2^(e+1))
+    y = rng.normal(0, 1, 1000)
+    assert np.all(np.abs(round_bf16(y) - y) <= np.abs(y) * 2.0 ** -8)
