@@ -131,7 +131,7 @@ def main():
     ap.add_argument("--gamma", type=int, default=0, help="override the workload's chain length")
     ap.add_argument("--kernel", default=None)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-rounds", type=int, default=3)
+    ap.add_argument("--cpu-rounds", type=int, default=5)
     ap.add_argument("--kv", choices=["f32", "bf16", "q8q5"], default="f32",
                     help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -576,69 +576,97 @@ def run_batched(args, cfg):
     dr.close()
 
 
-def cpu_baseline_batched(cfg, wd, lens, b_aux, b_tok, gamma):
-    """The oracle on a sample of the batched workload: the chain rounds of the two
-    shortest sequences (their prefill is untimed setup)."""
+def _blas_threads_and_vendor():
+    """(threads the BLAS may use = the CPUs this process is allowed on, vendor)."""
+    cores = len(os.sched_getaffinity(0))
+    vendor = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            vendor = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+    except Exception:
+        pass
+    return cores, vendor
+
+
+def _timed_rounds(fn, rounds, threads):
+    """Median seconds of `rounds` calls of fn(r) with the BLAS limited to `threads`."""
+    from contextlib import nullcontext
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=threads, user_api="blas")
+    except Exception:
+        ctx = nullcontext()
+    times = []
+    with ctx:
+        for r in range(rounds):
+            t1 = time.perf_counter()
+            fn(r)
+            times.append(time.perf_counter() - t1)
+    return sorted(times)[len(times) // 2]
+
+
+def cpu_baseline_batched(cfg, wd, lens, b_aux, b_tok, gamma, rounds=5):
+    """The oracle's fp32 timing mode on a sample of the batched workload: chain
+    rounds of the shortest sequence (its prefill is untimed setup); a batched round
+    on the host is the sequences' rounds one after another, so tokens/s is the
+    per-sequence rate."""
     import numpy as np
     from synth import gen
     from tests.common import make_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    cores, vendor = _blas_threads_and_vendor()
     wh = {k: v.cpu() for k, v in wd.items() if k != "embed"}
-    pick = sorted(range(len(lens)), key=lambda s: lens[s])[:2]
-    orc = make_oracle(cfg, wh, max_ctx=cfg.max_ctx, max_seqs=len(lens), lazy_embed=True)
+    s = int(np.argmin(lens))
+    orc = make_oracle(cfg, wh, max_ctx=cfg.max_ctx, max_seqs=len(lens), lazy_embed=True,
+                      dtype=np.float32)
+    aux = gen.aux_taps(cfg, 100 + s, lens[s])
+    tok = gen.tokens(cfg, 100 + s, lens[s])
+    orc.prefill(s, [a.numpy() for a in aux], tok.numpy())
     S = len(lens)
-    drafted, spent = 0, 0.0
-    for s in pick:
-        aux = gen.aux_taps(cfg, 100 + s, lens[s])
-        tok = gen.tokens(cfg, 100 + s, lens[s])
-        orc.prefill(s, [a.double().numpy() for a in aux], tok.numpy())
-        t1 = time.perf_counter()
-        recs = orc.draft_chain(s, [a[s].double().cpu().numpy() for a in b_aux], int(b_tok[s]), gamma)
-        spent += time.perf_counter() - t1
-        drafted += len(recs)
-    return {"value": round(drafted / spent, 3), "unit": "draft tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle: one gamma={gamma} chain round of each of the sequences "
-                      f"{pick} (committed rows {[lens[s] for s in pick]}), sequentially; prefill untimed"}
+
+    def one(r):
+        orc.draft_chain(s, [a[r * S + s].cpu().numpy() for a in b_aux], int(b_tok[r * S + s]), gamma)
+
+    med = _timed_rounds(one, rounds, cores)
+    med1 = _timed_rounds(one, 3, 1)
+    return {"value": round(gamma / med, 3), "unit": "draft tokens/s", "cores": cores,
+            "kind": "oracle fp32", "blas": vendor, "value_1thread": round(gamma / med1, 3),
+            "sample": f"the oracle's fp32 timing mode (numpy): median of {rounds} gamma={gamma} "
+                      f"chain rounds of sequence {s} ({lens[s]} committed rows) with {cores} BLAS "
+                      f"threads, and of 3 rounds with 1 thread; a batched round on the host runs "
+                      f"the sequences one after another; prefill untimed"}
 
 
 def cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, rounds, int4_weights=False):
-    """The oracle as it stands (fp64 numpy) on the host: prefill of the committed
-    rows (untimed setup), then `rounds` chain rounds of gamma steps, timed."""
+    """The oracle's fp32 timing mode (numpy) on the host: prefill of the committed
+    rows (untimed setup), then chain rounds of gamma steps, the median of `rounds`
+    with the BLAS on every allowed CPU and of 3 rounds on one thread."""
     import numpy as np
-    import torch
-    from synth import gen
     from tests.common import make_oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    cores, vendor = _blas_threads_and_vendor()
     wh = {k: v.cpu() for k, v in wd.items() if k != "embed"}
     if int4_weights:  # the same int4 weights the GPU streams (untimed setup)
         from oracle import int4
         wh = int4.int4_weights(wh)
     L = int(tok_c.numel())
-    orc = make_oracle(cfg, wh, max_ctx=L + 64, lazy_embed=True)
+    orc = make_oracle(cfg, wh, max_ctx=L + 64, lazy_embed=True, dtype=np.float32)
     t0 = time.perf_counter()
-    orc.prefill(0, [a.double().cpu().numpy() for a in aux_c], tok_c.cpu().numpy())
+    orc.prefill(0, [a.cpu().numpy() for a in aux_c], tok_c.cpu().numpy())
     setup_s = time.perf_counter() - t0
-    times = []
-    for r in range(rounds):
-        ba = [a[r].double().cpu().numpy() for a in b_aux]
-        t1 = time.perf_counter()
-        orc.draft_chain(0, ba, int(b_tok[r]), gamma)
-        times.append(time.perf_counter() - t1)
-    med = sorted(times)[len(times) // 2]
-    return {"value": round(gamma / med, 4), "unit": "draft tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle{' (int4 weights)' if int4_weights else ''}: {rounds} chain "
-                      f"rounds of gamma={gamma} over {L} committed "
-                      f"rows (median round {med:.2f}s; untimed setup prefill {setup_s:.1f}s)"}
+
+    def one(r):
+        orc.draft_chain(0, [a[r].cpu().numpy() for a in b_aux], int(b_tok[r]), gamma)
+
+    med = _timed_rounds(one, rounds, cores)
+    med1 = _timed_rounds(one, 3, 1)
+    return {"value": round(gamma / med, 4), "unit": "draft tokens/s", "cores": cores,
+            "kind": "oracle fp32", "blas": vendor, "value_1thread": round(gamma / med1, 4),
+            "sample": f"the oracle's fp32 timing mode (numpy"
+                      f"{', int4 weights' if int4_weights else ''}): median of {rounds} chain rounds "
+                      f"of gamma={gamma} over {L} committed rows with {cores} BLAS threads "
+                      f"({med:.3f} s a round), and of 3 rounds with 1 thread ({med1:.3f} s); "
+                      f"untimed setup prefill {setup_s:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -80,6 +80,7 @@ struct eagle3_ctx {
   char* kv = nullptr;
   int kv_f32 = 1;
   int kv_q = 0;             // quantized K/V regions (q8_0 K, q5_1 V); elements are bytes
+  int tf_split = 0;         // teacher-forced MFMA passes take (hi, lo) bf16 activation pairs
   float* kv_stage = nullptr;  // kv_q: the chain step's new K/V row in fp32 [2][kvd]
   size_t kv_esize = 4;      // bytes per cache element
   size_t kv_seq_elems = 0;  // K + V elements per sequence
@@ -257,6 +258,9 @@ int validate_config(const eagle3_config* cfg, const char** why) {
     return bad("quantized KV: batch-1 drafting only (max_seqs 1)", EAGLE3_E_UNSUPPORTED);
   if (cfg->weight_format != EAGLE3_WEIGHTS_BF16 && cfg->weight_format != EAGLE3_WEIGHTS_I4)
     return bad("unknown weight_format", EAGLE3_E_INVAL);
+  if (cfg->append_act != EAGLE3_APPEND_DEFAULT && cfg->append_act != EAGLE3_APPEND_BF16 &&
+      cfg->append_act != EAGLE3_APPEND_SPLIT)
+    return bad("unknown append_act", EAGLE3_E_INVAL);
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
     if (cfg->max_seqs != 1) return bad("int4 weights: batch-1 drafting only (max_seqs 1)", EAGLE3_E_UNSUPPORTED);
     if (cfg->n_embd % 32 || (int64_t(cfg->n_head) * cfg->head_dim) % 32 || cfg->n_ff % 32)
@@ -453,7 +457,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
   E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
   E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));
-  if (c->kv_f32 || c->kv_q) {  // fp32-grade K/V rows (quantized ones are decided from them)
+  c->tf_split = cfg->append_act == EAGLE3_APPEND_DEFAULT ? (c->kv_f32 || c->kv_q)
+                                                         : cfg->append_act == EAGLE3_APPEND_SPLIT;
+  if (c->tf_split) {  // fp32-grade K/V rows
     E3_TRY(dalloc(c, &c->tf_A_lo, size_t(c->tf_rows) * 3 * n));
     E3_TRY(dalloc(c, &c->tf_cat16_lo, size_t(c->tf_rows) * 2 * n));
   }

@@ -78,6 +78,7 @@ typedef struct {
   int32_t max_seqs;      /* sequence slots */
   int32_t kv_dtype;      /* EAGLE3_KV_F32 (default), EAGLE3_KV_BF16 or EAGLE3_KV_Q8Q5 */
   int32_t weight_format; /* EAGLE3_WEIGHTS_BF16 (default) or EAGLE3_WEIGHTS_I4, see below */
+  int32_t append_act;    /* activations of the teacher-forced MFMA passes, see below */
 } eagle3_config;
 
 /* Draft-KV precision.  EAGLE3_KV_F32 stores K/V rows in fp32 and feeds the
@@ -87,6 +88,17 @@ typedef struct {
    that alone moves draft logits by about 1-2e-2 relative to exact arithmetic. */
 #define EAGLE3_KV_F32 0
 #define EAGLE3_KV_BF16 1
+
+/* Activations of the teacher-forced (prefill / rebuild) MFMA passes of more than
+   16 rows, whose weights are exact in bf16: EAGLE3_APPEND_BF16 rounds the fp32
+   taps and the normalised K/V-projection inputs to bf16 once (one MFMA product);
+   EAGLE3_APPEND_SPLIT feeds them as two bf16 terms hi + lo (two products,
+   fp32-grade rows, twice the MFMA work).  EAGLE3_APPEND_DEFAULT (0) is SPLIT for
+   EAGLE3_KV_F32 and EAGLE3_KV_Q8Q5 and BF16 for EAGLE3_KV_BF16.  Passes of at most
+   16 rows stream the weights through fp32 GEMVs either way. */
+#define EAGLE3_APPEND_DEFAULT 0
+#define EAGLE3_APPEND_BF16 1
+#define EAGLE3_APPEND_SPLIT 2
 /* EAGLE3_KV_Q8Q5: K rows in q8_0 and V rows in q5_1, blocks of 32 values along
    head_dim (memra_engine `eagle.rs`, `Eagle3Scratch` doc and `attn`: the draft
    layer appends quantized K/V rows and decode attention reads the quantized views;
@@ -107,7 +119,9 @@ typedef struct {
    bf16(max|w| / 7), q = clamp(rint(w / scale), -7, 7), IEEE fp32 divisions) and
    every draft step and append streams those (about 4.5 bits a weight).  Requires
    max_seqs == 1 and input widths (n_embd, n_head * head_dim, n_ff) that are
-   multiples of 32; appends run in passes of at most 16 rows. */
+   multiples of 32.  Appends of at most 16 rows stream the int4 codes through the
+   GEMVs; longer appends run each MFMA product twice, on the exact bf16 (hi, lo)
+   halves of the int4 weights of fc and of the K/V rows. */
 #define EAGLE3_WEIGHTS_BF16 0
 #define EAGLE3_WEIGHTS_I4 1
 

@@ -79,12 +79,16 @@ class DrafterOracle:
     def __init__(self, geom, weights: Dict[str, object],
                  embed: Union[np.ndarray, Callable[[np.ndarray], np.ndarray], object],
                  d2t, max_ctx: int = 0, max_seqs: int = 1, max_gamma: int = 16,
-                 kv_format: str = "exact"):
+                 kv_format: str = "exact", dtype=np.float64):
         """kv_format: "exact" keeps K/V rows as computed; "bf16" stores every
         element of a row rounded to the nearest bfloat16 (ties to even); "q8q5"
         stores each row in its quantized form (oracle.kvquant: q8_0 K, q5_1 V).
         With "bf16" and "q8q5" every read of the cache, the new row's own
-        attention included, sees the stored values."""
+        attention included, sees the stored values.
+        dtype: float64 (the parity mode) or float32 (a timing mode: the same
+        operations on fp32 arrays, used only as a CPU speed baseline)."""
+        assert dtype in (np.float64, np.float32), dtype
+        self.dt = dtype
         assert kv_format in ("exact", "bf16", "q8q5"), kv_format
         self.kv_format = kv_format
         self.kv_q = kv_format == "q8q5"
@@ -101,7 +105,8 @@ class DrafterOracle:
         # bf16 weights (bit patterns or tensors), or fp64 arrays used as given (the
         # int4 weights' exact values, oracle.int4)
         W = {k: (weights[k] if isinstance(weights[k], np.ndarray) and weights[k].dtype == np.float64
-                 else bf16_bits_to_f64(_bits(weights[k]))) for k in WEIGHT_NAMES}
+                 else bf16_bits_to_f64(_bits(weights[k]))).astype(dtype, copy=False)
+             for k in WEIGHT_NAMES}
         self.W = W
         assert W["fc"].shape == (self.n, 3 * self.n), "fc in != 3 n_embd"
         assert W["q_proj"].shape == (self.nh * self.hd, 2 * self.n), "q_proj shape"
@@ -122,8 +127,8 @@ class DrafterOracle:
         if max_ctx > 0:
             self.ledger = Ledger(max_ctx, max_seqs, max_gamma)
             rows = self.ledger.rows
-            self.K = [np.zeros((rows, self.nkv, self.hd)) for _ in range(max_seqs)]
-            self.V = [np.zeros((rows, self.nkv, self.hd)) for _ in range(max_seqs)]
+            self.K = [np.zeros((rows, self.nkv, self.hd), dtype) for _ in range(max_seqs)]
+            self.V = [np.zeros((rows, self.nkv, self.hd), dtype) for _ in range(max_seqs)]
 
     # ------------------------------------------------------------------
     # pieces of the op sequence
@@ -131,12 +136,12 @@ class DrafterOracle:
     def embed(self, toks) -> np.ndarray:
         toks = np.asarray(toks, dtype=np.int64).reshape(-1)
         assert toks.min() >= 0 and toks.max() < self.vt
-        return bf16_bits_to_f64(_bits(self._embed_fn(toks)))
+        return bf16_bits_to_f64(_bits(self._embed_fn(toks))).astype(self.dt, copy=False)
 
     def encode(self, aux: Sequence[np.ndarray]) -> np.ndarray:
         """g = fc . concat(aux_0, aux_1, aux_2) (memra `encode`); rows or one vector."""
         assert len(aux) == 3
-        cat = np.concatenate([np.asarray(a, dtype=np.float64) for a in aux], axis=-1)
+        cat = np.concatenate([np.asarray(a, dtype=self.dt) for a in aux], axis=-1)
         return cat @ self.W["fc"].T
 
     def input_cat(self, g: np.ndarray, toks) -> np.ndarray:
@@ -225,7 +230,7 @@ class DrafterOracle:
         T = toks.shape[0]
         if T == 0:
             return
-        f = self.encode([np.asarray(a, dtype=np.float64).reshape(T, self.n) for a in aux])
+        f = self.encode([np.asarray(a).reshape(T, self.n) for a in aux])
         cat = self.input_cat(f, toks)
         _, k, v = self.qkv(cat, start + np.arange(T))
         k, v = self._kv_rows(k, v)
@@ -254,8 +259,7 @@ class DrafterOracle:
         over the persistent KV, then rewind (unless keep_spec)."""
         L = self.ledger.committed(s)
         g_eff = self.ledger.chain(s, gamma, keep_spec=keep_spec)
-        g = self.encode([np.asarray(a, dtype=np.float64).reshape(self.n)
-                         for a in boundary_aux])
+        g = self.encode([np.asarray(a).reshape(self.n) for a in boundary_aux])
         tok = int(boundary_tok)
         recs: List[StepRecord] = []
         for j in range(g_eff):
@@ -275,11 +279,10 @@ class DrafterOracle:
         committed length; the persistent KV and the ledger lengths are untouched."""
         L = self.ledger.committed(s)
         g_eff = self.ledger.chain(s, gamma, round_local=True)
-        g = self.encode([np.asarray(a, dtype=np.float64).reshape(self.n)
-                         for a in boundary_aux])
+        g = self.encode([np.asarray(a).reshape(self.n) for a in boundary_aux])
         tok = int(boundary_tok)
-        Ks = np.zeros((max(g_eff, 1), self.nkv, self.hd))
-        Vs = np.zeros((max(g_eff, 1), self.nkv, self.hd))
+        Ks = np.zeros((max(g_eff, 1), self.nkv, self.hd), self.dt)
+        Vs = np.zeros((max(g_eff, 1), self.nkv, self.hd), self.dt)
         recs: List[StepRecord] = []
         for j in range(g_eff):
             r = self.step(g, tok, L + j, Ks, Vs, nctx=j)
@@ -307,11 +310,10 @@ class StatelessChain:
         toks_c = np.asarray(committed_toks, dtype=np.int64).reshape(-1)
         L = toks_c.shape[0]
         if L:
-            G_c = d.encode([np.asarray(a, dtype=np.float64).reshape(L, d.n)
-                            for a in committed_aux])
+            G_c = d.encode([np.asarray(a).reshape(L, d.n) for a in committed_aux])
         else:
-            G_c = np.zeros((0, d.n))
-        g = d.encode([np.asarray(a, dtype=np.float64).reshape(d.n) for a in boundary_aux])
+            G_c = np.zeros((0, d.n), d.dt)
+        g = d.encode([np.asarray(a).reshape(d.n) for a in boundary_aux])
         chain_G: List[np.ndarray] = []
         chain_T: List[int] = []
         tok = int(boundary_tok)

@@ -27,6 +27,13 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _float(x) -> np.ndarray:
+    """x as a float array: float32 stays float32 (the oracle's timing mode),
+    everything else becomes float64."""
+    x = np.asarray(x)
+    return x if x.dtype == np.float32 else x.astype(np.float64)
+
+
 def round_bf16(x) -> np.ndarray:
     """Round fp64 values to the nearest bfloat16 (8 significant bits), ties to
     even, returned as fp64.  Exact for the normal bf16 range: with x = m * 2^e and
@@ -40,7 +47,7 @@ def round_bf16(x) -> np.ndarray:
 def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis (memra module doc: the four RMSNorms of the
     op-sequence; formula per the reading in the module docstring)."""
-    x = np.asarray(x, dtype=np.float64)
+    x = _float(x)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return w * (x / np.sqrt(ms + eps))
 
@@ -53,13 +60,13 @@ def silu(x: np.ndarray) -> np.ndarray:
 def rope_neox_partial(x: np.ndarray, pos, rot: int, theta: float) -> np.ndarray:
     """Rotate the first `rot` dims of every head of x [..., heads, head_dim] at
     position(s) `pos` (scalar, or an array broadcastable to x[..., 0, 0])."""
-    x = np.asarray(x, dtype=np.float64)
+    x = _float(x)
     assert rot % 2 == 0 and 0 < rot <= x.shape[-1]
     half = rot // 2
     inv_freq = theta ** (-2.0 * np.arange(half, dtype=np.float64) / rot)
     p = np.asarray(pos, dtype=np.float64)
     ang = p[..., None, None] * inv_freq          # [..., 1, half]
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = np.cos(ang).astype(x.dtype), np.sin(ang).astype(x.dtype)
     out = x.copy()
     a, b = x[..., :half], x[..., half:rot]
     out[..., :half] = a * c - b * s
@@ -83,10 +90,10 @@ def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     """
     n_head, hd = q.shape
     n_kv = K.shape[1]
-    out = np.empty_like(q, dtype=np.float64)
+    out = np.empty_like(q, dtype=np.result_type(q, K, V))
     for h in range(n_head):
         g = _kv_head(h, n_head, n_kv)
-        s = (K[:, g, :] @ q[h]) / np.sqrt(hd)
+        s = (K[:, g, :] @ q[h]) / float(np.sqrt(hd))
         p = np.exp(s - s.max())
         out[h] = (p / p.sum()) @ V[:, g, :]
     return out
@@ -98,7 +105,7 @@ def attention_causal(Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     Q [T, n_head, hd]; K, V [T, n_head_kv, hd]  ->  O [T, n_head, hd]
     """
     T = Q.shape[0]
-    out = np.empty_like(Q, dtype=np.float64)
+    out = np.empty_like(Q, dtype=np.result_type(Q, K, V))
     for t in range(T):
         out[t] = attention_decode(Q[t], K[: t + 1], V[: t + 1])
     return out
@@ -113,7 +120,7 @@ def attention_verify(Q: np.ndarray, K: np.ndarray, V: np.ndarray, ctx: int) -> n
     Q [M, n_head, hd]; K, V [>= ctx + M, n_head_kv, hd]  ->  O [M, n_head, hd]
     """
     M = Q.shape[0]
-    out = np.empty_like(Q, dtype=np.float64)
+    out = np.empty_like(Q, dtype=np.result_type(Q, K, V))
     for m in range(M):
         out[m] = attention_decode(Q[m], K[: ctx + m + 1], V[: ctx + m + 1])
     return out

@@ -62,12 +62,25 @@ def compare_round(recs, out_ids, geff, logits, hidden, b=0) -> List[StepCompare]
 
 
 def check_round(cmp: List[StepCompare], where=""):
+    """Pinned steps: ids, logits and hidden.  The first unpinned step still has the
+    oracle's inputs (every earlier id matched), so its logits and hidden are held
+    to the same bar; only its id may differ.  Later steps are not compared."""
     for j, c in enumerate(cmp):
+        assert c.logit_err <= LOGIT_TOL, f"{where} step {j}: logits max-abs {c.logit_err:.3e}"
+        assert c.hidden_rel <= HIDDEN_TOL, f"{where} step {j}: hidden rel-L2 {c.hidden_rel:.3e}"
         if not c.pinned:
             break
         assert c.id_gpu == c.id_ref, f"{where} step {j}: id {c.id_gpu} != {c.id_ref} (margin {c.margin:.3f})"
-        assert c.logit_err <= LOGIT_TOL, f"{where} step {j}: logits max-abs {c.logit_err:.3e}"
-        assert c.hidden_rel <= HIDDEN_TOL, f"{where} step {j}: hidden rel-L2 {c.hidden_rel:.3e}"
+
+
+def compared_steps(cmp: List[StepCompare]) -> int:
+    """Steps whose logits and hidden check_round compares."""
+    n = 0
+    for c in cmp:
+        n += 1
+        if not c.pinned:
+            break
+    return n
 
 
 def to_dev_aux(aux_np_list, rows=None):

@@ -35,7 +35,7 @@ def _rounds(cfg, lens, gamma, rounds, max_ctx, seed, min_pinned=None, kv_bf16=Fa
         dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx, max_seqs=S, kv_dtype=B.KV_BF16)
     else:
         dr = gpu_drafter(cfg, wd, max_ctx=max_ctx, max_seqs=S)
-    orc = make_oracle(cfg, wh, max_ctx=max_ctx, max_seqs=S)
+    orc = make_oracle(cfg, wh, max_ctx=max_ctx, max_seqs=S, kv_format="bf16" if kv_bf16 else "exact")
     total = sum(lens)
     aux, toks = aux_np(cfg, 30, max(total, 1)), toks_np(cfg, 30, max(total, 1))
     r0 = 0
@@ -62,13 +62,9 @@ def _rounds(cfg, lens, gamma, rounds, max_ctx, seed, min_pinned=None, kv_bf16=Fa
             assert geff[s] == len(recs), (s, geff[s], len(recs))
             assert out[s, len(recs):].tolist() == [-1] * (gamma - len(recs))
             cmp = compare_round(recs, out, geff[s], logits, hidden, b=s)
-            if kv_bf16:  # the bf16 draft-KV option: ids on pinned steps, wider logit bound
-                for c in cmp:
-                    if not c.pinned:
-                        break
-                    assert c.id_gpu == c.id_ref and c.logit_err < 5e-2 and c.hidden_rel < 1e-2, c
-            else:
-                check_round(cmp, f"{cfg.name} round {rd} seq {s} (L={orc.ledger.committed(s)})")
+            # the bf16 draft-KV option is held to the same bar against the oracle's
+            # bf16 KV storage
+            check_round(cmp, f"{cfg.name} round {rd} seq {s} (L={orc.ledger.committed(s)})")
             steps += len(cmp)
             for c in cmp:
                 if not c.pinned:
@@ -181,12 +177,13 @@ def test_batched_two_sequences():
 
 def test_batched_full_size_sampled():
     """32 sequences at the full drafter size with L_b in [512, 8192] and two at the
-    capacity edge; the oracle follows four of them, the rest are checked for
-    valid ids and exact lengths."""
+    capacity edge; the oracle follows eight of them, the rest are checked for
+    valid ids and exact lengths (the edge pair, the shortest, the longest below the
+    edge and four more are followed)."""
     cfg = BATCHED
     lens = gen.batch_lengths(cfg)
     S, gamma = len(lens), cfg.gamma
-    sample = [0, 1, int(np.argmin(lens)), 5]
+    sample = sorted({0, 1, int(np.argmin(lens)), int(np.argmax(lens[2:])) + 2, 5, 11, 19, 26})
     say(f"[batched-full] generating weights; lengths {lens}")
     wd = gen.drafter_weights(cfg, device="cuda")
     wh = {k: v.cpu() for k, v in wd.items() if k != "embed"}

@@ -318,3 +318,119 @@ def test_greedy_loop_full_acceptance_on_gpu(tiny, gamma):
     out, drafted, acc = greedy_speculative(trunk, GpuChainAdapter(dr), prompt, 30, gamma)
     assert out == ref
     assert acc == drafted > 0
+
+
+class _RecordingOracleAdapter:
+    """The oracle drafter through the loop's interface, keeping every round's
+    records (ids and margins)."""
+
+    def __init__(self, d):
+        self.d = d
+        self.rounds = []
+
+    def prefill(self, s, aux, toks):
+        self.d.prefill(s, aux, toks)
+
+    def draft_chain_ids(self, s, boundary_aux, boundary_tok, gamma):
+        recs = self.d.draft_chain(s, boundary_aux, boundary_tok, gamma)
+        self.rounds.append(recs)
+        return [r.target_id for r in recs]
+
+    def rebuild_after_verify(self, s, a, aux, toks):
+        self.d.rebuild_after_verify(s, a, aux, toks)
+        self.rounds[-1] = (self.rounds[-1], a, self.d.ledger.committed(s))
+
+
+class _RecordingGpuAdapter(GpuChainAdapter):
+    def __init__(self, dr):
+        super().__init__(dr)
+        self.rounds = []
+
+    def draft_chain_ids(self, s, boundary_aux, boundary_tok, gamma):
+        ids = super().draft_chain_ids(s, boundary_aux, boundary_tok, gamma)
+        self.rounds.append(ids)
+        return ids
+
+    def rebuild_after_verify(self, s, a, aux, toks):
+        super().rebuild_after_verify(s, a, aux, toks)
+        self.rounds[-1] = (self.rounds[-1], a, self.d.kv_len(s)[0])
+
+
+@pytest.mark.parametrize("plen,gamma,max_new", [(17, 3, 60), (64, 5, 60)])
+def test_greedy_loop_accept_counts_match_the_oracle_drafter(tiny, plen, gamma, max_new):
+    """The same loop driven by the oracle drafter and by the GPU drafter: while
+    every draft step of every round so far has an oracle margin above the pinning
+    bar, the two drafters see identical inputs, so their drafts, accept counts and
+    committed lengths must agree round by round."""
+    from tests.gpu_harness import MARGIN
+    wd, wh = tiny
+    tw = gen.trunk_weights(TINY)
+    prompt = gen.tokens(TINY, 50 + plen, plen).tolist()
+    max_ctx = plen + max_new + gamma + 8
+    t1 = TrunkOracle(TINY, tw, wh["embed"], TINY.trunk_layers)
+    oa = _RecordingOracleAdapter(make_oracle(TINY, wh, max_ctx=max_ctx))
+    out_o, drafted_o, acc_o = greedy_speculative(t1, oa, prompt, max_new, gamma)
+    t2 = TrunkOracle(TINY, tw, wh["embed"], TINY.trunk_layers)
+    ga = _RecordingGpuAdapter(gpu_drafter(TINY, wd, max_ctx=max_ctx))
+    out_g, drafted_g, acc_g = greedy_speculative(t2, ga, prompt, max_new, gamma)
+    assert out_o == out_g
+    compared = 0
+    for (recs, a_o, len_o), (ids, a_g, len_g) in zip(oa.rounds, ga.rounds):
+        if not all(r.margin > MARGIN for r in recs):
+            break
+        assert ids == [r.target_id for r in recs] and a_g == a_o and len_g == len_o
+        compared += 1
+    say(f"[loop] plen={plen} gamma={gamma}: {compared} of {len(oa.rounds)} rounds compared; "
+        f"accepted {acc_g}/{drafted_g} (oracle drafter {acc_o}/{drafted_o})")
+    assert compared >= 2
+    if compared == len(oa.rounds):
+        assert (drafted_g, acc_g) == (drafted_o, acc_o)
+
+
+def _tied_weights(wh, row, lower, higher):
+    """lm_head rows `lower` < `row` < `higher` set to copies of row `row`: those
+    three logits are equal on both sides, so a step whose maximum is row `row` has
+    a three-way tie that the lowest index must win."""
+    w = dict(wh)
+    lm = wh["lm_head"].clone()
+    lm[lower] = lm[row]
+    lm[higher] = lm[row]
+    w["lm_head"] = lm
+    return w
+
+
+@pytest.mark.parametrize("batched", [False, True])
+def test_argmax_tie_takes_the_lowest_draft_index(tiny, batched):
+    wd, wh = tiny
+    L, gamma = 40, 3
+    aux, toks = aux_np(TINY, 9, L + 2), toks_np(TINY, 9, L + 2)
+    orc = make_oracle(TINY, wh, max_ctx=96)
+    orc.prefill(0, row_slice(aux, 0, L), toks[:L])
+    b_aux = [a[L] for a in aux]
+    top = orc.draft_chain(0, b_aux, toks[L], 1)[0].draft_id
+    lower, higher = top // 2, (top + TINY.draft_vocab) // 2
+    assert lower < top < higher
+    wt = _tied_weights(wh, top, lower, higher)
+    orc = make_oracle(TINY, wt, max_ctx=96, max_seqs=2)
+    S = 2 if batched else 1
+    dr = gpu_drafter(TINY, {k: v.cuda() for k, v in wt.items()}, max_ctx=96, max_seqs=S)
+    for s in range(S):
+        orc.prefill(s, row_slice(aux, 0, L), toks[:L])
+        dr.prefill(s, _tok(toks[:L]), to_dev_aux(row_slice(aux, 0, L)))
+    recs = orc.draft_chain(0, b_aux, toks[L], gamma)
+    assert recs[0].draft_id == lower and recs[0].margin == 0.0
+    assert recs[0].logits[lower] == recs[0].logits[top] == recs[0].logits[higher]
+    baux_dev = to_dev_aux([np.stack([a[L]] * S) for a in aux])
+    out, geff, logits, hidden = dr.draft_chain(list(range(S)), _tok([toks[L]] * S), baux_dev, gamma,
+                                               debug=True)
+    torch.cuda.synchronize()
+    for s in range(S):
+        lg = logits[s, 0]
+        assert lg[lower] == lg[top] == lg[higher]            # an exact three-way tie on the GPU
+        assert int(out[s, 0]) == recs[0].target_id == lower + int(wh["d2t"][lower])
+        # the tied step's logits and hidden are within the bar; later steps see the
+        # same token, so they compare as usual
+        cmp = compare_round(recs, out, geff[s], logits, hidden, b=s)
+        assert cmp[0].logit_err <= 2e-2 and cmp[0].hidden_rel <= 1e-2
+        check_round(cmp[1:], f"after the tie, seq {s}")
+    dr.close()

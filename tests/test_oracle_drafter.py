@@ -257,3 +257,27 @@ def test_bf16_kv_cache_holds_the_rounded_exact_rows(tiny_w):
     assert np.array_equal(db.K[0][L], round_bf16(re[0].k)) and np.array_equal(rb[0].k, db.K[0][L])
     assert not np.array_equal(rb[0].logits, re[0].logits)   # the rounding is seen
     assert np.abs(rb[0].logits - re[0].logits).max() < 5e-3
+
+
+@pytest.mark.parametrize("cfg,L", [(TINY, 63), (small_variant(), 120)])
+def test_fp32_timing_mode_tracks_the_fp64_oracle(cfg, L):
+    """dtype=float32 runs the same operations on fp32 arrays (a CPU speed
+    baseline only): its arrays stay fp32 and its chain stays within fp32
+    rounding of the parity mode."""
+    w = gen.drafter_weights(cfg)
+    d64 = make_oracle(cfg, w)
+    d32 = make_oracle(cfg, w, dtype=np.float32)
+    aux, toks = aux_np(cfg, 4, L + 1), toks_np(cfg, 4, L + 1)
+    for d in (d64, d32):
+        d.prefill(0, row_slice(aux, 0, L), toks[:L])
+    assert d32.K[0].dtype == np.float32 and d32.W["lm_head"].dtype == np.float32
+    assert np.allclose(d32.K[0][:L], d64.K[0][:L], rtol=1e-4, atol=1e-5)
+    b_aux = [a[L] for a in aux]
+    r64 = d64.draft_chain(0, b_aux, toks[L], 3)
+    r32 = d32.draft_chain(0, b_aux, toks[L], 3)
+    for a, b in zip(r64, r32):
+        assert b.logits.dtype == np.float32 and b.gsum.dtype == np.float32
+        assert np.abs(a.logits - b.logits).max() < 1e-3
+        if a.margin <= 0.05:
+            break
+        assert a.target_id == b.target_id
