@@ -457,8 +457,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
   E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
   E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));
-  c->tf_split = cfg->append_act == EAGLE3_APPEND_DEFAULT ? (c->kv_f32 || c->kv_q)
-                                                         : cfg->append_act == EAGLE3_APPEND_SPLIT;
+  c->tf_split = cfg->append_act != EAGLE3_APPEND_BF16;
   if (c->tf_split) {  // fp32-grade K/V rows
     E3_TRY(dalloc(c, &c->tf_A_lo, size_t(c->tf_rows) * 3 * n));
     E3_TRY(dalloc(c, &c->tf_cat16_lo, size_t(c->tf_rows) * 2 * n));

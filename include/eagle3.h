@@ -81,21 +81,23 @@ typedef struct {
   int32_t append_act;    /* activations of the teacher-forced MFMA passes, see below */
 } eagle3_config;
 
-/* Draft-KV precision.  EAGLE3_KV_F32 stores K/V rows in fp32 and feeds the
-   teacher-forced MFMA products with activations split into two bf16 terms, so
-   committed rows carry fp32-grade values.  EAGLE3_KV_BF16 halves the KV bytes
-   (and rounds prefill activations to bf16); at the drafter sizes in the tests
-   that alone moves draft logits by about 1-2e-2 relative to exact arithmetic. */
+/* Draft-KV precision.  EAGLE3_KV_F32 stores K/V rows in fp32.  EAGLE3_KV_BF16
+   halves the KV bytes: every K/V element is computed at fp32 grade and stored
+   rounded to the nearest bf16 (ties to even), and every read, a chain step's own
+   new row included, sees the stored value.  At the drafter sizes in the tests the
+   storage rounding alone moves draft logits by about 1-2e-2 against exact rows. */
 #define EAGLE3_KV_F32 0
 #define EAGLE3_KV_BF16 1
 
 /* Activations of the teacher-forced (prefill / rebuild) MFMA passes of more than
-   16 rows, whose weights are exact in bf16: EAGLE3_APPEND_BF16 rounds the fp32
-   taps and the normalised K/V-projection inputs to bf16 once (one MFMA product);
-   EAGLE3_APPEND_SPLIT feeds them as two bf16 terms hi + lo (two products,
-   fp32-grade rows, twice the MFMA work).  EAGLE3_APPEND_DEFAULT (0) is SPLIT for
-   EAGLE3_KV_F32 and EAGLE3_KV_Q8Q5 and BF16 for EAGLE3_KV_BF16.  Passes of at most
-   16 rows stream the weights through fp32 GEMVs either way. */
+   16 rows, whose weights are exact in bf16.  EAGLE3_APPEND_SPLIT (the default,
+   also EAGLE3_APPEND_DEFAULT) feeds the fp32 taps and the normalised
+   K/V-projection inputs [eN ; gN] as two bf16 terms hi + lo (two MFMA products,
+   fp32-grade rows).  EAGLE3_APPEND_BF16 rounds both to the nearest bf16 once (one
+   product, half the MFMA work); at the drafter sizes in the tests that moves
+   draft logits by 1-2.3e-2 against exact rows, as much as the parity bar allows,
+   so it is a speed option, not the default.  Passes of at most 16 rows stream the
+   weights through fp32 GEMVs either way. */
 #define EAGLE3_APPEND_DEFAULT 0
 #define EAGLE3_APPEND_BF16 1
 #define EAGLE3_APPEND_SPLIT 2

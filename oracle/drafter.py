@@ -79,14 +79,20 @@ class DrafterOracle:
     def __init__(self, geom, weights: Dict[str, object],
                  embed: Union[np.ndarray, Callable[[np.ndarray], np.ndarray], object],
                  d2t, max_ctx: int = 0, max_seqs: int = 1, max_gamma: int = 16,
-                 kv_format: str = "exact", dtype=np.float64):
+                 kv_format: str = "exact", dtype=np.float64, append_act: str = "exact"):
         """kv_format: "exact" keeps K/V rows as computed; "bf16" stores every
         element of a row rounded to the nearest bfloat16 (ties to even); "q8q5"
         stores each row in its quantized form (oracle.kvquant: q8_0 K, q5_1 V).
         With "bf16" and "q8q5" every read of the cache, the new row's own
         attention included, sees the stored values.
         dtype: float64 (the parity mode) or float32 (a timing mode: the same
-        operations on fp32 arrays, used only as a CPU speed baseline)."""
+        operations on fp32 arrays, used only as a CPU speed baseline).
+        append_act: "exact", or "bf16": the rows of a teacher-forced append of
+        more than 16 rows take their taps and their K/V-projection input
+        [eN ; gN] rounded to the nearest bfloat16 (the engine's documented
+        single-bf16 activation format for such appends; shorter ones are exact)."""
+        assert append_act in ("exact", "bf16"), append_act
+        self.append_bf16 = append_act == "bf16"
         assert dtype in (np.float64, np.float32), dtype
         self.dt = dtype
         assert kv_format in ("exact", "bf16", "q8q5"), kv_format
@@ -230,8 +236,14 @@ class DrafterOracle:
         T = toks.shape[0]
         if T == 0:
             return
-        f = self.encode([np.asarray(a).reshape(T, self.n) for a in aux])
+        taps = [np.asarray(a).reshape(T, self.n) for a in aux]
+        rounded = self.append_bf16 and T > 16
+        if rounded:
+            taps = [round_bf16(a).astype(self.dt) for a in taps]
+        f = self.encode(taps)
         cat = self.input_cat(f, toks)
+        if rounded:
+            cat = round_bf16(cat).astype(self.dt)
         _, k, v = self.qkv(cat, start + np.arange(T))
         k, v = self._kv_rows(k, v)
         self.K[s][start:start + T] = k

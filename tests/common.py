@@ -10,7 +10,7 @@ from synth.configs import DrafterConfig
 
 def make_oracle(cfg: DrafterConfig, weights=None, max_ctx: int = 0, max_seqs: int = 1,
                 max_gamma: int = 16, lazy_embed: bool = False, kv_format: str = "exact",
-                dtype=np.float64):
+                dtype=np.float64, append_act: str = "exact"):
     from oracle import DrafterOracle
     if weights is None:
         weights = gen.drafter_weights(cfg, with_embed=not lazy_embed)
@@ -20,7 +20,8 @@ def make_oracle(cfg: DrafterConfig, weights=None, max_ctx: int = 0, max_seqs: in
         embed = weights["embed"]
     return DrafterOracle(cfg, weights, embed, weights["d2t"],
                          max_ctx=max_ctx or cfg.max_ctx_eff, max_seqs=max_seqs,
-                         max_gamma=max_gamma, kv_format=kv_format, dtype=dtype)
+                         max_gamma=max_gamma, kv_format=kv_format, dtype=dtype,
+                         append_act=append_act)
 
 
 def aux_np(cfg: DrafterConfig, stream: int, rows: int):

@@ -358,10 +358,12 @@ class _RecordingGpuAdapter(GpuChainAdapter):
 
 @pytest.mark.parametrize("plen,gamma,max_new", [(17, 3, 60), (64, 5, 60)])
 def test_greedy_loop_accept_counts_match_the_oracle_drafter(tiny, plen, gamma, max_new):
-    """The same loop driven by the oracle drafter and by the GPU drafter: while
-    every draft step of every round so far has an oracle margin above the pinning
-    bar, the two drafters see identical inputs, so their drafts, accept counts and
-    committed lengths must agree round by round."""
+    """The same loop driven by the oracle drafter and by the GPU drafter.  While
+    both drafters have seen identical inputs, the leading draft steps whose oracle
+    margin exceeds the pinning bar must give the same ids; when the oracle's
+    accept count falls inside that pinned prefix (or the whole round agrees), the
+    accept counts and committed lengths must agree too and the next round starts
+    from the same state."""
     from tests.gpu_harness import MARGIN
     wd, wh = tiny
     tw = gen.trunk_weights(TINY)
@@ -376,13 +378,18 @@ def test_greedy_loop_accept_counts_match_the_oracle_drafter(tiny, plen, gamma, m
     assert out_o == out_g
     compared = 0
     for (recs, a_o, len_o), (ids, a_g, len_g) in zip(oa.rounds, ga.rounds):
-        if not all(r.margin > MARGIN for r in recs):
+        p = 0
+        while p < len(recs) and recs[p].margin > MARGIN:
+            p += 1
+        assert ids[:p] == [r.target_id for r in recs[:p]]
+        if a_o < p or ids == [r.target_id for r in recs]:
+            assert a_g == a_o and len_g == len_o
+            compared += 1
+        else:
             break
-        assert ids == [r.target_id for r in recs] and a_g == a_o and len_g == len_o
-        compared += 1
     say(f"[loop] plen={plen} gamma={gamma}: {compared} of {len(oa.rounds)} rounds compared; "
         f"accepted {acc_g}/{drafted_g} (oracle drafter {acc_o}/{drafted_o})")
-    assert compared >= 2
+    assert compared >= 3
     if compared == len(oa.rounds):
         assert (drafted_g, acc_g) == (drafted_o, acc_o)
 

@@ -8,8 +8,9 @@ unpinned step), with rebuilds after full and partial acceptance in between.
 
 Every engine variant is held to the same bar against the oracle mode that
 stores its KV format: fp32 KV against exact rows, bf16 KV against rows rounded
-to bf16.  The variants also cover the teacher-forced MFMA passes with single
-bf16 activations (EAGLE3_APPEND_BF16) next to the split (hi, lo) form."""
+to bf16.  The single-bf16 teacher-forced activations (EAGLE3_APPEND_BF16) are
+held to it against the oracle's rows from bf16-rounded taps and projection
+inputs."""
 from __future__ import annotations
 
 import numpy as np
@@ -25,10 +26,11 @@ pytestmark = pytest.mark.gpu
 
 def _variants(names):
     from eagle_draft_head_amd import binding as B
+    # name: (KV format, teacher-forced activations, oracle KV format, oracle append)
     table = {
-        "f32": (B.KV_F32, B.APPEND_SPLIT, "exact"),
-        "f32-act16": (B.KV_F32, B.APPEND_BF16, "exact"),
-        "bf16": (B.KV_BF16, B.APPEND_BF16, "bf16"),
+        "f32": (B.KV_F32, B.APPEND_DEFAULT, "exact", "exact"),
+        "f32-act16": (B.KV_F32, B.APPEND_BF16, "exact", "bf16"),
+        "bf16": (B.KV_BF16, B.APPEND_DEFAULT, "bf16", "exact"),
     }
     return [(n,) + table[n] for n in names]
 
@@ -52,11 +54,11 @@ def _setup(cfg, L, max_ctx, variants):
     aux_h = [a.double().cpu().numpy() for a in aux]
     tok_h = tok.cpu().numpy()
     pairs = []
-    for name, kv, act, fmt in _variants(variants):
+    for name, kv, act, fmt, oact in _variants(variants):
         dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, kv_dtype=kv, append_act=act)
         dr.prefill(0, tok, aux)
-        say(f"[fullsize] {cfg.name} {name}: oracle prefill of {L} rows ({fmt} KV)")
-        orc = make_oracle(cfg, wh, max_ctx=max_ctx, lazy_embed=True, kv_format=fmt)
+        say(f"[fullsize] {cfg.name} {name}: oracle prefill of {L} rows ({fmt} KV, {oact} appends)")
+        orc = make_oracle(cfg, wh, max_ctx=max_ctx, lazy_embed=True, kv_format=fmt, append_act=oact)
         orc.prefill(0, aux_h, tok_h)
         pairs.append(_Pair(name, dr, orc))
     del wd

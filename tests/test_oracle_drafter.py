@@ -281,3 +281,26 @@ def test_fp32_timing_mode_tracks_the_fp64_oracle(cfg, L):
         if a.margin <= 0.05:
             break
         assert a.target_id == b.target_id
+
+
+def test_bf16_append_activations_round_taps_and_projection_inputs(tiny_w):
+    """append_act="bf16": a row of an append of more than 16 rows equals the exact
+    row computed from bf16-rounded taps with its [eN ; gN] rounded before the K/V
+    projection; appends of at most 16 rows are exact."""
+    from oracle import round_bf16
+    L = 30
+    aux, toks = aux_np(TINY, 5, L + 1), toks_np(TINY, 5, L + 1)
+    db = make_oracle(TINY, tiny_w, append_act="bf16")
+    db.prefill(0, row_slice(aux, 0, L), toks[:L])
+    de = make_oracle(TINY, tiny_w)
+    f = de.encode([round_bf16(a[:L]) for a in aux])
+    cat = round_bf16(de.input_cat(f, toks[:L]))
+    _, k, v = de.qkv(cat, np.arange(L))
+    assert np.array_equal(db.K[0][:L], k) and np.array_equal(db.V[0][:L], v)
+    de.prefill(0, row_slice(aux, 0, L), toks[:L])
+    assert not np.array_equal(db.K[0][:L], de.K[0][:L])
+    # a 16-row append is exact
+    db2, de2 = make_oracle(TINY, tiny_w, append_act="bf16"), make_oracle(TINY, tiny_w)
+    for d in (db2, de2):
+        d.prefill(0, row_slice(aux, 0, 16), toks[:16])
+    assert np.array_equal(db2.K[0][:16], de2.K[0][:16])
