@@ -87,6 +87,8 @@ def library() -> ctypes.CDLL:
                                               ctypes.c_size_t),
         "eagle3_verify_attention": ([P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32, c_int32,
                                      c_int32, P, P, ctypes.c_size_t, P], ctypes.c_int),
+        "eagle3_verify_attention_noalloc": ([P, P, P, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                             c_int32, c_int32, P, P], ctypes.c_int),
         "eagle3_last_error": ([P], c_char_p),
         "eagle3_profile_enable": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_profile_read": ([P, POINTER(c_double), POINTER(c_int64)], ctypes.c_int),
@@ -262,6 +264,18 @@ def eagle3_verify_attention(q, k, v, kv_dtype: int, cap: int, ctx_rows: int, M: 
                                            workspace_bytes, _stream(stream))
     if rc != OK:
         raise Eagle3Error(rc, "eagle3_verify_attention")
+
+
+VERIFY_SCRATCH_BYTES = 16 << 20
+
+
+def eagle3_verify_attention_noalloc(q, k, v, kv_dtype: int, cap: int, ctx_rows: int, M: int,
+                                    n_head: int, n_head_kv: int, head_dim: int, out,
+                                    stream=None) -> None:
+    rc = library().eagle3_verify_attention_noalloc(_ptr(q), _ptr(k), _ptr(v), kv_dtype, cap, ctx_rows,
+                                                   M, n_head, n_head_kv, head_dim, _ptr(out),
+                                                   _stream(stream))
+    _check(None, rc)
 
 
 def eagle3_last_error(ctx) -> str:

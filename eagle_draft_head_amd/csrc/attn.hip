@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 
 namespace e3 {
 
@@ -1209,6 +1210,36 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     }
   }
   return a.kv_f32 ? launch_kt<float>(a, G, chunk, S, s) : launch_kt<uint16_t>(a, G, chunk, S, s);
+}
+
+// ---------------------------------------------------------------------------
+// Device-resident scratch of the allocation-free verify attention: the split
+// partials of one call, at most kVerifyScratchBytes.  Every GPU the library runs
+// on holds its own copy until the process ends; its device address is looked up
+// once per device (with that device current) and kept.
+}  // namespace e3
+
+static __device__ __align__(256) unsigned char scratch[e3::kVerifyScratchBytes];
+
+namespace e3 {
+
+hipError_t verify_scratch_ptr(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *ptr = ptrs[dev];
+  return hipSuccess;
 }
 
 }  // namespace e3

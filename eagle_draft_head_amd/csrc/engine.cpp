@@ -655,6 +655,45 @@ int eagle3_verify_attention(const float* q_dev, const void* k_dev, const void* v
   return e == hipSuccess ? EAGLE3_OK : EAGLE3_E_HIP;
 }
 
+static_assert(EAGLE3_VERIFY_SCRATCH_BYTES == e3::kVerifyScratchBytes, "scratch size in the header");
+
+int eagle3_verify_attention_noalloc(const float* q_dev, const void* k_dev, const void* v_dev,
+                                    int32_t kv_dtype, int32_t cap, int32_t ctx_rows, int32_t M,
+                                    int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                                    float* out_dev, void* stream) {
+  g_load_error.clear();
+  if (!q_dev || !k_dev || !v_dev || !out_dev || M < 1 || ctx_rows < 0 || cap < 1 ||
+      int64_t(ctx_rows) + M > cap || n_head < 1 || n_head_kv < 1)
+    return set_err(nullptr, EAGLE3_E_INVAL, "verify attention: bad argument");
+  if (n_head % n_head_kv) return set_err(nullptr, EAGLE3_E_SHAPE, "n_head % n_head_kv != 0");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return set_err(nullptr, EAGLE3_E_UNSUPPORTED, "head_dim must be 64, 128 or 256");
+  if (kv_dtype != EAGLE3_KV_F32 && kv_dtype != EAGLE3_KV_BF16)
+    return set_err(nullptr, EAGLE3_E_UNSUPPORTED, "kv_dtype must be EAGLE3_KV_F32 or EAGLE3_KV_BF16");
+  const int f32 = kv_dtype == EAGLE3_KV_F32;
+  const size_t need = e3::attn_verify_workspace(M, n_head, n_head_kv, head_dim, ctx_rows, f32);
+  if (need > e3::kVerifyScratchBytes) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "verify attention: %zu bytes of split partials exceed the %zu-byte static scratch",
+             need, e3::kVerifyScratchBytes);
+    return set_err(nullptr, EAGLE3_E_CAPACITY, buf);
+  }
+  void* ws = nullptr;
+  hipError_t e = e3::verify_scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_fail(nullptr, e, "verify attention scratch");
+  e3::VerifyArgs a{};
+  a.q = q_dev; a.k = k_dev; a.v = v_dev; a.kv_f32 = f32;
+  a.cap = cap; a.ctx = ctx_rows; a.M = M;
+  a.n_head = n_head; a.n_head_kv = n_head_kv; a.head_dim = head_dim;
+  const size_t po = need / sizeof(float) / size_t(head_dim + 2) * size_t(head_dim);  // part_o floats
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = static_cast<float*>(ws) + po;
+  a.out = out_dev;
+  e = e3::launch_attn_verify(a, e3::kVerifyScratchBytes, as_stream(stream));
+  if (e == hipErrorInvalidValue) return set_err(nullptr, EAGLE3_E_INVAL, "verify attention: bad argument");
+  return e == hipSuccess ? EAGLE3_OK : hip_fail(nullptr, e, "verify attention launch");
+}
+
 int eagle3_kv_len(const eagle3_ctx* ctx, int32_t seq, int32_t* committed, int32_t* spec) {
   if (!ctx || !committed || !spec) return EAGLE3_E_INVAL;
   if (!ctx->ledger.valid_seq(seq)) return EAGLE3_E_INVAL;

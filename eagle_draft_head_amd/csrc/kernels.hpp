@@ -198,6 +198,9 @@ struct VerifyArgs {
 };
 size_t attn_verify_workspace(int M, int n_head, int n_head_kv, int head_dim, int ctx, int kv_f32);
 hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipStream_t s);
+// the allocation-free variant's device scratch (the current device's copy)
+constexpr size_t kVerifyScratchBytes = size_t(16) << 20;
+hipError_t verify_scratch_ptr(void** ptr);
 // Splits the context, then (when more than one split) runs the combine kernel.
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
 // Batched: split every row's context in chunks of one size, then combine per (row,

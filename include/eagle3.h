@@ -271,6 +271,23 @@ int eagle3_verify_attention(const float *q_dev, const void *k_dev, const void *v
                             int32_t n_head, int32_t n_head_kv, int32_t head_dim, float *out_dev,
                             void *workspace_dev, size_t workspace_bytes, void *stream);
 
+/* eagle3_verify_attention without a workspace argument, for callers that cannot
+   allocate device memory (code under HIP graph capture, tight serving loops,
+   harnesses that forbid allocation).  Same arguments, layouts, result and errors
+   as eagle3_verify_attention; the split partials go to a device array inside the
+   library of EAGLE3_VERIFY_SCRATCH_BYTES, of which every GPU holds one copy for the
+   life of the process.  The call allocates nothing: it looks the array's address up
+   on its first call on a device and launches the same kernels.  A call whose
+   partials (eagle3_verify_attention_workspace bytes) exceed the array returns
+   EAGLE3_E_CAPACITY before any device work; eagle3_last_error(NULL) gives the
+   message of a failing call.  Calls that overlap on one GPU (e.g. on two streams)
+   share the array and race; calls on one stream are ordered and safe. */
+#define EAGLE3_VERIFY_SCRATCH_BYTES (16u << 20)
+int eagle3_verify_attention_noalloc(const float *q_dev, const void *k_dev, const void *v_dev,
+                                    int32_t kv_dtype, int32_t cap, int32_t ctx_rows, int32_t M,
+                                    int32_t n_head, int32_t n_head_kv, int32_t head_dim,
+                                    float *out_dev, void *stream);
+
 /* Copy one int4 projection matrix (weight_format EAGLE3_WEIGHTS_I4) into caller
    buffers: codes_dev [rows][K / 2] bytes and scales_dev [rows][K / 32] bf16, in the
    layout of EAGLE3_WEIGHTS_I4.  Row order as stored: fc, o_proj, down_proj and
@@ -289,8 +306,8 @@ enum {
 int eagle3_weights_i4_read(const eagle3_ctx *ctx, int32_t matrix, void *codes_dev,
                            void *scales_dev, void *stream);
 
-/* Message of the last failing call on this handle (or of the last failing
-   eagle3_load when ctx is NULL). */
+/* Message of the last failing call on this handle (or, with ctx NULL, of the
+   last failing eagle3_load or eagle3_verify_attention_noalloc on this thread). */
 const char *eagle3_last_error(const eagle3_ctx *ctx);
 
 /* Timing of one kernel family with HIP events on the launching stream, for
