@@ -54,6 +54,22 @@ class eagle3_weights(ctypes.Structure):
         ("d2t_host", POINTER(c_int64)), ("d2t_len", c_int64), ("shape", (c_int64 * 2) * 14)]
 
 
+class eagle3_trunk_config(ctypes.Structure):
+    _fields_ = [("n_embd", c_int32), ("n_head", c_int32), ("n_head_kv", c_int32),
+                ("head_dim", c_int32), ("n_ff", c_int32), ("vocab", c_int32), ("n_layers", c_int32),
+                ("rope_theta", c_float), ("rms_eps", c_float), ("max_ctx", c_int32),
+                ("max_tokens", c_int32)]
+
+
+class eagle3_trunk_weights(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("final_norm", c_void_p), ("lm_head", c_void_p),
+                ("layers", POINTER(c_void_p)), ("shapes", POINTER(c_int64))]
+
+
+TRUNK_LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+TRUNK_BAD_TOKEN, TRUNK_NAN_LOGITS = 1, 2
+
+
 class eagle3_debug(ctypes.Structure):
     _fields_ = [("logits", c_void_p), ("hidden", c_void_p)]
 
@@ -92,6 +108,16 @@ def library() -> ctypes.CDLL:
         "eagle3_last_error": ([P], c_char_p),
         "eagle3_profile_enable": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_profile_read": ([P, POINTER(c_double), POINTER(c_int64)], ctypes.c_int),
+        "eagle3_trunk_load": ([POINTER(eagle3_trunk_config), POINTER(eagle3_trunk_weights), P, POINTER(P)],
+                              ctypes.c_int),
+        "eagle3_trunk_free": ([P], ctypes.c_int),
+        "eagle3_trunk_forward": ([P, c_int32, P, P, P, P, P, P], ctypes.c_int),
+        "eagle3_trunk_rollback": ([P, c_int32], ctypes.c_int),
+        "eagle3_trunk_len": ([P, POINTER(c_int32)], ctypes.c_int),
+        "eagle3_trunk_status": ([P, POINTER(c_uint32)], ctypes.c_int),
+        "eagle3_trunk_last_error": ([P], c_char_p),
+        "eagle3_generate": ([P, c_int32, P, POINTER(c_int32), c_int32, c_int32, c_int32, POINTER(c_int32),
+                             POINTER(c_int64), POINTER(c_int64), P], ctypes.c_int),
         "eagle3_ledger_create": ([c_int32, c_int32, c_int32, POINTER(P)], ctypes.c_int),
         "eagle3_ledger_destroy": ([P], None),
         "eagle3_ledger_prefill": ([P, c_int32, c_int32, c_int32], ctypes.c_int),
@@ -290,6 +316,81 @@ def eagle3_profile_read(ctx):
     ms, n = c_double(0), c_int64(0)
     _check(ctx, library().eagle3_profile_read(ctx, byref(ms), byref(n)))
     return ms.value, n.value
+
+
+# ---- the synthetic target trunk and the speculative runner (eagle3_trunk.h) ----
+
+def _check_trunk(t, rc: int):
+    if rc != OK:
+        msg = library().eagle3_trunk_last_error(t)
+        raise Eagle3Error(rc, (msg or b"").decode())
+
+
+def make_trunk_config(geom, n_layers: int, max_ctx: int, max_tokens: int) -> eagle3_trunk_config:
+    return eagle3_trunk_config(
+        n_embd=geom.n_embd, n_head=geom.n_head, n_head_kv=geom.n_head_kv, head_dim=geom.head_dim,
+        n_ff=geom.n_ff, vocab=geom.target_vocab, n_layers=int(n_layers),
+        rope_theta=float(geom.rope_theta), rms_eps=float(geom.rms_eps), max_ctx=int(max_ctx),
+        max_tokens=int(max_tokens))
+
+
+def make_trunk_weights(tensors: Dict[str, object], embed, n_layers: int) -> eagle3_trunk_weights:
+    """tensors: "layers.{l}.{name}", "final_norm", "lm_head" -> bf16 device tensors;
+    embed: the bf16 token embedding.  The struct keeps its pointer arrays alive."""
+    order = [embed, tensors["final_norm"], tensors["lm_head"]]
+    for l in range(n_layers):
+        order += [tensors[f"layers.{l}.{f}"] for f in TRUNK_LAYER_FIELDS]
+    shapes = []
+    for t in order:
+        shapes += list(t.shape) if t.dim() == 2 else [int(t.shape[0]), 1]
+    layers = (c_void_p * (9 * n_layers))(*[t.data_ptr() for t in order[3:]])
+    shp = (c_int64 * len(shapes))(*shapes)
+    w = eagle3_trunk_weights(order[0].data_ptr(), order[1].data_ptr(), order[2].data_ptr(),
+                             ctypes.cast(layers, POINTER(c_void_p)), ctypes.cast(shp, POINTER(c_int64)))
+    w._keep = (layers, shp)
+    return w
+
+
+def eagle3_trunk_load(cfg: eagle3_trunk_config, weights: eagle3_trunk_weights, stream=None) -> int:
+    out = c_void_p(None)
+    _check_trunk(None, library().eagle3_trunk_load(byref(cfg), byref(weights), _stream(stream), byref(out)))
+    return out.value
+
+
+def eagle3_trunk_free(t) -> None:
+    library().eagle3_trunk_free(t)
+
+
+def eagle3_trunk_forward(t, T: int, tok, ids, tap0=None, tap1=None, tap2=None, stream=None) -> None:
+    _check_trunk(t, library().eagle3_trunk_forward(t, int(T), _ptr(tok), _ptr(ids), _ptr(tap0), _ptr(tap1),
+                                                   _ptr(tap2), _stream(stream)))
+
+
+def eagle3_trunk_rollback(t, new_len: int) -> None:
+    _check_trunk(t, library().eagle3_trunk_rollback(t, int(new_len)))
+
+
+def eagle3_trunk_len(t) -> int:
+    v = c_int32(0)
+    _check_trunk(t, library().eagle3_trunk_len(t, byref(v)))
+    return v.value
+
+
+def eagle3_trunk_status(t) -> int:
+    v = c_uint32(0)
+    _check_trunk(t, library().eagle3_trunk_status(t, byref(v)))
+    return v.value
+
+
+def eagle3_generate(ctx, seq: int, trunk, prompt: Sequence[int], max_new: int, gamma: int, stream=None):
+    """Returns (tokens, drafted, accepted)."""
+    p = (c_int32 * len(prompt))(*[int(x) for x in prompt])
+    out = (c_int32 * max_new)()
+    dr, ac = c_int64(0), c_int64(0)
+    rc = library().eagle3_generate(ctx, int(seq), trunk, p, len(prompt), int(max_new), int(gamma), out,
+                                   byref(dr), byref(ac), _stream(stream))
+    _check_trunk(trunk, rc)
+    return list(out), dr.value, ac.value
 
 
 # ---- the ledger on its own (host only) ---------------------------------------

@@ -395,6 +395,42 @@ hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
                             int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
                             hipStream_t s);
 
+// ---- the synthetic target trunk (trunk.hip) ----
+// status word bits raised by the trunk kernels
+constexpr uint32_t kTrunkBadToken = 1u;   // an input id outside the vocabulary (row 0 read)
+constexpr uint32_t kTrunkNanLogits = 2u;  // a row whose logits are all NaN (id 0 given)
+struct TrunkLayer {
+  const float *attn_norm, *mlp_norm;  // fp32 [n]
+  const uint16_t *wq, *wk, *wv, *wo, *w_gate, *w_up, *w_down;  // bf16 [out][in]
+  float *k_cache, *v_cache;           // fp32 [nkv][cap][hd]
+};
+// scratch for up to max_tokens rows
+struct TrunkBufs {
+  float *x, *h, *z, *q, *k, *v, *o, *act, *logits;
+  float *part_o, *part_ml;  // verify-attention split partials (ws_bytes in all)
+  size_t ws_bytes;
+};
+struct TrunkArgs {
+  int n, nh, nkv, hd, ff, vocab, n_layers, cap;
+  float eps;
+  const uint16_t* embed;      // bf16 [vocab][n]
+  const float* final_norm;    // fp32 [n]
+  const uint16_t* lm_head;    // bf16 [vocab][n]
+  const double* inv_freq;     // [hd / 2]
+  const TrunkLayer* layer;    // host array [n_layers]
+  TrunkBufs buf;
+  uint32_t* status;           // device status word
+};
+// one forward over T tokens at positions pos0 .. pos0 + T - 1: ids [T]; taps[j]
+// [T][n] (or null): the residual stream entering the first layer, leaving layer
+// n_layers / 2 - 1 and leaving the last layer
+hipError_t launch_trunk_forward(const TrunkArgs& a, int T, int pos0, const int32_t* tok, int32_t* ids,
+                                float* const taps[3], hipStream_t s);
+// res = [a, bonus, status, drafts[0..g)]: a = longest prefix with drafts[i] ==
+// verify[i], bonus = verify[a]; the status word is copied and cleared
+hipError_t launch_accept(const int32_t* drafts, const int32_t* verify, int g, int32_t* res,
+                         uint32_t* status, hipStream_t s);
+
 // ---- load-time and bookkeeping helpers ----
 // dst row dst_rows[i] = src row src_rows[i] (bf16 rows of row_len elements)
 hipError_t launch_gather_rows(uint16_t* dst, const uint16_t* src, const int32_t* dst_rows,

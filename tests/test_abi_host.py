@@ -22,7 +22,7 @@ def _declared(header):
     return sorted(set(re.findall(r"\b(eagle3_[a-z_]+)\s*\(", txt)))
 
 
-@pytest.mark.parametrize("header", ["eagle3.h", "eagle3_ledger.h"])
+@pytest.mark.parametrize("header", ["eagle3.h", "eagle3_ledger.h", "eagle3_trunk.h"])
 def test_library_exports_every_declared_symbol(header):
     lib = B.library()
     names = _declared(header)

@@ -70,3 +70,32 @@ def test_full_acceptance_path(tiny, gamma):
     out, drafted, acc = greedy_speculative(trunk, OracleChainAdapter(d), prompt, 25, gamma)
     assert out == ref
     assert acc == drafted > 0                          # every draft accepted
+
+
+def alternating_weights(w, tw):
+    """The echo weights with the trunk's lm_head rows swapped in pairs (2i <-> 2i+1):
+    the trunk then alternates a, b, a, b, ... (b the pair partner of a), while the
+    drafter still predicts the token before its input one.  The first draft of a
+    round (x_{n-1} = x_{n+1}) is accepted and the second (x_{n-1} != x_{n+2}) is not,
+    so every round of gamma >= 2 accepts exactly one draft.  Returns the weights and
+    a prompt [a, b] whose pair lies in the drafter's vocabulary image."""
+    w, tw, image = echo_weights(w, tw)
+    E = w["embed"]
+    perm = torch.arange(E.shape[0]) ^ 1
+    tw["lm_head"] = E[perm].clone()
+    img = set(image.tolist())
+    a = next(int(t) for t in image.tolist() if t % 2 == 0 and t + 1 in img)
+    return w, tw, [a, a + 1]
+
+
+@pytest.mark.parametrize("gamma", [2, 3, 5])
+def test_partial_acceptance_path(tiny, gamma):
+    w, tw, prompt = alternating_weights(*tiny)
+    trunk = _trunk(tw, w["embed"])
+    ref = greedy_plain(trunk, prompt, 31)
+    assert ref[:4] == [prompt[0], prompt[1], prompt[0], prompt[1]]   # the trunk alternates
+    d = make_oracle(TINY, w, max_ctx=64)
+    out, drafted, acc = greedy_speculative(trunk, OracleChainAdapter(d), prompt, 31, gamma)
+    assert out == ref
+    rounds = drafted // gamma
+    assert acc == rounds                    # exactly one draft accepted per round
