@@ -73,6 +73,28 @@ KV_BYTES = {"f32": 4.0, "bf16": 2.0, "q8q5": (34.0 + 24.0) / 64}
 WB = WB_BF16
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def calibrate(B, torch, stream_bytes: int = 262_144_000):
+    """The ceilings on this GPU: the sustained bf16 MFMA rate (a pure MFMA loop)
+    and the streaming HBM read rate of a buffer of stream_bytes (the lm_head
+    matrix's size) read right after a 2 GiB flush read."""
+    sink = torch.empty(B.CALIB_SINK_BYTES, dtype=torch.uint8, device="cuda")
+    buf = torch.empty(stream_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda").fill_(2)
+    torch.cuda.synchronize()
+    tflops = B.eagle3_calibrate_mfma(10000, 3, sink)
+    gbs = B.eagle3_calibrate_stream(buf, stream_bytes, flush, flush.numel(), 5, sink)
+    del sink, buf, flush
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(tflops, 1), "hbm_stream_read_gbs": round(gbs, 1),
+            "stream_bytes": stream_bytes,
+            "how": "eagle3_calibrate_mfma (4 independent v_mfma_f32_32x32x16_bf16 chains per wave, "
+                   "register operands, 2048x256 threads, best of 3) and eagle3_calibrate_stream "
+                   "(coalesced 16-byte reads after a 2 GiB flush read, best of 5)"}
+
+
 def kernel_bytes(cfg, kernel: str, L: int, kv_bytes: int = 4) -> float:
     """Algorithmic HBM bytes of one launch of a kernel family (K/V elements of
     kv_bytes bytes)."""
@@ -325,6 +347,7 @@ def main():
         sb = [step_bytes(cfg, L_at[i], gamma, accepted[i], kvb, stored) for i in range(args.warmup, nsteps)]
     step_gbs = (sum(sb) / args.steps) / (elapsed / args.steps) / 1e9
 
+    cal = calibrate(B, torch)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, wd, aux_c, tok_c, b_aux, b_tok, gamma, args.cpu_rounds, int4_weights=i4)
@@ -361,7 +384,10 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if i4 else committed_traffic(args.kernel),
                      "avg_launch_us": round(k_avg_s * 1e6, 3),
-                     "launches": k_launches, "bytes_per_launch": k_bytes},
+                     "launches": k_launches, "bytes_per_launch": k_bytes,
+                     "calibrated_peak": cal["hbm_stream_read_gbs"],
+                     "frac_calibrated": round(achieved / cal["hbm_stream_read_gbs"], 4)},
+        "calibrated": cal,
         "step_hbm_gbs": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "round_ms": {"p10": round(pct(round_ms, 0.1), 4), "p50": round(pct(round_ms, 0.5), 4),
@@ -372,8 +398,15 @@ def main():
         "draft_step_hbm_frac": round(kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
                                      / (per_step_us * 1e-6) / 1e9
                                      / HBM_PEAK_GBS, 4),
+        "draft_step_hbm_frac_calibrated": round(kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
+                                                / (per_step_us * 1e-6) / 1e9
+                                                / cal["hbm_stream_read_gbs"], 4),
         "prefill": {"rows": L, "ms": round(prefill_s * 1e3, 3),
-                    "tflops": round(prefill_flop / prefill_s / 1e12, 2)},
+                    "tflops": round(prefill_flop / prefill_s / 1e12, 2),
+                    "frac_bf16_peak": round(prefill_flop / prefill_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "frac_calibrated": round(prefill_flop / prefill_s / 1e12 / cal["mfma_bf16_tflops"], 4),
+                    "note": "algorithmic flops (fc and K|V projections) over the wall time of the whole "
+                            "prefill call"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -544,6 +577,7 @@ def run_batched(args, cfg):
     round_bytes = 6.0 * n * n + gamma * (2.0 * p_step) + kv_bytes
     step_gbs = round_bytes / (elapsed / args.steps) / 1e9
 
+    cal = calibrate(B, torch)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_batched(cfg, wd, lens, b_aux, b_tok, gamma)
@@ -567,7 +601,10 @@ def run_batched(args, cfg):
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "avg_launch_us": round(k_avg_s * 1e6, 3),
-                     "launches": k_launches, "bytes_per_launch": k_bytes},
+                     "launches": k_launches, "bytes_per_launch": k_bytes,
+                     "calibrated_peak": cal["hbm_stream_read_gbs"],
+                     "frac_calibrated": round(achieved / cal["hbm_stream_read_gbs"], 4)},
+        "calibrated": cal,
         "round_hbm_gbs": round(step_gbs, 1),
         "round_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "cpu_baseline": cpu,

@@ -97,6 +97,7 @@ def library() -> ctypes.CDLL:
                                          P, P, P, P, P], ctypes.c_int),
         "eagle3_rewind": ([P, c_int32, c_int32], ctypes.c_int),
         "eagle3_kv_len": ([P, c_int32, POINTER(c_int32), POINTER(c_int32)], ctypes.c_int),
+        "eagle3_status": ([P, POINTER(c_uint32)], ctypes.c_int),
         "eagle3_kv_read": ([P, c_int32, c_int32, c_int32, P, P, P], ctypes.c_int),
         "eagle3_weights_i4_read": ([P, c_int32, P, P, P], ctypes.c_int),
         "eagle3_verify_attention_workspace": ([c_int32, c_int32, c_int32, c_int32, c_int32, c_int32],
@@ -118,6 +119,9 @@ def library() -> ctypes.CDLL:
         "eagle3_trunk_last_error": ([P], c_char_p),
         "eagle3_generate": ([P, c_int32, P, POINTER(c_int32), c_int32, c_int32, c_int32, POINTER(c_int32),
                              POINTER(c_int64), POINTER(c_int64), P], ctypes.c_int),
+        "eagle3_calibrate_mfma": ([c_int32, c_int32, P, POINTER(c_double), P], ctypes.c_int),
+        "eagle3_calibrate_stream": ([P, ctypes.c_size_t, P, ctypes.c_size_t, c_int32, P, POINTER(c_double), P],
+                                    ctypes.c_int),
         "eagle3_ledger_create": ([c_int32, c_int32, c_int32, POINTER(P)], ctypes.c_int),
         "eagle3_ledger_destroy": ([P], None),
         "eagle3_ledger_prefill": ([P, c_int32, c_int32, c_int32], ctypes.c_int),
@@ -257,6 +261,15 @@ def eagle3_rewind(ctx, seq: int, new_len: int) -> None:
     _check(ctx, library().eagle3_rewind(ctx, seq, new_len))
 
 
+STATUS_BAD_TOKEN, STATUS_NAN_LOGITS = 1, 2
+
+
+def eagle3_status(ctx) -> int:
+    v = c_uint32(0)
+    _check(ctx, library().eagle3_status(ctx, byref(v)))
+    return v.value
+
+
 def eagle3_kv_len(ctx, seq: int):
     c, s = c_int32(0), c_int32(0)
     _check(ctx, library().eagle3_kv_len(ctx, seq, byref(c), byref(s)))
@@ -391,6 +404,27 @@ def eagle3_generate(ctx, seq: int, trunk, prompt: Sequence[int], max_new: int, g
                                    byref(dr), byref(ac), _stream(stream))
     _check_trunk(trunk, rc)
     return list(out), dr.value, ac.value
+
+
+# ---- calibration -----------------------------------------------------------------
+CALIB_SINK_BYTES = 2 << 20
+
+
+def eagle3_calibrate_mfma(iters: int, reps: int, sink, stream=None) -> float:
+    v = c_double(0)
+    rc = library().eagle3_calibrate_mfma(int(iters), int(reps), _ptr(sink), byref(v), _stream(stream))
+    if rc != OK:
+        raise Eagle3Error(rc, "eagle3_calibrate_mfma")
+    return v.value
+
+
+def eagle3_calibrate_stream(buf, nbytes: int, flush, flush_bytes: int, reps: int, sink, stream=None) -> float:
+    v = c_double(0)
+    rc = library().eagle3_calibrate_stream(_ptr(buf), int(nbytes), _ptr(flush), int(flush_bytes), int(reps),
+                                           _ptr(sink), byref(v), _stream(stream))
+    if rc != OK:
+        raise Eagle3Error(rc, "eagle3_calibrate_stream")
+    return v.value
 
 
 # ---- the ledger on its own (host only) ---------------------------------------

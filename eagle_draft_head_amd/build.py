@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libeagle3.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["engine.cpp", "gemv.hip", "attn.hip", "prefill.hip", "batch.hip", "trunk.hip", "runner.cpp"]
+SOURCES = ["engine.cpp", "gemv.hip", "attn.hip", "prefill.hip", "batch.hip", "trunk.hip", "runner.cpp", "calib.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-Wno-unused-variable",
@@ -43,7 +43,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

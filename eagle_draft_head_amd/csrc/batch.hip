@@ -304,6 +304,7 @@ __global__ __launch_bounds__(kBRowThreads) void k_bprep(const BPrepArgs a) {
     const int i = block_argmax(a.cand_v + (size_t)r * a.ncand, a.cand_i + (size_t)r * a.ncand,
                                a.ncand, sv, si);
     if (threadIdx.x == 0) {
+      if (i < 0 || i >= a.dv) atomicOr(a.status, kStatusNanLogits);  // every logit NaN
       const int ic = min(max(i, 0), a.dv - 1);
       const int t = ic + a.d2t[ic];
       a.out_ids[(size_t)orig * a.gamma + a.step - 1] = t;
@@ -311,7 +312,8 @@ __global__ __launch_bounds__(kBRowThreads) void k_bprep(const BPrepArgs a) {
     }
   }
   __syncthreads();
-  const int tok = min(max(s_tok, 0), a.vocab - 1);
+  if (threadIdx.x == 0 && (s_tok < 0 || s_tok >= a.vocab)) atomicOr(a.status, kStatusBadToken);
+  const int tok = min(max(s_tok, 0), a.vocab - 1);  // reads the nearest row
   const uint2* erow = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);
   float4 ev[kBRowVec], gv[kBRowVec];
   float se = 0.f, sg = 0.f;
@@ -548,7 +550,7 @@ hipError_t launch_bcand(const float* P, int S, int N, int m, float* cand_v, int3
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bfinal(const BatchRows br, int gamma,
+__global__ __launch_bounds__(256) void k_bfinal(uint32_t* __restrict__ status, const BatchRows br, int gamma,
                                                 const float* __restrict__ cand_v,
                                                 const int32_t* __restrict__ cand_i, int ncand,
                                                 const int32_t* __restrict__ d2t, int dv,
@@ -558,15 +560,16 @@ __global__ __launch_bounds__(256) void k_bfinal(const BatchRows br, int gamma,
   const int r = blockIdx.x;
   const int i = block_argmax(cand_v + (size_t)r * ncand, cand_i + (size_t)r * ncand, ncand, sv, si);
   if (threadIdx.x == 0) {
+    if (i < 0 || i >= dv) atomicOr(status, kStatusNanLogits);  // every logit NaN
     const int ic = min(max(i, 0), dv - 1);
     out_ids[(size_t)br.orig[r] * gamma + br.geff[r] - 1] = ic + d2t[ic];
   }
 }
 
-hipError_t launch_bfinal(const BatchRows& br, int m, int gamma, const float* cand_v,
+hipError_t launch_bfinal(uint32_t* status, const BatchRows& br, int m, int gamma, const float* cand_v,
                          const int32_t* cand_i, int ncand, const int32_t* d2t, int dv,
                          int32_t* out_ids, hipStream_t s) {
-  hipLaunchKernelGGL(k_bfinal, dim3(m), dim3(256), 0, s, br, gamma, cand_v, cand_i, ncand, d2t, dv,
+  hipLaunchKernelGGL(k_bfinal, dim3(m), dim3(256), 0, s, status, br, gamma, cand_v, cand_i, ncand, d2t, dv,
                      out_ids);
   return hipGetLastError();
 }

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -24,9 +25,26 @@
 
 #include "../../include/eagle3.h"
 #include "../../include/eagle3_ledger.h"
+#include "../../include/eagle3_testing.h"
 #include "gemv_cfg.hpp"
 #include "kernels.hpp"
 #include "ledger.hpp"
+
+namespace e3 {
+
+namespace {
+std::atomic<int32_t> g_alloc_fault{0};
+}  // namespace
+
+bool alloc_fault_fires() {
+  int32_t v = g_alloc_fault.load(std::memory_order_relaxed);
+  while (v > 0) {
+    if (g_alloc_fault.compare_exchange_weak(v, v - 1, std::memory_order_relaxed)) return v == 1;
+  }
+  return false;
+}
+
+}  // namespace e3
 
 namespace {
 
@@ -74,6 +92,7 @@ struct eagle3_ctx {
            *w_lm = nullptr, *embed = nullptr;
   float *nrm_in = nullptr, *nrm_hid = nullptr, *nrm_post = nullptr, *nrm_fin = nullptr;
   int32_t* d2t = nullptr;
+  uint32_t* status = nullptr;  // device status word (e3::kStatus* bits)
   double* inv_freq = nullptr;  // [rot / 2]
   int gcfg[e3::kGemvKinds] = {};
   int lm_grid = 0;
@@ -192,6 +211,7 @@ int gemv_config_override(eagle3_ctx* c) {
 template <typename T>
 int dalloc(eagle3_ctx* c, T** p, size_t count) {
   void* v = nullptr;
+  if (e3::alloc_fault_fires()) return hip_fail(c, hipErrorOutOfMemory, "hipMalloc (injected failure)");
   hipError_t e = hipMalloc(&v, count * sizeof(T) > 0 ? count * sizeof(T) : 16);
   if (e != hipSuccess) return hip_fail(c, e, "hipMalloc");
   c->allocs.push_back(v);
@@ -212,19 +232,30 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // --- profiling of one kernel family with events on the launching stream -----
+// A scope of one kernel launch (one_launch) hands its event pair to that launch,
+// which records the kernel's own start and end (hipExtLaunchKernelGGL); a scope of
+// several launches records the pair around them on the stream.
 struct ProfScope {
   eagle3_ctx* c;
   hipStream_t s;
-  bool on;
-  ProfScope(eagle3_ctx* cx, int kernel, hipStream_t st) : c(cx), s(st), on(false) {
+  bool on, single;
+  ProfScope(eagle3_ctx* cx, int kernel, hipStream_t st, bool one_launch = false)
+      : c(cx), s(st), on(false), single(one_launch) {
     if (c->prof.kernel == kernel && c->prof.used + 2 <= c->prof.ev.size()) {
       on = true;
-      (void)hipEventRecord(c->prof.ev[c->prof.used], s);
+      if (single) {
+        e3::g_launch_ev.start = c->prof.ev[c->prof.used];
+        e3::g_launch_ev.stop = c->prof.ev[c->prof.used + 1];
+        e3::g_launch_ev.armed = true;
+      } else {
+        (void)hipEventRecord(c->prof.ev[c->prof.used], s);
+      }
     }
   }
   ~ProfScope() {
     if (on) {
-      (void)hipEventRecord(c->prof.ev[c->prof.used + 1], s);
+      if (single) e3::g_launch_ev.armed = false;
+      else (void)hipEventRecord(c->prof.ev[c->prof.used + 1], s);
       c->prof.used += 2;
     }
   }
@@ -397,6 +428,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->nrm_post, size_t(n)));
   E3_TRY(dalloc(c, &c->nrm_fin, size_t(n)));
   E3_TRY(dalloc(c, &c->d2t, size_t(dv)));
+  E3_TRY(dalloc(c, &c->status, 1));
   c->kv_f32 = cfg->kv_dtype == EAGLE3_KV_F32;
   c->kv_q = cfg->kv_dtype == EAGLE3_KV_Q8Q5;
   c->kv_esize = c->kv_f32 ? 4 : (c->kv_q ? 1 : 2);
@@ -524,6 +556,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
 
   // zero state
+  E3_TRYH(hipMemsetAsync(c->status, 0, 4, s), "clear status");
   E3_TRYH(hipMemsetAsync(c->kv, 0, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize, s),
           "memset kv");
 
@@ -694,6 +727,17 @@ int eagle3_verify_attention_noalloc(const float* q_dev, const void* k_dev, const
   return e == hipSuccess ? EAGLE3_OK : hip_fail(nullptr, e, "verify attention launch");
 }
 
+int eagle3_status(eagle3_ctx* ctx, uint32_t* flags) {
+  if (!ctx || !flags) return EAGLE3_E_INVAL;
+  hipError_t e = hipDeviceSynchronize();
+  uint32_t v = 0;
+  if (e == hipSuccess) e = hipMemcpy(&v, ctx->status, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(ctx->status, 0, 4);
+  if (e != hipSuccess) return hip_fail(ctx, e, "status");
+  *flags = v;
+  return EAGLE3_OK;
+}
+
 int eagle3_kv_len(const eagle3_ctx* ctx, int32_t seq, int32_t* committed, int32_t* spec) {
   if (!ctx || !committed || !spec) return EAGLE3_E_INVAL;
   if (!ctx->ledger.valid_seq(seq)) return EAGLE3_E_INVAL;
@@ -831,7 +875,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
                "fc gemv");
       }
       f_split = size_t(e3::gemv_multi_width(P)) * n;
-      E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
+      E3_HIP(c, e3::launch_tf_cat(c->status, c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
                                   c->nrm_hid, c->cfg.rms_eps, nullptr, nullptr, c->tf_cat32, s, &bo),
              "tf cat");
       if (T > 0) {
@@ -859,7 +903,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
                  "fc gemm lo");
       }
       f_split = size_t(P) * n;
-      E3_HIP(c, e3::launch_tf_cat(c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
+      E3_HIP(c, e3::launch_tf_cat(c->status, c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
                                   c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s,
                                   &bo),
              "tf cat");
@@ -1073,6 +1117,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       pa.bnd = stored ? c->bnd_y : nullptr;
       pa.Xhi = c->bx_a_hi; pa.Xlo = c->bx_a_lo; pa.ldx = c->bld_a;
       pa.dbg_hidden = dbg ? dbg->hidden : nullptr;
+      pa.status = c->status;
       const int Nqkv = c->qd + 2 * c->kvd;
       {
         ProfScope ps(c, 2, s);
@@ -1172,7 +1217,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
                                    c->b_logits + size_t(r) * c->dv, size_t(c->dv) * 4,
                                    hipMemcpyDeviceToDevice, s), "dbg logits");
     }
-    E3_HIP(c, e3::launch_bfinal(br, br.m, gamma, c->b_cand_v, c->b_cand_i, c->b_ncand, c->d2t,
+    E3_HIP(c, e3::launch_bfinal(c->status, br, br.m, gamma, c->b_cand_v, c->b_cand_i, c->b_ncand, c->d2t,
                                 c->dv, out, s), "argmax");
   }
   return EAGLE3_OK;
@@ -1247,7 +1292,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       g_bnd.count = 1;
     } else {
       e3::VecOut eo{ctx->gb[0].y, ctx->gb[0].w_hid, ctx->nrm_hid, nullptr, nullptr, ctx->gb[0].ssq};
-      ProfScope ps(ctx, 6, s);
+      ProfScope ps(ctx, 6, s, true);
       E3_HIP(ctx, e3::launch_encode(ctx->wq(ctx->w_fc, ctx->i4_fc), ctx->ws(ctx->i4_fc), n,
                                     aux0_dev + size_t(b) * n, aux1_dev + size_t(b) * n,
                                     aux2_dev + size_t(b) * n, eo, ctx->gcfg[e3::kGemvEncode], s),
@@ -1267,7 +1312,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       e3::QkvArgs qa{};
       qa.w_qkv = ctx->wq(ctx->w_qkv, ctx->i4_qkv); qa.s_qkv = ctx->ws(ctx->i4_qkv); qa.n = n; qa.n_head = ctx->nh; qa.n_head_kv = ctx->nkv;
       qa.head_dim = ctx->hd; qa.rope_dim = ctx->rot; qa.inv_freq = ctx->inv_freq;
-      qa.eps = ctx->cfg.rms_eps; qa.embed = ctx->embed; qa.vocab = ctx->vt;
+      qa.eps = ctx->cfg.rms_eps; qa.embed = ctx->embed; qa.vocab = ctx->vt; qa.status = ctx->status;
       if (j == 0) {
         qa.tok = boundary_tok_dev + b;
         qa.prev_count = 0;
@@ -1285,7 +1330,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
         qa.cap = 1; qa.row = 0; qa.kv_f32 = 1;
       }
       {
-        ProfScope ps(ctx, 2, s);
+        ProfScope ps(ctx, 2, s, true);
         E3_HIP(ctx, e3::launch_qkv(qa, ctx->gcfg[e3::kGemvQkv], s), "qkv");
       }
       e3::AttnArgs aa{};
@@ -1300,13 +1345,13 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       }
       {
         e3::VecOut oo{ctx->x1, ctx->x1w, ctx->nrm_post, nullptr, nullptr, ctx->x1_ssq};
-        ProfScope ps(ctx, 4, s);
+        ProfScope ps(ctx, 4, s, true);
         E3_HIP(ctx, e3::launch_gemv_resid(ctx->wq(ctx->w_o, ctx->i4_o), ctx->ws(ctx->i4_o), n, ctx->qd,
                                           ctx->ao, g->y, oo,
                                           ctx->gcfg[e3::kGemvO], s), "o_proj");
       }
       {
-        ProfScope ps(ctx, 1, s);
+        ProfScope ps(ctx, 1, s, true);
         E3_HIP(ctx, e3::launch_gateup(ctx->wq(ctx->w_gu, ctx->i4_gu), ctx->ws(ctx->i4_gu), ctx->ff, n,
                                       ctx->x1w, ctx->x1_ssq, ctx->x1_count,
                                       ctx->cfg.rms_eps, ctx->act, ctx->gcfg[e3::kGemvGateUp], s),
@@ -1314,7 +1359,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       }
       {
         e3::VecOut dn{gn->y, gn->w_norm, ctx->nrm_fin, gn->w_hid, ctx->nrm_hid, gn->ssq};
-        ProfScope ps(ctx, 3, s);
+        ProfScope ps(ctx, 3, s, true);
         E3_HIP(ctx, e3::launch_gemv_resid(ctx->wq(ctx->w_d, ctx->i4_d), ctx->ws(ctx->i4_d), n, ctx->ff,
                                           ctx->act, ctx->x1, dn,
                                           ctx->gcfg[e3::kGemvDown], s), "down");
@@ -1326,7 +1371,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;
       la.d2t = ctx->d2t; la.part_tok = ctx->lm_pt;
       {
-        ProfScope ps(ctx, 0, s);
+        ProfScope ps(ctx, 0, s, true);
         E3_HIP(ctx, e3::launch_lmhead(la, ctx->gcfg[e3::kGemvLmHead], s), "lm_head");
       }
       if (dbg && dbg->hidden)
@@ -1334,7 +1379,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
                                    size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
       g = gn;
     }
-    E3_HIP(ctx, e3::launch_argmax_finalize(ctx->lm_pv, ctx->lm_pi, ctx->lm_pt, ctx->lm_grid, ctx->d2t,
+    E3_HIP(ctx, e3::launch_argmax_finalize(ctx->status, ctx->lm_pv, ctx->lm_pi, ctx->lm_pt, ctx->lm_grid, ctx->d2t,
                                            ctx->dv, out_b + (ge - 1), ctx->tok_slots + (ge - 1), s),
            "argmax");
   }
@@ -1372,6 +1417,8 @@ int eagle3_profile_read(eagle3_ctx* ctx, double* total_ms, int64_t* launches) {
   *launches = int64_t(ctx->prof.used / 2);
   return EAGLE3_OK;
 }
+
+void eagle3_test_fail_allocation(int32_t n) { e3::g_alloc_fault.store(n > 0 ? n : 0); }
 
 // ---- the ledger on its own ----------------------------------------------------
 int eagle3_ledger_create(int32_t max_ctx, int32_t max_seqs, int32_t max_gamma, eagle3_ledger** out) {

@@ -26,11 +26,23 @@
 // for another block: cross-block reductions happen in the next kernel.
 #include <cstdlib>
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "gemv_cfg.hpp"
 #include "kernels.hpp"
 
 namespace e3 {
+
+// hipLaunchKernelGGL, or the event-timed extended launch when armed (LaunchEvents)
+#define E3_LAUNCH(K, G, B, SH, S, ...)                                                         \
+  do {                                                                                         \
+    if (g_launch_ev.armed)                                                                     \
+      hipExtLaunchKernelGGL(K, G, B, SH, S, g_launch_ev.start, g_launch_ev.stop, 0, __VA_ARGS__); \
+    else                                                                                       \
+      hipLaunchKernelGGL(K, G, B, SH, S, __VA_ARGS__);                                          \
+  } while (0)
+
 
 // Row pointers of the R rows a wave owns, at column k0 (rows past N repeat the last row).
 template <int R>
@@ -514,16 +526,22 @@ __device__ __forceinline__ int qkv_token(const QkvArgs& a, float* sv, int* si, i
   if (a.prev_count > 0) {
     int bt;
     int bi = block_argmax_carry(a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, sv, si, st, &bt);
-    if (bi < 0 || bi >= a.dv) tok = a.d2t[0];  // only reachable with NaN logits
+    const bool nan = bi < 0 || bi >= a.dv;  // every logit NaN
+    if (nan) tok = a.d2t[0];
     else tok = a.prev_tok ? bt : bi + a.d2t[bi];
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       *a.prev_out_id = tok;
       *a.tok_store = tok;
+      if (nan) atomicOr(a.status, kStatusNanLogits);
     }
   } else {
     tok = *a.tok;
   }
-  return min(max(tok, 0), a.vocab - 1);  // out-of-range ids are clamped
+  if (tok < 0 || tok >= a.vocab) {  // reads the nearest row, and says so
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.status, kStatusBadToken);
+    tok = min(max(tok, 0), a.vocab - 1);
+  }
+  return tok;
 }
 
 // the fused epilogue of a wave's R rows: 1/rms per half, NeoX rotation of q/k
@@ -887,7 +905,8 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead
 
 // the last step of a chain: argmax over the lm_head candidates, d2t (the
 // candidates' target ids come with them when pt is given)
-__global__ __launch_bounds__(256) void k_argmax_finalize(const float* __restrict__ pv,
+__global__ __launch_bounds__(256) void k_argmax_finalize(uint32_t* __restrict__ status,
+                                                         const float* __restrict__ pv,
                                                          const int32_t* __restrict__ pi,
                                                          const int32_t* __restrict__ pt, int count,
                                                          const int32_t* __restrict__ d2t, int dv,
@@ -898,8 +917,12 @@ __global__ __launch_bounds__(256) void k_argmax_finalize(const float* __restrict
   const int bi = block_argmax_carry(pv, pi, pt, count, sv, si, st, &bt);
   if (threadIdx.x == 0) {
     int t;
-    if (bi < 0 || bi >= dv) t = d2t[0];  // only reachable with NaN logits
-    else t = pt ? bt : bi + d2t[bi];
+    if (bi < 0 || bi >= dv) {  // every logit NaN
+      t = d2t[0];
+      atomicOr(status, kStatusNanLogits);
+    } else {
+      t = pt ? bt : bi + d2t[bi];
+    }
     *out_id = t;
     if (tok_store) *tok_store = t;
   }
@@ -1115,10 +1138,10 @@ hipError_t launch_encode(const uint16_t* w_fc, const uint16_t* S, int n, const f
   case ID:                                                                                      \
     if (S) {                                                                                    \
       E3_LDS_ALLOW((k_encode<WV, RR, UU, true>), xb + q_vec_bytes(3 * n));                      \
-      hipLaunchKernelGGL((k_encode<WV, RR, UU, true>), dim3(i4_grid(ceil_div(n, WV * RR))),     \
+      E3_LAUNCH((k_encode<WV, RR, UU, true>), dim3(i4_grid(ceil_div(n, WV * RR))),     \
                          dim3(64 * WV), xb + q_vec_bytes(3 * n), s, w_fc, S, n, a0, a1, a2, out); \
     } else                                                                                      \
-      hipLaunchKernelGGL((k_encode<WV, RR, UU, false>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
+      E3_LAUNCH((k_encode<WV, RR, UU, false>), dim3(ceil_div(n, WV * RR)), dim3(64 * WV), \
                          xb, s, w_fc, S, n, a0, a1, a2, out);                                   \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
@@ -1134,10 +1157,10 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
     if (RR % 2) return hipErrorInvalidValue;                                               \
     if (a.s_qkv) {                                                                         \
       E3_LDS_ALLOW((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), xb + 2 * q_vec_bytes(a.n));        \
-      hipLaunchKernelGGL((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), dim3(i4_grid(ceil_div(N, WV * RR))), \
+      E3_LAUNCH((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), dim3(i4_grid(ceil_div(N, WV * RR))), \
                          dim3(64 * WV), xb + 2 * q_vec_bytes(a.n), s, a);                  \
     } else                                                                                 \
-      hipLaunchKernelGGL((k_qkv<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(N, WV * RR)),   \
+      E3_LAUNCH((k_qkv<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(N, WV * RR)),   \
                          dim3(64 * WV), xb, s, a);                                         \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
@@ -1152,10 +1175,10 @@ hipError_t launch_gemv_resid(const uint16_t* w, const uint16_t* S, int N, int K,
   case ID:                                                                                      \
     if (S) {                                                                                    \
       E3_LDS_ALLOW((k_gemv_resid<WV, RR, UU, true>), xb + q_vec_bytes(K));                      \
-      hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, true>), dim3(i4_grid(ceil_div(N, WV * RR))), \
+      E3_LAUNCH((k_gemv_resid<WV, RR, UU, true>), dim3(i4_grid(ceil_div(N, WV * RR))), \
                          dim3(64 * WV), xb + q_vec_bytes(K), s, w, S, N, K, x, resid, out);    \
     } else                                                                                      \
-      hipLaunchKernelGGL((k_gemv_resid<WV, RR, UU, false>), dim3(ceil_div(N, WV * RR)),        \
+      E3_LAUNCH((k_gemv_resid<WV, RR, UU, false>), dim3(ceil_div(N, WV * RR)),        \
                          dim3(64 * WV), xb, s, w, S, N, K, x, resid, out);                     \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
@@ -1172,11 +1195,11 @@ hipError_t launch_gateup(const uint16_t* w_gu, const uint16_t* S, int n_ff, int 
     if (RR % 2) return hipErrorInvalidValue;                                                \
     if (S) {                                                                                \
       E3_LDS_ALLOW((k_gateup<WV, (RR < 2 ? 2 : RR), UU, true>), xb + q_vec_bytes(n));       \
-      hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU, true>),                       \
+      E3_LAUNCH((k_gateup<WV, (RR < 2 ? 2 : RR), UU, true>),                       \
                          dim3(i4_grid(ceil_div(2 * n_ff, WV * RR))), dim3(64 * WV),          \
                          xb + q_vec_bytes(n), s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act); \
     } else                                                                                  \
-      hipLaunchKernelGGL((k_gateup<WV, (RR < 2 ? 2 : RR), UU, false>),                      \
+      E3_LAUNCH((k_gateup<WV, (RR < 2 ? 2 : RR), UU, false>),                      \
                          dim3(ceil_div(2 * n_ff, WV * RR)), dim3(64 * WV), xb,              \
                          s, w_gu, S, n_ff, n, xw, x_ssq, ssq_count, eps, act);              \
     break;
@@ -1194,10 +1217,10 @@ hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
   case ID:                                                                                    \
     if (a.s_lm) {                                                                             \
       E3_LDS_ALLOW((k_lmhead<WV, RR, UU, true>), xb + q_vec_bytes(a.n));                      \
-      hipLaunchKernelGGL((k_lmhead<WV, RR, UU, true>), dim3(i4_grid(ceil_div(a.dv, WV * RR))), \
+      E3_LAUNCH((k_lmhead<WV, RR, UU, true>), dim3(i4_grid(ceil_div(a.dv, WV * RR))), \
                          dim3(64 * WV), xb + q_vec_bytes(a.n), s, a);                         \
     } else                                                                                    \
-      hipLaunchKernelGGL((k_lmhead<WV, RR, UU, false>), dim3(ceil_div(a.dv, WV * RR)),         \
+      E3_LAUNCH((k_lmhead<WV, RR, UU, false>), dim3(ceil_div(a.dv, WV * RR)),         \
                          dim3(64 * WV), xb, s, a);                                            \
     break;
   E3_DISPATCH_CFG(cfg, CASE)
@@ -1205,10 +1228,10 @@ hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, const int32_t* pt, int count,
-                                  const int32_t* d2t, int dv, int32_t* out_id, int32_t* tok_store,
+hipError_t launch_argmax_finalize(uint32_t* status, const float* pv, const int32_t* pi, const int32_t* pt,
+                                  int count, const int32_t* d2t, int dv, int32_t* out_id, int32_t* tok_store,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(256), 0, s, pv, pi, pt, count, d2t, dv, out_id,
+  hipLaunchKernelGGL(k_argmax_finalize, dim3(1), dim3(256), 0, s, status, pv, pi, pt, count, d2t, dv, out_id,
                      tok_store);
   return hipGetLastError();
 }

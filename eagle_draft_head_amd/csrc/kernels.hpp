@@ -7,6 +7,27 @@
 
 namespace e3 {
 
+// Kernel-accurate timing of one launch for measurement: when armed, the next GEMV
+// launch of the calling thread goes through hipExtLaunchKernelGGL with these
+// events, which record the kernel's own start and end (no extra queue packets).
+// Device status word of a drafter handle: bits raised by kernels that meet bad
+// device-side inputs (the kernel still reads in bounds: an out-of-range id reads the
+// nearest valid row, an argmax over NaN logits takes draft id 0).
+constexpr uint32_t kStatusBadToken = 1u;   // a token id outside [0, target_vocab)
+constexpr uint32_t kStatusNanLogits = 2u;  // a draft step whose logits were all NaN
+
+// Fault injection for tests (include/eagle3_testing.h): while positive, every
+// device allocation of the library counts it down and the one that brings it to
+// zero fails as out of memory.
+bool alloc_fault_fires();
+
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool armed = false;
+};
+inline thread_local LaunchEvents g_launch_ev;
+
+
 // ---- GEMV family (bf16 weights, fp32 activations and accumulate) ----
 // `cfg` selects a launch configuration from E3_GEMV_CONFIGS (gemv_cfg.hpp).
 
@@ -53,7 +74,8 @@ struct QkvArgs {
   const double* inv_freq;  // [rope_dim / 2]: theta^(-2i / rope_dim)
   float eps;
   const uint16_t* embed;
-  int vocab;               // rows of embed; token ids are clamped to [0, vocab)
+  int vocab;               // rows of embed; an id outside [0, vocab) raises kStatusBadToken
+  uint32_t* status;        // device status word
   const int32_t* tok;      // device: the token fed to this step (when prev_count == 0)
   // when prev_count > 0 the token is the argmax of the previous step's lm_head
   // candidates mapped through d2t; block 0 stores it to *prev_out_id and *tok_store
@@ -111,7 +133,7 @@ int lmhead_grid(int dv, int cfg);
 hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s);
 // argmax over the candidates, target = i + d2t[i] (taken from pt when given)
 // -> *out_id (and *tok_store if set)
-hipError_t launch_argmax_finalize(const float* pv, const int32_t* pi, const int32_t* pt, int count,
+hipError_t launch_argmax_finalize(uint32_t* status, const float* pv, const int32_t* pi, const int32_t* pt, int count,
                                   const int32_t* d2t, int dv, int32_t* out_id, int32_t* tok_store,
                                   hipStream_t s);
 
@@ -279,6 +301,7 @@ struct BPrepArgs {
   uint16_t* Xlo;
   int ldx;
   float* dbg_hidden;       // optional [n_seq][gamma + 1][n]
+  uint32_t* status;        // device status word
 };
 hipError_t launch_bprep(const BPrepArgs& a, hipStream_t s);
 // q|k|v of rows [0, m) from the QKV partials: rotate q, k at pos0 + step; q -> [32][qd],
@@ -330,7 +353,7 @@ inline int bcand_count(int N) { return (N + kBCandCols - 1) / kBCandCols; }
 hipError_t launch_bcand(const float* P, int S, int N, int m, float* cand_v, int32_t* cand_i,
                         float* logits, hipStream_t s);
 // rows [0, m): out_ids[orig * gamma + geff - 1] = d2t-mapped argmax of the candidates
-hipError_t launch_bfinal(const BatchRows& br, int m, int gamma, const float* cand_v,
+hipError_t launch_bfinal(uint32_t* status, const BatchRows& br, int m, int gamma, const float* cand_v,
                          const int32_t* cand_i, int ncand, const int32_t* d2t, int dv,
                          int32_t* out_ids, hipStream_t s);
 
@@ -356,7 +379,7 @@ struct BndOut {
 // stride n, split stride f_split (elements); written as fp32 (cat32) or as bf16
 // (cat16, plus the bf16 remainder in cat16_lo when given).  Rows T .. T + bnd.count - 1
 // of F are boundary rows, summed into bnd's slots.
-hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int n,
+hipError_t launch_tf_cat(uint32_t* status, const float* F, int splits, size_t f_split, int T, int n,
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
                          float* cat32, hipStream_t s, const BndOut* bnd = nullptr);

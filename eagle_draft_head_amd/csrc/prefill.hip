@@ -92,7 +92,8 @@ __device__ __forceinline__ float4 sum_splits4(const float* __restrict__ p, int s
 }
 
 // One block per row: f = sum of the fc partials, the two RMSNorms, the concat.
-__global__ __launch_bounds__(512) void k_tf_cat(const float* __restrict__ F, int splits,
+__global__ __launch_bounds__(512) void k_tf_cat(uint32_t* __restrict__ status, const float* __restrict__ F,
+                                                int splits,
                                                 size_t f_split, int T, int n,
                                                 const uint16_t* __restrict__ embed, int vocab,
                                                 const int32_t* __restrict__ tok,
@@ -123,7 +124,11 @@ __global__ __launch_bounds__(512) void k_tf_cat(const float* __restrict__ F, int
     if (threadIdx.x == 0) bnd.ssq[bnd.slot[j]] = sf;
     return;
   }
-  const int tk = min(max(tok[t], 0), vocab - 1);  // out-of-range ids are clamped
+  const int tid = tok[t];
+  if (tid < 0 || tid >= vocab) {  // reads the nearest row, and says so
+    if (threadIdx.x == 0) atomicOr(status, kStatusBadToken);
+  }
+  const int tk = min(max(tid, 0), vocab - 1);
   const uint2* e4 = reinterpret_cast<const uint2*>(embed + (size_t)tk * n);
   float4* f4 = reinterpret_cast<float4*>(fs);
   float se = 0.f, sf = 0.f;
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(512) void k_tf_cat(const float* __restrict__ F, int
   }
 }
 
-hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int n,
+hipError_t launch_tf_cat(uint32_t* status, const float* F, int splits, size_t f_split, int T, int n,
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
                          float* cat32, hipStream_t s, const BndOut* bnd) {
@@ -193,7 +198,7 @@ hipError_t launch_tf_cat(const float* F, int splits, size_t f_split, int T, int 
     b = *bnd;
   }
   if (T < 0 || T + b.count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tf_cat, dim3(T + b.count), dim3(512), size_t(n) * sizeof(float), s, F, splits,
+  hipLaunchKernelGGL(k_tf_cat, dim3(T + b.count), dim3(512), size_t(n) * sizeof(float), s, status, F, splits,
                      f_split, T, n, embed, vocab, tok, w_in, w_hid, eps, cat16, cat16_lo, cat32, b);
   return hipGetLastError();
 }

@@ -59,6 +59,7 @@ int t_hip(eagle3_trunk* t, hipError_t e, const char* what) {
 template <typename T>
 int t_alloc(eagle3_trunk* t, T** p, size_t count) {
   void* v = nullptr;
+  if (e3::alloc_fault_fires()) return t_hip(t, hipErrorOutOfMemory, "hipMalloc (injected failure)");
   const hipError_t e = hipMalloc(&v, std::max<size_t>(count * sizeof(T), 16));
   if (e != hipSuccess) return t_hip(t, e, "hipMalloc");
   t->allocs.push_back(v);
@@ -215,6 +216,7 @@ int eagle3_trunk_load(const eagle3_trunk_config* cfg, const eagle3_trunk_weights
   T_TRY(t_alloc(t, &t->r_ids, R));
   T_TRY(t_alloc(t, &t->r_res, R + 3));
   for (int j = 0; j < 3; ++j) T_TRY(t_alloc(t, &t->r_taps[j], (R + 1) * n));
+  if (e3::alloc_fault_fires()) return fail(t_hip(t, hipErrorOutOfMemory, "hipHostMalloc (injected failure)"));
   T_HIP(hipHostMalloc(reinterpret_cast<void**>(&t->h_res), (R + 3) * sizeof(int32_t)), "pinned result");
   T_HIP(hipStreamSynchronize(s), "load sync");
 #undef T_TRY

@@ -84,6 +84,10 @@ class Drafter:
     def rewind(self, seq: int, new_len: int):
         B.eagle3_rewind(self.ctx, seq, new_len)
 
+    def status(self) -> int:
+        """Device-side input problems since the last call (EAGLE3_STATUS_* bits)."""
+        return B.eagle3_status(self.ctx)
+
     def kv_len(self, seq: int):
         return B.eagle3_kv_len(self.ctx, seq)
 

@@ -25,6 +25,7 @@
 #ifndef EAGLE3_H
 #define EAGLE3_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -239,6 +240,19 @@ int eagle3_rebuild_after_verify(eagle3_ctx *ctx, int32_t n_seq, const int32_t *s
    Requires 0 <= new_len <= committed.  Host bookkeeping only: no device work. */
 int eagle3_rewind(eagle3_ctx *ctx, int32_t seq, int32_t new_len);
 
+/* Device-side input problems since the last call (a bit mask; the call
+   synchronises the device, returns the bits and clears them).  Token ids and
+   logits live in device memory, so they are checked where they are used:
+     EAGLE3_STATUS_BAD_TOKEN: a boundary token or a teacher-forced token outside
+       [0, target_vocab) (the embedding row read is the nearest valid one);
+     EAGLE3_STATUS_NAN_LOGITS: a draft step whose logits were all NaN (its draft
+       id is 0, target id d2t[0]).
+   A chain or append that raised a bit has produced values the caller should not
+   trust. */
+#define EAGLE3_STATUS_BAD_TOKEN 1u
+#define EAGLE3_STATUS_NAN_LOGITS 2u
+int eagle3_status(eagle3_ctx *ctx, uint32_t *flags);
+
 /* Lengths of a sequence: committed rows and live speculative rows. */
 int eagle3_kv_len(const eagle3_ctx *ctx, int32_t seq, int32_t *committed, int32_t *spec);
 
@@ -317,6 +331,23 @@ const char *eagle3_last_error(const eagle3_ctx *ctx);
 int eagle3_profile_enable(eagle3_ctx *ctx, int32_t kernel, int32_t enable);
 /* Synchronises the recorded events and returns the summed duration and count. */
 int eagle3_profile_read(eagle3_ctx *ctx, double *total_ms, int64_t *launches);
+
+/* Calibration of the ceilings the kernels are measured against, on this GPU (no
+   device memory is allocated; each result is the best of `reps` launches timed with
+   HIP events on `stream`).
+   eagle3_calibrate_mfma: the bf16 MFMA rate the chip sustains, in TFLOP/s: every
+     wave runs four independent chains of iters v_mfma_f32_32x32x16_bf16 on
+     register operands, with no memory traffic.
+   eagle3_calibrate_stream: the streaming read rate of buf_dev (bytes, a multiple of
+     16 is read), in GB/s, each timed read right after an untimed read of flush_dev
+     (flush_bytes; larger than the 256 MB infinity cache makes buf_dev come from
+     HBM).  Pointers 16-byte aligned.
+   sink_dev: EAGLE3_CALIB_SINK_BYTES of device memory a never-taken branch of the
+   kernels may write (it keeps their work from being optimised away). */
+#define EAGLE3_CALIB_SINK_BYTES (2u << 20)
+int eagle3_calibrate_mfma(int32_t iters, int32_t reps, float *sink_dev, double *tflops, void *stream);
+int eagle3_calibrate_stream(const void *buf_dev, size_t bytes, const void *flush_dev, size_t flush_bytes,
+                            int32_t reps, uint32_t *sink_dev, double *gbs, void *stream);
 
 #ifdef __cplusplus
 }

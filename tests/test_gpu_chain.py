@@ -441,3 +441,35 @@ def test_argmax_tie_takes_the_lowest_draft_index(tiny, batched):
         assert cmp[0].logit_err <= 2e-2 and cmp[0].hidden_rel <= 1e-2
         check_round(cmp[1:], f"after the tie, seq {s}")
     dr.close()
+
+
+@pytest.mark.parametrize("seqs", [1, 2])
+def test_status_reports_bad_tokens_and_nan_logits(tiny, seqs):
+    """Bad device-side inputs are not corrected silently: an out-of-range token id
+    (teacher-forced or boundary) raises EAGLE3_STATUS_BAD_TOKEN and taps that make
+    every logit NaN raise EAGLE3_STATUS_NAN_LOGITS; eagle3_status returns the bits
+    and clears them, and a clean round raises none."""
+    wd, _ = tiny
+    dr = gpu_drafter(TINY, wd, max_ctx=100, max_seqs=seqs)
+    S = list(range(seqs))
+    aux, toks = aux_np(TINY, 12, 40), toks_np(TINY, 12, 40)
+    assert dr.status() == 0
+    bad = toks[:10].copy()
+    bad[4] = TINY.target_vocab + 5
+    dr.prefill(0, _tok(bad), to_dev_aux(row_slice(aux, 0, 10)))
+    assert dr.status() == B.STATUS_BAD_TOKEN
+    assert dr.status() == 0
+    for s in S[1:]:
+        dr.prefill(s, _tok(toks[:10]), to_dev_aux(row_slice(aux, 0, 10)))
+    b_aux = to_dev_aux([np.stack([a[20]] * seqs) for a in aux])
+    dr.draft_chain(S, _tok([toks[20]] * seqs), b_aux, 3)
+    assert dr.status() == 0
+    dr.draft_chain(S, _tok([-3] * seqs), b_aux, 3)
+    assert dr.status() == B.STATUS_BAD_TOKEN
+    nan_aux = [a.clone() for a in b_aux]
+    nan_aux[1][:, 7] = float("nan")
+    dr.draft_chain(S, _tok([toks[20]] * seqs), nan_aux, 3)
+    assert dr.status() == B.STATUS_NAN_LOGITS
+    dr.draft_chain(S, _tok([toks[20]] * seqs), b_aux, 3)
+    assert dr.status() == 0
+    dr.close()
