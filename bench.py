@@ -155,7 +155,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rounds", type=int, default=5)
     ap.add_argument("--kv", choices=["f32", "bf16", "q8q5"], default="f32",
-                    help="draft-KV element type (bf16 also feeds the prefill MFMA single bf16 activations)")
+                    help="draft-KV element type")
+    ap.add_argument("--append", choices=["default", "split", "bf16", "f16"], default="default",
+                    help="teacher-forced activation form of the prefill and rebuild GEMMs (default: fp16 with "
+                         "bf16 weights, split with int4 weights)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration runs)")
     ap.add_argument("--weights", choices=["bf16", "int4"], default="bf16",
@@ -222,7 +225,9 @@ def main():
     global WB
     WB = WB_I4 if i4 else WB_BF16
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype,
-                 weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16)
+                 weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16,
+                 append_act={"default": B.APPEND_DEFAULT, "split": B.APPEND_SPLIT, "bf16": B.APPEND_BF16,
+                             "f16": B.APPEND_F16}[args.append])
     stream = torch.cuda.current_stream()
 
     # committed context
@@ -401,7 +406,7 @@ def main():
         "draft_step_hbm_frac_calibrated": round(kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
                                                 / (per_step_us * 1e-6) / 1e9
                                                 / cal["hbm_stream_read_gbs"], 4),
-        "prefill": {"rows": L, "ms": round(prefill_s * 1e3, 3),
+        "prefill": {"rows": L, "ms": round(prefill_s * 1e3, 3), "append_act": args.append,
                     "tflops": round(prefill_flop / prefill_s / 1e12, 2),
                     "frac_bf16_peak": round(prefill_flop / prefill_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                     "frac_calibrated": round(prefill_flop / prefill_s / 1e12 / cal["mfma_bf16_tflops"], 4),

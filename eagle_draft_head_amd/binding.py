@@ -20,7 +20,7 @@ KEEP_SPEC = 1
 STORED_BOUNDARY = 2
 ROUND_LOCAL = 4
 KV_F32, KV_BF16, KV_Q8Q5 = 0, 1, 2
-APPEND_DEFAULT, APPEND_BF16, APPEND_SPLIT = 0, 1, 2
+APPEND_DEFAULT, APPEND_BF16, APPEND_SPLIT, APPEND_F16 = 0, 1, 2, 3
 WEIGHTS_BF16, WEIGHTS_I4 = 0, 1
 
 ERR_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_SHAPE: "E_SHAPE", E_UNSUPPORTED: "E_UNSUPPORTED",
@@ -261,7 +261,7 @@ def eagle3_rewind(ctx, seq: int, new_len: int) -> None:
     _check(ctx, library().eagle3_rewind(ctx, seq, new_len))
 
 
-STATUS_BAD_TOKEN, STATUS_NAN_LOGITS = 1, 2
+STATUS_BAD_TOKEN, STATUS_NAN_LOGITS, STATUS_APPEND_RANGE = 1, 2, 4
 
 
 def eagle3_status(ctx) -> int:

@@ -34,7 +34,11 @@ namespace e3 {
 
 namespace {
 std::atomic<int32_t> g_alloc_fault{0};
+std::atomic<int64_t> g_live_allocs{0};
 }  // namespace
+
+void note_alloc() { g_live_allocs.fetch_add(1, std::memory_order_relaxed); }
+void note_free(size_t n) { g_live_allocs.fetch_sub(int64_t(n), std::memory_order_relaxed); }
 
 bool alloc_fault_fires() {
   int32_t v = g_alloc_fault.load(std::memory_order_relaxed);
@@ -100,6 +104,8 @@ struct eagle3_ctx {
   int kv_f32 = 1;
   int kv_q = 0;             // quantized K/V regions (q8_0 K, q5_1 V); elements are bytes
   int tf_split = 0;         // teacher-forced MFMA passes take (hi, lo) bf16 activation pairs
+  int tf_f16 = 0;           // ... or one fp16 term against fp16 weight copies scaled by 2^8
+  uint16_t *w_fc16 = nullptr, *w_kv16 = nullptr;  // tf_f16: fc and the K/V rows of QKV, fp16 x 2^8
   float* kv_stage = nullptr;  // kv_q: the chain step's new K/V row in fp32 [2][kvd]
   size_t kv_esize = 4;      // bytes per cache element
   size_t kv_seq_elems = 0;  // K + V elements per sequence
@@ -215,12 +221,14 @@ int dalloc(eagle3_ctx* c, T** p, size_t count) {
   hipError_t e = hipMalloc(&v, count * sizeof(T) > 0 ? count * sizeof(T) : 16);
   if (e != hipSuccess) return hip_fail(c, e, "hipMalloc");
   c->allocs.push_back(v);
+  e3::note_alloc();
   *p = static_cast<T*>(v);
   return EAGLE3_OK;
 }
 
 void free_all(eagle3_ctx* c) {
   for (void* p : c->allocs) (void)hipFree(p);
+  e3::note_free(c->allocs.size());
   c->allocs.clear();
   for (hipEvent_t e : c->prof.ev) (void)hipEventDestroy(e);
   c->prof.ev.clear();
@@ -290,8 +298,10 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (cfg->weight_format != EAGLE3_WEIGHTS_BF16 && cfg->weight_format != EAGLE3_WEIGHTS_I4)
     return bad("unknown weight_format", EAGLE3_E_INVAL);
   if (cfg->append_act != EAGLE3_APPEND_DEFAULT && cfg->append_act != EAGLE3_APPEND_BF16 &&
-      cfg->append_act != EAGLE3_APPEND_SPLIT)
+      cfg->append_act != EAGLE3_APPEND_SPLIT && cfg->append_act != EAGLE3_APPEND_F16)
     return bad("unknown append_act", EAGLE3_E_INVAL);
+  if (cfg->append_act == EAGLE3_APPEND_F16 && cfg->weight_format != EAGLE3_WEIGHTS_BF16)
+    return bad("fp16 teacher-forced activations need bf16 weights", EAGLE3_E_UNSUPPORTED);
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
     if (cfg->max_seqs != 1) return bad("int4 weights: batch-1 drafting only (max_seqs 1)", EAGLE3_E_UNSUPPORTED);
     if (cfg->n_embd % 32 || (int64_t(cfg->n_head) * cfg->head_dim) % 32 || cfg->n_ff % 32)
@@ -489,7 +499,16 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
   E3_TRY(dalloc(c, &c->tf_A, size_t(c->tf_rows) * 3 * n));
   E3_TRY(dalloc(c, &c->tf_cat16, size_t(c->tf_rows) * 2 * n));
-  c->tf_split = cfg->append_act != EAGLE3_APPEND_BF16;
+  // the default: one fp16 product with bf16 weights, split bf16 terms with int4 weights
+  const int32_t act = cfg->append_act != EAGLE3_APPEND_DEFAULT ? cfg->append_act
+                      : cfg->weight_format == EAGLE3_WEIGHTS_BF16 ? EAGLE3_APPEND_F16
+                                                                   : EAGLE3_APPEND_SPLIT;
+  c->tf_f16 = act == EAGLE3_APPEND_F16;
+  c->tf_split = act == EAGLE3_APPEND_SPLIT;
+  if (c->tf_f16) {
+    E3_TRY(dalloc(c, &c->w_fc16, size_t(n) * 3 * n));
+    E3_TRY(dalloc(c, &c->w_kv16, size_t(2 * kvd) * 2 * n));
+  }
   if (c->tf_split) {  // fp32-grade K/V rows
     E3_TRY(dalloc(c, &c->tf_A_lo, size_t(c->tf_rows) * 3 * n));
     E3_TRY(dalloc(c, &c->tf_cat16_lo, size_t(c->tf_rows) * 2 * n));
@@ -614,6 +633,12 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     E3_TRY(gather(c->w_gu, w->gate_proj, int(n)));
     for (int64_t i = 0; i < ff; ++i) dst[size_t(i)] = int32_t(2 * i + 1);
     E3_TRY(gather(c->w_gu, w->up_proj, int(n)));
+  }
+  if (c->tf_f16) {  // fp16 copies (x 2^8, exact) of the weights the MFMA appends multiply
+    E3_TRYH(e3::launch_bf16_to_f16_x256(c->w_fc, c->w_fc16, size_t(n) * 3 * n, c->status, s), "fp16 fc");
+    E3_TRYH(e3::launch_bf16_to_f16_x256(c->w_qkv + size_t(qd) * 2 * n, c->w_kv16, size_t(2 * kvd) * 2 * n,
+                                        c->status, s),
+            "fp16 kv");
   }
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
     c->i4 = true;
@@ -866,6 +891,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
     }
     int sp1 = 1, sp2 = 1;
     size_t f_split = 0, p_split = 0;
+    float p_scale = 1.0f;  // applied to the summed products of this pass
     if (P <= 16) {
       // weight-streaming path: every weight chunk applied to all rows of the pass
       {
@@ -889,14 +915,16 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       p_split = size_t(e3::gemv_multi_width(T > 0 ? T : 1)) * kvd2;
     } else {
       // MFMA path
-      E3_HIP(c, e3::launch_pack_aux(x0, x1, x2, P, n, c->tf_A, c->tf_A_lo, s, yb), "pack aux");
+      E3_HIP(c, e3::launch_pack_aux(x0, x1, x2, P, n, c->tf_A, c->tf_A_lo, s, yb, c->tf_f16, c->status),
+             "pack aux");
+      if (c->tf_f16) p_scale = 1.0f / 256.0f;  // the fp16 weight copies carry 2^8
       e3::GemmPlan p1 = e3::gemm_plan(P, n, 3 * n);
       while (p1.splits > 1 && size_t(wsp) * p1.splits * P * n > c->tf_F_cap) p1.splits /= 2;
       sp1 = p1.splits * wsp;
       {
         ProfScope ps(c, 7, s);
-        E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->w_fc, 3 * n, c->tf_F, P, n,
-                                       3 * n, p1, s), "fc gemm");
+        E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->tf_f16 ? c->w_fc16 : c->w_fc, 3 * n,
+                                       c->tf_F, P, n, 3 * n, p1, s, c->tf_f16 != 0), "fc gemm");
         if (c->i4)  // the weights' low halves into the next split slots
           E3_HIP(c, e3::launch_gemm_bf16(c->tf_A, c->tf_A_lo, 3 * n, c->i4_fc_lo, 3 * n,
                                          c->tf_F + size_t(p1.splits) * P * n, P, n, 3 * n, p1, s),
@@ -905,7 +933,7 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       f_split = size_t(P) * n;
       E3_HIP(c, e3::launch_tf_cat(c->status, c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
                                   c->nrm_hid, c->cfg.rms_eps, c->tf_cat16, c->tf_cat16_lo, nullptr, s,
-                                  &bo),
+                                  &bo, p_scale, c->tf_f16),
              "tf cat");
       if (T > 0) {
         e3::GemmPlan p2 = e3::gemm_plan(T, kvd2, 2 * n);
@@ -913,8 +941,8 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
         sp2 = p2.splits * wsp;
         ProfScope ps(c, 8, s);
         E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n,
-                                       c->w_qkv + size_t(c->qd) * 2 * n, 2 * n, c->tf_P, T, kvd2,
-                                       2 * n, p2, s), "kv gemm");
+                                       c->tf_f16 ? c->w_kv16 : c->w_qkv + size_t(c->qd) * 2 * n, 2 * n,
+                                       c->tf_P, T, kvd2, 2 * n, p2, s, c->tf_f16 != 0), "kv gemm");
         if (c->i4)
           E3_HIP(c, e3::launch_gemm_bf16(c->tf_cat16, c->tf_cat16_lo, 2 * n, c->i4_kv_lo, 2 * n,
                                          c->tf_P + size_t(p2.splits) * T * kvd2, T, kvd2, 2 * n, p2, s),
@@ -929,7 +957,8 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       auto flush = [&]() -> int {
         if (ss.n == 0) return EAGLE3_OK;
         E3_HIP(c, e3::launch_tf_store(c->tf_P, sp2, p_split, ss, c->nkv, c->hd, c->rot, c->inv_freq,
-                                      c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s, c->kv_q), "tf store");
+                                      c->kv, c->kv_seq_elems, c->cap, c->kv_f32, s, c->kv_q, p_scale),
+               "tf store");
         ss = e3::StoreSegs{};
         return EAGLE3_OK;
       };
@@ -1419,6 +1448,8 @@ int eagle3_profile_read(eagle3_ctx* ctx, double* total_ms, int64_t* launches) {
 }
 
 void eagle3_test_fail_allocation(int32_t n) { e3::g_alloc_fault.store(n > 0 ? n : 0); }
+
+int64_t eagle3_test_live_allocations(void) { return e3::g_live_allocs.load(); }
 
 // ---- the ledger on its own ----------------------------------------------------
 int eagle3_ledger_create(int32_t max_ctx, int32_t max_seqs, int32_t max_gamma, eagle3_ledger** out) {

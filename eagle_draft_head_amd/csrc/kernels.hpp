@@ -15,11 +15,15 @@ namespace e3 {
 // nearest valid row, an argmax over NaN logits takes draft id 0).
 constexpr uint32_t kStatusBadToken = 1u;   // a token id outside [0, target_vocab)
 constexpr uint32_t kStatusNanLogits = 2u;  // a draft step whose logits were all NaN
+constexpr uint32_t kStatusAppendRange = 4u;  // a teacher-forced fp16 activation out of range
 
 // Fault injection for tests (include/eagle3_testing.h): while positive, every
 // device allocation of the library counts it down and the one that brings it to
 // zero fails as out of memory.
 bool alloc_fault_fires();
+// count of the device and pinned host allocations the library holds (all handles)
+void note_alloc();
+void note_free(size_t n);
 
 struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
@@ -361,9 +365,11 @@ hipError_t launch_bfinal(uint32_t* status, const BatchRows& br, int m, int gamma
 // A[t, 0:3n] = [aux0[t]; aux1[t]; aux2[t]] as bf16 (A_hi), rows from yb.rows_x on
 // taken from yb's streams; with A_lo given, also the bf16 remainder
 // A_lo = bf16(a - A_hi), so A_hi + A_lo carries ~16 mantissa bits.
+// f16: the taps as fp16 (A_lo NULL; a value outside the fp16 range raises
+// kStatusAppendRange), else bf16 (hi, lo) pairs (A_lo may be NULL: hi only)
 hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
                            uint16_t* A_hi, uint16_t* A_lo, hipStream_t s,
-                           const TapRowsB& yb = no_tap_rows_b());
+                           const TapRowsB& yb = no_tap_rows_b(), int f16 = 0, uint32_t* status = nullptr);
 // Boundary features of a teacher-forced pass: fc rows [T_cat, T_cat + count) are the
 // next rounds' boundary rows; row T_cat + j goes to sequence slot slot[j]:
 // y[slot] = f [n], yw[slot] = f * w_hid [n], ssq[slot] = sum f^2.
@@ -382,7 +388,8 @@ struct BndOut {
 hipError_t launch_tf_cat(uint32_t* status, const float* F, int splits, size_t f_split, int T, int n,
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
-                         float* cat32, hipStream_t s, const BndOut* bnd = nullptr);
+                         float* cat32, hipStream_t s, const BndOut* bnd = nullptr, float f_scale = 1.0f,
+                         int f16 = 0);
 // Up to kStoreSegs runs of consecutive rows of one append pass: rows
 // [row0[s], row0[s + 1]) go to sequence slot[s] from position pos0[s] on.
 constexpr int kStoreSegs = 32;
@@ -399,7 +406,8 @@ struct StoreSegs {
 // (kv_q: quantized regions; seq_elems is then the bytes per slot, K region then V)
 hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const StoreSegs& segs,
                            int n_head_kv, int head_dim, int rope_dim, const double* inv_freq, void* kv,
-                           size_t seq_elems, int cap, int kv_f32, hipStream_t s, int kv_q = 0);
+                           size_t seq_elems, int cap, int kv_f32, hipStream_t s, int kv_q = 0,
+                           float p_scale = 1.0f);
 // rows [row0, row0 + nrows) of quantized K/V regions as fp32 [nrows][nkv][hd]
 hipError_t launch_kvq_read(const void* kreg, const void* vreg, int nkv, int cap, int hd, int row0,
                            int nrows, float* k_out, float* v_out, hipStream_t s);
@@ -414,9 +422,14 @@ struct GemmPlan {
   int splits;  // K split (z planes of C)
 };
 GemmPlan gemm_plan(int M, int N, int K);
+// f16: A and B hold fp16 values (one v_mfma_f32_16x16x32_f16 product, no A_lo)
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
                             int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
-                            hipStream_t s);
+                            hipStream_t s, bool f16 = false);
+// dst[i] = fp16 bits of (bf16 src[i]) * 2^8, exact for 2^-25 <= |src| < 256 (and 0);
+// any other weight raises kStatusAppendRange in *status
+hipError_t launch_bf16_to_f16_x256(const uint16_t* src, uint16_t* dst, size_t count, uint32_t* status,
+                                   hipStream_t s);
 
 // ---- the synthetic target trunk (trunk.hip) ----
 // status word bits raised by the trunk kernels

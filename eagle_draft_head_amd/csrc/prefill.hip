@@ -1,9 +1,12 @@
 // Teacher-forced append of T rows (prefill and rebuild_after_verify):
-//   A = bf16[aux0 | aux1 | aux2]            (pack)
+//   A = [aux0 | aux1 | aux2] in 16-bit form  (pack)
 //   F = A . W_fc^T                          (MFMA GEMM, fp32 out, optional split-K)
-//   cat = bf16[RMSNorm(E[tok]) | RMSNorm(F)]
+//   cat = 16-bit[RMSNorm(E[tok]) | RMSNorm(F)]
 //   KV = cat . W_kv^T                       (MFMA GEMM over the k|v rows of W_qkv)
-//   rotate k, round to bf16, store rows into the draft KV.
+//   rotate k, store rows into the draft KV.
+// The 16-bit forms: bf16 (hi, lo) pairs, so two products give fp32-grade rows; or
+// one fp16 term against fp16 copies of the weights scaled by 2^8 (a bf16 weight
+// times 2^8 is exact in fp16), 2^-8 applied when the products are summed.
 // Only K and V of teacher-forced rows are ever read again, so Q, attention,
 // the MLP and the head are not run for them.
 #include "common.hpp"
@@ -12,7 +15,46 @@
 namespace e3 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// one 16x16x32 MFMA on 16-byte fragments holding bf16 or (F16) fp16 values
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 a, const bf16x8 b, f32x4 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp16 bits of x, raising kStatusAppendRange when x is outside the fp16 range
+__device__ __forceinline__ uint16_t to_f16_checked(float x, uint32_t* status) {
+  if (!(fabsf(x) < 65504.f)) atomicOr(status, kStatusAppendRange);
+  return f32_to_f16_bits(x);
+}
+
+// dst[i] = fp16(src[i] * 2^8) for bf16 src: exact for 2^-25 <= |src| < 256 (eight
+// significant bits fit an fp16 normal or a subnormal down to 2^-17); a weight the
+// copy does not hold exactly raises kStatusAppendRange
+__global__ __launch_bounds__(256) void k_bf16_to_f16_x256(const uint16_t* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, size_t count,
+                                                         uint32_t* __restrict__ status) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const float x = bf16_to_f32(src[i]) * 256.0f;
+  const uint16_t h = f32_to_f16_bits(x);
+  if (!(f16_bits_to_f32(h) == x)) atomicOr(status, kStatusAppendRange);
+  dst[i] = h;
+}
+
+hipError_t launch_bf16_to_f16_x256(const uint16_t* src, uint16_t* dst, size_t count, uint32_t* status,
+                                   hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bf16_to_f16_x256, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, src, dst,
+                     count, status);
+  return hipGetLastError();
+}
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
@@ -22,7 +64,8 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
                                                   const float* __restrict__ a1,
                                                   const float* __restrict__ a2, int T, int n,
                                                   uint16_t* __restrict__ A_hi,
-                                                  uint16_t* __restrict__ A_lo, const TapRowsB yb) {
+                                                  uint16_t* __restrict__ A_lo, const TapRowsB yb,
+                                                  int f16, uint32_t* __restrict__ status) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (t >= T || c >= 3 * n) return;
@@ -34,10 +77,15 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
   const float4 v0 = src[0], v1 = src[1];
   const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   uint16_t h[8], l[8];
+  if (f16) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16(v[e]);
-    l[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
+    for (int e = 0; e < 8; ++e) h[e] = to_f16_checked(v[e], status);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[e] = f32_to_bf16(v[e]);
+      l[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
+    }
   }
   const size_t at = (size_t)t * 3 * n + c;
   *reinterpret_cast<uint4*>(A_hi + at) =
@@ -50,12 +98,13 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
 }
 
 hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
-                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s, const TapRowsB& yb) {
+                           uint16_t* A_hi, uint16_t* A_lo, hipStream_t s, const TapRowsB& yb, int f16,
+                           uint32_t* status) {
   if (T <= 0) return hipSuccess;
-  if ((n & 7) || T > 65535) return hipErrorInvalidValue;
+  if ((n & 7) || T > 65535 || (f16 && A_lo)) return hipErrorInvalidValue;
   if (yb.rows_x < T && (!yb.y[0] || !yb.y[1] || !yb.y[2])) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_pack_aux, dim3((3 * n + 2047) / 2048, T), dim3(256), 0, s, a0, a1, a2, T, n,
-                     A_hi, A_lo, yb);
+                     A_hi, A_lo, yb, f16, status);
   return hipGetLastError();
 }
 
@@ -101,7 +150,8 @@ __global__ __launch_bounds__(512) void k_tf_cat(uint32_t* __restrict__ status, c
                                                 const float* __restrict__ w_hid, float eps,
                                                 uint16_t* __restrict__ cat16,
                                                 uint16_t* __restrict__ cat16_lo,
-                                                float* __restrict__ cat32, const BndOut bnd) {
+                                                float* __restrict__ cat32, const BndOut bnd,
+                                                float f_scale, int f16) {
   extern __shared__ float fs[];  // [n]
   __shared__ float red[32];
   const int t = blockIdx.x;
@@ -114,7 +164,8 @@ __global__ __launch_bounds__(512) void k_tf_cat(uint32_t* __restrict__ status, c
     const float4* wh4 = reinterpret_cast<const float4*>(w_hid);
     float sf = 0.f, unused = 0.f;
     for (int i = threadIdx.x; i < (n >> 2); i += blockDim.x) {
-      const float4 f = sum_splits4(F + (size_t)t * n + 4 * i, splits, f_split);
+      float4 f = sum_splits4(F + (size_t)t * n + 4 * i, splits, f_split);
+      f = make_float4(f.x * f_scale, f.y * f_scale, f.z * f_scale, f.w * f_scale);
       const float4 wh = wh4[i];
       reinterpret_cast<float4*>(y)[i] = f;
       reinterpret_cast<float4*>(yw)[i] = make_float4(f.x * wh.x, f.y * wh.y, f.z * wh.z, f.w * wh.w);
@@ -135,7 +186,8 @@ __global__ __launch_bounds__(512) void k_tf_cat(uint32_t* __restrict__ status, c
   const int n4 = n >> 2;
 #pragma unroll 2
   for (int i = threadIdx.x; i < n4; i += blockDim.x) {
-    const float4 f = sum_splits4(F + (size_t)t * n + 4 * i, splits, f_split);
+    float4 f = sum_splits4(F + (size_t)t * n + 4 * i, splits, f_split);
+    f = make_float4(f.x * f_scale, f.y * f_scale, f.z * f_scale, f.w * f_scale);
     f4[i] = f;
     sf = fmaf(f.x, f.x, fmaf(f.y, f.y, fmaf(f.z, f.z, fmaf(f.w, f.w, sf))));
     const uint2 u = e4[i];
@@ -156,9 +208,10 @@ __global__ __launch_bounds__(512) void k_tf_cat(uint32_t* __restrict__ status, c
                                   wh.w * (f.w * iff));
     if (cat16) {
       uint16_t* row = cat16 + (size_t)t * 2 * n;
-      const uint16_t h[8] = {f32_to_bf16(ea.x), f32_to_bf16(ea.y), f32_to_bf16(ea.z),
-                             f32_to_bf16(ea.w), f32_to_bf16(fb.x), f32_to_bf16(fb.y),
-                             f32_to_bf16(fb.z), f32_to_bf16(fb.w)};
+      const float cv[8] = {ea.x, ea.y, ea.z, ea.w, fb.x, fb.y, fb.z, fb.w};
+      uint16_t h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h[q] = f16 ? to_f16_checked(cv[q], status) : f32_to_bf16(cv[q]);
       uint2 pa, pb;
       pa.x = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
       pa.y = uint32_t(h[2]) | (uint32_t(h[3]) << 16);
@@ -190,7 +243,8 @@ __global__ __launch_bounds__(512) void k_tf_cat(uint32_t* __restrict__ status, c
 hipError_t launch_tf_cat(uint32_t* status, const float* F, int splits, size_t f_split, int T, int n,
                          const uint16_t* embed, int vocab, const int32_t* tok, const float* w_in,
                          const float* w_hid, float eps, uint16_t* cat16, uint16_t* cat16_lo,
-                         float* cat32, hipStream_t s, const BndOut* bnd) {
+                         float* cat32, hipStream_t s, const BndOut* bnd, float f_scale, int f16) {
+  if (f16 && (cat16_lo || !cat16)) return hipErrorInvalidValue;
   BndOut b{};
   if (bnd) {
     if (bnd->count < 0 || bnd->count > kBndRows || (bnd->count > 0 && (!bnd->y || !bnd->yw || !bnd->ssq)))
@@ -199,7 +253,8 @@ hipError_t launch_tf_cat(uint32_t* status, const float* F, int splits, size_t f_
   }
   if (T < 0 || T + b.count <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_tf_cat, dim3(T + b.count), dim3(512), size_t(n) * sizeof(float), s, status, F, splits,
-                     f_split, T, n, embed, vocab, tok, w_in, w_hid, eps, cat16, cat16_lo, cat32, b);
+                     f_split, T, n, embed, vocab, tok, w_in, w_hid, eps, cat16, cat16_lo, cat32, b, f_scale,
+                     f16);
   return hipGetLastError();
 }
 
@@ -212,7 +267,7 @@ __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, i
                                                   int hd, int rope_dim,
                                                   const double* __restrict__ inv_freq,
                                                   char* __restrict__ kv, size_t seq_elems, int cap,
-                                                  int kv_f32) {
+                                                  int kv_f32, float p_scale) {
   const int t = segs.row0[0] + blockIdx.x;
   int sg = 0;
   while (sg + 1 < segs.n && t >= segs.row0[sg + 1]) ++sg;
@@ -225,8 +280,8 @@ __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, i
   // grid.y spreads the kvd value pairs of a row over blocks (one pair per thread)
   for (int pr = blockIdx.y * blockDim.x + threadIdx.x; pr < kvd; pr += gridDim.y * blockDim.x) {
     const int r = 2 * pr;
-    float y0 = sum_splits(row + r, splits, p_split);
-    float y1 = sum_splits(row + r + 1, splits, p_split);
+    float y0 = sum_splits(row + r, splits, p_split) * p_scale;
+    float y1 = sum_splits(row + r + 1, splits, p_split) * p_scale;
     const bool is_k = r < kvd;
     const int rr = is_k ? r : r - kvd;
     const int head = rr / hd, li = rr - head * hd;
@@ -256,7 +311,7 @@ __global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P,
                                                     int hd, int rope_dim,
                                                     const double* __restrict__ inv_freq,
                                                     uint8_t* __restrict__ kv, size_t seq_bytes,
-                                                    int cap) {
+                                                    int cap, float p_scale) {
   __shared__ float srow[512];
   const int t = segs.row0[0] + blockIdx.x;
   int sg = 0;
@@ -270,8 +325,8 @@ __global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P,
   {
     const int r = v0 + 2 * threadIdx.x;
     if (r < 2 * kvd) {
-      float y0 = sum_splits(row + r, splits, p_split);
-      float y1 = sum_splits(row + r + 1, splits, p_split);
+      float y0 = sum_splits(row + r, splits, p_split) * p_scale;
+      float y1 = sum_splits(row + r + 1, splits, p_split) * p_scale;
       const bool is_k = r < kvd;
       const int rr = is_k ? r : r - kvd;
       const int li = rr % hd;
@@ -305,7 +360,7 @@ __global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P,
 
 hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const StoreSegs& segs,
                            int n_head_kv, int head_dim, int rope_dim, const double* inv_freq, void* kv,
-                           size_t seq_elems, int cap, int kv_f32, hipStream_t s, int kv_q) {
+                           size_t seq_elems, int cap, int kv_f32, hipStream_t s, int kv_q, float p_scale) {
   if (segs.n < 1 || segs.n > kStoreSegs) return hipErrorInvalidValue;
   const int rows = segs.row0[segs.n] - segs.row0[0];
   if (rows <= 0) return hipSuccess;
@@ -313,12 +368,13 @@ hipError_t launch_tf_store(const float* P, int splits, size_t p_split, const Sto
     if (head_dim % 32 || 512 % head_dim) return hipErrorInvalidValue;
     const int blocks = (2 * n_head_kv * head_dim + 511) / 512;
     hipLaunchKernelGGL(k_tf_store_q, dim3(rows, blocks), dim3(256), 0, s, P, splits, p_split, segs,
-                       n_head_kv, head_dim, rope_dim, inv_freq, static_cast<uint8_t*>(kv), seq_elems, cap);
+                       n_head_kv, head_dim, rope_dim, inv_freq, static_cast<uint8_t*>(kv), seq_elems, cap,
+                       p_scale);
     return hipGetLastError();
   }
   const int pair_blocks = (n_head_kv * head_dim + 255) / 256;
   hipLaunchKernelGGL(k_tf_store, dim3(rows, pair_blocks), dim3(256), 0, s, P, splits, p_split, segs, n_head_kv,
-                     head_dim, rope_dim, inv_freq, static_cast<char*>(kv), seq_elems, cap, kv_f32);
+                     head_dim, rope_dim, inv_freq, static_cast<char*>(kv), seq_elems, cap, kv_f32, p_scale);
   return hipGetLastError();
 }
 
@@ -442,7 +498,7 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int BK, int NST>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int BK, int NST, bool F16 = false>
 __global__ __launch_bounds__(WM * WN * 64) void k_gemm(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, int lda,
     const uint16_t* __restrict__ B, int ldb, float* __restrict__ C, int M, int N, int kper,
@@ -533,7 +589,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma16<F16>(af[i], bfr[j], acc[i][j]);
       }
     }
   }
@@ -585,7 +641,7 @@ struct SgEpi {
   float* logits;      // kBEpiArgmax, optional: [m][N]
 };
 
-template <bool SPLIT, int EPI>
+template <bool SPLIT, int EPI, bool F16 = false>
 __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ A2, int lda,
                                                const uint16_t* __restrict__ B, int ldb,
@@ -659,7 +715,7 @@ __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
         }                                                                                    \
         _Pragma("unroll") for (int i2 = 0; i2 < 2; ++i2)                                     \
         _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i2][j] =                           \
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i2], bfr[j], acc[i2][j], 0, 0, 0);    \
+            mfma16<F16>(af[i2], bfr[j], acc[i2][j]);                                         \
       }                                                                                      \
     }                                                                                        \
   }
@@ -760,12 +816,16 @@ __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
 }
 
 static hipError_t launch_sgemm(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
-                               int ldb, float* C, int M, int N, int kper, int splits, hipStream_t s) {
+                               int ldb, float* C, int M, int N, int kper, int splits, hipStream_t s,
+                               bool f16) {
   if (M > 32 || kper % kSgBK) return hipErrorInvalidValue;
   const int nt = (N + kSgRows - 1) / kSgRows;
   dim3 grid((nt + 7) / 8 * 8, 1, splits);
   const SgEpi e{};
-  if (A_lo)
+  if (f16)
+    hipLaunchKernelGGL((k_sgemm<false, kBEpiPartial, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C,
+                       M, N, kper, nt, e);
+  else if (A_lo)
     hipLaunchKernelGGL((k_sgemm<true, kBEpiPartial>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C,
                        M, N, kper, nt, e);
   else
@@ -850,7 +910,7 @@ GemmPlan gemm_plan(int M, int N, int K) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, bool SPLIT, int BK, int NST>
+template <int BM, int BN, int WM, int WN, bool SPLIT, int BK, int NST, bool F16 = false>
 static hipError_t launch_tiles(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
                                const uint16_t* B, int ldb, float* C, int M, int N, int kper,
                                int splits, hipStream_t s) {
@@ -859,7 +919,7 @@ static hipError_t launch_tiles(const uint16_t* A_hi, const uint16_t* A_lo, int l
   static_assert(lds <= 160 * 1024, "LDS ring exceeds a workgroup's LDS");
   static bool attr_set = false;  // the attribute is per kernel; setting it twice is harmless
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, SPLIT, BK, NST>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<BM, BN, WM, WN, SPLIT, BK, NST, F16>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -867,22 +927,31 @@ static hipError_t launch_tiles(const uint16_t* A_hi, const uint16_t* A_lo, int l
   const int mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   const int nt8 = (nt + 7) / 8 * 8;
   dim3 grid(mt * nt8, 1, splits), block(WM * WN * 64);
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, SPLIT, BK, NST>), grid, block, lds, s, A_hi, A_lo, lda, B,
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, SPLIT, BK, NST, F16>), grid, block, lds, s, A_hi, A_lo, lda, B,
                      ldb, C, M, N, kper, mt, nt);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
                             int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
-                            hipStream_t s) {
+                            hipStream_t s, bool f16) {
   const int splits = plan.splits;
-  if (M <= 0 || N <= 0 || splits < 1 || K % (kBKPlain * splits) != 0 || (lda & 7) || (ldb & 7))
+  if (M <= 0 || N <= 0 || splits < 1 || K % (kBKPlain * splits) != 0 || (lda & 7) || (ldb & 7) ||
+      (f16 && A_lo))
     return hipErrorInvalidValue;
   const int kper = K / splits;
   const int bm = gemm_bm(M);
   if (bm == 32) {
     if (plan.bn != kSgRows) return hipErrorInvalidValue;
-    return launch_sgemm(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    return launch_sgemm(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s, f16);
+  }
+  if (f16) {  // one fp16 product
+    if (bm == 256 && plan.bn == 320)
+      return launch_tiles<256, 320, 4, 4, false, kBKPlain, 2, true>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    if (plan.bn != bm) return hipErrorInvalidValue;
+    if (bm == 256)
+      return launch_tiles<256, 256, 4, 4, false, kBKPlain, 2, true>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    return launch_tiles<128, 128, 2, 2, false, kBKPlain, 3, true>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
   }
   if (bm == 256 && plan.bn == 320) {
     if (A_lo) return launch_tiles<256, 320, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);

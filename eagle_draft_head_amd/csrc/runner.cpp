@@ -63,14 +63,19 @@ int t_alloc(eagle3_trunk* t, T** p, size_t count) {
   const hipError_t e = hipMalloc(&v, std::max<size_t>(count * sizeof(T), 16));
   if (e != hipSuccess) return t_hip(t, e, "hipMalloc");
   t->allocs.push_back(v);
+  e3::note_alloc();
   *p = static_cast<T*>(v);
   return EAGLE3_OK;
 }
 
 void t_free_all(eagle3_trunk* t) {
   for (void* p : t->allocs) (void)hipFree(p);
+  e3::note_free(t->allocs.size());
   t->allocs.clear();
-  if (t->h_res) (void)hipHostFree(t->h_res);
+  if (t->h_res) {
+    (void)hipHostFree(t->h_res);
+    e3::note_free(1);
+  }
   t->h_res = nullptr;
 }
 
@@ -218,6 +223,7 @@ int eagle3_trunk_load(const eagle3_trunk_config* cfg, const eagle3_trunk_weights
   for (int j = 0; j < 3; ++j) T_TRY(t_alloc(t, &t->r_taps[j], (R + 1) * n));
   if (e3::alloc_fault_fires()) return fail(t_hip(t, hipErrorOutOfMemory, "hipHostMalloc (injected failure)"));
   T_HIP(hipHostMalloc(reinterpret_cast<void**>(&t->h_res), (R + 3) * sizeof(int32_t)), "pinned result");
+  e3::note_alloc();
   T_HIP(hipStreamSynchronize(s), "load sync");
 #undef T_TRY
 #undef T_HIP

@@ -91,17 +91,29 @@ typedef struct {
 #define EAGLE3_KV_BF16 1
 
 /* Activations of the teacher-forced (prefill / rebuild) MFMA passes of more than
-   16 rows, whose weights are exact in bf16.  EAGLE3_APPEND_SPLIT (the default,
-   also EAGLE3_APPEND_DEFAULT) feeds the fp32 taps and the normalised
-   K/V-projection inputs [eN ; gN] as two bf16 terms hi + lo (two MFMA products,
-   fp32-grade rows).  EAGLE3_APPEND_BF16 rounds both to the nearest bf16 once (one
-   product, half the MFMA work); at the drafter sizes in the tests that moves
-   draft logits by 1-2.3e-2 against exact rows, as much as the parity bar allows,
-   so it is a speed option, not the default.  Passes of at most 16 rows stream the
-   weights through fp32 GEMVs either way. */
+   16 rows (the rows of one call, its boundary rows included, up to 2048 rows per
+   pass), whose weights are exact in bf16.  Passes of at most 16 rows stream the
+   weights through fp32 GEMVs in every mode.
+   EAGLE3_APPEND_DEFAULT: EAGLE3_APPEND_F16 with bf16 weights, EAGLE3_APPEND_SPLIT
+   with int4 weights.
+   EAGLE3_APPEND_SPLIT feeds the fp32 taps and the normalised K/V-projection inputs
+   [eN ; gN] as two bf16 terms hi + lo (two MFMA products, fp32-grade rows).
+   EAGLE3_APPEND_BF16 rounds both to the nearest bf16 once (one product); at the
+   drafter sizes in the tests that moves draft logits by 1-2.3e-2 against exact
+   rows, as much as the parity bar allows, so it is only a speed option. */
 #define EAGLE3_APPEND_DEFAULT 0
 #define EAGLE3_APPEND_BF16 1
 #define EAGLE3_APPEND_SPLIT 2
+/* EAGLE3_APPEND_F16: one fp16 product.  The taps and [eN ; gN] are rounded to the
+   nearest fp16 (11 significant bits against bf16's 8) and multiplied with fp16
+   copies of W_fc and of the K/V rows of QKV scaled by 2^8 (a bf16 weight w times
+   2^8 is exact in fp16 for 2^-25 <= |w| < 256), the products summed in fp32 and
+   scaled back by 2^-8.  Half the MFMA work of SPLIT; at the drafter sizes in the
+   tests draft logits stay within about 3e-3 of exact rows.  Needs bf16 weights
+   (EAGLE3_E_INVAL otherwise); a tap or input outside the fp16 range, or a weight
+   the scaled copy does not hold exactly, raises EAGLE3_STATUS_APPEND_RANGE (see
+   eagle3_status).  0.3 GB of weight copies at the 5120-wide drafter. */
+#define EAGLE3_APPEND_F16 3
 /* EAGLE3_KV_Q8Q5: K rows in q8_0 and V rows in q5_1, blocks of 32 values along
    head_dim (memra_engine `eagle.rs`, `Eagle3Scratch` doc and `attn`: the draft
    layer appends quantized K/V rows and decode attention reads the quantized views;
@@ -251,6 +263,11 @@ int eagle3_rewind(eagle3_ctx *ctx, int32_t seq, int32_t new_len);
    trust. */
 #define EAGLE3_STATUS_BAD_TOKEN 1u
 #define EAGLE3_STATUS_NAN_LOGITS 2u
+/*   EAGLE3_STATUS_APPEND_RANGE: with EAGLE3_APPEND_F16, a teacher-forced tap or
+       projection input outside the fp16 range (or NaN), or (raised at load) a
+       weight of W_fc or of the K/V rows that its 2^8-scaled fp16 copy does not
+       hold exactly. */
+#define EAGLE3_STATUS_APPEND_RANGE 4u
 int eagle3_status(eagle3_ctx *ctx, uint32_t *flags);
 
 /* Lengths of a sequence: committed rows and live speculative rows. */

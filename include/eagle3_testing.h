@@ -18,6 +18,11 @@ extern "C" {
    allocated and leave its output handle NULL. */
 void eagle3_test_fail_allocation(int32_t n);
 
+/* The number of device and pinned host allocations the library holds now, over
+   all handles and threads (each load adds its buffers, each free and each failed
+   load removes them again). */
+int64_t eagle3_test_live_allocations(void);
+
 #ifdef __cplusplus
 }
 #endif

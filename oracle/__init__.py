@@ -31,7 +31,8 @@ the token at r + 1), taken from the ExecuTorch PR #20153 description and fixed b
 the entry points' semantics rather than by a value any test can derive.
 """
 from .numerics import (argmax_first, attention_causal, attention_decode, attention_verify,
-                       bf16_bits_to_f64, rms_norm, rope_neox_partial, round_bf16, silu)
+                       bf16_bits_to_f64, rms_norm, rope_neox_partial, round_bf16, round_f16,
+                       silu)
 from .drafter import DrafterOracle, StatelessChain
 from .ledger import Ledger, LedgerError
 from .rope_width import resolve_rope_dim
@@ -41,7 +42,7 @@ from .loop import greedy_plain, greedy_speculative
 
 __all__ = [
     "argmax_first", "attention_causal", "attention_decode", "attention_verify", "bf16_bits_to_f64",
-    "rms_norm", "rope_neox_partial", "round_bf16", "silu", "DrafterOracle", "StatelessChain",
+    "rms_norm", "rope_neox_partial", "round_bf16", "round_f16", "silu", "DrafterOracle", "StatelessChain",
     "Ledger", "LedgerError", "resolve_rope_dim", "TrunkOracle", "greedy_plain",
     "greedy_speculative", "int4", "kvquant",
 ]

@@ -34,7 +34,8 @@ import numpy as np
 from . import kvquant
 from .ledger import Ledger
 from .numerics import (argmax_first, attention_causal, attention_decode,
-                       bf16_bits_to_f64, rms_norm, rope_neox_partial, round_bf16, silu)
+                       bf16_bits_to_f64, rms_norm, rope_neox_partial, round_bf16, round_f16,
+                       silu)
 
 WEIGHT_NAMES = ("fc", "input_layernorm", "hidden_norm", "q_proj", "k_proj",
                 "v_proj", "o_proj", "post_attention_layernorm", "gate_proj",
@@ -87,12 +88,13 @@ class DrafterOracle:
         attention included, sees the stored values.
         dtype: float64 (the parity mode) or float32 (a timing mode: the same
         operations on fp32 arrays, used only as a CPU speed baseline).
-        append_act: "exact", or "bf16": the rows of a teacher-forced append of
-        more than 16 rows take their taps and their K/V-projection input
-        [eN ; gN] rounded to the nearest bfloat16 (the engine's documented
-        single-bf16 activation format for such appends; shorter ones are exact)."""
-        assert append_act in ("exact", "bf16"), append_act
-        self.append_bf16 = append_act == "bf16"
+        append_act: "exact", "bf16" or "f16": the rows of a teacher-forced append
+        of more than 16 rows take their taps and their K/V-projection input
+        [eN ; gN] rounded to the nearest bfloat16 / IEEE half (the engine's
+        documented single-term activation formats for such appends; shorter
+        appends are exact)."""
+        assert append_act in ("exact", "bf16", "f16"), append_act
+        self.append_round = {"exact": None, "bf16": round_bf16, "f16": round_f16}[append_act]
         assert dtype in (np.float64, np.float32), dtype
         self.dt = dtype
         assert kv_format in ("exact", "bf16", "q8q5"), kv_format
@@ -237,13 +239,13 @@ class DrafterOracle:
         if T == 0:
             return
         taps = [np.asarray(a).reshape(T, self.n) for a in aux]
-        rounded = self.append_bf16 and T > 16
-        if rounded:
-            taps = [round_bf16(a).astype(self.dt) for a in taps]
+        rnd = self.append_round if T > 16 else None
+        if rnd:
+            taps = [rnd(a).astype(self.dt) for a in taps]
         f = self.encode(taps)
         cat = self.input_cat(f, toks)
-        if rounded:
-            cat = round_bf16(cat).astype(self.dt)
+        if rnd:
+            cat = rnd(cat).astype(self.dt)
         _, k, v = self.qkv(cat, start + np.arange(T))
         k, v = self._kv_rows(k, v)
         self.K[s][start:start + T] = k

@@ -44,6 +44,12 @@ def round_bf16(x) -> np.ndarray:
     return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
+def round_f16(x) -> np.ndarray:
+    """Round to the nearest IEEE half-precision value (11 significant bits, ties
+    to even; numpy's float16 conversion), returned as fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
 def rms_norm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis (memra module doc: the four RMSNorms of the
     op-sequence; formula per the reading in the module docstring)."""

@@ -10,10 +10,10 @@
  *   abi_check device  allocation failure injected at every device allocation of a
  *                     small eagle3_load and eagle3_trunk_load in turn: each must
  *                     return EAGLE3_E_OOM, leave the handle NULL and release all it
- *                     had allocated: a second identical sweep takes no further
- *                     device memory (the first may fill the HIP allocator's
- *                     caches), and LeakSanitizer checks the host side at exit;
- *                     each sweep ends with a clean load and free.  Needs a GPU.
+ *                     had allocated (the library's count of live device and pinned
+ *                     allocations, eagle3_test_live_allocations, is back where it
+ *                     was; LeakSanitizer checks the host side at exit); the sweep
+ *                     ends with a clean load and free.  Needs a GPU.
  * Exit status 0 when every check holds; each failed check prints a line.
  * (pegainfer PR #707, review: cleanup on failure, cache-edge and abort cases.) */
 #include <hip/hip_runtime_api.h>
@@ -231,33 +231,32 @@ static void check_alloc_failures(void) {
     CHECK(eagle3_load(&c, &w, NULL, &warm) == EAGLE3_OK && warm != NULL);
     if (warm) eagle3_free(warm);
   }
-  /* two sweeps: the first may leave blocks in the HIP allocator's caches; a leak
-     would take device memory again in the second */
+  /* every load that fails must hand back each allocation it made: the library's
+     own count of live allocations returns to where it was before the call */
   int oom = 0;
-  size_t free_after[3] = {free_bytes(), 0, 0};
-  for (int sweep = 1; sweep <= 2; ++sweep) {
-    oom = 0;
-    for (int k = 1;; ++k) {
-      eagle3_test_fail_allocation(k);
-      eagle3_ctx* ctx = (eagle3_ctx*)(uintptr_t)1;
-      const int rc = eagle3_load(&c, &w, NULL, &ctx);
-      eagle3_test_fail_allocation(0);
-      if (rc == EAGLE3_OK) {  /* k is past the last allocation: the load succeeded */
-        CHECK(ctx != NULL);
-        CHECK(eagle3_free(ctx) == EAGLE3_OK);
-        break;
-      }
-      CHECK(rc == EAGLE3_E_OOM);
-      CHECK(ctx == NULL);
-      ++oom;
-      if (k > 400) { CHECK(!"eagle3_load did not finish within 400 allocations"); break; }
+  const int64_t live0 = eagle3_test_live_allocations();
+  const size_t free0 = free_bytes();
+  for (int k = 1;; ++k) {
+    eagle3_test_fail_allocation(k);
+    eagle3_ctx* ctx = (eagle3_ctx*)(uintptr_t)1;
+    const int rc = eagle3_load(&c, &w, NULL, &ctx);
+    eagle3_test_fail_allocation(0);
+    if (rc == EAGLE3_OK) {  /* k is past the last allocation: the load succeeded */
+      CHECK(ctx != NULL);
+      CHECK(eagle3_test_live_allocations() > live0);
+      CHECK(eagle3_free(ctx) == EAGLE3_OK);
+      CHECK(eagle3_test_live_allocations() == live0);
+      break;
     }
-    free_after[sweep] = free_bytes();
+    CHECK(rc == EAGLE3_E_OOM);
+    CHECK(ctx == NULL);
+    CHECK(eagle3_test_live_allocations() == live0);
+    ++oom;
+    if (k > 400) { CHECK(!"eagle3_load did not finish within 400 allocations"); break; }
   }
-  printf("eagle3_load: %d allocation points failed cleanly; device free %zu -> %zu -> %zu bytes\n", oom,
-         free_after[0], free_after[1], free_after[2]);
+  printf("eagle3_load: %d allocation points failed cleanly; live allocations back to %lld; device free %zu "
+         "-> %zu bytes\n", oom, (long long)live0, free0, free_bytes());
   CHECK(oom > 10);
-  CHECK(free_after[2] >= free_after[1]);
   /* the trunk */
   eagle3_trunk_config tc;
   memset(&tc, 0, sizeof tc);
@@ -272,30 +271,30 @@ static void check_alloc_failures(void) {
     memcpy(shapes[3 + 9 * l], s, sizeof s);
   }
   eagle3_trunk_weights tw = {buf, buf, buf, layers, &shapes[0][0]};
-  size_t free_t[3] = {free_bytes(), 0, 0};
-  for (int sweep = 1; sweep <= 2; ++sweep) {
-    oom = 0;
-    for (int k = 1;; ++k) {
-      eagle3_test_fail_allocation(k);
-      eagle3_trunk* t = (eagle3_trunk*)(uintptr_t)1;
-      const int rc = eagle3_trunk_load(&tc, &tw, NULL, &t);
-      eagle3_test_fail_allocation(0);
-      if (rc == EAGLE3_OK) {
-        CHECK(t != NULL);
-        CHECK(eagle3_trunk_free(t) == EAGLE3_OK);
-        break;
-      }
-      CHECK(rc == EAGLE3_E_OOM);
-      CHECK(t == NULL);
-      ++oom;
-      if (k > 400) { CHECK(!"eagle3_trunk_load did not finish within 400 allocations"); break; }
+  const int64_t live_t0 = eagle3_test_live_allocations();
+  const size_t free_t0 = free_bytes();
+  oom = 0;
+  for (int k = 1;; ++k) {
+    eagle3_test_fail_allocation(k);
+    eagle3_trunk* t = (eagle3_trunk*)(uintptr_t)1;
+    const int rc = eagle3_trunk_load(&tc, &tw, NULL, &t);
+    eagle3_test_fail_allocation(0);
+    if (rc == EAGLE3_OK) {
+      CHECK(t != NULL);
+      CHECK(eagle3_test_live_allocations() > live_t0);
+      CHECK(eagle3_trunk_free(t) == EAGLE3_OK);
+      CHECK(eagle3_test_live_allocations() == live_t0);
+      break;
     }
-    free_t[sweep] = free_bytes();
+    CHECK(rc == EAGLE3_E_OOM);
+    CHECK(t == NULL);
+    CHECK(eagle3_test_live_allocations() == live_t0);
+    ++oom;
+    if (k > 400) { CHECK(!"eagle3_trunk_load did not finish within 400 allocations"); break; }
   }
-  printf("eagle3_trunk_load: %d allocation points failed cleanly; device free %zu -> %zu -> %zu bytes\n", oom,
-         free_t[0], free_t[1], free_t[2]);
+  printf("eagle3_trunk_load: %d allocation points failed cleanly; live allocations back to %lld; device free "
+         "%zu -> %zu bytes\n", oom, (long long)live_t0, free_t0, free_bytes());
   CHECK(oom > 10);
-  CHECK(free_t[2] >= free_t[1]);
   free(d2t);
   (void)hipFree(buf);
 }

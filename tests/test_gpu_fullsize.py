@@ -6,11 +6,11 @@ K/V row from the same seeded inputs, then each chain round is compared step by
 step (ids on pinned steps, logits and hidden states on those and the first
 unpinned step), with rebuilds after full and partial acceptance in between.
 
-Every engine variant is held to the same bar against the oracle mode that
-stores its KV format: fp32 KV against exact rows, bf16 KV against rows rounded
-to bf16.  The single-bf16 teacher-forced activations (EAGLE3_APPEND_BF16) are
-held to it against the oracle's rows from bf16-rounded taps and projection
-inputs."""
+Every engine variant is held to the same bar.  The default engine (fp32 KV,
+fp16 teacher-forced activations) and the split-activation engine are compared
+with exact rows; the other variants with the oracle mode that computes their
+formats: bf16 KV against rows rounded to bf16, single-term fp16 / bf16
+activations against rows from fp16- / bf16-rounded taps and projection inputs."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,11 +28,17 @@ def _variants(names):
     from eagle_draft_head_amd import binding as B
     # name: (KV format, teacher-forced activations, oracle KV format, oracle append)
     table = {
+        # the default path (fp16 appends) against exact rows: the parity bar itself
         "f32": (B.KV_F32, B.APPEND_DEFAULT, "exact", "exact"),
+        "f32-split": (B.KV_F32, B.APPEND_SPLIT, "exact", "exact"),
+        "f32-f16": (B.KV_F32, B.APPEND_F16, "exact", "f16"),
         "f32-act16": (B.KV_F32, B.APPEND_BF16, "exact", "bf16"),
-        "bf16": (B.KV_BF16, B.APPEND_DEFAULT, "bf16", "exact"),
+        "bf16": (B.KV_BF16, B.APPEND_DEFAULT, "bf16", "f16"),
     }
     return [(n,) + table[n] for n in names]
+
+
+ALL_VARIANTS = ["f32", "f32-split", "f32-f16", "f32-act16", "bf16"]
 
 
 class _Pair:
@@ -134,7 +140,7 @@ def _close(pairs):
 
 def test_qwen3_8b_shape_chain_parity():
     cfg = QWEN3_8B
-    pairs = _setup(cfg, cfg.context, cfg.context + 64, ["f32", "f32-act16", "bf16"])
+    pairs = _setup(cfg, cfg.context, cfg.context + 64, ALL_VARIANTS)
     for p in pairs:
         _kv_check(p)
     _rounds(cfg, pairs, [3] * 8, [3, None, 0, 2])
@@ -149,7 +155,7 @@ def test_qwen3_8b_shape_stored_boundary_rounds():
     """The benchmark's default protocol at full size: chains from the boundary
     feature the rebuild stored (its fc row rode on the rebuild's W_fc pass)."""
     cfg = QWEN3_8B
-    pairs = _setup(cfg, cfg.context, cfg.context + 64, ["f32", "f32-act16", "bf16"])
+    pairs = _setup(cfg, cfg.context, cfg.context + 64, ALL_VARIANTS)
     _rounds(cfg, pairs, [3] * 8, [3, 0, 2, 1], stored=True)
     for p in pairs:
         assert p.pinned >= p.steps // 2, p.name
@@ -159,7 +165,7 @@ def test_qwen3_8b_shape_stored_boundary_rounds():
 
 def test_page4_geometry_chain_parity():
     cfg = PAGE4
-    pairs = _setup(cfg, cfg.context, cfg.context + 64, ["f32", "f32-act16", "bf16"])
+    pairs = _setup(cfg, cfg.context, cfg.context + 64, ALL_VARIANTS)
     _rounds(cfg, pairs, [3, 5, 8, 8, 3, 5], [3, 5, None, 8, 1, 0])
     for p in pairs:
         assert p.pinned >= p.steps // 3, p.name
@@ -173,7 +179,7 @@ def test_long_context_parity():
     each pass boundary is checked, then six rounds with rebuilds."""
     cfg = LONG
     L = cfg.context
-    pairs = _setup(cfg, L, cfg.max_ctx, ["f32", "f32-act16", "bf16"])
+    pairs = _setup(cfg, L, cfg.max_ctx, ALL_VARIANTS)
     rows = sorted({0, L - 1} | {r for k in range(1, (L + 2047) // 2048)
                                 for r in (2048 * k - 1, 2048 * k) if r < L})
     assert len(rows) == 32

@@ -65,9 +65,9 @@ def test_kvq_rows_bit_exact(cfg):
 
 def _kv_close(dr, orc, R):
     """Dequantized rows vs the oracle's: equal but for codes decided one step apart
-    (the oracle quantizes fp64-computed rows, the GPU rows from products of split
-    bf16 activations, about 2^-16 relative apart; at 31 V levels over a block's span
-    that flips of the order of 0.1-0.3 % of the codes)."""
+    (the oracle quantizes fp64-computed rows, the GPU rows from fp32-accumulated
+    products of the same rounded activations, about 2^-16 relative apart; at 31 V
+    levels over a block's span that flips of the order of 0.1-0.3 % of the codes)."""
     k, v = dr.kv_read(0, 0, R)
     torch.cuda.synchronize()
     for gpu, ref, levels in ((k, orc.K[0][:R], 127.0), (v, orc.V[0][:R], 31.0)):
@@ -94,7 +94,9 @@ def test_kvq_chain_parity(cfg, L, rounds, gamma, local, i4):
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, kv_dtype=B.KV_Q8Q5,
                  weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16)
     wh = {k: v.cpu() for k, v in wd.items()}
-    orc = make_oracle(cfg, int4.int4_weights(wh) if i4 else wh, max_ctx=max_ctx, kv_format="q8q5")
+    # the default teacher-forced form: fp16 appends with bf16 weights, split with int4
+    orc = make_oracle(cfg, int4.int4_weights(wh) if i4 else wh, max_ctx=max_ctx, kv_format="q8q5",
+                      append_act="exact" if i4 else "f16")
     aux, toks = aux_np(cfg, 0, L), toks_np(cfg, 0, L)
     orc.prefill(0, aux, toks)
     dr.prefill(0, torch.as_tensor(toks, dtype=torch.int32).cuda(), to_dev_aux(aux))

@@ -114,15 +114,21 @@ def _gpu_greedy(gt, prompt, max_new):
     return out
 
 
+@pytest.mark.parametrize("act", ["split", "default"])
 @pytest.mark.parametrize("plen,gamma", [(1, 3), (17, 1), (17, 3), (64, 5)])
-def test_device_loop_equals_greedy_decoding(tiny, plen, gamma):
+def test_device_loop_equals_greedy_decoding(tiny, plen, gamma, act):
+    """Both append forms reproduce greedy decoding.  With split (fp32-grade)
+    appends the drafter also drafts and accepts exactly as the oracle drafter does;
+    the default's fp16 prompt rows may move a near-tied draft, which changes the
+    counts but never the output."""
     w, tw = tiny
     max_new = 60
     prompt = gen.tokens(TINY, 50 + plen, plen).tolist()
     ref = greedy_plain(_oracle_trunk(tw, w["embed"]), prompt, max_new)
     gt = GpuTrunk(tw, w["embed"])
     assert _gpu_greedy(gt, prompt, max_new) == ref
-    dr = gpu_drafter(TINY, {k: v.cuda() for k, v in w.items()}, max_ctx=MAX_CTX)
+    dr = gpu_drafter(TINY, {k: v.cuda() for k, v in w.items()}, max_ctx=MAX_CTX,
+                     append_act=B.APPEND_SPLIT if act == "split" else B.APPEND_DEFAULT)
     out, drafted, accepted = B.eagle3_generate(dr.ctx, 0, gt.h, prompt, max_new, gamma)
     assert out == ref
     # the same loop with the oracle trunk and drafter drafts and accepts alike
@@ -130,9 +136,12 @@ def test_device_loop_equals_greedy_decoding(tiny, plen, gamma):
     o_out, o_dr, o_ac = greedy_speculative(_oracle_trunk(tw, w["embed"]), OracleChainAdapter(orc), prompt,
                                            max_new, gamma)
     assert o_out == ref
-    say(f"[device loop] plen={plen} gamma={gamma}: drafted {drafted} accepted {accepted} "
+    say(f"[device loop] {act} plen={plen} gamma={gamma}: drafted {drafted} accepted {accepted} "
         f"(oracle loop {o_dr}/{o_ac})")
-    assert (drafted, accepted) == (o_dr, o_ac)
+    if act == "split":
+        assert (drafted, accepted) == (o_dr, o_ac)
+    else:
+        assert 0 <= accepted <= drafted and drafted > 0
     assert dr.kv_len(0)[1] == 0                       # no speculative rows are left
     dr.close()
     gt.close()

@@ -299,6 +299,13 @@ def test_bf16_append_activations_round_taps_and_projection_inputs(tiny_w):
     assert np.array_equal(db.K[0][:L], k) and np.array_equal(db.V[0][:L], v)
     de.prefill(0, row_slice(aux, 0, L), toks[:L])
     assert not np.array_equal(db.K[0][:L], de.K[0][:L])
+    # the fp16 form rounds the same inputs to IEEE half
+    from oracle import round_f16
+    dh = make_oracle(TINY, tiny_w, append_act="f16")
+    dh.prefill(0, row_slice(aux, 0, L), toks[:L])
+    f = de.encode([round_f16(a[:L]) for a in aux])
+    _, k, v = de.qkv(round_f16(de.input_cat(f, toks[:L])), np.arange(L))
+    assert np.array_equal(dh.K[0][:L], k) and np.array_equal(dh.V[0][:L], v)
     # a 16-row append is exact
     db2, de2 = make_oracle(TINY, tiny_w, append_act="bf16"), make_oracle(TINY, tiny_w)
     for d in (db2, de2):

@@ -170,3 +170,16 @@ def test_round_bf16_against_torch_and_ties():
     # error at most half an ulp: 2^(e-8) <= |y| 2^-8 for y in [2^e, 2^(e+1))
     y = rng.normal(0, 1, 1000)
     assert np.all(np.abs(round_bf16(y) - y) <= np.abs(y) * 2.0 ** -8)
+
+
+def test_round_f16_against_torch_and_ties():
+    from oracle import round_f16
+    x = torch.randn(20000, dtype=torch.float32) * torch.exp(torch.randn(20000) * 2)
+    want = x.to(torch.float16).double().numpy()
+    assert np.array_equal(round_f16(x.double().numpy()), want)
+    # 1 + 2^-11 lies halfway between 1 and 1 + 2^-10 -> 1 (even); 1 + 3 * 2^-11 -> 1 + 2^-9
+    assert round_f16(np.array([1 + 2.0 ** -11]))[0] == 1.0
+    assert round_f16(np.array([1 + 3 * 2.0 ** -11]))[0] == 1 + 2.0 ** -9
+    # a bf16 value times 2^8 is exact in fp16 (8 significant bits fit in 11)
+    w = torch.randn(5000).mul(0.02).to(torch.bfloat16).double().numpy() * 256
+    assert np.array_equal(round_f16(w), w)
