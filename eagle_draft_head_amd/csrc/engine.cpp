@@ -487,7 +487,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->kv_local, size_t(cfg->max_seqs) * c->kv_local_elems * c->kv_esize));
   E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
 
-  c->tf_rows = c->cap < 2048 ? c->cap : 2048;
+  // 4096-row passes: at the 5120-wide drafter W_fc's 256 x 320 output tiles then
+  // number 256, one per CU, with no K split
+  c->tf_rows = c->cap < 4096 ? c->cap : 4096;
   {  // small appends use split-K GEMV partials [splits][16][N]; large ones [splits][T][N]
     const size_t f_small = size_t(16) * n * size_t((3 * n + 511) / 512);
     const size_t p_small = size_t(16) * 2 * kvd * size_t((2 * n + 511) / 512);

@@ -873,8 +873,8 @@ GemmPlan gemm_plan(int M, int N, int K) {
   // up to 4 splits for long appends, up to 16 for short ones (<= 256 rows), whose
   // few tiles would leave most CUs idle and whose partials are small next to the
   // weights they stream.  The 320-wide tile exists for widths that 256 tiles
-  // cover in a count just past a multiple of 256 (5120 columns at 2048 rows:
-  // 160 tiles of 256, but 128 of 320, two K halves filling every CU once).
+  // cover in a count just past a multiple of 256 (5120 columns at 4096 rows: 320
+  // tiles of 256, but 256 of 320, filling every CU once with no K split).
   const int bm = gemm_bm(M);
   const int max_sp = M <= 256 ? 16 : 4;
   if (bm == 32) {
@@ -901,7 +901,7 @@ GemmPlan gemm_plan(int M, int N, int K) {
     for (int sp = 1; sp <= max_sp; sp *= 2) {
       if (K % (kBKPlain * sp) != 0) continue;
       const double cost = double((tiles * sp + 255) / 256) * bn / sp;
-      if (cost < best_cost * (1 - 1e-9)) {
+      if (cost < best_cost * (1 - 1e-9) || (cost < best_cost * (1 + 1e-9) && sp < best.splits)) {
         best_cost = cost;
         best = GemmPlan{bn, sp};
       }

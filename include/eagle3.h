@@ -91,7 +91,7 @@ typedef struct {
 #define EAGLE3_KV_BF16 1
 
 /* Activations of the teacher-forced (prefill / rebuild) MFMA passes of more than
-   16 rows (the rows of one call, its boundary rows included, up to 2048 rows per
+   16 rows (the rows of one call, its boundary rows included, up to 4096 rows per
    pass), whose weights are exact in bf16.  Passes of at most 16 rows stream the
    weights through fp32 GEMVs in every mode.
    EAGLE3_APPEND_DEFAULT: EAGLE3_APPEND_F16 with bf16 weights, EAGLE3_APPEND_SPLIT

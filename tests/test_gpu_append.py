@@ -64,10 +64,10 @@ def test_prefill_pieces_of_every_width(cfg, act):
 
 @pytest.mark.parametrize("act", ["split", "f16"])
 def test_prefill_longer_than_one_pass(act):
-    # the engine appends at most 2048 rows per pass; 2500 rows take two passes
+    # the engine appends at most 4096 rows per pass; 4500 rows take two passes
     cfg = TINY
     wd, wh = weights_both(cfg)
-    L = 2500
+    L = 4500
     dr = _drafter(cfg, wd, L + 8, act)
     aux, toks = aux_np(cfg, 8, L), toks_np(cfg, 8, L)
     dr.prefill(0, _tok(toks), to_dev_aux(aux))
@@ -75,7 +75,7 @@ def test_prefill_longer_than_one_pass(act):
     orc = make_oracle(cfg, wh, max_ctx=L + 8, append_act=ACTS[act][1])
     orc.prefill(0, aux, toks)
     # rows on both sides of the pass boundary, and everything else in bulk
-    for r in [0, 1, 1000, 2047, 2048, 2049, 2499]:
+    for r in [0, 1, 2000, 4095, 4096, 4097, 4499]:
         assert _rel_rows(k[r:r + 1], orc.K[0][r:r + 1]) < ROW_TOL
         assert _rel_rows(v[r:r + 1], orc.V[0][r:r + 1]) < ROW_TOL
     assert _rel_rows(k, orc.K[0][:L]) < ROW_TOL and _rel_rows(v, orc.V[0][:L]) < ROW_TOL

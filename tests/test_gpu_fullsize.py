@@ -174,15 +174,15 @@ def test_page4_geometry_chain_parity():
 
 
 def test_long_context_parity():
-    """5120-wide drafter with a 32767-row prefill (2048-row passes) and chains
+    """5120-wide drafter with a 32767-row prefill (4096-row passes) and chains
     whose attention splits across the whole cache: every row on both sides of
     each pass boundary is checked, then six rounds with rebuilds."""
     cfg = LONG
     L = cfg.context
     pairs = _setup(cfg, L, cfg.max_ctx, ALL_VARIANTS)
-    rows = sorted({0, L - 1} | {r for k in range(1, (L + 2047) // 2048)
-                                for r in (2048 * k - 1, 2048 * k) if r < L})
-    assert len(rows) == 32
+    rows = sorted({0, L - 1} | {r for k in range(1, (L + 4095) // 4096)
+                                for r in (4096 * k - 1, 4096 * k, 4096 * k + 1) if r < L})
+    assert len(rows) == 23
     for p in pairs:
         _kv_check(p, rows)
     _rounds(cfg, pairs, [3] * 6, [2, None, 3, 0, 1, 3])
