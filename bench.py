@@ -173,6 +173,10 @@ def main():
                          "chain encodes the boundary taps itself and every round is rewound to "
                          "the workload's length (the default for page4, whose rounds are rewound; "
                          "stored elsewhere)")
+    ap.add_argument("--graph-ab", action="store_true",
+                    help="launch-overhead A/B: one chain round (boundary taps, rewound, so every round "
+                         "runs at the same position) issued eagerly vs replayed from a captured HIP "
+                         "graph of 1 and of 10 rounds; also the host time to issue one round")
     ap.add_argument("--verify-attn", action="store_true",
                     help="time eagle3_verify_attention alone: the workload's KV heads over its "
                          "context plus a gamma+1-row window, against gamma+1 single-row calls")
@@ -195,6 +199,8 @@ def main():
     cfg = ALL[args.workload]
     if args.verify_attn:
         return run_verify_attn(args, cfg)
+    if args.graph_ab:
+        return run_graph_ab(args, cfg)
     if cfg.max_seqs > 1:
         return run_batched(args, cfg)
     gamma = args.gamma or cfg.gamma
@@ -430,6 +436,81 @@ def batched_kernel_bytes(cfg, kernel: str, lens, gamma: int, kv_bytes: int = 4) 
     act = {"lm_head": (dv, n), "gate_up": (2 * ff, n), "qkv": (qd + 2 * kvd, 2 * n),
            "down": (n, ff), "o_proj": (n, qd)}[kernel]
     return 2.0 * act[0] * act[1] + m * 4 * act[1]
+
+
+def run_graph_ab(args, cfg):
+    """Eager launches vs HIP graph replay of one chain round.  The round starts from
+    the boundary taps at the workload's committed length and is rewound afterwards,
+    so every round writes the same KV rows and a replay of its captured kernels
+    repeats it exactly.  Every replay is checked against the eager ids, with eager
+    rounds and synchronisations between replays."""
+    import torch
+
+    from eagle_draft_head_amd.drafter import Drafter
+    from synth import gen
+
+    gamma = args.gamma or cfg.gamma
+    L = cfg.context
+    torch.cuda.set_device(0)
+    wd = gen.drafter_weights(cfg, device="cuda")
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=L + gamma + 64, max_gamma=max(8, gamma))
+    dr.prefill(0, gen.tokens(cfg, 0, L, device="cuda"), gen.aux_taps(cfg, 0, L, device="cuda"))
+    b_aux = [a.contiguous() for a in gen.aux_taps(cfg, 1, 1, device="cuda")]
+    b_tok = gen.tokens(cfg, 1, 1, device="cuda")
+    out = torch.empty((1, gamma), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    N = max(args.steps, 10) // 10 * 10
+
+    def chain(o=out):
+        dr.draft_chain([0], b_tok, b_aux, gamma, out=o, stream=torch.cuda.current_stream())
+
+    def events(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    with torch.cuda.stream(side):
+        for _ in range(args.warmup):
+            chain()
+        torch.cuda.synchronize()
+        ref = out.clone()
+        eager_us = events(chain, N) / N
+        t0 = time.perf_counter()
+        for _ in range(N):
+            chain()
+        issue_us = (time.perf_counter() - t0) * 1e6 / N
+        torch.cuda.synchronize()
+    res = {"eager_us": round(eager_us, 2), "host_issue_us": round(issue_us, 2)}
+    other = torch.empty_like(out)
+    ok = True
+    for per in (1, 10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per):
+                chain()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            out.fill_(-7)
+            with torch.cuda.stream(side):
+                chain(other)                      # eager work between the replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ok = ok and torch.equal(out, ref) and torch.equal(other, ref)
+        res[f"graph{per}_us"] = round(events(g.replay, N // per) / N, 2)
+        del g
+    dr.close()
+    print(json.dumps({
+        "metric": "chain round time: eager launches vs HIP graph replay", "unit": "us per round",
+        "value": res["graph1_us"], "higher_is_better": False, "n_gpus": 1, "steps": N,
+        "warmup": args.warmup, "replays_equal_eager": bool(ok), **res,
+        "config": {"workload": f"{cfg.name}: one gamma={gamma} chain round from boundary taps over {L} "
+                               f"committed rows, rewound (every round at the same position)"}}),
+        flush=True)
 
 
 def run_verify_attn(args, cfg):
