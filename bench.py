@@ -173,6 +173,10 @@ def main():
                          "chain encodes the boundary taps itself and every round is rewound to "
                          "the workload's length (the default for page4, whose rounds are rewound; "
                          "stored elsewhere)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="reference only: the vendor GEMM (torch.mm, fp16 and bf16, contiguous operands) at "
+                         "the workload's prefill GEMM shapes (one append pass of up to 4096 rows), next to "
+                         "the MFMA calibration loop")
     ap.add_argument("--graph-ab", action="store_true",
                     help="launch-overhead A/B: one chain round (boundary taps, rewound, so every round "
                          "runs at the same position) issued eagerly vs replayed from a captured HIP "
@@ -201,6 +205,8 @@ def main():
         return run_verify_attn(args, cfg)
     if args.graph_ab:
         return run_graph_ab(args, cfg)
+    if args.vendor_gemm:
+        return run_vendor_gemm(args, cfg)
     if cfg.max_seqs > 1:
         return run_batched(args, cfg)
     gamma = args.gamma or cfg.gamma
@@ -436,6 +442,44 @@ def batched_kernel_bytes(cfg, kernel: str, lens, gamma: int, kv_bytes: int = 4) 
     act = {"lm_head": (dv, n), "gate_up": (2 * ff, n), "qkv": (qd + 2 * kvd, 2 * n),
            "down": (n, ff), "o_proj": (n, qd)}[kernel]
     return 2.0 * act[0] * act[1] + m * 4 * act[1]
+
+
+def run_vendor_gemm(args, cfg):
+    """What the vendor GEMM reaches at the prefill shapes: C = A . W^T for the fc
+    ([rows, 3n] x [3n, n]) and the K|V projection ([rows, 2n] x [2n, 2 kv_dim]) of
+    one append pass (rows = min(context, 4096)).  torch.mm dispatches to hipBLASLt;
+    the engine never calls it.  HIP events around `steps` calls after `warmup`."""
+    import torch
+
+    from eagle_draft_head_amd import binding as B
+
+    torch.cuda.set_device(0)
+    cal = calibrate(B, torch)
+    rows = min(cfg.context, 4096)
+    n, kvd = cfg.n_embd, cfg.kv_dim
+    shapes = {"fc": (rows, n, 3 * n), "kv": (rows, 2 * kvd, 2 * n)}
+    res = {}
+    for dt, tag in ((torch.float16, "fp16"), (torch.bfloat16, "bf16")):
+        for name, (M, N, K) in shapes.items():
+            a = torch.randn(M, K, device="cuda", dtype=dt)
+            bt = torch.randn(K, N, device="cuda", dtype=dt).contiguous()
+            for _ in range(args.warmup):
+                c = torch.mm(a, bt)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                c = torch.mm(a, bt)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps
+            res[f"{name}_{tag}"] = {"M": M, "N": N, "K": K, "us": round(us, 2),
+                                    "tflops": round(2.0 * M * N * K / us / 1e6, 1)}
+            del a, bt, c
+    print(json.dumps({"metric": "vendor GEMM TFLOP/s at the prefill shapes (reference)", "unit": "TFLOP/s",
+                      "value": res["fc_fp16"]["tflops"], "higher_is_better": True, "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "gemms": res, "calibrated": cal,
+                      "config": {"workload": f"{cfg.name}: one append pass of {rows} rows"}}), flush=True)
 
 
 def run_graph_ab(args, cfg):
