@@ -249,7 +249,10 @@ int eagle3_rebuild_after_verify(eagle3_ctx *ctx, int32_t n_seq, const int32_t *s
 
 /* Drop speculative rows and truncate the committed rows to new_len
    (abort / cleanup); the sequence's stored boundary feature is dropped too.
-   Requires 0 <= new_len <= committed.  Host bookkeeping only: no device work. */
+   Requires 0 <= new_len <= committed.  Host bookkeeping only: no device work.
+   (pegainfer PR #707, PR description: a chain round rewinds the speculative KV so
+   it has no side effects; memra_engine `eagle.rs`, `Eagle3Scratch`: the draft
+   cache length is reset rather than its rows cleared.) */
 int eagle3_rewind(eagle3_ctx *ctx, int32_t seq, int32_t new_len);
 
 /* Device-side input problems since the last call (a bit mask; the call
@@ -270,7 +273,9 @@ int eagle3_rewind(eagle3_ctx *ctx, int32_t seq, int32_t new_len);
 #define EAGLE3_STATUS_APPEND_RANGE 4u
 int eagle3_status(eagle3_ctx *ctx, uint32_t *flags);
 
-/* Lengths of a sequence: committed rows and live speculative rows. */
+/* Lengths of a sequence: committed rows and live speculative rows (the two
+   lengths the capacity rule of pegainfer PR #707, review, "start=97, k=3,
+   max=100", is stated in).  Host bookkeeping; no device work. */
 int eagle3_kv_len(const eagle3_ctx *ctx, int32_t seq, int32_t *committed, int32_t *spec);
 
 /* Copy draft-KV rows [row0, row0 + nrows) of a sequence into caller buffers
@@ -338,7 +343,11 @@ int eagle3_weights_i4_read(const eagle3_ctx *ctx, int32_t matrix, void *codes_de
                            void *scales_dev, void *stream);
 
 /* Message of the last failing call on this handle (or, with ctx NULL, of the
-   last failing eagle3_load or eagle3_verify_attention_noalloc on this thread). */
+   last failing eagle3_load or eagle3_verify_attention_noalloc on this thread).
+   The library's own error reporting (no passage of the pages defines it; it
+   answers pegainfer PR #707, review, which asks for clean failure paths).  The
+   string stays valid until the next failing call on the same handle (with NULL:
+   on the same thread) or until the handle is freed. */
 const char *eagle3_last_error(const eagle3_ctx *ctx);
 
 /* Timing of one kernel family with HIP events on the launching stream, for
