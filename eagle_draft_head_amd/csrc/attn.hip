@@ -24,6 +24,7 @@ namespace e3 {
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnMaxChunk = 512;
+constexpr int kAttnMfmaMaxChunk = 2048;  // the MFMA decode kernel's longest split
 // 256 rather than 512: a 4096-row context over 4 KV heads then splits 64 ways, and its
 // combine loads every split in one round trip (128 splits took two)
 constexpr int kAttnSingleBlocks = 256;
@@ -633,6 +634,215 @@ __global__ __launch_bounds__(256) void k_attn_mid_mfma(VerifyArgs a, int chunk, 
 }
 
 // ---------------------------------------------------------------------------
+// Decode attention over bf16 K/V on MFMA (head_dim 64 or 128, up to 16 query heads
+// per KV head).  Same grid, partials and batched form as k_attn.  The G query
+// vectors of the block's KV head are the 16 columns of an MFMA operand (unused
+// columns zero): per 16-row tile, S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (A = 16
+// K rows straight from memory, exact in bf16; B = the queries as bf16 (hi, lo)
+// pairs, two products), which leaves lane (query c16, group g4) holding the scores
+// of rows 4 g4 + v -- exactly the A operand of O += P V on v_mfma_f32_16x16x16bf16_1k
+// (rows = queries, k = the tile's rows), P entering as (hi, lo) pairs against exact
+// bf16 V.  V's B operand holds dim 16-column c16 over rows 4 g4 + v; a lane loads
+// 16 bytes (8 dims) of each of its 4 rows, so output tile k holds dims 8 c16 + k.
+// Tiles of a block go to its 4 waves round robin; each wave keeps the next
+// kMfmaRing tiles' loads in flight while it computes.  The online softmax keeps a
+// reference maximum per query that moves only when a tile's maximum passes it by
+// more than kRescale (weights stay below 2^kRescale), so O is rarely rescaled.
+typedef short bf16x4s_t __attribute__((ext_vector_type(4)));
+constexpr int kMfmaRing = 2;
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int S) {
+  constexpr int NT = HD / 16;               // output tiles of 16 dims
+  constexpr int KS = HD / 32;               // k steps of S
+  constexpr int VE = 8 < NT ? 8 : NT;       // bf16 elements per V load
+  constexpr int VD = 16 * VE;               // dims per group of output tiles
+  constexpr int NG = HD / VD;
+  constexpr int R = kMfmaRing;
+  constexpr int STRIDE = 16 * kAttnWaves;   // rows between a wave's consecutive tiles
+  static_assert(NT * 16 == HD && KS * 32 == HD && NG * VD == HD, "head_dim 64 or 128");
+  __shared__ float so[kAttnWaves][16][HD + 4];
+  __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
+
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int G = a.n_head / a.n_head_kv;
+  int T = a.T;
+  size_t kv_off = 0;
+  const float* qrow = a.q;
+  float* part_o = a.part_o;
+  float* part_ml = a.part_ml;
+  if (a.batched) {
+    const int rb = blockIdx.z;
+    T = a.br.row0[rb] + a.step + 1;
+    kv_off = (size_t)a.br.slot[rb] * a.seq_elems;
+    qrow += (size_t)rb * a.n_head * HD;
+    part_o += (size_t)rb * a.n_head * S * HD;
+    part_ml += (size_t)rb * a.n_head * S * 2;
+  }
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  if (r0 >= T) return;  // a split past this row's context (batched rows are ragged)
+  const bool direct = S == 1 && !a.batched;
+  const int rlast = r1 - 1;
+  const uint16_t* Kb = static_cast<const uint16_t*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD;
+  const uint16_t* Vb = static_cast<const uint16_t*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD;
+
+  // ring slot i: K rows tb + c16 (dims 32 ks + 8 g4 ..), V rows tb + 4 g4 + v (dims
+  // VD grp + VE c16 ..); row indices clamped to r1 - 1, masked when scored
+  uint4 kr[R][KS];
+  uint4 vr[R][NG][4];
+  auto load = [&](int i, int tb) {
+    const uint16_t* kp = Kb + (size_t)min(tb + c16, rlast) * HD + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[i][ks] = *reinterpret_cast<const uint4*>(kp + 32 * ks);
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint16_t* vp = Vb + (size_t)min(tb + 4 * g4 + v, rlast) * HD + VD * grp + VE * c16;
+        if constexpr (VE == 8) {
+          vr[i][grp][v] = *reinterpret_cast<const uint4*>(vp);
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(vp);
+          vr[i][grp][v] = make_uint4(w.x, w.y, 0u, 0u);
+        }
+      }
+  };
+  const int tb0 = r0 + 16 * wv;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tb0 + i * STRIDE < r1) load(i, tb0 + i * STRIDE);
+
+  // queries carry the base-2 score scale; columns past G are zero
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  const bool qok = c16 < G;
+  bf16x8_t qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float* qp = qrow + (size_t)(kvh * G + (qok ? c16 : 0)) * HD + 32 * ks + 8 * g4;
+    const float4 u = *reinterpret_cast<const float4*>(qp), w = *reinterpret_cast<const float4*>(qp + 4);
+    float x[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = qok ? x[e] * scale : 0.f;
+    split8(x, qh[ks], ql[ks]);
+  }
+  f32x4_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  auto step = [&](int i, int tb) {
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t kh = __builtin_bit_cast(bf16x8_t, kr[i][ks]);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
+    }
+    uint4 vv[NG][4];
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vv[grp][v] = vr[i][grp][v];
+    if (tb + R * STRIDE < r1) load(i, tb + R * STRIDE);
+    float sc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[v] = (tb + 4 * g4 + v < r1) ? st[v] : -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float fo = 1.f;
+    if (mx > m + kRescale) {
+      fo = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+      m = mx;
+    }
+    float pr[4], ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      pr[v] = sc[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[v] - m);
+      ps += pr[v];
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * fo + ps;
+    if (__any(fo != 1.f)) {  // O's D layout holds queries 4 g4 + v
+      float fv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) fv[v] = __shfl(fo, 4 * g4 + v, kWave);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[t][v] *= fv[v];
+    }
+    bf16x4s_t ph, pl;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const __bf16 h = (__bf16)pr[v];
+      ph[v] = __builtin_bit_cast(short, h);
+      pl[v] = __builtin_bit_cast(short, (__bf16)(pr[v] - (float)h));
+    }
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+      for (int k = 0; k < VE; ++k) {
+        bf16x4s_t vk;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 w = vv[grp][v];
+          const uint32_t word = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
+          vk[v] = (k & 1) ? short(word >> 16) : short(word & 0xffffu);
+        }
+        const int t = VE * grp + k;
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vk, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vk, o[t], 0, 0, 0);
+      }
+  };
+  int tb = tb0;
+  for (; tb + (R - 1) * STRIDE < r1; tb += R * STRIDE) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) step(i, tb + i * STRIDE);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tb + i * STRIDE < r1) step(i, tb + i * STRIDE);
+
+  // merge the waves
+  if (g4 == 0) {
+    sm[wv][c16] = m;
+    sl[wv][c16] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) so[wv][4 * g4 + v][VD * (t / VE) + VE * c16 + (t % VE)] = o[t][v];
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
+    const int q = i / HD, dd = i - q * HD;
+    float Mb = sm[0][q];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, sm[w][q]);
+    float v = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = (Mb == -INFINITY || sm[w][q] == -INFINITY) ? 0.f : exp2f(sm[w][q] - Mb);
+      v = fmaf(f, so[w][q][dd], v);
+      Ls = fmaf(f, sl[w][q], Ls);
+    }
+    const int h = kvh * G + q;
+    if (direct) {
+      a.out[(size_t)h * HD + dd] = v / Ls;
+    } else {
+      part_o[((size_t)h * S + s) * HD + dd] = v;
+      if (dd == 0) {
+        part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
+        part_ml[((size_t)h * S + s) * 2 + 1] = Ls;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_attn over quantized regions (q8_0 K, q5_1 V; layout in kernels.hpp).  A lane
 // holds 8 consecutive dims of a row, inside one block of 32: per row it loads 8 K
 // codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and its
@@ -979,10 +1189,32 @@ int attn_max_splits(int cap, int head_dim, int n_head_kv) {
   return (target > capped ? target : capped) + 1;
 }
 
+// EAGLE3_ATTN_VALU=1 keeps bf16 decode attention on the VALU kernel (for comparison)
+static bool attn_valu() {
+  static const bool v = [] {
+    const char* e = std::getenv("EAGLE3_ATTN_VALU");
+    return e && e[0] == '1';
+  }();
+  return v;
+}
+
+// bf16 K/V at head_dim <= 128 with at most 16 query heads per KV head run k_attn_mfma
+static bool attn_on_mfma(int hd, int kv_f32, int G) { return !kv_f32 && hd <= 128 && G <= 16 && !attn_valu(); }
+
 template <int HD, typename KT>
 static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStream_t s,
                             int rows = 1) {
   dim3 grid(S, a.n_head_kv, rows), block(64 * kAttnWaves);
+  if constexpr (sizeof(KT) == 2 && HD <= 128) {
+    if (attn_on_mfma(HD, 0, G)) {
+      hipLaunchKernelGGL((k_attn_mfma<HD>), grid, block, 0, s, a, chunk, S);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || S == 1 || a.batched) return e;
+      hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S, HD,
+                         a.out);
+      return hipGetLastError();
+    }
+  }
 #define E3_ATTN_CASE(GG)                                                        \
   case GG:                                                                    \
     hipLaunchKernelGGL((k_attn<HD, GG, KT>), grid, block, 0, s, a, chunk, S); \
@@ -1023,7 +1255,9 @@ static hipError_t launch_kt(const AttnArgs& a, int G, int chunk, int S, hipStrea
 constexpr int kAttnBatchMinChunk = 128;
 
 // (row, head, split) blocks aimed at per batched launch; EAGLE3_ATTN_BATCH_BLOCKS
-// overrides it (at least 256) for tuning
+// overrides it (at least 256) for tuning.  The MFMA kernel keeps this rule: with 32
+// rows x 8 KV heads already in the grid, longer chunks measured slower (batched32,
+// bf16 K/V: 118 us a step at 2048 blocks, 151 at 1024)
 static int attn_batch_target() {
   static const int t = [] {
     const char* e = std::getenv("EAGLE3_ATTN_BATCH_BLOCKS");
@@ -1196,11 +1430,29 @@ hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipSt
   }
 }
 
+// Splits of the MFMA decode kernel: about kAttnSingleBlocks (KV head, split) blocks,
+// chunks of whole 16-row tiles per wave (64 rows), at most kAttnMfmaMaxChunk rows;
+// longer chunks than the VALU kernel's, since a block's fixed work (queries, merge)
+// is larger (at 32K rows over 8 KV heads: 1024-row chunks 23.7 us, 512 27.8, 256 35.2)
+
+static void pick_split_mfma(int T, int n_head_kv, int* chunk, int* S) {
+  const int blocks = attn_single_blocks();
+  const int target = n_head_kv >= blocks ? 1 : blocks / n_head_kv;
+  constexpr int rpb = 16 * kAttnWaves;
+  int c = (T + target - 1) / target;
+  c = ((c + rpb - 1) / rpb) * rpb;
+  if (c < rpb) c = rpb;
+  if (c > kAttnMfmaMaxChunk) c = kAttnMfmaMaxChunk;
+  *chunk = c;
+  *S = (T + c - 1) / c;
+}
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batched) return hipErrorInvalidValue;
   int chunk, S;
-  pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   const int G = a.n_head / a.n_head_kv;
+  if (!a.kv_q && attn_on_mfma(a.head_dim, a.kv_f32, G)) pick_split_mfma(a.T, a.n_head_kv, &chunk, &S);
+  else pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   if (a.kv_q) {
     switch (a.head_dim) {
       case 64: return launch_q_hd<64>(a, G, chunk, S, s);

@@ -20,17 +20,19 @@ def _tok(x):
     return torch.as_tensor(np.asarray(x), dtype=torch.int32).reshape(-1).cuda()
 
 
-def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None, stored=False):
+def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None, stored=False, kv_bf16=False):
     """stored: every round starts from the boundary feature stored by the prefill
     or the previous rebuild (given the round's boundary taps as next taps), and
-    every round is followed by a rebuild."""
-    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds} stored={stored}")
+    every round is followed by a rebuild.  kv_bf16: the bf16 draft-KV option,
+    against the oracle storing bf16-rounded rows computed from the same fp16-rounded
+    append inputs as the engine's default append form."""
+    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds} stored={stored} bf16={kv_bf16}")
     if stored:
         rebuild_every = 1
     wd, wh = weights_both(cfg)
     max_ctx = max_ctx or (L + rounds * (gamma + 1) + gamma + 8)
-    dr = gpu_drafter(cfg, wd, max_ctx=max_ctx)
-    orc = make_oracle(cfg, wh, max_ctx=max_ctx)
+    dr = gpu_drafter(cfg, wd, max_ctx=max_ctx, kv_dtype=B.KV_BF16 if kv_bf16 else B.KV_F32)
+    orc = make_oracle(cfg, wh, max_ctx=max_ctx, **(dict(kv_format="bf16", append_act="f16") if kv_bf16 else {}))
     aux = aux_np(cfg, 0, L)
     toks = toks_np(cfg, 0, L)
     baux = aux_np(cfg, 1, rounds + 1)
@@ -93,6 +95,16 @@ def test_ragged_shape_chain_parity():
 def test_chain_from_empty_cache():
     pinned, steps = _run_rounds(TINY, rounds=10, L=0, gamma=5)
     assert steps == 50
+
+
+@pytest.mark.parametrize("cfg,L,gamma,rounds", [(TINY, 63, 3, 40), (small_variant(), 300, 4, 16),
+                                                (TINY, 0, 5, 6), (TINY, 1500, 3, 8)],
+                         ids=["tiny", "ragged", "empty", "long"])
+def test_bf16_kv_chain_parity(cfg, L, gamma, rounds):
+    """bf16 K/V: the decode attention runs on MFMA (head_dim 64 here) with ragged
+    tiles, one split and many; held to the standard bar."""
+    pinned, steps = _run_rounds(cfg, rounds=rounds, L=L, gamma=gamma, rebuild_every=3, kv_bf16=True)
+    assert pinned >= 0.25 * steps
 
 
 def test_stored_boundary_rounds_tiny():
