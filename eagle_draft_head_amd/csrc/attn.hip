@@ -843,6 +843,232 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int
 }
 
 // ---------------------------------------------------------------------------
+// Verify-window attention in k_attn_mfma's form: 16-row tiles, each wave keeping
+// its next kMfmaRing tiles' loads in flight, S^T on 16x16x32 and O += P V on
+// 16x16x16, for the 16 query vectors of a query group (as k_attn_mid_mfma: vector
+// j = qg * 16 + c16 over (m, g), m-major; query row m sees rows 0 .. ctx + m).
+// fp32 K and V enter as bf16 (hi, lo) pairs (hi*hi + hi*lo + lo*hi summed, 2^-18
+// relative); bf16 K and V are exact and only the queries and P are split.
+template <int HD, typename KT>
+__global__ __launch_bounds__(256, 2) void k_attn_vr(VerifyArgs a, int chunk, int S, int QG) {
+  constexpr bool F32 = sizeof(KT) == 4;
+  constexpr int NT = HD / 16;
+  constexpr int KS = HD / 32;
+  constexpr int VE0 = 16 / int(sizeof(KT));  // elements per 16-byte V load
+  constexpr int VE = VE0 < NT ? VE0 : NT;
+  constexpr int VD = 16 * VE;
+  constexpr int NG = HD / VD;
+  constexpr int KV = F32 ? 2 : 1;            // 16-byte K loads per k step
+  constexpr int R = F32 ? 1 : kMfmaRing;     // fp32 tiles take twice the registers
+  constexpr int STRIDE = 16 * kAttnWaves;
+  static_assert(NT * 16 == HD && KS * 32 == HD && NG * VD == HD, "head_dim 64 or 128");
+  __shared__ float so[kAttnWaves][16][HD + 4];
+  __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
+
+  const int nkv = a.n_head_kv, G = a.n_head / nkv;
+  const int tiles = S * nkv;
+  const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+  const int tile = (slot / QG) * 8 + xcd, qg = slot % QG;
+  if (tile >= tiles) return;
+  const int s = tile % S, kvh = tile / S;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int T = a.ctx + a.M;
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  const int rlast = r1 - 1;
+  const KT* Kb = static_cast<const KT*>(a.k) + (size_t)kvh * a.cap * HD;
+  const KT* Vb = static_cast<const KT*>(a.v) + (size_t)kvh * a.cap * HD;
+
+  uint4 kr[R][KS][KV];
+  uint4 vr[R][NG][4];
+  auto load = [&](int i, int tb) {
+    const KT* kp = Kb + (size_t)min(tb + c16, rlast) * HD + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int h = 0; h < KV; ++h) kr[i][ks][h] = *reinterpret_cast<const uint4*>(kp + 32 * ks + 4 * h);
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const KT* vp = Vb + (size_t)min(tb + 4 * g4 + v, rlast) * HD + VD * grp + VE * c16;
+        if constexpr (VE * sizeof(KT) == 16) {
+          vr[i][grp][v] = *reinterpret_cast<const uint4*>(vp);
+        } else {  // 4 bf16 (head_dim 64)
+          const uint2 w = *reinterpret_cast<const uint2*>(vp);
+          vr[i][grp][v] = make_uint4(w.x, w.y, 0u, 0u);
+        }
+      }
+  };
+  const int tb0 = r0 + 16 * wv;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tb0 + i * STRIDE < r1) load(i, tb0 + i * STRIDE);
+
+  // this lane's query vector (S layout)
+  const int jq = qg * 16 + c16, mq = jq / G;
+  const bool qok = mq < a.M;
+  const int lim = qok ? a.ctx + mq : -1;
+  const int qrow = qok ? mq * a.n_head + kvh * G + (jq - mq * G) : 0;
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  bf16x8_t qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float* qp = a.q + (size_t)qrow * HD + 32 * ks + 8 * g4;
+    const float4 u = *reinterpret_cast<const float4*>(qp), w = *reinterpret_cast<const float4*>(qp + 4);
+    float x[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = qok ? x[e] * scale : 0.f;
+    split8(x, qh[ks], ql[ks]);
+  }
+  f32x4_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  auto step = [&](int i, int tb) {
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (F32) {
+        const uint4 u = kr[i][ks][0], w = kr[i][ks][1];
+        const float x[8] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                            __uint_as_float(u.w), __uint_as_float(w.x), __uint_as_float(w.y),
+                            __uint_as_float(w.z), __uint_as_float(w.w)};
+        bf16x8_t kh, kl;
+        split8(x, kh, kl);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[ks], st, 0, 0, 0);
+      } else {
+        const bf16x8_t kh = __builtin_bit_cast(bf16x8_t, kr[i][ks][0]);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
+      }
+    }
+    uint4 vv[NG][4];
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vv[grp][v] = vr[i][grp][v];
+    if (tb + R * STRIDE < r1) load(i, tb + R * STRIDE);
+    float sc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = tb + 4 * g4 + v;
+      sc[v] = (row < r1 && row <= lim) ? st[v] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float fo = 1.f;
+    if (mx > m + kRescale) {
+      fo = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+      m = mx;
+    }
+    float pr[4], ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      pr[v] = sc[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[v] - m);
+      ps += pr[v];
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * fo + ps;
+    if (__any(fo != 1.f)) {
+      float fv[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) fv[v] = __shfl(fo, 4 * g4 + v, kWave);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[t][v] *= fv[v];
+    }
+    bf16x4s_t ph, pl;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const __bf16 h = (__bf16)pr[v];
+      ph[v] = __builtin_bit_cast(short, h);
+      pl[v] = __builtin_bit_cast(short, (__bf16)(pr[v] - (float)h));
+    }
+#pragma unroll
+    for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+      for (int k = 0; k < VE; ++k) {
+        const int t = VE * grp + k;
+        if constexpr (F32) {
+          bf16x4s_t vh, vl;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint4 w = vv[grp][v];
+            const float x = __uint_as_float(k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w);
+            const __bf16 h = (__bf16)x;
+            vh[v] = __builtin_bit_cast(short, h);
+            vl[v] = __builtin_bit_cast(short, (__bf16)(x - (float)h));
+          }
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vh, o[t], 0, 0, 0);
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vl, o[t], 0, 0, 0);
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vh, o[t], 0, 0, 0);
+        } else {
+          bf16x4s_t vk;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint4 w = vv[grp][v];
+            const uint32_t word = k < 2 ? w.x : k < 4 ? w.y : k < 6 ? w.z : w.w;
+            vk[v] = (k & 1) ? short(word >> 16) : short(word & 0xffffu);
+          }
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vk, o[t], 0, 0, 0);
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vk, o[t], 0, 0, 0);
+        }
+      }
+  };
+  int tb = tb0;
+  for (; tb + (R - 1) * STRIDE < r1; tb += R * STRIDE) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) step(i, tb + i * STRIDE);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tb + i * STRIDE < r1) step(i, tb + i * STRIDE);
+
+  if (g4 == 0) {
+    sm[wv][c16] = m;
+    sl[wv][c16] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) so[wv][4 * g4 + v][VD * (t / VE) + VE * c16 + (t % VE)] = o[t][v];
+  __syncthreads();
+  const bool direct = S == 1;
+  for (int i = threadIdx.x; i < 16 * HD; i += blockDim.x) {
+    const int q = i / HD, dd = i - q * HD;
+    const int j = qg * 16 + q, mm = j / G;
+    if (mm >= a.M) continue;
+    const int qr = mm * a.n_head + kvh * G + (j - mm * G);
+    float Mb = sm[0][q];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, sm[w][q]);
+    float v = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = (Mb == -INFINITY || sm[w][q] == -INFINITY) ? 0.f : exp2f(sm[w][q] - Mb);
+      v = fmaf(f, so[w][q][dd], v);
+      Ls = fmaf(f, sl[w][q], Ls);
+    }
+    if (direct) {
+      a.out[(size_t)qr * HD + dd] = v / Ls;
+    } else {
+      a.part_o[((size_t)qr * S + s) * HD + dd] = v;
+      if (dd == 0) {
+        a.part_ml[((size_t)qr * S + s) * 2 + 0] = Mb;
+        a.part_ml[((size_t)qr * S + s) * 2 + 1] = Ls;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_attn over quantized regions (q8_0 K, q5_1 V; layout in kernels.hpp).  A lane
 // holds 8 consecutive dims of a row, inside one block of 32: per row it loads 8 K
 // codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and its
@@ -1180,6 +1406,23 @@ static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int
   *S = (T + c - 1) / c;
 }
 
+// Splits of the MFMA decode kernel: about kAttnSingleBlocks (KV head, split) blocks,
+// chunks of whole 16-row tiles per wave (64 rows), at most kAttnMfmaMaxChunk rows;
+// longer chunks than the VALU kernel's, since a block's fixed work (queries, merge)
+// is larger (at 32K rows over 8 KV heads: 1024-row chunks 23.7 us, 512 27.8, 256 35.2)
+
+static void pick_split_mfma(int T, int n_head_kv, int* chunk, int* S) {
+  const int blocks = attn_single_blocks();
+  const int target = n_head_kv >= blocks ? 1 : blocks / n_head_kv;
+  constexpr int rpb = 16 * kAttnWaves;
+  int c = (T + target - 1) / target;
+  c = ((c + rpb - 1) / rpb) * rpb;
+  if (c < rpb) c = rpb;
+  if (c > kAttnMfmaMaxChunk) c = kAttnMfmaMaxChunk;
+  *chunk = c;
+  *S = (T + c - 1) / c;
+}
+
 int attn_max_splits(int cap, int head_dim, int n_head_kv) {
   // S = ceil(T / chunk) never exceeds the target split count while chunks are
   // uncapped, nor ceil(T / kAttnMaxChunk) once they are capped
@@ -1371,8 +1614,19 @@ static int verify_blocks() {
 
 static bool verify_mfma(int hd) { return hd <= 128 && !verify_valu(); }
 
+// EAGLE3_VERIFY_TILE32=1 selects the earlier MFMA kernel (32-row tiles, one in flight
+// per wave) for comparison
+static bool verify_tile32() {
+  static const bool v = [] {
+    const char* e = std::getenv("EAGLE3_VERIFY_TILE32");
+    return e && e[0] == '1';
+  }();
+  return v;
+}
+
 static void verify_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S) {
-  if (verify_mfma(hd)) pick_split(T, n_head_kv, hd, kv_f32, chunk, S, verify_blocks(), 32 * kAttnWaves);
+  if (verify_mfma(hd) && !verify_tile32()) pick_split_mfma(T, n_head_kv, chunk, S);
+  else if (verify_mfma(hd)) pick_split(T, n_head_kv, hd, kv_f32, chunk, S, verify_blocks(), 32 * kAttnWaves);
   else pick_split(T, n_head_kv, hd, kv_f32, chunk, S);
 }
 
@@ -1390,8 +1644,12 @@ static hipError_t launch_mid_hd(const VerifyArgs& a, int chunk, int S, hipStream
   if (verify_mfma(HD)) {
     const int QG = (MG + 15) / 16;
     const int tiles = S * a.n_head_kv;
-    hipLaunchKernelGGL((k_attn_mid_mfma<(HD <= 128 ? HD : 128), KT>), dim3(unsigned((tiles + 7) / 8 * 8 * QG)),
-                       dim3(64 * kAttnWaves), 0, s, a, chunk, S, QG);
+    if (verify_tile32())
+      hipLaunchKernelGGL((k_attn_mid_mfma<(HD <= 128 ? HD : 128), KT>), dim3(unsigned((tiles + 7) / 8 * 8 * QG)),
+                         dim3(64 * kAttnWaves), 0, s, a, chunk, S, QG);
+    else
+      hipLaunchKernelGGL((k_attn_vr<(HD <= 128 ? HD : 128), KT>), dim3(unsigned((tiles + 7) / 8 * 8 * QG)),
+                         dim3(64 * kAttnWaves), 0, s, a, chunk, S, QG);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || S == 1) return e;
     hipLaunchKernelGGL(k_attn_combine, dim3(a.M * a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S,
@@ -1430,22 +1688,6 @@ hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipSt
   }
 }
 
-// Splits of the MFMA decode kernel: about kAttnSingleBlocks (KV head, split) blocks,
-// chunks of whole 16-row tiles per wave (64 rows), at most kAttnMfmaMaxChunk rows;
-// longer chunks than the VALU kernel's, since a block's fixed work (queries, merge)
-// is larger (at 32K rows over 8 KV heads: 1024-row chunks 23.7 us, 512 27.8, 256 35.2)
-
-static void pick_split_mfma(int T, int n_head_kv, int* chunk, int* S) {
-  const int blocks = attn_single_blocks();
-  const int target = n_head_kv >= blocks ? 1 : blocks / n_head_kv;
-  constexpr int rpb = 16 * kAttnWaves;
-  int c = (T + target - 1) / target;
-  c = ((c + rpb - 1) / rpb) * rpb;
-  if (c < rpb) c = rpb;
-  if (c > kAttnMfmaMaxChunk) c = kAttnMfmaMaxChunk;
-  *chunk = c;
-  *S = (T + c - 1) / c;
-}
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batched) return hipErrorInvalidValue;
