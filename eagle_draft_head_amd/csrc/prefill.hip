@@ -894,13 +894,20 @@ GemmPlan gemm_plan(int M, int N, int K) {
   }
   GemmPlan best{bm, 1};
   double best_cost = 1e30;
-  const int widths[2] = {bm, 320};
-  for (int w = 0; w < (bm == 256 ? 2 : 1); ++w) {
+  // 256-row blocks come 320, 256 or 128 wide; a block's rate relative to the
+  // 320-wide one (measured over full rounds at 4096 rows, fp16: 1169, 1088, 980
+  // TFLOP/s) divides its cost, so a narrower tile wins only by filling more CUs
+  // (the 1024-row K|V GEMM of the 4096-wide drafter: 128 x 2048 columns in 256 x 128
+  // blocks split 4 ways, every CU once, 40 us against 56 us for 256 x 256 on half of them)
+  const int widths[3] = {bm, 320, 128};
+  const double rate[3] = {0.93, 1.0, 0.84};
+  for (int w = 0; w < (bm == 256 ? 3 : 1); ++w) {
     const int bn = widths[w];
+    const double eff = bm == 256 ? rate[w] : 1.0;
     const long long tiles = (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
     for (int sp = 1; sp <= max_sp; sp *= 2) {
       if (K % (kBKPlain * sp) != 0) continue;
-      const double cost = double((tiles * sp + 255) / 256) * bn / sp;
+      const double cost = double((tiles * sp + 255) / 256) * bn / sp / eff;
       if (cost < best_cost * (1 - 1e-9) || (cost < best_cost * (1 + 1e-9) && sp < best.splits)) {
         best_cost = cost;
         best = GemmPlan{bn, sp};
@@ -948,6 +955,8 @@ hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
   if (f16) {  // one fp16 product
     if (bm == 256 && plan.bn == 320)
       return launch_tiles<256, 320, 4, 4, false, kBKPlain, 2, true>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    if (bm == 256 && plan.bn == 128)
+      return launch_tiles<256, 128, 4, 4, false, kBKPlain, 2, true>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
     if (plan.bn != bm) return hipErrorInvalidValue;
     if (bm == 256)
       return launch_tiles<256, 256, 4, 4, false, kBKPlain, 2, true>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
@@ -956,6 +965,10 @@ hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda,
   if (bm == 256 && plan.bn == 320) {
     if (A_lo) return launch_tiles<256, 320, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
     return launch_tiles<256, 320, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+  }
+  if (bm == 256 && plan.bn == 128) {
+    if (A_lo) return launch_tiles<256, 128, 4, 4, true, kBKSplit, 3>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
+    return launch_tiles<256, 128, 4, 4, false, kBKPlain, 2>(A_hi, A_lo, lda, B, ldb, C, M, N, kper, splits, s);
   }
   if (plan.bn != bm) return hipErrorInvalidValue;
   if (A_lo) {
