@@ -82,11 +82,12 @@ PAGE4 = DrafterConfig(
 BATCHED = QWEN3_8B.with_(name="batched32", cfg_id=4, gamma=4, max_seqs=32,
                          context=8192, max_ctx=8192 + 4)
 
-# Long context: 32768-token prompt prefilled in 2048-row chunks, gamma 3.
+# Long context: a 32767-row prefill in one call (the engine appends it in passes of
+# up to 4096 rows), gamma 3.
 LONG = DrafterConfig(
     name="long32k", cfg_id=5, n_embd=5120, n_head=40, n_head_kv=8, head_dim=128,
     n_ff=17408, draft_vocab=32000, target_vocab=262144, rope_dim=128,
-    rope_theta=1e6, context=32767, gamma=3, max_ctx=32768 + 64, prefill_chunk=2048)
+    rope_theta=1e6, context=32767, gamma=3, max_ctx=32768 + 64)
 
 ALL = {c.name: c for c in (TINY, QWEN3_8B, PAGE4, BATCHED, LONG)}
 
