@@ -71,6 +71,10 @@ WB_BF16, WB_I4 = 2.0, 0.5 + 2.0 / 32
 # KV bytes per element, K and V averaged: q8_0 K is 34 bytes per 32 values, q5_1 V 24
 KV_BYTES = {"f32": 4.0, "bf16": 2.0, "q8q5": (34.0 + 24.0) / 64}
 WB = WB_BF16
+# the chain step's QKV embedding half read from the load-time token table (one
+# fp32 row of the table and a sum of squares instead of W_qkv[:, :n], the
+# embedding row and input_layernorm)
+TABLE = False
 
 
 BF16_MFMA_PEAK_TFLOPS = 2500.0
@@ -104,6 +108,8 @@ def kernel_bytes(cfg, kernel: str, L: int, kv_bytes: int = 4) -> float:
     if kernel == "gate_up":
         return WB * 2 * ff * n + 4 * n + 4 * n + 4 * ff
     if kernel == "qkv":
+        if TABLE:
+            return WB * (qd + 2 * kvd) * n + 4 * (qd + 2 * kvd) + 4 + 8 * n + 4 * qd + 2 * 2 * kvd
         return WB * (qd + 2 * kvd) * 2 * n + 2 * n + 4 * n + 8 * n + 4 * qd + 2 * 2 * kvd
     if kernel == "down":
         return WB * n * ff + 4 * ff + 4 * n + 4 * n
@@ -121,9 +127,20 @@ def kernel_bytes_step(cfg, L: int, gamma: int, kv_bytes: int = 4) -> float:
     rows: the step's weights, norms, the embedding row, the K/V rows it reads
     (L + j + 1 at step j) and the row it writes."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
-    p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
     rows = L + 1 + (gamma - 1) / 2 + 1
-    return WB * p_step + 8 * n + 2 * n + rows * 2 * kv_bytes * kvd
+    return WB * p_step_weights(cfg) + 8 * n + tok_bytes(cfg) + rows * 2 * kv_bytes * kvd
+
+
+def p_step_weights(cfg) -> float:
+    """Weight elements one draft step streams."""
+    n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
+    return (qd + 2 * kvd) * (1 if TABLE else 2) * n + n * qd + 3 * ff * n + dv * n
+
+
+def tok_bytes(cfg) -> float:
+    """What a draft step reads for its token: the embedding row, or the token
+    table's row and sum of squares."""
+    return 4.0 * (cfg.q_dim + 2 * cfg.kv_dim) + 4 if TABLE else 2.0 * cfg.n_embd
 
 
 def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
@@ -133,11 +150,11 @@ def step_bytes(cfg, L: int, gamma: int, accepted: int, kv_bytes: int = 4,
     next boundary: its taps in, the feature and its weighted copy out) on the
     rebuild's one pass over W_fc."""
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
-    p_step = (qd + 2 * kvd) * 2 * n + n * qd + 3 * ff * n + dv * n
+    p_step = p_step_weights(cfg)
     tot = 12.0 * n + 8 * n + 4 if stored else WB * 3 * n * n + 12 * n   # encode: W_fc + aux
     for j in range(gamma):
         rows = L + j                                      # rows attended before the new one
-        tot += WB * p_step + 8 * n + 2 * n + (rows + 1) * 2 * kv_bytes * kvd
+        tot += WB * p_step + 8 * n + tok_bytes(cfg) + (rows + 1) * 2 * kv_bytes * kvd
     if rebuild:
         T = accepted + 1                                  # rebuild rows
         tot += WB * 3 * n * n + WB * 2 * kvd * 2 * n + T * (12 * n + 4 + 2 * n + 2 * kv_bytes * kvd)
@@ -156,6 +173,9 @@ def main():
     ap.add_argument("--cpu-rounds", type=int, default=5)
     ap.add_argument("--kv", choices=["f32", "bf16", "q8q5"], default="f32",
                     help="draft-KV element type")
+    ap.add_argument("--token-table", choices=["default", "on", "off"], default="default",
+                    help="the chain step's QKV embedding half from the load-time token table (default: on with "
+                         "bf16 weights) or streamed (off)")
     ap.add_argument("--append", choices=["default", "split", "bf16", "f16"], default="default",
                     help="teacher-forced activation form of the prefill and rebuild GEMMs (default: fp16 with "
                          "bf16 weights, split with int4 weights)")
@@ -234,12 +254,14 @@ def main():
     max_ctx = max(L, max(L_at)) + gamma + 64
     kv_dtype = {"bf16": B.KV_BF16, "q8q5": B.KV_Q8Q5}.get(args.kv, B.KV_F32)
     i4 = args.weights == "int4"
-    global WB
+    global WB, TABLE
     WB = WB_I4 if i4 else WB_BF16
+    TABLE = not i4 and args.token_table != "off"
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype,
                  weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16,
                  append_act={"default": B.APPEND_DEFAULT, "split": B.APPEND_SPLIT, "bf16": B.APPEND_BF16,
-                             "f16": B.APPEND_F16}[args.append])
+                             "f16": B.APPEND_F16}[args.append],
+                 token_table={"default": B.TABLE_DEFAULT, "on": B.TABLE_ON, "off": B.TABLE_OFF}[args.token_table])
     stream = torch.cuda.current_stream()
 
     # committed context
@@ -389,7 +411,7 @@ def main():
                                + (" (not attended: round-local drafter)" if local else "")
                                + (f" (mean over the timed rounds; {L_at[args.warmup]}.."
                                   f"{L_at[-1]})" if stored else ""),
-                   "batch": 1, "gamma": gamma,
+                   "batch": 1, "gamma": gamma, "token_table": TABLE,
                    "step": ("draft_chain from the stored boundary feature + rebuild_after_verify("
                             f"a+1 rows, a cycling 0..{gamma}, with the next boundary's taps)")
                    if stored else

@@ -21,6 +21,7 @@ STORED_BOUNDARY = 2
 ROUND_LOCAL = 4
 KV_F32, KV_BF16, KV_Q8Q5 = 0, 1, 2
 APPEND_DEFAULT, APPEND_BF16, APPEND_SPLIT, APPEND_F16 = 0, 1, 2, 3
+TABLE_DEFAULT, TABLE_OFF, TABLE_ON = 0, 1, 2
 WEIGHTS_BF16, WEIGHTS_I4 = 0, 1
 
 ERR_NAMES = {OK: "OK", E_INVAL: "E_INVAL", E_SHAPE: "E_SHAPE", E_UNSUPPORTED: "E_UNSUPPORTED",
@@ -46,7 +47,8 @@ class eagle3_config(ctypes.Structure):
                 ("target_vocab", c_int32), ("n_aux", c_int32), ("rope_dim", c_int32),
                 ("rope_theta", c_float), ("rms_eps", c_float), ("max_ctx", c_int32),
                 ("max_gamma", c_int32), ("max_seqs", c_int32), ("kv_dtype", c_int32),
-                ("weight_format", c_int32), ("append_act", c_int32)]
+                ("weight_format", c_int32), ("append_act", c_int32),
+                ("token_table", c_int32)]
 
 
 class eagle3_weights(ctypes.Structure):
@@ -182,14 +184,14 @@ def eagle3_resolve_rope_dim(rotary_dim: Optional[int], partial_factor: Optional[
 
 def make_config(geom, max_ctx: int, max_gamma: int = 16, max_seqs: int = 1,
                 kv_dtype: int = KV_F32, weight_format: int = WEIGHTS_BF16,
-                append_act: int = APPEND_DEFAULT) -> eagle3_config:
+                append_act: int = APPEND_DEFAULT, token_table: int = TABLE_DEFAULT) -> eagle3_config:
     return eagle3_config(
         n_embd=geom.n_embd, n_head=geom.n_head, n_head_kv=geom.n_head_kv, head_dim=geom.head_dim,
         n_ff=geom.n_ff, draft_vocab=geom.draft_vocab, target_vocab=geom.target_vocab,
         n_aux=getattr(geom, "n_aux", 3), rope_dim=geom.rope_dim, rope_theta=float(geom.rope_theta),
         rms_eps=float(geom.rms_eps), max_ctx=int(max_ctx), max_gamma=int(max_gamma),
         max_seqs=int(max_seqs), kv_dtype=int(kv_dtype), weight_format=int(weight_format),
-        append_act=int(append_act))
+        append_act=int(append_act), token_table=int(token_table))
 
 
 def make_weights(tensors: Dict[str, object], d2t_host) -> eagle3_weights:

@@ -131,6 +131,11 @@ struct eagle3_ctx {
   int cap_local = 0;
   size_t kv_local_elems = 0;  // K + V elements per slot
 
+  // token table of the chain step's QKV embedding half: [target_vocab][N_qkv] fp32
+  // rows of W_qkv[:, :n] . (input_layernorm * E[t]) in the repacked row order, and
+  // sum E[t]^2 per token (null when off)
+  float *tok_tab = nullptr, *tok_ss = nullptr;
+
   int tf_rows = 0;
   size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
   uint16_t *tf_A = nullptr, *tf_A_lo = nullptr, *tf_cat16 = nullptr, *tf_cat16_lo = nullptr;
@@ -300,6 +305,11 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (cfg->append_act != EAGLE3_APPEND_DEFAULT && cfg->append_act != EAGLE3_APPEND_BF16 &&
       cfg->append_act != EAGLE3_APPEND_SPLIT && cfg->append_act != EAGLE3_APPEND_F16)
     return bad("unknown append_act", EAGLE3_E_INVAL);
+  if (cfg->token_table != EAGLE3_TABLE_DEFAULT && cfg->token_table != EAGLE3_TABLE_OFF &&
+      cfg->token_table != EAGLE3_TABLE_ON)
+    return bad("unknown token_table", EAGLE3_E_INVAL);
+  if (cfg->token_table == EAGLE3_TABLE_ON && cfg->weight_format != EAGLE3_WEIGHTS_BF16)
+    return bad("the token table needs bf16 weights", EAGLE3_E_INVAL);
   if (cfg->append_act == EAGLE3_APPEND_F16 && cfg->weight_format != EAGLE3_WEIGHTS_BF16)
     return bad("fp16 teacher-forced activations need bf16 weights", EAGLE3_E_UNSUPPORTED);
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
@@ -641,6 +651,27 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     E3_TRYH(e3::launch_bf16_to_f16_x256(c->w_qkv + size_t(qd) * 2 * n, c->w_kv16, size_t(2 * kvd) * 2 * n,
                                         c->status, s),
             "fp16 kv");
+  }
+  if (cfg->token_table == EAGLE3_TABLE_ON ||
+      (cfg->token_table == EAGLE3_TABLE_DEFAULT && cfg->weight_format == EAGLE3_WEIGHTS_BF16)) {
+    // the token table: passes of tf_rows tokens, w_in * E as (hi, lo) bf16 planes
+    // in tf_A, one MFMA GEMM against the embedding half of the repacked W_qkv
+    E3_TRY(dalloc(c, &c->tok_tab, size_t(vt) * N_qkv));
+    E3_TRY(dalloc(c, &c->tok_ss, size_t(vt)));
+    E3_TRYH(e3::launch_tok_ss(c->embed, int(vt), int(n), c->tok_ss, s), "token table norms");
+    const int T = c->tf_rows;
+    uint16_t* A_hi = c->tf_A;
+    uint16_t* A_lo = c->tf_A + size_t(T) * n;  // tf_A holds 3 n values per row
+    for (int64_t r0 = 0; r0 < vt; r0 += T) {
+      const int rows = int(std::min<int64_t>(T, vt - r0));
+      E3_TRYH(e3::launch_pack_embed(c->embed, c->nrm_in, int(r0), rows, int(n), A_hi, A_lo, s),
+              "token table pack");
+      e3::GemmPlan p = e3::gemm_plan(rows, int(N_qkv), int(n));
+      p.splits = 1;  // one plane: the table rows are written in place
+      E3_TRYH(e3::launch_gemm_bf16(A_hi, A_lo, int(n), c->w_qkv, int(2 * n), c->tok_tab + size_t(r0) * N_qkv,
+                                   rows, int(N_qkv), int(n), p, s),
+              "token table gemm");
+    }
   }
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
     c->i4 = true;
@@ -1354,6 +1385,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       }
       qa.gw = g->w_hid; qa.g_ssq = g->ssq; qa.g_ssq_count = g->count;
       qa.w_in = ctx->nrm_in; qa.pos = pos; qa.row = row; qa.q_out = ctx->q;
+      qa.tok_tab = ctx->tok_tab; qa.tok_ss = ctx->tok_ss;
       qa.k_cache = kc; qa.v_cache = vc; qa.cap = cap;
       qa.kv_f32 = ctx->kv_f32;
       if (ctx->kv_q) {  // the new row goes to the fp32 stage; attention quantizes it

@@ -611,6 +611,23 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   float sg = sum_partials(a.g_ssq, a.g_ssq_count);
   const int tok = qkv_token(a, sv, si, st);
   __syncthreads();  // hidden half staged
+  if (a.tok_tab) {
+    // embedding half from the token table: the wave's rows of the token's entry
+    float acc_e[R], acc_g[R];
+    const float* trow = a.tok_tab + (size_t)tok * N;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc_e[r] = trow[min(row0 + r, N - 1)];
+    const float se = a.tok_ss[tok];
+    if (issued) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, wpf, acc_g);
+    else if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
+    float zero = 0.f;
+    block_sum2(zero, sg, red);  // every wave takes part
+    if (row0 >= N) return;
+    const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
+    const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+    qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+    return;
+  }
   // the embedding row and input_layernorm go to registers; they land while the
   // hidden half streams
   const uint2* e4 = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);

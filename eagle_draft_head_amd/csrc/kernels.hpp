@@ -95,6 +95,11 @@ struct QkvArgs {
   const float* g_ssq;      // per-block partial sums of g^2
   int g_ssq_count;
   const float* w_in;       // input_layernorm
+  // optional token table: tok_tab[t][r] = W_qkv[r, :n] . (w_in * E[t]) for every row r of
+  // the repacked QKV matrix, tok_ss[t] = sum E[t]^2; with it the embedding half of W_qkv
+  // is not streamed
+  const float* tok_tab;
+  const float* tok_ss;
   int pos;                 // rotary position of the row
   int row;                 // KV row written (pos, or the step in a round-local scratch)
   float* q_out;
@@ -426,6 +431,10 @@ GemmPlan gemm_plan(int M, int N, int K);
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
                             int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
                             hipStream_t s, bool f16 = false);
+// the token table's build: ss[t] = sum E[t]^2; rows [r0, r0 + T) of w_in * E as bf16 (hi, lo)
+hipError_t launch_tok_ss(const uint16_t* E, int vocab, int n, float* ss, hipStream_t s);
+hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, int r0, int T, int n, uint16_t* A_hi,
+                             uint16_t* A_lo, hipStream_t s);
 // dst[i] = fp16 bits of (bf16 src[i]) * 2^8, exact for 2^-25 <= |src| < 256 (and 0);
 // any other weight raises kStatusAppendRange in *status
 hipError_t launch_bf16_to_f16_x256(const uint16_t* src, uint16_t* dst, size_t count, uint32_t* status,

@@ -97,6 +97,72 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
                    uint32_t(l[4]) | (uint32_t(l[5]) << 16), uint32_t(l[6]) | (uint32_t(l[7]) << 16));
 }
 
+// ---------------------------------------------------------------------------
+// The token table of the chain step's QKV embedding half (built at load):
+// k_tok_ss: ss[t] = sum of E[t]^2 (one block per token row);
+// k_pack_embed: rows [r0, r0 + T) of input_layernorm * E as bf16 (hi, lo) planes,
+// the activations of the table GEMM.  grid (ceil(n / 2048), T), 8 values a thread.
+__global__ __launch_bounds__(256) void k_tok_ss(const uint16_t* __restrict__ E, int n, float* __restrict__ ss) {
+  __shared__ float red[8];
+  const uint16_t* row = E + (size_t)blockIdx.x * n;
+  float acc = 0.f;
+  for (int c = threadIdx.x * 8; c < n; c += blockDim.x * 8) {
+    const uint4 w = *reinterpret_cast<const uint4*>(row + c);
+    const float v[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                        bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(v[e], v[e], acc);
+  }
+  acc = wave_sum(acc);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) red[wv] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) t += red[w];
+    ss[blockIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pack_embed(const uint16_t* __restrict__ E, const float* __restrict__ w_in,
+                                                    int r0, int T, int n, uint16_t* __restrict__ A_hi,
+                                                    uint16_t* __restrict__ A_lo) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (t >= T || c >= n) return;
+  const uint4 w = *reinterpret_cast<const uint4*>(E + (size_t)(r0 + t) * n + c);
+  const float4 g0 = *reinterpret_cast<const float4*>(w_in + c), g1 = *reinterpret_cast<const float4*>(w_in + c + 4);
+  const float v[8] = {bf16_lo(w.x) * g0.x, bf16_hi(w.x) * g0.y, bf16_lo(w.y) * g0.z, bf16_hi(w.y) * g0.w,
+                      bf16_lo(w.z) * g1.x, bf16_hi(w.z) * g1.y, bf16_lo(w.w) * g1.z, bf16_hi(w.w) * g1.w};
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f32_to_bf16(v[e]);
+    l[e] = f32_to_bf16(v[e] - bf16_to_f32(h[e]));
+  }
+  const size_t at = (size_t)t * n + c;
+  *reinterpret_cast<uint4*>(A_hi + at) =
+      make_uint4(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16),
+                 uint32_t(h[4]) | (uint32_t(h[5]) << 16), uint32_t(h[6]) | (uint32_t(h[7]) << 16));
+  *reinterpret_cast<uint4*>(A_lo + at) =
+      make_uint4(uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16),
+                 uint32_t(l[4]) | (uint32_t(l[5]) << 16), uint32_t(l[6]) | (uint32_t(l[7]) << 16));
+}
+
+hipError_t launch_tok_ss(const uint16_t* E, int vocab, int n, float* ss, hipStream_t s) {
+  if (vocab <= 0 || (n & 7)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tok_ss, dim3(vocab), dim3(256), 0, s, E, n, ss);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, int r0, int T, int n, uint16_t* A_hi,
+                             uint16_t* A_lo, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if ((n & 7) || T > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pack_embed, dim3((n + 2047) / 2048, T), dim3(256), 0, s, E, w_in, r0, T, n, A_hi, A_lo);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_aux(const float* a0, const float* a1, const float* a2, int T, int n,
                            uint16_t* A_hi, uint16_t* A_lo, hipStream_t s, const TapRowsB& yb, int f16,
                            uint32_t* status) {

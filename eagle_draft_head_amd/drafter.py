@@ -15,7 +15,8 @@ from . import binding as B
 class Drafter:
     def __init__(self, geom, weights: Dict[str, torch.Tensor], d2t, max_ctx: int,
                  max_gamma: int = 16, max_seqs: int = 1, kv_dtype: int = B.KV_F32, stream=None,
-                 weight_format: int = B.WEIGHTS_BF16, append_act: int = B.APPEND_DEFAULT):
+                 weight_format: int = B.WEIGHTS_BF16, append_act: int = B.APPEND_DEFAULT,
+                 token_table: int = B.TABLE_DEFAULT):
         if not torch.cuda.is_available():
             raise RuntimeError("the eagle3 engine needs a GPU")
         self.geom = geom
@@ -24,7 +25,7 @@ class Drafter:
         self.max_gamma = max_gamma
         self.kv_dtype = kv_dtype
         self.cfg = B.make_config(geom, max_ctx, max_gamma, max_seqs, kv_dtype, weight_format,
-                                 append_act)
+                                 append_act, token_table)
         self._w = B.make_weights(weights, d2t)
         self.ctx = B.eagle3_load(self.cfg, self._w, stream)
 

@@ -80,6 +80,7 @@ typedef struct {
   int32_t kv_dtype;      /* EAGLE3_KV_F32 (default), EAGLE3_KV_BF16 or EAGLE3_KV_Q8Q5 */
   int32_t weight_format; /* EAGLE3_WEIGHTS_BF16 (default) or EAGLE3_WEIGHTS_I4, see below */
   int32_t append_act;    /* activations of the teacher-forced MFMA passes, see below */
+  int32_t token_table;   /* embedding half of the chain step's QKV from a table, see below */
 } eagle3_config;
 
 /* Draft-KV precision.  EAGLE3_KV_F32 stores K/V rows in fp32.  EAGLE3_KV_BF16
@@ -114,6 +115,23 @@ typedef struct {
    the scaled copy does not hold exactly, raises EAGLE3_STATUS_APPEND_RANGE (see
    eagle3_status).  0.3 GB of weight copies at the 5120-wide drafter. */
 #define EAGLE3_APPEND_F16 3
+/* The embedding half of a chain step's QKV projection depends on the token alone:
+   W_qkv[:, :n] . RMSNorm(E[tok]) = (W_qkv[:, :n] . (input_layernorm * E[tok])) /
+   rms(E[tok]) (memra_engine `eagle.rs`, module doc "Op-sequence": the embedding is
+   normalised, concatenated first, then projected).  EAGLE3_TABLE_ON computes the
+   first factor for every target token at load into an fp32 table of target_vocab x
+   (n_head + 2 n_head_kv) head_dim values, plus sum(E[tok]^2) per token, and each
+   batch-1 chain step reads one table row instead of streaming the embedding half of
+   W_qkv (half of its QKV weight bytes).  The table is built by one MFMA GEMM whose
+   activations enter as bf16 (hi, lo) pairs (about 2^-17 relative), summed in fp32.
+   EAGLE3_TABLE_DEFAULT: on with bf16 weights, off with int4 weights; EAGLE3_TABLE_OFF
+   streams both halves.  Needs bf16 weights (EAGLE3_E_INVAL otherwise).  3.7 GB at
+   the Qwen3-8B shape (151936 tokens x 6144 rows).  Batched chains and the
+   teacher-forced appends do not use it. */
+#define EAGLE3_TABLE_DEFAULT 0
+#define EAGLE3_TABLE_OFF 1
+#define EAGLE3_TABLE_ON 2
+
 /* EAGLE3_KV_Q8Q5: K rows in q8_0 and V rows in q5_1, blocks of 32 values along
    head_dim (memra_engine `eagle.rs`, `Eagle3Scratch` doc and `attn`: the draft
    layer appends quantized K/V rows and decode attention reads the quantized views;

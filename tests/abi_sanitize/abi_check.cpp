@@ -44,6 +44,7 @@ static eagle3_config small_config(void) {
   c.draft_vocab = 1024; c.target_vocab = 4096; c.n_aux = 3; c.rope_dim = 64;
   c.rope_theta = 1e4f; c.rms_eps = 1e-6f; c.max_ctx = 128; c.max_gamma = 8; c.max_seqs = 2;
   c.kv_dtype = EAGLE3_KV_F32; c.weight_format = EAGLE3_WEIGHTS_BF16; c.append_act = EAGLE3_APPEND_DEFAULT;
+  c.token_table = EAGLE3_TABLE_DEFAULT;
   return c;
 }
 
@@ -134,6 +135,10 @@ static void check_load_validation(void) {
   CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);
   b = c; b.append_act = 9;
   CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);
+  b = c; b.token_table = 3;
+  CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);
+  b = c; b.max_seqs = 1; b.weight_format = EAGLE3_WEIGHTS_I4; b.token_table = EAGLE3_TABLE_ON;
+  CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);  /* the table needs bf16 weights */
   b = c; b.kv_dtype = EAGLE3_KV_Q8Q5;  /* batch-1 only */
   CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_UNSUPPORTED);
   b = c; b.max_ctx = 0;

@@ -23,10 +23,11 @@ def say(*a):
 
 
 def gpu_drafter(cfg: DrafterConfig, weights_dev, max_ctx=None, max_gamma=16, max_seqs=1, append_act=0,
-                kv_dtype=0):
+                kv_dtype=0, token_table=0):
     from eagle_draft_head_amd.drafter import Drafter
     return Drafter(cfg, weights_dev, weights_dev["d2t"].cpu(), max_ctx or cfg.max_ctx_eff,
-                   max_gamma=max_gamma, max_seqs=max_seqs, append_act=append_act, kv_dtype=kv_dtype)
+                   max_gamma=max_gamma, max_seqs=max_seqs, append_act=append_act, kv_dtype=kv_dtype,
+                   token_table=token_table)
 
 
 def weights_both(cfg: DrafterConfig, lazy_embed_host=False):

@@ -20,18 +20,23 @@ def _tok(x):
     return torch.as_tensor(np.asarray(x), dtype=torch.int32).reshape(-1).cuda()
 
 
-def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None, stored=False, kv_bf16=False):
+def _run_rounds(cfg, rounds, L, gamma, rebuild_every=0, max_ctx=None, stored=False, kv_bf16=False,
+                token_table=B.TABLE_DEFAULT):
     """stored: every round starts from the boundary feature stored by the prefill
     or the previous rebuild (given the round's boundary taps as next taps), and
     every round is followed by a rebuild.  kv_bf16: the bf16 draft-KV option,
     against the oracle storing bf16-rounded rows computed from the same fp16-rounded
-    append inputs as the engine's default append form."""
-    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds} stored={stored} bf16={kv_bf16}")
+    append inputs as the engine's default append form.  token_table: the chain
+    step's QKV embedding half from the load-time table (the default with bf16
+    weights) or streamed (TABLE_OFF)."""
+    say(f"[parity] cfg={cfg.name} L={L} gamma={gamma} rounds={rounds} stored={stored} bf16={kv_bf16} "
+        f"table={token_table}")
     if stored:
         rebuild_every = 1
     wd, wh = weights_both(cfg)
     max_ctx = max_ctx or (L + rounds * (gamma + 1) + gamma + 8)
-    dr = gpu_drafter(cfg, wd, max_ctx=max_ctx, kv_dtype=B.KV_BF16 if kv_bf16 else B.KV_F32)
+    dr = gpu_drafter(cfg, wd, max_ctx=max_ctx, kv_dtype=B.KV_BF16 if kv_bf16 else B.KV_F32,
+                     token_table=token_table)
     orc = make_oracle(cfg, wh, max_ctx=max_ctx, **(dict(kv_format="bf16", append_act="f16") if kv_bf16 else {}))
     aux = aux_np(cfg, 0, L)
     toks = toks_np(cfg, 0, L)
@@ -90,6 +95,54 @@ def test_ragged_shape_chain_parity():
     # rows, K and context all leave ragged tails over the kernels' tiles
     pinned, steps = _run_rounds(small_variant(), rounds=40, L=300, gamma=4, rebuild_every=3)
     assert pinned >= 0.25 * steps
+
+
+@pytest.mark.parametrize("cfg,L,gamma,rounds", [(TINY, 63, 3, 40), (small_variant(), 300, 4, 16)],
+                         ids=["tiny", "ragged"])
+def test_streamed_embedding_half_chain_parity(cfg, L, gamma, rounds):
+    """TABLE_OFF: both halves of W_qkv streamed every step; the same bar."""
+    pinned, steps = _run_rounds(cfg, rounds=rounds, L=L, gamma=gamma, rebuild_every=3,
+                                token_table=B.TABLE_OFF)
+    assert pinned >= 0.25 * steps
+
+
+def test_token_table_matches_streamed_half():
+    """The table holds W_qkv[:, :n] . (input_layernorm * E[t]) for every target
+    token (MFMA with (hi, lo) bf16 activations, relative error per product at most
+    2^-18); a chain with it agrees with the streamed form to fp32 rounding:
+    identical ids, logits and hidden within 1e-5 relative, over every step of
+    several rounds whose boundary tokens cover the vocabulary's ends."""
+    cfg = small_variant()
+    wd, _ = weights_both(cfg)
+    L, gamma = 40, 6
+    drs = [gpu_drafter(cfg, wd, max_ctx=200, token_table=t) for t in (B.TABLE_ON, B.TABLE_OFF)]
+    aux = aux_np(cfg, 0, L)
+    toks = toks_np(cfg, 0, L)
+    for dr in drs:
+        dr.prefill(0, _tok(toks), to_dev_aux(aux))
+    baux = aux_np(cfg, 1, 6)
+    for r, t in enumerate([0, cfg.target_vocab - 1, 1, 17, cfg.target_vocab // 2, 5]):
+        res = []
+        for dr in drs:
+            out, geff, logits, hidden = dr.draft_chain([0], _tok([t]), to_dev_aux(baux, slice(r, r + 1)), gamma,
+                                                       debug=True)
+            torch.cuda.synchronize()
+            res.append((out.cpu(), int(geff[0]), logits.double().cpu(), hidden.double().cpu()))
+            dr.rewind(0, L)
+        (o1, g1, l1, h1), (o2, g2, l2, h2) = res
+        assert g1 == g2 == gamma
+        # the ids agree up to the first near-tie of the streamed form's logits
+        top2 = torch.topk(l2[0, :g2], 2, dim=-1).values
+        gap = (top2[:, 0] - top2[:, 1]).abs()
+        ok = int(torch.nonzero(gap < 1e-4).min()) if bool((gap < 1e-4).any()) else g2
+        assert torch.equal(o1[0, :ok], o2[0, :ok]), (r, o1, o2)
+        # steps 0..ok read the same tokens: their logits and hidden states compare
+        for j in range(min(ok + 1, g2)):
+            assert (l1[0, j] - l2[0, j]).norm() / l2[0, j].norm() < 1e-5, (r, j)
+        for j in range(min(ok + 2, g2 + 1)):
+            assert (h1[0, j] - h2[0, j]).norm() / h2[0, j].norm() < 1e-5, (r, j)
+    for dr in drs:
+        dr.close()
 
 
 def test_chain_from_empty_cache():
