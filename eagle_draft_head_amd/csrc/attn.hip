@@ -28,6 +28,7 @@ constexpr int kAttnMfmaMaxChunk = 2048;  // the MFMA decode kernel's longest spl
 // 256 rather than 512: a 4096-row context over 4 KV heads then splits 64 ways, and its
 // combine loads every split in one round trip (128 splits took two)
 constexpr int kAttnSingleBlocks = 256;
+constexpr int kAttnQmBlocks = 512;  // the q8q5 MFMA kernel's target (within attn_max_splits)
 
 // 16 bytes of a KV row as floats: 8 bf16 or 4 fp32 values
 template <typename KT>
@@ -1070,19 +1071,46 @@ __global__ __launch_bounds__(256, 2) void k_attn_vr(VerifyArgs a, int chunk, int
 
 // ---------------------------------------------------------------------------
 // k_attn over quantized regions (q8_0 K, q5_1 V; layout in kernels.hpp).  A lane
-// holds 8 consecutive dims of a row, inside one block of 32: per row it loads 8 K
-// codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and its
-// V block's (D, M).  The K dot product is D_k * (sum_e code_e q_e - 128 sum_e q_e)
-// (codes are stored + 128, sum_e q_e per lane precomputed); V enters as
-// p D_v q_e per element plus p M_v once per row, added to every element at the end.
-// The block whose split holds row T - 1 first quantizes that row from kv_new into
-// the cache (other blocks never read it).
+// holds 8 consecutive K dims of a row, inside one block of 32, and the 8 V dims whose
+// codes sit in the lane's 4 nibble bytes (and its high-bit byte): per row it loads 8
+// K codes, its K block's scale, 4 bytes of V nibbles, the byte of V high bits and the
+// (D, M) of the V blocks those dims fall in.  The K dot product is
+// D_k * (sum_e code_e q_e - 128 sum_e q_e) (codes are stored + 128, sum_e q_e per lane
+// precomputed); V values are D_v q + M_v.  The block whose split holds row T - 1
+// first quantizes that row from kv_new into the cache (other blocks never read it).
+// The MFMA kernel below (k_attn_qm) covers head_dim 64 and 128; this one the rest.
+// Quantize the new row T - 1 of KV head kvh from kv_new into the cache (K dims then V
+// dims, one per thread; the V codes are packed through LDS), visible to the whole
+// block on return.  Every thread of the block calls it.
+template <int HD>
+__device__ __forceinline__ void quantize_new_row(const AttnArgs& a, int kvh) {
+  __shared__ uint8_t vcode[HD];
+  uint8_t* kreg = static_cast<uint8_t*>(const_cast<void*>(a.k_cache));
+  uint8_t* vreg = static_cast<uint8_t*>(const_cast<void*>(a.v_cache));
+  const int nkv = a.n_head_kv;
+  const KvqAt at(nkv, a.cap, HD, kvh, a.T - 1);
+  for (int i0 = 0; i0 < 2 * HD; i0 += blockDim.x) {
+    const int i = i0 + threadIdx.x;
+    const bool on = i < 2 * HD;  // whole groups of 32
+    const bool is_k = i < HD;
+    const int dim = is_k ? i : i - HD;
+    const float x = on ? a.kv_new[(is_k ? 0 : nkv * HD) + kvh * HD + dim] : 0.f;
+    const uint32_t q = kvq_quant(x, is_k, dim, kreg, vreg, at, on);
+    if (on && !is_k) vcode[dim] = uint8_t(q);
+  }
+  __syncthreads();
+  kvq_pack_v(vcode, HD, vreg, at, threadIdx.x, blockDim.x);
+  __threadfence();
+  __syncthreads();
+}
+
 template <int HD, int G>
 __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
   constexpr int LPR = HD / kAttnLaneElems;  // lanes per row
   constexpr int RPW = 64 / LPR;
   constexpr int RPB = RPW * kAttnWaves;
   constexpr int kDepth = 4;
+  constexpr int NB = HD / 32;
   __shared__ float obuf[kAttnWaves][G][HD];
   __shared__ float s_M[kAttnWaves][G], s_L[kAttnWaves][G];
 
@@ -1094,20 +1122,7 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
   if (r0 >= T) return;
   const uint8_t* kreg = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vreg = static_cast<const uint8_t*>(a.v_cache);
-  if (a.kv_new && r1 == T) {
-    // quantize the new row of this KV head: K dims then V dims, one per lane
-    for (int i0 = 0; i0 < 2 * HD; i0 += blockDim.x) {
-      const int i = i0 + threadIdx.x;
-      const bool on = i < 2 * HD;  // whole groups of 32
-      const bool is_k = i < HD;
-      const int dim = is_k ? i : i - HD;
-      const float x = on ? a.kv_new[(is_k ? 0 : nkv * HD) + kvh * HD + dim] : 0.f;
-      const KvqAt at(nkv, cap, HD, kvh, T - 1);
-      kvq_store(x, is_k, dim, const_cast<uint8_t*>(kreg), const_cast<uint8_t*>(vreg), at, on);
-    }
-    __threadfence();
-    __syncthreads();
-  }
+  if (a.kv_new && r1 == T) quantize_new_row<HD>(a, kvh);
   const bool direct = S == 1;
   const float scale = 1.4426950408889634f / sqrtf(float(HD));
   // per-lane bases: row r of this head at kc + r * HD etc.
@@ -1116,19 +1131,28 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
   const uint8_t* ks = kreg + all * HD + hr0 * (HD / 32) * 2 + (sub >> 2) * 2;
   const uint8_t* vn = vreg + hr0 * (HD / 2) + sub * 4;
   const uint8_t* vh = vreg + all * (HD / 2) + hr0 * (HD / 8) + sub;
-  const uint8_t* vd = vreg + all * (HD / 2 + HD / 8) + hr0 * (HD / 32) * 4 + (sub >> 2) * 4;
+  // the (D, M) of the V blocks of the lane's nibble bytes 4 sub + j: block (4 sub + j) % NB
+  constexpr int NDM = NB < 4 ? NB : 4;
+  const uint8_t* vd = vreg + all * (HD / 2 + HD / 8) + hr0 * NB * 4 + ((4 * sub) % NB) * 4;
 
   const int off = wv * RPW + slot;
   const int rlast = r1 - 1;
   uint2 kq[kDepth];
-  uint32_t kd[kDepth], vq[kDepth], vb[kDepth], vm[kDepth];
+  uint32_t kd[kDepth], vq[kDepth], vb[kDepth], vm[kDepth][NDM];
   auto load_row = [&](int i, int row) {
     row = min(row, rlast);
     kq[i] = *reinterpret_cast<const uint2*>(kc + (size_t)row * HD);
     kd[i] = *reinterpret_cast<const uint16_t*>(ks + (size_t)row * (HD / 32) * 2);
     vq[i] = *reinterpret_cast<const uint32_t*>(vn + (size_t)row * (HD / 2));
     vb[i] = vh[(size_t)row * (HD / 8)];
-    vm[i] = *reinterpret_cast<const uint32_t*>(vd + (size_t)row * (HD / 32) * 4);
+    const uint8_t* dp = vd + (size_t)row * NB * 4;
+    if constexpr (NDM == 4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(dp);
+      vm[i][0] = w.x; vm[i][1] = w.y; vm[i][2] = w.z; vm[i][3] = w.w;
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(dp);
+      vm[i][0] = w.x; vm[i][1] = w.y;
+    }
   };
   int rb = r0;
 #pragma unroll
@@ -1144,13 +1168,12 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
     }
     qs[g] *= -128.f;
   }
-  float m[G], mr[G], l[G], sm[G], acc[G][kAttnLaneElems];
+  float m[G], mr[G], l[G], acc[G][kAttnLaneElems];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     mr[g] = -INFINITY;
     l[g] = 0.f;
-    sm[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = 0.f;
   }
@@ -1164,11 +1187,19 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
     const uint32_t c_lo = (nb & 0x0F0F0F0Fu) | ((((hr & 0x08040201u) + 0x787C7E7Fu) & 0x80808080u) >> 3);
     const uint32_t c_hi = ((nb >> 4) & 0x0F0F0F0Fu) | ((((hr & 0x80402010u) + 0x00406070u) & 0x80808080u) >> 3);
     const float Dk = f16_bits_to_f32(uint16_t(kd[i]));
-    const float Dv = f16_bits_to_f32(uint16_t(vm[i] & 0xFFFFu)), Mv = f16_bits_to_f32(uint16_t(vm[i] >> 16));
     const float kf[8] = {float(k0 & 0xFFu), float((k0 >> 8) & 0xFFu), float((k0 >> 16) & 0xFFu), float(k0 >> 24),
                          float(k1 & 0xFFu), float((k1 >> 8) & 0xFFu), float((k1 >> 16) & 0xFFu), float(k1 >> 24)};
-    const float vf[8] = {float(c_lo & 0xFFu), float((c_lo >> 8) & 0xFFu), float((c_lo >> 16) & 0xFFu), float(c_lo >> 24),
+    const float vc[8] = {float(c_lo & 0xFFu), float((c_lo >> 8) & 0xFFu), float((c_lo >> 16) & 0xFFu), float(c_lo >> 24),
                          float(c_hi & 0xFFu), float((c_hi >> 8) & 0xFFu), float((c_hi >> 16) & 0xFFu), float(c_hi >> 24)};
+    // V values: byte j's two codes fall in block (4 sub + j) % NB
+    float vf[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = vm[i][j % NDM];
+      const float Dv = f16_bits_to_f32(uint16_t(w & 0xFFFFu)), Mv = f16_bits_to_f32(uint16_t(w >> 16));
+      vf[j] = fmaf(Dv, vc[j], Mv);
+      vf[j + 4] = fmaf(Dv, vc[j + 4], Mv);
+    }
     load_row(i, row + kDepth * RPB);
     float d[G];
 #pragma unroll
@@ -1186,7 +1217,6 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
       if (sc > mr[g]) {
         const float fo = __builtin_amdgcn_exp2f(m[g] - sc);
         l[g] *= fo;
-        sm[g] *= fo;
 #pragma unroll
         for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] *= fo;
         m[g] = sc;
@@ -1194,10 +1224,8 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
       }
       const float p = __builtin_amdgcn_exp2f(sc - m[g]);
       l[g] += p;
-      sm[g] = fmaf(p, Mv, sm[g]);
-      const float pd = p * Dv;
 #pragma unroll
-      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(pd, vf[e], acc[g][e]);
+      for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
     }
   };
   for (; rb + kDepth * RPB <= r1; rb += kDepth * RPB) {
@@ -1212,12 +1240,6 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
       step(i, rr);
     }
   }
-  // the V minimum's share goes to every element of the lane
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < kAttnLaneElems; ++e) acc[g][e] += sm[g];
-
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float mw = wave_max(m[g]);
@@ -1246,7 +1268,7 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][sub * 8 + e] = acc[g][e];
+      for (int e = 0; e < kAttnLaneElems; ++e) obuf[wv][g][vq_dim(4 * sub + (e & 3), e >> 2, HD)] = acc[g][e];
       if (sub == 0) s_L[wv][g] = l[g];
     }
   }
@@ -1272,6 +1294,289 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
     const int h = kvh * G + g;
     a.part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
     a.part_ml[((size_t)h * S + s) * 2 + 1] = L;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// q8q5 decode attention on MFMA (head_dim 64 or 128, at most 16 query heads per KV
+// head), 16-row tiles in k_attn_mfma's ring.  Scores: per 32-dim block ks,
+// S^T_ks = K_ks . Q^T on v_mfma_f32_16x16x32_f16 with the codes as fp16 1024 + u (u =
+// the stored code + 128; one byte permute per two codes) against the queries as fp16
+// (hi, lo) pairs scaled by 2^e per query; the block adds D_k (S^T_ks - 1152 sum_ks q),
+// the sum over the blocks is scaled back by 2^-e.  Values: O^T = V^T P^T on
+// v_mfma_f32_16x16x16bf16_1k, output tile t = (block b, half h) holding dims
+// 32 b + 16 h + (0..15): A = the tile's codes over the 16 rows as bf16 128 + c, B = P^T
+// with each row's weight times that row's D_v of block b, as bf16 (hi, lo); the
+// block's M_v and the 128 offset give a per-(query, block) term
+// sum_r p_r (M_v - 128 D_v) added at the end.  The lane holding query c16's scores of
+// rows 4 g4 + v is P^T's operand lane, and O^T's D layout keeps query c16 in the
+// lane's column, so the online softmax rescales O in place.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S) {
+  constexpr int NB = HD / 32;  // 32-dim blocks: the k steps of S, the V scale blocks
+  constexpr int NT = HD / 16;  // output tiles of O^T, t = 2 b + h
+  constexpr int R = kMfmaRing;
+  constexpr int STRIDE = 16 * kAttnWaves;
+  static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
+  __shared__ float so[kAttnWaves][16][HD + 4];
+  __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
+
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int G = a.n_head / a.n_head_kv;
+  const int T = a.T, nkv = a.n_head_kv, cap = a.cap;
+  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  if (r0 >= T) return;
+  if (a.kv_new && r1 == T) quantize_new_row<HD>(a, kvh);
+  const bool direct = S == 1;
+  const int rlast = r1 - 1;
+  const uint8_t* kreg = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* vreg = static_cast<const uint8_t*>(a.v_cache);
+  const size_t hr0 = (size_t)kvh * cap, all = (size_t)nkv * cap;
+  const uint8_t* Kc = kreg + hr0 * HD;                           // codes [row][HD]
+  const uint8_t* Ks = kreg + all * HD + hr0 * NB * 2;            // fp16 scales [row][NB]
+  const uint8_t* Vn = vreg + hr0 * (HD / 2) + c16 * NB;          // lane c16's nibble bytes
+  const uint8_t* Vh = vreg + all * (HD / 2) + hr0 * (HD / 8) + ((c16 * NB) >> 2);
+  const uint8_t* Vd = vreg + all * (HD / 2 + HD / 8) + hr0 * NB * 4;  // (D, M) [row][NB]
+  const int hsh = (c16 * NB) & 3;  // the lane's first bit in its high-bit byte
+
+  // ring slot i: K codes of row tb + c16 (dims 32 ks + 8 g4 ..); the K scales, V
+  // codes and V (D, M) of rows tb + 4 g4 + v; row indices clamped to r1 - 1
+  uint2 kq[R][NB];
+  uint32_t kd[R][4][(NB + 1) / 2], vn[R][4], vh[R][4], dm[R][4][NB];
+  // the K part of a slot is refilled once its scores are computed, the V part once
+  // its products are issued (no copies of a slot's data are held)
+  auto load_k = [&](int i, int tb) {
+    const int rk = min(tb + c16, rlast);
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks)
+      kq[i][ks] = *reinterpret_cast<const uint2*>(Kc + (size_t)rk * HD + 32 * ks + 8 * g4);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const size_t rv = (size_t)min(tb + 4 * g4 + v, rlast);
+      if constexpr (NB == 4) {
+        const uint2 w = *reinterpret_cast<const uint2*>(Ks + rv * 8);
+        kd[i][v][0] = w.x;
+        kd[i][v][1] = w.y;
+      } else {
+        kd[i][v][0] = *reinterpret_cast<const uint32_t*>(Ks + rv * 4);
+      }
+    }
+  };
+  auto load_v = [&](int i, int tb) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const size_t rv = (size_t)min(tb + 4 * g4 + v, rlast);
+      if constexpr (NB == 4) {
+        vn[i][v] = *reinterpret_cast<const uint32_t*>(Vn + rv * (HD / 2));
+        const uint4 d = *reinterpret_cast<const uint4*>(Vd + rv * 16);
+        dm[i][v][0] = d.x; dm[i][v][1] = d.y; dm[i][v][2] = d.z; dm[i][v][3] = d.w;
+      } else {
+        vn[i][v] = *reinterpret_cast<const uint16_t*>(Vn + rv * (HD / 2));
+        const uint2 d = *reinterpret_cast<const uint2*>(Vd + rv * 8);
+        dm[i][v][0] = d.x; dm[i][v][1] = d.y;
+      }
+      vh[i][v] = Vh[rv * (HD / 8)];
+    }
+  };
+  auto load = [&](int i, int tb) {
+    load_k(i, tb);
+    load_v(i, tb);
+  };
+  const int tb0 = r0 + 16 * wv;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tb0 + i * STRIDE < r1) load(i, tb0 + i * STRIDE);
+
+  // query c16's dims 32 ks + 8 g4 .. + 7 with the base-2 score scale, times 2^e
+  // putting the query's largest value in [2^14, 2^15), as fp16 (hi, lo); columns
+  // past G are zero.  qs[ks]: the block's sum of (hi + lo) over its 32 dims.
+  const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  const bool qok = c16 < G;
+  float x[NB][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NB; ++ks) {
+    const float* qp = a.q + (size_t)(kvh * G + (qok ? c16 : 0)) * HD + 32 * ks + 8 * g4;
+    const float4 u = *reinterpret_cast<const float4*>(qp), w = *reinterpret_cast<const float4*>(qp + 4);
+    const float y[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[ks][e] = qok ? y[e] * scale : 0.f;
+      amax = fmaxf(amax, fabsf(x[ks][e]));
+    }
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  int ex = 0;
+  if (amax > 0.f) (void)frexpf(amax, &ex);
+  ex = max(ex, -100);  // 2^(15 - ex) stays finite
+  const float up = ldexpf(1.f, 15 - ex), down = ldexpf(1.f, ex - 15);
+  f16x8_t qh[NB], ql[NB];
+  float qs[NB];
+#pragma unroll
+  for (int ks = 0; ks < NB; ++ks) {
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float yv = x[ks][e] * up;
+      const _Float16 h = (_Float16)yv;
+      const _Float16 lo = (_Float16)(yv - (float)h);
+      qh[ks][e] = h;
+      ql[ks][e] = lo;
+      t += (float)h + (float)lo;
+    }
+    t += __shfl_xor(t, 16, kWave);
+    t += __shfl_xor(t, 32, kWave);
+    qs[ks] = 1152.f * t;
+  }
+  f32x4_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float cb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) cb[b] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  auto step = [&](int i, int tb) {
+    // scores of rows tb + 4 g4 + v for query c16 (times 2^e)
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks) {
+      const uint32_t c0 = kq[i][ks].x, c1 = kq[i][ks].y;
+      const uint32_t e4 = 0x64646464u;  // fp16 1024 + u: high byte 0x64 over the code
+      uint4 av;
+      av.x = __builtin_amdgcn_perm(e4, c0, 0x04010400u);
+      av.y = __builtin_amdgcn_perm(e4, c0, 0x04030402u);
+      av.z = __builtin_amdgcn_perm(e4, c1, 0x04010400u);
+      av.w = __builtin_amdgcn_perm(e4, c1, 0x04030402u);
+      const f16x8_t ka = __builtin_bit_cast(f16x8_t, av);
+      f32x4_t st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[ks], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[ks], st, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t w = kd[i][v][ks >> 1];
+        const float Dk = f16_bits_to_f32(uint16_t((ks & 1) ? (w >> 16) : (w & 0xFFFFu)));
+        acc[v] = fmaf(Dk, st[v] - qs[ks], acc[v]);
+      }
+    }
+    const bool refill = tb + R * STRIDE < r1;
+    if (refill) load_k(i, tb + R * STRIDE);
+    float sc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc[v] = (tb + 4 * g4 + v < r1) ? acc[v] * down : -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    float fo = 1.f;
+    if (mx > m + kRescale) {
+      fo = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+      m = mx;
+    }
+    float pr[4], ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      pr[v] = sc[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[v] - m);
+      ps += pr[v];
+    }
+    ps += __shfl_xor(ps, 16, kWave);
+    ps += __shfl_xor(ps, 32, kWave);
+    l = l * fo + ps;
+    if (__any(fo != 1.f)) {  // O^T's D layout: the lane's column is query c16
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[t][v] *= fo;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) cb[b] *= fo;
+    }
+    // V codes: byte b of clo / chi = the code of dim 32 b + c16 / 32 b + 16 + c16
+    uint32_t clo[4], chi[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t nb = vn[i][v];
+      const uint32_t hr = ((vh[i][v] >> hsh) & 0xFFu) * 0x01010101u;
+      clo[v] = (nb & 0x0F0F0F0Fu) | ((((hr & 0x08040201u) + 0x787C7E7Fu) & 0x80808080u) >> 3);
+      chi[v] = ((nb >> 4) & 0x0F0F0F0Fu) | ((((hr & 0x80402010u) + 0x00406070u) & 0x80808080u) >> 3);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // P^T for block b: each row's weight times its D_v, as bf16 (hi, lo)
+      bf16x4s_t ph, pl;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float Dv = f16_bits_to_f32(uint16_t(dm[i][v][b] & 0xFFFFu));
+        const float Mv = f16_bits_to_f32(uint16_t(dm[i][v][b] >> 16));
+        const float pv = pr[v] * Dv;
+        const __bf16 h = (__bf16)pv;
+        ph[v] = __builtin_bit_cast(short, h);
+        pl[v] = __builtin_bit_cast(short, (__bf16)(pv - (float)h));
+        cb[b] = fmaf(pr[v], fmaf(-128.f, Dv, Mv), cb[b]);
+      }
+      const uint32_t sel = uint32_t(b) | (0x0Cu << 8) | (uint32_t(4 + b) << 16) | (0x0Cu << 24);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t* X = hh ? chi : clo;
+        uint2 w;
+        w.x = __builtin_amdgcn_perm(X[1], X[0], sel) | 0x43004300u;  // rows 0, 1 as bf16 128 + c
+        w.y = __builtin_amdgcn_perm(X[3], X[2], sel) | 0x43004300u;  // rows 2, 3
+        const bf16x4s_t av = __builtin_bit_cast(bf16x4s_t, w);
+        const int t = 2 * b + hh;
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, o[t], 0, 0, 0);
+      }
+    }
+    if (refill) load_v(i, tb + R * STRIDE);
+  };
+  int tb = tb0;
+  for (; tb + (R - 1) * STRIDE < r1; tb += R * STRIDE) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) step(i, tb + i * STRIDE);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (tb + i * STRIDE < r1) step(i, tb + i * STRIDE);
+
+  // the per-(query, block) terms over the lane group's rows, then the waves merge
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    cb[b] += __shfl_xor(cb[b], 16, kWave);
+    cb[b] += __shfl_xor(cb[b], 32, kWave);
+  }
+  if (g4 == 0) {
+    sm[wv][c16] = m;
+    sl[wv][c16] = l;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) so[wv][c16][16 * t + 4 * g4 + v] = o[t][v] + cb[t >> 1];
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * HD; i += blockDim.x) {
+    const int q = i / HD, dd = i - q * HD;
+    float Mb = sm[0][q];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, sm[w][q]);
+    float v = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float f = (Mb == -INFINITY || sm[w][q] == -INFINITY) ? 0.f : exp2f(sm[w][q] - Mb);
+      v = fmaf(f, so[w][q][dd], v);
+      Ls = fmaf(f, sl[w][q], Ls);
+    }
+    const int h = kvh * G + q;
+    if (direct) {
+      a.out[(size_t)h * HD + dd] = v / Ls;
+    } else {
+      a.part_o[((size_t)h * S + s) * HD + dd] = v;
+      if (dd == 0) {
+        a.part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
+        a.part_ml[((size_t)h * S + s) * 2 + 1] = Ls;
+      }
+    }
   }
 }
 
@@ -1411,8 +1716,8 @@ static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int
 // longer chunks than the VALU kernel's, since a block's fixed work (queries, merge)
 // is larger (at 32K rows over 8 KV heads: 1024-row chunks 23.7 us, 512 27.8, 256 35.2)
 
-static void pick_split_mfma(int T, int n_head_kv, int* chunk, int* S) {
-  const int blocks = attn_single_blocks();
+static void pick_split_mfma(int T, int n_head_kv, int* chunk, int* S, int blocks = 0) {
+  if (blocks <= 0) blocks = attn_single_blocks();
   const int target = n_head_kv >= blocks ? 1 : blocks / n_head_kv;
   constexpr int rpb = 16 * kAttnWaves;
   int c = (T + target - 1) / target;
@@ -1696,6 +2001,21 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (!a.kv_q && attn_on_mfma(a.head_dim, a.kv_f32, G)) pick_split_mfma(a.T, a.n_head_kv, &chunk, &S);
   else pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   if (a.kv_q) {
+    if (a.head_dim <= 128 && G <= 16 && !attn_valu()) {
+      // twice the blocks of the bf16 kernel: two waves a SIMD hide more of the
+      // decode's latency (32767 rows, 40/8 heads: 40.7 us against 43.9 with 256,
+      // attention and combine)
+      pick_split_mfma(a.T, a.n_head_kv, &chunk, &S, std::getenv("EAGLE3_ATTN_BLOCKS") ? 0 : kAttnQmBlocks);
+      dim3 grid(S, a.n_head_kv), block(64 * kAttnWaves);
+      if (a.head_dim == 64) hipLaunchKernelGGL(k_attn_qm<64>, grid, block, 0, s, a, chunk, S);
+      else if (a.head_dim == 128) hipLaunchKernelGGL(k_attn_qm<128>, grid, block, 0, s, a, chunk, S);
+      else return hipErrorInvalidValue;
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess || S == 1) return e;
+      hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(a.head_dim), 0, s, a.part_o, a.part_ml, S,
+                         a.head_dim, a.out);
+      return hipGetLastError();
+    }
     switch (a.head_dim) {
       case 64: return launch_q_hd<64>(a, G, chunk, S, s);
       case 128: return launch_q_hd<128>(a, G, chunk, S, s);

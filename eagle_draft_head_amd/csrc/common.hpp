@@ -158,34 +158,61 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// s_waitcnt vmcnt(N), the other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 constexpr int kArgmaxBatch = 8;  // candidate loads per thread in flight together
+
+// One thread's batch of argmax candidates: kArgmaxBatch (value, index, carried
+// value) triples, strided by the block size from b0.
+struct ArgmaxBatch {
+  float v[kArgmaxBatch];
+  int ix[kArgmaxBatch], t[kArgmaxBatch];
+};
+
+__device__ __forceinline__ void argmax_load(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+                                            const int32_t* __restrict__ pt, int count, int b0,
+                                            ArgmaxBatch& c) {
+#pragma unroll
+  for (int j = 0; j < kArgmaxBatch; ++j) {
+    const int b = b0 + int(threadIdx.x) + j * int(blockDim.x);
+    const bool in = b < count;
+    c.v[j] = in ? pv[b] : -INFINITY;
+    c.ix[j] = in ? pi[b] : 0x7FFFFFFF;
+    c.t[j] = (in && pt) ? pt[b] : 0;
+  }
+}
 
 // Argmax over `count` (value, index) candidates, the lower index winning a tie;
 // every thread gets the winning index.  When pt is given, pt[c] is a value
 // carried with candidate c and *tok receives the winner's.  Each thread's
 // candidates are loaded kArgmaxBatch at a time, so a block of T threads covers
-// kArgmaxBatch * T candidates per memory round trip.  sv/si/st: LDS, one slot
-// per wave (st only read when pt is given).
-__device__ __forceinline__ int block_argmax_carry(const float* __restrict__ pv,
-                                                  const int32_t* __restrict__ pi,
-                                                  const int32_t* __restrict__ pt, int count,
-                                                  float* sv, int* si, int* st, int* tok) {
+// kArgmaxBatch * T candidates per memory round trip; `first` is the batch from
+// 0, already loaded by argmax_load (a caller can issue it ahead of other loads).
+// sv/si/st: LDS, one slot per wave (st only read when pt is given).  MORE = false:
+// the caller guarantees count <= kArgmaxBatch * blockDim.x (no further batches,
+// and no loop, whose loads would make the compiler wait for every load in flight).
+template <bool MORE = true>
+__device__ __forceinline__ int block_argmax_from(const ArgmaxBatch& first, const float* __restrict__ pv,
+                                                 const int32_t* __restrict__ pi,
+                                                 const int32_t* __restrict__ pt, int count, float* sv,
+                                                 int* si, int* st, int* tok) {
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF, bt = 0;
-  for (int b0 = 0; b0 < count; b0 += kArgmaxBatch * int(blockDim.x)) {
-    float v[kArgmaxBatch];
-    int ix[kArgmaxBatch], t[kArgmaxBatch];
 #pragma unroll
-    for (int j = 0; j < kArgmaxBatch; ++j) {
-      const int b = b0 + int(threadIdx.x) + j * int(blockDim.x);
-      const bool in = b < count;
-      v[j] = in ? pv[b] : -INFINITY;
-      ix[j] = in ? pi[b] : 0x7FFFFFFF;
-      t[j] = (in && pt) ? pt[b] : 0;
-    }
+  for (int j = 0; j < kArgmaxBatch; ++j)
+    if (better(first.v[j], first.ix[j], bv, bi)) { bv = first.v[j]; bi = first.ix[j]; bt = first.t[j]; }
+  if constexpr (MORE)
+  for (int b0 = kArgmaxBatch * int(blockDim.x); b0 < count; b0 += kArgmaxBatch * int(blockDim.x)) {
+    ArgmaxBatch c;
+    argmax_load(pv, pi, pt, count, b0, c);
 #pragma unroll
     for (int j = 0; j < kArgmaxBatch; ++j)
-      if (better(v[j], ix[j], bv, bi)) { bv = v[j]; bi = ix[j]; bt = t[j]; }
+      if (better(c.v[j], c.ix[j], bv, bi)) { bv = c.v[j]; bi = c.ix[j]; bt = c.t[j]; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -213,6 +240,15 @@ __device__ __forceinline__ int block_argmax_carry(const float* __restrict__ pv,
   __syncthreads();
   if (tok) *tok = bt;
   return bi;
+}
+
+__device__ __forceinline__ int block_argmax_carry(const float* __restrict__ pv,
+                                                  const int32_t* __restrict__ pi,
+                                                  const int32_t* __restrict__ pt, int count,
+                                                  float* sv, int* si, int* st, int* tok) {
+  ArgmaxBatch c;
+  argmax_load(pv, pi, pt, count, 0, c);
+  return block_argmax_from(c, pv, pi, pt, count, sv, si, st, tok);
 }
 
 __device__ __forceinline__ int block_argmax(const float* __restrict__ pv,
@@ -254,14 +290,28 @@ struct KvqAt {
   }
 };
 
-// Quantize and store one value per lane.  The lanes come in aligned groups of 32
-// holding dims [32b, 32b + 32) of one head row, K (q8_0) or V (q5_1); every lane of
-// the wave calls it (the group reductions are shuffles); `on` lanes store.
+// q5_1 V code placement.  With NB = hd / 32 blocks, dim d = 32 b + 16 h + c (b < NB,
+// h < 2, c < 16) keeps its low 4 bits in nibble h of byte B = c NB + b of the row's
+// nibble array and its bit 4 in bit (B % 4) + 4 h of high-bit byte B / 4: the codes a
+// lane c of an MFMA tile over dims 16 t + c needs are one contiguous run of bytes.
+__device__ __forceinline__ int vq_byte(int dim, int hd) { return (dim & 15) * (hd >> 5) + (dim >> 5); }
+__device__ __forceinline__ int vq_half(int dim) { return (dim >> 4) & 1; }
+// the dim whose code sits in nibble h of byte B
+__device__ __forceinline__ int vq_dim(int B, int h, int hd) {
+  const int nb = hd >> 5, c = B / nb;
+  return 32 * (B - c * nb) + 16 * h + c;
+}
+
+// Quantize one value per lane.  The lanes come in aligned groups of 32 holding dims
+// [32b, 32b + 32) of one head row, K (q8_0) or V (q5_1); every lane of the wave calls
+// it (the group reductions are shuffles); `on` lanes store.  K: the code and the
+// block's scale are stored.  V: the block's (D, M) are stored and the 5-bit code is
+// returned; kvq_pack_v writes a head row's codes once all of them are known.
 // q8_0: D = fp16(max|x| / 127), q = clamp(rint(x / D), -127, 127), stored q + 128;
 // q5_1: D = fp16((max - min) / 31), M = fp16(min), q = clamp(rint((x - M) / D), 0, 31);
 // D == 0 gives code 0.  Subtraction and divisions are IEEE fp32.
-__device__ __forceinline__ void kvq_store(float x, bool is_k, int dim, uint8_t* kreg, uint8_t* vreg,
-                                          const KvqAt& at, bool on) {
+__device__ __forceinline__ uint32_t kvq_quant(float x, bool is_k, int dim, uint8_t* kreg, uint8_t* vreg,
+                                              const KvqAt& at, bool on) {
   float amax = fabsf(x), mn = x, mx = x;
 #pragma unroll
   for (int o = 1; o < 32; o <<= 1) {
@@ -269,7 +319,6 @@ __device__ __forceinline__ void kvq_store(float x, bool is_k, int dim, uint8_t* 
     mn = fminf(mn, __shfl_xor(mn, o, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   }
-  const int j = dim & 7;
   if (is_k) {
     const uint16_t Db = f32_to_f16_bits(__fdiv_rn(amax, 127.f));
     const float D = f16_bits_to_f32(Db);
@@ -278,23 +327,35 @@ __device__ __forceinline__ void kvq_store(float x, bool is_k, int dim, uint8_t* 
       kreg[at.k_code + dim] = uint8_t(int(q) + 128);
       if ((dim & 31) == 0) *reinterpret_cast<uint16_t*>(kreg + at.k_scale + (dim >> 5) * 2) = Db;
     }
-  } else {
-    const uint16_t Db = f32_to_f16_bits(__fdiv_rn(mx - mn, 31.f));
-    const uint16_t Mb = f32_to_f16_bits(mn);
-    const float D = f16_bits_to_f32(Db), M = f16_bits_to_f32(Mb);
-    const float qf = D > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x - M, D)), 0.f), 31.f) : 0.f;
-    const uint32_t q = uint32_t(qf);
-    // dims j and j + 4 of a group of 8 share a nibble byte; the 8 high bits one byte
-    const uint32_t partner = __shfl_xor(q, 4, kWave);
-    uint32_t hb = (q >> 4) << j;
-    hb |= __shfl_xor(hb, 1, kWave);
-    hb |= __shfl_xor(hb, 2, kWave);
-    hb |= __shfl_xor(hb, 4, kWave);
-    if (on) {
-      if (j < 4) vreg[at.v_nib + (dim >> 3) * 4 + j] = uint8_t((q & 15u) | ((partner & 15u) << 4));
-      if (j == 0) vreg[at.v_hi + (dim >> 3)] = uint8_t(hb);
-      if ((dim & 31) == 0)
-        *reinterpret_cast<uint32_t*>(vreg + at.v_dm + (dim >> 5) * 4) = uint32_t(Db) | (uint32_t(Mb) << 16);
+    return 0u;
+  }
+  const uint16_t Db = f32_to_f16_bits(__fdiv_rn(mx - mn, 31.f));
+  const uint16_t Mb = f32_to_f16_bits(mn);
+  const float D = f16_bits_to_f32(Db), M = f16_bits_to_f32(Mb);
+  const float qf = D > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x - M, D)), 0.f), 31.f) : 0.f;
+  if (on && (dim & 31) == 0)
+    *reinterpret_cast<uint32_t*>(vreg + at.v_dm + (dim >> 5) * 4) = uint32_t(Db) | (uint32_t(Mb) << 16);
+  return uint32_t(qf);
+}
+
+// Write the nibble and high-bit bytes of one V head row from its 5-bit codes
+// (codes[dim], dim < hd, e.g. in LDS); threads tid, tid + nthr, ... each write whole
+// bytes.
+__device__ __forceinline__ void kvq_pack_v(const uint8_t* codes, int hd, uint8_t* vreg, const KvqAt& at, int tid,
+                                           int nthr) {
+  for (int B = tid; B < hd / 2 + hd / 8; B += nthr) {
+    if (B < hd / 2) {
+      const uint32_t lo = codes[vq_dim(B, 0, hd)], hi = codes[vq_dim(B, 1, hd)];
+      vreg[at.v_nib + B] = uint8_t((lo & 15u) | ((hi & 15u) << 4));
+    } else {
+      const int k = B - hd / 2;  // high bits of nibble bytes 4k .. 4k + 3
+      uint32_t hb = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hb |= ((uint32_t(codes[vq_dim(4 * k + j, 0, hd)]) >> 4) & 1u) << j;
+        hb |= ((uint32_t(codes[vq_dim(4 * k + j, 1, hd)]) >> 4) & 1u) << (j + 4);
+      }
+      vreg[at.v_hi + k] = uint8_t(hb);
     }
   }
 }

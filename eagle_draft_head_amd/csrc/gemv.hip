@@ -519,13 +519,16 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_encode
 constexpr int kQkvERegs = 8;  // float4 chunks of the embedding row held per thread
 
 // finish the previous step (argmax over the lm_head candidates, d2t; the
-// candidates' target ids come with them when prev_tok is given) or read the
-// token; every thread of the block calls it and gets the token
-__device__ __forceinline__ int qkv_token(const QkvArgs& a, float* sv, int* si, int* st) {
+// candidates' target ids come with them when prev_tok is given) or take the
+// boundary token tok0; `first` is the candidates' first batch, already loaded;
+// every thread of the block calls it and gets the token
+template <bool MORE = true>
+__device__ __forceinline__ int qkv_token_from(const QkvArgs& a, const ArgmaxBatch& first, int tok0, float* sv,
+                                              int* si, int* st) {
   int tok;
   if (a.prev_count > 0) {
     int bt;
-    int bi = block_argmax_carry(a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, sv, si, st, &bt);
+    int bi = block_argmax_from<MORE>(first, a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, sv, si, st, &bt);
     const bool nan = bi < 0 || bi >= a.dv;  // every logit NaN
     if (nan) tok = a.d2t[0];
     else tok = a.prev_tok ? bt : bi + a.d2t[bi];
@@ -535,13 +538,28 @@ __device__ __forceinline__ int qkv_token(const QkvArgs& a, float* sv, int* si, i
       if (nan) atomicOr(a.status, kStatusNanLogits);
     }
   } else {
-    tok = *a.tok;
+    tok = tok0;
   }
   if (tok < 0 || tok >= a.vocab) {  // reads the nearest row, and says so
     if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.status, kStatusBadToken);
     tok = min(max(tok, 0), a.vocab - 1);
   }
   return tok;
+}
+
+// the loads qkv_token_from needs: the candidates' first batch or the boundary token
+__device__ __forceinline__ int qkv_token_load(const QkvArgs& a, ArgmaxBatch& first) {
+  if (a.prev_count > 0) {
+    argmax_load(a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, 0, first);
+    return 0;
+  }
+  return *a.tok;
+}
+
+__device__ __forceinline__ int qkv_token(const QkvArgs& a, float* sv, int* si, int* st) {
+  ArgmaxBatch first;
+  const int tok0 = qkv_token_load(a, first);
+  return qkv_token_from(a, first, tok0, sv, si, st);
 }
 
 // the fused epilogue of a wave's R rows: 1/rms per half, NeoX rotation of q/k
@@ -611,23 +629,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   float sg = sum_partials(a.g_ssq, a.g_ssq_count);
   const int tok = qkv_token(a, sv, si, st);
   __syncthreads();  // hidden half staged
-  if (a.tok_tab) {
-    // embedding half from the token table: the wave's rows of the token's entry
-    float acc_e[R], acc_g[R];
-    const float* trow = a.tok_tab + (size_t)tok * N;
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc_e[r] = trow[min(row0 + r, N - 1)];
-    const float se = a.tok_ss[tok];
-    if (issued) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, wpf, acc_g);
-    else if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs + n, acc_g);
-    float zero = 0.f;
-    block_sum2(zero, sg, red);  // every wave takes part
-    if (row0 >= N) return;
-    const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
-    const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
-    qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
-    return;
-  }
   // the embedding row and input_layernorm go to registers; they land while the
   // hidden half streams
   const uint2* e4 = reinterpret_cast<const uint2*>(a.embed + (size_t)tok * n);
@@ -666,6 +667,64 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv(QkvArgs a) {
   __syncthreads();
   if (row0 < N) rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, 0, n, xs, acc_e);
   block_sum2(se, sg, red);  // every wave takes part
+  if (row0 >= N) return;
+  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
+  const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+  qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+}
+
+constexpr int kQkvGRegs = 5;  // float4 chunks of the hidden half a thread stages at once
+
+// k_qkv with the token table: the table row stands for the embedding half, so only
+// the hidden half of W_qkv streams.  Wave loads complete in issue order, so the
+// loads the token depends on (the previous step's candidates, one batch of them,
+// or the boundary token) go out before the weights: the token is known, and its
+// table row and the hidden-half activations requested, while the weights are
+// still in flight.  ISSUE: the first U chunk steps of the weights go out before
+// the prologue (K / 8 >= 64 U; rows past N repeat the last row).  MORE: more
+// candidates than one batch (the later batches load after the weights).
+template <int WAVES, int R, int U, bool ISSUE, bool MORE>
+__global__ __launch_bounds__(64 * WAVES) void k_qkv_tab(QkvArgs a) {
+  static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
+  extern __shared__ float xs[];  // [0, n): hidden half
+  __shared__ float red[32];
+  __shared__ float sv[16];
+  __shared__ int si[16], st[16];
+  const int n = a.n;
+  const int N = (a.n_head + 2 * a.n_head_kv) * a.head_dim;
+  const int wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+
+  ArgmaxBatch first;
+  const int tok0 = qkv_token_load(a, first);
+  uint4 wpf[U][R];
+  if constexpr (ISSUE) rows_issue<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, wpf);
+  const int tok = qkv_token_from<MORE>(a, first, tok0, sv, si, st);
+  float acc_e[R], acc_g[R];
+  const float* trow = a.tok_tab + (size_t)tok * N;
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc_e[r] = trow[min(row0 + r, N - 1)];
+  const float se = a.tok_ss[tok];
+  // the hidden half: all of a thread's loads go out together (clamped indices; a
+  // clamped store rewrites the last chunk with its own value), so it lands one
+  // round trip after the weights at most
+  {
+    const float4* g4 = reinterpret_cast<const float4*>(a.gw);
+    float4* x4 = reinterpret_cast<float4*>(xs);
+    const int n4 = n >> 2;
+    float4 gr[kQkvGRegs];
+#pragma unroll
+    for (int j = 0; j < kQkvGRegs; ++j) gr[j] = g4[min(int(threadIdx.x + j * blockDim.x), n4 - 1)];
+#pragma unroll
+    for (int j = 0; j < kQkvGRegs; ++j) x4[min(int(threadIdx.x + j * blockDim.x), n4 - 1)] = gr[j];
+    for (int i = threadIdx.x + kQkvGRegs * blockDim.x; i < n4; i += blockDim.x) x4[i] = g4[i];
+  }
+  float sg = sum_partials(a.g_ssq, a.g_ssq_count);
+  __syncthreads();  // hidden half staged
+  if constexpr (ISSUE) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs, wpf, acc_g);
+  else rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs, acc_g);
+  float zero = 0.f;
+  block_sum2(zero, sg, red);  // every wave takes part
   if (row0 >= N) return;
   const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
   const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
@@ -1176,7 +1235,19 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
       E3_LDS_ALLOW((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), xb + 2 * q_vec_bytes(a.n));        \
       E3_LAUNCH((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), dim3(i4_grid(ceil_div(N, WV * RR))), \
                          dim3(64 * WV), xb + 2 * q_vec_bytes(a.n), s, a);                  \
-    } else                                                                                 \
+    } else if (a.tok_tab) {                                                                \
+      const bool iss = (a.n >> 3) >= 64 * UU, more = a.prev_count > kArgmaxBatch * 64 * WV;  \
+      if (iss && !more)                                                                    \
+        E3_LAUNCH((k_qkv_tab<WV, (RR < 2 ? 2 : RR), UU, true, false>), dim3(ceil_div(N, WV * RR)), \
+                  dim3(64 * WV), xb / 2, s, a);                                            \
+      else if (iss)                                                                        \
+        E3_LAUNCH((k_qkv_tab<WV, (RR < 2 ? 2 : RR), UU, true, true>), dim3(ceil_div(N, WV * RR)), \
+                  dim3(64 * WV), xb / 2, s, a);                                            \
+      else                                                                                 \
+        E3_LAUNCH((k_qkv_tab<WV, (RR < 2 ? 2 : RR), UU, false, true>), dim3(ceil_div(N, WV * RR)), \
+                  dim3(64 * WV), xb / 2, s, a);                                            \
+    }                                                                                      \
+    else                                                                                   \
       E3_LAUNCH((k_qkv<WV, (RR < 2 ? 2 : RR), UU>), dim3(ceil_div(N, WV * RR)),   \
                          dim3(64 * WV), xb, s, a);                                         \
     break;

@@ -181,13 +181,18 @@ struct BatchRows {
 // ---- attention over the draft KV (split over context, LSE combine) ----
 // ---- quantized draft KV (EAGLE3_KV_Q8Q5) ----
 // A sequence's K region holds, in bytes: codes [nkv][cap][hd] (q8_0 code + 128), then
-// fp16 scales [nkv][cap][hd / 32].  Its V region: code nibbles [nkv][cap][hd / 2] (per
-// 8 dims, byte j holds dim j's low 4 bits and dim j + 4's in its high half), high bits
-// [nkv][cap][hd / 8] (bit j of byte c is bit 4 of dim 8c + j), then (D, M) fp16 pairs
-// [nkv][cap][hd / 32] (one u32, D in the low half).  Both regions are
-// kvq_region_bytes long: 34 bytes per 32 K values and 24 per 32 V values, as in the
-// pages' block formats, with the V region padded to the K region's size.
-inline size_t kvq_region_bytes(int nkv, int cap, int hd) { return size_t(nkv) * cap * (hd / 32) * 34; }
+// fp16 scales [nkv][cap][hd / 32].  Its V region: code nibbles [nkv][cap][hd / 2], high
+// bits [nkv][cap][hd / 8], then (D, M) fp16 pairs [nkv][cap][hd / 32] (one u32, D in
+// the low half).  Within a row, with NB = hd / 32, dim 32 b + 16 h + c (c < 16) keeps
+// its low 4 bits in nibble h of byte c NB + b and its bit 4 in bit (B % 4) + 4 h of
+// high-bit byte B / 4, B = c NB + b (common.hpp vq_byte): an MFMA lane c reads its
+// dims 16 t + c as one run of NB bytes.  Both regions are kvq_region_bytes long: 34
+// bytes per 32 K values and 24 per 32 V values, as in the pages' block formats, with
+// the V region padded to the K region's size rounded up to 256 bytes (so the V arrays
+// start 16-byte aligned).
+inline size_t kvq_region_bytes(int nkv, int cap, int hd) {
+  return (size_t(nkv) * cap * (hd / 32) * 34 + 255) / 256 * 256;
+}
 
 struct AttnArgs {
   const float* q;          // [n_head * hd], roped

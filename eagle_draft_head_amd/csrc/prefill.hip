@@ -371,7 +371,8 @@ __global__ __launch_bounds__(256) void k_tf_store(const float* __restrict__ P, i
 
 // k_tf_store for quantized regions: a block's 256 pairs are 512 consecutive values of
 // the [k | v] row, i.e. whole heads (head_dim divides 512); they are rotated into
-// LDS at their final dims, then quantized 32 dims at a time (one value per lane).
+// LDS at their final dims, then quantized 32 dims at a time (one value per lane),
+// and the V heads' codes packed into their nibble and high-bit bytes.
 __global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P, int splits,
                                                     size_t p_split, const StoreSegs segs, int nkv,
                                                     int hd, int rope_dim,
@@ -379,6 +380,7 @@ __global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P,
                                                     uint8_t* __restrict__ kv, size_t seq_bytes,
                                                     int cap, float p_scale) {
   __shared__ float srow[512];
+  __shared__ uint8_t vcode[512];
   const int t = segs.row0[0] + blockIdx.x;
   int sg = 0;
   while (sg + 1 < segs.n && t >= segs.row0[sg + 1]) ++sg;
@@ -420,7 +422,14 @@ __global__ __launch_bounds__(256) void k_tf_store_q(const float* __restrict__ P,
     const int rr = is_k ? v : v - kvd;
     const int head = rr / hd, dim = rr - head * hd;
     const KvqAt at(nkv, cap, hd, on ? head : 0, pos);
-    kvq_store(on ? srow[i] : 0.f, is_k, dim, kreg, vreg, at, on);
+    vcode[i] = uint8_t(kvq_quant(on ? srow[i] : 0.f, is_k, dim, kreg, vreg, at, on));
+  }
+  __syncthreads();
+  for (int h0 = 0; h0 < 512; h0 += hd) {  // the block's V heads (uniform)
+    const int v = v0 + h0;
+    if (v < kvd || v >= 2 * kvd) continue;
+    const KvqAt at(nkv, cap, hd, (v - kvd) / hd, pos);
+    kvq_pack_v(vcode + h0, hd, vreg, at, threadIdx.x, blockDim.x);
   }
 }
 
@@ -458,9 +467,9 @@ __global__ __launch_bounds__(256) void k_kvq_read(const uint8_t* __restrict__ kr
   const KvqAt at(nkv, cap, hd, head, row0 + r);
   const float Dk = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(kreg + at.k_scale + (dim >> 5) * 2));
   ko[i] = Dk * float(int(kreg[at.k_code + dim]) - 128);
-  const int j = dim & 7;
-  const uint8_t nb = vreg[at.v_nib + (dim >> 3) * 4 + (j & 3)];
-  const uint32_t q = uint32_t(j < 4 ? (nb & 15) : (nb >> 4)) | (((uint32_t(vreg[at.v_hi + (dim >> 3)]) >> j) & 1u) << 4);
+  const int B = vq_byte(dim, hd), h = vq_half(dim);
+  const uint32_t nb = vreg[at.v_nib + B];
+  const uint32_t q = ((nb >> (4 * h)) & 15u) | (((uint32_t(vreg[at.v_hi + (B >> 2)]) >> ((B & 3) + 4 * h)) & 1u) << 4);
   const uint32_t dm = *reinterpret_cast<const uint32_t*>(vreg + at.v_dm + (dim >> 5) * 4);
   vo[i] = fmaf(f16_bits_to_f32(uint16_t(dm & 0xFFFFu)), float(q), f16_bits_to_f32(uint16_t(dm >> 16)));
 }
@@ -535,13 +544,6 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s) {
 template <int BK>
 __device__ __forceinline__ int tile_swizzle(int r) {
   return BK == 32 ? ((r >> 2) & 3) : ((r >> 1) & 7);
-}
-
-// s_waitcnt vmcnt(N), the other counters untouched
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {

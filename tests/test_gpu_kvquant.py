@@ -9,7 +9,8 @@
   attention block that quantizes a chain step's new row.
 * Chain rounds, rebuilds and round-local chains match the oracle run with the same
   quantized KV to the usual bar (ids where the top-2 margin allows, logits,
-  hidden states).
+  hidden states): head_dim 64 and 128 on the MFMA kernel (contexts of one split
+  and of many), 256 on the VALU kernel.
 """
 import numpy as np
 import pytest
@@ -25,6 +26,8 @@ from tests.gpu_harness import check_round, compare_round, say, to_dev_aux
 pytestmark = pytest.mark.gpu
 
 HD128 = small_variant(name="small-hd128", cfg_id=12, n_head=4, n_head_kv=2, head_dim=128, rope_dim=64)
+# head_dim 256 attends on the VALU kernel (the MFMA one covers 64 and 128)
+HD256 = small_variant(name="small-hd256", cfg_id=13, n_head=4, n_head_kv=2, head_dim=256, rope_dim=64)
 
 
 def _pair(cfg, max_ctx):
@@ -38,7 +41,7 @@ def _expect(k32, v32):
     return kvquant.k_stored(k32), kvquant.v_stored(v32)
 
 
-@pytest.mark.parametrize("cfg", [TINY, HD128], ids=["hd64", "hd128"])
+@pytest.mark.parametrize("cfg", [TINY, HD128, HD256], ids=["hd64", "hd128", "hd256"])
 def test_kvq_rows_bit_exact(cfg):
     L = 45  # an MFMA pass (> 16 rows) then a small pass (<= 16 rows)
     say(f"[kvq] {cfg.name}: append rows bit-exact")
@@ -83,10 +86,14 @@ def _kv_close(dr, orc, R):
 
 @pytest.mark.parametrize("cfg,L,rounds,gamma,local,i4", [(TINY, 63, 24, 3, False, False),
                                                          (HD128, 200, 12, 4, False, False),
+                                                         (HD128, 3001, 4, 4, False, False),
+                                                         (TINY, 1537, 4, 3, False, False),
+                                                         (HD256, 100, 8, 3, False, False),
                                                          (TINY, 63, 8, 4, True, False),
                                                          (TINY, 0, 4, 5, False, False),
                                                          (TINY, 63, 12, 3, False, True)],
-                         ids=["tiny", "hd128", "tiny-round-local", "empty", "tiny-int4-weights"])
+                         ids=["tiny", "hd128", "hd128-long", "tiny-long", "hd256", "tiny-round-local", "empty",
+                              "tiny-int4-weights"])
 def test_kvq_chain_parity(cfg, L, rounds, gamma, local, i4):
     say(f"[kvq] {cfg.name} L={L} rounds={rounds} gamma={gamma} local={local} int4={i4}")
     wd = gen.drafter_weights(cfg, device="cuda")
