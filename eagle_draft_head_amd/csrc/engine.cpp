@@ -155,6 +155,10 @@ struct eagle3_ctx {
   // LDS-tiled plans of the same projections (splits 0: K is not a multiple of 64,
   // the fragment-load GEMM above runs instead)
   e3::GemmPlan tp_enc{}, tp_qkv{}, tp_o{}, tp_gu{}, tp_d{}, tp_lm{};
+  // step-tiled copies of the projections those plans stream (e3::launch_tile_weights;
+  // null where the plan is the fragment-load GEMM)
+  uint16_t *bt_enc = nullptr, *bt_qkv = nullptr, *bt_o = nullptr, *bt_gu = nullptr, *bt_d = nullptr,
+           *bt_lm = nullptr;
   int b_ncand = 0;  // lm_head candidates per batch row
 
   e3::Ledger ledger;
@@ -548,6 +552,16 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     c->tp_gu = tplan(2 * ff, n);
     c->tp_d = tplan(n, ff);
     c->tp_lm = tplan(dv, n);
+    auto tiled = [&](uint16_t** t, const e3::GemmPlan& p, int64_t N, int64_t K) -> int {
+      if (p.splits) E3_TRY(dalloc(c, t, e3::tiled_weight_elems(int(N), int(K))));
+      return EAGLE3_OK;
+    };
+    E3_TRY(tiled(&c->bt_enc, c->tp_enc, n, 3 * n));
+    E3_TRY(tiled(&c->bt_qkv, c->tp_qkv, N_qkv, 2 * n));
+    E3_TRY(tiled(&c->bt_o, c->tp_o, n, qd));
+    E3_TRY(tiled(&c->bt_gu, c->tp_gu, 2 * ff, n));
+    E3_TRY(tiled(&c->bt_d, c->tp_d, n, ff));
+    E3_TRY(tiled(&c->bt_lm, c->tp_lm, dv, n));
     // lm_head candidates per row: one per 128 weight rows from the fused epilogue of an
     // unsplit skinny GEMM, one per 2048 columns from the partials otherwise
     c->b_ncand = c->tp_lm.splits == 1 ? e3::sgemm_tiles(int(dv))
@@ -672,6 +686,18 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
                                    rows, int(N_qkv), int(n), p, s),
               "token table gemm");
     }
+  }
+  {  // the batched projections' step-tiled weights (after the repacks)
+    auto tile = [&](uint16_t* t, const uint16_t* w, int64_t N, int64_t K) -> int {
+      if (t) E3_TRYH(e3::launch_tile_weights(w, int(N), int(K), t, s), "tile weights");
+      return EAGLE3_OK;
+    };
+    E3_TRY(tile(c->bt_enc, c->w_fc, n, 3 * n));
+    E3_TRY(tile(c->bt_qkv, c->w_qkv, N_qkv, 2 * n));
+    E3_TRY(tile(c->bt_o, c->w_o, n, qd));
+    E3_TRY(tile(c->bt_gu, c->w_gu, 2 * ff, n));
+    E3_TRY(tile(c->bt_d, c->w_d, n, ff));
+    E3_TRY(tile(c->bt_lm, c->w_lm, dv, n));
   }
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
     c->i4 = true;
@@ -1150,11 +1176,12 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
     // a projection into the split-K partials b_P [splits][32][N]: the LDS-tiled GEMM
     // over all 32 activation rows (rows past m are never read back), else the
     // fragment-load GEMM; *S receives the split count
-    auto proj = [&](const uint16_t* W, int N, int K, const uint16_t* xh, const uint16_t* xl,
-                    int ldx, int m, const e3::GemmPlan& tp, const e3::BGemmPlan& bp, int* S) {
-      if (tp.splits) {
+    auto proj = [&](const uint16_t* W, const uint16_t* Wt, int N, int K, const uint16_t* xh,
+                    const uint16_t* xl, int ldx, int m, const e3::GemmPlan& tp, const e3::BGemmPlan& bp,
+                    int* S) {
+      if (tp.splits) {  // the skinny GEMM over the step-tiled copy
         *S = tp.splits;
-        return e3::launch_gemm_bf16(xh, xl, ldx, W, K, c->b_P, kBatchRows, N, K, tp, s);
+        return e3::launch_gemm_tiled(xh, xl, ldx, Wt, c->b_P, kBatchRows, N, K, tp, s);
       }
       *S = bp.splits;
       return gemm(W, N, K, xh, xl, ldx, m, bp, e3::kBEpiPartial);
@@ -1163,7 +1190,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
     if (!stored) {
       ProfScope ps(c, 6, s);
       E3_HIP(c, e3::launch_bpack_aux(br, a0, a1, a2, n, c->bx_a_hi, c->bx_a_lo, c->bld_a, s), "pack");
-      E3_HIP(c, proj(c->w_fc, n, 3 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, br.m, c->tp_enc,
+      E3_HIP(c, proj(c->w_fc, c->bt_enc, n, 3 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, br.m, c->tp_enc,
                      c->bp_enc, &S_enc), "encode");
     }
     const int steps = br.geff[0];
@@ -1185,7 +1212,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
         ProfScope ps(c, 2, s);
         E3_HIP(c, e3::launch_bprep(pa, s), "prep");
         int S_qkv = 0;
-        E3_HIP(c, proj(c->w_qkv, Nqkv, 2 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->tp_qkv,
+        E3_HIP(c, proj(c->w_qkv, c->bt_qkv, Nqkv, 2 * n, c->bx_a_hi, c->bx_a_lo, c->bld_a, m, c->tp_qkv,
                        c->bp_qkv, &S_qkv), "qkv");
         e3::BQkvArgs qa{};
         qa.P = c->b_P; qa.S = S_qkv; qa.N = Nqkv; qa.br = br; qa.m = m; qa.step = j;
@@ -1211,7 +1238,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       {
         ProfScope ps(c, 4, s);
         int S_o = 0;
-        E3_HIP(c, proj(c->w_o, n, c->qd, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->tp_o, c->bp_o,
+        E3_HIP(c, proj(c->w_o, c->bt_o, n, c->qd, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->tp_o, c->bp_o,
                        &S_o), "o_proj");
         e3::BResidArgs ra{};
         ra.P = c->b_P; ra.S = S_o; ra.n = n; ra.m = m; ra.resid = c->b_G; ra.y = c->b_X1;
@@ -1223,13 +1250,13 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
         ProfScope ps(c, 1, s);
         if (c->tp_gu.splits == 1) {
           e3::BGemmArgs ga{};
-          ga.W = c->w_gu; ga.N = 2 * c->ff; ga.K = n; ga.Xhi = c->bx_z_hi; ga.Xlo = c->bx_z_lo;
+          ga.W = c->bt_gu; ga.tiled = 1; ga.N = 2 * c->ff; ga.K = n; ga.Xhi = c->bx_z_hi; ga.Xlo = c->bx_z_lo;
           ga.ldx = n; ga.m = m;
           ga.act_hi = c->bx_b_hi; ga.act_lo = c->bx_b_lo; ga.ld_act = c->bld_b;
           E3_HIP(c, e3::launch_sgemm_fused(ga, e3::kBEpiSilu, s), "gate/up");
         } else if (c->tp_gu.splits) {
-          E3_HIP(c, e3::launch_gemm_bf16(c->bx_z_hi, c->bx_z_lo, n, c->w_gu, n, c->b_P, kBatchRows,
-                                         2 * c->ff, n, c->tp_gu, s), "gate/up");
+          E3_HIP(c, e3::launch_gemm_tiled(c->bx_z_hi, c->bx_z_lo, n, c->bt_gu, c->b_P, kBatchRows,
+                                          2 * c->ff, n, c->tp_gu, s), "gate/up");
           E3_HIP(c, e3::launch_bact(c->b_P, c->tp_gu.splits, c->ff, m, c->bx_b_hi, c->bx_b_lo,
                                     c->bld_b, s), "silu");
         } else {
@@ -1240,7 +1267,7 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
       {
         ProfScope ps(c, 3, s);
         int S_d = 0;
-        E3_HIP(c, proj(c->w_d, n, c->ff, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->tp_d, c->bp_d,
+        E3_HIP(c, proj(c->w_d, c->bt_d, n, c->ff, c->bx_b_hi, c->bx_b_lo, c->bld_b, m, c->tp_d, c->bp_d,
                        &S_d), "down");
         // g_next; RMSNorm(g_next, norm) for the lm_head and RMSNorm(g_next, hidden_norm)
         // as the second half of the next step's QKV input
@@ -1257,14 +1284,14 @@ int draft_chain_batched(eagle3_ctx* c, int32_t n_seq, const int32_t* seq_ids,
         ProfScope ps(c, 0, s);
         if (c->tp_lm.splits == 1) {
           e3::BGemmArgs ga{};
-          ga.W = c->w_lm; ga.N = c->dv; ga.K = n; ga.Xhi = c->bx_h_hi; ga.Xlo = c->bx_h_lo;
+          ga.W = c->bt_lm; ga.tiled = 1; ga.N = c->dv; ga.K = n; ga.Xhi = c->bx_h_hi; ga.Xlo = c->bx_h_lo;
           ga.ldx = n; ga.m = m;
           ga.cand_v = c->b_cand_v; ga.cand_i = c->b_cand_i; ga.ncand = c->b_ncand;
           ga.logits = (dbg && dbg->logits) ? c->b_logits : nullptr;
           E3_HIP(c, e3::launch_sgemm_fused(ga, e3::kBEpiArgmax, s), "lm_head");
         } else if (c->tp_lm.splits) {
-          E3_HIP(c, e3::launch_gemm_bf16(c->bx_h_hi, c->bx_h_lo, n, c->w_lm, n, c->b_P, kBatchRows,
-                                         c->dv, n, c->tp_lm, s), "lm_head");
+          E3_HIP(c, e3::launch_gemm_tiled(c->bx_h_hi, c->bx_h_lo, n, c->bt_lm, c->b_P, kBatchRows,
+                                          c->dv, n, c->tp_lm, s), "lm_head");
           E3_HIP(c, e3::launch_bcand(c->b_P, c->tp_lm.splits, c->dv, m, c->b_cand_v, c->b_cand_i,
                                      (dbg && dbg->logits) ? c->b_logits : nullptr, s),
                  "lm_head candidates");

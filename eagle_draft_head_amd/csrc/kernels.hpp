@@ -265,6 +265,7 @@ struct BGemmArgs {
   int32_t* cand_i;
   int ncand;
   float* logits;           // kBEpiArgmax, optional: [32][N]
+  int tiled;               // W is the step-tiled copy (launch_tile_weights)
 };
 struct BGemmPlan {
   int variant, splits, kb, blocks;
@@ -436,6 +437,14 @@ GemmPlan gemm_plan(int M, int N, int K);
 hipError_t launch_gemm_bf16(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
                             int ldb, float* C, int M, int N, int K, const GemmPlan& plan,
                             hipStream_t s, bool f16 = false);
+// The skinny GEMM's step-tiled weight copy: T [ceil(N / 128)][K / 64][128][64] of W
+// [N][K] (K % 64 == 0; rows past N zero), tiled_weight_elems(N, K) elements; and the
+// split-activation GEMM of up to 32 rows over it (C as launch_gemm_bf16's, plan from
+// gemm_plan with bn 128)
+size_t tiled_weight_elems(int N, int K);
+hipError_t launch_tile_weights(const uint16_t* W, int N, int K, uint16_t* T, hipStream_t s);
+hipError_t launch_gemm_tiled(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* Bt, float* C,
+                             int M, int N, int K, const GemmPlan& plan, hipStream_t s);
 // the token table's build: ss[t] = sum E[t]^2; rows [r0, r0 + T) of w_in * E as bf16 (hi, lo)
 hipError_t launch_tok_ss(const uint16_t* E, int vocab, int n, float* ss, hipStream_t s);
 hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, int r0, int T, int n, uint16_t* A_hi,

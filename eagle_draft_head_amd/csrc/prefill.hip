@@ -689,7 +689,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_gemm(
 // 32 x 32 of C as 2 x 2 tiles of 16x16x32 MFMA.  One barrier per step: a buffer
 // is rewritten two steps after its last read, and every wave has passed the
 // barrier in between.  Refills past the last step re-read the last tile (in
-// bounds, never used).
+// bounds, never used).  TILED: B is the step-tiled copy of the weights
+// (launch_tile_weights: each block's [128 rows][64 k] step is one contiguous 16 KB
+// run), which the DRAM pages serve far better than 128 bytes from each of 128 rows
+// 8 KB or more apart (at M = 32: lm_head 55 -> 47 us, gate/up 47 -> 40, QKV 26 -> 22).
 constexpr int kSgRows = 128;
 constexpr int kSgBK = 64;
 constexpr int kSgDepth = 4;  // even: a step's LDS buffer is its parity
@@ -709,7 +712,7 @@ struct SgEpi {
   float* logits;      // kBEpiArgmax, optional: [m][N]
 };
 
-template <bool SPLIT, int EPI, bool F16 = false>
+template <bool SPLIT, int EPI, bool F16 = false, bool TILED = false>
 __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ A2, int lda,
                                                const uint16_t* __restrict__ B, int ldb,
@@ -733,7 +736,13 @@ __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
   const int lr = tid >> 3, lc = tid & 7;
   const uint16_t* wp[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) wp[q] = B + (size_t)min(n0 + lr + 32 * q, N - 1) * ldb + kb + 8 * lc;
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (TILED)  // ldb = K: K / 64 step tiles per 128-row block
+      wp[q] = B + ((size_t)n_t * (ldb / kSgBK) + kb / kSgBK) * (kSgRows * kSgBK) + (lr + 32 * q) * kSgBK + 8 * lc;
+    else
+      wp[q] = B + (size_t)min(n0 + lr + 32 * q, N - 1) * ldb + kb + 8 * lc;
+  }
+  constexpr size_t wstep = TILED ? size_t(kSgRows) * kSgBK : size_t(kSgBK);  // elements a step
   const size_t aoff = (size_t)min(lr, M - 1) * lda + kb + 8 * lc;
   f32x4 acc[2][2];
 #pragma unroll
@@ -747,9 +756,9 @@ __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
   u32x4 wreg[D][4], areg[D][NSA];  // native vectors: kept in registers
 #define E3_SG_ISSUE(I, ST)                                                                   \
   {                                                                                          \
-    const int k_ = min((ST), nsteps - 1) * kSgBK;                                            \
+    const int st_ = min((ST), nsteps - 1), k_ = st_ * kSgBK;                                 \
     _Pragma("unroll") for (int q = 0; q < 4; ++q) wreg[I][q] =                               \
-        *reinterpret_cast<const u32x4*>(wp[q] + k_);                                         \
+        *reinterpret_cast<const u32x4*>(wp[q] + st_ * wstep);                                \
     _Pragma("unroll") for (int h = 0; h < NSA; ++h) areg[I][h] =                             \
         *reinterpret_cast<const u32x4*>((h ? A2 : A) + aoff + k_);                           \
   }
@@ -885,12 +894,16 @@ __global__ __launch_bounds__(256) void k_sgemm(const uint16_t* __restrict__ A,
 
 static hipError_t launch_sgemm(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* B,
                                int ldb, float* C, int M, int N, int kper, int splits, hipStream_t s,
-                               bool f16) {
+                               bool f16, bool tiled = false) {
   if (M > 32 || kper % kSgBK) return hipErrorInvalidValue;
   const int nt = (N + kSgRows - 1) / kSgRows;
   dim3 grid((nt + 7) / 8 * 8, 1, splits);
   const SgEpi e{};
-  if (f16)
+  if (tiled) {
+    if (f16 || !A_lo || ldb != kper * splits) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_sgemm<true, kBEpiPartial, false, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb,
+                       C, M, N, kper, nt, e);
+  } else if (f16)
     hipLaunchKernelGGL((k_sgemm<false, kBEpiPartial, true>), grid, dim3(256), 0, s, A_hi, A_lo, lda, B, ldb, C,
                        M, N, kper, nt, e);
   else if (A_lo)
@@ -914,16 +927,59 @@ hipError_t launch_sgemm_fused(const BGemmArgs& a, int epi, hipStream_t s) {
   dim3 grid((nt + 7) / 8 * 8, 1, 1);
   if (epi == kBEpiSilu) {
     if (a.N % 2) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_sgemm<true, kBEpiSilu>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W, a.K,
-                       nullptr, kBatchRows, a.N, a.K, nt, e);
+    if (a.tiled)
+      hipLaunchKernelGGL((k_sgemm<true, kBEpiSilu, false, true>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W,
+                         a.K, nullptr, kBatchRows, a.N, a.K, nt, e);
+    else
+      hipLaunchKernelGGL((k_sgemm<true, kBEpiSilu>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W, a.K,
+                         nullptr, kBatchRows, a.N, a.K, nt, e);
   } else if (epi == kBEpiArgmax) {
     if (a.ncand < nt) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_sgemm<true, kBEpiArgmax>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W, a.K,
-                       nullptr, kBatchRows, a.N, a.K, nt, e);
+    if (a.tiled)
+      hipLaunchKernelGGL((k_sgemm<true, kBEpiArgmax, false, true>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx,
+                         a.W, a.K, nullptr, kBatchRows, a.N, a.K, nt, e);
+    else
+      hipLaunchKernelGGL((k_sgemm<true, kBEpiArgmax>), grid, dim3(256), 0, s, a.Xhi, a.Xlo, a.ldx, a.W, a.K,
+                         nullptr, kBatchRows, a.N, a.K, nt, e);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// The step-tiled copy of a weight matrix W [N][K] (K % 64 == 0) for the skinny GEMM:
+// T [ceil(N / 128)][K / 64][128][64], rows past N zero.  One thread per 16 bytes.
+__global__ __launch_bounds__(256) void k_tile_weights(const uint16_t* __restrict__ W, int N, int K,
+                                                      uint16_t* __restrict__ T, size_t chunks) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= chunks) return;
+  const int kts = K / kSgBK;
+  const int c = int(i % 8);
+  const size_t t = i / 8;
+  const int r = int(t % kSgRows);
+  const size_t u = t / kSgRows;
+  const int kt = int(u % kts);
+  const size_t row = (u / kts) * kSgRows + r;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < size_t(N)) v = *reinterpret_cast<const uint4*>(W + row * size_t(K) + size_t(kt) * kSgBK + 8 * c);
+  *reinterpret_cast<uint4*>(T + i * 8) = v;
+}
+
+size_t tiled_weight_elems(int N, int K) { return size_t((N + kSgRows - 1) / kSgRows) * kSgRows * size_t(K); }
+
+hipError_t launch_tile_weights(const uint16_t* W, int N, int K, uint16_t* T, hipStream_t s) {
+  if (N <= 0 || K <= 0 || K % kSgBK) return hipErrorInvalidValue;
+  const size_t chunks = tiled_weight_elems(N, K) / 8;
+  hipLaunchKernelGGL(k_tile_weights, dim3(unsigned((chunks + 255) / 256)), dim3(256), 0, s, W, N, K, T, chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled(const uint16_t* A_hi, const uint16_t* A_lo, int lda, const uint16_t* Bt, float* C,
+                             int M, int N, int K, const GemmPlan& plan, hipStream_t s) {
+  const int splits = plan.splits;
+  if (M <= 0 || M > 32 || N <= 0 || splits < 1 || K % (kSgBK * splits) || !A_lo || (lda & 7))
+    return hipErrorInvalidValue;
+  return launch_sgemm(A_hi, A_lo, lda, Bt, K, C, M, N, K / splits, splits, s, false, true);
 }
 
 // K tile: 32 with split activations (three stages fit), 64 otherwise (two stages)
