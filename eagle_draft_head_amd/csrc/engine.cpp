@@ -552,9 +552,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     c->tp_gu = tplan(2 * ff, n);
     c->tp_d = tplan(n, ff);
     c->tp_lm = tplan(dv, n);
+    // (helpers return the code; E3_TRY, which frees the context, runs at the call)
     auto tiled = [&](uint16_t** t, const e3::GemmPlan& p, int64_t N, int64_t K) -> int {
-      if (p.splits) E3_TRY(dalloc(c, t, e3::tiled_weight_elems(int(N), int(K))));
-      return EAGLE3_OK;
+      return p.splits ? dalloc(c, t, e3::tiled_weight_elems(int(N), int(K))) : EAGLE3_OK;
     };
     E3_TRY(tiled(&c->bt_enc, c->tp_enc, n, 3 * n));
     E3_TRY(tiled(&c->bt_qkv, c->tp_qkv, N_qkv, 2 * n));
@@ -689,8 +689,8 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
   {  // the batched projections' step-tiled weights (after the repacks)
     auto tile = [&](uint16_t* t, const uint16_t* w, int64_t N, int64_t K) -> int {
-      if (t) E3_TRYH(e3::launch_tile_weights(w, int(N), int(K), t, s), "tile weights");
-      return EAGLE3_OK;
+      const hipError_t e = t ? e3::launch_tile_weights(w, int(N), int(K), t, s) : hipSuccess;
+      return e == hipSuccess ? EAGLE3_OK : hip_fail(c, e, "tile weights");
     };
     E3_TRY(tile(c->bt_enc, c->w_fc, n, 3 * n));
     E3_TRY(tile(c->bt_qkv, c->w_qkv, N_qkv, 2 * n));
@@ -701,11 +701,12 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   }
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
     c->i4 = true;
+    // (returns the code; E3_TRY, which frees the context, runs at the call)
     auto quant = [&](const uint16_t* W, int64_t rows, int64_t K, eagle3_ctx::I4W* m) -> int {
-      E3_TRY(dalloc(c, &m->q, size_t(rows) * size_t(K) / 2));
-      E3_TRY(dalloc(c, &m->s, size_t(rows) * size_t(K) / 32));
-      E3_TRYH(e3::launch_quant_i4(W, int(rows), int(K), m->q, m->s, s), "int4 quantize");
-      return EAGLE3_OK;
+      if (int rc = dalloc(c, &m->q, size_t(rows) * size_t(K) / 2)) return rc;
+      if (int rc = dalloc(c, &m->s, size_t(rows) * size_t(K) / 32)) return rc;
+      const hipError_t e = e3::launch_quant_i4(W, int(rows), int(K), m->q, m->s, s);
+      return e == hipSuccess ? EAGLE3_OK : hip_fail(c, e, "int4 quantize");
     };
     E3_TRY(quant(c->w_fc, n, 3 * n, &c->i4_fc));
     E3_TRY(quant(c->w_qkv, N_qkv, 2 * n, &c->i4_qkv));

@@ -21,6 +21,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+#include <unistd.h>
+
+#include <sanitizer/lsan_interface.h>
 
 #include "eagle3.h"
 #include "eagle3_ledger.h"
@@ -237,31 +240,40 @@ static void check_alloc_failures(void) {
     if (warm) eagle3_free(warm);
   }
   /* every load that fails must hand back each allocation it made: the library's
-     own count of live allocations returns to where it was before the call */
-  int oom = 0;
-  const int64_t live0 = eagle3_test_live_allocations();
-  const size_t free0 = free_bytes();
-  for (int k = 1;; ++k) {
-    eagle3_test_fail_allocation(k);
-    eagle3_ctx* ctx = (eagle3_ctx*)(uintptr_t)1;
-    const int rc = eagle3_load(&c, &w, NULL, &ctx);
-    eagle3_test_fail_allocation(0);
-    if (rc == EAGLE3_OK) {  /* k is past the last allocation: the load succeeded */
-      CHECK(ctx != NULL);
-      CHECK(eagle3_test_live_allocations() > live0);
-      CHECK(eagle3_free(ctx) == EAGLE3_OK);
+     own count of live allocations returns to where it was before the call; both
+     the batched bf16 form (token table, step-tiled weights) and the batch-1 int4
+     form (quantized weights) */
+  eagle3_config ci = c;
+  ci.max_seqs = 1;
+  ci.weight_format = EAGLE3_WEIGHTS_I4;
+  const eagle3_config* forms[2] = {&c, &ci};
+  const char* names[2] = {"bf16 batched", "int4"};
+  for (int fi = 0; fi < 2; ++fi) {
+    int oom = 0;
+    const int64_t live0 = eagle3_test_live_allocations();
+    const size_t free0 = free_bytes();
+    for (int k = 1;; ++k) {
+      eagle3_test_fail_allocation(k);
+      eagle3_ctx* ctx = (eagle3_ctx*)(uintptr_t)1;
+      const int rc = eagle3_load(forms[fi], &w, NULL, &ctx);
+      eagle3_test_fail_allocation(0);
+      if (rc == EAGLE3_OK) {  /* k is past the last allocation: the load succeeded */
+        CHECK(ctx != NULL);
+        CHECK(eagle3_test_live_allocations() > live0);
+        CHECK(eagle3_free(ctx) == EAGLE3_OK);
+        CHECK(eagle3_test_live_allocations() == live0);
+        break;
+      }
+      CHECK(rc == EAGLE3_E_OOM);
+      CHECK(ctx == NULL);
       CHECK(eagle3_test_live_allocations() == live0);
-      break;
+      ++oom;
+      if (k > 400) { CHECK(!"eagle3_load did not finish within 400 allocations"); break; }
     }
-    CHECK(rc == EAGLE3_E_OOM);
-    CHECK(ctx == NULL);
-    CHECK(eagle3_test_live_allocations() == live0);
-    ++oom;
-    if (k > 400) { CHECK(!"eagle3_load did not finish within 400 allocations"); break; }
+    printf("eagle3_load (%s): %d allocation points failed cleanly; live allocations back to %lld; device "
+           "free %zu -> %zu bytes\n", names[fi], oom, (long long)live0, free0, free_bytes());
+    CHECK(oom > 10);
   }
-  printf("eagle3_load: %d allocation points failed cleanly; live allocations back to %lld; device free %zu "
-         "-> %zu bytes\n", oom, (long long)live0, free0, free_bytes());
-  CHECK(oom > 10);
   /* the trunk */
   eagle3_trunk_config tc;
   memset(&tc, 0, sizeof tc);
@@ -278,7 +290,7 @@ static void check_alloc_failures(void) {
   eagle3_trunk_weights tw = {buf, buf, buf, layers, &shapes[0][0]};
   const int64_t live_t0 = eagle3_test_live_allocations();
   const size_t free_t0 = free_bytes();
-  oom = 0;
+  int oom = 0;
   for (int k = 1;; ++k) {
     eagle3_test_fail_allocation(k);
     eagle3_trunk* t = (eagle3_trunk*)(uintptr_t)1;
@@ -305,6 +317,7 @@ static void check_alloc_failures(void) {
 }
 
 int main(int argc, char** argv) {
+  setvbuf(stdout, NULL, _IONBF, 0);  /* every line reaches the caller */
   const int device = argc > 1 && strcmp(argv[1], "device") == 0;
   check_ledger();
   check_rope();
@@ -312,5 +325,9 @@ int main(int argc, char** argv) {
   check_trunk_validation();
   if (device) check_alloc_failures();
   printf("abi_check %s: %d failed checks\n", device ? "device" : "host", failures);
-  return failures ? 1 : 0;
+  /* the leak check now (it ends the process if anything leaked), then leave without
+     the GPU runtime's exit-time teardown, which releases its own memory after the
+     sanitizer's allocator hooks have seen the runtime unload */
+  __lsan_do_leak_check();
+  _exit(failures ? 1 : 0);
 }

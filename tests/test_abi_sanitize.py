@@ -40,4 +40,5 @@ def test_abi_host_paths_under_sanitizers():
 @pytest.mark.gpu
 def test_allocation_failures_release_everything():
     out = _run("device")
-    assert "eagle3_load:" in out and "eagle3_trunk_load:" in out
+    assert "eagle3_load (bf16 batched):" in out and "eagle3_load (int4):" in out
+    assert "eagle3_trunk_load:" in out
