@@ -256,7 +256,7 @@ def main():
     i4 = args.weights == "int4"
     global WB, TABLE
     WB = WB_I4 if i4 else WB_BF16
-    TABLE = not i4 and args.token_table != "off"
+    TABLE = args.token_table != "off"
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype,
                  weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16,
                  append_act={"default": B.APPEND_DEFAULT, "split": B.APPEND_SPLIT, "bf16": B.APPEND_BF16,

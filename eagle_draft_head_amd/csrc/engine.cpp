@@ -84,7 +84,7 @@ struct eagle3_ctx {
   // int4: the teacher-forced MFMA passes multiply by the int4 weights of fc and of the
   // K/V rows of QKV as exact bf16 (hi, lo) pairs: hi overwrites those rows of w_fc /
   // w_qkv, lo lives here
-  uint16_t *i4_fc_lo = nullptr, *i4_kv_lo = nullptr;
+  uint16_t *i4_fc_lo = nullptr, *i4_qkv_lo = nullptr, *i4_kv_lo = nullptr;  // kv: rows qd.. of qkv
   // the weight stream a GEMV reads: the bf16 rows or the int4 codes, and the scales
   const uint16_t* wq(const uint16_t* bf16, const I4W& m, size_t row0 = 0, size_t K = 0) const {
     return i4 ? reinterpret_cast<const uint16_t*>(m.q + row0 * (K / 2)) : bf16 + row0 * K;
@@ -312,8 +312,6 @@ int validate_config(const eagle3_config* cfg, const char** why) {
   if (cfg->token_table != EAGLE3_TABLE_DEFAULT && cfg->token_table != EAGLE3_TABLE_OFF &&
       cfg->token_table != EAGLE3_TABLE_ON)
     return bad("unknown token_table", EAGLE3_E_INVAL);
-  if (cfg->token_table == EAGLE3_TABLE_ON && cfg->weight_format != EAGLE3_WEIGHTS_BF16)
-    return bad("the token table needs bf16 weights", EAGLE3_E_INVAL);
   if (cfg->append_act == EAGLE3_APPEND_F16 && cfg->weight_format != EAGLE3_WEIGHTS_BF16)
     return bad("fp16 teacher-forced activations need bf16 weights", EAGLE3_E_UNSUPPORTED);
   if (cfg->weight_format == EAGLE3_WEIGHTS_I4) {
@@ -666,27 +664,6 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
                                         c->status, s),
             "fp16 kv");
   }
-  if (cfg->token_table == EAGLE3_TABLE_ON ||
-      (cfg->token_table == EAGLE3_TABLE_DEFAULT && cfg->weight_format == EAGLE3_WEIGHTS_BF16)) {
-    // the token table: passes of tf_rows tokens, w_in * E as (hi, lo) bf16 planes
-    // in tf_A, one MFMA GEMM against the embedding half of the repacked W_qkv
-    E3_TRY(dalloc(c, &c->tok_tab, size_t(vt) * N_qkv));
-    E3_TRY(dalloc(c, &c->tok_ss, size_t(vt)));
-    E3_TRYH(e3::launch_tok_ss(c->embed, int(vt), int(n), c->tok_ss, s), "token table norms");
-    const int T = c->tf_rows;
-    uint16_t* A_hi = c->tf_A;
-    uint16_t* A_lo = c->tf_A + size_t(T) * n;  // tf_A holds 3 n values per row
-    for (int64_t r0 = 0; r0 < vt; r0 += T) {
-      const int rows = int(std::min<int64_t>(T, vt - r0));
-      E3_TRYH(e3::launch_pack_embed(c->embed, c->nrm_in, int(r0), rows, int(n), A_hi, A_lo, s),
-              "token table pack");
-      e3::GemmPlan p = e3::gemm_plan(rows, int(N_qkv), int(n));
-      p.splits = 1;  // one plane: the table rows are written in place
-      E3_TRYH(e3::launch_gemm_bf16(A_hi, A_lo, int(n), c->w_qkv, int(2 * n), c->tok_tab + size_t(r0) * N_qkv,
-                                   rows, int(N_qkv), int(n), p, s),
-              "token table gemm");
-    }
-  }
   {  // the batched projections' step-tiled weights (after the repacks)
     auto tile = [&](uint16_t* t, const uint16_t* w, int64_t N, int64_t K) -> int {
       const hipError_t e = t ? e3::launch_tile_weights(w, int(N), int(K), t, s) : hipSuccess;
@@ -715,12 +692,44 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     E3_TRY(quant(c->w_d, n, ff, &c->i4_d));
     E3_TRY(quant(c->w_lm, dv, n, &c->i4_lm));
     E3_TRY(dalloc(c, &c->i4_fc_lo, size_t(n) * 3 * n));
-    E3_TRY(dalloc(c, &c->i4_kv_lo, size_t(2 * kvd) * 2 * n));
+    // every QKV row as the int4 weights' (hi, lo) halves: hi over the bf16 rows (Q
+    // rows included: in this form only the token table reads them), lo beside them
+    E3_TRY(dalloc(c, &c->i4_qkv_lo, N_qkv * 2 * n));
+    c->i4_kv_lo = c->i4_qkv_lo + size_t(qd) * 2 * n;
     E3_TRYH(e3::launch_dequant_i4_split(c->i4_fc.q, c->i4_fc.s, int(n), int(3 * n), c->w_fc, c->i4_fc_lo, s),
             "int4 fc split");
-    E3_TRYH(e3::launch_dequant_i4_split(c->i4_qkv.q + size_t(qd) * n, c->i4_qkv.s + size_t(qd) * (2 * n / 32),
-                                        int(2 * kvd), int(2 * n), c->w_qkv + size_t(qd) * 2 * n, c->i4_kv_lo, s),
-            "int4 kv split");
+    E3_TRYH(e3::launch_dequant_i4_split(c->i4_qkv.q, c->i4_qkv.s, int(N_qkv), int(2 * n), c->w_qkv, c->i4_qkv_lo,
+                                        s),
+            "int4 qkv split");
+  }
+  if (cfg->token_table != EAGLE3_TABLE_OFF) {
+    // the token table: passes of T tokens, input_layernorm * E as (hi, lo) bf16 planes
+    // in tf_A, one MFMA GEMM against the embedding half of the repacked W_qkv (int4:
+    // a second against the weights' lo halves, summed through tf_F)
+    E3_TRY(dalloc(c, &c->tok_tab, size_t(vt) * N_qkv));
+    E3_TRY(dalloc(c, &c->tok_ss, size_t(vt)));
+    E3_TRYH(e3::launch_tok_ss(c->embed, int(vt), int(n), c->tok_ss, s), "token table norms");
+    int T = c->tf_rows;
+    if (c->i4) T = int(std::min<size_t>(size_t(T), c->tf_F_cap / N_qkv));
+    if (T < 1) return fail(set_err(c, EAGLE3_E_UNSUPPORTED, "token table: no room for a pass"));
+    uint16_t* A_hi = c->tf_A;
+    uint16_t* A_lo = c->tf_A + size_t(T) * n;  // tf_A holds 3 n values per row
+    for (int64_t r0 = 0; r0 < vt; r0 += T) {
+      const int rows = int(std::min<int64_t>(T, vt - r0));
+      E3_TRYH(e3::launch_pack_embed(c->embed, c->nrm_in, int(r0), rows, int(n), A_hi, A_lo, s),
+              "token table pack");
+      e3::GemmPlan p = e3::gemm_plan(rows, int(N_qkv), int(n));
+      p.splits = 1;  // one plane: the table rows are written in place
+      float* dst = c->tok_tab + size_t(r0) * N_qkv;
+      E3_TRYH(e3::launch_gemm_bf16(A_hi, A_lo, int(n), c->w_qkv, int(2 * n), dst, rows, int(N_qkv), int(n), p, s),
+              "token table gemm");
+      if (c->i4) {
+        E3_TRYH(e3::launch_gemm_bf16(A_hi, A_lo, int(n), c->i4_qkv_lo, int(2 * n), c->tf_F, rows, int(N_qkv),
+                                     int(n), p, s),
+                "token table gemm lo");
+        E3_TRYH(e3::launch_add_f32(dst, c->tf_F, size_t(rows) * N_qkv, s), "token table sum");
+      }
+    }
   }
   E3_TRYH(hipStreamSynchronize(s), "load sync");
 #undef E3_TRY

@@ -731,6 +731,55 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv_tab(QkvArgs a) {
   qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
 }
 
+// k_qkv_q with the token table: only the hidden half's codes stream and only the
+// hidden half is quantised; the table row stands for the embedding half.  The
+// token's loads go out first (a wave's loads complete in issue order).
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_qkv_q_tab(QkvArgs a) {
+  static_assert(R % 2 == 0, "rotary pairs need an even row count per wave");
+  extern __shared__ float xs[];  // [0, n) hidden half, then its quantised planes
+  __shared__ float red[32];
+  __shared__ float sv[16];
+  __shared__ int si[16], st[16];
+  const int n = a.n;
+  const int N = (a.n_head + 2 * a.n_head_kv) * a.head_dim;
+  const int wv = threadIdx.x >> 6;
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.w_qkv);
+  const size_t ldw = size_t(2) * n;
+  const int nvb = (N + WAVES * R - 1) / (WAVES * R);
+  ArgmaxBatch first;
+  const int tok0 = qkv_token_load(a, first);
+  QLoad<R, U> Lg;
+  int row0 = (blockIdx.x * WAVES + wv) * R;
+  if (row0 < N) q_issue<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg);
+  uint4* xpg = reinterpret_cast<uint4*>(xs + n);
+  int* xeg = reinterpret_cast<int*>(xpg + n / 8);
+  stage_plain(xs, a.gw, n);
+  float sg = sum_partials(a.g_ssq, a.g_ssq_count);
+  const int tok = qkv_token_from(a, first, tok0, sv, si, st);
+  const float* trow = a.tok_tab + (size_t)tok * N;
+  const float se = a.tok_ss[tok];
+  __syncthreads();  // hidden half staged
+  quant_x_i4(xs, n, xpg, xeg);
+  float zero = 0.f;
+  block_sum2(zero, sg, red);  // its barriers also publish the quantised vector
+  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
+  const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
+  for (int vb = blockIdx.x;; vb += gridDim.x) {
+    if (row0 < N) {
+      float acc_g[R], acc_e[R];
+      q_dot_issued<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg, xpg, xeg, acc_g);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc_e[r] = trow[min(row0 + r, N - 1)];
+      qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+    }
+    const int vn = vb + int(gridDim.x);
+    if (vn >= nvb) break;
+    row0 = (vn * WAVES + wv) * R;
+    if (row0 < N) q_issue<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg);
+  }
+}
+
 // k_qkv with int4 weights: the first row set's codes of both halves go out first;
 // both halves are then staged and quantised once per block, and the block covers
 // its virtual blocks of rows
@@ -1231,7 +1280,11 @@ hipError_t launch_qkv(const QkvArgs& a, int cfg, hipStream_t s) {
 #define CASE(ID, WV, RR, UU)                                                               \
   case ID:                                                                                 \
     if (RR % 2) return hipErrorInvalidValue;                                               \
-    if (a.s_qkv) {                                                                         \
+    if (a.s_qkv && a.tok_tab) {                                                            \
+      E3_LDS_ALLOW((k_qkv_q_tab<WV, (RR < 2 ? 2 : RR), UU>), xb / 2 + q_vec_bytes(a.n));    \
+      E3_LAUNCH((k_qkv_q_tab<WV, (RR < 2 ? 2 : RR), UU>), dim3(i4_grid(ceil_div(N, WV * RR))), \
+                         dim3(64 * WV), xb / 2 + q_vec_bytes(a.n), s, a);                  \
+    } else if (a.s_qkv) {                                                                  \
       E3_LDS_ALLOW((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), xb + 2 * q_vec_bytes(a.n));        \
       E3_LAUNCH((k_qkv_q<WV, (RR < 2 ? 2 : RR), UU>), dim3(i4_grid(ceil_div(N, WV * RR))), \
                          dim3(64 * WV), xb + 2 * q_vec_bytes(a.n), s, a);                  \

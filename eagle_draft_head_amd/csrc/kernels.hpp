@@ -449,6 +449,8 @@ hipError_t launch_gemm_tiled(const uint16_t* A_hi, const uint16_t* A_lo, int lda
 hipError_t launch_tok_ss(const uint16_t* E, int vocab, int n, float* ss, hipStream_t s);
 hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, int r0, int T, int n, uint16_t* A_hi,
                              uint16_t* A_lo, hipStream_t s);
+// dst[i] += src[i], i < count
+hipError_t launch_add_f32(float* dst, const float* src, size_t count, hipStream_t s);
 // dst[i] = fp16 bits of (bf16 src[i]) * 2^8, exact for 2^-25 <= |src| < 256 (and 0);
 // any other weight raises kStatusAppendRange in *status
 hipError_t launch_bf16_to_f16_x256(const uint16_t* src, uint16_t* dst, size_t count, uint32_t* status,

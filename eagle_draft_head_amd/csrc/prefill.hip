@@ -12,6 +12,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace e3 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -152,6 +154,18 @@ __global__ __launch_bounds__(256) void k_pack_embed(const uint16_t* __restrict__
 hipError_t launch_tok_ss(const uint16_t* E, int vocab, int n, float* ss, hipStream_t s) {
   if (vocab <= 0 || (n & 7)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tok_ss, dim3(vocab), dim3(256), 0, s, E, n, ss);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_add_f32(float* __restrict__ dst, const float* __restrict__ src, size_t count) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] += src[i];
+}
+
+hipError_t launch_add_f32(float* dst, const float* src, size_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((count + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_add_f32, dim3(unsigned(blocks)), dim3(256), 0, s, dst, src, count);
   return hipGetLastError();
 }
 

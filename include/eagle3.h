@@ -122,12 +122,12 @@ typedef struct {
    first factor for every target token at load into an fp32 table of target_vocab x
    (n_head + 2 n_head_kv) head_dim values, plus sum(E[tok]^2) per token, and each
    batch-1 chain step reads one table row instead of streaming the embedding half of
-   W_qkv (half of its QKV weight bytes).  The table is built by one MFMA GEMM whose
-   activations enter as bf16 (hi, lo) pairs (about 2^-17 relative), summed in fp32.
-   EAGLE3_TABLE_DEFAULT: on with bf16 weights, off with int4 weights; EAGLE3_TABLE_OFF
-   streams both halves.  Needs bf16 weights (EAGLE3_E_INVAL otherwise).  3.7 GB at
-   the Qwen3-8B shape (151936 tokens x 6144 rows).  Batched chains and the
-   teacher-forced appends do not use it. */
+   W_qkv (half of its QKV weight bytes).  The table is built by an MFMA GEMM whose
+   activations enter as bf16 (hi, lo) pairs (about 2^-17 relative), summed in fp32;
+   with int4 weights it multiplies the weights' exact values (scale * q, as a bf16
+   hi + lo pair: two GEMMs).  EAGLE3_TABLE_DEFAULT and EAGLE3_TABLE_ON build it;
+   EAGLE3_TABLE_OFF streams both halves.  3.7 GB at the Qwen3-8B shape (151936 tokens
+   x 6144 rows).  Batched chains and the teacher-forced appends do not use it. */
 #define EAGLE3_TABLE_DEFAULT 0
 #define EAGLE3_TABLE_OFF 1
 #define EAGLE3_TABLE_ON 2

@@ -140,8 +140,8 @@ static void check_load_validation(void) {
   CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);
   b = c; b.token_table = 3;
   CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);
-  b = c; b.max_seqs = 1; b.weight_format = EAGLE3_WEIGHTS_I4; b.token_table = EAGLE3_TABLE_ON;
-  CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);  /* the table needs bf16 weights */
+  b = c; b.token_table = -1;
+  CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_INVAL);
   b = c; b.kv_dtype = EAGLE3_KV_Q8Q5;  /* batch-1 only */
   CHECK(eagle3_load(&b, &w, NULL, &ctx) == EAGLE3_E_UNSUPPORTED);
   b = c; b.max_ctx = 0;

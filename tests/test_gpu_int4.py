@@ -67,14 +67,18 @@ def test_int4_codes_and_scales_bit_exact():
     dr.close()
 
 
-@pytest.mark.parametrize("L,rounds,gamma", [(63, 40, 3), (0, 5, 5)])
-def test_int4_chain_parity_tiny(L, rounds, gamma):
+@pytest.mark.parametrize("L,rounds,gamma,table", [(63, 40, 3, B.TABLE_DEFAULT), (0, 5, 5, B.TABLE_DEFAULT),
+                                                  (63, 20, 3, B.TABLE_OFF)],
+                         ids=["table", "empty-table", "streamed"])
+def test_int4_chain_parity_tiny(L, rounds, gamma, table):
+    """The default keeps the QKV embedding half in the token table (built from the
+    int4 weights' exact values); TABLE_OFF streams both halves' codes."""
     cfg = TINY
-    say(f"[int4] tiny L={L} rounds={rounds} gamma={gamma}")
+    say(f"[int4] tiny L={L} rounds={rounds} gamma={gamma} table={table}")
     wd = gen.drafter_weights(cfg, device="cuda")
     wh = int4.int4_weights({k: v.cpu() for k, v in wd.items()})
     max_ctx = L + rounds * (gamma + 1) + 16
-    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, weight_format=B.WEIGHTS_I4)
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, weight_format=B.WEIGHTS_I4, token_table=table)
     orc = make_oracle(cfg, wh, max_ctx=max_ctx)
     aux, toks = aux_np(cfg, 0, L), toks_np(cfg, 0, L)
     orc.prefill(0, aux, toks)
