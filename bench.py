@@ -105,6 +105,11 @@ def kernel_bytes(cfg, kernel: str, L: int, kv_bytes: int = 4) -> float:
     n, qd, kvd, ff, dv = cfg.n_embd, cfg.q_dim, cfg.kv_dim, cfg.n_ff, cfg.draft_vocab
     if kernel == "lm_head":
         return WB * dv * n + 4 * n + 4 * n
+    if kernel == "lm_head_qkv":
+        # lm_head and the next step's hidden-half QKV rows (deferred QKV): both weight
+        # streams, both staged vectors, the hidden-half sums written
+        N = qd + 2 * kvd
+        return WB * dv * n + 4 * n + 4 * n + WB * N * n + 4 * n + 4 * N
     if kernel == "gate_up":
         return WB * 2 * ff * n + 4 * n + 4 * n + 4 * ff
     if kernel == "qkv":
@@ -206,8 +211,6 @@ def main():
                          "context plus a gamma+1-row window, against gamma+1 single-row calls")
     args = ap.parse_args()
     args.kernel_set = args.kernel is not None
-    if args.kernel is None:
-        args.kernel = "lm_head"
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU (--gpus 1); "
                                    "the engine has no multi-GPU sharding"}))
@@ -257,6 +260,13 @@ def main():
     global WB, TABLE
     WB = WB_I4 if i4 else WB_BF16
     TABLE = args.token_table != "off"
+    if args.kernel is None:
+        # the dominant kernel: with the token table and bf16 weights the engine runs
+        # lm_head together with the next step's hidden-half QKV (deferred QKV) in every
+        # step but a chain's last
+        deferred = (TABLE and not i4 and args.kv != "q8q5" and gamma > 1
+                    and os.environ.get("EAGLE3_DEFER_QKV", "1") != "0")
+        args.kernel = "lm_head_qkv" if deferred else "lm_head"
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype,
                  weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16,
                  append_act={"default": B.APPEND_DEFAULT, "split": B.APPEND_SPLIT, "bf16": B.APPEND_BF16,
@@ -663,7 +673,7 @@ def run_batched(args, cfg):
     from synth import gen
 
     gamma = args.gamma or cfg.gamma
-    kernel = args.kernel if args.kernel != "lm_head" or args.kernel_set else "attention"
+    kernel = args.kernel if args.kernel_set else "attention"
     dev = "cuda"
     torch.cuda.set_device(0)
     lens = gen.batch_lengths(cfg)

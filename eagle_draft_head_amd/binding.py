@@ -32,7 +32,7 @@ WEIGHT_FIELDS = ("fc", "input_layernorm", "hidden_norm", "q_proj", "k_proj", "v_
                  "lm_head", "embed")
 
 PROFILE_KERNELS = {"lm_head": 0, "gate_up": 1, "qkv": 2, "down": 3, "o_proj": 4, "attention": 5,
-                   "encode": 6, "prefill_fc_gemm": 7, "prefill_kv_gemm": 8}
+                   "encode": 6, "prefill_fc_gemm": 7, "prefill_kv_gemm": 8, "lm_head_qkv": 9}
 
 
 class Eagle3Error(RuntimeError):

@@ -15,6 +15,7 @@
 // splits per query head; with S == 1 the block writes the normalised output.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "qkv_token.hpp"
 
 #include <algorithm>
 #include <cstdlib>
@@ -53,7 +54,135 @@ struct KvVec<float> {
 constexpr int kAttnLaneElems = 8;  // elements of a row per lane
 constexpr float kRescale = 8.0f;   // log2 headroom of the online softmax reference
 
-template <int HD, int G, typename KT>
+// ---------------------------------------------------------------------------
+// Deferred QKV (AttnArgs dq): a draft step's q and new K/V row are finished in the
+// attention kernel.  The previous kernel left hsum (the hidden half of every QKV row,
+// divided by rms(g)); a block takes its KV head's rows of the repacked QKV matrix --
+// the G query heads, then the K head and the V head, (G + 2) hd rows -- as rotary
+// pairs (rows 2p, 2p + 1 of a head hold dims p and p + r/2 when 2p < r, dims 2p and
+// 2p + 1 otherwise), adds the token table's row of the step's token (the embedding
+// half, divided by rms(E[tok])), and rotates q and k at the step's position (the
+// fused QKV kernel's epilogue).
+constexpr int kDqPairs = 6;     // rotary pairs per thread, at most
+constexpr int kDqThreads = 256;  // the attention blocks' size (kAttnWaves waves)
+static_assert(kDqThreads == 64 * kAttnWaves, "the decode kernels' block size");
+
+struct DqPre {
+  ArgmaxBatch first;                 // the previous step's candidates (first batch)
+  int tok0;                          // or the boundary token
+  float h0[kDqPairs], h1[kDqPairs];  // normalised hidden-half sums of the thread's pairs
+  double f[kDqPairs];                // their rotary frequencies (pairs that rotate)
+};
+
+// repacked QKV row of pair pp of KV head kvh's (G + 2) hd rows; hs = head slot (G: K,
+// G + 1: V), p = pair within the head
+__device__ __forceinline__ int dq_row(const AttnArgs& a, int kvh, int G, int pp, int* hs, int* p) {
+  const int hd = a.head_dim, hp = hd >> 1;
+  const int h = pp / hp;
+  *hs = h;
+  *p = pp - h * hp;
+  const int qd = a.n_head * hd, kvd = a.n_head_kv * hd;
+  const int base = h < G ? (kvh * G + h) * hd : (h == G ? qd + kvh * hd : qd + kvd + kvh * hd);
+  return base + 2 * *p;
+}
+
+// The loads that do not depend on the token, issued before the block's K/V rows (a
+// wave's loads complete in issue order, so the token's come first).  No loops and no
+// blockDim (a load): the waits for these then leave the K/V loads in flight.
+__device__ __forceinline__ void dq_issue(const AttnArgs& a, int kvh, int G, DqPre& pre) {
+  pre.tok0 = qkv_token_load<kDqThreads>(a.dqa, pre.first);
+  const int P = (G + 2) * (a.head_dim >> 1);
+#pragma unroll
+  for (int k = 0; k < kDqPairs; ++k) {
+    const int pp = int(threadIdx.x) + k * kDqThreads;
+    pre.h0[k] = 0.f;
+    pre.h1[k] = 0.f;
+    pre.f[k] = 0.0;
+    if (pp < P) {
+      int hs, p;
+      const float2 h = *reinterpret_cast<const float2*>(a.dq_hsum + dq_row(a, kvh, G, pp, &hs, &p));
+      pre.h0[k] = h.x;
+      pre.h1[k] = h.y;
+      if (hs <= G && 2 * p < a.dqa.rope_dim) pre.f[k] = a.dqa.inv_freq[p];
+    }
+  }
+}
+
+// Finish q (sq[g * HD + d], natural dims, unscaled) and the new row (snew[d] = K,
+// snew[HD + d] = V, rounded as the cache stores them).  The owner block (its split
+// holds row T - 1) stores the row to the cache and leaves the row's base-2 scores
+// (score scale `scale`) in sdot[g]; sdot is read after the caller's next barrier.
+// Every thread of the block (kDqThreads) calls it.
+template <int HD>
+__device__ __forceinline__ void dq_finish(const AttnArgs& a, int kvh, int G, int T, bool owner, const DqPre& pre,
+                                          float scale, float* sq, float* snew, float* sdot, float* sv, int* si,
+                                          int* st) {
+  const QkvArgs& d = a.dqa;
+  const int tok = qkv_token_from<false, kDqThreads>(d, pre.first, pre.tok0, sv, si, st);
+  const int N = (a.n_head + 2 * a.n_head_kv) * HD;
+  const float* trow = d.tok_tab + (size_t)tok * N;
+  const int P = (G + 2) * (HD / 2);
+  float t0[kDqPairs], t1[kDqPairs];
+#pragma unroll
+  for (int k = 0; k < kDqPairs; ++k) {
+    const int pp = int(threadIdx.x) + k * kDqThreads;
+    t0[k] = 0.f;
+    t1[k] = 0.f;
+    if (pp < P) {
+      int hs, p;
+      const float2 t = *reinterpret_cast<const float2*>(trow + dq_row(a, kvh, G, pp, &hs, &p));
+      t0[k] = t.x;
+      t1[k] = t.y;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDqPairs; ++k) {
+    const int pp = int(threadIdx.x) + k * kDqThreads;
+    if (pp >= P) break;
+    int hs, p;
+    (void)dq_row(a, kvh, G, pp, &hs, &p);
+    float y0 = t0[k] + pre.h0[k];  // both halves arrive normalised
+    float y1 = t1[k] + pre.h1[k];
+    int d0 = 2 * p, d1 = 2 * p + 1;
+    if (hs <= G && 2 * p < d.rope_dim) {
+      d0 = p;
+      d1 = p + (d.rope_dim >> 1);
+      float c, s;
+      rope_cs(d.pos, pre.f[k], &c, &s);
+      const float r0 = y0 * c - y1 * s;
+      const float r1 = y1 * c + y0 * s;
+      y0 = r0;
+      y1 = r1;
+    }
+    if (hs < G) {
+      sq[hs * HD + d0] = y0;
+      sq[hs * HD + d1] = y1;
+    } else {
+      if (!a.kv_f32) {  // the value a read of the bf16 cache gives
+        y0 = bf16_to_f32(f32_to_bf16(y0));
+        y1 = bf16_to_f32(f32_to_bf16(y1));
+      }
+      snew[(hs - G) * HD + d0] = y0;
+      snew[(hs - G) * HD + d1] = y1;
+    }
+  }
+  __syncthreads();
+  if (!owner) return;
+  const size_t row = ((size_t)kvh * a.cap + (T - 1)) * HD;
+  for (int i = threadIdx.x; i < HD; i += kDqThreads) {
+    kv_store(d.k_cache, row + i, snew[i], a.kv_f32);
+    kv_store(d.v_cache, row + i, snew[HD + i], a.kv_f32);
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int g = wv; g < G; g += kDqThreads / 64) {
+    float t = 0.f;
+    for (int e = lane; e < HD; e += 64) t = fmaf(snew[e], sq[g * HD + e] * scale, t);
+    t = wave_sum(t);
+    if (lane == 0) sdot[g] = t;
+  }
+}
+
+template <int HD, int G, typename KT, bool DQ = false>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   constexpr int E = KvVec<KT>::E;            // elements per 16-byte vector
   constexpr int NV = kAttnLaneElems / E;     // vectors per lane per row (K, and V)
@@ -66,6 +195,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   static_assert(LPR <= 64 && RPW >= 1 && NV * E == kAttnLaneElems, "a row must fit in one wave");
   __shared__ float obuf[kAttnWaves][G][HD];
   __shared__ float s_M[kAttnWaves][G], s_L[kAttnWaves][G];
+  // deferred QKV: the step's queries, its new K/V row and that row's scores
+  __shared__ __align__(16) float dq_q[DQ ? G * HD : 1];
+  __shared__ float dq_kv[DQ ? 2 * HD : 1], dq_s[DQ ? G : 1], dq_sv[DQ ? 16 : 1];
+  __shared__ int dq_si[DQ ? 16 : 1], dq_st[DQ ? 16 : 1];
 
   const int s = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -87,8 +220,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
     part_o += (size_t)rb * a.n_head * S * HD;
     part_ml += (size_t)rb * a.n_head * S * 2;
   }
-  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  const int r0 = s * chunk;
   if (r0 >= T) return;  // a split past this row's context (batched rows are ragged)
+  // deferred QKV: row T - 1 is made here, so the ring covers the rows before it and
+  // the block whose split holds it takes it from LDS
+  const bool owner = DQ && T - 1 < r0 + chunk;
+  const int r1 = min(DQ ? T - 1 : T, r0 + chunk);
   const bool direct = S == 1 && !a.batched;
   // scores in base 2: s * log2(e) / sqrt(hd), so every exponential is one exp2
   const float scale = 1.4426950408889634f / sqrtf(float(HD));
@@ -100,7 +237,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   // clamped to r1 - 1, so every load is in bounds and unconditional; a slot that
   // holds a clamped row is never consumed.
   const int off = wv * RPW + slot;
-  const int rlast = r1 - 1;
+  const int rlast = max(r1 - 1, 0);  // (an owner's ring may be empty: its loads are never consumed)
+  DqPre pre;
+  if constexpr (DQ) dq_issue(a, kvh, G, pre);
   uint4 kw[kDepth][NV], vw[kDepth][NV];
   auto load_row = [&](int i, int row) {
     row = min(row, rlast);
@@ -114,12 +253,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
 #pragma unroll
   for (int i = 0; i < kDepth; ++i) load_row(i, rb + off + i * RPB);
   // q carries the score scale, so a row's dot product is its base-2 score
+  if constexpr (DQ) dq_finish<HD>(a, kvh, G, T, owner, pre, scale, dq_q, dq_kv, dq_s, dq_sv, dq_si, dq_st);
   float qv[G][kAttnLaneElems];
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < kAttnLaneElems; ++e)
-      qv[g][e] = qrow[(size_t)(kvh * G + g) * HD + dim(e)] * scale;
+      qv[g][e] = (DQ ? dq_q[g * HD + dim(e)] : qrow[(size_t)(kvh * G + g) * HD + dim(e)]) * scale;
   float m[G], mr[G], l[G], acc[G][kAttnLaneElems];  // mr = m + kRescale
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -192,11 +332,17 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
     if (lane == 0) s_M[wv][g] = mw;
   }
   __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
+  // the block's reference per head: the waves' and (owner) the new row's score
+  auto block_ref = [&](int g) {
     float Mb = s_M[0][g];
 #pragma unroll
     for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    if (DQ && owner) Mb = fmaxf(Mb, dq_s[g]);
+    return Mb;
+  };
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float Mb = block_ref(g);
     const float f = (m[g] == -INFINITY) ? 0.f : exp2f(m[g] - Mb);
     l[g] *= f;
 #pragma unroll
@@ -228,6 +374,11 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
       v += obuf[w][g][dd];
       L += s_L[w][g];
     }
+    if (DQ && owner) {  // the new row, weight 2^(score - reference)
+      const float fn = exp2f(dq_s[g] - block_ref(g));
+      v = fmaf(fn, dq_kv[HD + dd], v);
+      L += fn;
+    }
     const int h = kvh * G + g;
     if (direct) a.out[(size_t)h * HD + dd] = v / L;
     else part_o[((size_t)h * S + s) * HD + dd] = v;
@@ -235,9 +386,10 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int chunk, int S) {
   if (direct) return;
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
-    float Mb = s_M[0][g], L = 0.f;
-    for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, s_M[w][g]);
+    const float Mb = block_ref(g);
+    float L = 0.f;
     for (int w = 0; w < kAttnWaves; ++w) L += s_L[w][g];
+    if (DQ && owner) L += exp2f(dq_s[g] - Mb);
     const int h = kvh * G + g;
     part_ml[((size_t)h * S + s) * 2 + 0] = Mb;
     part_ml[((size_t)h * S + s) * 2 + 1] = L;
@@ -652,7 +804,7 @@ __global__ __launch_bounds__(256) void k_attn_mid_mfma(VerifyArgs a, int chunk, 
 typedef short bf16x4s_t __attribute__((ext_vector_type(4)));
 constexpr int kMfmaRing = 2;
 
-template <int HD>
+template <int HD, bool DQ = false>
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int S) {
   constexpr int NT = HD / 16;               // output tiles of 16 dims
   constexpr int KS = HD / 32;               // k steps of S
@@ -664,6 +816,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int
   static_assert(NT * 16 == HD && KS * 32 == HD && NG * VD == HD, "head_dim 64 or 128");
   __shared__ float so[kAttnWaves][16][HD + 4];
   __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
+  // deferred QKV: the step's queries, its new K/V row and that row's scores
+  __shared__ __align__(16) float dq_q[DQ ? 16 * HD : 1];
+  __shared__ float dq_kv[DQ ? 2 * HD : 1], dq_s[DQ ? 16 : 1], dq_sv[DQ ? 16 : 1];
+  __shared__ int dq_si[DQ ? 16 : 1], dq_st[DQ ? 16 : 1];
 
   const int s = blockIdx.x, kvh = blockIdx.y;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -682,10 +838,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int
     part_o += (size_t)rb * a.n_head * S * HD;
     part_ml += (size_t)rb * a.n_head * S * 2;
   }
-  const int r0 = s * chunk, r1 = min(T, r0 + chunk);
+  const int r0 = s * chunk;
   if (r0 >= T) return;  // a split past this row's context (batched rows are ragged)
+  // deferred QKV: row T - 1 is made here, so the tiles cover the rows before it and
+  // the block whose split holds it takes it from LDS
+  const bool owner = DQ && T - 1 < r0 + chunk;
+  const int r1 = min(DQ ? T - 1 : T, r0 + chunk);
   const bool direct = S == 1 && !a.batched;
-  const int rlast = r1 - 1;
+  const int rlast = max(r1 - 1, 0);
+  DqPre pre;
+  if constexpr (DQ) dq_issue(a, kvh, G, pre);
   const uint16_t* Kb = static_cast<const uint16_t*>(a.k_cache) + kv_off + (size_t)kvh * a.cap * HD;
   const uint16_t* Vb = static_cast<const uint16_t*>(a.v_cache) + kv_off + (size_t)kvh * a.cap * HD;
 
@@ -717,11 +879,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int
 
   // queries carry the base-2 score scale; columns past G are zero
   const float scale = 1.4426950408889634f / sqrtf(float(HD));
+  if constexpr (DQ) dq_finish<HD>(a, kvh, G, T, owner, pre, scale, dq_q, dq_kv, dq_s, dq_sv, dq_si, dq_st);
   const bool qok = c16 < G;
   bf16x8_t qh[KS], ql[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const float* qp = qrow + (size_t)(kvh * G + (qok ? c16 : 0)) * HD + 32 * ks + 8 * g4;
+    const float* qp = DQ ? dq_q + (qok ? c16 : 0) * HD + 32 * ks + 8 * g4
+                         : qrow + (size_t)(kvh * G + (qok ? c16 : 0)) * HD + 32 * ks + 8 * g4;
     const float4 u = *reinterpret_cast<const float4*>(qp), w = *reinterpret_cast<const float4*>(qp + 4);
     float x[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -823,12 +987,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a, int chunk, int
     float Mb = sm[0][q];
 #pragma unroll
     for (int w = 1; w < kAttnWaves; ++w) Mb = fmaxf(Mb, sm[w][q]);
+    if (DQ && owner) Mb = fmaxf(Mb, dq_s[q]);
     float v = 0.f, Ls = 0.f;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) {
       const float f = (Mb == -INFINITY || sm[w][q] == -INFINITY) ? 0.f : exp2f(sm[w][q] - Mb);
       v = fmaf(f, so[w][q][dd], v);
       Ls = fmaf(f, sl[w][q], Ls);
+    }
+    if (DQ && owner) {  // the new row, weight 2^(score - reference)
+      const float fn = exp2f(dq_s[q] - Mb);
+      v = fmaf(fn, dq_kv[HD + dd], v);
+      Ls += fn;
     }
     const int h = kvh * G + q;
     if (direct) {
@@ -1755,7 +1925,8 @@ static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStrea
   dim3 grid(S, a.n_head_kv, rows), block(64 * kAttnWaves);
   if constexpr (sizeof(KT) == 2 && HD <= 128) {
     if (attn_on_mfma(HD, 0, G)) {
-      hipLaunchKernelGGL((k_attn_mfma<HD>), grid, block, 0, s, a, chunk, S);
+      if (a.dq) hipLaunchKernelGGL((k_attn_mfma<HD, true>), grid, block, 0, s, a, chunk, S);
+      else hipLaunchKernelGGL((k_attn_mfma<HD, false>), grid, block, 0, s, a, chunk, S);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || S == 1 || a.batched) return e;
       hipLaunchKernelGGL(k_attn_combine, dim3(a.n_head), dim3(HD), 0, s, a.part_o, a.part_ml, S, HD,
@@ -1763,9 +1934,10 @@ static hipError_t launch_hd(const AttnArgs& a, int G, int chunk, int S, hipStrea
       return hipGetLastError();
     }
   }
-#define E3_ATTN_CASE(GG)                                                        \
-  case GG:                                                                    \
-    hipLaunchKernelGGL((k_attn<HD, GG, KT>), grid, block, 0, s, a, chunk, S); \
+#define E3_ATTN_CASE(GG)                                                                  \
+  case GG:                                                                              \
+    if (a.dq) hipLaunchKernelGGL((k_attn<HD, GG, KT, true>), grid, block, 0, s, a, chunk, S); \
+    else hipLaunchKernelGGL((k_attn<HD, GG, KT, false>), grid, block, 0, s, a, chunk, S);      \
     break;
   switch (G) {
     E3_ATTN_CASE(1)
@@ -1996,6 +2168,12 @@ hipError_t launch_attn_verify(const VerifyArgs& a, size_t workspace_bytes, hipSt
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (a.batched) return hipErrorInvalidValue;
+  // deferred QKV: fp32 or bf16 K/V, its register and LDS budgets (kDqPairs pairs per
+  // thread, at most 16 query heads), and one batch of candidates per thread
+  if (a.dq && (a.kv_q || !a.dq_hsum || !a.dqa.tok_tab || a.T < 1 ||
+               (a.n_head / a.n_head_kv + 2) * (a.head_dim / 2) > kDqPairs * 64 * kAttnWaves ||
+               a.n_head / a.n_head_kv > 16 || a.dqa.prev_count > kArgmaxBatch * 64 * kAttnWaves))
+    return hipErrorInvalidValue;
   int chunk, S;
   const int G = a.n_head / a.n_head_kv;
   if (!a.kv_q && attn_on_mfma(a.head_dim, a.kv_f32, G)) pick_split_mfma(a.T, a.n_head_kv, &chunk, &S);

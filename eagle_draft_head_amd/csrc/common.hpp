@@ -131,10 +131,20 @@ __device__ __forceinline__ void wave_reduce_scatter(float (&v)[32]) {
   v[0] += lane_exchange<1>(v[0]);
 }
 
+// sum of `count` per-block partial sums (this thread's share)
+__device__ __forceinline__ float sum_partials(const float* __restrict__ p, int count) {
+  float s = 0.f;
+  for (int i = threadIdx.x; i < count; i += blockDim.x) s += p[i];
+  return s;
+}
+
 // sum over the block of two values; `red` is LDS with room for 2 * waves floats.
-// Every thread gets the totals.
+// Every thread gets the totals.  NT: the block's thread count when known at compile
+// time (blockDim.x is a memory load, whose wait would also wait for every load
+// issued before it).
+template <int NT = 0>
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (NT ? NT : int(blockDim.x)) >> 6;
   a = wave_sum(a);
   b = wave_sum(b);
   if (lane == 0) { red[w] = a; red[nw + w] = b; }
@@ -174,12 +184,13 @@ struct ArgmaxBatch {
   int ix[kArgmaxBatch], t[kArgmaxBatch];
 };
 
+template <int NT = 0>
 __device__ __forceinline__ void argmax_load(const float* __restrict__ pv, const int32_t* __restrict__ pi,
                                             const int32_t* __restrict__ pt, int count, int b0,
                                             ArgmaxBatch& c) {
 #pragma unroll
   for (int j = 0; j < kArgmaxBatch; ++j) {
-    const int b = b0 + int(threadIdx.x) + j * int(blockDim.x);
+    const int b = b0 + int(threadIdx.x) + j * (NT ? NT : int(blockDim.x));
     const bool in = b < count;
     c.v[j] = in ? pv[b] : -INFINITY;
     c.ix[j] = in ? pi[b] : 0x7FFFFFFF;
@@ -196,7 +207,8 @@ __device__ __forceinline__ void argmax_load(const float* __restrict__ pv, const 
 // sv/si/st: LDS, one slot per wave (st only read when pt is given).  MORE = false:
 // the caller guarantees count <= kArgmaxBatch * blockDim.x (no further batches,
 // and no loop, whose loads would make the compiler wait for every load in flight).
-template <bool MORE = true>
+// NT: the block's thread count when known at compile time (as block_sum2).
+template <bool MORE = true, int NT = 0>
 __device__ __forceinline__ int block_argmax_from(const ArgmaxBatch& first, const float* __restrict__ pv,
                                                  const int32_t* __restrict__ pi,
                                                  const int32_t* __restrict__ pt, int count, float* sv,
@@ -221,7 +233,7 @@ __device__ __forceinline__ int block_argmax_from(const ArgmaxBatch& first, const
     const int ot = __shfl_xor(bt, o, kWave);
     if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; bt = ot; }
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (NT ? NT : int(blockDim.x)) >> 6;
   if (lane == 0) {
     sv[w] = bv;
     si[w] = bi;

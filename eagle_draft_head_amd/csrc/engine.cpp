@@ -54,7 +54,7 @@ namespace {
 
 thread_local std::string g_load_error;
 
-constexpr int kProfKernels = 9;
+constexpr int kProfKernels = 10;
 // gfx950 gives a workgroup up to 160 KB of LDS; the GEMVs keep one fp32
 // activation vector there (the down projection of a 5120-wide drafter: 68 KB)
 constexpr int64_t kMaxStageBytes = 128 * 1024;
@@ -132,9 +132,19 @@ struct eagle3_ctx {
   size_t kv_local_elems = 0;  // K + V elements per slot
 
   // token table of the chain step's QKV embedding half: [target_vocab][N_qkv] fp32
-  // rows of W_qkv[:, :n] . (input_layernorm * E[t]) in the repacked row order, and
-  // sum E[t]^2 per token (null when off)
+  // rows of W_qkv[:, :n] . (input_layernorm * E[t]) / rms(E[t]) in the repacked row
+  // order, and sum E[t]^2 per token, which the build uses (null when off)
   float *tok_tab = nullptr, *tok_ss = nullptr;
+  // deferred QKV of the batch-1 chain step (with the token table and bf16 weights):
+  // the hidden half of every QKV row, computed in the previous step's lm_head launch
+  // (or alone for a chain's first step) and finished by the attention kernel
+  float* hsum = nullptr;
+  bool defer_qkv = false;
+  // with the table (bf16 weights): the hidden half of W_qkv as a contiguous [N][n]
+  // matrix, the only part of W_qkv a chain step streams
+  uint16_t* w_qkv_h = nullptr;
+  const uint16_t* hid_rows() const { return w_qkv_h ? w_qkv_h : w_qkv + n; }
+  size_t hid_ldw() const { return w_qkv_h ? size_t(n) : size_t(2) * n; }
 
   int tf_rows = 0;
   size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
@@ -703,11 +713,26 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
             "int4 qkv split");
   }
   if (cfg->token_table != EAGLE3_TABLE_OFF) {
-    // the token table: passes of T tokens, input_layernorm * E as (hi, lo) bf16 planes
-    // in tf_A, one MFMA GEMM against the embedding half of the repacked W_qkv (int4:
-    // a second against the weights' lo halves, summed through tf_F)
+    // the token table: passes of T tokens, input_layernorm * E / rms(E) as (hi, lo) bf16
+    // planes in tf_A, one MFMA GEMM against the embedding half of the repacked W_qkv
+    // (int4: a second against the weights' lo halves, summed through tf_F)
     E3_TRY(dalloc(c, &c->tok_tab, size_t(vt) * N_qkv));
     E3_TRY(dalloc(c, &c->tok_ss, size_t(vt)));
+    if (!c->i4) {
+      // the hidden half as its own matrix: read in place, 8 KB-aligned halves of 16 KB
+      // rows, it streamed at about 60 % of the contiguous rate (measured in the fused
+      // lm_head launch: 55.6 against 51.5 us at the Qwen3-8B shape)
+      E3_TRY(dalloc(c, &c->w_qkv_h, N_qkv * n));
+      E3_TRYH(hipMemcpy2DAsync(c->w_qkv_h, size_t(n) * 2, c->w_qkv + n, size_t(2 * n) * 2, size_t(n) * 2, N_qkv,
+                               hipMemcpyDeviceToDevice, s),
+              "hidden-half copy");
+    }
+    if (!c->i4 && !c->kv_q) {
+      // EAGLE3_DEFER_QKV=0 keeps the fused QKV kernel (for comparison)
+      const char* dq = std::getenv("EAGLE3_DEFER_QKV");
+      c->defer_qkv = !(dq && dq[0] == '0') && c->lm_grid <= e3::kDqMaxCandidates;
+      if (c->defer_qkv) E3_TRY(dalloc(c, &c->hsum, N_qkv));
+    }
     E3_TRYH(e3::launch_tok_ss(c->embed, int(vt), int(n), c->tok_ss, s), "token table norms");
     int T = c->tf_rows;
     if (c->i4) T = int(std::min<size_t>(size_t(T), c->tf_F_cap / N_qkv));
@@ -716,7 +741,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
     uint16_t* A_lo = c->tf_A + size_t(T) * n;  // tf_A holds 3 n values per row
     for (int64_t r0 = 0; r0 < vt; r0 += T) {
       const int rows = int(std::min<int64_t>(T, vt - r0));
-      E3_TRYH(e3::launch_pack_embed(c->embed, c->nrm_in, int(r0), rows, int(n), A_hi, A_lo, s),
+      E3_TRYH(e3::launch_pack_embed(c->embed, c->nrm_in, c->tok_ss, c->cfg.rms_eps, int(r0), rows, int(n), A_hi, A_lo, s),
               "token table pack");
       e3::GemmPlan p = e3::gemm_plan(rows, int(N_qkv), int(n));
       p.splits = 1;  // one plane: the table rows are written in place
@@ -1422,16 +1447,25 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       }
       qa.gw = g->w_hid; qa.g_ssq = g->ssq; qa.g_ssq_count = g->count;
       qa.w_in = ctx->nrm_in; qa.pos = pos; qa.row = row; qa.q_out = ctx->q;
-      qa.tok_tab = ctx->tok_tab; qa.tok_ss = ctx->tok_ss;
+      qa.tok_tab = ctx->tok_tab; qa.w_hid_rows = ctx->w_qkv_h;
       qa.k_cache = kc; qa.v_cache = vc; qa.cap = cap;
       qa.kv_f32 = ctx->kv_f32;
       if (ctx->kv_q) {  // the new row goes to the fp32 stage; attention quantizes it
         qa.k_cache = ctx->kv_stage; qa.v_cache = ctx->kv_stage + ctx->kvd;
         qa.cap = 1; qa.row = 0; qa.kv_f32 = 1;
       }
-      {
+      const int N_qkv = (ctx->nh + 2 * ctx->nkv) * ctx->hd;
+      if (!ctx->defer_qkv) {
         ProfScope ps(ctx, 2, s, true);
         E3_HIP(ctx, e3::launch_qkv(qa, ctx->gcfg[e3::kGemvQkv], s), "qkv");
+      } else if (j == 0) {
+        // deferred QKV: the first step's hidden half alone (later steps' run in the
+        // lm_head launch of the step before); the attention kernel finishes the step
+        e3::QhArgs qh{ctx->hid_rows(), ctx->hid_ldw(), N_qkv, n, g->w_hid, g->ssq, g->count,
+                      ctx->cfg.rms_eps, ctx->hsum};
+        e3::LmHeadArgs none{};
+        ProfScope ps(ctx, 2, s, true);
+        E3_HIP(ctx, e3::launch_lmhead_qh(none, qh, ctx->gcfg[e3::kGemvLmHead], s), "qkv hidden half");
       }
       e3::AttnArgs aa{};
       aa.q = ctx->q; aa.k_cache = kc; aa.v_cache = vc; aa.cap = cap;
@@ -1439,6 +1473,11 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       aa.kv_q = ctx->kv_q; aa.kv_new = ctx->kv_q ? ctx->kv_stage : nullptr;
       aa.T = row + 1; aa.n_head = ctx->nh; aa.n_head_kv = ctx->nkv; aa.head_dim = ctx->hd;
       aa.part_o = ctx->part_o; aa.part_ml = ctx->part_ml; aa.out = ctx->ao;
+      if (ctx->defer_qkv) {
+        aa.dq = 1;
+        aa.dq_hsum = ctx->hsum;
+        aa.dqa = qa;
+      }
       {
         ProfScope ps(ctx, 5, s);
         E3_HIP(ctx, e3::launch_attn(aa, s), "attention");
@@ -1470,7 +1509,12 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       la.logits_dbg = (dbg && dbg->logits) ? dbg->logits + (size_t(b) * gamma + j) * ctx->dv : nullptr;
       la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;
       la.d2t = ctx->d2t; la.part_tok = ctx->lm_pt;
-      {
+      if (ctx->defer_qkv && j + 1 < ge) {  // with the next step's hidden-half QKV
+        e3::QhArgs qh{ctx->hid_rows(), ctx->hid_ldw(), N_qkv, n, gn->w_hid, gn->ssq, gn->count,
+                      ctx->cfg.rms_eps, ctx->hsum};
+        ProfScope ps(ctx, 9, s, true);
+        E3_HIP(ctx, e3::launch_lmhead_qh(la, qh, ctx->gcfg[e3::kGemvLmHead], s), "lm_head + qkv hidden half");
+      } else {
         ProfScope ps(ctx, 0, s, true);
         E3_HIP(ctx, e3::launch_lmhead(la, ctx->gcfg[e3::kGemvLmHead], s), "lm_head");
       }

@@ -12,9 +12,13 @@
 //                 in flight, then the embedding half; epilogue: 1/rms per half,
 //                 NeoX rotation (q/k rows repacked so partners are adjacent),
 //                 q to fp32, k/v rows to the KV cache
+//   k_qkv_tab     k_qkv with the token table: the embedding half is one table row,
+//                 only the hidden half streams (from its own contiguous copy)
 //   k_gemv_resid  y = W x + resid            -> y, y*w1, y*w2, partial sum y^2
 //   k_gateup      silu(gate . z) * (up . z) with z = x1*w_post/rms (rows interleaved)
 //   k_lmhead      logits = lm_head . (h*w_norm/rms) -> per-block (max, argmax)
+//   k_lmhead_qh   k_lmhead plus the next step's hidden-half QKV sums (deferred
+//                 QKV: the attention kernel finishes that step's q and K/V row)
 // The multi-vector kernel (teacher-forced rows) applies each weight chunk to
 // M activation vectors and splits K so the M vectors fit in LDS; it writes
 // split partials that the next kernel sums.
@@ -31,6 +35,7 @@
 #include "common.hpp"
 #include "gemv_cfg.hpp"
 #include "kernels.hpp"
+#include "qkv_token.hpp"
 
 namespace e3 {
 
@@ -397,12 +402,6 @@ hipError_t launch_quant_i4(const uint16_t* W, int rows, int K, uint8_t* Q, uint1
   return hipGetLastError();
 }
 
-// sum of `count` per-block partial sums (this thread's share)
-__device__ __forceinline__ float sum_partials(const float* __restrict__ p, int count) {
-  float s = 0.f;
-  for (int i = threadIdx.x; i < count; i += blockDim.x) s += p[i];
-  return s;
-}
 
 // Emit the R rows of a wave: y, y*w1, y*w2 (when given) and the block's sum of
 // y^2 (when given) as partial `slot`.  Every thread of the block must call it.
@@ -517,50 +516,6 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_encode
 
 // ---------------------------------------------------------------------------
 constexpr int kQkvERegs = 8;  // float4 chunks of the embedding row held per thread
-
-// finish the previous step (argmax over the lm_head candidates, d2t; the
-// candidates' target ids come with them when prev_tok is given) or take the
-// boundary token tok0; `first` is the candidates' first batch, already loaded;
-// every thread of the block calls it and gets the token
-template <bool MORE = true>
-__device__ __forceinline__ int qkv_token_from(const QkvArgs& a, const ArgmaxBatch& first, int tok0, float* sv,
-                                              int* si, int* st) {
-  int tok;
-  if (a.prev_count > 0) {
-    int bt;
-    int bi = block_argmax_from<MORE>(first, a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, sv, si, st, &bt);
-    const bool nan = bi < 0 || bi >= a.dv;  // every logit NaN
-    if (nan) tok = a.d2t[0];
-    else tok = a.prev_tok ? bt : bi + a.d2t[bi];
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      *a.prev_out_id = tok;
-      *a.tok_store = tok;
-      if (nan) atomicOr(a.status, kStatusNanLogits);
-    }
-  } else {
-    tok = tok0;
-  }
-  if (tok < 0 || tok >= a.vocab) {  // reads the nearest row, and says so
-    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(a.status, kStatusBadToken);
-    tok = min(max(tok, 0), a.vocab - 1);
-  }
-  return tok;
-}
-
-// the loads qkv_token_from needs: the candidates' first batch or the boundary token
-__device__ __forceinline__ int qkv_token_load(const QkvArgs& a, ArgmaxBatch& first) {
-  if (a.prev_count > 0) {
-    argmax_load(a.prev_val, a.prev_idx, a.prev_tok, a.prev_count, 0, first);
-    return 0;
-  }
-  return *a.tok;
-}
-
-__device__ __forceinline__ int qkv_token(const QkvArgs& a, float* sv, int* si, int* st) {
-  ArgmaxBatch first;
-  const int tok0 = qkv_token_load(a, first);
-  return qkv_token_from(a, first, tok0, sv, si, st);
-}
 
 // the fused epilogue of a wave's R rows: 1/rms per half, NeoX rotation of q/k
 // pairs, q to fp32, k/v rows to the KV cache
@@ -695,16 +650,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv_tab(QkvArgs a) {
   const int wv = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * WAVES + wv) * R;
 
+  // the hidden half's rows: a contiguous copy, or the second halves of W_qkv's rows
+  const uint16_t* wh = a.w_hid_rows ? a.w_hid_rows : a.w_qkv + n;
+  const size_t ldh = a.w_hid_rows ? size_t(n) : size_t(2) * n;
   ArgmaxBatch first;
   const int tok0 = qkv_token_load(a, first);
   uint4 wpf[U][R];
-  if constexpr (ISSUE) rows_issue<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, wpf);
+  if constexpr (ISSUE) rows_issue<R, U>(wh, ldh, row0, N, 0, wpf);
   const int tok = qkv_token_from<MORE>(a, first, tok0, sv, si, st);
   float acc_e[R], acc_g[R];
-  const float* trow = a.tok_tab + (size_t)tok * N;
+  const float* trow = a.tok_tab + (size_t)tok * N;  // already divided by rms(E[tok])
 #pragma unroll
   for (int r = 0; r < R; ++r) acc_e[r] = trow[min(row0 + r, N - 1)];
-  const float se = a.tok_ss[tok];
   // the hidden half: all of a thread's loads go out together (clamped indices; a
   // clamped store rewrites the last chunk with its own value), so it lands one
   // round trip after the weights at most
@@ -721,14 +678,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_qkv_tab(QkvArgs a) {
   }
   float sg = sum_partials(a.g_ssq, a.g_ssq_count);
   __syncthreads();  // hidden half staged
-  if constexpr (ISSUE) rows_dot_issued<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs, wpf, acc_g);
-  else rows_dot<R, U>(a.w_qkv, size_t(2) * n, row0, N, n, n, xs, acc_g);
+  if constexpr (ISSUE) rows_dot_issued<R, U>(wh, ldh, row0, N, 0, n, xs, wpf, acc_g);
+  else rows_dot<R, U>(wh, ldh, row0, N, 0, n, xs, acc_g);
   float zero = 0.f;
   block_sum2(zero, sg, red);  // every wave takes part
   if (row0 >= N) return;
-  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
   const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
-  qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+  qkv_epilogue<R>(a, row0, acc_e, acc_g, 1.0f, ig);
 }
 
 // k_qkv_q with the token table: only the hidden half's codes stream and only the
@@ -757,13 +713,11 @@ __global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_qkv_q_tab(QkvAr
   stage_plain(xs, a.gw, n);
   float sg = sum_partials(a.g_ssq, a.g_ssq_count);
   const int tok = qkv_token_from(a, first, tok0, sv, si, st);
-  const float* trow = a.tok_tab + (size_t)tok * N;
-  const float se = a.tok_ss[tok];
+  const float* trow = a.tok_tab + (size_t)tok * N;  // already divided by rms(E[tok])
   __syncthreads();  // hidden half staged
   quant_x_i4(xs, n, xpg, xeg);
   float zero = 0.f;
   block_sum2(zero, sg, red);  // its barriers also publish the quantised vector
-  const float ie = 1.0f / sqrtf(se / float(n) + a.eps);
   const float ig = 1.0f / sqrtf(sg / float(n) + a.eps);
   for (int vb = blockIdx.x;; vb += gridDim.x) {
     if (row0 < N) {
@@ -771,7 +725,7 @@ __global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_qkv_q_tab(QkvAr
       q_dot_issued<R, U>(Q, a.s_qkv, ldw, row0, N, n, n, Lg, xpg, xeg, acc_g);
 #pragma unroll
       for (int r = 0; r < R; ++r) acc_e[r] = trow[min(row0 + r, N - 1)];
-      qkv_epilogue<R>(a, row0, acc_e, acc_g, ie, ig);
+      qkv_epilogue<R>(a, row0, acc_e, acc_g, 1.0f, ig);
     }
     const int vn = vb + int(gridDim.x);
     if (vn >= nvb) break;
@@ -949,57 +903,77 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_gateup
 }
 
 // ---------------------------------------------------------------------------
+// The block's lm_head candidate for virtual block vb from its waves' R logits each:
+// the best (value, index) (lowest index on ties) and, with d2t, that index's target
+// id; dt is lane r's d2t of row row0 + r.  Every thread of the block calls it.
+template <int R, int WAVES>
+__device__ __forceinline__ void lm_candidates(const LmHeadArgs& a, const float (&acc)[R], int row0, float inv,
+                                              int dt, int vb, float* bv_s, int* bi_s, int* bt_s) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF, br = 0;
+  if (row0 < a.dv) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (row0 + r < a.dv) {
+        const float v = acc[r] * inv;
+        if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; br = r; }
+        if (a.logits_dbg && lane == r) a.logits_dbg[row0 + r] = v;
+      }
+    }
+  }
+  int bt = bi + __shfl(dt, br, kWave);
+  if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; bt_s[wv] = bt; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < WAVES; ++w)
+      if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; bt = bt_s[w]; }
+    a.part_val[vb] = bv;
+    a.part_idx[vb] = bi;
+    if (a.d2t) a.part_tok[vb] = bt;
+  }
+}
+
+// d2t of a wave's rows (lane r holds row0 + r's)
+template <int R>
+__device__ __forceinline__ int lm_d2t_of(const LmHeadArgs& a, int row0) {
+  const int lane = threadIdx.x & 63;
+  return (a.d2t && lane < R && row0 + lane < a.dv) ? a.d2t[row0 + lane] : 0;
+}
+
+// one block of the bf16 lm_head: rows [bid * WAVES * R, ...), candidate slot bid
+template <int WAVES, int R, int U>
+__device__ __forceinline__ void lmhead_bf16(const LmHeadArgs& a, int bid, float* xs, float* red, float* bv_s,
+                                            int* bi_s, int* bt_s) {
+  const int wv = threadIdx.x >> 6;
+  const int row0 = (bid * WAVES + wv) * R;
+  const int dt = lm_d2t_of<R>(a, row0);  // loaded before the stream
+  stage_plain(xs, a.hw, a.n);
+  float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
+  __syncthreads();
+  float acc[R];
+  if (row0 < a.dv) rows_dot<R, U>(a.w_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
+  block_sum2(ss, dummy, red);
+  lm_candidates<R, WAVES>(a, acc, row0, 1.0f / sqrtf(ss / float(a.n) + a.eps), dt, bid, bv_s, bi_s, bt_s);
+}
+
 template <int WAVES, int R, int U, bool I4>
 __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead(LmHeadArgs a) {
   extern __shared__ float xs[];  // [n]; int4: then the quantised vector
   __shared__ float red[32];
   __shared__ float bv_s[16];
   __shared__ int bi_s[16], bt_s[16];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // d2t of a wave's rows (lane r holds row0 + r's)
-  auto d2t_of = [&](int row0) { return (a.d2t && lane < R && row0 + lane < a.dv) ? a.d2t[row0 + lane] : 0; };
-  // the block's candidate for virtual block vb from the waves' R logits each
-  auto candidates = [&](const float (&acc)[R], int row0, float inv, int dt, int vb) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF, br = 0;
-    if (row0 < a.dv) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        if (row0 + r < a.dv) {
-          const float v = acc[r] * inv;
-          if (better(v, row0 + r, bv, bi)) { bv = v; bi = row0 + r; br = r; }
-          if (a.logits_dbg && lane == r) a.logits_dbg[row0 + r] = v;
-        }
-      }
-    }
-    int bt = bi + __shfl(dt, br, kWave);
-    if (lane == 0) { bv_s[wv] = bv; bi_s[wv] = bi; bt_s[wv] = bt; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 1; w < WAVES; ++w)
-        if (better(bv_s[w], bi_s[w], bv, bi)) { bv = bv_s[w]; bi = bi_s[w]; bt = bt_s[w]; }
-      a.part_val[vb] = bv;
-      a.part_idx[vb] = bi;
-      if (a.d2t) a.part_tok[vb] = bt;
-    }
-  };
-  int row0 = (blockIdx.x * WAVES + wv) * R;
   if constexpr (!I4) {
-    const int dt = d2t_of(row0);  // loaded before the stream
-    stage_plain(xs, a.hw, a.n);
-    float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
-    __syncthreads();
-    float acc[R];
-    if (row0 < a.dv) rows_dot<R, U>(a.w_lm, size_t(a.n), row0, a.dv, 0, a.n, xs, acc);
-    block_sum2(ss, dummy, red);
-    candidates(acc, row0, 1.0f / sqrtf(ss / float(a.n) + a.eps), dt, blockIdx.x);
+    lmhead_bf16<WAVES, R, U>(a, blockIdx.x, xs, red, bv_s, bi_s, bt_s);
   } else {
+    const int wv = threadIdx.x >> 6;
+    int row0 = (blockIdx.x * WAVES + wv) * R;
     const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.w_lm);
     const size_t ldw = size_t(a.n);
     const int nvb = (a.dv + WAVES * R - 1) / (WAVES * R);
     QLoad<R, U> L;
     if (row0 < a.dv) q_issue<R, U>(Q, a.s_lm, ldw, row0, a.dv, 0, a.n, L);
-    int dt = d2t_of(row0);
+    int dt = lm_d2t_of<R>(a, row0);
     stage_plain(xs, a.hw, a.n);
     float ss = sum_partials(a.h_ssq, a.h_ssq_count), dummy = 0.f;
     __syncthreads();
@@ -1014,11 +988,11 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead
       int dtn = 0;
       if (vn < nvb) {
         if (rn < a.dv) q_issue<R, U>(Q, a.s_lm, ldw, rn, a.dv, 0, a.n, Ln);
-        dtn = d2t_of(rn);
+        dtn = lm_d2t_of<R>(a, rn);
       }
       float acc[R];
       if (row0 < a.dv) q_dot_issued<R, U>(Q, a.s_lm, ldw, row0, a.dv, 0, a.n, L, xp, xe, acc);
-      candidates(acc, row0, inv, dt, vb);
+      lm_candidates<R, WAVES>(a, acc, row0, inv, dt, vb, bv_s, bi_s, bt_s);
       if (vn >= nvb) break;
       __syncthreads();  // the candidate slots are reused
       L = Ln;
@@ -1026,6 +1000,38 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead
       dt = dtn;
     }
   }
+}
+
+// The next step's hidden-half QKV sums (QhArgs, scaled by 1/rms(g)) in the first qb
+// blocks, the bf16 lm_head in the rest: two independent weight streams in one launch.
+// ISSUE (the hidden half alone, one wave of blocks): the first U chunk steps of the
+// weights go out before g is staged (K / 8 >= 64 U).
+template <int WAVES, int R, int U, bool ISSUE>
+__global__ __launch_bounds__(64 * WAVES) void k_lmhead_qh(LmHeadArgs a, QhArgs q, int qb) {
+  extern __shared__ float xs[];  // [n]
+  __shared__ float red[32];
+  __shared__ float bv_s[16];
+  __shared__ int bi_s[16], bt_s[16];
+  if (int(blockIdx.x) >= qb) {
+    lmhead_bf16<WAVES, R, U>(a, int(blockIdx.x) - qb, xs, red, bv_s, bi_s, bt_s);
+    return;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  uint4 wpf[ISSUE ? U : 1][R];
+  if constexpr (ISSUE) rows_issue<R, U>(q.w, q.ldw, row0, q.N, 0, wpf);
+  stage_plain(xs, q.gw, q.n);
+  float sg = sum_partials(q.g_ssq, q.g_ssq_count), dummy = 0.f;
+  __syncthreads();
+  float acc[R];
+  if constexpr (ISSUE) rows_dot_issued<R, U>(q.w, q.ldw, row0, q.N, 0, q.n, xs, wpf, acc);
+  else if (row0 < q.N) rows_dot<R, U>(q.w, q.ldw, row0, q.N, 0, q.n, xs, acc);
+  block_sum2(sg, dummy, red);  // every wave takes part
+  if (row0 >= q.N) return;
+  const float ig = 1.0f / sqrtf(sg / float(q.n) + q.eps);
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (lane == r && row0 + r < q.N) q.hsum[row0 + r] = acc[r] * ig;
 }
 
 // the last step of a chain: argmax over the lm_head candidates, d2t (the
@@ -1364,6 +1370,22 @@ hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
       E3_LAUNCH((k_lmhead<WV, RR, UU, false>), dim3(ceil_div(a.dv, WV * RR)),         \
                          dim3(64 * WV), xb, s, a);                                            \
     break;
+  E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_qh(const LmHeadArgs& a, const QhArgs& q, int cfg, hipStream_t s) {
+  if (a.s_lm || (q.n % 8) || (a.w_lm && a.n != q.n)) return hipErrorInvalidValue;
+  const size_t xb = size_t(q.n) * sizeof(float);
+#define CASE(ID, WV, RR, UU)                                                                 \
+  case ID: {                                                                                 \
+    const int qb = ceil_div(q.N, WV * RR), lb = a.w_lm ? ceil_div(a.dv, WV * RR) : 0;          \
+    if (!a.w_lm && (q.n >> 3) >= 64 * UU)                                                     \
+      E3_LAUNCH((k_lmhead_qh<WV, RR, UU, true>), dim3(qb), dim3(64 * WV), xb, s, a, q, qb);     \
+    else                                                                                       \
+      E3_LAUNCH((k_lmhead_qh<WV, RR, UU, false>), dim3(qb + lb), dim3(64 * WV), xb, s, a, q, qb); \
+  } break;
   E3_DISPATCH_CFG(cfg, CASE)
 #undef CASE
   return hipGetLastError();

@@ -95,11 +95,13 @@ struct QkvArgs {
   const float* g_ssq;      // per-block partial sums of g^2
   int g_ssq_count;
   const float* w_in;       // input_layernorm
-  // optional token table: tok_tab[t][r] = W_qkv[r, :n] . (w_in * E[t]) for every row r of
-  // the repacked QKV matrix, tok_ss[t] = sum E[t]^2; with it the embedding half of W_qkv
-  // is not streamed
+  // optional token table: tok_tab[t][r] = W_qkv[r, :n] . (w_in * E[t]) / rms(E[t]) for
+  // every row r of the repacked QKV matrix (the normalised embedding half); with it the
+  // embedding half of W_qkv is not streamed
   const float* tok_tab;
-  const float* tok_ss;
+  // with the table: the hidden half of W_qkv as its own contiguous [N][n] matrix (or
+  // NULL: the rows' second halves are read in place, 2n apart)
+  const uint16_t* w_hid_rows;
   int pos;                 // rotary position of the row
   int row;                 // KV row written (pos, or the step in a round-local scratch)
   float* q_out;
@@ -140,6 +142,28 @@ struct LmHeadArgs {
 };
 int lmhead_grid(int dv, int cfg);
 hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s);
+// The recurrent half of the next draft step's QKV projection: it needs only that
+// step's hidden state g, not its token, so it runs in the lm_head launch of the step
+// before (or alone for a chain's first step): hsum[r] = W_qkv[r, n:2n] . gw / rms(g)
+// for the N rows of the repacked QKV matrix, gw = g * hidden_norm.  The step's
+// attention kernel adds the token table's row, rotates, and stores the K/V row
+// (AttnArgs dq).
+struct QhArgs {
+  const uint16_t* w;      // row 0 of the hidden half: N rows of n bf16, ldw apart
+  size_t ldw;
+  int N, n;
+  const float* gw;
+  const float* g_ssq;     // per-block partial sums of g^2
+  int g_ssq_count;
+  float eps;
+  float* hsum;            // [N]: W_qkv[r, n:2n] . gw / rms(g)
+};
+// lm_head as launch_lmhead (same configuration and candidate count) and hsum in one
+// launch; with a.w_lm == NULL only hsum
+hipError_t launch_lmhead_qh(const LmHeadArgs& a, const QhArgs& q, int cfg, hipStream_t s);
+// the deferred-QKV attention reduces at most this many lm_head candidates (one batch
+// per thread of its 256-thread blocks)
+constexpr int kDqMaxCandidates = 2048;
 // argmax over the candidates, target = i + d2t[i] (taken from pt when given)
 // -> *out_id (and *tok_store if set)
 hipError_t launch_argmax_finalize(uint32_t* status, const float* pv, const int32_t* pi, const int32_t* pt, int count,
@@ -214,6 +238,14 @@ struct AttnArgs {
   int step;
   size_t seq_elems;
   BatchRows br;
+  // deferred QKV (dq != 0; batch 1, fp32 or bf16 K/V): the step's q and its new K/V
+  // row T - 1 are finished in this kernel from dq_hsum (QhArgs) and the token table
+  // row of the step's token (dqa: token source, table, norms' partial sums, rotary
+  // position, cache); q is then not read, and the block whose split holds row T - 1
+  // stores the row and takes it into its softmax from LDS
+  int dq;
+  const float* dq_hsum;
+  QkvArgs dqa;
 };
 int attn_max_splits(int cap, int head_dim, int n_head_kv);
 
@@ -447,8 +479,8 @@ hipError_t launch_gemm_tiled(const uint16_t* A_hi, const uint16_t* A_lo, int lda
                              int M, int N, int K, const GemmPlan& plan, hipStream_t s);
 // the token table's build: ss[t] = sum E[t]^2; rows [r0, r0 + T) of w_in * E as bf16 (hi, lo)
 hipError_t launch_tok_ss(const uint16_t* E, int vocab, int n, float* ss, hipStream_t s);
-hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, int r0, int T, int n, uint16_t* A_hi,
-                             uint16_t* A_lo, hipStream_t s);
+hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, const float* ss, float eps, int r0, int T,
+                             int n, uint16_t* A_hi, uint16_t* A_lo, hipStream_t s);
 // dst[i] += src[i], i < count
 hipError_t launch_add_f32(float* dst, const float* src, size_t count, hipStream_t s);
 // dst[i] = fp16 bits of (bf16 src[i]) * 2^8, exact for 2^-25 <= |src| < 256 (and 0);

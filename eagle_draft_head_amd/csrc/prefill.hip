@@ -102,8 +102,10 @@ __global__ __launch_bounds__(256) void k_pack_aux(const float* __restrict__ a0,
 // ---------------------------------------------------------------------------
 // The token table of the chain step's QKV embedding half (built at load):
 // k_tok_ss: ss[t] = sum of E[t]^2 (one block per token row);
-// k_pack_embed: rows [r0, r0 + T) of input_layernorm * E as bf16 (hi, lo) planes,
-// the activations of the table GEMM.  grid (ceil(n / 2048), T), 8 values a thread.
+// k_pack_embed: rows [r0, r0 + T) of input_layernorm * E / rms(E) as bf16 (hi, lo)
+// planes (rms from ss: sqrt(ss / n + eps)), the activations of the table GEMM, so the
+// table holds the normalised embedding half.  grid (ceil(n / 2048), T), 8 values a
+// thread.
 __global__ __launch_bounds__(256) void k_tok_ss(const uint16_t* __restrict__ E, int n, float* __restrict__ ss) {
   __shared__ float red[8];
   const uint16_t* row = E + (size_t)blockIdx.x * n;
@@ -127,15 +129,17 @@ __global__ __launch_bounds__(256) void k_tok_ss(const uint16_t* __restrict__ E, 
 }
 
 __global__ __launch_bounds__(256) void k_pack_embed(const uint16_t* __restrict__ E, const float* __restrict__ w_in,
-                                                    int r0, int T, int n, uint16_t* __restrict__ A_hi,
-                                                    uint16_t* __restrict__ A_lo) {
+                                                    const float* __restrict__ ss, float eps, int r0, int T, int n,
+                                                    uint16_t* __restrict__ A_hi, uint16_t* __restrict__ A_lo) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (t >= T || c >= n) return;
   const uint4 w = *reinterpret_cast<const uint4*>(E + (size_t)(r0 + t) * n + c);
   const float4 g0 = *reinterpret_cast<const float4*>(w_in + c), g1 = *reinterpret_cast<const float4*>(w_in + c + 4);
-  const float v[8] = {bf16_lo(w.x) * g0.x, bf16_hi(w.x) * g0.y, bf16_lo(w.y) * g0.z, bf16_hi(w.y) * g0.w,
-                      bf16_lo(w.z) * g1.x, bf16_hi(w.z) * g1.y, bf16_lo(w.w) * g1.z, bf16_hi(w.w) * g1.w};
+  const float ie = 1.0f / sqrtf(ss[r0 + t] / float(n) + eps);
+  const float v[8] = {bf16_lo(w.x) * g0.x * ie, bf16_hi(w.x) * g0.y * ie, bf16_lo(w.y) * g0.z * ie,
+                      bf16_hi(w.y) * g0.w * ie, bf16_lo(w.z) * g1.x * ie, bf16_hi(w.z) * g1.y * ie,
+                      bf16_lo(w.w) * g1.z * ie, bf16_hi(w.w) * g1.w * ie};
   uint16_t h[8], l[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -169,11 +173,12 @@ hipError_t launch_add_f32(float* dst, const float* src, size_t count, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, int r0, int T, int n, uint16_t* A_hi,
-                             uint16_t* A_lo, hipStream_t s) {
+hipError_t launch_pack_embed(const uint16_t* E, const float* w_in, const float* ss, float eps, int r0, int T, int n,
+                             uint16_t* A_hi, uint16_t* A_lo, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if ((n & 7) || T > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_pack_embed, dim3((n + 2047) / 2048, T), dim3(256), 0, s, E, w_in, r0, T, n, A_hi, A_lo);
+  hipLaunchKernelGGL(k_pack_embed, dim3((n + 2047) / 2048, T), dim3(256), 0, s, E, w_in, ss, eps, r0, T, n, A_hi,
+                     A_lo);
   return hipGetLastError();
 }
 

@@ -118,12 +118,13 @@ typedef struct {
 /* The embedding half of a chain step's QKV projection depends on the token alone:
    W_qkv[:, :n] . RMSNorm(E[tok]) = (W_qkv[:, :n] . (input_layernorm * E[tok])) /
    rms(E[tok]) (memra_engine `eagle.rs`, module doc "Op-sequence": the embedding is
-   normalised, concatenated first, then projected).  EAGLE3_TABLE_ON computes the
-   first factor for every target token at load into an fp32 table of target_vocab x
-   (n_head + 2 n_head_kv) head_dim values, plus sum(E[tok]^2) per token, and each
-   batch-1 chain step reads one table row instead of streaming the embedding half of
-   W_qkv (half of its QKV weight bytes).  The table is built by an MFMA GEMM whose
-   activations enter as bf16 (hi, lo) pairs (about 2^-17 relative), summed in fp32;
+   normalised, concatenated first, then projected).  EAGLE3_TABLE_ON computes that
+   value for every target token at load into an fp32 table of target_vocab x
+   (n_head + 2 n_head_kv) head_dim values, and each batch-1 chain step reads one
+   table row instead of streaming the embedding half of W_qkv (half of its QKV weight
+   bytes).  The table is built by an MFMA GEMM whose activations,
+   input_layernorm * E[tok] / rms(E[tok]) in fp32, enter as bf16 (hi, lo) pairs
+   (about 2^-17 relative), summed in fp32;
    with int4 weights it multiplies the weights' exact values (scale * q, as a bf16
    hi + lo pair: two GEMMs).  EAGLE3_TABLE_DEFAULT and EAGLE3_TABLE_ON build it;
    EAGLE3_TABLE_OFF streams both halves.  3.7 GB at the Qwen3-8B shape (151936 tokens
@@ -369,9 +370,11 @@ int eagle3_weights_i4_read(const eagle3_ctx *ctx, int32_t matrix, void *codes_de
 const char *eagle3_last_error(const eagle3_ctx *ctx);
 
 /* Timing of one kernel family with HIP events on the launching stream, for
-   measurement.  kernel: 0 = lm_head+argmax, 1 = gate/up+SwiGLU, 2 = fused QKV,
-   3 = down, 4 = o_proj, 5 = attention, 6 = fc encode, 7 = prefill fc GEMM,
-   8 = prefill K|V GEMM.  enable != 0 starts a fresh accumulation. */
+   measurement.  kernel: 0 = lm_head+argmax, 1 = gate/up+SwiGLU, 2 = fused QKV (or,
+   with the deferred QKV, the first step's hidden half), 3 = down, 4 = o_proj,
+   5 = attention, 6 = fc encode, 7 = prefill fc GEMM, 8 = prefill K|V GEMM,
+   9 = lm_head+argmax with the next step's hidden-half QKV (deferred QKV).
+   enable != 0 starts a fresh accumulation. */
 int eagle3_profile_enable(eagle3_ctx *ctx, int32_t kernel, int32_t enable);
 /* Synchronises the recorded events and returns the summed duration and count. */
 int eagle3_profile_read(eagle3_ctx *ctx, double *total_ms, int64_t *launches);
