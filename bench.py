@@ -55,15 +55,13 @@ def committed_traffic(kernel: str):
         txt = open(TRAFFIC_SUMMARY).read()
     except OSError:
         return None
-    vals = {}
     for line in txt.splitlines():
-        if line.startswith("traffic:"):
-            for kv in line[len("traffic:"):].split():
-                k, v = kv.split("=")
-                vals[k] = v
-    if vals.get("kernel") != kernel or vals.get("source") != kernel_source_digest():
-        return None
-    return float(vals["bytes_per_launch"])
+        if not line.startswith("traffic:"):
+            continue
+        vals = dict(kv.split("=") for kv in line[len("traffic:"):].split())
+        if vals.get("kernel") == kernel and vals.get("source") == kernel_source_digest():
+            return float(vals["bytes_per_launch"])
+    return None
 
 
 # HBM bytes per projection weight: bf16, or int4 codes plus one bf16 scale per 32
@@ -206,6 +204,9 @@ def main():
                     help="launch-overhead A/B: one chain round (boundary taps, rewound, so every round "
                          "runs at the same position) issued eagerly vs replayed from a captured HIP "
                          "graph of 1 and of 10 rounds; also the host time to issue one round")
+    ap.add_argument("--stream-sizes", action="store_true",
+                    help="the streaming read rate (the calibration kernel: the weight stream's access "
+                         "pattern) against the size of the buffer read, 16 MB to 1 GiB")
     ap.add_argument("--verify-attn", action="store_true",
                     help="time eagle3_verify_attention alone: the workload's KV heads over its "
                          "context plus a gamma+1-row window, against gamma+1 single-row calls")
@@ -224,6 +225,8 @@ def main():
     from synth import ALL, gen
 
     cfg = ALL[args.workload]
+    if args.stream_sizes:
+        return run_stream_sizes(args)
     if args.verify_attn:
         return run_verify_attn(args, cfg)
     if args.graph_ab:
@@ -587,6 +590,31 @@ def run_graph_ab(args, cfg):
         "config": {"workload": f"{cfg.name}: one gamma={gamma} chain round from boundary taps over {L} "
                                f"committed rows, rewound (every round at the same position)"}}),
         flush=True)
+
+
+def run_stream_sizes(args):
+    """Streaming read rate against buffer size: each read of a buffer follows an
+    untimed 2 GiB flush read (best of 5).  A launch pays a fixed ramp and drain, so
+    smaller reads see a lower rate."""
+    import torch
+    from eagle_draft_head_amd import binding as B
+    torch.cuda.set_device(0)
+    sink = torch.empty(B.CALIB_SINK_BYTES, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda").fill_(2)
+    rates = []
+    for mb in (16, 32, 64, 128, 262.144, 512, 1024):
+        nbytes = int(mb * 1e6) // 16 * 16 if mb != 1024 else 1 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        torch.cuda.synchronize()
+        gbs = B.eagle3_calibrate_stream(buf, nbytes, flush, flush.numel(), 5, sink)
+        rates.append({"bytes": nbytes, "gbs": round(gbs, 1), "us": round(nbytes / gbs / 1e3, 2)})
+        print(f"[bench] {nbytes / 1e6:8.1f} MB: {gbs:7.1f} GB/s ({nbytes / gbs / 1e3:.1f} us)", file=sys.stderr,
+              flush=True)
+        del buf
+    print(json.dumps({"metric": "streaming read rate by buffer size (HBM, after a 2 GiB flush read)",
+                      "unit": "GB/s", "peak": HBM_PEAK_GBS, "rates": rates,
+                      "how": "eagle3_calibrate_stream: each wave reads contiguous 16 KB runs with "
+                             "non-temporal 16-byte loads, four in flight per lane; best of 5"}), flush=True)
 
 
 def run_verify_attn(args, cfg):

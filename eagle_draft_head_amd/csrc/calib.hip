@@ -4,9 +4,10 @@
 //     v_mfma_f32_32x32x16_bf16 on register operands, with no memory traffic (the
 //     loop compiles to the four MFMAs and the counter; with the 16x16x32 form the
 //     compiler copies accumulators between the MFMAs);
-//   * its streaming HBM read rate: a coalesced 16-byte-per-lane read of a buffer,
-//     right after reading another buffer larger than the infinity cache, so the
-//     measured buffer comes from HBM.
+//   * its streaming HBM read rate: the weight stream's access pattern -- each wave
+//     reads contiguous 16 KB runs, a non-temporal 16-byte load per lane, four loads
+//     in flight per lane -- over a buffer read right after another buffer larger than
+//     the infinity cache, so the measured buffer comes from HBM.
 // Each is timed with HIP events over single launches, the best of several.
 #include <hip/hip_runtime.h>
 
@@ -43,13 +44,28 @@ __global__ __launch_bounds__(kCalThreads) void k_calib_mfma(int iters, float* __
   if (s == 1.2345e30f) out[blockIdx.x * blockDim.x + threadIdx.x] = s;  // keeps the chains
 }
 
+constexpr int kCalRun16 = 1024;  // 16-byte chunks of a wave's contiguous run (16 KB)
+constexpr int kCalReadU = 4;
+
+// waves take runs w, w + (waves in the grid), ...; the last run may be short (loads
+// are clamped to it)
 __global__ __launch_bounds__(kCalThreads) void k_calib_read(const uint4* __restrict__ p, size_t n16,
                                                             uint32_t* __restrict__ out) {
   uint32_t acc = 0;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  const int lane = threadIdx.x & 63;
+  const size_t wave = (size_t)blockIdx.x * (kCalThreads / 64) + (threadIdx.x >> 6);
+  const size_t waves = (size_t)gridDim.x * (kCalThreads / 64);
+  const size_t runs = (n16 + kCalRun16 - 1) / kCalRun16;
+  for (size_t r = wave; r < runs; r += waves) {
+    const uint4* q = p + r * kCalRun16;
+    const int len = int(min<size_t>(kCalRun16, n16 - r * kCalRun16));
+    for (int j = lane; j < len; j += 64 * kCalReadU) {
+      uint4 v[kCalReadU];
+#pragma unroll
+      for (int u = 0; u < kCalReadU; ++u) v[u] = ld_stream(q + min(j + 64 * u, len - 1));
+#pragma unroll
+      for (int u = 0; u < kCalReadU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
   }
   if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;  // keeps the loads
 }
