@@ -145,6 +145,15 @@ struct eagle3_ctx {
   uint16_t* w_qkv_h = nullptr;
   const uint16_t* hid_rows() const { return w_qkv_h ? w_qkv_h : w_qkv + n; }
   size_t hid_ldw() const { return w_qkv_h ? size_t(n) : size_t(2) * n; }
+  // the deferred QKV's hidden-half stream of g: bf16 rows, or the int4 codes of
+  // columns n .. 2n of W_qkv
+  e3::QhArgs qh_args(const GBuf& g) const {
+    const int N = (nh + 2 * nkv) * hd;
+    if (i4)
+      return e3::QhArgs{reinterpret_cast<const uint16_t*>(i4_qkv.q), i4_qkv.s, size_t(2) * n, n, N, n, g.w_hid,
+                        g.ssq, g.count, cfg.rms_eps, hsum};
+    return e3::QhArgs{hid_rows(), nullptr, hid_ldw(), 0, N, n, g.w_hid, g.ssq, g.count, cfg.rms_eps, hsum};
+  }
 
   int tf_rows = 0;
   size_t tf_F_cap = 0, tf_P_cap = 0;  // floats
@@ -727,7 +736,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
                                hipMemcpyDeviceToDevice, s),
               "hidden-half copy");
     }
-    if (!c->i4 && !c->kv_q) {
+    if (!c->kv_q) {
       // EAGLE3_DEFER_QKV=0 keeps the fused QKV kernel (for comparison)
       const char* dq = std::getenv("EAGLE3_DEFER_QKV");
       c->defer_qkv = !(dq && dq[0] == '0') && c->lm_grid <= e3::kDqMaxCandidates;
@@ -1461,8 +1470,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       } else if (j == 0) {
         // deferred QKV: the first step's hidden half alone (later steps' run in the
         // lm_head launch of the step before); the attention kernel finishes the step
-        e3::QhArgs qh{ctx->hid_rows(), ctx->hid_ldw(), N_qkv, n, g->w_hid, g->ssq, g->count,
-                      ctx->cfg.rms_eps, ctx->hsum};
+        const e3::QhArgs qh = ctx->qh_args(*g);
         e3::LmHeadArgs none{};
         ProfScope ps(ctx, 2, s, true);
         E3_HIP(ctx, e3::launch_lmhead_qh(none, qh, ctx->gcfg[e3::kGemvLmHead], s), "qkv hidden half");
@@ -1510,8 +1518,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       la.part_val = ctx->lm_pv; la.part_idx = ctx->lm_pi;
       la.d2t = ctx->d2t; la.part_tok = ctx->lm_pt;
       if (ctx->defer_qkv && j + 1 < ge) {  // with the next step's hidden-half QKV
-        e3::QhArgs qh{ctx->hid_rows(), ctx->hid_ldw(), N_qkv, n, gn->w_hid, gn->ssq, gn->count,
-                      ctx->cfg.rms_eps, ctx->hsum};
+        const e3::QhArgs qh = ctx->qh_args(*gn);
         ProfScope ps(ctx, 9, s, true);
         E3_HIP(ctx, e3::launch_lmhead_qh(la, qh, ctx->gcfg[e3::kGemvLmHead], s), "lm_head + qkv hidden half");
       } else {

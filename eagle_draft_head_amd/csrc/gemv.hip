@@ -957,17 +957,14 @@ __device__ __forceinline__ void lmhead_bf16(const LmHeadArgs& a, int bid, float*
   lm_candidates<R, WAVES>(a, acc, row0, 1.0f / sqrtf(ss / float(a.n) + a.eps), dt, bid, bv_s, bi_s, bt_s);
 }
 
-template <int WAVES, int R, int U, bool I4>
-__global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead(LmHeadArgs a) {
-  extern __shared__ float xs[];  // [n]; int4: then the quantised vector
-  __shared__ float red[32];
-  __shared__ float bv_s[16];
-  __shared__ int bi_s[16], bt_s[16];
-  if constexpr (!I4) {
-    lmhead_bf16<WAVES, R, U>(a, blockIdx.x, xs, red, bv_s, bi_s, bt_s);
-  } else {
+// The int4 lm_head's blocks: block bid of nblk covers virtual blocks (candidate slots)
+// bid, bid + nblk, ... of the dv rows
+template <int WAVES, int R, int U>
+__device__ __forceinline__ void lmhead_i4(const LmHeadArgs& a, int bid, int nblk, float* xs, float* red,
+                                          float* bv_s, int* bi_s, int* bt_s) {
+  {
     const int wv = threadIdx.x >> 6;
-    int row0 = (blockIdx.x * WAVES + wv) * R;
+    int row0 = (bid * WAVES + wv) * R;
     const uint8_t* Q = reinterpret_cast<const uint8_t*>(a.w_lm);
     const size_t ldw = size_t(a.n);
     const int nvb = (a.dv + WAVES * R - 1) / (WAVES * R);
@@ -982,8 +979,8 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead
     quant_x_i4(xs, a.n, xp, xe);
     block_sum2(ss, dummy, red);  // its barriers also publish the quantised vector
     const float inv = 1.0f / sqrtf(ss / float(a.n) + a.eps);
-    for (int vb = blockIdx.x;; vb += gridDim.x) {
-      const int vn = vb + int(gridDim.x), rn = (vn * WAVES + wv) * R;
+    for (int vb = bid;; vb += nblk) {
+      const int vn = vb + nblk, rn = (vn * WAVES + wv) * R;
       QLoad<R, U> Ln;
       int dtn = 0;
       if (vn < nvb) {
@@ -999,6 +996,19 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead
       row0 = rn;
       dt = dtn;
     }
+  }
+}
+
+template <int WAVES, int R, int U, bool I4>
+__global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead(LmHeadArgs a) {
+  extern __shared__ float xs[];  // [n]; int4: then the quantised vector
+  __shared__ float red[32];
+  __shared__ float bv_s[16];
+  __shared__ int bi_s[16], bt_s[16];
+  if constexpr (!I4) {
+    lmhead_bf16<WAVES, R, U>(a, blockIdx.x, xs, red, bv_s, bi_s, bt_s);
+  } else {
+    lmhead_i4<WAVES, R, U>(a, blockIdx.x, gridDim.x, xs, red, bv_s, bi_s, bt_s);
   }
 }
 
@@ -1032,6 +1042,50 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead_qh(LmHeadArgs a, QhArgs q
 #pragma unroll
   for (int r = 0; r < R; ++r)
     if (lane == r && row0 + r < q.N) q.hsum[row0 + r] = acc[r] * ig;
+}
+
+// k_lmhead_qh with int4 weights: the first qb blocks cover the nvq virtual blocks of
+// hidden-half rows (int4 codes of columns k0 .. k0 + n; g quantised once per block),
+// the next lb blocks the int4 lm_head's nvl virtual blocks (candidate slots)
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_lmhead_qh_i4(LmHeadArgs a, QhArgs q, int qb,
+                                                                                int nvq, int lb) {
+  extern __shared__ float xs[];  // [n], then the quantised vector
+  __shared__ float red[32];
+  __shared__ float bv_s[16];
+  __shared__ int bi_s[16], bt_s[16];
+  if (int(blockIdx.x) >= qb) {
+    lmhead_i4<WAVES, R, U>(a, int(blockIdx.x) - qb, lb, xs, red, bv_s, bi_s, bt_s);
+    return;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(q.w);
+  int row0 = (blockIdx.x * WAVES + wv) * R;
+  QLoad<R, U> L;
+  if (row0 < q.N) q_issue<R, U>(Q, q.s, q.ldw, row0, q.N, q.k0, q.n, L);
+  stage_plain(xs, q.gw, q.n);
+  float sg = sum_partials(q.g_ssq, q.g_ssq_count), dummy = 0.f;
+  __syncthreads();
+  uint4* xp = reinterpret_cast<uint4*>(xs + q.n);
+  int* xe = reinterpret_cast<int*>(xp + q.n / 8);
+  quant_x_i4(xs, q.n, xp, xe);
+  block_sum2(sg, dummy, red);  // its barriers also publish the quantised vector
+  const float ig = 1.0f / sqrtf(sg / float(q.n) + q.eps);
+  for (int vb = blockIdx.x;; vb += qb) {
+    const int vn = vb + qb, rn = (vn * WAVES + wv) * R;
+    QLoad<R, U> Ln;
+    if (vn < nvq && rn < q.N) q_issue<R, U>(Q, q.s, q.ldw, rn, q.N, q.k0, q.n, Ln);
+    if (row0 < q.N) {
+      float acc[R];
+      q_dot_issued<R, U>(Q, q.s, q.ldw, row0, q.N, q.k0, q.n, L, xp, xe, acc);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == r && row0 + r < q.N) q.hsum[row0 + r] = acc[r] * ig;
+    }
+    if (vn >= nvq) break;
+    L = Ln;
+    row0 = rn;
+  }
 }
 
 // the last step of a chain: argmax over the lm_head candidates, d2t (the
@@ -1376,8 +1430,23 @@ hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s) {
 }
 
 hipError_t launch_lmhead_qh(const LmHeadArgs& a, const QhArgs& q, int cfg, hipStream_t s) {
-  if (a.s_lm || (q.n % 8) || (a.w_lm && a.n != q.n)) return hipErrorInvalidValue;
+  const bool i4 = q.s != nullptr;
+  if ((a.w_lm && (a.n != q.n || (a.s_lm != nullptr) != i4)) || (q.n % (i4 ? 32 : 8)) || (q.k0 % (i4 ? 32 : 8)))
+    return hipErrorInvalidValue;
   const size_t xb = size_t(q.n) * sizeof(float);
+  if (i4) {
+#define CASE(ID, WV, RR, UU)                                                                              \
+  case ID: {                                                                                              \
+    const int nvq = ceil_div(q.N, WV * RR), qb = i4_grid(nvq);                                             \
+    const int lb = a.w_lm ? i4_grid(ceil_div(a.dv, WV * RR)) : 0;                                          \
+    E3_LDS_ALLOW((k_lmhead_qh_i4<WV, RR, UU>), xb + q_vec_bytes(q.n));                                     \
+    E3_LAUNCH((k_lmhead_qh_i4<WV, RR, UU>), dim3(qb + lb), dim3(64 * WV), xb + q_vec_bytes(q.n), s, a, q, qb, \
+              nvq, lb);                                                                                   \
+  } break;
+    E3_DISPATCH_CFG(cfg, CASE)
+#undef CASE
+    return hipGetLastError();
+  }
 #define CASE(ID, WV, RR, UU)                                                                 \
   case ID: {                                                                                 \
     const int qb = ceil_div(q.N, WV * RR), lb = a.w_lm ? ceil_div(a.dv, WV * RR) : 0;          \

@@ -149,8 +149,11 @@ hipError_t launch_lmhead(const LmHeadArgs& a, int cfg, hipStream_t s);
 // attention kernel adds the token table's row, rotates, and stores the K/V row
 // (AttnArgs dq).
 struct QhArgs {
-  const uint16_t* w;      // row 0 of the hidden half: N rows of n bf16, ldw apart
+  const uint16_t* w;      // bf16: row 0 of the hidden half (N rows of n values, ldw apart);
+                          // int4: the codes of W_qkv (columns k0 .. k0 + n of N rows of ldw)
+  const uint16_t* s;      // int4 scales (w then holds codes), or NULL
   size_t ldw;
+  int k0;                 // int4: the hidden half's first column (n); bf16: 0
   int N, n;
   const float* gw;
   const float* g_ssq;     // per-block partial sums of g^2
