@@ -227,6 +227,66 @@ def test_deferred_qkv_matches_the_fused_qkv_kernel(cfg, kv, weights, monkeypatch
         dr.close()
 
 
+@pytest.mark.parametrize("hd,nh,nkv,kv", [(128, 4, 2, "f32"), (128, 4, 2, "bf16"), (256, 4, 1, "f32"),
+                                          (256, 4, 1, "bf16")],
+                         ids=["hd128-f32", "hd128-bf16-mfma", "hd256-f32", "hd256-bf16"])
+def test_deferred_qkv_at_split_boundaries(hd, nh, nkv, kv, monkeypatch):
+    """The deferred QKV's new row is taken into the softmax from LDS by the block whose
+    split holds it; with 16-, 32- or 64-row splits (fp32 and bf16 on the VALU kernel,
+    bf16 at head_dim 128 on the MFMA kernel) contexts of 0 to 2048 rows put the new row
+    first, last and alone in its split.  Against the fused QKV kernel: ids equal up to
+    near-ties, logits and hidden within 1e-5 (bf16 K/V: 1e-3), every chain K/V row
+    within the same bars."""
+    from eagle_draft_head_amd.drafter import Drafter
+    cfg = small_variant(f"dq-hd{hd}", head_dim=hd, n_head=nh, n_head_kv=nkv, max_ctx=2200)
+    wd, _ = weights_both(cfg)
+    gamma = 4
+    kvd = B.KV_BF16 if kv == "bf16" else B.KV_F32
+
+    def make():
+        return Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=2200, max_gamma=8, kv_dtype=kvd)
+
+    monkeypatch.setenv("EAGLE3_DEFER_QKV", "0")
+    ref = make()
+    monkeypatch.delenv("EAGLE3_DEFER_QKV")
+    dq = make()
+    Lmax = 2048
+    aux = aux_np(cfg, 0, Lmax)
+    toks = toks_np(cfg, 0, Lmax)
+    baux = aux_np(cfg, 1, 16)
+    btok = toks_np(cfg, 1, 16)
+    tol = 1e-3 if kv == "bf16" else 1e-5
+    have = 0  # committed rows (rewind only shrinks: contexts grow by prefilled pieces)
+    for r, L in enumerate([0, 1, 15, 16, 63, 64, 65, 127, 128, 511, 512, 1023, 2044, 2047]):
+        say(f"[deferred qkv boundaries] hd={hd} kv={kv} L={L}")
+        if L > have:
+            for dr in (dq, ref):
+                dr.prefill(0, _tok(toks[have:L]), to_dev_aux([a[have:L] for a in aux]))
+            have = L
+        res = []
+        for dr in (dq, ref):
+            out, geff, logits, hidden = dr.draft_chain([0], _tok([btok[r % 16]]), to_dev_aux(baux, slice(r % 16, r % 16 + 1)),
+                                                       gamma, debug=True, keep_spec=True)
+            torch.cuda.synchronize()
+            rows = [x.double().cpu() for x in dr.kv_read(0, L, gamma)]
+            res.append((out.cpu(), int(geff[0]), logits.double().cpu(), hidden.double().cpu(), rows))
+            dr.rewind(0, L)
+        (o1, g1, l1, h1, kv1), (o2, g2, l2, h2, kv2) = res
+        assert g1 == g2 == gamma
+        top2 = torch.topk(l2[0, :g2], 2, dim=-1).values
+        gap = (top2[:, 0] - top2[:, 1]).abs()
+        ok = int(torch.nonzero(gap < 1e-4).min()) if bool((gap < 1e-4).any()) else g2
+        assert torch.equal(o1[0, :ok], o2[0, :ok]), (L, o1, o2)
+        for j in range(min(ok + 1, g2)):
+            assert (l1[0, j] - l2[0, j]).norm() / l2[0, j].norm() < tol, (L, j)
+            for a1, a2 in zip(kv1, kv2):
+                assert (a1[j] - a2[j]).norm() / a2[j].norm() < tol, (L, j)
+        for j in range(min(ok + 2, g2 + 1)):
+            assert (h1[0, j] - h2[0, j]).norm() / h2[0, j].norm() < tol, (L, j)
+    for dr in (dq, ref):
+        dr.close()
+
+
 def test_chain_from_empty_cache():
     pinned, steps = _run_rounds(TINY, rounds=10, L=0, gamma=5)
     assert steps == 50
