@@ -263,13 +263,15 @@ def main():
     global WB, TABLE
     WB = WB_I4 if i4 else WB_BF16
     TABLE = args.token_table != "off"
+    # with the token table (bf16 weights, not q8q5 K/V) the engine runs lm_head together
+    # with the next step's hidden-half QKV (deferred QKV) in every step but a chain's
+    # last; with stored boundaries the first step's hidden half is computed by the
+    # append that stores the boundary (in its K/V launch), so a chain streams it gamma-1
+    # times, not gamma
+    deferred = (TABLE and not i4 and args.kv != "q8q5" and os.environ.get("EAGLE3_DEFER_QKV", "1") != "0")
+    first_in_append = deferred and stored and os.environ.get("EAGLE3_BOUNDARY_QH", "1") != "0"
     if args.kernel is None:
-        # the dominant kernel: with the token table and bf16 weights the engine runs
-        # lm_head together with the next step's hidden-half QKV (deferred QKV) in every
-        # step but a chain's last
-        deferred = (TABLE and not i4 and args.kv != "q8q5" and gamma > 1
-                    and os.environ.get("EAGLE3_DEFER_QKV", "1") != "0")
-        args.kernel = "lm_head_qkv" if deferred else "lm_head"
+        args.kernel = "lm_head_qkv" if deferred and gamma > 1 else "lm_head"
     dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, max_gamma=max(8, gamma), kv_dtype=kv_dtype,
                  weight_format=B.WEIGHTS_I4 if i4 else B.WEIGHTS_BF16,
                  append_act={"default": B.APPEND_DEFAULT, "split": B.APPEND_SPLIT, "bf16": B.APPEND_BF16,
@@ -399,6 +401,11 @@ def main():
         sb = [step_bytes(cfg, L_at[i], gamma, accepted[i], kvb, stored) for i in range(args.warmup, nsteps)]
     step_gbs = (sum(sb) / args.steps) / (elapsed / args.steps) / 1e9
 
+    # a draft step's bytes as the chain streams them (the first step's hidden half
+    # comes from the append when first_in_append)
+    chain_b = kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
+    if first_in_append:
+        chain_b -= WB * cfg.n_embd * (cfg.q_dim + 2 * cfg.kv_dim) / gamma
     cal = calibrate(B, torch)
     cpu = None
     if not args.no_cpu:
@@ -447,12 +454,11 @@ def main():
         "chain_ms_p50": round(pct(chain_ms, 0.5), 4),
         "encode_us": round(encode_us, 2),
         "draft_step_us": round(per_step_us, 2),
-        "draft_step_hbm_frac": round(kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
-                                     / (per_step_us * 1e-6) / 1e9
-                                     / HBM_PEAK_GBS, 4),
-        "draft_step_hbm_frac_calibrated": round(kernel_bytes_step(cfg, 0 if local else L, gamma, kvb)
-                                                / (per_step_us * 1e-6) / 1e9
+        "draft_step_bytes": round(chain_b),
+        "draft_step_hbm_frac": round(chain_b / (per_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "draft_step_hbm_frac_calibrated": round(chain_b / (per_step_us * 1e-6) / 1e9
                                                 / cal["hbm_stream_read_gbs"], 4),
+        "first_hidden_half_in_append": first_in_append,
         "prefill": {"rows": L, "ms": round(prefill_s * 1e3, 3), "append_act": args.append,
                     "tflops": round(prefill_flop / prefill_s / 1e12, 2),
                     "frac_bf16_peak": round(prefill_flop / prefill_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),

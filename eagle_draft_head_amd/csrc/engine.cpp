@@ -140,6 +140,12 @@ struct eagle3_ctx {
   // (or alone for a chain's first step) and finished by the attention kernel
   float* hsum = nullptr;
   bool defer_qkv = false;
+  // with the deferred QKV (bf16 weights): the hidden-half sums of each slot's stored
+  // boundary feature [max_seqs][N_qkv], computed by the append pass that writes the
+  // feature (its K/V launch); bnd_hsum_ok[slot] says whether the slot's current
+  // feature came with them (EAGLE3_BOUNDARY_QH=0: never, for comparison)
+  float* bnd_hsum = nullptr;
+  std::vector<uint8_t> bnd_hsum_ok;
   // with the table (bf16 weights): the hidden half of W_qkv as a contiguous [N][n]
   // matrix, the only part of W_qkv a chain step streams
   uint16_t* w_qkv_h = nullptr;
@@ -741,6 +747,11 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
       const char* dq = std::getenv("EAGLE3_DEFER_QKV");
       c->defer_qkv = !(dq && dq[0] == '0') && c->lm_grid <= e3::kDqMaxCandidates;
       if (c->defer_qkv) E3_TRY(dalloc(c, &c->hsum, N_qkv));
+      const char* bq = std::getenv("EAGLE3_BOUNDARY_QH");
+      if (c->defer_qkv && !c->i4 && !(bq && bq[0] == '0')) {
+        E3_TRY(dalloc(c, &c->bnd_hsum, size_t(cfg->max_seqs) * N_qkv));
+        c->bnd_hsum_ok.assign(size_t(cfg->max_seqs), 0);
+      }
     }
     E3_TRYH(e3::launch_tok_ss(c->embed, int(vt), int(n), c->tok_ss, s), "token table norms");
     int T = c->tf_rows;
@@ -991,6 +1002,10 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       bo.ssq = c->bnd_ssq;
       bo.count = Tb;
       for (int j = 0; j < Tb; ++j) bo.slot[j] = bi.slots[size_t(b0 + j)];
+      // a new boundary feature: its hidden-half sums are stale until this pass's
+      // K/V launch computes them (below, when it does)
+      if (c->bnd_hsum)
+        for (int j = 0; j < Tb; ++j) c->bnd_hsum_ok[size_t(bo.slot[j])] = 0;
     }
     int sp1 = 1, sp2 = 1;
     size_t f_split = 0, p_split = 0;
@@ -1007,7 +1022,19 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
       E3_HIP(c, e3::launch_tf_cat(c->status, c->tf_F, sp1, f_split, T, n, c->embed, c->vt, tok + c0, c->nrm_in,
                                   c->nrm_hid, c->cfg.rms_eps, nullptr, nullptr, c->tf_cat32, s, &bo),
              "tf cat");
-      if (T > 0) {
+      // the boundary row's hidden-half QKV sums ride in the K/V launch (one boundary
+      // row with teacher-forced rows in the pass)
+      if (T > 0 && Tb == 1 && c->bnd_hsum) {
+        const int slot = bo.slot[0];
+        e3::QhArgs q = c->qh_args(eagle3_ctx::GBuf{c->bnd_y + size_t(slot) * n, c->bnd_w + size_t(slot) * n,
+                                                   nullptr, c->bnd_ssq + slot, 1});
+        q.hsum = c->bnd_hsum + size_t(slot) * q.N;
+        ProfScope ps(c, 8, s);
+        E3_HIP(c, e3::launch_gemv_multi_qh(c->w_qkv + size_t(c->qd) * 2 * n, kvd2, 2 * n, c->tf_cat32, T, c->tf_P,
+                                           &sp2, q, s),
+               "kv gemv + boundary qkv hidden half");
+        c->bnd_hsum_ok[size_t(slot)] = 1;
+      } else if (T > 0) {
         ProfScope ps(c, 8, s);
         // the K and V rows of the fused QKV matrix
         E3_HIP(c, e3::launch_gemv_multi(c->wq(c->w_qkv, c->i4_qkv, size_t(c->qd), 2 * n),
@@ -1432,6 +1459,11 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
              "encode");
     }
     const eagle3_ctx::GBuf* g = stored ? &g_bnd : &ctx->gb[0];
+    // the first step's hidden-half sums, when the append that stored the boundary
+    // feature computed them
+    const float* hsum0 = (stored && ctx->defer_qkv && ctx->bnd_hsum && ctx->bnd_hsum_ok[size_t(sq)])
+                             ? ctx->bnd_hsum + size_t(sq) * ((ctx->nh + 2 * ctx->nkv) * ctx->hd)
+                             : nullptr;
     if (dbg && dbg->hidden)
       E3_HIP(ctx, hipMemcpyAsync(dbg->hidden + size_t(b) * (gamma + 1) * n, g->y,
                                  size_t(n) * 4, hipMemcpyDeviceToDevice, s), "dbg hidden");
@@ -1467,7 +1499,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       if (!ctx->defer_qkv) {
         ProfScope ps(ctx, 2, s, true);
         E3_HIP(ctx, e3::launch_qkv(qa, ctx->gcfg[e3::kGemvQkv], s), "qkv");
-      } else if (j == 0) {
+      } else if (j == 0 && !hsum0) {
         // deferred QKV: the first step's hidden half alone (later steps' run in the
         // lm_head launch of the step before); the attention kernel finishes the step
         const e3::QhArgs qh = ctx->qh_args(*g);
@@ -1483,7 +1515,7 @@ int eagle3_draft_chain(eagle3_ctx* ctx, int32_t n_seq, const int32_t* seq_ids_ho
       aa.part_o = ctx->part_o; aa.part_ml = ctx->part_ml; aa.out = ctx->ao;
       if (ctx->defer_qkv) {
         aa.dq = 1;
-        aa.dq_hsum = ctx->hsum;
+        aa.dq_hsum = (j == 0 && hsum0) ? hsum0 : ctx->hsum;
         aa.dqa = qa;
       }
       {

@@ -21,13 +21,16 @@
 //                 QKV: the attention kernel finishes that step's q and K/V row)
 // The multi-vector kernel (teacher-forced rows) applies each weight chunk to
 // M activation vectors and splits K so the M vectors fit in LDS; it writes
-// split partials that the next kernel sums.
+// split partials that the next kernel sums.  k_gemv_multi_qh is its K/V pass
+// with the hidden-half QKV sums of the boundary feature the pass writes in the
+// same launch (the next chain's first step then starts at its attention).
 //
 // Work split: a wave owns R consecutive rows; lane l reads 16-byte chunks
 // l, l+64, ... of each row (1 KB per row per wave instruction); U chunk steps
 // are issued before their FMAs so each lane keeps U*R loads in flight.  The
 // per-row sums are reduced across the wave at the end.  No block ever waits
 // for another block: cross-block reductions happen in the next kernel.
+#include <algorithm>
 #include <cstdlib>
 
 #include <hip/hip_ext.h>
@@ -1016,18 +1019,12 @@ __global__ __launch_bounds__(64 * WAVES, I4 ? kI4WavesPerSimd : 1) void k_lmhead
 // blocks, the bf16 lm_head in the rest: two independent weight streams in one launch.
 // ISSUE (the hidden half alone, one wave of blocks): the first U chunk steps of the
 // weights go out before g is staged (K / 8 >= 64 U).
+// One block's hidden-half QKV sums: each wave owns R rows of the N hidden-half rows
+// (ISSUE: its first U chunk steps are in flight before gw is staged)
 template <int WAVES, int R, int U, bool ISSUE>
-__global__ __launch_bounds__(64 * WAVES) void k_lmhead_qh(LmHeadArgs a, QhArgs q, int qb) {
-  extern __shared__ float xs[];  // [n]
-  __shared__ float red[32];
-  __shared__ float bv_s[16];
-  __shared__ int bi_s[16], bt_s[16];
-  if (int(blockIdx.x) >= qb) {
-    lmhead_bf16<WAVES, R, U>(a, int(blockIdx.x) - qb, xs, red, bv_s, bi_s, bt_s);
-    return;
-  }
+__device__ __forceinline__ void qh_block(const QhArgs& q, int bid, float* xs, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  const int row0 = (bid * WAVES + wv) * R;
   uint4 wpf[ISSUE ? U : 1][R];
   if constexpr (ISSUE) rows_issue<R, U>(q.w, q.ldw, row0, q.N, 0, wpf);
   stage_plain(xs, q.gw, q.n);
@@ -1042,6 +1039,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead_qh(LmHeadArgs a, QhArgs q
 #pragma unroll
   for (int r = 0; r < R; ++r)
     if (lane == r && row0 + r < q.N) q.hsum[row0 + r] = acc[r] * ig;
+}
+
+template <int WAVES, int R, int U, bool ISSUE>
+__global__ __launch_bounds__(64 * WAVES) void k_lmhead_qh(LmHeadArgs a, QhArgs q, int qb) {
+  extern __shared__ float xs[];  // [n]
+  __shared__ float red[32];
+  __shared__ float bv_s[16];
+  __shared__ int bi_s[16], bt_s[16];
+  if (int(blockIdx.x) >= qb) {
+    lmhead_bf16<WAVES, R, U>(a, int(blockIdx.x) - qb, xs, red, bv_s, bi_s, bt_s);
+    return;
+  }
+  qh_block<WAVES, R, U, ISSUE>(q, int(blockIdx.x), xs, red);
 }
 
 // k_lmhead_qh with int4 weights: the first qb blocks cover the nvq virtual blocks of
@@ -1126,23 +1136,21 @@ struct MultiShape {
   static constexpr int ROWS = WAVES * R;
 };
 
+// one block: row block bx of the weights over K chunk z; xs holds [M][kc] floats
 template <int M, bool I4>
-__global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__ W,
-                                                    const uint16_t* __restrict__ S, int N, int K,
-                                                    int kc, const float* __restrict__ x0,
-                                                    const float* __restrict__ x1,
-                                                    const float* __restrict__ x2, int seg,
-                                                    int rows, float* __restrict__ P,
-                                                    const TapRowsB yb) {
+__device__ __forceinline__ void gemv_multi_block(int bx, int z, const uint16_t* __restrict__ W,
+                                                 const uint16_t* __restrict__ S, int N, int K, int kc,
+                                                 const float* __restrict__ x0, const float* __restrict__ x1,
+                                                 const float* __restrict__ x2, int seg, int rows,
+                                                 float* __restrict__ P, const TapRowsB& yb, float* xs) {
   constexpr int R = MultiShape<M>::R;
   constexpr int WAVES = MultiShape<M>::WAVES;
-  extern __shared__ float xs[];  // [M][kc]
-  const int z = blockIdx.y;
+  constexpr int NT = 64 * WAVES;
   const int k0 = z * kc;
   const int klen = min(kc, K - k0);
   const int k4 = klen >> 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * WAVES + wv) * R;
+  const int row0 = (bx * WAVES + wv) * R;
   const int nch = I4 ? (klen >> 5) : (klen >> 3);  // 16-byte chunks of the K range
   const uint4* wp[R];
   const uint16_t* sp[R];
@@ -1163,7 +1171,7 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
     float4* dst = reinterpret_cast<float4*>(xs);
     const int total = M * k4;
 #pragma unroll 4
-    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < total; idx += NT) {
       const int m = idx / k4, i = idx - m * k4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (m < rows) {
@@ -1271,6 +1279,41 @@ __global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__
     const int r = j / M, m = j - r * M;
     if (row0 + r < N) P[((size_t)z * M + m) * N + row0 + r] = v[0];
   }
+}
+
+template <int M, bool I4>
+__global__ __launch_bounds__(512) void k_gemv_multi(const uint16_t* __restrict__ W,
+                                                    const uint16_t* __restrict__ S, int N, int K,
+                                                    int kc, const float* __restrict__ x0,
+                                                    const float* __restrict__ x1,
+                                                    const float* __restrict__ x2, int seg,
+                                                    int rows, float* __restrict__ P,
+                                                    const TapRowsB yb) {
+  static_assert(MultiShape<M>::WAVES == 8, "512 threads");
+  extern __shared__ float xs[];  // [M][kc]
+  gemv_multi_block<M, I4>(int(blockIdx.x), int(blockIdx.y), W, S, N, K, kc, x0, x1, x2, seg, rows, P, yb, xs);
+}
+
+// The K/V rows of a teacher-forced pass (bf16 weights, one fp32 activation matrix)
+// and, in the same launch, the hidden-half QKV sums of the boundary feature the pass
+// writes (the next chain's first step; qh_block in its 8-wave, 2-row form): blocks
+// [0, qb) the sums, the rest the (row block, K chunk) grid of the multi-vector GEMV,
+// gx row blocks per chunk
+template <int M>
+__global__ __launch_bounds__(512) void k_gemv_multi_qh(const uint16_t* __restrict__ W, int N, int K, int kc,
+                                                       const float* __restrict__ x0, int rows,
+                                                       float* __restrict__ P, QhArgs q, int qb, int gx) {
+  static_assert(MultiShape<M>::WAVES == 8, "512 threads");
+  extern __shared__ float xs[];  // [max(M * kc, n)]
+  __shared__ float red[32];
+  const int b = int(blockIdx.x);
+  if (b < qb) {
+    qh_block<8, 2, 4, false>(q, b, xs, red);
+    return;
+  }
+  const int t = b - qb;
+  const TapRowsB none{{nullptr, nullptr, nullptr}, 1 << 30};
+  gemv_multi_block<M, false>(t % gx, t / gx, W, nullptr, N, K, kc, x0, nullptr, nullptr, 0, rows, P, none, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1527,6 +1570,30 @@ hipError_t launch_gemv_multi(const uint16_t* W, const uint16_t* S, int N, int K,
     else                                                                                       \
       hipLaunchKernelGGL((k_gemv_multi<MM, false>), grid, block, lds, s, W, S, N, K, kc, x0, x1,  \
                          x2, seg, rows, P, yb);                                                \
+    break;
+    MCASE(1) MCASE(2) MCASE(3) MCASE(4) MCASE(5) MCASE(6) MCASE(8) MCASE(9) MCASE(12) MCASE(16)
+#undef MCASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_multi_qh(const uint16_t* W, int N, int K, const float* x0, int rows, float* P,
+                                int* splits_out, const QhArgs& q, hipStream_t s) {
+  const int m = gemv_multi_width(rows);
+  if (m < 0 || (K % 8) || q.s || (q.n % 8) || q.N < 1) return hipErrorInvalidValue;
+  const int kc = multi_kchunk(m, N, K);
+  const int splits = ceil_div(K, kc);
+  *splits_out = splits;
+  const int gx = ceil_div(N, multi_rows_per_block(m)), qb = ceil_div(q.N, 16);
+  const size_t lds = std::max(size_t(m) * kc, size_t(q.n)) * sizeof(float);
+  switch (m) {
+#define MCASE(MM)                                                                                  \
+  case MM:                                                                                         \
+    E3_LDS_ALLOW((k_gemv_multi_qh<MM>), lds);                                                      \
+    E3_LAUNCH((k_gemv_multi_qh<MM>), dim3(qb + gx * splits), dim3(512), lds, s, W, N, K, kc, x0, rows, P, q, \
+              qb, gx);                                                                             \
     break;
     MCASE(1) MCASE(2) MCASE(3) MCASE(4) MCASE(5) MCASE(6) MCASE(8) MCASE(9) MCASE(12) MCASE(16)
 #undef MCASE

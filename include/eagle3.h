@@ -48,7 +48,14 @@ enum {
 #define EAGLE3_KEEP_SPEC 1u
 /* eagle3_draft_chain flag: start each listed sequence from its stored boundary
    feature (set by eagle3_prefill / eagle3_rebuild_after_verify from next-boundary
-   taps) instead of encoding taps; the tap pointers must then be NULL. */
+   taps) instead of encoding taps; the tap pointers must then be NULL.  With the
+   token table and bf16 weights, an append pass of at most 16 rows that stores one
+   boundary feature with teacher-forced rows also computes the hidden half of that
+   feature's QKV projection (in its K/V launch), and the batch-1 chain that starts
+   from it runs no launch of its own for it (environment EAGLE3_BOUNDARY_QH=0 turns
+   this off).  Which launches a stored-boundary round issues thus depends on the
+   append that stored the feature: a round captured in a graph replays the launches
+   of its capture, so replay it only over the same stored feature. */
 #define EAGLE3_STORED_BOUNDARY 2u
 /* eagle3_draft_chain flag: the round-local drafter (memra_engine `eagle.rs`,
    `Eagle3Scratch`: the draft KV is a small scratch emptied every round).  Step j

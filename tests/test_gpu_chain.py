@@ -287,6 +287,89 @@ def test_deferred_qkv_at_split_boundaries(hd, nh, nkv, kv, monkeypatch):
         dr.close()
 
 
+@pytest.mark.parametrize("cfg", [TINY, small_variant()], ids=["tiny", "ragged"])
+def test_boundary_hidden_half_from_the_append(cfg, monkeypatch):
+    """With the deferred QKV, the append pass that stores a boundary feature (one
+    boundary row with teacher-forced rows, multi-vector path) computes the feature's
+    hidden-half QKV sums in its K/V launch, and the chain that starts from the stored
+    feature runs no hidden-half launch of its own.  Against EAGLE3_BOUNDARY_QH=0 (that
+    launch in every chain): ids equal up to near-ties, logits and hidden within 1e-5,
+    over stored-boundary rounds on two sequence slots -- a prefill whose pass takes the
+    boundary row past 16 rows (MFMA pass: no sums, the chain computes them), short
+    prefills and single-sequence rebuilds (sums from the K/V launch), rebuilds of both
+    sequences in one pass (two boundary rows: no sums) and a boundary-only prefill
+    (no K/V launch: no sums)."""
+    from eagle_draft_head_amd.drafter import Drafter
+    wd, _ = weights_both(cfg)
+    gamma = 4
+
+    def make():
+        return Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=400, max_gamma=8, max_seqs=2)
+
+    monkeypatch.setenv("EAGLE3_BOUNDARY_QH", "0")
+    ref = make()
+    monkeypatch.delenv("EAGLE3_BOUNDARY_QH")
+    bq = make()
+    drs = (bq, ref)
+    aux = aux_np(cfg, 0, 300)
+    toks = toks_np(cfg, 0, 300)
+    baux = aux_np(cfg, 1, 64)
+    btok = toks_np(cfg, 1, 64)
+    raux = aux_np(cfg, 2, 64 * (gamma + 1))
+    nb = 0  # next boundary row
+
+    def nxt(k=1):
+        nonlocal nb
+        nb += k
+        return slice(nb - k, nb)
+
+    sl = nxt()
+    for dr in drs:  # 40 rows + the boundary: one MFMA pass
+        dr.prefill(0, _tok(toks[:40]), to_dev_aux([a[:40] for a in aux]), next_aux=to_dev_aux(baux, sl))
+    sl = nxt()
+    for dr in drs:  # 5 rows + the boundary: the multi-vector pass with the sums
+        dr.prefill(1, _tok(toks[40:45]), to_dev_aux([a[40:45] for a in aux]), next_aux=to_dev_aux(baux, sl))
+    last_tok = {0: int(toks[39]), 1: int(toks[44])}
+    for r in range(12):
+        for sq in (0, 1):
+            say(f"[boundary qh] {cfg.name} round {r} seq {sq}")
+            res = []
+            for dr in drs:
+                out, geff, logits, hidden = dr.draft_chain([sq], _tok([last_tok[sq]]), None, gamma, debug=True)
+                torch.cuda.synchronize()
+                res.append((out.cpu(), int(geff[0]), logits.double().cpu(), hidden.double().cpu()))
+            (o1, g1, l1, h1), (o2, g2, l2, h2) = res
+            assert g1 == g2 == gamma
+            top2 = torch.topk(l2[0, :g2], 2, dim=-1).values
+            gap = (top2[:, 0] - top2[:, 1]).abs()
+            ok = int(torch.nonzero(gap < 1e-4).min()) if bool((gap < 1e-4).any()) else g2
+            assert torch.equal(o1[0, :ok], o2[0, :ok]), (r, o1, o2)
+            for j in range(min(ok + 1, g2)):
+                assert (l1[0, j] - l2[0, j]).norm() / l2[0, j].norm() < 1e-5, (r, j)
+            for j in range(min(ok + 2, g2 + 1)):
+                assert (h1[0, j] - h2[0, j]).norm() / h2[0, j].norm() < 1e-5, (r, j)
+        # the next boundary: rebuild one sequence, both in one pass, or (round 7)
+        # a boundary-only prefill
+        a = r % (gamma + 1)
+        if r == 7:
+            sl = nxt()
+            for dr in drs:
+                dr.prefill(1, _tok([]), [None, None, None], next_aux=to_dev_aux(baux, sl))
+            continue
+        both = r % 4 == 3
+        rs = [0, 1] if both else [r % 2]
+        rows = slice(r * (gamma + 1), r * (gamma + 1) + (a + 1) * len(rs))
+        new_tok = toks_np(cfg, 3 + r, (a + 1) * len(rs))
+        sl = nxt(len(rs))
+        for dr in drs:
+            dr.rebuild_after_verify(rs, [a] * len(rs), _tok(new_tok), to_dev_aux(raux, rows),
+                                    next_aux=to_dev_aux(baux, sl))
+        for i, sq in enumerate(rs):
+            last_tok[sq] = int(new_tok[(i + 1) * (a + 1) - 1])
+    for dr in drs:
+        dr.close()
+
+
 def test_chain_from_empty_cache():
     pinned, steps = _run_rounds(TINY, rounds=10, L=0, gamma=5)
     assert steps == 50
