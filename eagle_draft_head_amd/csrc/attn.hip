@@ -1469,32 +1469,141 @@ __global__ __launch_bounds__(256) void k_attn_q(AttnArgs a, int chunk, int S) {
 
 // ---------------------------------------------------------------------------
 // q8q5 decode attention on MFMA (head_dim 64 or 128, at most 16 query heads per KV
-// head), 16-row tiles in k_attn_mfma's ring.  Scores: per 32-dim block ks,
-// S^T_ks = K_ks . Q^T on v_mfma_f32_16x16x32_f16 with the codes as fp16 1024 + u (u =
-// the stored code + 128; one byte permute per two codes) against the queries as fp16
-// (hi, lo) pairs scaled by 2^e per query; the block adds D_k (S^T_ks - 1152 sum_ks q),
-// the sum over the blocks is scaled back by 2^-e.  Values: O^T = V^T P^T on
-// v_mfma_f32_16x16x16bf16_1k, output tile t = (block b, half h) holding dims
-// 32 b + 16 h + (0..15): A = the tile's codes over the 16 rows as bf16 128 + c, B = P^T
-// with each row's weight times that row's D_v of block b, as bf16 (hi, lo); the
-// block's M_v and the 128 offset give a per-(query, block) term
-// sum_r p_r (M_v - 128 D_v) added at the end.  The lane holding query c16's scores of
-// rows 4 g4 + v is P^T's operand lane, and O^T's D layout keeps query c16 in the
-// lane's column, so the online softmax rescales O in place.
+// head) over 16-row tiles.  Scores: per 32-dim block ks, S^T_ks = K_ks . Q^T on
+// v_mfma_f32_16x16x32_f16 with the codes as fp16 1024 + u (u = the stored code + 128;
+// one byte permute per two codes) against the queries as fp16 (hi, lo) pairs scaled
+// by 2^e per query; the product's accumulator starts at -1152 sum_ks q, the block
+// scales it by D_k, the sum over the blocks is scaled back by 2^-e.  Values: O^T =
+// V^T P^T on v_mfma_f32_16x16x16bf16_1k, output tile t = (block b, half h) holding
+// dims 32 b + 16 h + (0..15): A = the tile's codes over the 16 rows as bf16 128 + c, B
+// = P^T with each row's weight times that row's D_v of block b, as bf16 (hi, lo); the
+// block's M_v and the 128 offset give a per-(query, block) term sum_r p_r (M_v - 128
+// D_v) added at the end.  The lane holding query c16's scores of rows 4 g4 + v is
+// P^T's operand lane, and O^T's D layout keeps query c16 in the lane's column, so the
+// online softmax rescales O in place.
+//
+// Each wave streams its own tiles through a ring of kQmRing LDS slots: a tile's five
+// arrays (K codes, V nibbles, K scales, V high bits, V (D, M)) are contiguous runs of
+// the head's region, read with global_load_lds (a lane's 16 bytes land at its lane
+// slot of a 1 KB wave write), so kQmRing - 1 tiles are in flight without holding
+// registers.  Lanes choose their source chunks so that the reads are spread over the
+// LDS banks: chunk p of K row r holds the row's chunk p ^ (r % (hd / 16)); V nibble
+// rows sit in the order 4 (r % 4) + r / 4.  Tiles past the chunk's last row read rows
+// of the region beyond T (the region holds a multiple of 16 rows, zeroed at
+// allocation, so they are finite) and are masked out of the softmax.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// ring depth: three slots (three blocks a CU by LDS; 32767 rows, 40/8 heads: 22.5 us
+// against 23.7 with four slots and two blocks a CU); EAGLE3_QM_RING=4 for comparison
+constexpr int kQmRing = 3;
+// EAGLE3_QM_ODD=0 keeps the q8q5 kernel's split length as picked (for comparison)
+static bool T_odd_steps() {
+  static const bool v = [] {
+    const char* e = std::getenv("EAGLE3_QM_ODD");
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+static int qm_ring() {
+  static const int r = [] {
+    const char* e = std::getenv("EAGLE3_QM_RING");
+    return (e && e[0] == '4') ? 4 : kQmRing;
+  }();
+  return r;
+}
+
+// One lane's reads of a ring slot (LDS byte addresses), issued together and waited
+// for in the same statement: the compiler does not see them as LDS reads that the
+// ring's in-flight global_load_lds writes might alias (it would wait for every
+// outstanding write before each); the ring's own vmcnt wait orders them, and the
+// memory clobber keeps the slot's refill (issued after them) from moving above them.
+// kc[ks]: the lane's 8 K code bytes of block ks (ak[ks]); ksc: the K scales of rows
+// 4 g4 .. + 3 (as); vn[v], vh[v], dm[v]: the V nibbles, high-bit byte and (D, M) of
+// row 4 g4 + v (an, ah, ad: row 4 g4's, in the slot's row orders).
+__device__ __forceinline__ void qm_read(u32x2_t (&kc)[4], u32x4_t (&ksc)[2], uint32_t (&vn)[4], uint32_t (&vh)[4],
+                                        u32x4_t (&dm)[4], const uint32_t (&ak)[4], uint32_t as, uint32_t an,
+                                        uint32_t ah, uint32_t ad) {  // head_dim 128
+  asm volatile(
+      "ds_read_b64 %0, %18\n"
+      "ds_read_b64 %1, %19\n"
+      "ds_read_b64 %2, %20\n"
+      "ds_read_b64 %3, %21\n"
+      "ds_read_b128 %4, %22\n"
+      "ds_read_b128 %5, %22 offset:16\n"
+      "ds_read_b32 %6, %23\n"
+      "ds_read_b32 %7, %23 offset:256\n"
+      "ds_read_b32 %8, %23 offset:512\n"
+      "ds_read_b32 %9, %23 offset:768\n"
+      "ds_read_u8 %10, %24\n"
+      "ds_read_u8 %11, %24 offset:16\n"
+      "ds_read_u8 %12, %24 offset:32\n"
+      "ds_read_u8 %13, %24 offset:48\n"
+      "ds_read_b128 %14, %25\n"
+      "ds_read_b128 %15, %25 offset:16\n"
+      "ds_read_b128 %16, %25 offset:32\n"
+      "ds_read_b128 %17, %25 offset:48\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kc[0]), "=&v"(kc[1]), "=&v"(kc[2]), "=&v"(kc[3]), "=&v"(ksc[0]), "=&v"(ksc[1]), "=&v"(vn[0]),
+        "=&v"(vn[1]), "=&v"(vn[2]), "=&v"(vn[3]), "=&v"(vh[0]), "=&v"(vh[1]), "=&v"(vh[2]), "=&v"(vh[3]),
+        "=&v"(dm[0]), "=&v"(dm[1]), "=&v"(dm[2]), "=&v"(dm[3])
+      : "v"(ak[0]), "v"(ak[1]), "v"(ak[2]), "v"(ak[3]), "v"(as), "v"(an), "v"(ah), "v"(ad)
+      : "memory");
+}
+__device__ __forceinline__ void qm_read(u32x2_t (&kc)[2], u32x4_t& ksc, uint32_t (&vn)[4], uint32_t (&vh)[4],
+                                        u32x2_t (&dm)[4], const uint32_t (&ak)[2], uint32_t as, uint32_t an,
+                                        uint32_t ah, uint32_t ad) {  // head_dim 64
+  asm volatile(
+      "ds_read_b64 %0, %15\n"
+      "ds_read_b64 %1, %16\n"
+      "ds_read_b128 %2, %17\n"
+      "ds_read_u16 %3, %18\n"
+      "ds_read_u16 %4, %18 offset:128\n"
+      "ds_read_u16 %5, %18 offset:256\n"
+      "ds_read_u16 %6, %18 offset:384\n"
+      "ds_read_u8 %7, %19\n"
+      "ds_read_u8 %8, %19 offset:8\n"
+      "ds_read_u8 %9, %19 offset:16\n"
+      "ds_read_u8 %10, %19 offset:24\n"
+      "ds_read_b64 %11, %20\n"
+      "ds_read_b64 %12, %20 offset:8\n"
+      "ds_read_b64 %13, %20 offset:16\n"
+      "ds_read_b64 %14, %20 offset:24\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kc[0]), "=&v"(kc[1]), "=&v"(ksc), "=&v"(vn[0]), "=&v"(vn[1]), "=&v"(vn[2]), "=&v"(vn[3]),
+        "=&v"(vh[0]), "=&v"(vh[1]), "=&v"(vh[2]), "=&v"(vh[3]), "=&v"(dm[0]), "=&v"(dm[1]), "=&v"(dm[2]),
+        "=&v"(dm[3])
+      : "v"(ak[0]), "v"(ak[1]), "v"(as), "v"(an), "v"(ah), "v"(ad)
+      : "memory");
+}
 
 template <int HD>
-__global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S) {
-  constexpr int NB = HD / 32;  // 32-dim blocks: the k steps of S, the V scale blocks
+struct QmTile {
+  static constexpr int NB = HD / 32;       // 32-dim blocks
+  static constexpr int CPR = HD / 16;      // 16-byte chunks of a K row
+  static constexpr int CPV = HD / 32;      // 16-byte chunks of a V nibble row
+  // the arrays' first 16-byte chunk in a slot
+  static constexpr int K = 0, VN = HD, KS = VN + HD / 2, VH = KS + 2 * NB, VD = VH + HD / 8, END = VD + 4 * NB;
+  static constexpr int NI = (END + 63) / 64;  // 1 KB wave writes per tile
+  static constexpr int BYTES = NI * 1024;
+};
+
+template <int HD, int D>
+__global__ __launch_bounds__(256, D == 3 ? 3 : 2) void k_attn_qm(AttnArgs a, int chunk, int S) {
+  using TL = QmTile<HD>;
+  constexpr int NB = TL::NB;
   constexpr int NT = HD / 16;  // output tiles of O^T, t = 2 b + h
-  constexpr int R = kMfmaRing;
+  constexpr int NI = TL::NI;
   constexpr int STRIDE = 16 * kAttnWaves;
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
-  __shared__ float so[kAttnWaves][16][HD + 4];
+  static_assert(kAttnWaves * 16 * (HD + 4) * 4 <= kAttnWaves * D * TL::BYTES, "the merge fits in the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kAttnWaves * D * TL::BYTES];
   __shared__ float sm[kAttnWaves][16], sl[kAttnWaves][16];
 
   const int s = blockIdx.x, kvh = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
   const int G = a.n_head / a.n_head_kv;
   const int T = a.T, nkv = a.n_head_kv, cap = a.cap;
@@ -1502,76 +1611,90 @@ __global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S
   if (r0 >= T) return;
   if (a.kv_new && r1 == T) quantize_new_row<HD>(a, kvh);
   const bool direct = S == 1;
-  const int rlast = r1 - 1;
   const uint8_t* kreg = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* vreg = static_cast<const uint8_t*>(a.v_cache);
   const size_t hr0 = (size_t)kvh * cap, all = (size_t)nkv * cap;
-  const uint8_t* Kc = kreg + hr0 * HD;                           // codes [row][HD]
-  const uint8_t* Ks = kreg + all * HD + hr0 * NB * 2;            // fp16 scales [row][NB]
-  const uint8_t* Vn = vreg + hr0 * (HD / 2) + c16 * NB;          // lane c16's nibble bytes
-  const uint8_t* Vh = vreg + all * (HD / 2) + hr0 * (HD / 8) + ((c16 * NB) >> 2);
-  const uint8_t* Vd = vreg + all * (HD / 2 + HD / 8) + hr0 * NB * 4;  // (D, M) [row][NB]
-  const int hsh = (c16 * NB) & 3;  // the lane's first bit in its high-bit byte
 
-  // ring slot i: K codes of row tb + c16 (dims 32 ks + 8 g4 ..); the K scales, V
-  // codes and V (D, M) of rows tb + 4 g4 + v; row indices clamped to r1 - 1
-  uint2 kq[R][NB];
-  uint32_t kd[R][4][(NB + 1) / 2], vn[R][4], vh[R][4], dm[R][4][NB];
-  // the K part of a slot is refilled once its scores are computed, the V part once
-  // its products are issued (no copies of a slot's data are held)
-  auto load_k = [&](int i, int tb) {
-    const int rk = min(tb + c16, rlast);
+  // this lane's source for each of the tile's NI wave writes: the chunk's address at
+  // tile row 0 and the bytes per row of its array
+  const uint8_t* src[NI];
+  uint32_t rowb[NI];
 #pragma unroll
-    for (int ks = 0; ks < NB; ++ks)
-      kq[i][ks] = *reinterpret_cast<const uint2*>(Kc + (size_t)rk * HD + 32 * ks + 8 * g4);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const size_t rv = (size_t)min(tb + 4 * g4 + v, rlast);
-      if constexpr (NB == 4) {
-        const uint2 w = *reinterpret_cast<const uint2*>(Ks + rv * 8);
-        kd[i][v][0] = w.x;
-        kd[i][v][1] = w.y;
-      } else {
-        kd[i][v][0] = *reinterpret_cast<const uint32_t*>(Ks + rv * 4);
-      }
+  for (int k = 0; k < NI; ++k) {
+    const int c = 64 * k + lane;
+    if (c < TL::VN) {  // K codes: row r, slot p <- chunk p ^ (r % CPR)
+      const int r = c / TL::CPR, p = c % TL::CPR;
+      src[k] = kreg + hr0 * HD + r * HD + 16 * (p ^ (r % TL::CPR));
+      rowb[k] = HD;
+    } else if (c < TL::KS) {  // V nibbles: slot row q holds row 4 (q % 4) + q / 4
+      const int w = c - TL::VN, q = w / TL::CPV, p = w % TL::CPV;
+      const int r = 4 * (q % 4) + q / 4;
+      src[k] = vreg + hr0 * (HD / 2) + r * (HD / 2) + 16 * p;
+      rowb[k] = HD / 2;
+    } else if (c < TL::VH) {  // K scales
+      src[k] = kreg + all * HD + hr0 * NB * 2 + 16 * (c - TL::KS);
+      rowb[k] = NB * 2;
+    } else if (c < TL::VD) {  // V high bits
+      src[k] = vreg + all * (HD / 2) + hr0 * (HD / 8) + 16 * (c - TL::VH);
+      rowb[k] = HD / 8;
+    } else if (c < TL::END) {  // V (D, M)
+      src[k] = vreg + all * (HD / 2 + HD / 8) + hr0 * NB * 4 + 16 * (c - TL::VD);
+      rowb[k] = NB * 4;
+    } else {  // past the tile's bytes: a K chunk into the slot's unused tail
+      src[k] = kreg + hr0 * HD;
+      rowb[k] = HD;
     }
-  };
-  auto load_v = [&](int i, int tb) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const size_t rv = (size_t)min(tb + 4 * g4 + v, rlast);
-      if constexpr (NB == 4) {
-        vn[i][v] = *reinterpret_cast<const uint32_t*>(Vn + rv * (HD / 2));
-        const uint4 d = *reinterpret_cast<const uint4*>(Vd + rv * 16);
-        dm[i][v][0] = d.x; dm[i][v][1] = d.y; dm[i][v][2] = d.z; dm[i][v][3] = d.w;
-      } else {
-        vn[i][v] = *reinterpret_cast<const uint16_t*>(Vn + rv * (HD / 2));
-        const uint2 d = *reinterpret_cast<const uint2*>(Vd + rv * 8);
-        dm[i][v][0] = d.x; dm[i][v][1] = d.y;
-      }
-      vh[i][v] = Vh[rv * (HD / 8)];
-    }
-  };
-  auto load = [&](int i, int tb) {
-    load_k(i, tb);
-    load_v(i, tb);
-  };
+  }
+  uint8_t* wring = ring + wv * D * TL::BYTES;
+  // tile k of this wave starts at row tb0 + k STRIDE and goes to slot k % D.  Every
+  // step issues one tile D ahead, past the wave's last tile that tile again (a wave
+  // without tiles takes the block's first), so exactly D - 1 tiles' writes are in
+  // flight behind the one a step reads, and every lane takes part in every write.
   const int tb0 = r0 + 16 * wv;
+  const int ntile = tb0 < r1 ? (r1 - tb0 + STRIDE - 1) / STRIDE : 0;
+  // byte offsets of the chunks from kreg (a sequence's K and V regions span well under
+  // 4 GiB), at the wave's first tile
+  // (off: the next tile to issue; it advances by one wave step per tile up to the
+  // wave's last tile; islot: that tile's slot)
+  uint32_t off[NI], step[NI];
+  const int tfirst = ntile > 0 ? tb0 : r0;
 #pragma unroll
-  for (int i = 0; i < R; ++i)
-    if (tb0 + i * STRIDE < r1) load(i, tb0 + i * STRIDE);
+  for (int i = 0; i < NI; ++i) {
+    off[i] = uint32_t(src[i] - kreg) + uint32_t(tfirst) * rowb[i];
+    step[i] = uint32_t(STRIDE) * rowb[i];
+  }
+  int islot = 0;
+  auto issue = [&](int k) {
+    uint8_t* dst = wring + islot * TL::BYTES;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(kreg + off[i]),
+                                       (void __attribute__((address_space(3)))*)(dst + 1024 * i), 16, 0, 0);
+    if (k < ntile - 1)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) off[i] += step[i];
+    islot = islot + 1 == D ? 0 : islot + 1;
+  };
 
   // query c16's dims 32 ks + 8 g4 .. + 7 with the base-2 score scale, times 2^e
   // putting the query's largest value in [2^14, 2^15), as fp16 (hi, lo); columns
-  // past G are zero.  qs[ks]: the block's sum of (hi + lo) over its 32 dims.
+  // past G are zero.  qs[ks]: -1152 times the block's sum of (hi + lo) over its 32 dims.
   const float scale = 1.4426950408889634f / sqrtf(float(HD));
   const bool qok = c16 < G;
+  float4 qv[NB][2];  // loaded before the ring's first tiles are issued
+#pragma unroll
+  for (int ks = 0; ks < NB; ++ks) {
+    const float* qp = a.q + (size_t)(kvh * G + (qok ? c16 : 0)) * HD + 32 * ks + 8 * g4;
+    qv[ks][0] = *reinterpret_cast<const float4*>(qp);
+    qv[ks][1] = *reinterpret_cast<const float4*>(qp + 4);
+  }
+#pragma unroll
+  for (int k = 0; k < D; ++k) issue(k);
   float x[NB][8];
   float amax = 0.f;
 #pragma unroll
   for (int ks = 0; ks < NB; ++ks) {
-    const float* qp = a.q + (size_t)(kvh * G + (qok ? c16 : 0)) * HD + 32 * ks + 8 * g4;
-    const float4 u = *reinterpret_cast<const float4*>(qp), w = *reinterpret_cast<const float4*>(qp + 4);
+    const float4 u = qv[ks][0], w = qv[ks][1];
     const float y[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -1601,7 +1724,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S
     }
     t += __shfl_xor(t, 16, kWave);
     t += __shfl_xor(t, 32, kWave);
-    qs[ks] = 1152.f * t;
+    qs[ks] = -1152.f * t;
   }
   f32x4_t o[NT];
 #pragma unroll
@@ -1610,31 +1733,70 @@ __global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S
 #pragma unroll
   for (int b = 0; b < NB; ++b) cb[b] = 0.f;
   float m = -INFINITY, l = 0.f;
+  const int hsh = (c16 * NB) & 3;  // the lane's first bit in its high-bit byte
+  // the lane's LDS byte offsets in a slot (qm_read)
+  const uint32_t lds_w = uint32_t((uintptr_t)((__attribute__((address_space(3))) uint8_t*)wring));
+  uint32_t ak[NB];
+#pragma unroll
+  for (int ks = 0; ks < NB; ++ks)
+    ak[ks] = c16 * HD + 16 * ((2 * ks + (g4 >> 1)) ^ (c16 % TL::CPR)) + 8 * (g4 & 1);
+  const uint32_t o_s = 16 * TL::KS + 4 * g4 * (NB * 2), o_n = 16 * TL::VN + g4 * (HD / 2) + c16 * NB,
+                 o_h = 16 * TL::VH + 4 * g4 * (HD / 8) + ((c16 * NB) >> 2), o_d = 16 * TL::VD + 4 * g4 * (NB * 4);
 
-  auto step = [&](int i, int tb) {
+  int rslot = 0;
+  for (int k = 0; k < ntile; ++k) {
+    // tile k has landed once at most the D - 1 later tiles' writes are outstanding
+    wait_vmcnt<(D - 1) * NI>();
+    const int tb = tb0 + k * STRIDE;
+    const uint32_t sb = lds_w + uint32_t(rslot * TL::BYTES);
+    rslot = rslot + 1 == D ? 0 : rslot + 1;
+    u32x2_t kc[NB];
+    uint32_t kd[4][(NB + 1) / 2], vn[4], vh[4], dm[4][NB];
+    uint32_t aks[NB];
+#pragma unroll
+    for (int ks = 0; ks < NB; ++ks) aks[ks] = sb + ak[ks];
+    if constexpr (NB == 4) {
+      u32x4_t ksc[2], dmv[4];
+      qm_read(kc, ksc, vn, vh, dmv, aks, sb + o_s, sb + o_n, sb + o_h, sb + o_d);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        kd[v][0] = (v & 1) ? ksc[v >> 1].z : ksc[v >> 1].x;
+        kd[v][1] = (v & 1) ? ksc[v >> 1].w : ksc[v >> 1].y;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dm[v][b] = dmv[v][b];
+      }
+    } else {
+      u32x4_t ksc;
+      u32x2_t dmv[4];
+      qm_read(kc, ksc, vn, vh, dmv, aks, sb + o_s, sb + o_n, sb + o_h, sb + o_d);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        kd[v][0] = ksc[v];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dm[v][b] = dmv[v][b];
+      }
+    }
     // scores of rows tb + 4 g4 + v for query c16 (times 2^e)
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NB; ++ks) {
-      const uint32_t c0 = kq[i][ks].x, c1 = kq[i][ks].y;
+      const u32x2_t kq = kc[ks];
       const uint32_t e4 = 0x64646464u;  // fp16 1024 + u: high byte 0x64 over the code
       uint4 av;
-      av.x = __builtin_amdgcn_perm(e4, c0, 0x04010400u);
-      av.y = __builtin_amdgcn_perm(e4, c0, 0x04030402u);
-      av.z = __builtin_amdgcn_perm(e4, c1, 0x04010400u);
-      av.w = __builtin_amdgcn_perm(e4, c1, 0x04030402u);
+      av.x = __builtin_amdgcn_perm(e4, kq.x, 0x04010400u);
+      av.y = __builtin_amdgcn_perm(e4, kq.x, 0x04030402u);
+      av.z = __builtin_amdgcn_perm(e4, kq.y, 0x04010400u);
+      av.w = __builtin_amdgcn_perm(e4, kq.y, 0x04030402u);
       const f16x8_t ka = __builtin_bit_cast(f16x8_t, av);
-      f32x4_t st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[ks], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      f32x4_t st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[ks], f32x4_t{qs[ks], qs[ks], qs[ks], qs[ks]}, 0, 0, 0);
       st = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[ks], st, 0, 0, 0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint32_t w = kd[i][v][ks >> 1];
+        const uint32_t w = kd[v][ks >> 1];
         const float Dk = f16_bits_to_f32(uint16_t((ks & 1) ? (w >> 16) : (w & 0xFFFFu)));
-        acc[v] = fmaf(Dk, st[v] - qs[ks], acc[v]);
+        acc[v] = fmaf(Dk, st[v], acc[v]);
       }
     }
-    const bool refill = tb + R * STRIDE < r1;
-    if (refill) load_k(i, tb + R * STRIDE);
     float sc[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) sc[v] = (tb + 4 * g4 + v < r1) ? acc[v] * down : -INFINITY;
@@ -1667,25 +1829,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S
     uint32_t clo[4], chi[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const uint32_t nb = vn[i][v];
-      const uint32_t hr = ((vh[i][v] >> hsh) & 0xFFu) * 0x01010101u;
+      const uint32_t nb = vn[v];
+      const uint32_t hr = ((vh[v] >> hsh) & 0xFFu) * 0x01010101u;
       clo[v] = (nb & 0x0F0F0F0Fu) | ((((hr & 0x08040201u) + 0x787C7E7Fu) & 0x80808080u) >> 3);
       chi[v] = ((nb >> 4) & 0x0F0F0F0Fu) | ((((hr & 0x80402010u) + 0x00406070u) & 0x80808080u) >> 3);
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      // P^T for block b: each row's weight times its D_v, as bf16 (hi, lo)
-      bf16x4s_t ph, pl;
+      // P^T for block b: each row's weight times its D_v, as bf16 (hi, lo), converted
+      // two values an instruction
+      f32x4_t pv;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float Dv = f16_bits_to_f32(uint16_t(dm[i][v][b] & 0xFFFFu));
-        const float Mv = f16_bits_to_f32(uint16_t(dm[i][v][b] >> 16));
-        const float pv = pr[v] * Dv;
-        const __bf16 h = (__bf16)pv;
-        ph[v] = __builtin_bit_cast(short, h);
-        pl[v] = __builtin_bit_cast(short, (__bf16)(pv - (float)h));
+        const float Dv = f16_bits_to_f32(uint16_t(dm[v][b] & 0xFFFFu));
+        const float Mv = f16_bits_to_f32(uint16_t(dm[v][b] >> 16));
+        pv[v] = pr[v] * Dv;
         cb[b] = fmaf(pr[v], fmaf(-128.f, Dv, Mv), cb[b]);
       }
+      const f32x2_t p01 = {pv[0], pv[1]}, p23 = {pv[2], pv[3]};
+      const bf16x2_t h01 = __builtin_convertvector(p01, bf16x2_t), h23 = __builtin_convertvector(p23, bf16x2_t);
+      const bf16x2_t l01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2_t), bf16x2_t);
+      const bf16x2_t l23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2_t), bf16x2_t);
+      const bf16x4s_t ph = __builtin_bit_cast(bf16x4s_t, u32x2_t{__builtin_bit_cast(uint32_t, h01),
+                                                                  __builtin_bit_cast(uint32_t, h23)});
+      const bf16x4s_t pl = __builtin_bit_cast(bf16x4s_t, u32x2_t{__builtin_bit_cast(uint32_t, l01),
+                                                                  __builtin_bit_cast(uint32_t, l23)});
       const uint32_t sel = uint32_t(b) | (0x0Cu << 8) | (uint32_t(4 + b) << 16) | (0x0Cu << 24);
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -1699,18 +1867,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S
         o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, o[t], 0, 0, 0);
       }
     }
-    if (refill) load_v(i, tb + R * STRIDE);
-  };
-  int tb = tb0;
-  for (; tb + (R - 1) * STRIDE < r1; tb += R * STRIDE) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) step(i, tb + i * STRIDE);
+    // the slot is free once every lane's reads of it are done
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    issue(k + D);
   }
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-    if (tb + i * STRIDE < r1) step(i, tb + i * STRIDE);
+  wait_vmcnt<0>();  // the ring's last writes have landed before it turns into the merge buffer
 
   // the per-(query, block) terms over the lane group's rows, then the waves merge
+  // (the merge buffer takes the ring's place once every wave is done with it)
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     cb[b] += __shfl_xor(cb[b], 16, kWave);
@@ -1720,6 +1884,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_qm(AttnArgs a, int chunk, int S
     sm[wv][c16] = m;
     sl[wv][c16] = l;
   }
+  __syncthreads();
+  float(*so)[16][HD + 4] = reinterpret_cast<float(*)[16][HD + 4]>(ring);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1868,6 +2034,18 @@ static int attn_single_blocks() {
   return t;
 }
 
+// A power-of-two split length of the VALU decode kernel grows by one row block: then
+// not every block's reads start at the same power-of-two offsets (32767 fp32 rows,
+// 40/8 heads: 47.5 against 49.1 us with 512-row splits; the bf16 MFMA kernel showed no
+// difference).  EAGLE3_ATTN_ODD=0 keeps the power of two.
+static bool attn_odd() {
+  static const bool v = [] {
+    const char* e = std::getenv("EAGLE3_ATTN_ODD");
+    return !(e && e[0] == '0');
+  }();
+  return v;
+}
+
 static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int* S, int blocks = 0,
                        int rpb = 0) {
   if (rpb <= 0) rpb = rows_per_block(hd, kv_f32);
@@ -1877,6 +2055,7 @@ static void pick_split(int T, int n_head_kv, int hd, int kv_f32, int* chunk, int
   c = ((c + rpb - 1) / rpb) * rpb;
   if (c < rpb) c = rpb;
   if (c > kAttnMaxChunk) c = kAttnMaxChunk;
+  if (attn_odd() && (c & (c - 1)) == 0 && c >= 256 && c < T) c += rpb;
   *chunk = c;
   *S = (T + c - 1) / c;
 }
@@ -2180,13 +2359,28 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   else pick_split(a.T, a.n_head_kv, a.head_dim, a.kv_f32, &chunk, &S);
   if (a.kv_q) {
     if (a.head_dim <= 128 && G <= 16 && !attn_valu()) {
+      // the MFMA kernel reads whole 16-row tiles: the region must hold a multiple of
+      // 16 rows (zeroed at allocation)
+      if (a.cap % 16) return hipErrorInvalidValue;
       // twice the blocks of the bf16 kernel: two waves a SIMD hide more of the
       // decode's latency (32767 rows, 40/8 heads: 40.7 us against 43.9 with 256,
       // attention and combine)
       pick_split_mfma(a.T, a.n_head_kv, &chunk, &S, std::getenv("EAGLE3_ATTN_BLOCKS") ? 0 : kAttnQmBlocks);
+      // an odd number of 64-row wave steps per split: with an even number (512- or
+      // 1024-row splits) every block's reads start at the same power-of-two offsets
+      // and the kernel ran 25-40 % slower (32767 rows, 40/8 heads: 33-36 us against
+      // 24-28 with 576-row splits)
+      if (T_odd_steps() && (chunk / 64) % 2 == 0 && chunk < a.T) {
+        chunk += 64;
+        S = (a.T + chunk - 1) / chunk;
+      }
       dim3 grid(S, a.n_head_kv), block(64 * kAttnWaves);
-      if (a.head_dim == 64) hipLaunchKernelGGL(k_attn_qm<64>, grid, block, 0, s, a, chunk, S);
-      else if (a.head_dim == 128) hipLaunchKernelGGL(k_attn_qm<128>, grid, block, 0, s, a, chunk, S);
+      if (qm_ring() == 4) {
+        if (a.head_dim == 64) hipLaunchKernelGGL((k_attn_qm<64, 4>), grid, block, 0, s, a, chunk, S);
+        else if (a.head_dim == 128) hipLaunchKernelGGL((k_attn_qm<128, 4>), grid, block, 0, s, a, chunk, S);
+        else return hipErrorInvalidValue;
+      } else if (a.head_dim == 64) hipLaunchKernelGGL((k_attn_qm<64, 3>), grid, block, 0, s, a, chunk, S);
+      else if (a.head_dim == 128) hipLaunchKernelGGL((k_attn_qm<128, 3>), grid, block, 0, s, a, chunk, S);
       else return hipErrorInvalidValue;
       hipError_t e = hipGetLastError();
       if (e != hipSuccess || S == 1) return e;

@@ -440,6 +440,9 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   c->qd = int(qd); c->kvd = int(kvd); c->ff = int(ff); c->dv = int(dv); c->vt = int(vt);
   c->rot = cfg->rope_dim;
   c->cap = cfg->max_ctx + 1;
+  // quantized regions hold a multiple of 16 rows: their decode attention reads whole
+  // 16-row tiles (rows past T stay finite: the regions are zeroed below)
+  if (cfg->kv_dtype == EAGLE3_KV_Q8Q5) c->cap = (c->cap + 15) / 16 * 16;
   c->ledger = e3::Ledger(cfg->max_ctx, cfg->max_seqs, cfg->max_gamma);
   hipStream_t s = as_stream(stream);
 
@@ -483,6 +486,8 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
                             : size_t(2) * kvd * size_t(c->cap);
   if (c->kv_q) E3_TRY(dalloc(c, &c->kv_stage, size_t(2) * kvd));
   E3_TRY(dalloc(c, &c->kv, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize));
+  if (c->kv_q)
+    E3_TRYH(hipMemsetAsync(c->kv, 0, c->kv_seq_elems * size_t(cfg->max_seqs) * c->kv_esize, s), "kv zero");
 
   E3_TRY(dalloc(c, &c->x1, size_t(n)));
   E3_TRY(dalloc(c, &c->x1w, size_t(n)));
@@ -518,10 +523,13 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
   E3_TRY(dalloc(c, &c->bnd_y, size_t(cfg->max_seqs) * n));
   E3_TRY(dalloc(c, &c->bnd_w, size_t(cfg->max_seqs) * n));
   E3_TRY(dalloc(c, &c->bnd_ssq, size_t(cfg->max_seqs)));
-  c->cap_local = cfg->max_gamma;
+  c->cap_local = c->kv_q ? (cfg->max_gamma + 15) / 16 * 16 : cfg->max_gamma;
   c->kv_local_elems = c->kv_q ? 2 * e3::kvq_region_bytes(int(c->nkv), c->cap_local, int(c->hd))
                              : size_t(2) * c->nkv * c->cap_local * c->hd;
   E3_TRY(dalloc(c, &c->kv_local, size_t(cfg->max_seqs) * c->kv_local_elems * c->kv_esize));
+  if (c->kv_q)
+    E3_TRYH(hipMemsetAsync(c->kv_local, 0, size_t(cfg->max_seqs) * c->kv_local_elems * c->kv_esize, s),
+            "local kv zero");
   E3_TRY(dalloc(c, &c->inv_freq, size_t(c->rot / 2)));
 
   // 4096-row passes: at the 5120-wide drafter W_fc's 256 x 320 output tiles then

@@ -150,7 +150,8 @@ typedef struct {
    when appended (teacher-forced rows as they are stored, a chain step's row by the
    attention block that owns it), and every read sees the quantized values, the new
    row's included.  Batch-1 drafting only (max_seqs 1); prefill activations keep the
-   fp32-grade path of EAGLE3_KV_F32. */
+   fp32-grade path of EAGLE3_KV_F32.  The quantized regions hold max_ctx + 1 rows
+   rounded up to a multiple of 16 and are zeroed by eagle3_load. */
 #define EAGLE3_KV_Q8Q5 2
 
 /* Projection-weight format (ExecuTorch PR #20154 names a weight-stationary INT4
