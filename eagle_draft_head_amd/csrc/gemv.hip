@@ -20,8 +20,9 @@
 //   k_lmhead_qh   k_lmhead plus the next step's hidden-half QKV sums (deferred
 //                 QKV: the attention kernel finishes that step's q and K/V row)
 // The multi-vector kernel (teacher-forced rows) applies each weight chunk to
-// M activation vectors and splits K so the M vectors fit in LDS; it writes
-// split partials that the next kernel sums.  k_gemv_multi_qh is its K/V pass
+// M activation vectors and splits K so the M vectors fit in LDS (with int4 weights
+// as five-digit fixed point per group, v_dot8 products); it writes split partials
+// that the next kernel sums.  k_gemv_multi_qh is its K/V pass
 // with the hidden-half QKV sums of the boundary feature the pass writes in the
 // same launch (the next chain's first step then starts at its attention).
 //
@@ -208,6 +209,69 @@ __device__ __forceinline__ void quant_x_i4(const float* __restrict__ xs, int K,
       xp[(j & 3) * G + (j >> 2)] = pl;
       if ((j & 3) == 0) xe[j >> 2] = e;
     }
+  }
+}
+
+// The five-digit form for the teacher-forced rows (their K/V rows are stored, so they
+// keep about the precision of fp32 products): e = 18 - E, |x_q| <= 2^18, and
+// x_q + 0x88888 has five base-16 digits; planes 0..3 laid out as above, plane 4 as
+// [G] uint4 (component i holds elements 8i..8i+7 of group g).
+// Eight elements of a group (one of its four quads of threads) in five-digit fixed
+// point: planes 0..3 (pl), plane 4 (p4, element k in nibble k) and the group's
+// exponent e.  Every lane of the quad calls it (the group maximum is a quad reduction).
+__device__ __forceinline__ void quant8_5(const float (&v)[8], uint4& pl, uint32_t& p4, int& e) {
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[k]));
+  m = fmaxf(m, dpp_move<kDppQuadSwap1>(m));
+  m = fmaxf(m, dpp_move<kDppQuadSwap2>(m));
+  e = 18 - (int((__float_as_uint(m) >> 23) & 0xFFu) - 126);
+  uint32_t u[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float t = __builtin_amdgcn_fmed3f(rintf(ldexpf(v[k], e)), -262144.f, 262144.f);
+    u[k] = uint32_t(int(t) + 0x88888);  // 20 bits
+  }
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = swap_mid_nibbles(__builtin_amdgcn_perm(u[2 * i + 1], u[2 * i], 0x05010400u));
+  const uint32_t t01l = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);
+  const uint32_t t01h = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);
+  const uint32_t t23l = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+  const uint32_t t23h = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+  pl = make_uint4(__builtin_amdgcn_perm(t23l, t01l, 0x05040100u) ^ 0x88888888u,
+                  __builtin_amdgcn_perm(t23l, t01l, 0x07060302u) ^ 0x88888888u,
+                  __builtin_amdgcn_perm(t23h, t01h, 0x05040100u) ^ 0x88888888u,
+                  __builtin_amdgcn_perm(t23h, t01h, 0x07060302u) ^ 0x88888888u);
+  uint32_t q = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q |= ((u[k] >> 16) & 0xFu) << (4 * k);
+  p4 = q ^ 0x88888888u;
+}
+
+// q_group with the five digit planes
+template <int R>
+__device__ __forceinline__ void q_group5(const uint4 (&w)[R], const uint16_t (&sc)[R], int g, int G,
+                                         const uint4* __restrict__ xp, const uint4* __restrict__ x4p,
+                                         const int* __restrict__ xe, float (&acc)[R]) {
+  const uint4 p0 = xp[g], p1 = xp[G + g], p2 = xp[2 * G + g], p3 = xp[3 * G + g], p4 = x4p[g];
+  const int e = xe[g];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int w0 = int(w[r].x ^ 0x88888888u), w1 = int(w[r].y ^ 0x88888888u);
+    const int w2 = int(w[r].z ^ 0x88888888u), w3 = int(w[r].w ^ 0x88888888u);
+    const uint32_t pp[5][4] = {{p0.x, p1.x, p2.x, p3.x}, {p0.y, p1.y, p2.y, p3.y}, {p0.z, p1.z, p2.z, p3.z},
+                               {p0.w, p1.w, p2.w, p3.w}, {p4.x, p4.y, p4.z, p4.w}};
+    int gs = 0;
+#pragma unroll
+    for (int t = 4; t >= 0; --t) {
+      if (t < 4) gs <<= 4;
+      gs = __builtin_amdgcn_sdot8(w0, int(pp[t][0]), gs, false);
+      gs = __builtin_amdgcn_sdot8(w1, int(pp[t][1]), gs, false);
+      gs = __builtin_amdgcn_sdot8(w2, int(pp[t][2]), gs, false);
+      gs = __builtin_amdgcn_sdot8(w3, int(pp[t][3]), gs, false);
+    }
+    acc[r] = fmaf(ldexpf(float(gs), -e), bf16_to_f32(sc[r]), acc[r]);
   }
 }
 
@@ -1165,30 +1229,54 @@ __device__ __forceinline__ void gemv_multi_block(int bx, int z, const uint16_t* 
       sp[r] = nullptr;
     }
   }
-  // stage the M vectors: one flat loop over all M * k4 float4 of the chunk, so every
-  // thread's loads are in flight together (vectors past `rows` are zero)
-  {
+  // element k of vector m (fp32): from the tap streams or one matrix
+  auto src_of = [&](int m, int k) -> const float* {
+    if (x1) {
+      const int sgi = k / seg;
+      // rows from yb.rows_x on come from the second set of streams
+      const bool second = m >= yb.rows_x;
+      const float* base = second ? (sgi == 0 ? yb.y[0] : (sgi == 1 ? yb.y[1] : yb.y[2]))
+                                 : (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2));
+      return base + (size_t)(second ? m - yb.rows_x : m) * seg + (k - sgi * seg);
+    }
+    return x0 + (size_t)m * K + k;
+  };
+  // int4: each vector's chunk in five-digit fixed point per group of 32, quantised
+  // straight from the sources once per block (planes [M][4][G] uint4, plane 4
+  // [M][G] uint4, exponents [M][G]); bf16: the M vectors staged as floats
+  uint4* xpl = reinterpret_cast<uint4*>(xs);
+  uint4* xp4 = xpl + (size_t)M * (kc >> 3);
+  int* xex = reinterpret_cast<int*>(xp4 + (size_t)M * (kc >> 5));
+  if constexpr (I4) {
+    const int nq = klen >> 3, G = klen >> 5, total = M * nq;  // nq % 4 == 0: quads stay in one vector
+    for (int j0 = 0; j0 < total; j0 += NT) {  // same trip count for every lane
+      const int j = j0 + int(threadIdx.x);
+      const int m = j / nq, jj = j - m * nq;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (j < total && m < rows) {
+        const float* p = src_of(m, k0 + 8 * jj);
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+      }
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint4 pl;
+      uint32_t p4;
+      int e;
+      quant8_5(v, pl, p4, e);
+      if (j < total) {
+        xpl[(size_t)m * (kc >> 3) + (jj & 3) * G + (jj >> 2)] = pl;
+        reinterpret_cast<uint32_t*>(xp4 + (size_t)m * (kc >> 5))[jj] = p4;
+        if ((jj & 3) == 0) xex[m * (kc >> 5) + (jj >> 2)] = e;
+      }
+    }
+  } else {
     float4* dst = reinterpret_cast<float4*>(xs);
     const int total = M * k4;
 #pragma unroll 4
     for (int idx = threadIdx.x; idx < total; idx += NT) {
       const int m = idx / k4, i = idx - m * k4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m < rows) {
-        const int k = k0 + 4 * i;
-        const float* src;
-        if (x1) {
-          const int sgi = k / seg;
-          // rows from yb.rows_x on come from the second set of streams
-          const bool second = m >= yb.rows_x;
-          const float* base = second ? (sgi == 0 ? yb.y[0] : (sgi == 1 ? yb.y[1] : yb.y[2]))
-                                     : (sgi == 0 ? x0 : (sgi == 1 ? x1 : x2));
-          src = base + (size_t)(second ? m - yb.rows_x : m) * seg + (k - sgi * seg);
-        } else {
-          src = x0 + (size_t)m * K + k;
-        }
-        v = *reinterpret_cast<const float4*>(src);
-      }
+      if (m < rows) v = *reinterpret_cast<const float4*>(src_of(m, k0 + 4 * i));
       dst[(size_t)m * (kc >> 2) + i] = v;
     }
   }
@@ -1209,52 +1297,27 @@ __device__ __forceinline__ void gemv_multi_block(int bx, int z, const uint16_t* 
     }
   };
   if constexpr (I4) {
-    // group c: each row's 32 codes are converted and scaled once and applied to
-    // the M vectors; the -8 * scale * sum(x) term per group at the end
+    // group c: v_dot8 of each row's 32 codes with each vector's five digit planes,
+    // scaled by the row's scale and the vector's 2^-e (q_group5)
+    const int G = nch;
     for (int c = lane; c < nch; c += 64) {
       uint4 w[R];
-      float sr[R];
+      uint16_t sc[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         w[r] = ld_stream(wp[r] + c);
-        sr[r] = bf16_to_f32(sp[r][c]);
-      }
-      float xsum[M];
-#pragma unroll
-      for (int m = 0; m < M; ++m) xsum[m] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float4 xa[M], xb[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const float4* x4 = reinterpret_cast<const float4*>(xs + m * kc);
-          xa[m] = x4[8 * c + 2 * i];
-          xb[m] = x4[8 * c + 2 * i + 1];
-          xsum[m] += ((xa[m].x + xa[m].y) + (xa[m].z + xa[m].w)) + ((xb[m].x + xb[m].y) + (xb[m].z + xb[m].w));
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t wd = i == 0 ? w[r].x : (i == 1 ? w[r].y : (i == 2 ? w[r].z : w[r].w));
-          const uint32_t lo = wd & 0x0F0F0F0Fu, hi = (wd >> 4) & 0x0F0F0F0Fu;
-          const float f0 = float(lo & 0xFFu) * sr[r], f1 = float(hi & 0xFFu) * sr[r];
-          const float f2 = float((lo >> 8) & 0xFFu) * sr[r], f3 = float((hi >> 8) & 0xFFu) * sr[r];
-          const float f4 = float((lo >> 16) & 0xFFu) * sr[r], f5 = float((hi >> 16) & 0xFFu) * sr[r];
-          const float f6 = float(lo >> 24) * sr[r], f7 = float(hi >> 24) * sr[r];
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            float t = acc[r][m];
-            t = fmaf(f0, xa[m].x, t); t = fmaf(f1, xa[m].y, t);
-            t = fmaf(f2, xa[m].z, t); t = fmaf(f3, xa[m].w, t);
-            t = fmaf(f4, xb[m].x, t); t = fmaf(f5, xb[m].y, t);
-            t = fmaf(f6, xb[m].z, t); t = fmaf(f7, xb[m].w, t);
-            acc[r][m] = t;
-          }
-        }
+        sc[r] = sp[r][c];
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int m = 0; m < M; ++m) {
+        float am[R];
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[r][m] = fmaf(-8.f * sr[r], xsum[m], acc[r][m]);
+        for (int r = 0; r < R; ++r) am[r] = acc[r][m];
+        q_group5<R>(w, sc, c, G, xpl + (size_t)m * (kc >> 3), xp4 + (size_t)m * (kc >> 5), xex + m * (kc >> 5),
+                    am);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][m] = am[r];
+      }
     }
   } else {
     for (int c = lane; c < nch; c += 64) {
@@ -1560,14 +1623,16 @@ hipError_t launch_gemv_multi(const uint16_t* W, const uint16_t* S, int N, int K,
   const int splits = ceil_div(K, kc);
   *splits_out = splits;
   dim3 grid(ceil_div(N, multi_rows_per_block(m)), splits), block(512);
-  const size_t lds = size_t(m) * kc * sizeof(float);
+  // the staged floats, and with int4 weights their digit planes and exponents
+  const size_t lds = S ? size_t(m) * (2 * kc + kc / 2 + kc / 8) : size_t(m) * kc * sizeof(float);
   switch (m) {
 #define MCASE(MM)                                                                              \
   case MM:                                                                                     \
-    if (S)                                                                                     \
+    if (S) {                                                                                   \
+      E3_LDS_ALLOW((k_gemv_multi<MM, true>), lds);                                             \
       hipLaunchKernelGGL((k_gemv_multi<MM, true>), grid, block, lds, s, W, S, N, K, kc, x0, x1, x2, \
                          seg, rows, P, yb);                                                    \
-    else                                                                                       \
+    } else                                                                                     \
       hipLaunchKernelGGL((k_gemv_multi<MM, false>), grid, block, lds, s, W, S, N, K, kc, x0, x1,  \
                          x2, seg, rows, P, yb);                                                \
     break;
