@@ -140,7 +140,7 @@ struct eagle3_ctx {
   // (or alone for a chain's first step) and finished by the attention kernel
   float* hsum = nullptr;
   bool defer_qkv = false;
-  // with the deferred QKV (bf16 weights): the hidden-half sums of each slot's stored
+  // with the deferred QKV: the hidden-half sums of each slot's stored
   // boundary feature [max_seqs][N_qkv], computed by the append pass that writes the
   // feature (its K/V launch); bnd_hsum_ok[slot] says whether the slot's current
   // feature came with them (EAGLE3_BOUNDARY_QH=0: never, for comparison)
@@ -756,7 +756,7 @@ int eagle3_load(const eagle3_config* cfg, const eagle3_weights* w, void* stream,
       c->defer_qkv = !(dq && dq[0] == '0') && c->lm_grid <= e3::kDqMaxCandidates;
       if (c->defer_qkv) E3_TRY(dalloc(c, &c->hsum, N_qkv));
       const char* bq = std::getenv("EAGLE3_BOUNDARY_QH");
-      if (c->defer_qkv && !c->i4 && !(bq && bq[0] == '0')) {
+      if (c->defer_qkv && !(bq && bq[0] == '0')) {
         E3_TRY(dalloc(c, &c->bnd_hsum, size_t(cfg->max_seqs) * N_qkv));
         c->bnd_hsum_ok.assign(size_t(cfg->max_seqs), 0);
       }
@@ -1038,8 +1038,9 @@ int append_rows(eagle3_ctx* c, const std::vector<AppendSeg>& segs, int total, co
                                                    nullptr, c->bnd_ssq + slot, 1});
         q.hsum = c->bnd_hsum + size_t(slot) * q.N;
         ProfScope ps(c, 8, s);
-        E3_HIP(c, e3::launch_gemv_multi_qh(c->w_qkv + size_t(c->qd) * 2 * n, kvd2, 2 * n, c->tf_cat32, T, c->tf_P,
-                                           &sp2, q, s),
+        E3_HIP(c, e3::launch_gemv_multi_qh(c->wq(c->w_qkv, c->i4_qkv, size_t(c->qd), 2 * n),
+                                           c->ws(c->i4_qkv, size_t(c->qd), 2 * n), kvd2, 2 * n, c->tf_cat32, T,
+                                           c->tf_P, &sp2, q, s),
                "kv gemv + boundary qkv hidden half");
         c->bnd_hsum_ok[size_t(slot)] = 1;
       } else if (T > 0) {

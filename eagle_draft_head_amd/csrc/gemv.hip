@@ -1118,23 +1118,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_lmhead_qh(LmHeadArgs a, QhArgs q
   qh_block<WAVES, R, U, ISSUE>(q, int(blockIdx.x), xs, red);
 }
 
-// k_lmhead_qh with int4 weights: the first qb blocks cover the nvq virtual blocks of
-// hidden-half rows (int4 codes of columns k0 .. k0 + n; g quantised once per block),
-// the next lb blocks the int4 lm_head's nvl virtual blocks (candidate slots)
+// The int4 hidden-half sums of virtual blocks bid, bid + qb, ... (of nvq; WAVES x R
+// rows each): g staged and quantised once per block, each virtual block's first U
+// chunk steps issued before the previous one's products
 template <int WAVES, int R, int U>
-__global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_lmhead_qh_i4(LmHeadArgs a, QhArgs q, int qb,
-                                                                                int nvq, int lb) {
-  extern __shared__ float xs[];  // [n], then the quantised vector
-  __shared__ float red[32];
-  __shared__ float bv_s[16];
-  __shared__ int bi_s[16], bt_s[16];
-  if (int(blockIdx.x) >= qb) {
-    lmhead_i4<WAVES, R, U>(a, int(blockIdx.x) - qb, lb, xs, red, bv_s, bi_s, bt_s);
-    return;
-  }
+__device__ __forceinline__ void qh_i4_block(const QhArgs& q, int bid, int qb, int nvq, float* xs, float* red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint8_t* Q = reinterpret_cast<const uint8_t*>(q.w);
-  int row0 = (blockIdx.x * WAVES + wv) * R;
+  int row0 = (bid * WAVES + wv) * R;
   QLoad<R, U> L;
   if (row0 < q.N) q_issue<R, U>(Q, q.s, q.ldw, row0, q.N, q.k0, q.n, L);
   stage_plain(xs, q.gw, q.n);
@@ -1145,7 +1136,7 @@ __global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_lmhead_qh_i4(Lm
   quant_x_i4(xs, q.n, xp, xe);
   block_sum2(sg, dummy, red);  // its barriers also publish the quantised vector
   const float ig = 1.0f / sqrtf(sg / float(q.n) + q.eps);
-  for (int vb = blockIdx.x;; vb += qb) {
+  for (int vb = bid;; vb += qb) {
     const int vn = vb + qb, rn = (vn * WAVES + wv) * R;
     QLoad<R, U> Ln;
     if (vn < nvq && rn < q.N) q_issue<R, U>(Q, q.s, q.ldw, rn, q.N, q.k0, q.n, Ln);
@@ -1160,6 +1151,23 @@ __global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_lmhead_qh_i4(Lm
     L = Ln;
     row0 = rn;
   }
+}
+
+// k_lmhead_qh with int4 weights: the first qb blocks cover the nvq virtual blocks of
+// hidden-half rows (int4 codes of columns k0 .. k0 + n; g quantised once per block),
+// the next lb blocks the int4 lm_head's nvl virtual blocks (candidate slots)
+template <int WAVES, int R, int U>
+__global__ __launch_bounds__(64 * WAVES, kI4WavesPerSimd) void k_lmhead_qh_i4(LmHeadArgs a, QhArgs q, int qb,
+                                                                                int nvq, int lb) {
+  extern __shared__ float xs[];  // [n], then the quantised vector
+  __shared__ float red[32];
+  __shared__ float bv_s[16];
+  __shared__ int bi_s[16], bt_s[16];
+  if (int(blockIdx.x) >= qb) {
+    lmhead_i4<WAVES, R, U>(a, int(blockIdx.x) - qb, lb, xs, red, bv_s, bi_s, bt_s);
+    return;
+  }
+  qh_i4_block<WAVES, R, U>(q, int(blockIdx.x), qb, nvq, xs, red);
 }
 
 // the last step of a chain: argmax over the lm_head candidates, d2t (the
@@ -1644,9 +1652,51 @@ hipError_t launch_gemv_multi(const uint16_t* W, const uint16_t* S, int N, int K,
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_multi_qh(const uint16_t* W, int N, int K, const float* x0, int rows, float* P,
-                                int* splits_out, const QhArgs& q, hipStream_t s) {
+// k_gemv_multi_qh with int4 weights: blocks [0, qb) the hidden-half sums (qh_i4_block in
+// the int4 GEMVs' 8-wave, 2-row, 2-step form over nvq virtual blocks), the rest the
+// int4 multi-vector GEMV's (row block, K chunk) grid
+template <int M>
+__global__ __launch_bounds__(512) void k_gemv_multi_qh_i4(const uint16_t* __restrict__ W,
+                                                          const uint16_t* __restrict__ S, int N, int K, int kc,
+                                                          const float* __restrict__ x0, int rows,
+                                                          float* __restrict__ P, QhArgs q, int qb, int nvq, int gx) {
+  static_assert(MultiShape<M>::WAVES == 8, "512 threads");
+  extern __shared__ float xs[];
+  __shared__ float red[32];
+  const int b = int(blockIdx.x);
+  if (b < qb) {
+    qh_i4_block<8, 2, 2>(q, b, qb, nvq, xs, red);
+    return;
+  }
+  const int t = b - qb;
+  const TapRowsB none{{nullptr, nullptr, nullptr}, 1 << 30};
+  gemv_multi_block<M, true>(t % gx, t / gx, W, S, N, K, kc, x0, nullptr, nullptr, 0, rows, P, none, xs);
+}
+
+hipError_t launch_gemv_multi_qh(const uint16_t* W, const uint16_t* S, int N, int K, const float* x0, int rows,
+                                float* P, int* splits_out, const QhArgs& q, hipStream_t s) {
   const int m = gemv_multi_width(rows);
+  if (S) {  // int4: W codes and S scales of the K/V rows, q the int4 hidden half
+    if (m < 0 || (K % 32) || !q.s || (q.n % 32) || (q.k0 % 32) || q.N < 1) return hipErrorInvalidValue;
+    const int kc = multi_kchunk(m, N, K);
+    const int splits = ceil_div(K, kc);
+    *splits_out = splits;
+    const int gx = ceil_div(N, multi_rows_per_block(m)), nvq = ceil_div(q.N, 16), qb = i4_grid(nvq);
+    const size_t lds = std::max(size_t(m) * (2 * kc + kc / 2 + kc / 8), size_t(q.n) * sizeof(float) + q_vec_bytes(q.n));
+    switch (m) {
+#define MCASE(MM)                                                                                        \
+  case MM:                                                                                               \
+    E3_LDS_ALLOW((k_gemv_multi_qh_i4<MM>), lds);                                                         \
+    E3_LAUNCH((k_gemv_multi_qh_i4<MM>), dim3(qb + gx * splits), dim3(512), lds, s, W, S, N, K, kc, x0, rows, \
+              P, q, qb, nvq, gx);                                                                        \
+    break;
+      MCASE(1) MCASE(2) MCASE(3) MCASE(4) MCASE(5) MCASE(6) MCASE(8) MCASE(9) MCASE(12) MCASE(16)
+#undef MCASE
+      default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   if (m < 0 || (K % 8) || q.s || (q.n % 8) || q.N < 1) return hipErrorInvalidValue;
   const int kc = multi_kchunk(m, N, K);
   const int splits = ceil_div(K, kc);

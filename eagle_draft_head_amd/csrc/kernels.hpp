@@ -191,11 +191,11 @@ int gemv_multi_splits(int rows, int N, int K);  // chunk count the launch will u
 hipError_t launch_gemv_multi(const uint16_t* W, const uint16_t* S, int N, int K, const float* x0,
                              const float* x1, const float* x2, int seg, int rows, float* P,
                              int* splits_out, hipStream_t s, const TapRowsB& yb = no_tap_rows_b());
-// launch_gemv_multi over bf16 W with one fp32 activation matrix x0 [rows, K], plus
-// the hidden-half sums q (as launch_lmhead_qh without lm_head, bf16 rows only) in
-// the same launch
-hipError_t launch_gemv_multi_qh(const uint16_t* W, int N, int K, const float* x0, int rows, float* P,
-                                int* splits_out, const QhArgs& q, hipStream_t s);
+// launch_gemv_multi with one fp32 activation matrix x0 [rows, K], plus the hidden-half
+// sums q (as launch_lmhead_qh without lm_head) in the same launch; S non-null: W
+// holds int4 codes and S their scales, and q the int4 hidden half
+hipError_t launch_gemv_multi_qh(const uint16_t* W, const uint16_t* S, int N, int K, const float* x0, int rows,
+                                float* P, int* splits_out, const QhArgs& q, hipStream_t s);
 
 // ---- batched drafting: up to kBatchRows sequences per pass ----
 constexpr int kBatchRows = 32;

@@ -49,7 +49,7 @@ enum {
 /* eagle3_draft_chain flag: start each listed sequence from its stored boundary
    feature (set by eagle3_prefill / eagle3_rebuild_after_verify from next-boundary
    taps) instead of encoding taps; the tap pointers must then be NULL.  With the
-   token table and bf16 weights, an append pass of at most 16 rows that stores one
+   token table (and fp32 or bf16 K/V), an append pass of at most 16 rows that stores one
    boundary feature with teacher-forced rows also computes the hidden half of that
    feature's QKV projection (in its K/V launch), and the batch-1 chain that starts
    from it runs no launch of its own for it (environment EAGLE3_BOUNDARY_QH=0 turns

@@ -287,8 +287,9 @@ def test_deferred_qkv_at_split_boundaries(hd, nh, nkv, kv, monkeypatch):
         dr.close()
 
 
-@pytest.mark.parametrize("cfg", [TINY, small_variant()], ids=["tiny", "ragged"])
-def test_boundary_hidden_half_from_the_append(cfg, monkeypatch):
+@pytest.mark.parametrize("cfg,weights", [(TINY, "bf16"), (small_variant(), "bf16"), (TINY, "int4")],
+                         ids=["tiny", "ragged", "tiny-int4"])
+def test_boundary_hidden_half_from_the_append(cfg, weights, monkeypatch):
     """With the deferred QKV, the append pass that stores a boundary feature (one
     boundary row with teacher-forced rows, multi-vector path) computes the feature's
     hidden-half QKV sums in its K/V launch, and the chain that starts from the stored
@@ -298,13 +299,16 @@ def test_boundary_hidden_half_from_the_append(cfg, monkeypatch):
     boundary row past 16 rows (MFMA pass: no sums, the chain computes them), short
     prefills and single-sequence rebuilds (sums from the K/V launch), rebuilds of both
     sequences in one pass (two boundary rows: no sums) and a boundary-only prefill
-    (no K/V launch: no sums)."""
+    (no K/V launch: no sums); with int4 weights the sums stream the int4 codes of the
+    hidden half in the int4 K/V launch."""
     from eagle_draft_head_amd.drafter import Drafter
     wd, _ = weights_both(cfg)
     gamma = 4
+    wf = B.WEIGHTS_I4 if weights == "int4" else B.WEIGHTS_BF16
+    nseq = 1 if weights == "int4" else 2  # int4 weights: batch-1 drafting only (one slot)
 
     def make():
-        return Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=400, max_gamma=8, max_seqs=2)
+        return Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=400, max_gamma=8, max_seqs=nseq, weight_format=wf)
 
     monkeypatch.setenv("EAGLE3_BOUNDARY_QH", "0")
     ref = make()
@@ -328,11 +332,11 @@ def test_boundary_hidden_half_from_the_append(cfg, monkeypatch):
         dr.prefill(0, _tok(toks[:40]), to_dev_aux([a[:40] for a in aux]), next_aux=to_dev_aux(baux, sl))
     sl = nxt()
     for dr in drs:  # 5 rows + the boundary: the multi-vector pass with the sums
-        dr.prefill(1, _tok(toks[40:45]), to_dev_aux([a[40:45] for a in aux]), next_aux=to_dev_aux(baux, sl))
-    last_tok = {0: int(toks[39]), 1: int(toks[44])}
+        dr.prefill(nseq - 1, _tok(toks[40:45]), to_dev_aux([a[40:45] for a in aux]), next_aux=to_dev_aux(baux, sl))
+    last_tok = {0: int(toks[39]) if nseq == 2 else int(toks[44]), nseq - 1: int(toks[44])}
     for r in range(12):
-        for sq in (0, 1):
-            say(f"[boundary qh] {cfg.name} round {r} seq {sq}")
+        for sq in range(nseq):
+            say(f"[boundary qh] {cfg.name} {weights} round {r} seq {sq}")
             res = []
             for dr in drs:
                 out, geff, logits, hidden = dr.draft_chain([sq], _tok([last_tok[sq]]), None, gamma, debug=True)
@@ -354,10 +358,10 @@ def test_boundary_hidden_half_from_the_append(cfg, monkeypatch):
         if r == 7:
             sl = nxt()
             for dr in drs:
-                dr.prefill(1, _tok([]), [None, None, None], next_aux=to_dev_aux(baux, sl))
+                dr.prefill(nseq - 1, _tok([]), [None, None, None], next_aux=to_dev_aux(baux, sl))
             continue
-        both = r % 4 == 3
-        rs = [0, 1] if both else [r % 2]
+        both = r % 4 == 3 and nseq == 2
+        rs = [0, 1] if both else [r % nseq]
         rows = slice(r * (gamma + 1), r * (gamma + 1) + (a + 1) * len(rs))
         new_tok = toks_np(cfg, 3 + r, (a + 1) * len(rs))
         sl = nxt(len(rs))
