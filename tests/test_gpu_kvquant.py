@@ -142,3 +142,53 @@ def test_kvq_chain_parity(cfg, L, rounds, gamma, local, i4):
     if R:
         _kv_close(dr, orc, R)
     dr.close()
+
+
+@pytest.mark.parametrize("cfg,max_ctx", [(TINY, 95), (TINY, 90), (HD128, 127), (HD128, 121)],
+                         ids=["hd64-cap96", "hd64-cap96-slack", "hd128-cap128", "hd128-cap128-slack"])
+def test_kvq_chain_to_capacity(cfg, max_ctx):
+    """The MFMA q8q5 attention reads whole 16-row tiles, past T up to the region's
+    row count (max_ctx + 1 rounded up to 16, zeroed at load): chains and rebuilds
+    that fill the cache to its last row (the tile past T then ends exactly at the
+    region's end, or inside the rounding slack) match the oracle round by round,
+    down to gamma_eff 0."""
+    say(f"[kvq] {cfg.name} chains to capacity, max_ctx={max_ctx}")
+    gamma = 4
+    wd = gen.drafter_weights(cfg, device="cuda")
+    dr = Drafter(cfg, wd, wd["d2t"].cpu(), max_ctx=max_ctx, kv_dtype=B.KV_Q8Q5)
+    wh = {k: v.cpu() for k, v in wd.items()}
+    orc = make_oracle(cfg, wh, max_ctx=max_ctx, kv_format="q8q5", append_act="f16")
+    L = max_ctx - 12
+    aux, toks = aux_np(cfg, 0, L), toks_np(cfg, 0, L)
+    orc.prefill(0, aux, toks)
+    dr.prefill(0, torch.as_tensor(toks, dtype=torch.int32).cuda(), to_dev_aux(aux))
+    rounds = 12
+    baux, btok = aux_np(cfg, 1, rounds), toks_np(cfg, 1, rounds)
+    raux = aux_np(cfg, 2, rounds * (gamma + 1))
+    seen_full = False
+    for r in range(rounds):
+        b_aux = [a[r] for a in baux]
+        recs = orc.draft_chain(0, b_aux, btok[r], gamma)
+        out, geff, logits, hidden = dr.draft_chain([0], torch.tensor([int(btok[r])], dtype=torch.int32).cuda(),
+                                                   to_dev_aux(baux, slice(r, r + 1)), gamma, debug=True)
+        torch.cuda.synchronize()
+        g = int(geff[0])
+        assert g == len(recs), (g, len(recs))
+        if g == 0:
+            seen_full = True
+            assert out[0].eq(-1).all()
+            break
+        check_round(compare_round(recs, out, g, logits, hidden), f"kvq capacity round {r}")
+        committed = orc.ledger.committed(0)
+        a = min(r % (g + 1), max_ctx - committed - 1)
+        if a < 0:
+            break
+        rows = slice(r * (gamma + 1), r * (gamma + 1) + a)
+        new_aux = [np.concatenate([ba[r:r + 1], ra[rows]]) for ba, ra in zip(baux, raux)]
+        new_tok = np.array([btok[r]] + [x.target_id for x in recs[:a]], dtype=np.int32)
+        orc.rebuild_after_verify(0, a, new_aux, new_tok)
+        dr.rebuild_after_verify([0], [a], torch.as_tensor(new_tok).cuda(), to_dev_aux(new_aux))
+        assert dr.kv_len(0) == (orc.ledger.committed(0), 0)
+    assert seen_full or orc.ledger.committed(0) >= max_ctx - gamma
+    _kv_close(dr, orc, orc.ledger.committed(0))
+    dr.close()
