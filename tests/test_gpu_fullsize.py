@@ -34,6 +34,7 @@ def _variants(names):
         "f32-f16": (B.KV_F32, B.APPEND_F16, "exact", "f16"),
         "f32-act16": (B.KV_F32, B.APPEND_BF16, "exact", "bf16"),
         "bf16": (B.KV_BF16, B.APPEND_DEFAULT, "bf16", "f16"),
+        "q8q5": (B.KV_Q8Q5, B.APPEND_DEFAULT, "q8q5", "f16"),
     }
     return [(n,) + table[n] for n in names]
 
@@ -186,6 +187,23 @@ def test_long_context_parity():
     for p in pairs:
         _kv_check(p, rows)
     _rounds(cfg, pairs, [3] * 6, [2, None, 3, 0, 1, 3])
+    for p in pairs:
+        assert p.pinned >= p.steps // 3, p.name
+    _close(pairs)
+
+
+def test_long_context_parity_q8q5():
+    """The q8_0 / q5_1 draft KV at the 5120-wide drafter with a 32767-row prefill: the
+    MFMA decode kernel streams the whole cache through its LDS ring in splits of an
+    odd number of 64-row wave steps (576 rows here); rows on both sides of the first
+    pass boundary and the last row, then four rounds with rebuilds, against the
+    oracle's q8q5 mode."""
+    cfg = LONG
+    L = cfg.context
+    pairs = _setup(cfg, L, cfg.max_ctx, ["q8q5"])
+    for p in pairs:
+        _kv_check(p, [0, 1, 4095, 4096, 4097, L - 1])
+    _rounds(cfg, pairs, [3] * 4, [2, None, 3, 0])
     for p in pairs:
         assert p.pinned >= p.steps // 3, p.name
     _close(pairs)
